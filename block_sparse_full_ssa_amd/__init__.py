@@ -1,0 +1,9 @@
+"""SSA (Sparse Sparse Attention) dual-stream attention for MI355X (gfx950).
+
+The computation lives in libssa.so (HIP kernels behind a C interface,
+include/ssa.h); this package only binds it to torch tensors.
+"""
+from ._lib import (DUAL_ACTIVE_FULL, DUAL_ACTIVE_SPARSE, FULL_ONLY, SPARSE_ONLY,  # noqa: F401
+                   SSAError)
+from .ops import (kernel_names, ssa_attn_bwd, ssa_attn_fwd, ssa_select_blocks,  # noqa: F401
+                  timing_enable, timing_query)

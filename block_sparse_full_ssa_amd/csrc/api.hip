@@ -1,0 +1,285 @@
+// C entry points of libssa: argument validation on the host, workspace
+// carving, kernel dispatch on the caller's stream, status reporting and the
+// optional event timing.  See include/ssa.h for the contract.
+
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "ssa.h"
+#include "internal.h"
+
+namespace ssa {
+
+static thread_local std::string g_last_error;
+
+static ssa_status_t fail(ssa_status_t st, const char* fmt, const char* detail = "") {
+  char buf[512];
+  snprintf(buf, sizeof(buf), fmt, detail);
+  g_last_error = buf;
+  return st;
+}
+
+// ---------------------------------------------------------------- timing ---
+struct TimingRec {
+  int kernel;
+  hipEvent_t a, b;
+};
+static bool g_timing = false;
+static std::vector<TimingRec> g_recs;
+static const char* kKernelNames[kKernelCount] = {
+    "block_mean", "select", "fwd_simt", "fwd_mfma", "loss_reduce",
+    "bwd_pre",    "bwd_simt", "bwd_mfma", "convert", "zero"};
+
+void timing_begin(int kernel, hipStream_t s) {
+  if (!g_timing) return;
+  TimingRec r{kernel, nullptr, nullptr};
+  if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return;
+  (void)hipEventRecord(r.a, s);
+  g_recs.push_back(r);
+}
+
+void timing_end(int kernel, hipStream_t s) {
+  if (!g_timing || g_recs.empty()) return;
+  TimingRec& r = g_recs.back();
+  if (r.kernel == kernel) (void)hipEventRecord(r.b, s);
+}
+
+static void timing_clear() {
+  for (auto& r : g_recs) {
+    if (r.a) (void)hipEventDestroy(r.a);
+    if (r.b) (void)hipEventDestroy(r.b);
+  }
+  g_recs.clear();
+}
+
+// ------------------------------------------------------------ validation ---
+static ssa_status_t make_dims(const ssa_shape_t* sh, Dims* D) {
+  if (!sh) return fail(SSA_ERR_NULL, "shape is NULL%s");
+  if (sh->batch < 1 || sh->heads_q < 1 || sh->group < 1 || sh->seqlen < 1 || sh->top_k < 1)
+    return fail(SSA_ERR_SHAPE, "batch, heads_q, group, seqlen and top_k must be >= 1%s");
+  if (sh->heads_q % sh->group != 0) return fail(SSA_ERR_SHAPE, "group must divide heads_q%s");
+  if (sh->dtype != SSA_F32 && sh->dtype != SSA_BF16) return fail(SSA_ERR_UNSUPPORTED, "dtype must be SSA_F32 or SSA_BF16%s");
+  if (sh->head_dim != 64 && sh->head_dim != 128) return fail(SSA_ERR_UNSUPPORTED, "head_dim must be 64 or 128%s");
+  if (sh->block != 32 && sh->block != 64 && sh->block != 128)
+    return fail(SSA_ERR_UNSUPPORTED, "block must be 32, 64 or 128%s");
+  if (sh->seqlen % sh->block != 0) return fail(SSA_ERR_SHAPE, "seqlen must be a multiple of block%s");
+  const int nb = sh->seqlen / sh->block;
+  if (sh->top_k > 64 && sh->top_k < nb)
+    return fail(SSA_ERR_UNSUPPORTED, "top_k above 64 is supported only when it selects every block%s");
+  const int64_t rows = static_cast<int64_t>(sh->batch) * sh->heads_q * sh->seqlen;
+  if (rows * sh->head_dim >= (static_cast<int64_t>(1) << 40) || rows / 4 >= (static_cast<int64_t>(1) << 31))
+    return fail(SSA_ERR_SHAPE, "layer too large%s");
+  if (!(sh->softmax_scale == sh->softmax_scale)) return fail(SSA_ERR_SHAPE, "softmax_scale is NaN%s");
+  D->B = sh->batch;
+  D->Hq = sh->heads_q;
+  D->G = sh->group;
+  D->Hkv = sh->heads_q / sh->group;
+  D->N = sh->seqlen;
+  D->d = sh->head_dim;
+  D->block = sh->block;
+  D->nb = nb;
+  D->K = sh->top_k;
+  D->dtype = sh->dtype;
+  D->scale = sh->softmax_scale > 0.f ? sh->softmax_scale : static_cast<float>(1.0 / sqrt(static_cast<double>(sh->head_dim)));
+  return SSA_OK;
+}
+
+static bool valid_mode(int32_t m) { return m >= kDualFull && m <= kSparseOnly; }
+
+static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+static size_t esize(const Dims& D) { return D.dtype == 1 ? 2 : 4; }
+
+// Workspace carving: a bump allocator over the caller's buffer.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  template <typename T>
+  T* take(size_t bytes) {
+    T* p = reinterpret_cast<T*>(base ? base + used : nullptr);
+    used += align256(bytes);
+    return p;
+  }
+};
+
+struct FwdWs {
+  float* row_sq;
+};
+static FwdWs carve_fwd(const Dims& D, int mode, Carver& c) {
+  FwdWs w{};
+  if (mode == kDualFull || mode == kDualSparse) w.row_sq = c.take<float>(D.rows() * sizeof(float));
+  return w;
+}
+
+struct BwdWs {
+  float *dk_acc, *dv_acc;
+};
+static BwdWs carve_bwd(const Dims& D, int mode, Carver& c) {
+  (void)mode;
+  BwdWs w{};
+  w.dk_acc = c.take<float>(D.kv_elems() * sizeof(float));
+  w.dv_acc = c.take<float>(D.kv_elems() * sizeof(float));
+  return w;
+}
+
+static size_t ws_need(const Dims& D, int mode, int op) {
+  Carver c{nullptr};
+  if (op == SSA_OP_SELECT) c.take<float>(static_cast<size_t>(D.B) * D.Hkv * D.d * D.nb * sizeof(float));
+  else if (op == SSA_OP_FWD) carve_fwd(D, mode, c);
+  else carve_bwd(D, mode, c);
+  return c.used;
+}
+
+static ssa_status_t check_ws(const Dims& D, int mode, int op, void* ws, size_t ws_bytes) {
+  const size_t need = ws_need(D, mode, op);
+  if (need == 0) return SSA_OK;
+  if (!ws) return fail(SSA_ERR_NULL, "workspace is NULL%s");
+  if (ws_bytes < need) return fail(SSA_ERR_WORKSPACE, "workspace too small%s");
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(SSA_ERR_WORKSPACE, "workspace not 256-byte aligned%s");
+  return SSA_OK;
+}
+
+static ssa_status_t launch_status() {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(SSA_ERR_HIP, "HIP launch failed: %s", hipGetErrorString(e));
+  return SSA_OK;
+}
+
+}  // namespace ssa
+
+using namespace ssa;
+
+extern "C" {
+
+size_t ssa_workspace_size(const ssa_shape_t* shape, int32_t mode, int32_t op) {
+  Dims D;
+  if (make_dims(shape, &D) != SSA_OK || !valid_mode(mode) || op < SSA_OP_SELECT || op > SSA_OP_BWD) return 0;
+  return ws_need(D, mode, op);
+}
+
+ssa_status_t ssa_select_blocks(const ssa_shape_t* shape, const void* q, const void* k, int32_t* sel,
+                               void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  Dims D;
+  ssa_status_t st = make_dims(shape, &D);
+  if (st != SSA_OK) return st;
+  if (!q || !k || !sel) return fail(SSA_ERR_NULL, "q, k and sel are required%s");
+  if ((st = check_ws(D, 0, SSA_OP_SELECT, ws, ws_bytes)) != SSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* muT = static_cast<float*>(ws);
+  launch_block_mean(D, k, muT, s);
+  if ((st = launch_status()) != SSA_OK) return st;
+  launch_select(D, q, muT, sel, s);
+  return launch_status();
+}
+
+ssa_status_t ssa_attn_fwd(const ssa_shape_t* shape, int32_t mode, const void* q, const void* k,
+                          const void* v, const int32_t* sel, void* h_full, void* h_sparse,
+                          float* lse_full, float* lse_sparse, float* delta, float* losses, void* ws,
+                          size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  Dims D;
+  ssa_status_t st = make_dims(shape, &D);
+  if (st != SSA_OK) return st;
+  if (!valid_mode(mode)) return fail(SSA_ERR_SHAPE, "unknown mode%s");
+  const bool dual = mode == kDualFull || mode == kDualSparse;
+  if (!q || !k || !v) return fail(SSA_ERR_NULL, "q, k and v are required%s");
+  if (mode != kFullOnly && (!sel || !h_sparse)) return fail(SSA_ERR_NULL, "sel and h_sparse are required%s");
+  if (mode != kSparseOnly && !h_full) return fail(SSA_ERR_NULL, "h_full is required%s");
+  if (dual && (!delta || !losses)) return fail(SSA_ERR_NULL, "delta and losses are required in dual modes%s");
+  if ((st = check_ws(D, mode, SSA_OP_FWD, ws, ws_bytes)) != SSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c{static_cast<char*>(ws)};
+  FwdWs w = carve_fwd(D, mode, c);
+  FwdArgs a{q, k, v, sel, h_full, h_sparse, lse_full, lse_sparse, delta, w.row_sq, mode};
+  if (fwd_mfma_supported(D)) launch_fwd_mfma(D, a, s);
+  else launch_fwd_simt(D, a, s);
+  if ((st = launch_status()) != SSA_OK) return st;
+  if (dual) {
+    launch_loss_reduce(w.row_sq, D.rows(), 1.0 / static_cast<double>(D.q_elems()), losses, s);
+    st = launch_status();
+  }
+  return st;
+}
+
+ssa_status_t ssa_attn_bwd(const ssa_shape_t* shape, int32_t mode, float w_sparsity, float w_commit,
+                          const void* q, const void* k, const void* v, const int32_t* sel,
+                          const void* h_full, const void* h_sparse, const float* lse_full,
+                          const float* lse_sparse, const void* d_out, void* dq, void* dk, void* dv,
+                          void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  Dims D;
+  ssa_status_t st = make_dims(shape, &D);
+  if (st != SSA_OK) return st;
+  if (!valid_mode(mode)) return fail(SSA_ERR_SHAPE, "unknown mode%s");
+  if (!q || !k || !v || !dq || !dk || !dv) return fail(SSA_ERR_NULL, "q, k, v, dq, dk and dv are required%s");
+  if (mode != kFullOnly && (!sel || !h_sparse || !lse_sparse))
+    return fail(SSA_ERR_NULL, "sel, h_sparse and lse_sparse are required%s");
+  if (mode != kSparseOnly && (!h_full || !lse_full)) return fail(SSA_ERR_NULL, "h_full and lse_full are required%s");
+  if (!(w_sparsity == w_sparsity) || !(w_commit == w_commit)) return fail(SSA_ERR_SHAPE, "loss weight is NaN%s");
+  if ((st = check_ws(D, mode, SSA_OP_BWD, ws, ws_bytes)) != SSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Carver c{static_cast<char*>(ws)};
+  BwdWs w = carve_bwd(D, mode, c);
+  launch_zero_f32(w.dk_acc, D.kv_elems(), s);
+  launch_zero_f32(w.dv_acc, D.kv_elems(), s);
+  if ((st = launch_status()) != SSA_OK) return st;
+  BwdArgs a{q, k, v, sel, h_full, h_sparse, lse_full, lse_sparse, d_out, dq, w.dk_acc, w.dv_acc,
+            w_sparsity, w_commit, mode};
+  launch_bwd_simt(D, a, s);
+  if ((st = launch_status()) != SSA_OK) return st;
+  launch_convert(w.dk_acc, dk, D.dtype, D.kv_elems(), s);
+  launch_convert(w.dv_acc, dv, D.dtype, D.kv_elems(), s);
+  return launch_status();
+}
+
+const char* ssa_status_string(int32_t status) {
+  switch (status) {
+    case SSA_OK: return "ok";
+    case SSA_ERR_NULL: return "null pointer";
+    case SSA_ERR_SHAPE: return "invalid shape or argument";
+    case SSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SSA_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case SSA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* ssa_last_error(void) { return g_last_error.c_str(); }
+
+ssa_status_t ssa_timing_enable(int32_t enabled) {
+  timing_clear();
+  g_timing = enabled != 0;
+  return SSA_OK;
+}
+
+ssa_status_t ssa_timing_query(const char* kernel, double* total_ms, int64_t* launches) {
+  if (!kernel || !total_ms || !launches) return fail(SSA_ERR_NULL, "null argument%s");
+  int id = -1;
+  for (int i = 0; i < kKernelCount; ++i)
+    if (strcmp(kernel, kKernelNames[i]) == 0) id = i;
+  if (id < 0) return fail(SSA_ERR_SHAPE, "unknown kernel name %s", kernel);
+  double tot = 0.0;
+  int64_t n = 0;
+  for (auto& r : g_recs) {
+    if (r.kernel != id || !r.b) continue;
+    if (hipEventSynchronize(r.b) != hipSuccess) return fail(SSA_ERR_HIP, "event synchronize failed%s");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) return fail(SSA_ERR_HIP, "event elapsed time failed%s");
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return SSA_OK;
+}
+
+int32_t ssa_kernel_count(void) { return kKernelCount; }
+
+const char* ssa_kernel_name(int32_t i) { return (i >= 0 && i < kKernelCount) ? kKernelNames[i] : ""; }
+
+}  // extern "C"

@@ -1,0 +1,67 @@
+// Device-side helpers shared by the libssa kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssa {
+
+constexpr int kWave = 64;
+
+// bf16 is carried as its raw 16 bits; widening to fp32 is a shift.
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+  return __uint_as_float(static_cast<uint32_t>(x.bits) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (gfx950 has a hardware conversion).
+__device__ __forceinline__ bf16_t to_bf16(float x) {
+  __bf16 h = static_cast<__bf16>(x);
+  bf16_t r;
+  r.bits = __builtin_bit_cast(uint16_t, h);
+  return r;
+}
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return to_bf16(x); }
+
+// Sum over the 64 lanes of a wave; every lane receives the total.  The
+// butterfly order is fixed, so the result is deterministic.
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, kWave);
+  return x;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+  return x;
+}
+
+// Order-preserving map of a finite fp32 score to an unsigned integer.
+__device__ __forceinline__ uint32_t ordered_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = __shfl_xor(static_cast<uint32_t>(x), off, kWave);
+    uint32_t hi = __shfl_xor(static_cast<uint32_t>(x >> 32), off, kWave);
+    uint64_t y = (static_cast<uint64_t>(hi) << 32) | lo;
+    x = y > x ? y : x;
+  }
+  return x;
+}
+
+}  // namespace ssa

@@ -1,0 +1,80 @@
+// Internal launch interface between the C entry points (api.hip) and the
+// kernel translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssa {
+
+// Validated layer dimensions.
+struct Dims {
+  int B, Hq, Hkv, G, N, d, block, nb, K;
+  int dtype;        // 0 fp32, 1 bf16
+  float scale;      // softmax scale on q.k
+  int64_t rows() const { return static_cast<int64_t>(B) * Hq * N; }
+  int64_t q_elems() const { return rows() * d; }
+  int64_t kv_elems() const { return static_cast<int64_t>(B) * Hkv * N * d; }
+};
+
+enum Mode { kDualFull = 0, kDualSparse = 1, kFullOnly = 2, kSparseOnly = 3 };
+
+// Kernel identifiers for the optional event timing.
+enum KernelId {
+  kKBlockMean = 0,
+  kKSelect,
+  kKFwdSimt,
+  kKFwdMfma,
+  kKLossReduce,
+  kKBwdPre,
+  kKBwdSimt,
+  kKBwdMfma,
+  kKConvert,
+  kKZero,
+  kKernelCount
+};
+
+// Timing hooks (api.hip); no-ops unless timing is enabled.
+void timing_begin(int kernel, hipStream_t s);
+void timing_end(int kernel, hipStream_t s);
+
+// --- selection (select.hip) ---
+void launch_block_mean(const Dims& D, const void* k, float* muT, hipStream_t s);
+void launch_select(const Dims& D, const void* q, const float* muT, int32_t* sel, hipStream_t s);
+
+// --- generic SIMT kernels (simt.hip): every supported shape, fp32 and bf16 ---
+struct FwdArgs {
+  const void *q, *k, *v;
+  const int32_t* sel;
+  void *h_full, *h_sparse;
+  float *lse_full, *lse_sparse, *delta;
+  float* row_sq;     // per-row sum of (h_full - h_sparse)^2, dual modes only
+  int mode;
+};
+void launch_fwd_simt(const Dims& D, const FwdArgs& a, hipStream_t s);
+
+struct BwdArgs {
+  const void *q, *k, *v;
+  const int32_t* sel;
+  const void *h_full, *h_sparse;
+  const float *lse_full, *lse_sparse;
+  const void* dout;
+  void* dq;           // SIMT: written directly in dtype
+  float *dk_acc, *dv_acc;  // fp32 accumulators [B,Hkv,N,d], zeroed first
+  float w_sparsity, w_commit;
+  int mode;
+};
+void launch_bwd_simt(const Dims& D, const BwdArgs& a, hipStream_t s);
+
+// --- bf16 MFMA kernels ---
+bool fwd_mfma_supported(const Dims& D);
+void launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s);
+
+// --- small kernels (misc.hip) ---
+void launch_zero_f32(float* p, int64_t n, hipStream_t s);
+void launch_convert(const float* src, void* dst, int dtype, int64_t n, hipStream_t s);
+void launch_loss_reduce(const float* row_sq, int64_t n_rows, double inv_count, float* losses,
+                        hipStream_t s);
+
+}  // namespace ssa

@@ -1,0 +1,77 @@
+// Small helper kernels: fills, fp32 -> dtype conversion, and the
+// deterministic reduction of the alignment losses.
+//
+// L_sparsity and L_commit have the same value, the mean of
+// (h_full - h_sparse)^2 over all B*Hq*N*d elements of the layer; they differ
+// only in which output their gradient moves (Sintesi Tecnica, section 2,
+// 'Allineamento Bidirezionale').  The forward kernels leave one partial sum
+// per row (or per tile); this kernel adds them in a fixed order in fp64.
+
+#include "common.h"
+#include "internal.h"
+
+namespace ssa {
+
+__global__ void k_zero_f32(float* __restrict__ p, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0.f;
+}
+
+void launch_zero_f32(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  timing_begin(kKZero, s);
+  hipLaunchKernelGGL(k_zero_f32, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, p, n);
+  timing_end(kKZero, s);
+}
+
+template <typename T>
+__global__ void k_convert(const float* __restrict__ src, T* __restrict__ dst, int64_t n) {
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride)
+    dst[i] = from_f32<T>(src[i]);
+}
+
+void launch_convert(const float* src, void* dst, int dtype, int64_t n, hipStream_t s) {
+  if (n <= 0) return;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  timing_begin(kKConvert, s);
+  if (dtype == 1)
+    hipLaunchKernelGGL(k_convert<bf16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, src,
+                       static_cast<bf16_t*>(dst), n);
+  else
+    hipLaunchKernelGGL(k_convert<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, src,
+                       static_cast<float*>(dst), n);
+  timing_end(kKConvert, s);
+}
+
+// One workgroup: thread t adds partials t, t+1024, ... in fp64, then a fixed
+// tree combines the 1024 sums.
+__global__ void __launch_bounds__(1024) k_loss_reduce(const float* __restrict__ part, int64_t n,
+                                                      double inv_count, float* __restrict__ losses) {
+  __shared__ double buf[1024];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) acc += static_cast<double>(part[i]);
+  buf[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 512; w >= 1; w >>= 1) {
+    if (threadIdx.x < w) buf[threadIdx.x] += buf[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const float L = static_cast<float>(buf[0] * inv_count);
+    losses[0] = L;   // L_sparsity
+    losses[1] = L;   // L_commit
+  }
+}
+
+void launch_loss_reduce(const float* row_sq, int64_t n_rows, double inv_count, float* losses,
+                        hipStream_t s) {
+  timing_begin(kKLossReduce, s);
+  hipLaunchKernelGGL(k_loss_reduce, dim3(1), dim3(1024), 0, s, row_sq, n_rows, inv_count, losses);
+  timing_end(kKLossReduce, s);
+}
+
+}  // namespace ssa

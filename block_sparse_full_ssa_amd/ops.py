@@ -1,0 +1,147 @@
+"""Torch-facing binding of libssa: argument marshalling only.
+
+Each function checks tensor placement, allocates its outputs and workspace
+with torch on the inputs' device, and calls the C entry point of the same
+name on torch's current stream.  Every step of the computation runs in the
+library's HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Dict, Optional, Tuple
+
+import torch
+
+from . import _lib
+from ._lib import DUAL_ACTIVE_FULL, DUAL_ACTIVE_SPARSE, FULL_ONLY, SPARSE_ONLY  # noqa: F401
+
+_DT = {torch.float32: _lib.SSA_F32, torch.bfloat16: _lib.SSA_BF16}
+
+
+def make_shape(q: torch.Tensor, k: torch.Tensor, block: int, top_k: int,
+               scale: Optional[float] = None) -> _lib.ShapeT:
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q and k must be [B, H, N, d]")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape[0] != B or k.shape[2] != N or k.shape[3] != d or Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    if q.dtype not in _DT or k.dtype != q.dtype:
+        raise ValueError("q and k must both be float32 or bfloat16")
+    return _lib.ShapeT(B, Hq, Hq // Hkv, N, d, int(block), int(top_k),
+                       0.0 if scale is None else float(scale), _DT[q.dtype])
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev_check(*ts):
+    dev = None
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("libssa works on GPU tensors")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+        dev = t.device if dev is None else dev
+        if t.device != dev:
+            raise ValueError("all tensors must be on one device")
+    return dev
+
+
+def _stream(dev) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _workspace(shape, mode, op, dev) -> Tuple[Optional[torch.Tensor], int, int]:
+    n = _lib.lib().ssa_workspace_size(ctypes.byref(shape), mode, op)
+    if n == 0:
+        return None, 0, 0
+    buf = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+    off = (-buf.data_ptr()) % 256
+    return buf, buf.data_ptr() + off, n
+
+
+def ssa_select_blocks(q: torch.Tensor, k: torch.Tensor, block: int, top_k: int) -> torch.Tensor:
+    """Selected key blocks [B, Hq, N, top_k] int32, ascending, -1 padded."""
+    dev = _dev_check(q, k)
+    shape = make_shape(q, k, block, top_k)
+    B, Hq, N, _ = q.shape
+    sel = torch.empty(B, Hq, N, top_k, dtype=torch.int32, device=dev)
+    ws, wp, wn = _workspace(shape, 0, _lib.OP_SELECT, dev)
+    st = _lib.lib().ssa_select_blocks(ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(sel),
+                                      ctypes.c_void_p(wp), wn, _stream(dev))
+    _lib.check(st, "ssa_select_blocks")
+    return sel
+
+
+def ssa_attn_fwd(q, k, v, sel, block: int, top_k: int, mode: int = DUAL_ACTIVE_FULL,
+                 scale: Optional[float] = None, want_lse: bool = True) -> Dict[str, torch.Tensor]:
+    """Forward of one SSA layer; returns the outputs the mode defines."""
+    dev = _dev_check(q, k, v, sel)
+    shape = make_shape(q, k, block, top_k, scale)
+    B, Hq, N, d = q.shape
+    dual = mode in (DUAL_ACTIVE_FULL, DUAL_ACTIVE_SPARSE)
+    out: Dict[str, torch.Tensor] = {}
+    f32 = dict(dtype=torch.float32, device=dev)
+    if mode != SPARSE_ONLY:
+        out["h_full"] = torch.empty_like(q)
+        if want_lse:
+            out["lse_full"] = torch.empty(B, Hq, N, **f32)
+    if mode != FULL_ONLY:
+        out["h_sparse"] = torch.empty_like(q)
+        if want_lse:
+            out["lse_sparse"] = torch.empty(B, Hq, N, **f32)
+    if dual:
+        out["delta"] = torch.empty(B, Hq, N, **f32)
+        out["losses"] = torch.empty(2, **f32)
+    ws, wp, wn = _workspace(shape, mode, _lib.OP_FWD, dev)
+    st = _lib.lib().ssa_attn_fwd(
+        ctypes.byref(shape), int(mode), _ptr(q), _ptr(k), _ptr(v), _ptr(sel),
+        _ptr(out.get("h_full")), _ptr(out.get("h_sparse")), _ptr(out.get("lse_full")),
+        _ptr(out.get("lse_sparse")), _ptr(out.get("delta")), _ptr(out.get("losses")),
+        ctypes.c_void_p(wp), wn, _stream(dev))
+    _lib.check(st, "ssa_attn_fwd")
+    if ws is not None:
+        out["_ws"] = ws   # keeps the workspace alive until the caller drops the dict
+    return out
+
+
+def ssa_attn_bwd(q, k, v, sel, fwd: Dict[str, torch.Tensor], d_out: Optional[torch.Tensor],
+                 block: int, top_k: int, mode: int = DUAL_ACTIVE_FULL, w_sparsity: float = 1.0,
+                 w_commit: float = 1.0, scale: Optional[float] = None):
+    """(dq, dk, dv) of one SSA layer from the forward's saved outputs."""
+    dev = _dev_check(q, k, v, sel, d_out)
+    shape = make_shape(q, k, block, top_k, scale)
+    dq = torch.empty_like(q)
+    dk = torch.empty_like(k)
+    dv = torch.empty_like(v)
+    ws, wp, wn = _workspace(shape, mode, _lib.OP_BWD, dev)
+    st = _lib.lib().ssa_attn_bwd(
+        ctypes.byref(shape), int(mode), float(w_sparsity), float(w_commit),
+        _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(fwd.get("h_full")), _ptr(fwd.get("h_sparse")),
+        _ptr(fwd.get("lse_full")), _ptr(fwd.get("lse_sparse")), _ptr(d_out),
+        _ptr(dq), _ptr(dk), _ptr(dv), ctypes.c_void_p(wp), wn, _stream(dev))
+    _lib.check(st, "ssa_attn_bwd")
+    del ws
+    return dq, dk, dv
+
+
+def timing_enable(on: bool = True) -> None:
+    _lib.check(_lib.lib().ssa_timing_enable(1 if on else 0), "ssa_timing_enable")
+
+
+def timing_query(kernel: str) -> Tuple[float, int]:
+    """(total milliseconds, launches) of one library kernel since timing_enable."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _lib.check(_lib.lib().ssa_timing_query(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)),
+               "ssa_timing_query")
+    return ms.value, n.value
+
+
+def kernel_names():
+    L = _lib.lib()
+    return [L.ssa_kernel_name(i).decode() for i in range(L.ssa_kernel_count())]

@@ -1,0 +1,178 @@
+/*
+ * ssa.h -- C interface of libssa: SSA (Sparse Sparse Attention) dual-stream
+ * causal attention for AMD Instinct MI355X (gfx950).
+ *
+ * SSA trains one attention layer in two streams over the same q, k, v
+ * (arXiv 2511.20102, "SSA: Sparse Sparse Attention by Aligning Full and Sparse
+ * Attention Outputs in Feature Space"; Sintesi Tecnica, section 2):
+ *   - the full stream: causal softmax attention over every earlier key;
+ *   - the sparse stream: block-sparse attention, each query restricted to the
+ *     keys of its selected key blocks and renormalised over them;
+ *   - per training step one stream is drawn as the active one; the other
+ *     (counterpart) output serves only the alignment losses and receives no
+ *     upstream gradient;
+ *   - L_sparsity pulls h_full toward a fixed h_sparse, L_commit pulls h_sparse
+ *     toward a fixed h_full; their sum is L_align in the total objective.
+ * The discarded mass delta(t) is the full-attention probability of query t
+ * that falls on keys outside its sparse support (Sintesi Tecnica, section 2,
+ * 'Allineamento Bidirezionale'; the error of sparse attention grows linearly
+ * with it, section 1).
+ *
+ * Block selection (the pages leave it open; fixed here): for query t in block
+ * i_t = t / block, every earlier block j < i_t scores q_t . mean(k over block
+ * j) in fp32; the own block i_t is always kept; the top_k - 1 best-scoring
+ * earlier blocks complete the set, the lower index winning a tie.
+ *
+ * Conventions shared by every entry point
+ *   Layout     q, h_full, h_sparse, d_out, dq: [B, Hq, N, d] contiguous;
+ *              k, v, dk, dv: [B, Hkv, N, d] with Hkv = Hq / group;
+ *              query head h reads KV head h / group.
+ *              lse_full, lse_sparse, delta: [B, Hq, N] fp32.
+ *              sel: [B, Hq, N, top_k] int32, each row ascending block indices
+ *              followed by -1 padding (a row of block i holds min(top_k, i+1)
+ *              entries).
+ *   dtype      SSA_BF16: q/k/v/outputs/gradients bf16 (bf16 MFMA, fp32
+ *              accumulation); SSA_F32: all fp32 (fp32 arithmetic throughout).
+ *   Logits     z = softmax_scale * q . k, causal (key index <= query index);
+ *              softmax_scale <= 0 selects 1/sqrt(d).  lse = log sum exp z over
+ *              the stream's keys (natural log).
+ *   Pointers   All tensor pointers are DEVICE pointers owned by the caller.
+ *              The library allocates no device memory: every scratch buffer
+ *              lives in the caller's workspace ``ws`` of ``ws_bytes`` bytes,
+ *              sized by ssa_workspace_size() and aligned to 256 bytes.
+ *   Streams    ``stream`` is a hipStream_t (NULL = the null stream).  Every
+ *              call only enqueues work on it and returns; results are valid
+ *              once the stream has reached that point.
+ *   Errors     Arguments are validated on the host before anything is
+ *              enqueued; an invalid call returns a status other than SSA_OK
+ *              and enqueues nothing.  SSA_ERR_HIP reports a failed launch
+ *              (details in ssa_last_error()).  No C++ exception crosses this
+ *              interface.  Calls on different streams may run concurrently if
+ *              their workspaces differ.
+ */
+#ifndef SSA_H_
+#define SSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SSA_OK = 0,
+  SSA_ERR_NULL = 1,        /* a required pointer is NULL */
+  SSA_ERR_SHAPE = 2,       /* inconsistent sizes (group, N % block, top_k < 1, ...) */
+  SSA_ERR_UNSUPPORTED = 3, /* valid but not implemented (head_dim, block, dtype) */
+  SSA_ERR_WORKSPACE = 4,   /* ws_bytes below ssa_workspace_size() or ws misaligned */
+  SSA_ERR_HIP = 5          /* the HIP runtime reported an error */
+} ssa_status_t;
+
+typedef enum { SSA_F32 = 0, SSA_BF16 = 1 } ssa_dtype_t;
+
+/* Which outputs exist and where the upstream gradient goes. */
+typedef enum {
+  SSA_DUAL_ACTIVE_FULL = 0,   /* training step, full stream active   */
+  SSA_DUAL_ACTIVE_SPARSE = 1, /* training step, sparse stream active */
+  SSA_FULL_ONLY = 2,          /* full attention alone                */
+  SSA_SPARSE_ONLY = 3         /* block-sparse attention alone        */
+} ssa_mode_t;
+
+typedef enum { SSA_OP_SELECT = 0, SSA_OP_FWD = 1, SSA_OP_BWD = 2 } ssa_op_t;
+
+typedef struct {
+  int32_t batch;          /* B >= 1                                  */
+  int32_t heads_q;        /* Hq >= 1                                 */
+  int32_t group;          /* G = Hq / Hkv >= 1, divides Hq           */
+  int32_t seqlen;         /* N >= block, N % block == 0              */
+  int32_t head_dim;       /* d: 64 or 128                            */
+  int32_t block;          /* key block size: 32, 64 or 128           */
+  int32_t top_k;          /* selected blocks per query incl. own, >= 1;
+                             larger than N/block selects every block */
+  float softmax_scale;    /* <= 0: 1/sqrt(d)                         */
+  int32_t dtype;          /* ssa_dtype_t                             */
+} ssa_shape_t;
+
+/* Bytes of workspace that ``op`` needs for ``shape`` in ``mode`` (0 on an
+ * invalid shape).  A workspace of this size may be reused across calls that
+ * are ordered on one stream. */
+size_t ssa_workspace_size(const ssa_shape_t* shape, int32_t mode, int32_t op);
+
+/*
+ * Block selection (the rule in the header comment).
+ *   q [B,Hq,N,d], k [B,Hkv,N,d] in shape->dtype  -> sel [B,Hq,N,top_k] int32.
+ * Block means are accumulated in fp32 and scores are fp32 dot products, so a
+ * cutoff whose two scores differ by less than fp32 rounding may rank either
+ * way.  Workspace: the fp32 block means.
+ */
+ssa_status_t ssa_select_blocks(const ssa_shape_t* shape, const void* q, const void* k,
+                               int32_t* sel, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Forward of one SSA layer (Sintesi Tecnica, section 2).
+ *   Dual modes: writes h_full, h_sparse (dtype), lse_full, lse_sparse,
+ *     delta (fp32 [B,Hq,N]; delta = 1 - exp(lse_sparse - lse_full)) and
+ *     losses[2] = {L_sparsity, L_commit} (fp32, device), each the mean of
+ *     (h_full - h_sparse)^2 over all B*Hq*N*d elements, accumulated from the
+ *     fp32 outputs before rounding.  The two values are equal; they differ
+ *     only in their gradients.  sel is required.
+ *   SSA_FULL_ONLY: writes h_full, lse_full; sel, h_sparse, lse_sparse, delta
+ *     and losses may be NULL and are not touched.
+ *   SSA_SPARSE_ONLY: writes h_sparse, lse_sparse; h_full, lse_full, delta and
+ *     losses may be NULL.
+ * lse pointers may be NULL when the caller will not run the backward.
+ */
+ssa_status_t ssa_attn_fwd(const ssa_shape_t* shape, int32_t mode, const void* q,
+                          const void* k, const void* v, const int32_t* sel, void* h_full,
+                          void* h_sparse, float* lse_full, float* lse_sparse, float* delta,
+                          float* losses, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Backward of one SSA layer.  With M = B*Hq*N*d the gradients reaching the
+ * two outputs are
+ *   G_full   = [active = full]   d_out + w_sparsity (2/M) (h_full - h_sparse)
+ *   G_sparse = [active = sparse] d_out + w_commit   (2/M) (h_sparse - h_full)
+ * in the dual modes (stop-gradient targets: Sintesi Tecnica section 2, items
+ * 1 and 2 of 'Allineamento Bidirezionale'); single-stream modes take
+ * G = d_out for their one stream and ignore the weights.  Then for each
+ * stream with probabilities p (recomputed from q, k and the stored lse):
+ *   dq_t = scale sum_i p_ti (G_t.v_i - G_t.h_t) k_i,  dk_i = scale sum_t (same) q_t,
+ *   dv_i = sum_t p_ti G_t, summed over both streams and, for dk/dv, over the
+ *   query heads of a group.  No gradient flows through the selection.
+ * Inputs are the forward's q, k, v, sel and outputs (h_* and lse_* of the
+ * streams the mode has; the others may be NULL).  d_out may be NULL for a
+ * zero upstream gradient.  Writes dq [B,Hq,N,d], dk, dv [B,Hkv,N,d] (dtype),
+ * overwriting them.
+ */
+ssa_status_t ssa_attn_bwd(const ssa_shape_t* shape, int32_t mode, float w_sparsity,
+                          float w_commit, const void* q, const void* k, const void* v,
+                          const int32_t* sel, const void* h_full, const void* h_sparse,
+                          const float* lse_full, const float* lse_sparse, const void* d_out,
+                          void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                          void* stream);
+
+/* Static text for a status code. */
+const char* ssa_status_string(int32_t status);
+
+/* Details of the last error returned on this thread ("" if none). */
+const char* ssa_last_error(void);
+
+/*
+ * Kernel timing for measurement harnesses.  While enabled, the library
+ * records a HIP event pair on the launch stream around every launch of its
+ * kernels.  ssa_timing_query() waits for the recorded events and returns the
+ * summed duration (ms) and launch count of one kernel, by name as returned
+ * by ssa_kernel_name(i) for i = 0 .. ssa_kernel_count()-1.  Enabling clears
+ * earlier records.  Host-side state, not thread-safe; off by default.
+ */
+ssa_status_t ssa_timing_enable(int32_t enabled);
+ssa_status_t ssa_timing_query(const char* kernel, double* total_ms, int64_t* launches);
+int32_t ssa_kernel_count(void);
+const char* ssa_kernel_name(int32_t i);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSA_H_ */

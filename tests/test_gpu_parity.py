@@ -1,0 +1,272 @@
+"""GPU parity of the HIP path against the CPU oracle (through the C interface).
+
+Selection must match bit for bit on screened inputs (no two scores within
+1e-3 at any cutoff tested); floating-point outputs within the tolerances in
+gpu_cases.  Cases span several tiles, ragged tails, the block sizes 32 / 64 /
+128, GQA groups 1..4, top_k = 1 and top_k >= number of blocks.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssa_inputs as si
+
+from gpu_cases import (TOL, assert_close, assert_normwise, inputs, oracle_fwd, oracle_select,
+                       scale_of, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+W = si.WORKLOADS
+TINY = W["tiny_mha_n256_fp32"]
+# bf16 layers small enough for the oracle, each spanning several 128-query tiles
+SMALL = {
+    "gqa_n512_b64_k4": si.scaled_down(W["gqa_n4k_fwd"], seqlen=512, hq=4, hkv=2, top_k=4),
+    "gqa_n320_ragged": si.scaled_down(W["gqa_n4k_fwd"], seqlen=320, hq=4, hkv=1, top_k=3),
+    "mha_n384_b32_k5": si.scaled_down(W["gqa_n4k_fwd"], seqlen=384, hq=2, hkv=2, block=32, top_k=5),
+    "gqa_n512_b128_k2": si.scaled_down(W["gqa_n4k_fwd"], seqlen=512, hq=4, hkv=1, block=128, top_k=2),
+    "sinks_n1024_k8": si.scaled_down(W["long_n64k_sinks"], seqlen=1024, hq=4, hkv=1, top_k=8),
+    "gqa_n256_d64": si.scaled_down(W["gqa_n4k_fwd"], seqlen=256, hq=2, hkv=1, head_dim=64, top_k=2),
+}
+MODES = [oracle.DUAL_ACTIVE_FULL, oracle.DUAL_ACTIVE_SPARSE, oracle.FULL_ONLY, oracle.SPARSE_ONLY]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_full_ssa_amd  # noqa: F401  (fails loudly when libssa is missing)
+
+
+def ssa():
+    import block_sparse_full_ssa_amd as m
+    return m
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _check_fwd(name, wl, out, ref, mode):
+    dt = wl.dtype
+    if mode != oracle.SPARSE_ONLY:
+        assert_close(f"{name} h_full", out["h_full"], ref["h_full"], dt)
+        assert_close(f"{name} lse_full", out["lse_full"], ref["lse_full"], dt)
+    if mode != oracle.FULL_ONLY:
+        assert_close(f"{name} h_sparse", out["h_sparse"], ref["h_sparse"], dt)
+        assert_close(f"{name} lse_sparse", out["lse_sparse"], ref["lse_sparse"], dt)
+    if mode in (oracle.DUAL_ACTIVE_FULL, oracle.DUAL_ACTIVE_SPARSE):
+        assert_close(f"{name} delta", out["delta"], ref["delta"], dt)
+        L = out["losses"].cpu().numpy()
+        rtol = TOL[dt][1]
+        assert L[0] == L[1]
+        assert abs(L[0] - ref["L_sparsity"]) <= rtol * ref["L_sparsity"] + 1e-30, (L, ref["L_sparsity"])
+
+
+# ------------------------------------------------------------------ select --
+
+@pytest.mark.parametrize("name", ["tiny"] + list(SMALL))
+def test_select_matches_oracle(name):
+    wl = TINY if name == "tiny" else SMALL[name]
+    _say(f"select {name}")
+    (q, k, v), _ = inputs(wl, 0, (wl.top_k,))
+    qd, kd = to_dev(q, k)
+    sel = ssa().ssa_select_blocks(qd, kd, wl.block, wl.top_k)
+    want, _ = oracle_select(wl, 0, (wl.top_k,), wl.top_k)
+    assert np.array_equal(sel.cpu().numpy(), want)
+
+
+def test_select_topk_sweep_gqa_n2048():
+    """top_k 4, 8, 16, 32 of the 16K training layer's sweep, on a 2048-token slice."""
+    wl = si.scaled_down(W["train_b2_h32_n16k"], batch=1, seqlen=2048, hq=4, hkv=1)
+    ks = (4, 8, 16, 32)
+    (q, k, v), _ = inputs(wl, 0, ks)
+    qd, kd = to_dev(q, k)
+    for K in ks:
+        _say(f"select sweep K={K}")
+        sel = ssa().ssa_select_blocks(qd, kd, wl.block, K)
+        want, _ = oracle_select(wl, 0, ks, K)
+        assert np.array_equal(sel.cpu().numpy(), want), K
+
+
+def test_select_all_blocks_and_top1():
+    wl = SMALL["gqa_n512_b64_k4"]
+    (q, k, v), _ = inputs(wl, 0, (wl.top_k,))
+    qd, kd = to_dev(q, k)
+    for K in (1, 8, 11, 100):            # nb = 8: 8, 11 and 100 select everything
+        sel = ssa().ssa_select_blocks(qd, kd, wl.block, K).cpu().numpy()
+        want, _ = oracle_select(wl, 0, (wl.top_k,), K)
+        assert np.array_equal(sel, want), K
+
+
+# ----------------------------------------------------------------- forward --
+
+@pytest.mark.parametrize("mode", MODES)
+def test_fwd_tiny_fp32(mode):
+    wl = TINY
+    _say(f"fwd tiny mode {mode}")
+    (q, k, v), _ = inputs(wl, 0, (wl.top_k,))
+    qd, kd, vd = to_dev(q, k, v)
+    sel = torch.from_numpy(oracle_select(wl, 0, (wl.top_k,), wl.top_k)[0]).to("cuda:0")
+    out = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, wl.top_k, mode)
+    torch.cuda.synchronize()
+    _check_fwd("tiny", wl, out, oracle_fwd(wl, 0, (wl.top_k,), wl.top_k, mode), mode)
+
+
+@pytest.mark.parametrize("mode", [oracle.DUAL_ACTIVE_FULL, oracle.FULL_ONLY, oracle.SPARSE_ONLY])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fwd_small_bf16(name, mode):
+    wl = SMALL[name]
+    _say(f"fwd {name} mode {mode}")
+    (q, k, v), _ = inputs(wl, 0, (wl.top_k,))
+    qd, kd, vd = to_dev(q, k, v)
+    sel = torch.from_numpy(oracle_select(wl, 0, (wl.top_k,), wl.top_k)[0]).to("cuda:0")
+    out = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, wl.top_k, mode)
+    torch.cuda.synchronize()
+    _check_fwd(name, wl, out, oracle_fwd(wl, 0, (wl.top_k,), wl.top_k, mode), mode)
+
+
+@pytest.mark.parametrize("mode", [oracle.DUAL_ACTIVE_SPARSE, oracle.FULL_ONLY, oracle.SPARSE_ONLY])
+def test_fwd_gqa_n4k_full_layer(mode):
+    """The 4K GQA layer (16 query / 4 KV heads, d 128, block 64, top_k 16) whole.
+
+    Its late query tiles contain waves for which no row selects some key
+    tile, which exercises the skip of the sparse update (a wave-uniform
+    branch around matrix instructions).
+    """
+    wl = W["gqa_n4k_fwd"]
+    _say(f"fwd gqa_n4k_fwd full layer mode {mode}")
+    (q, k, v), _ = inputs(wl, 0, (wl.top_k,))
+    qd, kd, vd = to_dev(q, k, v)
+    sel = ssa().ssa_select_blocks(qd, kd, wl.block, wl.top_k)
+    want_sel, _ = oracle_select(wl, 0, (wl.top_k,), wl.top_k)
+    assert np.array_equal(sel.cpu().numpy(), want_sel)
+    out = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, wl.top_k, mode)
+    torch.cuda.synchronize()
+    ref_mode = oracle.DUAL_ACTIVE_FULL if mode == oracle.DUAL_ACTIVE_SPARSE else mode
+    _check_fwd("gqa_n4k", wl, out, oracle_fwd(wl, 0, (wl.top_k,), wl.top_k, ref_mode), ref_mode)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gqa_n512_b64_k4", "mha_n384_b32_k5"])
+def test_all_blocks_selected_streams_identical(name):
+    """top_k >= number of blocks: h_sparse == h_full bit for bit and delta == 0."""
+    wl = TINY if name == "tiny" else SMALL[name]
+    (q, k, v), _ = inputs(wl, 0, (wl.top_k,))
+    qd, kd, vd = to_dev(q, k, v)
+    K = wl.nblocks + 1
+    sel = ssa().ssa_select_blocks(qd, kd, wl.block, K)
+    out = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, K, oracle.DUAL_ACTIVE_FULL)
+    torch.cuda.synchronize()
+    assert torch.equal(out["h_full"], out["h_sparse"])
+    assert torch.equal(out["lse_full"], out["lse_sparse"])
+    assert float(out["delta"].abs().max()) == 0.0
+    assert float(out["losses"][0]) == 0.0
+
+
+@pytest.mark.parametrize("name", ["tiny", "sinks_n1024_k8"])
+def test_delta_bound_on_gpu_outputs(name):
+    """||h_full - h_sparse|| <= 2 delta max||v|| per query (up to output rounding)."""
+    wl = TINY if name == "tiny" else SMALL[name]
+    (q, k, v), _ = inputs(wl, 0, (wl.top_k,))
+    qd, kd, vd = to_dev(q, k, v)
+    sel = ssa().ssa_select_blocks(qd, kd, wl.block, wl.top_k)
+    out = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, wl.top_k, oracle.DUAL_ACTIVE_FULL)
+    torch.cuda.synchronize()
+    diff = (out["h_full"].double() - out["h_sparse"].double()).norm(dim=-1).cpu()
+    vmax = v.double().norm(dim=-1).max()
+    slack = 1e-5 if wl.dtype == torch.float32 else 2 ** -7 * float(out["h_full"].double().norm(dim=-1).max())
+    assert bool((diff <= 2 * out["delta"].double().cpu() * vmax + slack).all())
+
+
+def test_fwd_deterministic():
+    wl = SMALL["gqa_n512_b64_k4"]
+    (q, k, v), _ = inputs(wl, 0, (wl.top_k,))
+    qd, kd, vd = to_dev(q, k, v)
+    sel = ssa().ssa_select_blocks(qd, kd, wl.block, wl.top_k)
+    a = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, wl.top_k, oracle.DUAL_ACTIVE_FULL)
+    b = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, wl.top_k, oracle.DUAL_ACTIVE_FULL)
+    for key in ("h_full", "h_sparse", "lse_full", "lse_sparse", "delta", "losses"):
+        assert torch.equal(a[key], b[key]), key
+
+
+# ---------------------------------------------------------------- backward --
+
+def _bwd_case(wl, mode, with_dout=True, ws=0.7, wc=1.3):
+    (q, k, v), (qf, kf, vf) = inputs(wl, 0, (wl.top_k,))
+    g = si.draw_dout(wl, 0)
+    qd, kd, vd, gd = to_dev(q, k, v, g)
+    osel = oracle_select(wl, 0, (wl.top_k,), wl.top_k)[0]
+    sel = torch.from_numpy(osel).to("cuda:0")
+    fwd = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, wl.top_k, mode)
+    dq, dk, dv = ssa().ssa_attn_bwd(qd, kd, vd, sel, fwd, gd if with_dout else None, wl.block,
+                                    wl.top_k, mode, ws, wc)
+    torch.cuda.synchronize()
+    ref_f = oracle_fwd(wl, 0, (wl.top_k,), wl.top_k, mode)
+    rq, rk, rv = oracle.backward(qf, kf, vf, None if mode == oracle.FULL_ONLY else osel, wl.block,
+                                 scale_of(wl), wl.group, mode, si.to_f64(g) if with_dout else None,
+                                 ws, wc, fwd=ref_f)
+    return (dq, dk, dv), (rq, rk, rv)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_bwd_tiny_fp32(mode):
+    _say(f"bwd tiny mode {mode}")
+    got, want = _bwd_case(TINY, mode)
+    for n, a, b in zip(("dq", "dk", "dv"), got, want):
+        assert_close(f"tiny {n}", a, b, torch.float32)
+
+
+@pytest.mark.parametrize("mode", [oracle.DUAL_ACTIVE_FULL, oracle.DUAL_ACTIVE_SPARSE])
+def test_bwd_tiny_alignment_only(mode):
+    """No upstream gradient: only L_sparsity / L_commit move q, k, v."""
+    _say(f"bwd tiny alignment-only mode {mode}")
+    got, want = _bwd_case(TINY, mode, with_dout=False, ws=1.0, wc=1.0)
+    for n, a, b in zip(("dq", "dk", "dv"), got, want):
+        assert_normwise(f"tiny align {n}", a, b, 1e-4)
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("name", ["gqa_n512_b64_k4", "gqa_n320_ragged", "mha_n384_b32_k5",
+                                  "gqa_n512_b128_k2", "gqa_n256_d64"])
+def test_bwd_small_bf16(name, mode):
+    _say(f"bwd {name} mode {mode}")
+    got, want = _bwd_case(SMALL[name], mode)
+    for n, a, b in zip(("dq", "dk", "dv"), got, want):
+        assert_close(f"{name} {n}", a, b, torch.bfloat16)
+
+
+@pytest.mark.parametrize("mode", [oracle.DUAL_ACTIVE_FULL, oracle.DUAL_ACTIVE_SPARSE])
+def test_bwd_bf16_alignment_only(mode):
+    _say(f"bwd bf16 alignment-only mode {mode}")
+    got, want = _bwd_case(SMALL["gqa_n512_b64_k4"], mode, with_dout=False, ws=1.0, wc=1.0)
+    for n, a, b in zip(("dq", "dk", "dv"), got, want):
+        assert_normwise(f"bf16 align {n}", a, b, 1e-2)
+
+
+def test_sparse_only_gradient_deficiency():
+    """SPARSE_ONLY: a key outside every query's support gets dk = dv = 0 exactly.
+
+    With the upstream gradient on a single query row, keys of blocks that row
+    did not select receive nothing from the sparse stream.
+    """
+    wl = SMALL["gqa_n512_b64_k4"]
+    (q, k, v), _ = inputs(wl, 0, (wl.top_k,))
+    qd, kd, vd = to_dev(q, k, v)
+    sel = ssa().ssa_select_blocks(qd, kd, wl.block, wl.top_k)
+    g = torch.zeros_like(qd)
+    t = 500
+    g[0, 0, t] = 1.0
+    fwd = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, wl.top_k, oracle.SPARSE_ONLY)
+    dq, dk, dv = ssa().ssa_attn_bwd(qd, kd, vd, sel, fwd, g, wl.block, wl.top_k, oracle.SPARSE_ONLY)
+    torch.cuda.synchronize()
+    chosen = set(int(x) for x in sel[0, 0, t].cpu() if x >= 0)
+    outside = [i for i in range(t + 1) if i // wl.block not in chosen]
+    assert len(outside) > 0
+    assert float(dk[0, 0, outside].abs().max()) == 0.0
+    assert float(dv[0, 0, outside].abs().max()) == 0.0
+    inside = [i for i in range(t + 1) if i // wl.block in chosen]
+    assert float(dv[0, 0, inside].abs().max()) > 0.0

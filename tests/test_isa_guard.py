@@ -1,0 +1,29 @@
+"""Compiled-code guard (CPU, needs hipcc): no MFMA issued under a narrowed EXEC."""
+import pytest
+
+from block_sparse_full_ssa_amd import isa_check
+
+
+def test_scanner_flags_masked_mfma():
+    asm = "\n".join([
+        "s_and_saveexec_b64 s[4:5], s[34:35]",
+        "v_mfma_f32_32x32x16_bf16 a[48:63], v[20:23], v[128:131], a[48:63]",
+        "s_or_b64 exec, exec, s[4:5]",
+        "s_and_saveexec_b64 s[4:5], s[34:35]",
+        "s_cbranch_execz .LBB2_77",
+        "v_mfma_f32_32x32x16_bf16 a[112:127], v[20:23], v[128:131], a[112:127]",
+    ])
+    hits = isa_check.masked_mfmas(asm)
+    assert [ln for ln, _ in hits] == [1]
+
+
+@pytest.mark.parametrize("src", isa_check.MFMA_SOURCES)
+def test_no_masked_mfma_in_kernels(src):
+    import os
+    from block_sparse_full_ssa_amd import build
+    if not os.path.exists(os.path.join(build.CSRC, src)):
+        pytest.skip(f"{src} not present")
+    asm = isa_check.device_asm(src)
+    if "v_mfma" not in asm:
+        pytest.skip(f"{src} has no MFMA")
+    assert isa_check.masked_mfmas(asm) == []
