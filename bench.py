@@ -1,0 +1,217 @@
+"""Throughput of one SSA training step of attention on one MI355X.
+
+A step is the whole hot path over one batch of the 16K-context training
+layer (B=2, 32 query / 8 KV heads, N=16384, d=128, bf16, block 64, top_k 16
+by default): block selection, the dual-stream forward (full and sparse
+outputs, delta, alignment losses) and the backward with the active stream
+drawn 50/50 per step from the seed.  Inputs are synthetic and resident in
+HBM before timing starts.
+
+Reported (one JSON line): algorithmic TFLOP/s of the step, tokens/s, the
+roofline of the dominant kernel (its algorithmic flops per launch over its
+HIP-event-timed average launch), and the CPU oracle timed on a bounded
+sample of the same workload.
+
+Algorithmic work (FlashAttention convention, recompute included): per causal
+(query, key) pair 4d flops forward and 10d backward, counted for the full
+stream (P_full = N(N+1)/2 pairs per head) and for the sparse stream
+(P_sparse = sum over queries of the selected causal keys), i.e.
+14 d (P_full + P_sparse) B Hq per step.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 matrix peak
+HBM_PEAK_GBS = 8000.0
+
+
+def pairs(N: int, block: int, K: int):
+    """(P_full, P_sparse) causal pairs per head for the stated selection."""
+    nb = N // block
+    p_full = N * (N + 1) // 2
+    # query block i keeps min(K-1, i) earlier full blocks plus its own causal part
+    p_sparse = block * block * sum(min(i, K - 1) for i in range(nb)) + nb * block * (block + 1) // 2
+    return p_full, p_sparse
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="train_b2_h32_n16k")
+    ap.add_argument("--top-k", type=int, default=None)
+    ap.add_argument("--seqlen", type=int, default=None, help="override N (experiments only)")
+    ap.add_argument("--batch", type=int, default=None, help="override B (experiments only)")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--sweep", action="store_true", help="also time every top_k of the workload's sweep")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows in the CPU-oracle sample")
+    return ap.parse_args()
+
+
+def run_steps(ssa, q, k, v, dout, wl, K, modes, steps, warmup):
+    import torch
+
+    def step(mode):
+        sel = ssa.ssa_select_blocks(q, k, wl.block, K)
+        fwd = ssa.ssa_attn_fwd(q, k, v, sel, wl.block, K, mode)
+        grads = ssa.ssa_attn_bwd(q, k, v, sel, fwd, dout, wl.block, K, mode)
+        return fwd, grads
+
+    for i in range(warmup):
+        step(modes[i])
+    torch.cuda.synchronize()
+    ssa.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        out = step(modes[warmup + i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kernels = {}
+    for name in ssa.kernel_names():
+        ms, n = ssa.timing_query(name)
+        if n:
+            kernels[name] = {"total_ms": ms, "launches": n, "avg_ms": ms / n}
+    ssa.timing_enable(False)
+    del out
+    return (t1 - t0) * 1000.0 / steps, kernels
+
+
+def cpu_baseline(wl, K, seed, rows):
+    """The fp64 oracle on the host: select + forward + backward of the last
+    ``rows`` query rows of batch 0 / query head 0 (each with all its causal
+    keys), as algorithmic TFLOP/s of that sample."""
+    import numpy as np
+    import threadpoolctl
+
+    import oracle
+    import ssa_inputs as si
+
+    q, k, v, _ = si.draw_qkv(wl, seed)
+    dout = si.draw_dout(wl, seed)
+    N, d, G = wl.seqlen, wl.head_dim, wl.group
+    t_idx = np.arange(N - rows, N)
+    # only the KV head of query head 0 and the sampled rows are converted
+    qf = si.to_f64(q[:1, :1])
+    kf, vf = si.to_f64(k[:1, :1]), si.to_f64(v[:1, :1])
+    gf = si.to_f64(dout[:1, :1])
+    scale = 1.0 / np.sqrt(d)
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    mu = oracle.block_means(kf, wl.block)
+    sel_rows, _ = oracle.select_rows(qf[0, 0, t_idx], t_idx, mu[0, 0], wl.block, K)
+    sel = np.full((1, 1, N, K), -1, np.int32)
+    sel[0, 0, t_idx] = sel_rows
+    oracle.attend_rows(qf[0, 0, t_idx], t_idx, kf[0, 0], vf[0, 0], sel_rows, wl.block, scale)
+    oracle.dq_rows(qf, kf, vf, sel, wl.block, scale, 1, oracle.DUAL_ACTIVE_FULL, gf, 0, 0, t_idx)
+    dt = time.perf_counter() - t0
+    n_sparse = sum(min(K, t // wl.block + 1) * wl.block - (wl.block - 1 - t % wl.block) for t in t_idx)
+    n_full = int((t_idx + 1).sum())
+    flops = 14.0 * d * (n_full + n_sparse)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"batch 0, query head 0, last {rows} query rows with all their causal keys: "
+                      f"selection + dual forward + backward (dq and these rows' dk/dv terms), fp64 numpy; "
+                      f"{flops:.3g} algorithmic flops"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the attention path has no multi-GPU sharding)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_full_ssa_amd as ssa
+    import ssa_inputs as si
+
+    wl = si.WORKLOADS[args.workload]
+    changes = {}
+    if args.seqlen:
+        changes["seqlen"] = args.seqlen
+    if args.batch:
+        changes["batch"] = args.batch
+    if changes:
+        wl = si.scaled_down(wl, **changes)
+    K = args.top_k or wl.top_k
+    dev = torch.device("cuda:0")
+    q, k, v, _ = si.draw_qkv(wl, args.seed)
+    dout = si.draw_dout(wl, args.seed)
+    q, k, v, dout = (x.to(dev) for x in (q, k, v, dout))
+    modes = si.draw_modes(args.seed, args.warmup + args.steps)
+    modes = [ssa.DUAL_ACTIVE_FULL if m == 0 else ssa.DUAL_ACTIVE_SPARSE for m in modes]
+    torch.cuda.synchronize()
+
+    B, Hq, N, d = wl.batch, wl.hq, wl.seqlen, wl.head_dim
+    ms, kernels = run_steps(ssa, q, k, v, dout, wl, K, modes, args.steps, args.warmup)
+    pf, ps = pairs(N, wl.block, K)
+    flops = 14.0 * d * (pf + ps) * B * Hq
+    tflops = flops / (ms / 1000.0) / 1e12
+
+    # dominant kernel and its roofline
+    dom = max(kernels, key=lambda n: kernels[n]["total_ms"])
+    per_launch = {"fwd_mfma": 4.0 * d * (pf + ps) * B * Hq, "fwd_simt": 4.0 * d * (pf + ps) * B * Hq,
+                  "bwd_mfma": 10.0 * d * (pf + ps) * B * Hq, "bwd_simt": 10.0 * d * (pf + ps) * B * Hq}
+    roofline = None
+    if dom in per_launch:
+        achieved = per_launch[dom] / (kernels[dom]["avg_ms"] / 1000.0) / 1e12
+        roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
+                    "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+
+    sweep = None
+    if args.sweep and wl.top_k_sweep:
+        sweep = {}
+        for kk in wl.top_k_sweep:
+            m2, _ = run_steps(ssa, q, k, v, dout, wl, kk, modes, max(3, args.steps // 2), 1)
+            a, b = pairs(N, wl.block, kk)
+            sweep[str(kk)] = {"ms_per_step": round(m2, 3),
+                              "TFLOP/s": round(14.0 * d * (a + b) * B * Hq / (m2 / 1000) / 1e12, 2)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, K, args.seed, min(args.cpu_rows, N))
+
+    line = {
+        "metric": "SSA fwd+bwd attention TFLOP/s and tokens/s at 16K ctx; % of bf16 MFMA peak",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "heads_q": Hq, "heads_kv": wl.hkv, "seq_len": N,
+                   "head_dim": d, "block": wl.block, "top_k": K,
+                   "step": "select + dual fwd + bwd, active stream 50/50 per step"},
+        "tokens_per_s": round(B * N / (ms / 1000.0), 1),
+        "frac_of_bf16_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+        "algorithmic_flops_per_step": flops,
+        "kernels_ms_avg": {n: round(kk["avg_ms"], 4) for n, kk in kernels.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if sweep:
+        line["top_k_sweep"] = sweep
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -92,8 +92,6 @@ static bool valid_mode(int32_t m) { return m >= kDualFull && m <= kSparseOnly; }
 
 static size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-static size_t esize(const Dims& D) { return D.dtype == 1 ? 2 : 4; }
-
 // Workspace carving: a bump allocator over the caller's buffer.
 struct Carver {
   char* base;
@@ -116,13 +114,31 @@ static FwdWs carve_fwd(const Dims& D, int mode, Carver& c) {
 }
 
 struct BwdWs {
+  // generic path
   float *dk_acc, *dv_acc;
+  // MFMA path
+  uint16_t *g_full, *g_sparse;
+  float *D_full, *D_sparse, *lse2_full, *lse2_sparse, *dq_acc;
 };
 static BwdWs carve_bwd(const Dims& D, int mode, Carver& c) {
-  (void)mode;
   BwdWs w{};
-  w.dk_acc = c.take<float>(D.kv_elems() * sizeof(float));
-  w.dv_acc = c.take<float>(D.kv_elems() * sizeof(float));
+  if (bwd_mfma_supported(D)) {
+    const bool f = mode != kSparseOnly, sp = mode != kFullOnly;
+    if (f) {
+      w.g_full = c.take<uint16_t>(D.q_elems() * sizeof(uint16_t));
+      w.D_full = c.take<float>(D.rows() * sizeof(float));
+      w.lse2_full = c.take<float>(D.rows() * sizeof(float));
+    }
+    if (sp) {
+      w.g_sparse = c.take<uint16_t>(D.q_elems() * sizeof(uint16_t));
+      w.D_sparse = c.take<float>(D.rows() * sizeof(float));
+      w.lse2_sparse = c.take<float>(D.rows() * sizeof(float));
+    }
+    w.dq_acc = c.take<float>(D.q_elems() * sizeof(float));
+  } else {
+    w.dk_acc = c.take<float>(D.kv_elems() * sizeof(float));
+    w.dv_acc = c.take<float>(D.kv_elems() * sizeof(float));
+  }
   return w;
 }
 
@@ -225,6 +241,18 @@ ssa_status_t ssa_attn_bwd(const ssa_shape_t* shape, int32_t mode, float w_sparsi
   hipStream_t s = static_cast<hipStream_t>(stream);
   Carver c{static_cast<char*>(ws)};
   BwdWs w = carve_bwd(D, mode, c);
+  if (bwd_mfma_supported(D)) {
+    BwdPreArgs p{d_out, h_full, h_sparse, lse_full, lse_sparse, w.g_full, w.g_sparse, w.D_full, w.D_sparse,
+                 w.lse2_full, w.lse2_sparse, w.dq_acc, mode};
+    launch_bwd_pre(D, p, w_sparsity, w_commit, s);
+    if ((st = launch_status()) != SSA_OK) return st;
+    BwdMainArgs m{q, k, v, sel, w.g_full, w.g_sparse, w.lse2_full, w.lse2_sparse, w.D_full, w.D_sparse,
+                  w.dq_acc, dk, dv, mode};
+    launch_bwd_mfma(D, m, s);
+    if ((st = launch_status()) != SSA_OK) return st;
+    launch_convert(w.dq_acc, dq, D.dtype, D.q_elems(), s);
+    return launch_status();
+  }
   launch_zero_f32(w.dk_acc, D.kv_elems(), s);
   launch_zero_f32(w.dv_acc, D.kv_elems(), s);
   if ((st = launch_status()) != SSA_OK) return st;

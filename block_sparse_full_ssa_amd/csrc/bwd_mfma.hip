@@ -1,2 +1,397 @@
-// placeholder until the MFMA backward lands
+// Backward of SSA dual-stream attention, bf16 MFMA on gfx950.
+//
+// Each output receives its own gradient (Sintesi Tecnica, section 2,
+// 'Allineamento Bidirezionale'): the upstream gradient goes to the active
+// stream only, L_sparsity adds (2/M) w_s (h_full - h_sparse) to the full
+// stream and L_commit adds (2/M) w_c (h_sparse - h_full) to the sparse
+// stream (the other output held fixed in each).  With those stream
+// gradients G_f, G_s, both streams are differentiated in one pass that
+// recomputes the shared logits once:
+//   P_X = 2^(S c - lse_X)                          (c = scale * log2 e)
+//   dS  = P_f (G_f V^T - D_f) + P_s (G_s V^T - D_s),  D_X = rowsum(G_X o h_X)
+//   dV  = P_f^T G_f + P_s^T G_s,  dK = scale dS^T Q,  dQ = scale dS K.
+// Keys outside a query's selected blocks have P_s = 0, so they receive
+// gradient through the full stream only.
+//
+// Kernels:
+//   bwd_pre:  per row, G_f / G_s in bf16, D_f / D_s from the rounded G, the
+//             lse values in log2 units, and a zeroed fp32 dQ accumulator row;
+//   bwd_mfma: key-stationary.  A workgroup owns 128 keys of one KV head (32
+//             per wave, kept in registers as K and V operands) and walks the
+//             G query heads of the group and every 32-query tile at or after
+//             its keys.  dK and dV accumulate in registers over all of them
+//             (no atomics); dQ of each tile is reduced over the 128 keys
+//             through LDS and added to the fp32 accumulator with atomics;
+//   convert:  dQ accumulator -> bf16.
+//
+// Layout: the logits are kept as S = Q K^T (lane l owns key l % 32 and 16
+// queries), which is the B-operand layout of dV^T = G^T P and dK^T = Q^T dS;
+// the transposed A operands G^T, Q^T and dS come from row-major LDS tiles
+// through transpose reads.  All MFMA guards are wave-uniform.
+
+#include "common.h"
 #include "internal.h"
+#include "mfma.h"
+
+namespace ssa {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kBN = 128;       // keys per workgroup
+constexpr int kBM = 32;        // queries per iteration
+constexpr int kQPitch = 136;   // Q / G tile pitch (elements)
+constexpr int kSPitch = 40;    // dS^T tile pitch (elements), [key][query]
+constexpr float kLog2e = 1.4426950408889634f;
+
+enum { kModeDual = 0, kModeFull = 1, kModeSparse = 2 };
+
+// ---------------------------------------------------------------- bwd_pre --
+__global__ void __launch_bounds__(256)
+    k_bwd_pre(BwdPreArgs a, int64_t rows, float w_f, float w_s_align, float inv_m) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int64_t off = row * kD + lane * 2;
+  const bool has_f = a.mode != kSparseOnly, has_s = a.mode != kFullOnly;
+  const bool dual = a.mode == kDualFull || a.mode == kDualSparse;
+  const bool up_f = a.mode == kDualFull || a.mode == kFullOnly;
+  const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
+  const uint16_t* hf = static_cast<const uint16_t*>(a.h_full);
+  const uint16_t* hs = static_cast<const uint16_t*>(a.h_sparse);
+  float Df = 0.f, Ds = 0.f;
+  uint32_t gfw = 0, gsw = 0;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const float g = dout ? to_f32(bf16_t{dout[off + e]}) : 0.f;
+    const float vf = has_f ? to_f32(bf16_t{hf[off + e]}) : 0.f;
+    const float vs = has_s ? to_f32(bf16_t{hs[off + e]}) : 0.f;
+    float gf = 0.f, gs = 0.f;
+    if (dual) {
+      const float diff = vf - vs;
+      gf = w_f * 2.f * inv_m * diff + (up_f ? g : 0.f);
+      gs = -w_s_align * 2.f * inv_m * diff + (up_f ? 0.f : g);
+    } else {
+      gf = up_f ? g : 0.f;
+      gs = up_f ? 0.f : g;
+    }
+    const bf16_t bf = to_bf16(gf), bs = to_bf16(gs);
+    Df += to_f32(bf) * vf;
+    Ds += to_f32(bs) * vs;
+    gfw |= static_cast<uint32_t>(bf.bits) << (16 * e);
+    gsw |= static_cast<uint32_t>(bs.bits) << (16 * e);
+  }
+  if (has_f) *reinterpret_cast<uint32_t*>(a.g_full + off) = gfw;
+  if (has_s) *reinterpret_cast<uint32_t*>(a.g_sparse + off) = gsw;
+  *reinterpret_cast<float2*>(a.dq_acc + off) = make_float2(0.f, 0.f);
+  Df = wave_sum(Df);
+  Ds = wave_sum(Ds);
+  if (lane == 0) {
+    if (has_f) {
+      a.D_full[row] = Df;
+      a.lse2_full[row] = a.lse_full[row] * kLog2e;
+    }
+    if (has_s) {
+      a.D_sparse[row] = Ds;
+      a.lse2_sparse[row] = a.lse_sparse[row] * kLog2e;
+    }
+  }
+}
+
+// --------------------------------------------------------------- bwd_mfma --
+template <int MODE>
+__global__ void __launch_bounds__(256, 1)
+    k_bwd_mfma(BwdMainArgs a, int Hq, int G, int N, int block, int K, float scale, float scale_log2) {
+  constexpr bool kFull = MODE != kModeSparse;
+  constexpr bool kSparse = MODE != kModeFull;
+  // LDS: staging of the key tile at start, then per-iteration tiles
+  // K staging (128 x 128) at start; afterwards Q, G_f, G_s tiles and dS^T
+  constexpr int kSm = (kBN * kD > 3 * kBM * kQPitch + kBN * kSPitch) ? kBN * kD : 3 * kBM * kQPitch + kBN * kSPitch;
+  __shared__ __attribute__((aligned(16))) uint16_t sm[kSm];
+  uint16_t* Qs = sm;                                // [32][136]
+  uint16_t* Gfs = sm + kBM * kQPitch;               // [32][136]
+  uint16_t* Gss = sm + 2 * kBM * kQPitch;           // [32][136]
+  uint16_t* dSt = sm + 3 * kBM * kQPitch;           // [128][40]
+  __shared__ float rowv[4][kBM];                    // lse2_f, lse2_s, D_f, D_s
+  __shared__ uint32_t selmask[4];                   // per 32-key group: rows that selected its block
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, col = lane & 31;
+  const int grp = lane >> 4, li = lane & 15;
+  const int gk = grp >> 1, sub16 = (grp & 1) * 16, srow = li >> 2, m4 = li & 3;
+
+  const int bc = blockIdx.x;                        // batch * Hkv + kv head
+  const int Hkv = Hq / G;
+  const int b = bc / Hkv, c = bc % Hkv;
+  const int k0 = blockIdx.y * kBN;
+  const int kw0 = k0 + 32 * wave;                   // this wave's first key
+  const int64_t kvbase = static_cast<int64_t>(bc) * N * kD;
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + kvbase;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + kvbase;
+
+  // ---- stage the key tile for the dQ operand, read it transposed
+  for (int e = tid; e < kBN * kD / 8; e += 256) {
+    const int row = e >> 4, c8 = e & 15;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (k0 + row < N) u = *reinterpret_cast<const uint4*>(kg + static_cast<int64_t>(k0 + row) * kD + 8 * c8);
+    *reinterpret_cast<uint4*>(&sm[row * kD + 8 * c8]) = u;
+  }
+  __syncthreads();
+  // dQ B operand [16 keys x 32 d]: d = 32*wave + col, keys of k-step ks in slots
+  bf16x8 kq[kBN / 16];
+#pragma unroll
+  for (int ks = 0; ks < kBN / 16; ++ks) {
+    const uint16_t* p0 = &sm[(16 * ks + 4 * gk + srow) * kD + 32 * wave + sub16 + 4 * m4];
+    kq[ks] = lds_tr_pair(p0, p0 + 8 * kD);
+  }
+  // S and dP B operands [16 d x 32 keys]: key = kw0 + col, d = 16*ds + 8*g + s
+  bf16x8 kb[kD / 16], vb[kD / 16];
+  {
+    const int key = kw0 + col;
+#pragma unroll
+    for (int ds = 0; ds < kD / 16; ++ds) {
+      uint4 u = make_uint4(0, 0, 0, 0), w = make_uint4(0, 0, 0, 0);
+      if (key < N) {
+        u = *reinterpret_cast<const uint4*>(kg + static_cast<int64_t>(key) * kD + 16 * ds + 8 * g);
+        w = *reinterpret_cast<const uint4*>(vg + static_cast<int64_t>(key) * kD + 16 * ds + 8 * g);
+      }
+      kb[ds] = __builtin_bit_cast(bf16x8, u);
+      vb[ds] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+  __syncthreads();   // the staging area is reused below
+
+  f32x16 dv[4], dk[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    dv[dt] = f32x16{};
+    dk[dt] = f32x16{};
+  }
+
+  const int nqt = (N + kBM - 1) / kBM;
+  const int qt0 = k0 / kBM;                         // first query tile that sees these keys
+  const int iters = G * (nqt - qt0);
+  const int blk_lo = k0 / block;
+
+  // per-iteration global -> register prefetch: Q, G_f, G_s rows and row values
+  uint4 pq[2], pgf[2], pgs[2];
+  float prow = 0.f;
+  auto iter_coords = [&](int it, int& hq, int& q0) {
+    const int hg = it / (nqt - qt0);
+    hq = c * G + hg;
+    q0 = (qt0 + it % (nqt - qt0)) * kBM;
+  };
+  auto prefetch = [&](int it) {
+    int hq, q0;
+    iter_coords(it, hq, q0);
+    const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int cidx = tid + 256 * r, row = cidx >> 4, c8 = cidx & 15;
+      const int t = q0 + row;
+      uint4 z = make_uint4(0, 0, 0, 0);
+      pq[r] = pgf[r] = pgs[r] = z;
+      if (t < N) {
+        const int64_t o = (rowbase + t) * kD + 8 * c8;
+        pq[r] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + o);
+        if (kFull) pgf[r] = *reinterpret_cast<const uint4*>(a.g_full + o);
+        if (kSparse) pgs[r] = *reinterpret_cast<const uint4*>(a.g_sparse + o);
+      }
+    }
+    if (tid < 4 * kBM) {
+      const int which = tid >> 5, r = tid & 31, t = q0 + r;
+      const float* src = which == 0 ? a.lse2_full : which == 1 ? a.lse2_sparse : which == 2 ? a.D_full : a.D_sparse;
+      const bool need = (which & 1) ? kSparse : kFull;
+      prow = (which < 2) ? INFINITY : 0.f;            // rows past the end: P = 0
+      if (need && t < N) prow = src[rowbase + t];
+    }
+  };
+
+  if (iters > 0) prefetch(0);
+  for (int it = 0; it < iters; ++it) {
+    int hq, q0;
+    iter_coords(it, hq, q0);
+    const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N;
+    // ---- registers -> LDS
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int cidx = tid + 256 * r, row = cidx >> 4, c8 = cidx & 15;
+      *reinterpret_cast<uint4*>(&Qs[row * kQPitch + 8 * c8]) = pq[r];
+      if (kFull) *reinterpret_cast<uint4*>(&Gfs[row * kQPitch + 8 * c8]) = pgf[r];
+      if (kSparse) *reinterpret_cast<uint4*>(&Gss[row * kQPitch + 8 * c8]) = pgs[r];
+    }
+    if (tid < 4 * kBM) rowv[tid >> 5][tid & 31] = prow;
+    if (tid < 4) selmask[tid] = 0u;
+    __syncthreads();
+    // ---- selection: rows of this tile that picked the blocks of these keys
+    if (kSparse) {
+      for (int e = tid; e < kBM * K; e += 256) {
+        const int r = e / K, t = q0 + r;
+        if (t < N) {
+          const int blk = a.sel[(rowbase + t) * K + (e - r * K)];
+          const int rel = blk - blk_lo;
+          if (blk >= 0 && rel >= 0 && rel * block < kBN) {
+            // key groups of 32 covered by this block
+            const int g0 = (blk * block - k0) / 32, g1 = (blk * block + block - 1 - k0) / 32;
+            for (int gg = max(g0, 0); gg <= min(g1, 3); ++gg) atomicOr(&selmask[gg], 1u << r);
+          }
+        }
+      }
+    }
+    if (it + 1 < iters) prefetch(it + 1);
+    if (kSparse) __syncthreads();
+
+    const bool wave_has_pairs = q0 + kBM - 1 >= kw0 && kw0 < N;   // uniform
+    uint32_t smask = 0;
+    if (kSparse) smask = __builtin_amdgcn_readfirstlane(selmask[wave]);
+    const bool do_sparse = kSparse && smask != 0u;
+    const bool diag = q0 < kw0 + 31;                               // some key > some query
+
+    if (wave_has_pairs) {
+      // ---- S = Q K^T  [32 q x 32 keys], lane: key col, queries 8(i/4)+4g+(i%4)
+      f32x16 s = f32x16{};
+#pragma unroll
+      for (int ds = 0; ds < kD / 16; ++ds) s = mfma32x32x16(lds_read8(&Qs[col * kQPitch + 16 * ds + 8 * g]), kb[ds], s);
+      f32x16 dpf = f32x16{}, dps = f32x16{};
+      if (kFull) {
+#pragma unroll
+        for (int ds = 0; ds < kD / 16; ++ds)
+          dpf = mfma32x32x16(lds_read8(&Gfs[col * kQPitch + 16 * ds + 8 * g]), vb[ds], dpf);
+      }
+      if (do_sparse) {
+#pragma unroll
+        for (int ds = 0; ds < kD / 16; ++ds)
+          dps = mfma32x32x16(lds_read8(&Gss[col * kQPitch + 16 * ds + 8 * g]), vb[ds], dps);
+      }
+      // ---- probabilities and dS
+      const int key = kw0 + col;
+      float pf[16], ps[16], dsv[16];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int qb = 8 * a4 + 4 * g;
+        const float4 lf = *reinterpret_cast<const float4*>(&rowv[0][qb]);
+        const float4 lsp = *reinterpret_cast<const float4*>(&rowv[1][qb]);
+        const float4 df = *reinterpret_cast<const float4*>(&rowv[2][qb]);
+        const float4 dsp = *reinterpret_cast<const float4*>(&rowv[3][qb]);
+        const float lfa[4] = {lf.x, lf.y, lf.z, lf.w}, lsa[4] = {lsp.x, lsp.y, lsp.z, lsp.w};
+        const float dfa[4] = {df.x, df.y, df.z, df.w}, dsa[4] = {dsp.x, dsp.y, dsp.z, dsp.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * a4 + e;
+          const int qloc = qb + e;
+          const bool live = !diag || key <= q0 + qloc;
+          const float x = s[i] * scale_log2;
+          float d = 0.f;
+          pf[i] = 0.f;
+          ps[i] = 0.f;
+          if (kFull) {
+            pf[i] = live ? fast_exp2(x - lfa[e]) : 0.f;
+            d += pf[i] * (dpf[i] - dfa[e]);
+          }
+          if (kSparse) {
+            const bool on = live && ((smask >> qloc) & 1u);
+            ps[i] = on ? fast_exp2(x - lsa[e]) : 0.f;
+            d += ps[i] * (dps[i] - dsa[e]);
+          }
+          dsv[i] = d;
+        }
+      }
+      // ---- dS^T -> LDS (bf16) for the dQ reduction over the 128 keys
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        uint2 u = make_uint2(pack_bf16x2(dsv[4 * a4], dsv[4 * a4 + 1]), pack_bf16x2(dsv[4 * a4 + 2], dsv[4 * a4 + 3]));
+        *reinterpret_cast<uint2*>(&dSt[(32 * wave + col) * kSPitch + 8 * a4 + 4 * g]) = u;
+      }
+      // ---- dV^T += G^T P, dK^T += Q^T dS  (k = queries; 2 steps of 16)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int o = 8 * st;
+        const bf16x8 bpf = to_bf16x8(pf[o], pf[o + 1], pf[o + 2], pf[o + 3], pf[o + 4], pf[o + 5], pf[o + 6], pf[o + 7]);
+        const bf16x8 bps = to_bf16x8(ps[o], ps[o + 1], ps[o + 2], ps[o + 3], ps[o + 4], ps[o + 5], ps[o + 6], ps[o + 7]);
+        const bf16x8 bds = to_bf16x8(dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3], dsv[o + 4], dsv[o + 5], dsv[o + 6], dsv[o + 7]);
+        const int r0 = (16 * st + 4 * gk + srow) * kQPitch + sub16 + 4 * m4;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int off = r0 + 32 * dt;
+          if (kFull) dv[dt] = mfma32x32x16(lds_tr_pair(&Gfs[off], &Gfs[off + 8 * kQPitch]), bpf, dv[dt]);
+          if (do_sparse) dv[dt] = mfma32x32x16(lds_tr_pair(&Gss[off], &Gss[off + 8 * kQPitch]), bps, dv[dt]);
+          dk[dt] = mfma32x32x16(lds_tr_pair(&Qs[off], &Qs[off + 8 * kQPitch]), bds, dk[dt]);
+        }
+      }
+    } else {
+      // no causal pairs for this wave: its dS rows are zero
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+        *reinterpret_cast<uint2*>(&dSt[(32 * wave + col) * kSPitch + 8 * a4 + 4 * g]) = make_uint2(0, 0);
+    }
+    __syncthreads();
+
+    // ---- dQ[32 q x 32 d] of this wave's d-slice = dS[32 q x 128 keys] K[128 keys x 32 d]
+    {
+      f32x16 dq = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < kBN / 16; ++ks) {
+        const uint16_t* p0 = &dSt[(16 * ks + 4 * gk + srow) * kSPitch + sub16 + 4 * m4];
+        dq = mfma32x32x16(lds_tr_pair(p0, p0 + 8 * kSPitch), kq[ks], dq);
+      }
+      const int dcol = 32 * wave + col;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = q0 + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (t < N) unsafeAtomicAdd(a.dq_acc + (rowbase + t) * kD + dcol, scale * dq[i]);
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: dK = scale * dK^T^T, dV (bf16); lane owns key kw0 + col
+  const int key = kw0 + col;
+  if (key < N) {
+    uint16_t* dkg = static_cast<uint16_t*>(a.dk) + kvbase + static_cast<int64_t>(key) * kD;
+    uint16_t* dvg = static_cast<uint16_t*>(a.dv) + kvbase + static_cast<int64_t>(key) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d0 = 32 * dt + 8 * a4 + 4 * g;
+        const int i = 4 * a4;
+        *reinterpret_cast<uint2*>(dkg + d0) =
+            make_uint2(pack_bf16x2(scale * dk[dt][i], scale * dk[dt][i + 1]),
+                       pack_bf16x2(scale * dk[dt][i + 2], scale * dk[dt][i + 3]));
+        *reinterpret_cast<uint2*>(dvg + d0) =
+            make_uint2(pack_bf16x2(dv[dt][i], dv[dt][i + 1]), pack_bf16x2(dv[dt][i + 2], dv[dt][i + 3]));
+      }
+    }
+  }
+}
+
+}  // namespace
+
+bool bwd_mfma_supported(const Dims& D) { return D.dtype == 1 && D.d == kD; }
+
+void launch_bwd_pre(const Dims& D, const BwdPreArgs& a, float w_sparsity, float w_commit, hipStream_t s) {
+  const float inv_m = static_cast<float>(1.0 / static_cast<double>(D.q_elems()));
+  dim3 grid(static_cast<unsigned>((D.rows() + 3) / 4));
+  timing_begin(kKBwdPre, s);
+  hipLaunchKernelGGL(k_bwd_pre, grid, dim3(256), 0, s, a, D.rows(), w_sparsity, w_commit, inv_m);
+  timing_end(kKBwdPre, s);
+}
+
+void launch_bwd_mfma(const Dims& D, const BwdMainArgs& a, hipStream_t s) {
+  dim3 grid(D.B * D.Hkv, (D.N + kBN - 1) / kBN);
+  const float scale_log2 = D.scale * kLog2e;
+  timing_begin(kKBwdMfma, s);
+  if (a.mode == kFullOnly)
+    hipLaunchKernelGGL(k_bwd_mfma<kModeFull>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.block, D.K, D.scale,
+                       scale_log2);
+  else if (a.mode == kSparseOnly)
+    hipLaunchKernelGGL(k_bwd_mfma<kModeSparse>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.block, D.K, D.scale,
+                       scale_log2);
+  else
+    hipLaunchKernelGGL(k_bwd_mfma<kModeDual>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.block, D.K, D.scale,
+                       scale_log2);
+  timing_end(kKBwdMfma, s);
+}
+
+}  // namespace ssa

@@ -71,6 +71,29 @@ void launch_bwd_simt(const Dims& D, const BwdArgs& a, hipStream_t s);
 bool fwd_mfma_supported(const Dims& D);
 void launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s);
 
+struct BwdPreArgs {
+  const void* dout;                 // may be null: zero upstream gradient
+  const void *h_full, *h_sparse;
+  const float *lse_full, *lse_sparse;
+  uint16_t *g_full, *g_sparse;      // bf16 stream gradients [rows][d]
+  float *D_full, *D_sparse;         // rowsum(G o h)
+  float *lse2_full, *lse2_sparse;   // lse * log2(e)
+  float* dq_acc;                    // zeroed here
+  int mode;
+};
+struct BwdMainArgs {
+  const void *q, *k, *v;
+  const int32_t* sel;
+  const uint16_t *g_full, *g_sparse;
+  const float *lse2_full, *lse2_sparse, *D_full, *D_sparse;
+  float* dq_acc;
+  void *dk, *dv;
+  int mode;
+};
+bool bwd_mfma_supported(const Dims& D);
+void launch_bwd_pre(const Dims& D, const BwdPreArgs& a, float w_sparsity, float w_commit, hipStream_t s);
+void launch_bwd_mfma(const Dims& D, const BwdMainArgs& a, hipStream_t s);
+
 // --- small kernels (misc.hip) ---
 void launch_zero_f32(float* p, int64_t n, hipStream_t s);
 void launch_convert(const float* src, void* dst, int dtype, int64_t n, hipStream_t s);
