@@ -119,6 +119,7 @@ struct BwdWs {
   // MFMA path
   uint16_t *g_full, *g_sparse;
   float *D_full, *D_sparse, *lse2_full, *lse2_sparse, *dq_acc;
+  uint32_t* rowbits;
 };
 static BwdWs carve_bwd(const Dims& D, int mode, Carver& c) {
   BwdWs w{};
@@ -133,6 +134,7 @@ static BwdWs carve_bwd(const Dims& D, int mode, Carver& c) {
       w.g_sparse = c.take<uint16_t>(D.q_elems() * sizeof(uint16_t));
       w.D_sparse = c.take<float>(D.rows() * sizeof(float));
       w.lse2_sparse = c.take<float>(D.rows() * sizeof(float));
+      w.rowbits = c.take<uint32_t>(D.rows() * ((D.nb + 31) / 32) * sizeof(uint32_t));
     }
     w.dq_acc = c.take<float>(D.q_elems() * sizeof(float));
   } else {
@@ -242,12 +244,13 @@ ssa_status_t ssa_attn_bwd(const ssa_shape_t* shape, int32_t mode, float w_sparsi
   Carver c{static_cast<char*>(ws)};
   BwdWs w = carve_bwd(D, mode, c);
   if (bwd_mfma_supported(D)) {
+    const int W = (D.nb + 31) / 32;
     BwdPreArgs p{d_out, h_full, h_sparse, lse_full, lse_sparse, w.g_full, w.g_sparse, w.D_full, w.D_sparse,
-                 w.lse2_full, w.lse2_sparse, w.dq_acc, mode};
+                 w.lse2_full, w.lse2_sparse, w.dq_acc, sel, w.rowbits, D.K, W, mode};
     launch_bwd_pre(D, p, w_sparsity, w_commit, s);
     if ((st = launch_status()) != SSA_OK) return st;
     BwdMainArgs m{q, k, v, sel, w.g_full, w.g_sparse, w.lse2_full, w.lse2_sparse, w.D_full, w.D_sparse,
-                  w.dq_acc, dk, dv, mode};
+                  w.dq_acc, dk, dv, w.rowbits, W, mode};
     launch_bwd_mfma(D, m, s);
     if ((st = launch_status()) != SSA_OK) return st;
     launch_convert(w.dq_acc, dq, D.dtype, D.q_elems(), s);

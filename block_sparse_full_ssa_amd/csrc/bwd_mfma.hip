@@ -85,6 +85,18 @@ __global__ void __launch_bounds__(256)
   *reinterpret_cast<float2*>(a.dq_acc + off) = make_float2(0.f, 0.f);
   Df = wave_sum(Df);
   Ds = wave_sum(Ds);
+  if (has_s) {
+    // bitmask over key blocks of this row's selection (word w covers blocks 32w..32w+31)
+    const int32_t* selr = a.sel + row * a.K;
+    for (int w = lane; w < a.W; w += 64) {
+      uint32_t word = 0u;
+      for (int e = 0; e < a.K; ++e) {
+        const int blk = selr[e];
+        if (blk >= 0 && (blk >> 5) == w) word |= 1u << (blk & 31);
+      }
+      a.rowbits[row * a.W + w] = word;
+    }
+  }
   if (lane == 0) {
     if (has_f) {
       a.D_full[row] = Df;
@@ -103,16 +115,17 @@ __global__ void __launch_bounds__(256, 1)
     k_bwd_mfma(BwdMainArgs a, int Hq, int G, int N, int block, int K, float scale, float scale_log2) {
   constexpr bool kFull = MODE != kModeSparse;
   constexpr bool kSparse = MODE != kModeFull;
-  // LDS: staging of the key tile at start, then per-iteration tiles
-  // K staging (128 x 128) at start; afterwards Q, G_f, G_s tiles and dS^T
-  constexpr int kSm = (kBN * kD > 3 * kBM * kQPitch + kBN * kSPitch) ? kBN * kD : 3 * kBM * kQPitch + kBN * kSPitch;
-  __shared__ __attribute__((aligned(16))) uint16_t sm[kSm];
-  uint16_t* Qs = sm;                                // [32][136]
-  uint16_t* Gfs = sm + kBM * kQPitch;               // [32][136]
-  uint16_t* Gss = sm + 2 * kBM * kQPitch;           // [32][136]
-  uint16_t* dSt = sm + 3 * kBM * kQPitch;           // [128][40]
-  __shared__ float rowv[4][kBM];                    // lse2_f, lse2_s, D_f, D_s
-  __shared__ uint32_t selmask[4];                   // per 32-key group: rows that selected its block
+  // dynamic LDS: the 128 x 128 key tile staged once at start, then two sets
+  // of {Q, G_f, G_s tiles [32][136], dS^T [128][40], row values [4][32]}
+  extern __shared__ __attribute__((aligned(16))) uint16_t sm[];
+  constexpr int kTileSet = 3 * kBM * kQPitch + kBN * kSPitch + 2 * 4 * kBM;   // elements (row values as 2 halves)
+  auto Qs = [&](int buf) { return sm + buf * kTileSet; };
+  auto Gfs = [&](int buf) { return sm + buf * kTileSet + kBM * kQPitch; };
+  auto Gss = [&](int buf) { return sm + buf * kTileSet + 2 * kBM * kQPitch; };
+  auto dSt = [&](int buf) { return sm + buf * kTileSet + 3 * kBM * kQPitch; };
+  auto rowv = [&](int buf) {
+    return reinterpret_cast<float*>(sm + buf * kTileSet + 3 * kBM * kQPitch + kBN * kSPitch);
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -172,11 +185,13 @@ __global__ void __launch_bounds__(256, 1)
   const int nqt = (N + kBM - 1) / kBM;
   const int qt0 = k0 / kBM;                         // first query tile that sees these keys
   const int iters = G * (nqt - qt0);
-  const int blk_lo = k0 / block;
+  const int wblk = (kw0 < N ? kw0 : N - 1) / block; // key block of this wave (block >= 32)
 
-  // per-iteration global -> register prefetch: Q, G_f, G_s rows and row values
+  // per-iteration global -> register prefetch: Q, G_f, G_s rows, row values
+  // and the selection word of this wave's block for row q0 + col
   uint4 pq[2], pgf[2], pgs[2];
   float prow = 0.f;
+  uint32_t pbits = 0u;
   auto iter_coords = [&](int it, int& hq, int& q0) {
     const int hg = it / (nqt - qt0);
     hq = c * G + hg;
@@ -206,45 +221,45 @@ __global__ void __launch_bounds__(256, 1)
       prow = (which < 2) ? INFINITY : 0.f;            // rows past the end: P = 0
       if (need && t < N) prow = src[rowbase + t];
     }
+    if (kSparse) {
+      const int t = q0 + col;
+      pbits = t < N ? a.rowbits[(rowbase + t) * a.W + (wblk >> 5)] : 0u;
+    }
+  };
+  auto stage = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int cidx = tid + 256 * r, row = cidx >> 4, c8 = cidx & 15;
+      *reinterpret_cast<uint4*>(&Qs(buf)[row * kQPitch + 8 * c8]) = pq[r];
+      if (kFull) *reinterpret_cast<uint4*>(&Gfs(buf)[row * kQPitch + 8 * c8]) = pgf[r];
+      if (kSparse) *reinterpret_cast<uint4*>(&Gss(buf)[row * kQPitch + 8 * c8]) = pgs[r];
+    }
+    if (tid < 4 * kBM) rowv(buf)[tid] = prow;
   };
 
-  if (iters > 0) prefetch(0);
+  uint32_t cur_bits = 0u;
+  if (iters > 0) {
+    prefetch(0);
+    stage(0);
+    cur_bits = pbits;
+  }
+  __syncthreads();
+  int cur = 0;
   for (int it = 0; it < iters; ++it) {
     int hq, q0;
     iter_coords(it, hq, q0);
     const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N;
-    // ---- registers -> LDS
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int cidx = tid + 256 * r, row = cidx >> 4, c8 = cidx & 15;
-      *reinterpret_cast<uint4*>(&Qs[row * kQPitch + 8 * c8]) = pq[r];
-      if (kFull) *reinterpret_cast<uint4*>(&Gfs[row * kQPitch + 8 * c8]) = pgf[r];
-      if (kSparse) *reinterpret_cast<uint4*>(&Gss[row * kQPitch + 8 * c8]) = pgs[r];
-    }
-    if (tid < 4 * kBM) rowv[tid >> 5][tid & 31] = prow;
-    if (tid < 4) selmask[tid] = 0u;
-    __syncthreads();
-    // ---- selection: rows of this tile that picked the blocks of these keys
-    if (kSparse) {
-      for (int e = tid; e < kBM * K; e += 256) {
-        const int r = e / K, t = q0 + r;
-        if (t < N) {
-          const int blk = a.sel[(rowbase + t) * K + (e - r * K)];
-          const int rel = blk - blk_lo;
-          if (blk >= 0 && rel >= 0 && rel * block < kBN) {
-            // key groups of 32 covered by this block
-            const int g0 = (blk * block - k0) / 32, g1 = (blk * block + block - 1 - k0) / 32;
-            for (int gg = max(g0, 0); gg <= min(g1, 3); ++gg) atomicOr(&selmask[gg], 1u << r);
-          }
-        }
-      }
-    }
+    const uint16_t* Q = Qs(cur);
+    const uint16_t* Gf = Gfs(cur);
+    const uint16_t* Gs = Gss(cur);
+    const float* rv = rowv(cur);
+    uint16_t* dS = dSt(cur);
     if (it + 1 < iters) prefetch(it + 1);
-    if (kSparse) __syncthreads();
 
     const bool wave_has_pairs = q0 + kBM - 1 >= kw0 && kw0 < N;   // uniform
-    uint32_t smask = 0;
-    if (kSparse) smask = __builtin_amdgcn_readfirstlane(selmask[wave]);
+    // rows of this tile that selected this wave's key block (ballot: uniform)
+    uint32_t smask = 0u;
+    if (kSparse) smask = static_cast<uint32_t>(__ballot(lane < 32 && ((cur_bits >> (wblk & 31)) & 1u)));
     const bool do_sparse = kSparse && smask != 0u;
     const bool diag = q0 < kw0 + 31;                               // some key > some query
 
@@ -252,17 +267,17 @@ __global__ void __launch_bounds__(256, 1)
       // ---- S = Q K^T  [32 q x 32 keys], lane: key col, queries 8(i/4)+4g+(i%4)
       f32x16 s = f32x16{};
 #pragma unroll
-      for (int ds = 0; ds < kD / 16; ++ds) s = mfma32x32x16(lds_read8(&Qs[col * kQPitch + 16 * ds + 8 * g]), kb[ds], s);
+      for (int ds = 0; ds < kD / 16; ++ds) s = mfma32x32x16(lds_read8(&Q[col * kQPitch + 16 * ds + 8 * g]), kb[ds], s);
       f32x16 dpf = f32x16{}, dps = f32x16{};
       if (kFull) {
 #pragma unroll
         for (int ds = 0; ds < kD / 16; ++ds)
-          dpf = mfma32x32x16(lds_read8(&Gfs[col * kQPitch + 16 * ds + 8 * g]), vb[ds], dpf);
+          dpf = mfma32x32x16(lds_read8(&Gf[col * kQPitch + 16 * ds + 8 * g]), vb[ds], dpf);
       }
       if (do_sparse) {
 #pragma unroll
         for (int ds = 0; ds < kD / 16; ++ds)
-          dps = mfma32x32x16(lds_read8(&Gss[col * kQPitch + 16 * ds + 8 * g]), vb[ds], dps);
+          dps = mfma32x32x16(lds_read8(&Gs[col * kQPitch + 16 * ds + 8 * g]), vb[ds], dps);
       }
       // ---- probabilities and dS
       const int key = kw0 + col;
@@ -270,10 +285,10 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int qb = 8 * a4 + 4 * g;
-        const float4 lf = *reinterpret_cast<const float4*>(&rowv[0][qb]);
-        const float4 lsp = *reinterpret_cast<const float4*>(&rowv[1][qb]);
-        const float4 df = *reinterpret_cast<const float4*>(&rowv[2][qb]);
-        const float4 dsp = *reinterpret_cast<const float4*>(&rowv[3][qb]);
+        const float4 lf = *reinterpret_cast<const float4*>(&rv[0 * kBM + qb]);
+        const float4 lsp = *reinterpret_cast<const float4*>(&rv[1 * kBM + qb]);
+        const float4 df = *reinterpret_cast<const float4*>(&rv[2 * kBM + qb]);
+        const float4 dsp = *reinterpret_cast<const float4*>(&rv[3 * kBM + qb]);
         const float lfa[4] = {lf.x, lf.y, lf.z, lf.w}, lsa[4] = {lsp.x, lsp.y, lsp.z, lsp.w};
         const float dfa[4] = {df.x, df.y, df.z, df.w}, dsa[4] = {dsp.x, dsp.y, dsp.z, dsp.w};
 #pragma unroll
@@ -301,7 +316,7 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         uint2 u = make_uint2(pack_bf16x2(dsv[4 * a4], dsv[4 * a4 + 1]), pack_bf16x2(dsv[4 * a4 + 2], dsv[4 * a4 + 3]));
-        *reinterpret_cast<uint2*>(&dSt[(32 * wave + col) * kSPitch + 8 * a4 + 4 * g]) = u;
+        *reinterpret_cast<uint2*>(&dS[(32 * wave + col) * kSPitch + 8 * a4 + 4 * g]) = u;
       }
       // ---- dV^T += G^T P, dK^T += Q^T dS  (k = queries; 2 steps of 16)
 #pragma unroll
@@ -314,17 +329,18 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const int off = r0 + 32 * dt;
-          if (kFull) dv[dt] = mfma32x32x16(lds_tr_pair(&Gfs[off], &Gfs[off + 8 * kQPitch]), bpf, dv[dt]);
-          if (do_sparse) dv[dt] = mfma32x32x16(lds_tr_pair(&Gss[off], &Gss[off + 8 * kQPitch]), bps, dv[dt]);
-          dk[dt] = mfma32x32x16(lds_tr_pair(&Qs[off], &Qs[off + 8 * kQPitch]), bds, dk[dt]);
+          if (kFull) dv[dt] = mfma32x32x16(lds_tr_pair(&Gf[off], &Gf[off + 8 * kQPitch]), bpf, dv[dt]);
+          if (do_sparse) dv[dt] = mfma32x32x16(lds_tr_pair(&Gs[off], &Gs[off + 8 * kQPitch]), bps, dv[dt]);
+          dk[dt] = mfma32x32x16(lds_tr_pair(&Q[off], &Q[off + 8 * kQPitch]), bds, dk[dt]);
         }
       }
     } else {
       // no causal pairs for this wave: its dS rows are zero
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4)
-        *reinterpret_cast<uint2*>(&dSt[(32 * wave + col) * kSPitch + 8 * a4 + 4 * g]) = make_uint2(0, 0);
+        *reinterpret_cast<uint2*>(&dS[(32 * wave + col) * kSPitch + 8 * a4 + 4 * g]) = make_uint2(0, 0);
     }
+    if (it + 1 < iters) stage(cur ^ 1);
     __syncthreads();
 
     // ---- dQ[32 q x 32 d] of this wave's d-slice = dS[32 q x 128 keys] K[128 keys x 32 d]
@@ -332,7 +348,7 @@ __global__ void __launch_bounds__(256, 1)
       f32x16 dq = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < kBN / 16; ++ks) {
-        const uint16_t* p0 = &dSt[(16 * ks + 4 * gk + srow) * kSPitch + sub16 + 4 * m4];
+        const uint16_t* p0 = &dS[(16 * ks + 4 * gk + srow) * kSPitch + sub16 + 4 * m4];
         dq = mfma32x32x16(lds_tr_pair(p0, p0 + 8 * kSPitch), kq[ks], dq);
       }
       const int dcol = 32 * wave + col;
@@ -342,7 +358,8 @@ __global__ void __launch_bounds__(256, 1)
         if (t < N) unsafeAtomicAdd(a.dq_acc + (rowbase + t) * kD + dcol, scale * dq[i]);
       }
     }
-    __syncthreads();
+    cur ^= 1;
+    cur_bits = pbits;
   }
 
   // ---- epilogue: dK = scale * dK^T^T, dV (bf16); lane owns key kw0 + col
@@ -378,19 +395,29 @@ void launch_bwd_pre(const Dims& D, const BwdPreArgs& a, float w_sparsity, float 
   timing_end(kKBwdPre, s);
 }
 
-void launch_bwd_mfma(const Dims& D, const BwdMainArgs& a, hipStream_t s) {
+constexpr size_t kBwdLds =
+    2 * (3 * kBM * kQPitch + kBN * kSPitch + 2 * 4 * kBM) * sizeof(uint16_t) > kBN * kD * sizeof(uint16_t)
+        ? 2 * (3 * kBM * kQPitch + kBN * kSPitch + 2 * 4 * kBM) * sizeof(uint16_t)
+        : kBN * kD * sizeof(uint16_t);
+
+template <int MODE>
+static void launch_bwd_mode(const Dims& D, const BwdMainArgs& a, hipStream_t s) {
+  static bool granted = false;   // dynamic LDS above 64 KiB must be requested per kernel
+  if (!granted) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bwd_mfma<MODE>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kBwdLds));
+    granted = true;
+  }
   dim3 grid(D.B * D.Hkv, (D.N + kBN - 1) / kBN);
-  const float scale_log2 = D.scale * kLog2e;
+  hipLaunchKernelGGL(k_bwd_mfma<MODE>, grid, dim3(256), kBwdLds, s, a, D.Hq, D.G, D.N, D.block, D.K, D.scale,
+                     D.scale * kLog2e);
+}
+
+void launch_bwd_mfma(const Dims& D, const BwdMainArgs& a, hipStream_t s) {
   timing_begin(kKBwdMfma, s);
-  if (a.mode == kFullOnly)
-    hipLaunchKernelGGL(k_bwd_mfma<kModeFull>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.block, D.K, D.scale,
-                       scale_log2);
-  else if (a.mode == kSparseOnly)
-    hipLaunchKernelGGL(k_bwd_mfma<kModeSparse>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.block, D.K, D.scale,
-                       scale_log2);
-  else
-    hipLaunchKernelGGL(k_bwd_mfma<kModeDual>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.block, D.K, D.scale,
-                       scale_log2);
+  if (a.mode == kFullOnly) launch_bwd_mode<kModeFull>(D, a, s);
+  else if (a.mode == kSparseOnly) launch_bwd_mode<kModeSparse>(D, a, s);
+  else launch_bwd_mode<kModeDual>(D, a, s);
   timing_end(kKBwdMfma, s);
 }
 

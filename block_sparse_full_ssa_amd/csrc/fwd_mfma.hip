@@ -36,15 +36,19 @@ constexpr int kBN = 64;        // keys per tile
 constexpr int kKPitch = 136;   // K tile row pitch (elements), padded against bank conflicts
 constexpr int kVPitch = 128;   // V tile row pitch (read with transpose reads)
 constexpr float kLn2 = 0.69314718055994531f;
+constexpr float kTau = 8.f;    // lazy-rescale threshold (log2 units)
 
 enum { kModeDual = 0, kModeFull = 1, kModeSparse = 2 };
 
 template <int MODE>
 __global__ void __launch_bounds__(256, 1)
     k_fwd_mfma(FwdArgs a, int Hq, int G, int N, int block, int nb, int K, float scale_log2, int n_qtiles) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * kKPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kBN * kVPitch];
-  extern __shared__ uint32_t bits[];   // [kBM][W] row selection bits, then [W] union
+  // dynamic LDS: K tiles [2][64][136], V tiles [2][64][128], then the
+  // selection bits [kBM][W] of the rows and their union [W]
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  uint16_t* Kbuf = lds;
+  uint16_t* Vbuf = lds + 2 * kBN * kKPitch;
+  uint32_t* bits = reinterpret_cast<uint32_t*>(lds + 2 * kBN * kKPitch + 2 * kBN * kVPitch);
   const int W = (nb + 31) >> 5;
   uint32_t* anybits = bits + kBM * W;
 
@@ -132,16 +136,28 @@ __global__ void __launch_bounds__(256, 1)
     }
   };
 
-  int j = MODE == kModeSparse ? next_tile(-1) : 0;
-  if (j <= j_last) prefetch(j);
-  while (j <= j_last) {
+  auto stage = [&](int buf) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int c = tid + 256 * r, row = c >> 4, c8 = c & 15;
-      *reinterpret_cast<uint4*>(&Ks[row * kKPitch + 8 * c8]) = kpre[r];
-      *reinterpret_cast<uint4*>(&Vs[row * kVPitch + 8 * c8]) = vpre[r];
+      *reinterpret_cast<uint4*>(&Kbuf[buf * kBN * kKPitch + row * kKPitch + 8 * c8]) = kpre[r];
+      *reinterpret_cast<uint4*>(&Vbuf[buf * kBN * kVPitch + row * kVPitch + 8 * c8]) = vpre[r];
     }
-    __syncthreads();
+  };
+
+  // Double-buffered K/V: tile j is read from buffer `cur` while tile jn is
+  // loaded into registers and then written to the other buffer; one barrier
+  // per tile.
+  int j = MODE == kModeSparse ? next_tile(-1) : 0;
+  int cur = 0;
+  if (j <= j_last) {
+    prefetch(j);
+    stage(0);
+  }
+  __syncthreads();
+  while (j <= j_last) {
+    const uint16_t* Ks = Kbuf + cur * kBN * kKPitch;
+    const uint16_t* Vs = Vbuf + cur * kBN * kVPitch;
     const int jn = MODE == kModeSparse ? next_tile(j) : j + 1;
     if (jn <= j_last) prefetch(jn);
 
@@ -193,13 +209,16 @@ __global__ void __launch_bounds__(256, 1)
         mx[kh] = fmaxf(m, __shfl_xor(m, 32, 64));
       }
 
-      const float mfn = MODE != kModeSparse ? fmaxf(mf, fmaxf(mx[0], mx[1])) : 0.f;
+      // lazy rescaling: the running maximum moves only when a tile exceeds it
+      // by more than kTau (log2 units), so probabilities stay below 2^kTau
+      const float mxf = fmaxf(mx[0], mx[1]);
+      const float mfn = MODE != kModeSparse ? (mxf > mf + kTau ? mxf : mf) : 0.f;
       float pv[2][16];
       float msn = ms, sum_s = 0.f;
       bool rescale = false;
       if (MODE != kModeFull && sparse_any) {
         const float mxs = fmaxf(sb[0] ? mx[0] : -INFINITY, sb[1] ? mx[1] : -INFINITY);
-        msn = fmaxf(ms, mxs);
+        msn = mxs > ms + kTau ? mxs : ms;
         // dual mode: derive P_sparse from P_full when 2^(m_full - m_sparse) is safe
         rescale = MODE == kModeDual && !__any((sb[0] || sb[1]) && (mfn - msn > 64.f));
         if (!rescale) {
@@ -285,7 +304,9 @@ __global__ void __launch_bounds__(256, 1)
         }
       }
     }
+    if (jn <= j_last) stage(cur ^ 1);
     __syncthreads();
+    cur ^= 1;
     j = jn;
   }
 
@@ -336,24 +357,41 @@ __global__ void __launch_bounds__(256, 1)
 
 }  // namespace
 
-bool fwd_mfma_supported(const Dims& D) { return D.dtype == 1 && D.d == kD; }
+size_t fwd_mfma_lds_bytes(const Dims& D);
+
+bool fwd_mfma_supported(const Dims& D) {
+  // the selection bits of 128 rows must fit in LDS next to the K/V tiles
+  return D.dtype == 1 && D.d == kD && fwd_mfma_lds_bytes(D) <= 160 * 1024;
+}
+
+template <int MODE>
+static void launch_mode(const Dims& D, const FwdArgs& a, size_t lds, int n_qtiles, float scale_log2,
+                        hipStream_t s) {
+  static size_t granted = 0;    // dynamic LDS above 64 KiB must be requested per kernel
+  if (lds > granted) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fwd_mfma<MODE>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    granted = lds;
+  }
+  dim3 grid(D.B * D.Hq, n_qtiles);
+  hipLaunchKernelGGL(k_fwd_mfma<MODE>, grid, dim3(256), lds, s, a, D.Hq, D.G, D.N, D.block, D.nb, D.K,
+                     scale_log2, n_qtiles);
+}
+
+size_t fwd_mfma_lds_bytes(const Dims& D) {
+  const int W = (D.nb + 31) / 32;
+  return static_cast<size_t>(2 * kBN * kKPitch + 2 * kBN * kVPitch) * sizeof(uint16_t) +
+         static_cast<size_t>(kBM * W + W) * sizeof(uint32_t);
+}
 
 void launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s) {
   const int n_qtiles = (D.N + kBM - 1) / kBM;
-  dim3 grid(D.B * D.Hq, n_qtiles);
-  const int W = (D.nb + 31) / 32;
-  const size_t lds = static_cast<size_t>(kBM * W + W) * sizeof(uint32_t);
+  const size_t lds = fwd_mfma_lds_bytes(D);
   const float scale_log2 = D.scale * 1.4426950408889634f;
   timing_begin(kKFwdMfma, s);
-  if (a.mode == kFullOnly)
-    hipLaunchKernelGGL(k_fwd_mfma<kModeFull>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.block, D.nb, D.K,
-                       scale_log2, n_qtiles);
-  else if (a.mode == kSparseOnly)
-    hipLaunchKernelGGL(k_fwd_mfma<kModeSparse>, grid, dim3(256), lds, s, a, D.Hq, D.G, D.N, D.block, D.nb,
-                       D.K, scale_log2, n_qtiles);
-  else
-    hipLaunchKernelGGL(k_fwd_mfma<kModeDual>, grid, dim3(256), lds, s, a, D.Hq, D.G, D.N, D.block, D.nb, D.K,
-                       scale_log2, n_qtiles);
+  if (a.mode == kFullOnly) launch_mode<kModeFull>(D, a, lds, n_qtiles, scale_log2, s);
+  else if (a.mode == kSparseOnly) launch_mode<kModeSparse>(D, a, lds, n_qtiles, scale_log2, s);
+  else launch_mode<kModeDual>(D, a, lds, n_qtiles, scale_log2, s);
   timing_end(kKFwdMfma, s);
 }
 

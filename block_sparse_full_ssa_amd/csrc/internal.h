@@ -79,6 +79,9 @@ struct BwdPreArgs {
   float *D_full, *D_sparse;         // rowsum(G o h)
   float *lse2_full, *lse2_sparse;   // lse * log2(e)
   float* dq_acc;                    // zeroed here
+  const int32_t* sel;               // sparse modes: selection rows [rows][K]
+  uint32_t* rowbits;                // sparse modes: [rows][W] bitmask over key blocks
+  int K, W;
   int mode;
 };
 struct BwdMainArgs {
@@ -88,6 +91,8 @@ struct BwdMainArgs {
   const float *lse2_full, *lse2_sparse, *D_full, *D_sparse;
   float* dq_acc;
   void *dk, *dv;
+  const uint32_t* rowbits;          // [rows][W] selection bitmask from bwd_pre
+  int W;
   int mode;
 };
 bool bwd_mfma_supported(const Dims& D);
