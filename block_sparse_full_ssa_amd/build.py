@@ -23,6 +23,8 @@ SOURCES = ["api.hip", "select.hip", "simt.hip", "misc.hip", "fwd_mfma.hip", "bwd
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
     "-munsafe-fp-atomics",
+    # keep MFMA accumulators in VGPRs where they fit (no AGPR round trips)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     # no packed fp32 instructions in any kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",

@@ -15,13 +15,22 @@
 // registers) leaves lane l with 16 keys of query l % 32 in its accumulator,
 // the softmax statistics of a query live in one lane pair (l, l ^ 32), and
 // O^T += V^T P^T (A = V^T via LDS transpose reads, B = P^T straight from the
-// S^T accumulator) keeps the output of query l % 32 in lane l.
+// S^T accumulator) keeps the output of query l % 32 in lane l.  Keys are
+// processed in halves of 32 so that the logits need 16 registers and both
+// output accumulators stay in VGPRs.
 //
-// Sparse stream: P_sparse = P_full * 2^(m_full - m_sparse) on selected key
-// blocks (one multiply instead of a second exponential) whenever that factor
-// is at most 2^64 for every lane of the wave; otherwise the exponential is
-// evaluated directly.  When every block is selected the two streams execute
-// identical operations and their outputs agree bit for bit.
+// K/V tiles of 64 keys move from HBM straight into LDS (global_load_lds,
+// 16 bytes per lane), double-buffered, one barrier per tile.  16-byte chunks
+// are XOR-swizzled within each 256-byte row so that the matrix-operand reads
+// of K rows and the transpose reads of V columns avoid bank conflicts.
+//
+// Softmax: the running maxima are integers (ceil of a tile maximum) and move
+// lazily, only when a tile exceeds them by more than kTau, so every rescale
+// factor is an exact power of two.  In particular the sparse probabilities of
+// a selected block are P_full * 2^(m_full - m_sparse), an exact fp32 product,
+// whenever that exponent is at most 64; otherwise they are evaluated
+// directly.  When every block is selected the two streams execute identical
+// operations and agree bit for bit.
 
 #include "common.h"
 #include "internal.h"
@@ -30,34 +39,51 @@
 namespace ssa {
 namespace {
 
-constexpr int kD = 128;        // head dimension
-constexpr int kBM = 128;       // queries per workgroup
-constexpr int kBN = 64;        // keys per tile
-constexpr int kKPitch = 136;   // K tile row pitch (elements), padded against bank conflicts
-constexpr int kVPitch = 128;   // V tile row pitch (read with transpose reads)
+constexpr int kD = 128;          // head dimension
+constexpr int kBM = 128;         // queries per workgroup
+constexpr int kBN = 64;          // keys per tile
+constexpr int kTile = kBN * kD;  // elements of one K or V tile
 constexpr float kLn2 = 0.69314718055994531f;
-constexpr float kTau = 8.f;    // lazy-rescale threshold (log2 units)
+constexpr float kTau = 8.f;      // lazy-rescale threshold (log2 units)
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
 
 enum { kModeDual = 0, kModeFull = 1, kModeSparse = 2 };
+
+// Physical 16-byte chunk of logical chunk c in row r.
+__device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
+__device__ __forceinline__ int swz_v(int r, int c) { return c ^ (((r >> 2) & 3) << 2); }
+
+__device__ __forceinline__ float max16(const f32x16& v) {
+  float m = fmaxf(v[0], v[1]);
+#pragma unroll
+  for (int i = 2; i < 16; i += 2) m = fmaxf(m, fmaxf(v[i], v[i + 1]));
+  return m;
+}
 
 template <int MODE>
 __global__ void __launch_bounds__(256, 1)
     k_fwd_mfma(FwdArgs a, int Hq, int G, int N, int block, int nb, int K, float scale_log2, int n_qtiles) {
-  // dynamic LDS: K tiles [2][64][136], V tiles [2][64][128], then the
-  // selection bits [kBM][W] of the rows and their union [W]
+  constexpr bool kFull = MODE != kModeSparse;
+  constexpr bool kSparse = MODE != kModeFull;
+  // dynamic LDS: K tiles [2][64][128], V tiles [2][64][128] (swizzled), then
+  // the selection bits [kBM][W] of the rows and their union [W]
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   uint16_t* Kbuf = lds;
-  uint16_t* Vbuf = lds + 2 * kBN * kKPitch;
-  uint32_t* bits = reinterpret_cast<uint32_t*>(lds + 2 * kBN * kKPitch + 2 * kBN * kVPitch);
+  uint16_t* Vbuf = lds + 2 * kTile;
+  uint32_t* bits = reinterpret_cast<uint32_t*>(lds + 4 * kTile);
   const int W = (nb + 31) >> 5;
   uint32_t* anybits = bits + kBM * W;
 
+  // The wave index and every condition that guards an MFMA are wave-uniform
+  // for the compiler: matrix instructions must sit behind scalar branches,
+  // never behind an EXEC mask.
   const int tid = threadIdx.x;
-  // The wave index and every condition that guards an MFMA are made
-  // wave-uniform for the compiler (readfirstlane): matrix instructions must
-  // sit behind scalar branches, never behind an EXEC mask.
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, col = lane & 31;
+  const int grp = lane >> 4, li = lane & 15;
+  const int gk = grp >> 1, srow = li >> 2, m4 = li & 3;
   const int bh = blockIdx.x;
   const int q0 = (n_qtiles - 1 - static_cast<int>(blockIdx.y)) * kBM;   // longest tiles first
   const int b = bh / Hq, h = bh % Hq;
@@ -67,7 +93,7 @@ __global__ void __launch_bounds__(256, 1)
   const uint16_t* vg = static_cast<const uint16_t*>(a.v) + bc * N * kD;
 
   // ---- selection bits of the workgroup's rows
-  if (MODE != kModeFull) {
+  if (kSparse) {
     for (int e = tid; e < kBM * W + W; e += 256) bits[e] = 0u;
     __syncthreads();
     for (int e = tid; e < kBM * K; e += 256) {
@@ -85,7 +111,8 @@ __global__ void __launch_bounds__(256, 1)
   // ---- the wave's 32 queries as B operands (query = col, d = 16*ds + 8*g + s)
   const int qrow = q0 + wave * 32 + col;           // this lane's query
   const bool wave_live = q0 + wave * 32 < N;
-  const int wave_last_q = min(N - 1, q0 + wave * 32 + 31);
+  const int wave_q0 = q0 + wave * 32;
+  const int wave_last_q = min(N - 1, wave_q0 + 31);
   bf16x8 qreg[kD / 16];
 #pragma unroll
   for (int ds = 0; ds < kD / 16; ++ds) {
@@ -103,7 +130,7 @@ __global__ void __launch_bounds__(256, 1)
   float mf = -INFINITY, lf = 0.f, ms = -INFINITY, ls = 0.f;
 
   const int j_last = min(N - 1, q0 + kBM - 1) / kBN;
-  if (MODE != kModeFull) __syncthreads();
+  if (kSparse) __syncthreads();
 
   // tile needed by the workgroup? (sparse-only mode skips unselected tiles)
   auto tile_needed = [&](int j) -> bool {
@@ -119,192 +146,163 @@ __global__ void __launch_bounds__(256, 1)
     return j_last + 1;
   };
 
-  // global -> register prefetch of one K/V tile: thread owns chunks tid + 256 r
-  uint4 kpre[4], vpre[4];
-  auto prefetch = [&](int j) {
+  // HBM -> LDS copy of one K/V tile: each wave moves rows 16*wave .. +15, one
+  // 1 KiB instruction per 4 rows; lane l fills physical chunk l % 16 of row
+  // 4n + l / 16, so it fetches the logical chunk stored there.  Keys past the
+  // end read the last key: finite values that the causal mask removes.
+  auto load_tile = [&](int j, int buf) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int c = tid + 256 * r, row = c >> 4, c8 = c & 15;
-      const int key = j * kBN + row;
-      if (key < N) {
-        kpre[r] = *reinterpret_cast<const uint4*>(kg + static_cast<int64_t>(key) * kD + 8 * c8);
-        vpre[r] = *reinterpret_cast<const uint4*>(vg + static_cast<int64_t>(key) * kD + 8 * c8);
-      } else {
-        kpre[r] = make_uint4(0, 0, 0, 0);
-        vpre[r] = make_uint4(0, 0, 0, 0);
-      }
+      const int n = wave * 4 + r;
+      const int row = 4 * n + (lane >> 4);
+      const int p = lane & 15;
+      const int64_t key = min(j * kBN + row, N - 1);
+      const uint16_t* srck = kg + key * kD + 8 * swz_k(row, p);
+      const uint16_t* srcv = vg + key * kD + 8 * swz_v(row, p);
+      __builtin_amdgcn_global_load_lds((const glb_void*)srck, (lds_void*)(Kbuf + buf * kTile + n * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const glb_void*)srcv, (lds_void*)(Vbuf + buf * kTile + n * 512), 16, 0, 0);
     }
   };
 
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int c = tid + 256 * r, row = c >> 4, c8 = c & 15;
-      *reinterpret_cast<uint4*>(&Kbuf[buf * kBN * kKPitch + row * kKPitch + 8 * c8]) = kpre[r];
-      *reinterpret_cast<uint4*>(&Vbuf[buf * kBN * kVPitch + row * kVPitch + 8 * c8]) = vpre[r];
-    }
-  };
-
-  // Double-buffered K/V: tile j is read from buffer `cur` while tile jn is
-  // loaded into registers and then written to the other buffer; one barrier
-  // per tile.
   int j = MODE == kModeSparse ? next_tile(-1) : 0;
   int cur = 0;
-  if (j <= j_last) {
-    prefetch(j);
-    stage(0);
-  }
+  if (j <= j_last) load_tile(j, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   while (j <= j_last) {
-    const uint16_t* Ks = Kbuf + cur * kBN * kKPitch;
-    const uint16_t* Vs = Vbuf + cur * kBN * kVPitch;
+    const uint16_t* Ks = Kbuf + cur * kTile;
+    const uint16_t* Vs = Vbuf + cur * kTile;
     const int jn = MODE == kModeSparse ? next_tile(j) : j + 1;
-    if (jn <= j_last) prefetch(jn);
+    if (jn <= j_last) load_tile(jn, cur ^ 1);
 
-    // ---- selection of this tile's (one or two) key blocks for the lane's query
-    bool sb[2] = {false, false};
-    bool sparse_any = false;
-    const bool wave_in = wave_live && j * kBN <= wave_last_q;
-    if (MODE != kModeFull && wave_in) {
-      const int r = wave * 32 + col;
+    if (wave_live && j * kBN <= wave_last_q) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
-        const int blk = (j * kBN + kh * 32) / block;
-        sb[kh] = qrow < N && blk < nb && ((bits[r * W + (blk >> 5)] >> (blk & 31)) & 1u);
-      }
-      sparse_any = __builtin_amdgcn_readfirstlane(__any(sb[0] || sb[1]) ? 1 : 0) != 0;
-    }
+        const int kbase = j * kBN + kh * 32;          // first key of this half
+        if (kbase > wave_last_q) break;               // uniform: later keys are all masked
 
-    if (wave_in && (MODE != kModeSparse || sparse_any)) {
-      // ---- S^T = K Q^T for the two 32-key halves
-      f32x16 s[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int ds = 0; ds < kD / 16; ++ds) {
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          bf16x8 ka = lds_read8(&Ks[(kh * 32 + col) * kKPitch + 16 * ds + 8 * g]);
-          s[kh] = mfma32x32x16(ka, qreg[ds], s[kh]);
+        // selection bit of this half's key block for the lane's query
+        bool sb = false;
+        bool sparse_any = false;
+        if (kSparse) {
+          const int blk = kbase / block;
+          sb = qrow < N && blk < nb && ((bits[(wave * 32 + col) * W + (blk >> 5)] >> (blk & 31)) & 1u);
+          sparse_any = __builtin_amdgcn_readfirstlane(__any(sb) ? 1 : 0) != 0;
+          if (MODE == kModeSparse && !sparse_any) continue;
         }
-      }
-      // ---- scale to log2 units, causal mask near the diagonal
-      const bool diag = j * kBN + kBN - 1 > q0 + wave * 32;
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float x = s[kh][i] * scale_log2;
-          if (diag) {
-            const int key = j * kBN + kh * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key > qrow) x = -INFINITY;
-          }
-          s[kh][i] = x;
-        }
-      }
-      float mx[2];
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        float m = s[kh][0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) m = fmaxf(m, s[kh][i]);
-        mx[kh] = fmaxf(m, __shfl_xor(m, 32, 64));
-      }
 
-      // lazy rescaling: the running maximum moves only when a tile exceeds it
-      // by more than kTau (log2 units), so probabilities stay below 2^kTau
-      const float mxf = fmaxf(mx[0], mx[1]);
-      const float mfn = MODE != kModeSparse ? (mxf > mf + kTau ? mxf : mf) : 0.f;
-      float pv[2][16];
-      float msn = ms, sum_s = 0.f;
-      bool rescale = false;
-      if (MODE != kModeFull && sparse_any) {
-        const float mxs = fmaxf(sb[0] ? mx[0] : -INFINITY, sb[1] ? mx[1] : -INFINITY);
-        msn = mxs > ms + kTau ? mxs : ms;
-        // dual mode: derive P_sparse from P_full when 2^(m_full - m_sparse) is safe
-        rescale = MODE == kModeDual && !__any((sb[0] || sb[1]) && (mfn - msn > 64.f));
-        if (!rescale) {
+        // ---- S^T = K Q^T for 32 keys, in log2 units
+        f32x16 s = f32x16{};
+        {
+          const int r = kh * 32 + col;
 #pragma unroll
-          for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float p = sb[kh] ? fast_exp2(s[kh][i] - msn) : 0.f;
-              pv[kh][i] = p;
-              sum_s += p;
-            }
+          for (int ds = 0; ds < kD / 16; ++ds)
+            s = mfma32x32x16(lds_read8(&Ks[r * kD + 8 * swz_k(r, 2 * ds + g)]), qreg[ds], s);
         }
-      }
-
-      bf16x8 pf[4], ps[4];
-      if (MODE != kModeSparse) {
-        // full stream
-        const float alpha = fast_exp2(mf - mfn);
-        float sum = 0.f;
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
+        for (int i = 0; i < 16; ++i) s[i] *= scale_log2;
+        if (kbase + 31 > wave_q0) {                  // uniform: the diagonal needs the causal mask
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const float p = fast_exp2(s[kh][i] - mfn);
-            s[kh][i] = p;
-            sum += p;
+            const int key = kbase + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (key > qrow) s[i] = -INFINITY;
           }
-        lf = lf * alpha + sum;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) of[dt] *= alpha;
         }
-        mf = mfn;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int kh = st >> 1, o = 8 * (st & 1);
-          pf[st] = to_bf16x8(s[kh][o], s[kh][o + 1], s[kh][o + 2], s[kh][o + 3], s[kh][o + 4], s[kh][o + 5],
-                             s[kh][o + 6], s[kh][o + 7]);
-        }
-      }
-      if (MODE != kModeFull && sparse_any) {
-        if (rescale) {
-          const float c = (sb[0] || sb[1]) ? fast_exp2(mfn - msn) : 0.f;
-#pragma unroll
-          for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const float p = sb[kh] ? s[kh][i] * c : 0.f;
-              pv[kh][i] = p;
-              sum_s += p;
-            }
-        }
-        const float alpha_s = msn == -INFINITY ? 1.f : fast_exp2(ms - msn);
-        ls = ls * alpha_s + sum_s;
-        if (__any(alpha_s != 1.f)) {
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) os[dt] *= alpha_s;
-        }
-        ms = msn;
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-          const int kh = st >> 1, o = 8 * (st & 1);
-          ps[st] = to_bf16x8(pv[kh][o], pv[kh][o + 1], pv[kh][o + 2], pv[kh][o + 3], pv[kh][o + 4],
-                             pv[kh][o + 5], pv[kh][o + 6], pv[kh][o + 7]);
-        }
-      }
+        float mx = max16(s);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
 
-      // ---- O^T += V^T P^T; V^T operand through transpose reads
-      const bool do_full = MODE != kModeSparse;
-      const bool do_sparse = MODE != kModeFull && sparse_any;
-      const int grp = lane >> 4, li = lane & 15;
-      const int dsub = (grp & 1) * 16, gk = grp >> 1;   // d half and key group of this 16-lane group
-      const int srow = li >> 2, m4 = li & 3;
+        // ---- new maxima (integers, moved lazily)
+        float mfn = mf, alpha = 1.f;
+        if (kFull) {
+          if (mx > mf + kTau) mfn = ceilf(mx);
+          alpha = fast_exp2(mf - mfn);               // 1, 0 (first update) or an exact power of two
+        }
+        float msn = ms, alpha_s = 1.f;
+        bool rescale = false;
+        if (kSparse && sparse_any) {
+          const float mxs = sb ? mx : -INFINITY;
+          if (mxs > ms + kTau) msn = ceilf(mxs);
+          alpha_s = msn == -INFINITY ? 1.f : fast_exp2(ms - msn);
+          rescale = MODE == kModeDual &&
+                    __builtin_amdgcn_readfirstlane(__any(sb && mfn - msn > 64.f) ? 1 : 0) == 0;
+        }
+
+        // ---- sparse probabilities evaluated directly (sparse-only, or factor too large)
+        bf16x8 ps[2];
+        float sum_s = 0.f;
+        if (kSparse && sparse_any && !rescale) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const uint16_t* r0 = &Vs[(16 * st + 4 * gk + srow) * kVPitch + dsub + 4 * m4];
-        const uint16_t* r1 = r0 + 8 * kVPitch;
+          for (int st = 0; st < 2; ++st) {
+            float p[8];
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          bf16x8 va = lds_tr_pair(r0 + 32 * dt, r1 + 32 * dt);
-          if (do_full) of[dt] = mfma32x32x16(va, pf[st], of[dt]);
-          if (do_sparse) os[dt] = mfma32x32x16(va, ps[st], os[dt]);
+            for (int e = 0; e < 8; ++e) {
+              p[e] = sb ? fast_exp2(s[8 * st + e] - msn) : 0.f;
+              sum_s += p[e];
+            }
+            ps[st] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+          }
+        }
+
+        // ---- full stream
+        bf16x8 pf[2];
+        if (kFull) {
+          float sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            s[i] = fast_exp2(s[i] - mfn);
+            sum += s[i];
+          }
+          lf = lf * alpha + sum;
+          if (__any(alpha != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) of[dt] *= alpha;
+          }
+          mf = mfn;
+#pragma unroll
+          for (int st = 0; st < 2; ++st)
+            pf[st] = to_bf16x8(s[8 * st], s[8 * st + 1], s[8 * st + 2], s[8 * st + 3], s[8 * st + 4],
+                               s[8 * st + 5], s[8 * st + 6], s[8 * st + 7]);
+        }
+        if (kSparse && sparse_any) {
+          if (rescale) {
+            // exact: the factor is a power of two
+            const float c = sb ? fast_exp2(mfn - msn) : 0.f;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+              float p[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                p[e] = s[8 * st + e] * c;
+                sum_s += p[e];
+              }
+              ps[st] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+            }
+          }
+          ls = ls * alpha_s + sum_s;
+          if (__any(alpha_s != 1.f)) {
+#pragma unroll
+            for (int dt = 0; dt < 4; ++dt) os[dt] *= alpha_s;
+          }
+          ms = msn;
+        }
+
+        // ---- O^T += V^T P^T over the 32 keys (two k-steps of 16)
+#pragma unroll
+        for (int st2 = 0; st2 < 2; ++st2) {
+          const int r0 = kh * 32 + st2 * 16 + 4 * gk + srow;   // key row of this lane's first read
+          const int r1 = r0 + 8;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const int c = 4 * dt + 2 * (grp & 1) + (m4 >> 1);   // logical 16-byte chunk
+            const int e = 4 * (m4 & 1);
+            const bf16x8 va = lds_tr_pair(&Vs[r0 * kD + 8 * swz_v(r0, c) + e], &Vs[r1 * kD + 8 * swz_v(r1, c) + e]);
+            if (kFull) of[dt] = mfma32x32x16(va, pf[st2], of[dt]);
+            if (kSparse && sparse_any) os[dt] = mfma32x32x16(va, ps[st2], os[dt]);
+          }
         }
       }
     }
-    if (jn <= j_last) stage(cur ^ 1);
+    __builtin_amdgcn_s_waitcnt(0);     // the next tile has landed in LDS
     __syncthreads();
     cur ^= 1;
     j = jn;
@@ -331,11 +329,11 @@ __global__ void __launch_bounds__(256, 1)
         if (MODE == kModeDual) sq += (hf[e] - hs[e]) * (hf[e] - hs[e]);
       }
       if (row_ok) {
-        if (MODE != kModeSparse) {
+        if (kFull) {
           uint2 u = make_uint2(pack_bf16x2(hf[0], hf[1]), pack_bf16x2(hf[2], hf[3]));
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h_full) + row * kD + dcol) = u;
         }
-        if (MODE != kModeFull) {
+        if (kSparse) {
           uint2 u = make_uint2(pack_bf16x2(hs[0], hs[1]), pack_bf16x2(hs[2], hs[3]));
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h_sparse) + row * kD + dcol) = u;
         }
@@ -346,8 +344,8 @@ __global__ void __launch_bounds__(256, 1)
   if (row_ok && g == 0) {
     const float lse_f = (mf + fast_log2(lf)) * kLn2;
     const float lse_s = (ms + fast_log2(ls)) * kLn2;
-    if (MODE != kModeSparse && a.lse_full) a.lse_full[row] = lse_f;
-    if (MODE != kModeFull && a.lse_sparse) a.lse_sparse[row] = lse_s;
+    if (kFull && a.lse_full) a.lse_full[row] = lse_f;
+    if (kSparse && a.lse_sparse) a.lse_sparse[row] = lse_s;
     if (MODE == kModeDual) {
       a.delta[row] = -expm1f(lse_s - lse_f);
       a.row_sq[row] = sq;
@@ -355,18 +353,8 @@ __global__ void __launch_bounds__(256, 1)
   }
 }
 
-}  // namespace
-
-size_t fwd_mfma_lds_bytes(const Dims& D);
-
-bool fwd_mfma_supported(const Dims& D) {
-  // the selection bits of 128 rows must fit in LDS next to the K/V tiles
-  return D.dtype == 1 && D.d == kD && fwd_mfma_lds_bytes(D) <= 160 * 1024;
-}
-
 template <int MODE>
-static void launch_mode(const Dims& D, const FwdArgs& a, size_t lds, int n_qtiles, float scale_log2,
-                        hipStream_t s) {
+void launch_mode(const Dims& D, const FwdArgs& a, size_t lds, int n_qtiles, float scale_log2, hipStream_t s) {
   static size_t granted = 0;    // dynamic LDS above 64 KiB must be requested per kernel
   if (lds > granted) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fwd_mfma<MODE>),
@@ -378,15 +366,21 @@ static void launch_mode(const Dims& D, const FwdArgs& a, size_t lds, int n_qtile
                      scale_log2, n_qtiles);
 }
 
-size_t fwd_mfma_lds_bytes(const Dims& D) {
+size_t lds_bytes(const Dims& D) {
   const int W = (D.nb + 31) / 32;
-  return static_cast<size_t>(2 * kBN * kKPitch + 2 * kBN * kVPitch) * sizeof(uint16_t) +
-         static_cast<size_t>(kBM * W + W) * sizeof(uint32_t);
+  return static_cast<size_t>(4 * kTile) * sizeof(uint16_t) + static_cast<size_t>(kBM * W + W) * sizeof(uint32_t);
+}
+
+}  // namespace
+
+bool fwd_mfma_supported(const Dims& D) {
+  // the selection bits of 128 rows must fit in LDS next to the K/V tiles
+  return D.dtype == 1 && D.d == kD && lds_bytes(D) <= 160 * 1024;
 }
 
 void launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s) {
   const int n_qtiles = (D.N + kBM - 1) / kBM;
-  const size_t lds = fwd_mfma_lds_bytes(D);
+  const size_t lds = lds_bytes(D);
   const float scale_log2 = D.scale * 1.4426950408889634f;
   timing_begin(kKFwdMfma, s);
   if (a.mode == kFullOnly) launch_mode<kModeFull>(D, a, lds, n_qtiles, scale_log2, s);
