@@ -39,8 +39,6 @@ namespace {
 constexpr int kD = 128;
 constexpr int kBN = 128;       // keys per workgroup
 constexpr int kBM = 32;        // queries per iteration
-constexpr int kQPitch = 136;   // Q / G tile pitch (elements)
-constexpr int kSPitch = 40;    // dS^T tile pitch (elements), [key][query]
 constexpr float kLog2e = 1.4426950408889634f;
 
 enum { kModeDual = 0, kModeFull = 1, kModeSparse = 2 };
@@ -110,22 +108,28 @@ __global__ void __launch_bounds__(256)
 }
 
 // --------------------------------------------------------------- bwd_mfma --
+// Physical 16-byte chunk of logical chunk c: Q / G tiles (256-byte rows) and
+// dS^T tiles (64-byte rows).  Both the row reads of matrix operands and the
+// transpose reads then spread over all banks.
+__device__ __forceinline__ int swz_t(int r, int c) { return c ^ (r & 7); }
+__device__ __forceinline__ int swz_s(int r, int c) { return c ^ ((r >> 1) & 3); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
 template <int MODE>
 __global__ void __launch_bounds__(256, 1)
     k_bwd_mfma(BwdMainArgs a, int Hq, int G, int N, int block, int K, float scale, float scale_log2) {
   constexpr bool kFull = MODE != kModeSparse;
   constexpr bool kSparse = MODE != kModeFull;
   // dynamic LDS: the 128 x 128 key tile staged once at start, then two sets
-  // of {Q, G_f, G_s tiles [32][136], dS^T [128][40], row values [4][32]}
+  // of {Q, G_f, G_s tiles [32][128], dS^T [128][32], row values [4][32] fp32}
   extern __shared__ __attribute__((aligned(16))) uint16_t sm[];
-  constexpr int kTileSet = 3 * kBM * kQPitch + kBN * kSPitch + 2 * 4 * kBM;   // elements (row values as 2 halves)
-  auto Qs = [&](int buf) { return sm + buf * kTileSet; };
-  auto Gfs = [&](int buf) { return sm + buf * kTileSet + kBM * kQPitch; };
-  auto Gss = [&](int buf) { return sm + buf * kTileSet + 2 * kBM * kQPitch; };
-  auto dSt = [&](int buf) { return sm + buf * kTileSet + 3 * kBM * kQPitch; };
-  auto rowv = [&](int buf) {
-    return reinterpret_cast<float*>(sm + buf * kTileSet + 3 * kBM * kQPitch + kBN * kSPitch);
-  };
+  constexpr int kT = kBM * kD;                       // one Q / G tile
+  constexpr int kSet = 3 * kT + kBN * kBM + 2 * 4 * kBM;
+  auto tile = [&](int buf, int which) { return sm + buf * kSet + which * kT; };   // 0 Q, 1 G_f, 2 G_s
+  auto dSt = [&](int buf) { return sm + buf * kSet + 3 * kT; };
+  auto rowv = [&](int buf) { return reinterpret_cast<float*>(sm + buf * kSet + 3 * kT + kBN * kBM); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -182,79 +186,75 @@ __global__ void __launch_bounds__(256, 1)
     dk[dt] = f32x16{};
   }
 
-  const int nqt = (N + kBM - 1) / kBM;
+  // N is a multiple of 32 (block >= 32 divides it), so query tiles are whole.
+  const int nqt = N / kBM;
   const int qt0 = k0 / kBM;                         // first query tile that sees these keys
   const int iters = G * (nqt - qt0);
   const int wblk = (kw0 < N ? kw0 : N - 1) / block; // key block of this wave (block >= 32)
 
-  // per-iteration global -> register prefetch: Q, G_f, G_s rows, row values
-  // and the selection word of this wave's block for row q0 + col
-  uint4 pq[2], pgf[2], pgs[2];
-  float prow = 0.f;
-  uint32_t pbits = 0u;
   auto iter_coords = [&](int it, int& hq, int& q0) {
     const int hg = it / (nqt - qt0);
     hq = c * G + hg;
     q0 = (qt0 + it % (nqt - qt0)) * kBM;
   };
-  auto prefetch = [&](int it) {
+  // HBM -> LDS copy of the Q / G_f / G_s tiles of one iteration: 24 (or 16)
+  // 1 KiB instructions, 6 per wave; lane l fills physical chunk l % 16 of row
+  // 4n + l / 16 with the logical chunk stored there.
+  auto load_tiles = [&](int it, int buf) {
     int hq, q0;
     iter_coords(it, hq, q0);
-    const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N;
+    const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N + q0;
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int cidx = tid + 256 * r, row = cidx >> 4, c8 = cidx & 15;
-      const int t = q0 + row;
-      uint4 z = make_uint4(0, 0, 0, 0);
-      pq[r] = pgf[r] = pgs[r] = z;
-      if (t < N) {
-        const int64_t o = (rowbase + t) * kD + 8 * c8;
-        pq[r] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + o);
-        if (kFull) pgf[r] = *reinterpret_cast<const uint4*>(a.g_full + o);
-        if (kSparse) pgs[r] = *reinterpret_cast<const uint4*>(a.g_sparse + o);
-      }
-    }
-    if (tid < 4 * kBM) {
-      const int which = tid >> 5, r = tid & 31, t = q0 + r;
-      const float* src = which == 0 ? a.lse2_full : which == 1 ? a.lse2_sparse : which == 2 ? a.D_full : a.D_sparse;
-      const bool need = (which & 1) ? kSparse : kFull;
-      prow = (which < 2) ? INFINITY : 0.f;            // rows past the end: P = 0
-      if (need && t < N) prow = src[rowbase + t];
-    }
-    if (kSparse) {
-      const int t = q0 + col;
-      pbits = t < N ? a.rowbits[(rowbase + t) * a.W + (wblk >> 5)] : 0u;
+    for (int r = 0; r < 6; ++r) {
+      const int n = wave * 6 + r;                   // 0..23, uniform
+      const int which = n >> 3, n8 = n & 7;
+      if ((which == 1 && !kFull) || (which == 2 && !kSparse)) continue;
+      const uint16_t* src = which == 0 ? static_cast<const uint16_t*>(a.q) : which == 1 ? a.g_full : a.g_sparse;
+      const int row = 4 * n8 + (lane >> 4);
+      const int cl = swz_t(row, lane & 15);
+      __builtin_amdgcn_global_load_lds((const glb_void*)(src + (rowbase + row) * kD + 8 * cl),
+                                       (lds_void*)(tile(buf, which) + n8 * 512), 16, 0, 0);
     }
   };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int cidx = tid + 256 * r, row = cidx >> 4, c8 = cidx & 15;
-      *reinterpret_cast<uint4*>(&Qs(buf)[row * kQPitch + 8 * c8]) = pq[r];
-      if (kFull) *reinterpret_cast<uint4*>(&Gfs(buf)[row * kQPitch + 8 * c8]) = pgf[r];
-      if (kSparse) *reinterpret_cast<uint4*>(&Gss(buf)[row * kQPitch + 8 * c8]) = pgs[r];
+  // row values and this wave's selection word, through registers
+  float prow = 0.f;
+  uint32_t pbits = 0u;
+  auto load_rows = [&](int it) {
+    int hq, q0;
+    iter_coords(it, hq, q0);
+    const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N + q0;
+    if (tid < 4 * kBM) {
+      const int which = tid >> 5, r = tid & 31;
+      const float* src = which == 0 ? a.lse2_full : which == 1 ? a.lse2_sparse : which == 2 ? a.D_full : a.D_sparse;
+      const bool need = (which & 1) ? kSparse : kFull;
+      prow = need ? src[rowbase + r] : (which < 2 ? INFINITY : 0.f);
     }
-    if (tid < 4 * kBM) rowv(buf)[tid] = prow;
+    if (kSparse) pbits = a.rowbits[(rowbase + col) * a.W + (wblk >> 5)];
   };
 
   uint32_t cur_bits = 0u;
   if (iters > 0) {
-    prefetch(0);
-    stage(0);
+    load_tiles(0, 0);
+    load_rows(0);
+    if (tid < 4 * kBM) rowv(0)[tid] = prow;
     cur_bits = pbits;
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   int cur = 0;
   for (int it = 0; it < iters; ++it) {
     int hq, q0;
     iter_coords(it, hq, q0);
-    const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N;
-    const uint16_t* Q = Qs(cur);
-    const uint16_t* Gf = Gfs(cur);
-    const uint16_t* Gs = Gss(cur);
+    const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N + q0;
+    const uint16_t* Q = tile(cur, 0);
+    const uint16_t* Gf = tile(cur, 1);
+    const uint16_t* Gs = tile(cur, 2);
     const float* rv = rowv(cur);
     uint16_t* dS = dSt(cur);
-    if (it + 1 < iters) prefetch(it + 1);
+    if (it + 1 < iters) {
+      load_tiles(it + 1, cur ^ 1);
+      load_rows(it + 1);
+    }
 
     const bool wave_has_pairs = q0 + kBM - 1 >= kw0 && kw0 < N;   // uniform
     // rows of this tile that selected this wave's key block (ballot: uniform)
@@ -264,20 +264,16 @@ __global__ void __launch_bounds__(256, 1)
     const bool diag = q0 < kw0 + 31;                               // some key > some query
 
     if (wave_has_pairs) {
-      // ---- S = Q K^T  [32 q x 32 keys], lane: key col, queries 8(i/4)+4g+(i%4)
-      f32x16 s = f32x16{};
+      // ---- S = Q K^T, dP_f = G_f V^T, dP_s = G_s V^T  [32 q x 32 keys], three
+      // independent accumulation chains interleaved; lane: key col, queries 8(i/4)+4g+(i%4)
+      f32x16 s = f32x16{}, dpf = f32x16{}, dps = f32x16{};
+      const int ra = col * kD;
 #pragma unroll
-      for (int ds = 0; ds < kD / 16; ++ds) s = mfma32x32x16(lds_read8(&Q[col * kQPitch + 16 * ds + 8 * g]), kb[ds], s);
-      f32x16 dpf = f32x16{}, dps = f32x16{};
-      if (kFull) {
-#pragma unroll
-        for (int ds = 0; ds < kD / 16; ++ds)
-          dpf = mfma32x32x16(lds_read8(&Gf[col * kQPitch + 16 * ds + 8 * g]), vb[ds], dpf);
-      }
-      if (do_sparse) {
-#pragma unroll
-        for (int ds = 0; ds < kD / 16; ++ds)
-          dps = mfma32x32x16(lds_read8(&Gs[col * kQPitch + 16 * ds + 8 * g]), vb[ds], dps);
+      for (int ds = 0; ds < kD / 16; ++ds) {
+        const int off = ra + 8 * swz_t(col, 2 * ds + g);
+        s = mfma32x32x16(lds_read8(&Q[off]), kb[ds], s);
+        if (kFull) dpf = mfma32x32x16(lds_read8(&Gf[off]), vb[ds], dpf);
+        if (do_sparse) dps = mfma32x32x16(lds_read8(&Gs[off]), vb[ds], dps);
       }
       // ---- probabilities and dS
       const int key = kw0 + col;
@@ -313,10 +309,13 @@ __global__ void __launch_bounds__(256, 1)
         }
       }
       // ---- dS^T -> LDS (bf16) for the dQ reduction over the 128 keys
+      {
+        const int r = 32 * wave + col;
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        uint2 u = make_uint2(pack_bf16x2(dsv[4 * a4], dsv[4 * a4 + 1]), pack_bf16x2(dsv[4 * a4 + 2], dsv[4 * a4 + 3]));
-        *reinterpret_cast<uint2*>(&dS[(32 * wave + col) * kSPitch + 8 * a4 + 4 * g]) = u;
+        for (int a4 = 0; a4 < 4; ++a4) {
+          uint2 u = make_uint2(pack_bf16x2(dsv[4 * a4], dsv[4 * a4 + 1]), pack_bf16x2(dsv[4 * a4 + 2], dsv[4 * a4 + 3]));
+          *reinterpret_cast<uint2*>(&dS[r * kBM + 8 * swz_s(r, a4) + 4 * g]) = u;
+        }
       }
       // ---- dV^T += G^T P, dK^T += Q^T dS  (k = queries; 2 steps of 16)
 #pragma unroll
@@ -325,38 +324,42 @@ __global__ void __launch_bounds__(256, 1)
         const bf16x8 bpf = to_bf16x8(pf[o], pf[o + 1], pf[o + 2], pf[o + 3], pf[o + 4], pf[o + 5], pf[o + 6], pf[o + 7]);
         const bf16x8 bps = to_bf16x8(ps[o], ps[o + 1], ps[o + 2], ps[o + 3], ps[o + 4], ps[o + 5], ps[o + 6], ps[o + 7]);
         const bf16x8 bds = to_bf16x8(dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3], dsv[o + 4], dsv[o + 5], dsv[o + 6], dsv[o + 7]);
-        const int r0 = (16 * st + 4 * gk + srow) * kQPitch + sub16 + 4 * m4;
+        const int r0 = 16 * st + 4 * gk + srow, r1 = r0 + 8;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
-          const int off = r0 + 32 * dt;
-          if (kFull) dv[dt] = mfma32x32x16(lds_tr_pair(&Gf[off], &Gf[off + 8 * kQPitch]), bpf, dv[dt]);
-          if (do_sparse) dv[dt] = mfma32x32x16(lds_tr_pair(&Gs[off], &Gs[off + 8 * kQPitch]), bps, dv[dt]);
-          dk[dt] = mfma32x32x16(lds_tr_pair(&Q[off], &Q[off + 8 * kQPitch]), bds, dk[dt]);
+          const int cl = 4 * dt + 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
+          const int o0 = r0 * kD + 8 * swz_t(r0, cl) + e4, o1 = r1 * kD + 8 * swz_t(r1, cl) + e4;
+          if (kFull) dv[dt] = mfma32x32x16(lds_tr_pair(&Gf[o0], &Gf[o1]), bpf, dv[dt]);
+          if (do_sparse) dv[dt] = mfma32x32x16(lds_tr_pair(&Gs[o0], &Gs[o1]), bps, dv[dt]);
+          dk[dt] = mfma32x32x16(lds_tr_pair(&Q[o0], &Q[o1]), bds, dk[dt]);
         }
       }
     } else {
       // no causal pairs for this wave: its dS rows are zero
+      const int r = 32 * wave + col;
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4)
-        *reinterpret_cast<uint2*>(&dS[(32 * wave + col) * kSPitch + 8 * a4 + 4 * g]) = make_uint2(0, 0);
+        *reinterpret_cast<uint2*>(&dS[r * kBM + 8 * swz_s(r, a4) + 4 * g]) = make_uint2(0, 0);
     }
-    if (it + 1 < iters) stage(cur ^ 1);
+    if (it + 1 < iters && tid < 4 * kBM) rowv(cur ^ 1)[tid] = prow;
+    __builtin_amdgcn_s_waitcnt(0);     // next tiles landed, dS^T written
     __syncthreads();
 
     // ---- dQ[32 q x 32 d] of this wave's d-slice = dS[32 q x 128 keys] K[128 keys x 32 d]
     {
-      f32x16 dq = f32x16{};
+      f32x16 dq0 = f32x16{}, dq1 = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < kBN / 16; ++ks) {
-        const uint16_t* p0 = &dS[(16 * ks + 4 * gk + srow) * kSPitch + sub16 + 4 * m4];
-        dq = mfma32x32x16(lds_tr_pair(p0, p0 + 8 * kSPitch), kq[ks], dq);
+        const int r0 = 16 * ks + 4 * gk + srow, r1 = r0 + 8;
+        const int cl = 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
+        const bf16x8 ds_op = lds_tr_pair(&dS[r0 * kBM + 8 * swz_s(r0, cl) + e4], &dS[r1 * kBM + 8 * swz_s(r1, cl) + e4]);
+        if (ks & 1) dq1 = mfma32x32x16(ds_op, kq[ks], dq1);
+        else dq0 = mfma32x32x16(ds_op, kq[ks], dq0);
       }
-      const int dcol = 32 * wave + col;
+      float* dqp = a.dq_acc + (rowbase + 4 * g) * kD + 32 * wave + col;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int t = q0 + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (t < N) unsafeAtomicAdd(a.dq_acc + (rowbase + t) * kD + dcol, scale * dq[i]);
-      }
+      for (int i = 0; i < 16; ++i)
+        unsafeAtomicAdd(dqp + (8 * (i >> 2) + (i & 3)) * kD, scale * (dq0[i] + dq1[i]));
     }
     cur ^= 1;
     cur_bits = pbits;
@@ -395,10 +398,8 @@ void launch_bwd_pre(const Dims& D, const BwdPreArgs& a, float w_sparsity, float 
   timing_end(kKBwdPre, s);
 }
 
-constexpr size_t kBwdLds =
-    2 * (3 * kBM * kQPitch + kBN * kSPitch + 2 * 4 * kBM) * sizeof(uint16_t) > kBN * kD * sizeof(uint16_t)
-        ? 2 * (3 * kBM * kQPitch + kBN * kSPitch + 2 * 4 * kBM) * sizeof(uint16_t)
-        : kBN * kD * sizeof(uint16_t);
+constexpr size_t kBwdLds = 2 * (3 * kBM * kD + kBN * kBM + 2 * 4 * kBM) * sizeof(uint16_t);
+static_assert(kBwdLds >= kBN * kD * sizeof(uint16_t), "key staging must fit");
 
 template <int MODE>
 static void launch_bwd_mode(const Dims& D, const BwdMainArgs& a, hipStream_t s) {

@@ -25,7 +25,7 @@ _EXEC_WRITE = re.compile(r"^(s_and_saveexec|s_andn2_saveexec|s_or_saveexec|s_and
 
 def masked_mfmas(asm: str):
     """(line number, instruction) of every MFMA issued under a narrowed EXEC."""
-    lines = [l.strip() for l in asm.splitlines()]
+    lines = [l.split(";")[0].strip() for l in asm.splitlines()]
     found = []
     for i, t in enumerate(lines):
         if not t.startswith("v_mfma"):

@@ -15,6 +15,13 @@ def test_scanner_flags_masked_mfma():
     ])
     hits = isa_check.masked_mfmas(asm)
     assert [ln for ln, _ in hits] == [1]
+    # a block label (even with a trailing comment) ends the backward scan
+    asm2 = "\n".join([
+        "s_and_saveexec_b64 s[4:5], s[34:35]",
+        ".LBB2_60:                               ;   in Loop: Header=BB2_39 Depth=1",
+        "v_mfma_f32_32x32x16_bf16 v[144:159], v[198:201], a[44:47], v[144:159]",
+    ])
+    assert isa_check.masked_mfmas(asm2) == []
 
 
 @pytest.mark.parametrize("src", isa_check.MFMA_SOURCES)
