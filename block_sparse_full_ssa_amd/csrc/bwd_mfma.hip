@@ -122,14 +122,15 @@ __global__ void __launch_bounds__(256, 1)
     k_bwd_mfma(BwdMainArgs a, int Hq, int G, int N, int block, int K, float scale, float scale_log2) {
   constexpr bool kFull = MODE != kModeSparse;
   constexpr bool kSparse = MODE != kModeFull;
-  // dynamic LDS: the 128 x 128 key tile staged once at start, then two sets
-  // of {Q, G_f, G_s tiles [32][128], dS^T [128][32], row values [4][32] fp32}
-  extern __shared__ __attribute__((aligned(16))) uint16_t sm[];
+  // LDS: the 128 x 128 key tile staged once at start, then two sets of
+  // {Q, G_f, G_s tiles [32][128], dS^T [128][32], row values [4][32] fp32},
+  // each buffer its own object so that the compiler can tell the set being
+  // read from the set being filled by the HBM -> LDS copies
   constexpr int kT = kBM * kD;                       // one Q / G tile
-  constexpr int kSet = 3 * kT + kBN * kBM + 2 * 4 * kBM;
-  auto tile = [&](int buf, int which) { return sm + buf * kSet + which * kT; };   // 0 Q, 1 G_f, 2 G_s
-  auto dSt = [&](int buf) { return sm + buf * kSet + 3 * kT; };
-  auto rowv = [&](int buf) { return reinterpret_cast<float*>(sm + buf * kSet + 3 * kT + kBN * kBM); };
+  __shared__ __attribute__((aligned(16))) uint16_t Kst[kBN * kD];
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[kT], Q1[kT], F0[kT], F1[kT], S0[kT], S1[kT];
+  __shared__ __attribute__((aligned(16))) uint16_t D0[kBN * kBM], D1[kBN * kBM];
+  __shared__ __attribute__((aligned(16))) float R0[4 * kBM], R1[4 * kBM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -152,14 +153,14 @@ __global__ void __launch_bounds__(256, 1)
     const int row = e >> 4, c8 = e & 15;
     uint4 u = make_uint4(0, 0, 0, 0);
     if (k0 + row < N) u = *reinterpret_cast<const uint4*>(kg + static_cast<int64_t>(k0 + row) * kD + 8 * c8);
-    *reinterpret_cast<uint4*>(&sm[row * kD + 8 * c8]) = u;
+    *reinterpret_cast<uint4*>(&Kst[row * kD + 8 * c8]) = u;
   }
   __syncthreads();
   // dQ B operand [16 keys x 32 d]: d = 32*wave + col, keys of k-step ks in slots
   bf16x8 kq[kBN / 16];
 #pragma unroll
   for (int ks = 0; ks < kBN / 16; ++ks) {
-    const uint16_t* p0 = &sm[(16 * ks + 4 * gk + srow) * kD + 32 * wave + sub16 + 4 * m4];
+    const uint16_t* p0 = &Kst[(16 * ks + 4 * gk + srow) * kD + 32 * wave + sub16 + 4 * m4];
     kq[ks] = lds_tr_pair(p0, p0 + 8 * kD);
   }
   // S and dP B operands [16 d x 32 keys]: key = kw0 + col, d = 16*ds + 8*g + s
@@ -177,7 +178,7 @@ __global__ void __launch_bounds__(256, 1)
       vb[ds] = __builtin_bit_cast(bf16x8, w);
     }
   }
-  __syncthreads();   // the staging area is reused below
+  __syncthreads();
 
   f32x16 dv[4], dk[4];
 #pragma unroll
@@ -200,7 +201,7 @@ __global__ void __launch_bounds__(256, 1)
   // HBM -> LDS copy of the Q / G_f / G_s tiles of one iteration: 24 (or 16)
   // 1 KiB instructions, 6 per wave; lane l fills physical chunk l % 16 of row
   // 4n + l / 16 with the logical chunk stored there.
-  auto load_tiles = [&](int it, int buf) {
+  auto load_tiles = [&](int it, uint16_t* Qd, uint16_t* Fd, uint16_t* Sd) {
     int hq, q0;
     iter_coords(it, hq, q0);
     const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N + q0;
@@ -210,10 +211,11 @@ __global__ void __launch_bounds__(256, 1)
       const int which = n >> 3, n8 = n & 7;
       if ((which == 1 && !kFull) || (which == 2 && !kSparse)) continue;
       const uint16_t* src = which == 0 ? static_cast<const uint16_t*>(a.q) : which == 1 ? a.g_full : a.g_sparse;
+      uint16_t* dst = which == 0 ? Qd : which == 1 ? Fd : Sd;
       const int row = 4 * n8 + (lane >> 4);
       const int cl = swz_t(row, lane & 15);
       __builtin_amdgcn_global_load_lds((const glb_void*)(src + (rowbase + row) * kD + 8 * cl),
-                                       (lds_void*)(tile(buf, which) + n8 * 512), 16, 0, 0);
+                                       (lds_void*)(dst + n8 * 512), 16, 0, 0);
     }
   };
   // row values and this wave's selection word, through registers
@@ -233,27 +235,15 @@ __global__ void __launch_bounds__(256, 1)
   };
 
   uint32_t cur_bits = 0u;
-  if (iters > 0) {
-    load_tiles(0, 0);
-    load_rows(0);
-    if (tid < 4 * kBM) rowv(0)[tid] = prow;
-    cur_bits = pbits;
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  int cur = 0;
-  for (int it = 0; it < iters; ++it) {
+  // one iteration on set (Q, Gf, Gs, dS, rv) while the next streams into (Qn, Fn, Sn, Rn)
+  auto step = [&](int it, const uint16_t* Q, const uint16_t* Gf, const uint16_t* Gs, uint16_t* dS, const float* rv,
+                  uint16_t* Qn, uint16_t* Fn, uint16_t* Sn, float* Rn) {
     int hq, q0;
     iter_coords(it, hq, q0);
     const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N + q0;
-    const uint16_t* Q = tile(cur, 0);
-    const uint16_t* Gf = tile(cur, 1);
-    const uint16_t* Gs = tile(cur, 2);
-    const float* rv = rowv(cur);
-    uint16_t* dS = dSt(cur);
     if (it + 1 < iters) {
-      load_tiles(it + 1, cur ^ 1);
-      load_rows(it + 1);
+      load_rows(it + 1);      // plain loads first: no VMEM load may follow the copies
+      load_tiles(it + 1, Qn, Fn, Sn);
     }
 
     const bool wave_has_pairs = q0 + kBM - 1 >= kw0 && kw0 < N;   // uniform
@@ -341,7 +331,7 @@ __global__ void __launch_bounds__(256, 1)
       for (int a4 = 0; a4 < 4; ++a4)
         *reinterpret_cast<uint2*>(&dS[r * kBM + 8 * swz_s(r, a4) + 4 * g]) = make_uint2(0, 0);
     }
-    if (it + 1 < iters && tid < 4 * kBM) rowv(cur ^ 1)[tid] = prow;
+    if (it + 1 < iters && tid < 4 * kBM) Rn[tid] = prow;
     __builtin_amdgcn_s_waitcnt(0);     // next tiles landed, dS^T written
     __syncthreads();
 
@@ -361,8 +351,21 @@ __global__ void __launch_bounds__(256, 1)
       for (int i = 0; i < 16; ++i)
         unsafeAtomicAdd(dqp + (8 * (i >> 2) + (i & 3)) * kD, scale * (dq0[i] + dq1[i]));
     }
-    cur ^= 1;
     cur_bits = pbits;
+  };
+
+  if (iters > 0) {
+    load_tiles(0, Q0, F0, S0);
+    load_rows(0);
+    if (tid < 4 * kBM) R0[tid] = prow;
+    cur_bits = pbits;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int it = 0; it < iters; it += 2) {
+    step(it, Q0, F0, S0, D0, R0, Q1, F1, S1, R1);
+    if (it + 1 >= iters) break;
+    step(it + 1, Q1, F1, S1, D1, R1, Q0, F0, S0, R0);
   }
 
   // ---- epilogue: dK = scale * dK^T^T, dV (bf16); lane owns key kw0 + col
@@ -398,19 +401,10 @@ void launch_bwd_pre(const Dims& D, const BwdPreArgs& a, float w_sparsity, float 
   timing_end(kKBwdPre, s);
 }
 
-constexpr size_t kBwdLds = 2 * (3 * kBM * kD + kBN * kBM + 2 * 4 * kBM) * sizeof(uint16_t);
-static_assert(kBwdLds >= kBN * kD * sizeof(uint16_t), "key staging must fit");
-
 template <int MODE>
 static void launch_bwd_mode(const Dims& D, const BwdMainArgs& a, hipStream_t s) {
-  static bool granted = false;   // dynamic LDS above 64 KiB must be requested per kernel
-  if (!granted) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_bwd_mfma<MODE>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(kBwdLds));
-    granted = true;
-  }
   dim3 grid(D.B * D.Hkv, (D.N + kBN - 1) / kBN);
-  hipLaunchKernelGGL(k_bwd_mfma<MODE>, grid, dim3(256), kBwdLds, s, a, D.Hq, D.G, D.N, D.block, D.K, D.scale,
+  hipLaunchKernelGGL(k_bwd_mfma<MODE>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.block, D.K, D.scale,
                      D.scale * kLog2e);
 }
 

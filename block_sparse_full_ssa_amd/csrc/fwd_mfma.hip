@@ -67,12 +67,11 @@ __global__ void __launch_bounds__(256, 1)
     k_fwd_mfma(FwdArgs a, int Hq, int G, int N, int block, int nb, int K, float scale_log2, int n_qtiles) {
   constexpr bool kFull = MODE != kModeSparse;
   constexpr bool kSparse = MODE != kModeFull;
-  // dynamic LDS: K tiles [2][64][128], V tiles [2][64][128] (swizzled), then
-  // the selection bits [kBM][W] of the rows and their union [W]
-  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  uint16_t* Kbuf = lds;
-  uint16_t* Vbuf = lds + 2 * kTile;
-  uint32_t* bits = reinterpret_cast<uint32_t*>(lds + 4 * kTile);
+  // K and V tiles [64][128] (swizzled), two of each; separate objects so that
+  // the compiler can tell the tile being read from the one being filled
+  __shared__ __attribute__((aligned(16))) uint16_t K0[kTile], K1[kTile], V0[kTile], V1[kTile];
+  // dynamic LDS: the selection bits [kBM][W] of the rows and their union [W]
+  extern __shared__ __attribute__((aligned(16))) uint32_t bits[];
   const int W = (nb + 31) >> 5;
   uint32_t* anybits = bits + kBM * W;
 
@@ -150,7 +149,7 @@ __global__ void __launch_bounds__(256, 1)
   // 1 KiB instruction per 4 rows; lane l fills physical chunk l % 16 of row
   // 4n + l / 16, so it fetches the logical chunk stored there.  Keys past the
   // end read the last key: finite values that the causal mask removes.
-  auto load_tile = [&](int j, int buf) {
+  auto load_tile = [&](int j, uint16_t* Kd, uint16_t* Vd) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int n = wave * 4 + r;
@@ -159,153 +158,156 @@ __global__ void __launch_bounds__(256, 1)
       const int64_t key = min(j * kBN + row, N - 1);
       const uint16_t* srck = kg + key * kD + 8 * swz_k(row, p);
       const uint16_t* srcv = vg + key * kD + 8 * swz_v(row, p);
-      __builtin_amdgcn_global_load_lds((const glb_void*)srck, (lds_void*)(Kbuf + buf * kTile + n * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const glb_void*)srcv, (lds_void*)(Vbuf + buf * kTile + n * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const glb_void*)srck, (lds_void*)(Kd + n * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const glb_void*)srcv, (lds_void*)(Vd + n * 512), 16, 0, 0);
     }
   };
 
-  int j = MODE == kModeSparse ? next_tile(-1) : 0;
-  int cur = 0;
-  if (j <= j_last) load_tile(j, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  while (j <= j_last) {
-    const uint16_t* Ks = Kbuf + cur * kTile;
-    const uint16_t* Vs = Vbuf + cur * kTile;
+  // one tile: compute on (Ks, Vs) while the next needed tile streams into
+  // (Kn, Vn); returns the index of that next tile
+  auto step = [&](int j, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn) -> int {
     const int jn = MODE == kModeSparse ? next_tile(j) : j + 1;
-    if (jn <= j_last) load_tile(jn, cur ^ 1);
-
-    if (wave_live && j * kBN <= wave_last_q) {
+    if (jn <= j_last) load_tile(jn, Kn, Vn);
+  if (wave_live && j * kBN <= wave_last_q) {
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const int kbase = j * kBN + kh * 32;          // first key of this half
-        if (kbase > wave_last_q) break;               // uniform: later keys are all masked
+    for (int kh = 0; kh < 2; ++kh) {
+      const int kbase = j * kBN + kh * 32;          // first key of this half
+      if (kbase > wave_last_q) break;               // uniform: later keys are all masked
 
-        // selection bit of this half's key block for the lane's query
-        bool sb = false;
-        bool sparse_any = false;
-        if (kSparse) {
-          const int blk = kbase / block;
-          sb = qrow < N && blk < nb && ((bits[(wave * 32 + col) * W + (blk >> 5)] >> (blk & 31)) & 1u);
-          sparse_any = __builtin_amdgcn_readfirstlane(__any(sb) ? 1 : 0) != 0;
-          if (MODE == kModeSparse && !sparse_any) continue;
+      // selection bit of this half's key block for the lane's query
+      bool sb = false;
+      bool sparse_any = false;
+      if (kSparse) {
+        const int blk = kbase / block;
+        sb = qrow < N && blk < nb && ((bits[(wave * 32 + col) * W + (blk >> 5)] >> (blk & 31)) & 1u);
+        sparse_any = __builtin_amdgcn_readfirstlane(__any(sb) ? 1 : 0) != 0;
+        if (MODE == kModeSparse && !sparse_any) continue;
+      }
+
+      // ---- S^T = K Q^T for 32 keys, in log2 units
+      f32x16 s = f32x16{};
+      {
+        const int r = kh * 32 + col;
+#pragma unroll
+        for (int ds = 0; ds < kD / 16; ++ds)
+          s = mfma32x32x16(lds_read8(&Ks[r * kD + 8 * swz_k(r, 2 * ds + g)]), qreg[ds], s);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[i] *= scale_log2;
+      if (kbase + 31 > wave_q0) {                  // uniform: the diagonal needs the causal mask
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kbase + 8 * (i >> 2) + 4 * g + (i & 3);
+          if (key > qrow) s[i] = -INFINITY;
         }
+      }
+      float mx = max16(s);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
 
-        // ---- S^T = K Q^T for 32 keys, in log2 units
-        f32x16 s = f32x16{};
-        {
-          const int r = kh * 32 + col;
+      // ---- new maxima (integers, moved lazily)
+      float mfn = mf, alpha = 1.f;
+      if (kFull) {
+        if (mx > mf + kTau) mfn = ceilf(mx);
+        alpha = fast_exp2(mf - mfn);               // 1, 0 (first update) or an exact power of two
+      }
+      float msn = ms, alpha_s = 1.f;
+      bool rescale = false;
+      if (kSparse && sparse_any) {
+        const float mxs = sb ? mx : -INFINITY;
+        if (mxs > ms + kTau) msn = ceilf(mxs);
+        alpha_s = msn == -INFINITY ? 1.f : fast_exp2(ms - msn);
+        rescale = MODE == kModeDual &&
+                  __builtin_amdgcn_readfirstlane(__any(sb && mfn - msn > 64.f) ? 1 : 0) == 0;
+      }
+
+      // ---- sparse probabilities evaluated directly (sparse-only, or factor too large)
+      bf16x8 ps[2];
+      float sum_s = 0.f;
+      if (kSparse && sparse_any && !rescale) {
 #pragma unroll
-          for (int ds = 0; ds < kD / 16; ++ds)
-            s = mfma32x32x16(lds_read8(&Ks[r * kD + 8 * swz_k(r, 2 * ds + g)]), qreg[ds], s);
-        }
+        for (int st = 0; st < 2; ++st) {
+          float p[8];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) s[i] *= scale_log2;
-        if (kbase + 31 > wave_q0) {                  // uniform: the diagonal needs the causal mask
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kbase + 8 * (i >> 2) + 4 * g + (i & 3);
-            if (key > qrow) s[i] = -INFINITY;
+          for (int e = 0; e < 8; ++e) {
+            p[e] = sb ? fast_exp2(s[8 * st + e] - msn) : 0.f;
+            sum_s += p[e];
           }
+          ps[st] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
         }
-        float mx = max16(s);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      }
 
-        // ---- new maxima (integers, moved lazily)
-        float mfn = mf, alpha = 1.f;
-        if (kFull) {
-          if (mx > mf + kTau) mfn = ceilf(mx);
-          alpha = fast_exp2(mf - mfn);               // 1, 0 (first update) or an exact power of two
+      // ---- full stream
+      bf16x8 pf[2];
+      if (kFull) {
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          s[i] = fast_exp2(s[i] - mfn);
+          sum += s[i];
         }
-        float msn = ms, alpha_s = 1.f;
-        bool rescale = false;
-        if (kSparse && sparse_any) {
-          const float mxs = sb ? mx : -INFINITY;
-          if (mxs > ms + kTau) msn = ceilf(mxs);
-          alpha_s = msn == -INFINITY ? 1.f : fast_exp2(ms - msn);
-          rescale = MODE == kModeDual &&
-                    __builtin_amdgcn_readfirstlane(__any(sb && mfn - msn > 64.f) ? 1 : 0) == 0;
+        lf = lf * alpha + sum;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) of[dt] *= alpha;
         }
-
-        // ---- sparse probabilities evaluated directly (sparse-only, or factor too large)
-        bf16x8 ps[2];
-        float sum_s = 0.f;
-        if (kSparse && sparse_any && !rescale) {
+        mf = mfn;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+          pf[st] = to_bf16x8(s[8 * st], s[8 * st + 1], s[8 * st + 2], s[8 * st + 3], s[8 * st + 4],
+                             s[8 * st + 5], s[8 * st + 6], s[8 * st + 7]);
+      }
+      if (kSparse && sparse_any) {
+        if (rescale) {
+          // exact: the factor is a power of two
+          const float c = sb ? fast_exp2(mfn - msn) : 0.f;
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
             float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-              p[e] = sb ? fast_exp2(s[8 * st + e] - msn) : 0.f;
+              p[e] = s[8 * st + e] * c;
               sum_s += p[e];
             }
             ps[st] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
           }
         }
-
-        // ---- full stream
-        bf16x8 pf[2];
-        if (kFull) {
-          float sum = 0.f;
+        ls = ls * alpha_s + sum_s;
+        if (__any(alpha_s != 1.f)) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            s[i] = fast_exp2(s[i] - mfn);
-            sum += s[i];
-          }
-          lf = lf * alpha + sum;
-          if (__any(alpha != 1.f)) {
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) of[dt] *= alpha;
-          }
-          mf = mfn;
-#pragma unroll
-          for (int st = 0; st < 2; ++st)
-            pf[st] = to_bf16x8(s[8 * st], s[8 * st + 1], s[8 * st + 2], s[8 * st + 3], s[8 * st + 4],
-                               s[8 * st + 5], s[8 * st + 6], s[8 * st + 7]);
+          for (int dt = 0; dt < 4; ++dt) os[dt] *= alpha_s;
         }
-        if (kSparse && sparse_any) {
-          if (rescale) {
-            // exact: the factor is a power of two
-            const float c = sb ? fast_exp2(mfn - msn) : 0.f;
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-              float p[8];
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                p[e] = s[8 * st + e] * c;
-                sum_s += p[e];
-              }
-              ps[st] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
-            }
-          }
-          ls = ls * alpha_s + sum_s;
-          if (__any(alpha_s != 1.f)) {
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) os[dt] *= alpha_s;
-          }
-          ms = msn;
-        }
+        ms = msn;
+      }
 
-        // ---- O^T += V^T P^T over the 32 keys (two k-steps of 16)
+      // ---- O^T += V^T P^T over the 32 keys (two k-steps of 16)
 #pragma unroll
-        for (int st2 = 0; st2 < 2; ++st2) {
-          const int r0 = kh * 32 + st2 * 16 + 4 * gk + srow;   // key row of this lane's first read
-          const int r1 = r0 + 8;
+      for (int st2 = 0; st2 < 2; ++st2) {
+        const int r0 = kh * 32 + st2 * 16 + 4 * gk + srow;   // key row of this lane's first read
+        const int r1 = r0 + 8;
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const int c = 4 * dt + 2 * (grp & 1) + (m4 >> 1);   // logical 16-byte chunk
-            const int e = 4 * (m4 & 1);
-            const bf16x8 va = lds_tr_pair(&Vs[r0 * kD + 8 * swz_v(r0, c) + e], &Vs[r1 * kD + 8 * swz_v(r1, c) + e]);
-            if (kFull) of[dt] = mfma32x32x16(va, pf[st2], of[dt]);
-            if (kSparse && sparse_any) os[dt] = mfma32x32x16(va, ps[st2], os[dt]);
-          }
+        for (int dt = 0; dt < 4; ++dt) {
+          const int c = 4 * dt + 2 * (grp & 1) + (m4 >> 1);   // logical 16-byte chunk
+          const int e = 4 * (m4 & 1);
+          const bf16x8 va = lds_tr_pair(&Vs[r0 * kD + 8 * swz_v(r0, c) + e], &Vs[r1 * kD + 8 * swz_v(r1, c) + e]);
+          if (kFull) of[dt] = mfma32x32x16(va, pf[st2], of[dt]);
+          if (kSparse && sparse_any) os[dt] = mfma32x32x16(va, ps[st2], os[dt]);
         }
       }
     }
+  }
     __builtin_amdgcn_s_waitcnt(0);     // the next tile has landed in LDS
     __syncthreads();
-    cur ^= 1;
-    j = jn;
+    return jn;
+  };
+
+  int j = MODE == kModeSparse ? next_tile(-1) : 0;
+  if (j <= j_last) load_tile(j, K0, V0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  while (j <= j_last) {
+    j = step(j, K0, V0, K1, V1);
+    if (j > j_last) break;
+    j = step(j, K1, V1, K0, V0);
   }
 
   // ---- epilogue
@@ -355,7 +357,7 @@ __global__ void __launch_bounds__(256, 1)
 
 template <int MODE>
 void launch_mode(const Dims& D, const FwdArgs& a, size_t lds, int n_qtiles, float scale_log2, hipStream_t s) {
-  static size_t granted = 0;    // dynamic LDS above 64 KiB must be requested per kernel
+  static size_t granted = 0;    // LDS above 64 KiB in total must be requested per kernel
   if (lds > granted) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fwd_mfma<MODE>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
@@ -366,16 +368,18 @@ void launch_mode(const Dims& D, const FwdArgs& a, size_t lds, int n_qtiles, floa
                      scale_log2, n_qtiles);
 }
 
-size_t lds_bytes(const Dims& D) {
+constexpr size_t kStaticLds = 4 * kTile * sizeof(uint16_t);
+
+size_t lds_bytes(const Dims& D) {   // dynamic part: selection bits
   const int W = (D.nb + 31) / 32;
-  return static_cast<size_t>(4 * kTile) * sizeof(uint16_t) + static_cast<size_t>(kBM * W + W) * sizeof(uint32_t);
+  return static_cast<size_t>(kBM * W + W) * sizeof(uint32_t);
 }
 
 }  // namespace
 
 bool fwd_mfma_supported(const Dims& D) {
   // the selection bits of 128 rows must fit in LDS next to the K/V tiles
-  return D.dtype == 1 && D.d == kD && lds_bytes(D) <= 160 * 1024;
+  return D.dtype == 1 && D.d == kD && kStaticLds + lds_bytes(D) <= 160 * 1024;
 }
 
 void launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s) {
