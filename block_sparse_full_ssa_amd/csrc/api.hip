@@ -68,6 +68,7 @@ static ssa_status_t make_dims(const ssa_shape_t* sh, Dims* D) {
     return fail(SSA_ERR_UNSUPPORTED, "block must be 32, 64 or 128%s");
   if (sh->seqlen % sh->block != 0) return fail(SSA_ERR_SHAPE, "seqlen must be a multiple of block%s");
   const int nb = sh->seqlen / sh->block;
+  if (nb > 4096) return fail(SSA_ERR_UNSUPPORTED, "at most 4096 key blocks (seqlen / block) per sequence%s");
   if (sh->top_k > 64 && sh->top_k < nb)
     return fail(SSA_ERR_UNSUPPORTED, "top_k above 64 is supported only when it selects every block%s");
   const int64_t rows = static_cast<int64_t>(sh->batch) * sh->heads_q * sh->seqlen;
@@ -188,10 +189,10 @@ ssa_status_t ssa_select_blocks(const ssa_shape_t* shape, const void* q, const vo
   if (!q || !k || !sel) return fail(SSA_ERR_NULL, "q, k and sel are required%s");
   if ((st = check_ws(D, 0, SSA_OP_SELECT, ws, ws_bytes)) != SSA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* muT = static_cast<float*>(ws);
-  launch_block_mean(D, k, muT, s);
+  float* mu = static_cast<float*>(ws);
+  launch_block_mean(D, k, mu, s);
   if ((st = launch_status()) != SSA_OK) return st;
-  launch_select(D, q, muT, sel, s);
+  launch_select(D, q, mu, sel, s);
   return launch_status();
 }
 

@@ -47,6 +47,19 @@ __device__ __forceinline__ float wave_max(float x) {
   return x;
 }
 
+// Maximum of an unsigned value over the 64 lanes of a wave, returned to every
+// lane: DPP row shifts build prefix maxima within each row of 16 lanes, row
+// broadcasts carry them across rows, and lane 63 ends with the total.
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t x) {
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x111, 0xf, 0xf, false)));  // row_shr:1
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x112, 0xf, 0xf, false)));  // row_shr:2
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x114, 0xf, 0xf, false)));  // row_shr:4
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x118, 0xf, 0xf, false)));  // row_shr:8
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x142, 0xa, 0xf, false)));  // row_bcast:15
+  x = max(x, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(x), 0x143, 0xc, 0xf, false)));  // row_bcast:31
+  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(x), 63));
+}
+
 // Order-preserving map of a finite fp32 score to an unsigned integer.
 __device__ __forceinline__ uint32_t ordered_bits(float x) {
   uint32_t u = __float_as_uint(x);

@@ -40,8 +40,8 @@ void timing_begin(int kernel, hipStream_t s);
 void timing_end(int kernel, hipStream_t s);
 
 // --- selection (select.hip) ---
-void launch_block_mean(const Dims& D, const void* k, float* muT, hipStream_t s);
-void launch_select(const Dims& D, const void* q, const float* muT, int32_t* sel, hipStream_t s);
+void launch_block_mean(const Dims& D, const void* k, float* mu, hipStream_t s);
+void launch_select(const Dims& D, const void* q, const float* mu, int32_t* sel, hipStream_t s);
 
 // --- generic SIMT kernels (simt.hip): every supported shape, fp32 and bf16 ---
 struct FwdArgs {

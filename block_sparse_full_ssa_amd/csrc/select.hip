@@ -8,11 +8,10 @@
 // a tie.  sel rows are written ascending, padded with -1.
 //
 // Two kernels:
-//   block_mean: mean of each key block, stored transposed (muT[bc][dim][j]) so
-//               that lanes reading consecutive blocks read consecutive words;
-//   select:     one workgroup per (head, R rows of one query block); scores
-//               for all candidates land in LDS, then each wave ranks its rows
-//               with repeated 64-bit wave-max reductions of (score, -index).
+//   block_mean: mean of each key block, fp32, [B*Hkv][nb][d];
+//   select:     one workgroup per (head, up to 64 rows of one query block);
+//               candidate scores are computed chunk by chunk into LDS, then a
+//               wave ranks each row by a bitwise threshold search (see below).
 
 #include "common.h"
 #include "internal.h"
@@ -20,7 +19,7 @@
 namespace ssa {
 
 template <typename T>
-__global__ void __launch_bounds__(128) k_block_mean(const T* __restrict__ k, float* __restrict__ muT,
+__global__ void __launch_bounds__(128) k_block_mean(const T* __restrict__ k, float* __restrict__ mu,
                                                     int N, int d, int block, int nb) {
   const int j = blockIdx.x;          // key block
   const int64_t bc = blockIdx.y;     // batch * Hkv + kv head
@@ -29,122 +28,221 @@ __global__ void __launch_bounds__(128) k_block_mean(const T* __restrict__ k, flo
   for (int c = threadIdx.x; c < d; c += blockDim.x) {
     float acc = 0.f;
     for (int r = 0; r < block; ++r) acc += to_f32(src[static_cast<int64_t>(r) * d + c]);
-    muT[(bc * d + c) * nb + j] = acc * inv;
+    mu[(bc * nb + j) * d + c] = acc * inv;
   }
 }
 
-void launch_block_mean(const Dims& D, const void* k, float* muT, hipStream_t s) {
+void launch_block_mean(const Dims& D, const void* k, float* mu, hipStream_t s) {
   dim3 grid(D.nb, D.B * D.Hkv);
   timing_begin(kKBlockMean, s);
   if (D.dtype == 1)
     hipLaunchKernelGGL(k_block_mean<bf16_t>, grid, dim3(128), 0, s,
-                       static_cast<const bf16_t*>(k), muT, D.N, D.d, D.block, D.nb);
+                       static_cast<const bf16_t*>(k), mu, D.N, D.d, D.block, D.nb);
   else
     hipLaunchKernelGGL(k_block_mean<float>, grid, dim3(128), 0, s,
-                       static_cast<const float*>(k), muT, D.N, D.d, D.block, D.nb);
+                       static_cast<const float*>(k), mu, D.N, D.d, D.block, D.nb);
   timing_end(kKBlockMean, s);
 }
 
-// Rows of one query block handled by a workgroup; the score buffer R x nb
-// fp32 stays within 32 KiB of LDS.
-static int select_rows_per_wg(const Dims& D) {
-  int r = 16;
-  while (r > 1 && static_cast<int64_t>(r) * D.nb * 4 > 32768) r >>= 1;
-  return r;
-}
+constexpr int kSelChunk = 64;     // candidate blocks scored per pass
 
-template <typename T>
-__global__ void __launch_bounds__(256) k_select(const T* __restrict__ q, const float* __restrict__ muT,
+// One workgroup (256 threads) per R rows of one query block (R divides the
+// block and R x nb fp32 scores fit in 64 KiB); the rows share the candidate
+// blocks j < i.
+//  1. Scores: candidates stream through in chunks of 64; each thread computes
+//     a tile of R/16 rows x 4 candidates (q . mu in fp32, sequential over the
+//     head dimension) into the row's score line in LDS.
+//  2. Ranking, in registers: lane l of a wave holds the scores of candidates
+//     l, l + 64, ..., l + 64 (TM - 1) of a row as order-preserving unsigned
+//     codes.  A 32-step bitwise search (one ballot and popcount per register
+//     per step) finds the largest code c with at least top_k - 1 candidates
+//     >= c: the (top_k - 1)-th largest score.  Every candidate above c is
+//     kept, and candidates equal to c fill the remaining places lowest index
+//     first.  Candidate order is (register, lane) = block order, so prefix
+//     counts of the ballots place the winners ascending.
+template <typename T, int TM>
+__global__ void __launch_bounds__(256) k_select(const T* __restrict__ q, const float* __restrict__ mu_all,
                                                 int32_t* __restrict__ sel, int Hq, int G, int N,
                                                 int d, int block, int nb, int K, int R) {
-  extern __shared__ float smem[];
-  float* qs = smem;                 // [R][d]
-  float* scores = smem + R * d;     // [R][nb]
+  // LDS: q rows [R][d + 4], candidate block means [64][d + 4], scores [R][nb]
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  const int dp = d + 4;
+  float* qs = smem;
+  float* mus = qs + R * dp;
+  float* scores = mus + kSelChunk * dp;
   const int bh = blockIdx.y;
   const int b = bh / Hq, h = bh % Hq;
   const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
   const int t0 = blockIdx.x * R;    // R divides block, so all rows share i
   const int i = t0 / block;         // own block = number of candidates
   const int keep = min(K - 1, i);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const T* qrow0 = q + (static_cast<int64_t>(bh) * N + t0) * d;
   int32_t* out0 = sel + (static_cast<int64_t>(bh) * N + t0) * K;
 
-  if (keep == i) {
-    // every earlier block is kept: 0, 1, ..., i, then padding
-    for (int e = threadIdx.x; e < R * K; e += blockDim.x) {
-      int slot = e % K;
-      out0[e] = slot <= i ? slot : -1;
+  if (keep == i || keep == 0) {
+    // nothing to rank: every earlier block (keep == i) or none (top_k == 1)
+    for (int e = tid; e < R * K; e += blockDim.x) {
+      const int slot = e % K;
+      out0[e] = slot < keep ? slot : (slot == keep ? i : -1);
     }
     return;
   }
 
-  for (int e = threadIdx.x; e < R * d; e += blockDim.x) qs[e] = to_f32(qrow0[e]);
-  __syncthreads();
+  for (int e = tid; e < R * d / 8; e += blockDim.x) {
+    const int r = (e * 8) / d, c0 = (e * 8) % d;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) qs[r * dp + c0 + u] = to_f32(qrow0[r * d + c0 + u]);
+  }
 
-  // scores[r][j] = q_r . mu_j, sequential fp32 FMA over the head dimension
-  const float* mu = muT + bc * d * nb;
-  for (int j0 = 0; j0 < i; j0 += 64) {
-    const int j = j0 + lane;
-    if (j < i) {
-      for (int r = wave; r < R; r += 4) {
-        float acc = 0.f;
-        const float* qr = qs + r * d;
-        for (int c = 0; c < d; ++c) acc = fmaf(qr[c], mu[static_cast<int64_t>(c) * nb + j], acc);
-        scores[r * nb + j] = acc;
+  // ---- 1. scores
+  const float* mu = mu_all + bc * nb * d;
+  const int rpt = R >= 16 ? R >> 4 : 1;   // rows per scoring thread
+  const int rg = tid >> 4, cg = tid & 15;
+  for (int j0 = 0; j0 < i; j0 += kSelChunk) {
+    const int nc = min(kSelChunk, i - j0);
+    __syncthreads();                // q staged; previous chunk's means consumed
+    for (int e = tid; e < kSelChunk * d / 4; e += blockDim.x) {
+      const int cc = (e * 4) / d, dd = (e * 4) % d;
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (cc < nc) v = *reinterpret_cast<const float4*>(mu + static_cast<int64_t>(j0 + cc) * d + dd);
+      *reinterpret_cast<float4*>(mus + cc * dp + dd) = v;
+    }
+    __syncthreads();
+    if (rg * rpt < R) {
+      float acc[4][4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = 0.f;
+      for (int dd = 0; dd < d; dd += 4) {
+        float4 mv[4], qv[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mv[c] = *reinterpret_cast<const float4*>(mus + (4 * cg + c) * dp + dd);
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+          if (a < rpt) qv[a] = *reinterpret_cast<const float4*>(qs + (rg * rpt + a) * dp + dd);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          if (a < rpt) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              acc[a][c] = fmaf(qv[a].x, mv[c].x, acc[a][c]);
+              acc[a][c] = fmaf(qv[a].y, mv[c].y, acc[a][c]);
+              acc[a][c] = fmaf(qv[a].z, mv[c].z, acc[a][c]);
+              acc[a][c] = fmaf(qv[a].w, mv[c].w, acc[a][c]);
+            }
+          }
+        }
       }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        if (a < rpt)
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (4 * cg + c < nc) scores[(rg * rpt + a) * nb + j0 + 4 * cg + c] = acc[a][c];
     }
   }
   __syncthreads();
 
-  for (int r = wave; r < R; r += 4) {
-    float* sc = scores + r * nb;
-    // best candidate of this lane: largest score, then smallest index
-    auto lane_best = [&]() -> uint64_t {
-      uint64_t best = 0;
-      for (int j = lane; j < i; j += 64) {
-        float v = sc[j];
-        if (v != -INFINITY) {
-          uint64_t key = (static_cast<uint64_t>(ordered_bits(v)) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(j));
-          best = key > best ? key : best;
+  // ---- 2. ranking, RW rows per wave at a time
+  constexpr int RW = TM <= 8 ? 2 : 1;
+  const int nt = (i + 63) >> 6;     // registers holding candidates of this block
+  for (int r0 = wave * RW; r0 < R; r0 += 4 * RW) {
+    uint32_t u[RW][TM];
+#pragma unroll
+    for (int w = 0; w < RW; ++w)
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const int j = 64 * t + lane;
+        // + 0.0f turns -0 into +0, so the two zeros tie as the values do
+        u[w][t] = (t < nt && j < i) ? ordered_bits(scores[(r0 + w) * nb + j] + 0.0f) : 0u;
+      }
+    // codes of absent candidates are 0, below every threshold tried (>= 1)
+    uint32_t th[RW];
+#pragma unroll
+    for (int w = 0; w < RW; ++w) th[w] = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+#pragma unroll
+      for (int w = 0; w < RW; ++w) {
+        const uint32_t c = th[w] | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) cnt += __popcll(__ballot(u[w][t] >= c));
+        th[w] = cnt >= keep ? c : th[w];
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < RW; ++w) {
+      int32_t* out = out0 + static_cast<int64_t>(r0 + w) * K;
+      int need = keep;              // places left for codes equal to th
+#pragma unroll
+      for (int t = 0; t < TM; ++t) need -= __popcll(__ballot(u[w][t] > th[w]));
+      int base = 0;
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        {
+          uint64_t eq = __ballot(u[w][t] == th[w]);
+          if (__popcll(eq) > need) {    // keep only the `need` lowest lanes
+            uint64_t take = 0;
+            for (int n = 0; n < need; ++n) {
+              const uint64_t low = eq & (~eq + 1);
+              take |= low;
+              eq ^= low;
+            }
+            eq = take;
+          }
+          need -= __popcll(eq);
+          const uint64_t won = __ballot(u[w][t] > th[w]) | eq;
+          if ((won >> lane) & 1) {
+            const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(won >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(won), 0));
+            out[base + below] = 64 * t + lane;
+          }
+          base += __popcll(won);
         }
       }
-      return best;
-    };
-    uint64_t mine = lane_best();
-    int chosen = 0x7fffffff;        // lane m holds the m-th winner
-    for (int m = 0; m < keep; ++m) {
-      uint64_t top = wave_max_u64(mine);
-      int j = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(top));
-      if (lane == m) chosen = j;
-      if ((j & 63) == lane) {       // owner removes it and rescans
-        sc[j] = -INFINITY;
-        mine = lane_best();
-      }
+      for (int slot = keep + lane; slot < K; slot += 64) out[slot] = (slot == keep) ? i : -1;
     }
-    // ascending order: rank of each winner among the winners
-    int rank = 0;
-    for (int m = 0; m < keep; ++m) {
-      int other = __shfl(chosen, m, 64);
-      rank += (other < chosen) ? 1 : 0;
-    }
-    int32_t* out = out0 + static_cast<int64_t>(r) * K;
-    if (lane < keep) out[rank] = chosen;
-    for (int slot = keep + lane; slot < K; slot += 64) out[slot] = (slot == keep) ? i : -1;
   }
 }
 
-void launch_select(const Dims& D, const void* q, const float* muT, int32_t* sel, hipStream_t s) {
-  const int R = select_rows_per_wg(D);
+template <typename T, int TM>
+static void launch_select_tm(const Dims& D, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
+  int R = D.block < 64 ? D.block : 64;
+  while (R > 4 && static_cast<size_t>(R) * D.nb * sizeof(float) > 65536) R >>= 1;
   dim3 grid(D.N / R, D.B * D.Hq);
-  size_t lds = static_cast<size_t>(R) * (D.d + D.nb) * sizeof(float);
+  const size_t lds =
+      (static_cast<size_t>(R + kSelChunk) * (D.d + 4) + static_cast<size_t>(R) * D.nb) * sizeof(float);
+  static size_t granted = 0;     // above 64 KiB of LDS must be requested
+  if (lds > granted) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_select<T, TM>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    granted = lds;
+  }
+  hipLaunchKernelGGL((k_select<T, TM>), grid, dim3(256), lds, s, static_cast<const T*>(q), mu, sel, D.Hq, D.G,
+                     D.N, D.d, D.block, D.nb, D.K, R);
+}
+
+// TM = registers per lane for a row's candidates: ceil(nb / 64), rounded up
+// to a power of two (nb <= 4096).
+template <typename T>
+static void launch_select_t(const Dims& D, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
+  const int tm = (D.nb + 63) / 64;
+  if (tm <= 1) launch_select_tm<T, 1>(D, q, mu, sel, s);
+  else if (tm <= 2) launch_select_tm<T, 2>(D, q, mu, sel, s);
+  else if (tm <= 4) launch_select_tm<T, 4>(D, q, mu, sel, s);
+  else if (tm <= 8) launch_select_tm<T, 8>(D, q, mu, sel, s);
+  else if (tm <= 16) launch_select_tm<T, 16>(D, q, mu, sel, s);
+  else if (tm <= 32) launch_select_tm<T, 32>(D, q, mu, sel, s);
+  else launch_select_tm<T, 64>(D, q, mu, sel, s);
+}
+
+void launch_select(const Dims& D, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
   timing_begin(kKSelect, s);
-  if (D.dtype == 1)
-    hipLaunchKernelGGL(k_select<bf16_t>, grid, dim3(256), lds, s, static_cast<const bf16_t*>(q), muT, sel,
-                       D.Hq, D.G, D.N, D.d, D.block, D.nb, D.K, R);
-  else
-    hipLaunchKernelGGL(k_select<float>, grid, dim3(256), lds, s, static_cast<const float*>(q), muT, sel,
-                       D.Hq, D.G, D.N, D.d, D.block, D.nb, D.K, R);
+  if (D.dtype == 1) launch_select_t<bf16_t>(D, q, mu, sel, s);
+  else launch_select_t<float>(D, q, mu, sel, s);
   timing_end(kKSelect, s);
 }
 

@@ -85,7 +85,8 @@ typedef struct {
   int32_t batch;          /* B >= 1                                  */
   int32_t heads_q;        /* Hq >= 1                                 */
   int32_t group;          /* G = Hq / Hkv >= 1, divides Hq           */
-  int32_t seqlen;         /* N >= block, N % block == 0              */
+  int32_t seqlen;         /* N >= block, N % block == 0,
+                             N / block <= 4096 (else UNSUPPORTED)   */
   int32_t head_dim;       /* d: 64 or 128                            */
   int32_t block;          /* key block size: 32, 64 or 128           */
   int32_t top_k;          /* selected blocks per query incl. own, >= 1;

@@ -66,6 +66,7 @@ FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails va
     (dict(block=48), 3),
     (dict(dtype=5), 3),
     (dict(top_k=65, seqlen=64 * 100), 3),
+    (dict(seqlen=64 * 4097), 3),       # more than 4096 key blocks
 ])
 def test_shape_errors(L, kw, status):
     s = _shape(**kw)
