@@ -9,8 +9,9 @@ HBM before timing starts.
 
 Reported (one JSON line): algorithmic TFLOP/s of the step, tokens/s, the
 roofline of the dominant kernel (its algorithmic flops per launch over its
-HIP-event-timed average launch), and the CPU oracle timed on a bounded
-sample of the same workload.
+HIP-event-timed average launch), the CPU oracle timed on a bounded sample of
+the same workload, the FULL_ONLY fwd+bwd rate on the same layer and the
+sparse-stream forward speedup t(FULL_ONLY fwd) / t(SPARSE_ONLY fwd).
 
 Algorithmic work (FlashAttention convention, recompute included): per causal
 (query, key) pair 4d flops forward and 10d backward, counted for the full
@@ -54,6 +55,8 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--sweep", action="store_true", help="also time every top_k of the workload's sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-single-stream", action="store_true",
+                    help="skip the FULL_ONLY / SPARSE_ONLY measurements")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows in the CPU-oracle sample")
     return ap.parse_args()
 
@@ -85,6 +88,54 @@ def run_steps(ssa, q, k, v, dout, wl, K, modes, steps, warmup):
     ssa.timing_enable(False)
     del out
     return (t1 - t0) * 1000.0 / steps, kernels
+
+
+def time_calls(fn, reps, warm=1):
+    """Wall-clock milliseconds per call of ``fn`` (GPU work included), after warm-up."""
+    import torch
+
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1000.0 / reps
+
+
+def single_stream(ssa, q, k, v, dout, wl, ks, reps):
+    """FULL_ONLY fwd+bwd TFLOP/s (14 d P_full B Hq per step) and, per top_k,
+    the sparse-stream forward speedup t(FULL_ONLY fwd) / t(SPARSE_ONLY fwd)
+    next to P_full / P_sparse and N / (top_k block)."""
+    B, Hq, N, d = q.shape
+    blk = wl.block
+    pf, _ = pairs(N, blk, wl.top_k)
+
+    def full_step():
+        f = ssa.ssa_attn_fwd(q, k, v, None, blk, wl.top_k, ssa.FULL_ONLY)
+        ssa.ssa_attn_bwd(q, k, v, None, f, dout, blk, wl.top_k, ssa.FULL_ONLY)
+
+    ms_full = time_calls(full_step, reps)
+    ms_full_fwd = time_calls(lambda: ssa.ssa_attn_fwd(q, k, v, None, blk, wl.top_k, ssa.FULL_ONLY), reps)
+    fl = 14.0 * d * pf * B * Hq
+    out = {"full_only": {"ms_per_step": round(ms_full, 3), "TFLOP/s": round(fl / (ms_full / 1e3) / 1e12, 2),
+                         "frac_of_bf16_peak": round(fl / (ms_full / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "fwd_ms": round(ms_full_fwd, 3),
+                         "step": "FULL_ONLY fwd + bwd, 14 d P_full B Hq flops"}}
+    sp = {}
+    for kk in ks:
+        sel = ssa.ssa_select_blocks(q, k, blk, kk)
+        ms_sel = time_calls(lambda: ssa.ssa_select_blocks(q, k, blk, kk), reps)
+        ms_sp = time_calls(lambda: ssa.ssa_attn_fwd(q, k, v, sel, blk, kk, ssa.SPARSE_ONLY), reps)
+        a, b = pairs(N, blk, kk)
+        sp[str(kk)] = {"sparse_only_fwd_ms": round(ms_sp, 3), "select_ms": round(ms_sel, 3),
+                       "speedup": round(ms_full_fwd / ms_sp, 2),
+                       "speedup_incl_select": round(ms_full_fwd / (ms_sp + ms_sel), 2),
+                       "P_full/P_sparse": round(a / b, 2), "N/(K*block)": round(N / (kk * blk), 2)}
+        del sel
+    out["sparse_fwd_speedup"] = sp
+    return out
 
 
 def cpu_baseline(wl, K, seed, rows):
@@ -181,6 +232,11 @@ def main():
             sweep[str(kk)] = {"ms_per_step": round(m2, 3),
                               "TFLOP/s": round(14.0 * d * (a + b) * B * Hq / (m2 / 1000) / 1e12, 2)}
 
+    single = None
+    if not args.no_single_stream:
+        ks = list(wl.top_k_sweep) if (args.sweep and wl.top_k_sweep) else [K]
+        single = single_stream(ssa, q, k, v, dout, wl, ks, max(3, args.steps // 2))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, K, args.seed, min(args.cpu_rows, N))
@@ -208,6 +264,8 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
     }
+    if single:
+        line.update(single)
     if sweep:
         line["top_k_sweep"] = sweep
     print(json.dumps(line), flush=True)

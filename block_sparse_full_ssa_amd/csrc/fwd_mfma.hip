@@ -62,8 +62,10 @@ __device__ __forceinline__ float max16(const f32x16& v) {
   return m;
 }
 
+// Two workgroups per CU (256 VGPRs and 68 KiB of LDS each at nb <= 256), so
+// one wave's softmax overlaps the other wave's matrix work on every SIMD.
 template <int MODE>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(256, 2)
     k_fwd_mfma(FwdArgs a, int Hq, int G, int N, int block, int nb, int K, float scale_log2, int n_qtiles) {
   constexpr bool kFull = MODE != kModeSparse;
   constexpr bool kSparse = MODE != kModeFull;
