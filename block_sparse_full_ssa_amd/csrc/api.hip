@@ -32,7 +32,7 @@ static bool g_timing = false;
 static std::vector<TimingRec> g_recs;
 static const char* kKernelNames[kKernelCount] = {
     "block_mean", "select", "fwd_simt", "fwd_mfma", "loss_reduce",
-    "bwd_pre",    "bwd_simt", "bwd_mfma", "convert", "zero"};
+    "bwd_pre",    "bwd_simt", "bwd_mfma", "convert", "zero", "bucket", "sparse_part", "sparse_merge"};
 
 void timing_begin(int kernel, hipStream_t s) {
   if (!g_timing) return;
@@ -75,6 +75,8 @@ static ssa_status_t make_dims(const ssa_shape_t* sh, Dims* D) {
   if (rows * sh->head_dim >= (static_cast<int64_t>(1) << 40) || rows / 4 >= (static_cast<int64_t>(1) << 31))
     return fail(SSA_ERR_SHAPE, "layer too large%s");
   if (!(sh->softmax_scale == sh->softmax_scale)) return fail(SSA_ERR_SHAPE, "softmax_scale is NaN%s");
+  if (rows * (sh->top_k < nb ? sh->top_k : nb) >= (static_cast<int64_t>(1) << 31))
+    return fail(SSA_ERR_SHAPE, "layer too large (rows * min(top_k, N / block) must stay below 2^31)%s");
   D->B = sh->batch;
   D->Hq = sh->heads_q;
   D->G = sh->group;
@@ -105,12 +107,31 @@ struct Carver {
   }
 };
 
+static Buckets carve_buckets(const Dims& D, Carver& c) {
+  Buckets b{};
+  const int64_t nbk = static_cast<int64_t>(D.B) * D.Hkv * D.nb;
+  b.mask = c.take<uint32_t>(bucket_mask_words(D) * sizeof(uint32_t));
+  b.count = c.take<int32_t>(nbk * sizeof(int32_t));
+  b.offs = c.take<int32_t>((nbk + 1) * sizeof(int32_t));
+  b.rows = c.take<int32_t>(bucket_capacity(D) * sizeof(int32_t));
+  b.wpos = c.take<int32_t>(bucket_mask_words(D) * sizeof(int32_t));
+  return b;
+}
+
 struct FwdWs {
   float* row_sq;
+  Buckets bk;                 // sparse-only forward on buckets
+  uint16_t* part_o;
+  float* part_lse;
 };
 static FwdWs carve_fwd(const Dims& D, int mode, Carver& c) {
   FwdWs w{};
   if (mode == kDualFull || mode == kDualSparse) w.row_sq = c.take<float>(D.rows() * sizeof(float));
+  if (mode == kSparseOnly && sparse_fwd_supported(D)) {
+    w.bk = carve_buckets(D, c);
+    w.part_o = c.take<uint16_t>(bucket_capacity(D) * D.d * sizeof(uint16_t));
+    w.part_lse = c.take<float>(bucket_capacity(D) * sizeof(float));
+  }
   return w;
 }
 
@@ -214,6 +235,14 @@ ssa_status_t ssa_attn_fwd(const ssa_shape_t* shape, int32_t mode, const void* q,
   hipStream_t s = static_cast<hipStream_t>(stream);
   Carver c{static_cast<char*>(ws)};
   FwdWs w = carve_fwd(D, mode, c);
+  if (mode == kSparseOnly && sparse_fwd_supported(D)) {
+    launch_buckets(D, sel, w.bk, s);
+    if ((st = launch_status()) != SSA_OK) return st;
+    SparseFwdArgs p{q, k, v, sel, w.bk.mask, w.bk.offs, w.bk.rows, w.bk.wpos, w.part_o, w.part_lse, h_sparse,
+                    lse_sparse};
+    launch_sparse_fwd(D, p, s);
+    return launch_status();
+  }
   FwdArgs a{q, k, v, sel, h_full, h_sparse, lse_full, lse_sparse, delta, w.row_sq, mode};
   if (fwd_mfma_supported(D)) launch_fwd_mfma(D, a, s);
   else launch_fwd_simt(D, a, s);

@@ -1,0 +1,162 @@
+// Key-block buckets: the query rows that selected each key block.
+//
+// The sparse stream's support (Sintesi Tecnica, section 2: each query keeps
+// its top-scoring key blocks plus its own block) is a per-row list of
+// blocks.  The sparse-only kernels work key-block-stationary instead: for
+// every (batch, KV head c, key block j) they need the rows of the G query
+// heads of group c whose selection holds j, gathered into 32-row batches.
+// Selections of neighbouring rows need not overlap, so a row-stationary
+// tile would touch almost every key block; a bucket keeps the matrix work
+// proportional to the selected pairs.
+//
+// Built in four steps, deterministic (no global atomics):
+//   mask:  per (b, h, 32-row tile) of sel, one 32-bit row mask per key block
+//          -> mask[b, c][j][h % G][tile]   (bit r: row 32 tile + r selected j)
+//   count: rows per bucket (popcounts of the bucket's masks);
+//   scan:  exclusive prefix of the counts -> offs (one workgroup);
+//   fill:  entries (h % G) * N + t of bucket (b, c, j), ordered by (head, t),
+//          at rows[offs[(b*Hkv + c)*nb + j] ...], and for every mask word the
+//          position of its first entry (wpos, same layout as mask), so that
+//          the entry of (row, j) is wpos[word] + popcount of the word's bits
+//          below the row.
+// Entries of sel that are negative or above the row's own block are ignored.
+
+#include "common.h"
+#include "internal.h"
+
+namespace ssa {
+namespace {
+
+constexpr int kScanThreads = 256;
+
+// Exclusive prefix sum over the 256 threads of a workgroup; *total receives
+// the sum.  scratch: 4 ints of LDS.
+__device__ __forceinline__ int block_exclusive_scan(int x, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  int base = 0, sum = 0;
+#pragma unroll
+  for (int w = 0; w < kScanThreads / 64; ++w) {
+    const int v = scratch[w];
+    base += w < wave ? v : 0;
+    sum += v;
+  }
+  __syncthreads();
+  *total = sum;
+  return base + incl - x;
+}
+
+__global__ void __launch_bounds__(64) k_bucket_mask(const int32_t* __restrict__ sel, uint32_t* __restrict__ mask,
+                                                    int Hq, int G, int N, int nb, int K, int block) {
+  extern __shared__ uint32_t words[];    // [own block + 1]
+  const int qt = blockIdx.x, bh = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int nqt = N / 32;
+  const int b = bh / Hq, h = bh % Hq, Hkv = Hq / G;
+  const int c = h / G, hl = h % G;
+  const int t0 = qt * 32;
+  const int own = t0 / block;            // block >= 32 divides into whole tiles
+  for (int j = lane; j <= own; j += 64) words[j] = 0u;
+  __syncthreads();
+  const int32_t* s = sel + (static_cast<int64_t>(bh) * N + t0) * K;
+  for (int e = lane; e < 32 * K; e += 64) {
+    const int blk = s[e];
+    if (blk >= 0 && blk <= own) atomicOr(&words[blk], 1u << (e / K));
+  }
+  __syncthreads();
+  uint32_t* out = mask + ((static_cast<int64_t>(b) * Hkv + c) * nb * G + hl) * nqt + qt;
+  for (int j = lane; j <= own; j += 64) out[static_cast<int64_t>(j) * G * nqt] = words[j];
+}
+
+__global__ void __launch_bounds__(kScanThreads) k_bucket_count(const uint32_t* __restrict__ mask,
+                                                               int32_t* __restrict__ count, int G, int N,
+                                                               int nb, int block) {
+  __shared__ int scratch[4];
+  const int j = blockIdx.x, bc = blockIdx.y;
+  const int nqt = N / 32;
+  const int qt0 = j * block / 32;        // earlier rows cannot select block j
+  const uint32_t* m = mask + (static_cast<int64_t>(bc) * nb + j) * G * nqt;
+  int cnt = 0;
+  for (int hl = 0; hl < G; ++hl)
+    for (int qt = qt0 + static_cast<int>(threadIdx.x); qt < nqt; qt += kScanThreads)
+      cnt += __popc(m[static_cast<int64_t>(hl) * nqt + qt]);
+  int total;
+  block_exclusive_scan(cnt, scratch, &total);
+  if (threadIdx.x == 0) count[static_cast<int64_t>(bc) * nb + j] = total;
+}
+
+__global__ void __launch_bounds__(kScanThreads) k_bucket_scan(const int32_t* __restrict__ count,
+                                                              int32_t* __restrict__ offs, int n) {
+  __shared__ int scratch[4];
+  int carry = 0;
+  for (int i0 = 0; i0 < n; i0 += kScanThreads) {
+    const int i = i0 + static_cast<int>(threadIdx.x);
+    const int x = i < n ? count[i] : 0;
+    int total;
+    const int ex = block_exclusive_scan(x, scratch, &total);
+    if (i < n) offs[i] = carry + ex;
+    carry += total;
+  }
+  if (threadIdx.x == 0) offs[n] = carry;
+}
+
+__global__ void __launch_bounds__(kScanThreads) k_bucket_fill(const uint32_t* __restrict__ mask,
+                                                              const int32_t* __restrict__ offs,
+                                                              int32_t* __restrict__ rows,
+                                                              int32_t* __restrict__ wpos, int G, int N, int nb,
+                                                              int block) {
+  __shared__ int scratch[4];
+  const int j = blockIdx.x, bc = blockIdx.y;
+  const int nqt = N / 32;
+  const int qt0 = j * block / 32;
+  const int64_t w0 = (static_cast<int64_t>(bc) * nb + j) * G * nqt;
+  const uint32_t* m = mask + w0;
+  int run = offs[static_cast<int64_t>(bc) * nb + j];
+  for (int hl = 0; hl < G; ++hl) {
+    for (int q0 = qt0; q0 < nqt; q0 += kScanThreads) {
+      const int qt = q0 + static_cast<int>(threadIdx.x);
+      uint32_t w = qt < nqt ? m[static_cast<int64_t>(hl) * nqt + qt] : 0u;
+      int total;
+      int pos = run + block_exclusive_scan(__popc(w), scratch, &total);
+      if (qt < nqt) wpos[w0 + static_cast<int64_t>(hl) * nqt + qt] = pos;
+      while (w) {
+        const int r = __builtin_ctz(w);
+        w &= w - 1;
+        rows[pos++] = hl * N + 32 * qt + r;
+      }
+      run += total;
+    }
+  }
+}
+
+}  // namespace
+
+int64_t bucket_mask_words(const Dims& D) {
+  return static_cast<int64_t>(D.B) * D.Hkv * D.nb * D.G * (D.N / 32);
+}
+
+int64_t bucket_capacity(const Dims& D) {
+  return D.rows() * static_cast<int64_t>(D.K < D.nb ? D.K : D.nb);
+}
+
+void launch_buckets(const Dims& D, const int32_t* sel, const Buckets& bk, hipStream_t s) {
+  const int nbk = D.B * D.Hkv * D.nb;
+  timing_begin(kKBucket, s);
+  hipLaunchKernelGGL(k_bucket_mask, dim3(D.N / 32, D.B * D.Hq), dim3(64), static_cast<size_t>(D.nb) * 4, s, sel,
+                     bk.mask, D.Hq, D.G, D.N, D.nb, D.K, D.block);
+  hipLaunchKernelGGL(k_bucket_count, dim3(D.nb, D.B * D.Hkv), dim3(kScanThreads), 0, s, bk.mask, bk.count, D.G,
+                     D.N, D.nb, D.block);
+  hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(kScanThreads), 0, s, bk.count, bk.offs, nbk);
+  hipLaunchKernelGGL(k_bucket_fill, dim3(D.nb, D.B * D.Hkv), dim3(kScanThreads), 0, s, bk.mask, bk.offs, bk.rows,
+                     bk.wpos, D.G, D.N, D.nb, D.block);
+  timing_end(kKBucket, s);
+}
+
+}  // namespace ssa

@@ -32,6 +32,9 @@ enum KernelId {
   kKBwdMfma,
   kKConvert,
   kKZero,
+  kKBucket,
+  kKSparsePart,
+  kKSparseMerge,
   kKernelCount
 };
 
@@ -98,6 +101,32 @@ struct BwdMainArgs {
 bool bwd_mfma_supported(const Dims& D);
 void launch_bwd_pre(const Dims& D, const BwdPreArgs& a, float w_sparsity, float w_commit, hipStream_t s);
 void launch_bwd_mfma(const Dims& D, const BwdMainArgs& a, hipStream_t s);
+
+// --- key-block buckets (bucket.hip) ---
+struct Buckets {
+  uint32_t* mask;    // [B*Hkv][nb][G][N/32] row masks of each bucket
+  int32_t* count;    // [B*Hkv*nb] rows per bucket
+  int32_t* offs;     // [B*Hkv*nb + 1] exclusive prefix of count
+  int32_t* rows;     // entries (h % G) * N + t, bucket after bucket
+  int32_t* wpos;     // [as mask] position in rows of each mask word's first entry
+};
+int64_t bucket_mask_words(const Dims& D);
+int64_t bucket_capacity(const Dims& D);   // upper bound on the entries: rows * min(K, nb)
+void launch_buckets(const Dims& D, const int32_t* sel, const Buckets& bk, hipStream_t s);
+
+// --- sparse-only forward on buckets (sparse_fwd.hip) ---
+struct SparseFwdArgs {
+  const void *q, *k, *v;
+  const int32_t* sel;
+  const uint32_t* mask;                 // buckets
+  const int32_t *offs, *rows, *wpos;
+  uint16_t* part_o;                     // [bucket entries][d] bf16 partial outputs, bucket order
+  float* part_lse;                      // [bucket entries] partial log-sum-exps (log2 units)
+  void* h_sparse;
+  float* lse_sparse;                    // may be null
+};
+bool sparse_fwd_supported(const Dims& D);
+void launch_sparse_fwd(const Dims& D, const SparseFwdArgs& a, hipStream_t s);
 
 // --- small kernels (misc.hip) ---
 void launch_zero_f32(float* p, int64_t n, hipStream_t s);

@@ -130,6 +130,23 @@ def test_fwd_small_bf16(name, mode):
     _check_fwd(name, wl, out, oracle_fwd(wl, 0, (wl.top_k,), wl.top_k, mode), mode)
 
 
+@pytest.mark.parametrize("top_k", [1, 2, 8, 11])
+def test_sparse_only_fwd_topk_extremes(top_k):
+    """SPARSE_ONLY on key-block buckets when each query keeps only its own
+    block (top_k 1, every bucket holds just its own block's rows), one
+    earlier block, or every block (top_k = N / block and above)."""
+    wl = SMALL["gqa_n512_b64_k4"]
+    ks = (top_k,) if top_k == 2 else ()
+    _say(f"sparse-only fwd top_k {top_k}")
+    (q, k, v), _ = inputs(wl, 0, ks)
+    qd, kd, vd = to_dev(q, k, v)
+    sel = torch.from_numpy(oracle_select(wl, 0, ks, top_k)[0]).to("cuda:0")
+    out = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, top_k, oracle.SPARSE_ONLY)
+    torch.cuda.synchronize()
+    ref = oracle_fwd(wl, 0, ks, top_k, oracle.SPARSE_ONLY)
+    _check_fwd(f"top_k {top_k}", wl, out, ref, oracle.SPARSE_ONLY)
+
+
 @pytest.mark.parametrize("mode", [oracle.DUAL_ACTIVE_SPARSE, oracle.FULL_ONLY, oracle.SPARSE_ONLY])
 def test_fwd_gqa_n4k_full_layer(mode):
     """The 4K GQA layer (16 query / 4 KV heads, d 128, block 64, top_k 16) whole.
