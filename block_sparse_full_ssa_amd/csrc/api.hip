@@ -32,7 +32,8 @@ static bool g_timing = false;
 static std::vector<TimingRec> g_recs;
 static const char* kKernelNames[kKernelCount] = {
     "block_mean", "select", "fwd_simt", "fwd_mfma", "loss_reduce",
-    "bwd_pre",    "bwd_simt", "bwd_mfma", "convert", "zero", "bucket", "sparse_part", "sparse_merge"};
+    "bwd_pre",    "bwd_simt", "bwd_mfma", "convert", "zero", "bucket", "sparse_part", "sparse_merge",
+    "bwd_sparse"};
 
 void timing_begin(int kernel, hipStream_t s) {
   if (!g_timing) return;
@@ -141,7 +142,8 @@ struct BwdWs {
   // MFMA path
   uint16_t *g_full, *g_sparse;
   float *D_full, *D_sparse, *lse2_full, *lse2_sparse, *dq_acc;
-  uint32_t* rowbits;
+  Buckets bk;                 // sparse stream
+  float *dk_part, *dv_part;   // sparse-stream dK / dV in training modes
 };
 static BwdWs carve_bwd(const Dims& D, int mode, Carver& c) {
   BwdWs w{};
@@ -156,7 +158,11 @@ static BwdWs carve_bwd(const Dims& D, int mode, Carver& c) {
       w.g_sparse = c.take<uint16_t>(D.q_elems() * sizeof(uint16_t));
       w.D_sparse = c.take<float>(D.rows() * sizeof(float));
       w.lse2_sparse = c.take<float>(D.rows() * sizeof(float));
-      w.rowbits = c.take<uint32_t>(D.rows() * ((D.nb + 31) / 32) * sizeof(uint32_t));
+      w.bk = carve_buckets(D, c);
+    }
+    if (f && sp) {
+      w.dk_part = c.take<float>(D.kv_elems() * sizeof(float));
+      w.dv_part = c.take<float>(D.kv_elems() * sizeof(float));
     }
     w.dq_acc = c.take<float>(D.q_elems() * sizeof(float));
   } else {
@@ -274,15 +280,25 @@ ssa_status_t ssa_attn_bwd(const ssa_shape_t* shape, int32_t mode, float w_sparsi
   Carver c{static_cast<char*>(ws)};
   BwdWs w = carve_bwd(D, mode, c);
   if (bwd_mfma_supported(D)) {
-    const int W = (D.nb + 31) / 32;
+    // stream gradients, then the sparse stream on key-block buckets (its dK /
+    // dV as fp32 partials when the full stream follows), then the full stream
     BwdPreArgs p{d_out, h_full, h_sparse, lse_full, lse_sparse, w.g_full, w.g_sparse, w.D_full, w.D_sparse,
-                 w.lse2_full, w.lse2_sparse, w.dq_acc, sel, w.rowbits, D.K, W, mode};
+                 w.lse2_full, w.lse2_sparse, w.dq_acc, mode};
     launch_bwd_pre(D, p, w_sparsity, w_commit, s);
     if ((st = launch_status()) != SSA_OK) return st;
-    BwdMainArgs m{q, k, v, sel, w.g_full, w.g_sparse, w.lse2_full, w.lse2_sparse, w.D_full, w.D_sparse,
-                  w.dq_acc, dk, dv, w.rowbits, W, mode};
-    launch_bwd_mfma(D, m, s);
-    if ((st = launch_status()) != SSA_OK) return st;
+    if (mode != kFullOnly) {
+      launch_buckets(D, sel, w.bk, s);
+      if ((st = launch_status()) != SSA_OK) return st;
+      SparseBwdArgs sp{q, k, v, w.bk.offs, w.bk.rows, w.g_sparse, w.lse2_sparse, w.D_sparse, w.dq_acc,
+                       w.dk_part, w.dv_part, dk, dv};
+      launch_bwd_sparse(D, sp, s);
+      if ((st = launch_status()) != SSA_OK) return st;
+    }
+    if (mode != kSparseOnly) {
+      BwdMainArgs m{q, k, v, w.g_full, w.lse2_full, w.D_full, w.dq_acc, dk, dv, w.dk_part, w.dv_part};
+      launch_bwd_mfma(D, m, s);
+      if ((st = launch_status()) != SSA_OK) return st;
+    }
     launch_convert(w.dq_acc, dq, D.dtype, D.q_elems(), s);
     return launch_status();
   }

@@ -1,17 +1,17 @@
-// Backward of SSA dual-stream attention, bf16 MFMA on gfx950.
+// Backward of SSA dual-stream attention, bf16 MFMA on gfx950: the stream
+// gradients and the full stream.
 //
 // Each output receives its own gradient (Sintesi Tecnica, section 2,
 // 'Allineamento Bidirezionale'): the upstream gradient goes to the active
 // stream only, L_sparsity adds (2/M) w_s (h_full - h_sparse) to the full
 // stream and L_commit adds (2/M) w_c (h_sparse - h_full) to the sparse
 // stream (the other output held fixed in each).  With those stream
-// gradients G_f, G_s, both streams are differentiated in one pass that
-// recomputes the shared logits once:
-//   P_X = 2^(S c - lse_X)                          (c = scale * log2 e)
-//   dS  = P_f (G_f V^T - D_f) + P_s (G_s V^T - D_s),  D_X = rowsum(G_X o h_X)
-//   dV  = P_f^T G_f + P_s^T G_s,  dK = scale dS^T Q,  dQ = scale dS K.
-// Keys outside a query's selected blocks have P_s = 0, so they receive
-// gradient through the full stream only.
+// gradients G_f, G_s the two streams are differentiated separately and the
+// results added: the sparse stream on key-block buckets (sparse_bwd.hip),
+// the full stream here:
+//   P   = 2^(S c - lse_f)                          (c = scale * log2 e)
+//   dS  = P (G_f V^T - D_f),  D_f = rowsum(G_f o h_full)
+//   dV  = P^T G_f,  dK = scale dS^T Q,  dQ = scale dS K.
 //
 // Kernels:
 //   bwd_pre:  per row, G_f / G_s in bf16, D_f / D_s from the rounded G, the
@@ -20,8 +20,9 @@
 //             per wave, kept in registers as K and V operands) and walks the
 //             G query heads of the group and every 32-query tile at or after
 //             its keys.  dK and dV accumulate in registers over all of them
-//             (no atomics); dQ of each tile is reduced over the 128 keys
-//             through LDS and added to the fp32 accumulator with atomics;
+//             (no atomics) and leave with the sparse stream's fp32 dK / dV
+//             added; dQ of each tile is reduced over the 128 keys through
+//             LDS and added to the fp32 accumulator with atomics;
 //   convert:  dQ accumulator -> bf16.
 //
 // Layout: the logits are kept as S = Q K^T (lane l owns key l % 32 and 16
@@ -40,8 +41,6 @@ constexpr int kD = 128;
 constexpr int kBN = 128;       // keys per workgroup
 constexpr int kBM = 32;        // queries per iteration
 constexpr float kLog2e = 1.4426950408889634f;
-
-enum { kModeDual = 0, kModeFull = 1, kModeSparse = 2 };
 
 // ---------------------------------------------------------------- bwd_pre --
 __global__ void __launch_bounds__(256)
@@ -83,18 +82,6 @@ __global__ void __launch_bounds__(256)
   *reinterpret_cast<float2*>(a.dq_acc + off) = make_float2(0.f, 0.f);
   Df = wave_sum(Df);
   Ds = wave_sum(Ds);
-  if (has_s) {
-    // bitmask over key blocks of this row's selection (word w covers blocks 32w..32w+31)
-    const int32_t* selr = a.sel + row * a.K;
-    for (int w = lane; w < a.W; w += 64) {
-      uint32_t word = 0u;
-      for (int e = 0; e < a.K; ++e) {
-        const int blk = selr[e];
-        if (blk >= 0 && (blk >> 5) == w) word |= 1u << (blk & 31);
-      }
-      a.rowbits[row * a.W + w] = word;
-    }
-  }
   if (lane == 0) {
     if (has_f) {
       a.D_full[row] = Df;
@@ -117,20 +104,17 @@ __device__ __forceinline__ int swz_s(int r, int c) { return c ^ ((r >> 1) & 3); 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-template <int MODE>
 __global__ void __launch_bounds__(256, 1)
-    k_bwd_mfma(BwdMainArgs a, int Hq, int G, int N, int block, int K, float scale, float scale_log2) {
-  constexpr bool kFull = MODE != kModeSparse;
-  constexpr bool kSparse = MODE != kModeFull;
+    k_bwd_mfma(BwdMainArgs a, int Hq, int G, int N, float scale, float scale_log2) {
   // LDS: the 128 x 128 key tile staged once at start, then two sets of
-  // {Q, G_f, G_s tiles [32][128], dS^T [128][32], row values [4][32] fp32},
-  // each buffer its own object so that the compiler can tell the set being
-  // read from the set being filled by the HBM -> LDS copies
+  // {Q, G_f tiles [32][128], dS^T [128][32], row values [2][32] fp32}, each
+  // buffer its own object so that the compiler can tell the set being read
+  // from the set being filled by the HBM -> LDS copies
   constexpr int kT = kBM * kD;                       // one Q / G tile
   __shared__ __attribute__((aligned(16))) uint16_t Kst[kBN * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t Q0[kT], Q1[kT], F0[kT], F1[kT], S0[kT], S1[kT];
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[kT], Q1[kT], F0[kT], F1[kT];
   __shared__ __attribute__((aligned(16))) uint16_t D0[kBN * kBM], D1[kBN * kBM];
-  __shared__ __attribute__((aligned(16))) float R0[4 * kBM], R1[4 * kBM];
+  __shared__ __attribute__((aligned(16))) float R0[2 * kBM], R1[2 * kBM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -191,111 +175,84 @@ __global__ void __launch_bounds__(256, 1)
   const int nqt = N / kBM;
   const int qt0 = k0 / kBM;                         // first query tile that sees these keys
   const int iters = G * (nqt - qt0);
-  const int wblk = (kw0 < N ? kw0 : N - 1) / block; // key block of this wave (block >= 32)
 
   auto iter_coords = [&](int it, int& hq, int& q0) {
     const int hg = it / (nqt - qt0);
     hq = c * G + hg;
     q0 = (qt0 + it % (nqt - qt0)) * kBM;
   };
-  // HBM -> LDS copy of the Q / G_f / G_s tiles of one iteration: 24 (or 16)
-  // 1 KiB instructions, 6 per wave; lane l fills physical chunk l % 16 of row
+  // HBM -> LDS copy of the Q / G_f tiles of one iteration: 16 1 KiB
+  // instructions, 4 per wave; lane l fills physical chunk l % 16 of row
   // 4n + l / 16 with the logical chunk stored there.
-  auto load_tiles = [&](int it, uint16_t* Qd, uint16_t* Fd, uint16_t* Sd) {
+  auto load_tiles = [&](int it, uint16_t* Qd, uint16_t* Fd) {
     int hq, q0;
     iter_coords(it, hq, q0);
     const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N + q0;
 #pragma unroll
-    for (int r = 0; r < 6; ++r) {
-      const int n = wave * 6 + r;                   // 0..23, uniform
+    for (int r = 0; r < 4; ++r) {
+      const int n = wave * 4 + r;                   // 0..15, uniform
       const int which = n >> 3, n8 = n & 7;
-      if ((which == 1 && !kFull) || (which == 2 && !kSparse)) continue;
-      const uint16_t* src = which == 0 ? static_cast<const uint16_t*>(a.q) : which == 1 ? a.g_full : a.g_sparse;
-      uint16_t* dst = which == 0 ? Qd : which == 1 ? Fd : Sd;
+      const uint16_t* src = which == 0 ? static_cast<const uint16_t*>(a.q) : a.g_full;
+      uint16_t* dst = which == 0 ? Qd : Fd;
       const int row = 4 * n8 + (lane >> 4);
       const int cl = swz_t(row, lane & 15);
       __builtin_amdgcn_global_load_lds((const glb_void*)(src + (rowbase + row) * kD + 8 * cl),
                                        (lds_void*)(dst + n8 * 512), 16, 0, 0);
     }
   };
-  // row values and this wave's selection word, through registers
+  // row values (lse2, D) through registers
   float prow = 0.f;
-  uint32_t pbits = 0u;
   auto load_rows = [&](int it) {
     int hq, q0;
     iter_coords(it, hq, q0);
     const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N + q0;
-    if (tid < 4 * kBM) {
+    if (tid < 2 * kBM) {
       const int which = tid >> 5, r = tid & 31;
-      const float* src = which == 0 ? a.lse2_full : which == 1 ? a.lse2_sparse : which == 2 ? a.D_full : a.D_sparse;
-      const bool need = (which & 1) ? kSparse : kFull;
-      prow = need ? src[rowbase + r] : (which < 2 ? INFINITY : 0.f);
+      prow = (which == 0 ? a.lse2_full : a.D_full)[rowbase + r];
     }
-    if (kSparse) pbits = a.rowbits[(rowbase + col) * a.W + (wblk >> 5)];
   };
 
-  uint32_t cur_bits = 0u;
-  // one iteration on set (Q, Gf, Gs, dS, rv) while the next streams into (Qn, Fn, Sn, Rn)
-  auto step = [&](int it, const uint16_t* Q, const uint16_t* Gf, const uint16_t* Gs, uint16_t* dS, const float* rv,
-                  uint16_t* Qn, uint16_t* Fn, uint16_t* Sn, float* Rn) {
+  // one iteration on set (Q, Gf, dS, rv) while the next streams into (Qn, Fn, Rn)
+  auto step = [&](int it, const uint16_t* Q, const uint16_t* Gf, uint16_t* dS, const float* rv, uint16_t* Qn,
+                  uint16_t* Fn, float* Rn) {
     int hq, q0;
     iter_coords(it, hq, q0);
     const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N + q0;
     if (it + 1 < iters) {
       load_rows(it + 1);      // plain loads first: no VMEM load may follow the copies
-      load_tiles(it + 1, Qn, Fn, Sn);
+      load_tiles(it + 1, Qn, Fn);
     }
 
     const bool wave_has_pairs = q0 + kBM - 1 >= kw0 && kw0 < N;   // uniform
-    // rows of this tile that selected this wave's key block (ballot: uniform)
-    uint32_t smask = 0u;
-    if (kSparse) smask = static_cast<uint32_t>(__ballot(lane < 32 && ((cur_bits >> (wblk & 31)) & 1u)));
-    const bool do_sparse = kSparse && smask != 0u;
     const bool diag = q0 < kw0 + 31;                               // some key > some query
 
     if (wave_has_pairs) {
-      // ---- S = Q K^T, dP_f = G_f V^T, dP_s = G_s V^T  [32 q x 32 keys], three
-      // independent accumulation chains interleaved; lane: key col, queries 8(i/4)+4g+(i%4)
-      f32x16 s = f32x16{}, dpf = f32x16{}, dps = f32x16{};
+      // ---- S = Q K^T, dP = G_f V^T  [32 q x 32 keys], two independent
+      // accumulation chains interleaved; lane: key col, queries 8(i/4)+4g+(i%4)
+      f32x16 s = f32x16{}, dpf = f32x16{};
       const int ra = col * kD;
 #pragma unroll
       for (int ds = 0; ds < kD / 16; ++ds) {
         const int off = ra + 8 * swz_t(col, 2 * ds + g);
         s = mfma32x32x16(lds_read8(&Q[off]), kb[ds], s);
-        if (kFull) dpf = mfma32x32x16(lds_read8(&Gf[off]), vb[ds], dpf);
-        if (do_sparse) dps = mfma32x32x16(lds_read8(&Gs[off]), vb[ds], dps);
+        dpf = mfma32x32x16(lds_read8(&Gf[off]), vb[ds], dpf);
       }
       // ---- probabilities and dS
       const int key = kw0 + col;
-      float pf[16], ps[16], dsv[16];
+      float pf[16], dsv[16];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int qb = 8 * a4 + 4 * g;
-        const float4 lf = *reinterpret_cast<const float4*>(&rv[0 * kBM + qb]);
-        const float4 lsp = *reinterpret_cast<const float4*>(&rv[1 * kBM + qb]);
-        const float4 df = *reinterpret_cast<const float4*>(&rv[2 * kBM + qb]);
-        const float4 dsp = *reinterpret_cast<const float4*>(&rv[3 * kBM + qb]);
-        const float lfa[4] = {lf.x, lf.y, lf.z, lf.w}, lsa[4] = {lsp.x, lsp.y, lsp.z, lsp.w};
-        const float dfa[4] = {df.x, df.y, df.z, df.w}, dsa[4] = {dsp.x, dsp.y, dsp.z, dsp.w};
+        const float4 lf = *reinterpret_cast<const float4*>(&rv[qb]);
+        const float4 df = *reinterpret_cast<const float4*>(&rv[kBM + qb]);
+        const float lfa[4] = {lf.x, lf.y, lf.z, lf.w};
+        const float dfa[4] = {df.x, df.y, df.z, df.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * a4 + e;
-          const int qloc = qb + e;
-          const bool live = !diag || key <= q0 + qloc;
-          const float x = s[i] * scale_log2;
-          float d = 0.f;
-          pf[i] = 0.f;
-          ps[i] = 0.f;
-          if (kFull) {
-            pf[i] = live ? fast_exp2(x - lfa[e]) : 0.f;
-            d += pf[i] * (dpf[i] - dfa[e]);
-          }
-          if (kSparse) {
-            const bool on = live && ((smask >> qloc) & 1u);
-            ps[i] = on ? fast_exp2(x - lsa[e]) : 0.f;
-            d += ps[i] * (dps[i] - dsa[e]);
-          }
-          dsv[i] = d;
+          const bool live = !diag || key <= q0 + qb + e;
+          pf[i] = live ? fast_exp2(s[i] * scale_log2 - lfa[e]) : 0.f;
+          dsv[i] = pf[i] * (dpf[i] - dfa[e]);
         }
       }
       // ---- dS^T -> LDS (bf16) for the dQ reduction over the 128 keys
@@ -312,15 +269,13 @@ __global__ void __launch_bounds__(256, 1)
       for (int st = 0; st < 2; ++st) {
         const int o = 8 * st;
         const bf16x8 bpf = to_bf16x8(pf[o], pf[o + 1], pf[o + 2], pf[o + 3], pf[o + 4], pf[o + 5], pf[o + 6], pf[o + 7]);
-        const bf16x8 bps = to_bf16x8(ps[o], ps[o + 1], ps[o + 2], ps[o + 3], ps[o + 4], ps[o + 5], ps[o + 6], ps[o + 7]);
         const bf16x8 bds = to_bf16x8(dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3], dsv[o + 4], dsv[o + 5], dsv[o + 6], dsv[o + 7]);
         const int r0 = 16 * st + 4 * gk + srow, r1 = r0 + 8;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const int cl = 4 * dt + 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
           const int o0 = r0 * kD + 8 * swz_t(r0, cl) + e4, o1 = r1 * kD + 8 * swz_t(r1, cl) + e4;
-          if (kFull) dv[dt] = mfma32x32x16(lds_tr_pair(&Gf[o0], &Gf[o1]), bpf, dv[dt]);
-          if (do_sparse) dv[dt] = mfma32x32x16(lds_tr_pair(&Gs[o0], &Gs[o1]), bps, dv[dt]);
+          dv[dt] = mfma32x32x16(lds_tr_pair(&Gf[o0], &Gf[o1]), bpf, dv[dt]);
           dk[dt] = mfma32x32x16(lds_tr_pair(&Q[o0], &Q[o1]), bds, dk[dt]);
         }
       }
@@ -331,7 +286,7 @@ __global__ void __launch_bounds__(256, 1)
       for (int a4 = 0; a4 < 4; ++a4)
         *reinterpret_cast<uint2*>(&dS[r * kBM + 8 * swz_s(r, a4) + 4 * g]) = make_uint2(0, 0);
     }
-    if (it + 1 < iters && tid < 4 * kBM) Rn[tid] = prow;
+    if (it + 1 < iters && tid < 2 * kBM) Rn[tid] = prow;
     __builtin_amdgcn_s_waitcnt(0);     // next tiles landed, dS^T written
     __syncthreads();
 
@@ -351,39 +306,45 @@ __global__ void __launch_bounds__(256, 1)
       for (int i = 0; i < 16; ++i)
         unsafeAtomicAdd(dqp + (8 * (i >> 2) + (i & 3)) * kD, scale * (dq0[i] + dq1[i]));
     }
-    cur_bits = pbits;
   };
 
   if (iters > 0) {
-    load_tiles(0, Q0, F0, S0);
+    load_tiles(0, Q0, F0);
     load_rows(0);
-    if (tid < 4 * kBM) R0[tid] = prow;
-    cur_bits = pbits;
+    if (tid < 2 * kBM) R0[tid] = prow;
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int it = 0; it < iters; it += 2) {
-    step(it, Q0, F0, S0, D0, R0, Q1, F1, S1, R1);
+    step(it, Q0, F0, D0, R0, Q1, F1, R1);
     if (it + 1 >= iters) break;
-    step(it + 1, Q1, F1, S1, D1, R1, Q0, F0, S0, R0);
+    step(it + 1, Q1, F1, D1, R1, Q0, F0, R0);
   }
 
-  // ---- epilogue: dK = scale * dK^T^T, dV (bf16); lane owns key kw0 + col
+  // ---- epilogue: dK = scale * dK^T^T (+ sparse stream), dV (+ sparse stream),
+  // in bf16; lane owns key kw0 + col
   const int key = kw0 + col;
   if (key < N) {
-    uint16_t* dkg = static_cast<uint16_t*>(a.dk) + kvbase + static_cast<int64_t>(key) * kD;
-    uint16_t* dvg = static_cast<uint16_t*>(a.dv) + kvbase + static_cast<int64_t>(key) * kD;
+    const int64_t kro = kvbase + static_cast<int64_t>(key) * kD;
+    uint16_t* dkg = static_cast<uint16_t*>(a.dk) + kro;
+    uint16_t* dvg = static_cast<uint16_t*>(a.dv) + kro;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int d0 = 32 * dt + 8 * a4 + 4 * g;
         const int i = 4 * a4;
+        float4 xk = make_float4(0.f, 0.f, 0.f, 0.f), xv = xk;
+        if (a.dk_part) {
+          xk = *reinterpret_cast<const float4*>(a.dk_part + kro + d0);
+          xv = *reinterpret_cast<const float4*>(a.dv_part + kro + d0);
+        }
         *reinterpret_cast<uint2*>(dkg + d0) =
-            make_uint2(pack_bf16x2(scale * dk[dt][i], scale * dk[dt][i + 1]),
-                       pack_bf16x2(scale * dk[dt][i + 2], scale * dk[dt][i + 3]));
+            make_uint2(pack_bf16x2(scale * dk[dt][i] + xk.x, scale * dk[dt][i + 1] + xk.y),
+                       pack_bf16x2(scale * dk[dt][i + 2] + xk.z, scale * dk[dt][i + 3] + xk.w));
         *reinterpret_cast<uint2*>(dvg + d0) =
-            make_uint2(pack_bf16x2(dv[dt][i], dv[dt][i + 1]), pack_bf16x2(dv[dt][i + 2], dv[dt][i + 3]));
+            make_uint2(pack_bf16x2(dv[dt][i] + xv.x, dv[dt][i + 1] + xv.y),
+                       pack_bf16x2(dv[dt][i + 2] + xv.z, dv[dt][i + 3] + xv.w));
       }
     }
   }
@@ -401,18 +362,10 @@ void launch_bwd_pre(const Dims& D, const BwdPreArgs& a, float w_sparsity, float 
   timing_end(kKBwdPre, s);
 }
 
-template <int MODE>
-static void launch_bwd_mode(const Dims& D, const BwdMainArgs& a, hipStream_t s) {
-  dim3 grid(D.B * D.Hkv, (D.N + kBN - 1) / kBN);
-  hipLaunchKernelGGL(k_bwd_mfma<MODE>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.block, D.K, D.scale,
-                     D.scale * kLog2e);
-}
-
 void launch_bwd_mfma(const Dims& D, const BwdMainArgs& a, hipStream_t s) {
+  dim3 grid(D.B * D.Hkv, (D.N + kBN - 1) / kBN);
   timing_begin(kKBwdMfma, s);
-  if (a.mode == kFullOnly) launch_bwd_mode<kModeFull>(D, a, s);
-  else if (a.mode == kSparseOnly) launch_bwd_mode<kModeSparse>(D, a, s);
-  else launch_bwd_mode<kModeDual>(D, a, s);
+  hipLaunchKernelGGL(k_bwd_mfma, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.scale, D.scale * kLog2e);
   timing_end(kKBwdMfma, s);
 }
 

@@ -35,6 +35,7 @@ enum KernelId {
   kKBucket,
   kKSparsePart,
   kKSparseMerge,
+  kKBwdSparse,
   kKernelCount
 };
 
@@ -82,21 +83,16 @@ struct BwdPreArgs {
   float *D_full, *D_sparse;         // rowsum(G o h)
   float *lse2_full, *lse2_sparse;   // lse * log2(e)
   float* dq_acc;                    // zeroed here
-  const int32_t* sel;               // sparse modes: selection rows [rows][K]
-  uint32_t* rowbits;                // sparse modes: [rows][W] bitmask over key blocks
-  int K, W;
   int mode;
 };
+// Full-stream backward: G_f, D_f, lse2_f of every row.
 struct BwdMainArgs {
   const void *q, *k, *v;
-  const int32_t* sel;
-  const uint16_t *g_full, *g_sparse;
-  const float *lse2_full, *lse2_sparse, *D_full, *D_sparse;
+  const uint16_t* g_full;
+  const float *lse2_full, *D_full;
   float* dq_acc;
   void *dk, *dv;
-  const uint32_t* rowbits;          // [rows][W] selection bitmask from bwd_pre
-  int W;
-  int mode;
+  const float *dk_part, *dv_part;   // fp32 sparse-stream dK / dV to add (training modes) or null
 };
 bool bwd_mfma_supported(const Dims& D);
 void launch_bwd_pre(const Dims& D, const BwdPreArgs& a, float w_sparsity, float w_commit, hipStream_t s);
@@ -127,6 +123,19 @@ struct SparseFwdArgs {
 };
 bool sparse_fwd_supported(const Dims& D);
 void launch_sparse_fwd(const Dims& D, const SparseFwdArgs& a, hipStream_t s);
+
+// --- sparse-stream backward on buckets (sparse_bwd.hip) ---
+struct SparseBwdArgs {
+  const void *q, *k, *v;
+  const int32_t *offs, *rows;           // buckets
+  const uint16_t* g_sparse;             // bf16 G_s [rows][d]
+  const float *lse2_sparse, *D_sparse;
+  float* dq_acc;                        // fp32 [rows][d], added to atomically
+  float *dk_part, *dv_part;             // fp32 [B*Hkv][N][d] results, or null: write dk, dv (bf16)
+  void *dk, *dv;
+};
+bool sparse_bwd_supported(const Dims& D);
+void launch_bwd_sparse(const Dims& D, const SparseBwdArgs& a, hipStream_t s);
 
 // --- small kernels (misc.hip) ---
 void launch_zero_f32(float* p, int64_t n, hipStream_t s);

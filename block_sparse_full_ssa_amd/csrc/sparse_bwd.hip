@@ -1,0 +1,361 @@
+// Backward of SSA's sparse stream on key-block buckets, bf16 MFMA on gfx950.
+//
+// The sparse stream's gradient (Sintesi Tecnica, section 2: the stream
+// gradient G_s of the sparse output through the softmax renormalised over
+// each query's selected blocks) touches only the selected (query, key)
+// pairs.  With the bucket of every (batch, KV head c, key block j) -- the
+// rows of the G query heads of group c that selected j -- one workgroup per
+// key block computes
+//   P  = 2^(S c - lse_s)  on the block's keys (own block: keys <= t),
+//   dS = P (G_s V^T - D_s),
+//   dV_j = sum over the bucket of P^T G_s,   dK_j = scale sum of dS^T Q,
+//   dQ_r += scale dS K_j                      (fp32 atomics, one per (row, block)),
+// over the gathered rows in batches of 32.  dK and dV of the block stay in
+// registers over the whole bucket and are written once: as fp32 partials
+// that the full-stream kernel adds (training modes), or as the bf16 result
+// (sparse-only).  Keys of a block that no row selected get zero.
+//
+// Waves: wave w owns key half kh = w % KH (32 keys, B operands in registers)
+// of query stream qs = w / KH; the 4 / KH streams take consecutive batches.
+// Each stream's gathered Q and G_s rows move HBM -> LDS (one row per 16
+// lanes, double-buffered); dS^T of the block passes through LDS so that each
+// wave of a stream reduces dQ over all the block's keys for its slice of d.
+// The layout of every product is the full-stream kernel's (S = Q K^T, lane l
+// owns key l % 32).
+
+#include "common.h"
+#include "internal.h"
+#include "mfma.h"
+
+namespace ssa {
+namespace {
+
+constexpr int kD = 128;
+
+__device__ __forceinline__ int swz_t(int r, int c) { return c ^ (r & 7); }
+__device__ __forceinline__ int swz_s(int r, int c) { return c ^ ((r >> 1) & 3); }
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+template <int KH>
+__global__ void __launch_bounds__(256, 1)
+    k_bwd_sparse(SparseBwdArgs a, int Hq, int G, int N, int nb, float scale, float scale_log2) {
+  constexpr int kBlk = 32 * KH;
+  constexpr int QS = 4 / KH;                 // query streams
+  constexpr int kT = 32 * kD;                // one Q / G tile
+  constexpr int kDS = kBlk * 32;             // one dS^T tile
+  constexpr int kSlice = kD / KH;            // dQ columns per wave
+  // LDS: the key block (for the dQ operand), then per stream two sets of
+  // {Q, G_s tiles, dS^T tile, row values}; separate objects per set so that
+  // the compiler can tell the set being read from the one being filled
+  __shared__ __attribute__((aligned(16))) uint16_t Kst[kBlk * kD];
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[QS * kT], Q1[QS * kT], F0[QS * kT], F1[QS * kT];
+  __shared__ __attribute__((aligned(16))) uint16_t D0[QS * kDS], D1[QS * kDS];
+  // row values per stream: lse2 [32], D [32], t [32] (int, -1: no row), row id [32] (int)
+  __shared__ __attribute__((aligned(16))) float R0[QS * 128], R1[QS * 128];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kh = wave % KH, qs = wave / KH;
+  const int g = lane >> 5, col = lane & 31;
+  const int grp = lane >> 4, li = lane & 15;
+  const int gk = grp >> 1, sub16 = (grp & 1) * 16, srow = li >> 2, m4 = li & 3;
+
+  const int bc = blockIdx.x, j = blockIdx.y;
+  const int Hkv = Hq / G;
+  const int b = bc / Hkv, c = bc % Hkv;
+  const int64_t bucket = static_cast<int64_t>(bc) * nb + j;
+  const int p0 = a.offs[bucket];
+  const int n = a.offs[bucket + 1] - p0;
+  const int32_t* list = a.rows + p0;
+  const int kblk0 = j * kBlk;
+  const int key = kblk0 + 32 * kh + col;      // this lane's key
+  const int64_t kvbase = static_cast<int64_t>(bc) * N * kD;
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + kvbase;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + kvbase;
+  const int64_t qhead0 = static_cast<int64_t>(b) * Hq + c * G;
+
+  // result rows of the lane's key: d = 32 dt + 8 a4 + 4 g + e
+  auto write_kv = [&](const f32x16* dk, const f32x16* dv) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int d0 = 32 * dt + 8 * a4 + 4 * g;
+        const int i = 4 * a4;
+        const int64_t o = kvbase + static_cast<int64_t>(key) * kD + d0;
+        if (a.dk_part) {
+          *reinterpret_cast<float4*>(a.dk_part + o) =
+              make_float4(scale * dk[dt][i], scale * dk[dt][i + 1], scale * dk[dt][i + 2], scale * dk[dt][i + 3]);
+          *reinterpret_cast<float4*>(a.dv_part + o) = make_float4(dv[dt][i], dv[dt][i + 1], dv[dt][i + 2], dv[dt][i + 3]);
+        } else {
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.dk) + o) =
+              make_uint2(pack_bf16x2(scale * dk[dt][i], scale * dk[dt][i + 1]),
+                         pack_bf16x2(scale * dk[dt][i + 2], scale * dk[dt][i + 3]));
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.dv) + o) =
+              make_uint2(pack_bf16x2(dv[dt][i], dv[dt][i + 1]), pack_bf16x2(dv[dt][i + 2], dv[dt][i + 3]));
+        }
+      }
+  };
+
+  f32x16 dv[4], dk[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    dv[dt] = f32x16{};
+    dk[dt] = f32x16{};
+  }
+  if (n == 0) {                                // nobody selected this block
+    if (qs == 0) write_kv(dk, dv);
+    return;
+  }
+
+  // ---- the key block in LDS (plain layout) for the dQ operand
+  for (int e = tid; e < kBlk * kD / 8; e += 256) {
+    const int row = e >> 4, c8 = e & 15;
+    *reinterpret_cast<uint4*>(&Kst[row * kD + 8 * c8]) =
+        *reinterpret_cast<const uint4*>(kg + static_cast<int64_t>(kblk0 + row) * kD + 8 * c8);
+  }
+  // S and dP B operands [16 d x 32 keys]: key = this lane's key, d = 16 ds + 8 g + s
+  bf16x8 kb[kD / 16], vb[kD / 16];
+#pragma unroll
+  for (int ds = 0; ds < kD / 16; ++ds) {
+    kb[ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kg + static_cast<int64_t>(key) * kD + 16 * ds + 8 * g));
+    vb[ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vg + static_cast<int64_t>(key) * kD + 16 * ds + 8 * g));
+  }
+  __syncthreads();
+  // dQ B operands [16 keys x 32 d]: d = slice + 32 dt + col, keys of k-step ks
+  // in the transpose-read order of the dS^T tile
+  constexpr int kDt = kSlice / 32;
+  bf16x8 kq[2 * KH][kDt];
+#pragma unroll
+  for (int ks = 0; ks < 2 * KH; ++ks)
+#pragma unroll
+    for (int dt = 0; dt < kDt; ++dt) {
+      const uint16_t* p = &Kst[(16 * ks + 4 * gk + srow) * kD + kSlice * kh + 32 * dt + sub16 + 4 * m4];
+      kq[ks][dt] = lds_tr_pair(p, p + 8 * kD);
+    }
+
+  const int nbat = (n + 31) >> 5;
+  const int iters = (nbat + QS - 1) / QS;
+  // lane col's entry of the stream's batch bt (-1: none)
+  auto entry = [&](int bt) -> int {
+    const int idx = bt * 32 + col;
+    return (bt < nbat && idx < n) ? list[idx] : -1;
+  };
+  auto row_of = [&](int e) -> int {
+    if (e < 0) return 0;
+    const int hl = e / N;
+    return static_cast<int>((qhead0 + hl) * N + (e - hl * N));
+  };
+  // HBM -> LDS copy of the stream's Q and G_s rows of an entry set: 16
+  // instructions of 4 rows, split over the stream's KH waves; lane l fills
+  // physical chunk l % 16 of row 4 n + l / 16
+  auto load_tiles = [&](int e, uint16_t* Qd, uint16_t* Fd) {
+    const int R = row_of(e);
+#pragma unroll
+    for (int u = 0; u < 16 / KH; ++u) {
+      const int nn = u * KH + kh;                 // 0..15, uniform
+      const int which = nn >> 3, n8 = nn & 7;
+      const int row = 4 * n8 + (lane >> 4);
+      const int Rr = __shfl(R, row, 64);
+      const uint16_t* src = which == 0 ? static_cast<const uint16_t*>(a.q) : a.g_sparse;
+      uint16_t* dst = (which == 0 ? Qd : Fd) + qs * kT;
+      const int cl = swz_t(row, lane & 15);
+      __builtin_amdgcn_global_load_lds((const glb_void*)(src + static_cast<int64_t>(Rr) * kD + 8 * cl),
+                                       (lds_void*)(dst + n8 * 512), 16, 0, 0);
+    }
+  };
+  // row values of an entry set, through registers (lanes 0..31 of wave kh = 0)
+  float rv_lse = 0.f, rv_d = 0.f;
+  int rv_t = -1, rv_r = 0;
+  auto load_rows = [&](int e) {
+    rv_t = -1;
+    rv_r = 0;
+    rv_lse = INFINITY;
+    rv_d = 0.f;
+    if (e >= 0) {
+      const int hl = e / N;
+      rv_t = e - hl * N;
+      rv_r = row_of(e);
+      rv_lse = a.lse2_sparse[rv_r];
+      rv_d = a.D_sparse[rv_r];
+    }
+  };
+  auto store_rows = [&](float* Rd) {
+    if (kh == 0 && g == 0) {
+      float* r = Rd + qs * 128;
+      r[col] = rv_lse;
+      r[32 + col] = rv_d;
+      r[64 + col] = __int_as_float(rv_t);
+      r[96 + col] = __int_as_float(rv_r);
+    }
+  };
+
+  // one iteration on set (Q, F, dS, rv) while the next batch streams into (Qn, Fn, Rn)
+  auto step = [&](int it, int e_next, const uint16_t* Q, const uint16_t* F, uint16_t* dS, const float* rv,
+                  uint16_t* Qn, uint16_t* Fn, float* Rn) {
+    const bool more = it + 1 < iters;
+    if (more) {
+      load_rows(e_next);
+      load_tiles(e_next, Qn, Fn);
+    }
+    const bool has = it * QS + qs < nbat;                       // uniform
+    const uint16_t* Qs = Q + qs * kT;
+    const uint16_t* Fs = F + qs * kT;
+    uint16_t* dSs = dS + qs * kDS;
+    const float* rs = rv + qs * 128;
+    // row ids and validity of the lane's 16 query rows for the dQ atomics,
+    // taken before the barrier (the row values are refilled after it)
+    int rq[16];
+    uint32_t rowok = 0u;
+    if (has) {
+      // ---- S = Q K^T, dP = G_s V^T [32 q x 32 keys]; lane: key col, queries 8(i/4)+4g+(i%4)
+      f32x16 s = f32x16{}, dp = f32x16{};
+      const int ra = col * kD;
+#pragma unroll
+      for (int ds = 0; ds < kD / 16; ++ds) {
+        const int off = ra + 8 * swz_t(col, 2 * ds + g);
+        s = mfma32x32x16(lds_read8(&Qs[off]), kb[ds], s);
+        dp = mfma32x32x16(lds_read8(&Fs[off]), vb[ds], dp);
+      }
+      float p[16], dsv[16];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const int qb = 8 * a4 + 4 * g;
+        const float4 l4 = *reinterpret_cast<const float4*>(&rs[qb]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&rs[32 + qb]);
+        const float4 t4 = *reinterpret_cast<const float4*>(&rs[64 + qb]);
+        const float la[4] = {l4.x, l4.y, l4.z, l4.w}, da[4] = {d4.x, d4.y, d4.z, d4.w};
+        const float4 r4 = *reinterpret_cast<const float4*>(&rs[96 + qb]);
+        const int ta[4] = {__float_as_int(t4.x), __float_as_int(t4.y), __float_as_int(t4.z), __float_as_int(t4.w)};
+        const int ra[4] = {__float_as_int(r4.x), __float_as_int(r4.y), __float_as_int(r4.z), __float_as_int(r4.w)};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = 4 * a4 + e;
+          rq[i] = ra[e];
+          rowok |= ta[e] >= 0 ? (1u << i) : 0u;
+          const bool live = key <= ta[e];                  // t = -1: no row
+          p[i] = live ? fast_exp2(s[i] * scale_log2 - la[e]) : 0.f;
+          dsv[i] = p[i] * (dp[i] - da[e]);
+        }
+      }
+      // ---- dS^T -> LDS (bf16) for the dQ reduction over the block's keys
+      {
+        const int r = 32 * kh + col;
+#pragma unroll
+        for (int a4 = 0; a4 < 4; ++a4) {
+          uint2 u = make_uint2(pack_bf16x2(dsv[4 * a4], dsv[4 * a4 + 1]), pack_bf16x2(dsv[4 * a4 + 2], dsv[4 * a4 + 3]));
+          *reinterpret_cast<uint2*>(&dSs[r * 32 + 8 * swz_s(r, a4) + 4 * g]) = u;
+        }
+      }
+      // ---- dV^T += G_s^T P, dK^T += Q^T dS  (k = queries; 2 steps of 16)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int o = 8 * st;
+        const bf16x8 bp = to_bf16x8(p[o], p[o + 1], p[o + 2], p[o + 3], p[o + 4], p[o + 5], p[o + 6], p[o + 7]);
+        const bf16x8 bds = to_bf16x8(dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3], dsv[o + 4], dsv[o + 5], dsv[o + 6], dsv[o + 7]);
+        const int r0 = 16 * st + 4 * gk + srow, r1 = r0 + 8;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const int cl = 4 * dt + 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
+          const int o0 = r0 * kD + 8 * swz_t(r0, cl) + e4, o1 = r1 * kD + 8 * swz_t(r1, cl) + e4;
+          dv[dt] = mfma32x32x16(lds_tr_pair(&Fs[o0], &Fs[o1]), bp, dv[dt]);
+          dk[dt] = mfma32x32x16(lds_tr_pair(&Qs[o0], &Qs[o1]), bds, dk[dt]);
+        }
+      }
+    }
+    if (more) store_rows(Rn);
+    __builtin_amdgcn_s_waitcnt(0);     // next tiles landed, dS^T written
+    __syncthreads();
+
+    // ---- dQ[32 q x slice] of the stream's batch = dS[32 q x block keys] K[block keys x slice]
+    if (has) {
+      f32x16 dq[kDt];
+#pragma unroll
+      for (int dt = 0; dt < kDt; ++dt) dq[dt] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < 2 * KH; ++ks) {
+        const int r0 = 16 * ks + 4 * gk + srow, r1 = r0 + 8;
+        const int cl = 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
+        const bf16x8 ds_op =
+            lds_tr_pair(&dSs[r0 * 32 + 8 * swz_s(r0, cl) + e4], &dSs[r1 * 32 + 8 * swz_s(r1, cl) + e4]);
+#pragma unroll
+        for (int dt = 0; dt < kDt; ++dt) dq[dt] = mfma32x32x16(ds_op, kq[ks][dt], dq[dt]);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (!((rowok >> i) & 1u)) continue;
+        float* dqp = a.dq_acc + static_cast<int64_t>(rq[i]) * kD + kSlice * kh + col;
+#pragma unroll
+        for (int dt = 0; dt < kDt; ++dt) unsafeAtomicAdd(dqp + 32 * dt, scale * dq[dt][i]);
+      }
+    }
+  };
+
+  // prologue: the first batch of every stream
+  int e_cur = entry(qs);
+  load_rows(e_cur);
+  load_tiles(e_cur, Q0, F0);
+  store_rows(R0);
+  int e_next = entry(QS + qs);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int it = 0; it < iters; it += 2) {
+    int e_after = entry((it + 2) * QS + qs);
+    step(it, e_next, Q0, F0, D0, R0, Q1, F1, R1);
+    e_next = e_after;
+    if (it + 1 >= iters) break;
+    e_after = entry((it + 3) * QS + qs);
+    step(it + 1, e_next, Q1, F1, D1, R1, Q0, F0, R0);
+    e_next = e_after;
+  }
+
+  // ---- reduce dK / dV over the streams of each key half (one stream and
+  // one tensor at a time through 16 KiB of the free Q tiles: Q0 for key
+  // half 0, Q1 for key half 1), then write
+  if (QS > 1) {
+    float* red = reinterpret_cast<float*>(kh == 0 ? Q0 : Q1);
+    for (int o = 1; o < QS; ++o) {
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        f32x16* acc = part == 0 ? dk : dv;
+        __syncthreads();
+        if (qs == o) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) red[(dt * 16 + i) * 64 + lane] = acc[dt][i];
+        }
+        __syncthreads();
+        if (qs == 0) {
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[dt][i] += red[(dt * 16 + i) * 64 + lane];
+        }
+      }
+    }
+  }
+  if (qs == 0) write_kv(dk, dv);
+}
+
+}  // namespace
+
+bool sparse_bwd_supported(const Dims& D) { return D.dtype == 1 && D.d == kD; }
+
+void launch_bwd_sparse(const Dims& D, const SparseBwdArgs& a, hipStream_t s) {
+  dim3 grid(D.B * D.Hkv, D.nb);
+  const float scale_log2 = D.scale * 1.4426950408889634f;
+  timing_begin(kKBwdSparse, s);
+  if (D.block == 32)
+    hipLaunchKernelGGL(k_bwd_sparse<1>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.scale, scale_log2);
+  else if (D.block == 64)
+    hipLaunchKernelGGL(k_bwd_sparse<2>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.scale, scale_log2);
+  else
+    hipLaunchKernelGGL(k_bwd_sparse<4>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.scale, scale_log2);
+  timing_end(kKBwdSparse, s);
+}
+
+}  // namespace ssa
