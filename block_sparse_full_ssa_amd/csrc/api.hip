@@ -33,7 +33,7 @@ static std::vector<TimingRec> g_recs;
 static const char* kKernelNames[kKernelCount] = {
     "block_mean", "select", "fwd_simt", "fwd_mfma", "loss_reduce",
     "bwd_pre",    "bwd_simt", "bwd_mfma", "convert", "zero", "bucket", "sparse_part", "sparse_merge",
-    "bwd_sparse"};
+    "bwd_sparse", "bwd_dq"};
 
 void timing_begin(int kernel, hipStream_t s) {
   if (!g_timing) return;
@@ -164,7 +164,7 @@ static BwdWs carve_bwd(const Dims& D, int mode, Carver& c) {
       w.dk_part = c.take<float>(D.kv_elems() * sizeof(float));
       w.dv_part = c.take<float>(D.kv_elems() * sizeof(float));
     }
-    w.dq_acc = c.take<float>(D.q_elems() * sizeof(float));
+    if (sp) w.dq_acc = c.take<float>(D.q_elems() * sizeof(float));
   } else {
     w.dk_acc = c.take<float>(D.kv_elems() * sizeof(float));
     w.dv_acc = c.take<float>(D.kv_elems() * sizeof(float));
@@ -280,8 +280,9 @@ ssa_status_t ssa_attn_bwd(const ssa_shape_t* shape, int32_t mode, float w_sparsi
   Carver c{static_cast<char*>(ws)};
   BwdWs w = carve_bwd(D, mode, c);
   if (bwd_mfma_supported(D)) {
-    // stream gradients, then the sparse stream on key-block buckets (its dK /
-    // dV as fp32 partials when the full stream follows), then the full stream
+    // stream gradients, then the sparse stream on key-block buckets (fp32 dQ,
+    // and dK / dV as fp32 partials when the full stream follows), then the
+    // full stream's dK / dV and dQ, each adding the sparse stream's part
     BwdPreArgs p{d_out, h_full, h_sparse, lse_full, lse_sparse, w.g_full, w.g_sparse, w.D_full, w.D_sparse,
                  w.lse2_full, w.lse2_sparse, w.dq_acc, mode};
     launch_bwd_pre(D, p, w_sparsity, w_commit, s);
@@ -294,12 +295,15 @@ ssa_status_t ssa_attn_bwd(const ssa_shape_t* shape, int32_t mode, float w_sparsi
       launch_bwd_sparse(D, sp, s);
       if ((st = launch_status()) != SSA_OK) return st;
     }
-    if (mode != kSparseOnly) {
-      BwdMainArgs m{q, k, v, w.g_full, w.lse2_full, w.D_full, w.dq_acc, dk, dv, w.dk_part, w.dv_part};
-      launch_bwd_mfma(D, m, s);
-      if ((st = launch_status()) != SSA_OK) return st;
+    if (mode == kSparseOnly) {
+      launch_convert(w.dq_acc, dq, D.dtype, D.q_elems(), s);
+      return launch_status();
     }
-    launch_convert(w.dq_acc, dq, D.dtype, D.q_elems(), s);
+    BwdMainArgs m{q, k, v, w.g_full, w.lse2_full, w.D_full, dk, dv, w.dk_part, w.dv_part};
+    launch_bwd_mfma(D, m, s);
+    if ((st = launch_status()) != SSA_OK) return st;
+    BwdDqArgs dqa{q, k, v, w.g_full, w.lse2_full, w.D_full, w.dq_acc, dq};
+    launch_bwd_dq(D, dqa, s);
     return launch_status();
   }
   launch_zero_f32(w.dk_acc, D.kv_elems(), s);

@@ -1,0 +1,177 @@
+// dQ of SSA's full stream, bf16 MFMA on gfx950, query-stationary.
+//
+// The full stream's query gradient (Sintesi Tecnica, section 2: the full
+// output's stream gradient G_f through the causal softmax) is
+//   dQ = scale sum over keys of P (G_f V^T - D_f) K,   P = 2^(S c - lse_f).
+// A workgroup owns 128 queries of one head (32 per wave) and walks the
+// causal key tiles of 64 keys, recomputing the logits and dP on the way, so
+// that dQ accumulates in registers: no atomics and no exchange through LDS.
+// The layout is the forward's: S^T = K Q^T and dP^T = V G^T (A = K / V rows
+// from LDS, B = the wave's Q / G rows in registers) leave lane l with query
+// l % 32; dS^T = P^T (dP^T - D) is then the B operand of dQ^T += K^T dS^T,
+// with K^T read from the same K tile by transpose reads.  K / V tiles move
+// HBM -> LDS double-buffered, one barrier per tile.
+//
+// The epilogue adds the sparse stream's fp32 dQ (training modes) and writes
+// bf16.
+
+#include "common.h"
+#include "internal.h"
+#include "mfma.h"
+
+namespace ssa {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kBM = 128;         // queries per workgroup
+constexpr int kBN = 64;          // keys per tile
+constexpr int kTile = kBN * kD;
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void glb_void;
+
+// Physical 16-byte chunk of logical chunk c in a 256-byte row r.
+__device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
+
+__global__ void __launch_bounds__(256, 2)
+    k_bwd_dq(BwdDqArgs a, int Hq, int G, int N, float scale, float scale_log2, int n_qtiles) {
+  __shared__ __attribute__((aligned(16))) uint16_t K0[kTile], K1[kTile], V0[kTile], V1[kTile];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5, col = lane & 31;
+  const int grp = lane >> 4, li = lane & 15;
+  const int gk = grp >> 1, srow = li >> 2, m4 = li & 3;
+  const int bh = blockIdx.x;
+  const int q0 = (n_qtiles - 1 - static_cast<int>(blockIdx.y)) * kBM;   // longest tiles first
+  const int b = bh / Hq, h = bh % Hq;
+  const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + bc * N * kD;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + bc * N * kD;
+
+  const int qrow = q0 + wave * 32 + col;           // this lane's query
+  const bool wave_live = q0 + wave * 32 < N;
+  const int wave_q0 = q0 + wave * 32;
+  const int wave_last_q = min(N - 1, wave_q0 + 31);
+  const int64_t row = static_cast<int64_t>(bh) * N + qrow;
+  // the wave's Q and G_f rows as B operands (query = col, d = 16 ds + 8 g + s)
+  bf16x8 qreg[kD / 16], greg[kD / 16];
+#pragma unroll
+  for (int ds = 0; ds < kD / 16; ++ds) {
+    uint4 u = make_uint4(0, 0, 0, 0), w = make_uint4(0, 0, 0, 0);
+    if (qrow < N) {
+      u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.q) + row * kD + 16 * ds + 8 * g);
+      w = *reinterpret_cast<const uint4*>(a.g_full + row * kD + 16 * ds + 8 * g);
+    }
+    qreg[ds] = __builtin_bit_cast(bf16x8, u);
+    greg[ds] = __builtin_bit_cast(bf16x8, w);
+  }
+  const float lse2 = qrow < N ? a.lse2_full[row] : 0.f;
+  const float Dq = qrow < N ? a.D_full[row] : 0.f;
+
+  f32x16 dq[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) dq[dt] = f32x16{};
+
+  const int j_last = min(N - 1, q0 + kBM - 1) / kBN;
+
+  // HBM -> LDS copy of one K/V tile: each wave moves rows 16*wave .. +15, one
+  // 1 KiB instruction per 4 rows; lane l fills physical chunk l % 16 of row
+  // 4n + l / 16.  Keys past the end read the last key (masked later).
+  auto load_tile = [&](int j, uint16_t* Kd, uint16_t* Vd) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int n = wave * 4 + r;
+      const int rw = 4 * n + (lane >> 4);
+      const int p = lane & 15;
+      const int64_t key = min(j * kBN + rw, N - 1);
+      __builtin_amdgcn_global_load_lds((const glb_void*)(kg + key * kD + 8 * swz_k(rw, p)),
+                                       (lds_void*)(Kd + n * 512), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const glb_void*)(vg + key * kD + 8 * swz_k(rw, p)),
+                                       (lds_void*)(Vd + n * 512), 16, 0, 0);
+    }
+  };
+
+  auto step = [&](int j, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn) {
+    if (j + 1 <= j_last) load_tile(j + 1, Kn, Vn);
+    if (wave_live && j * kBN <= wave_last_q) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const int kbase = j * kBN + kh * 32;
+        if (kbase > wave_last_q) break;                // uniform: later keys are all masked
+        // ---- S^T = K Q^T, dP^T = V G^T for 32 keys (A: key row kh*32 + col)
+        f32x16 s = f32x16{}, dp = f32x16{};
+        {
+          const int r = kh * 32 + col;
+#pragma unroll
+          for (int ds = 0; ds < kD / 16; ++ds) {
+            const int off = r * kD + 8 * swz_k(r, 2 * ds + g);
+            s = mfma32x32x16(lds_read8(&Ks[off]), qreg[ds], s);
+            dp = mfma32x32x16(lds_read8(&Vs[off]), greg[ds], dp);
+          }
+        }
+        // ---- dS^T = P^T (dP^T - D); key of register i: kbase + 8(i/4) + 4g + i%4
+        const bool diag = kbase + 31 > wave_q0;      // uniform
+        float dsv[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kbase + 8 * (i >> 2) + 4 * g + (i & 3);
+          const bool live = !diag || key <= qrow;
+          const float p = live ? fast_exp2(s[i] * scale_log2 - lse2) : 0.f;
+          dsv[i] = p * (dp[i] - Dq);
+        }
+        // ---- dQ^T += K^T dS^T over the 32 keys (two k-steps of 16)
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const bf16x8 bds = to_bf16x8(dsv[8 * st], dsv[8 * st + 1], dsv[8 * st + 2], dsv[8 * st + 3],
+                                       dsv[8 * st + 4], dsv[8 * st + 5], dsv[8 * st + 6], dsv[8 * st + 7]);
+          const int r0 = kh * 32 + st * 16 + 4 * gk + srow, r1 = r0 + 8;
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            const int c = 4 * dt + 2 * (grp & 1) + (m4 >> 1), e = 4 * (m4 & 1);
+            const bf16x8 ka = lds_tr_pair(&Ks[r0 * kD + 8 * swz_k(r0, c) + e], &Ks[r1 * kD + 8 * swz_k(r1, c) + e]);
+            dq[dt] = mfma32x32x16(ka, bds, dq[dt]);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);     // the next tile has landed in LDS
+    __syncthreads();
+  };
+
+  load_tile(0, K0, V0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int j = 0; j <= j_last; j += 2) {
+    step(j, K0, V0, K1, V1);
+    if (j + 1 > j_last) break;
+    step(j + 1, K1, V1, K0, V0);
+  }
+
+  // ---- epilogue: dq = scale dQ^T^T (+ the sparse stream's fp32 dQ), bf16
+  if (!wave_live || qrow >= N) return;
+  uint16_t* out = static_cast<uint16_t*>(a.dq) + row * kD;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = 32 * dt + 8 * i4 + 4 * g;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (a.dq_sparse) x = *reinterpret_cast<const float4*>(a.dq_sparse + row * kD + d0);
+      *reinterpret_cast<uint2*>(out + d0) =
+          make_uint2(pack_bf16x2(scale * dq[dt][4 * i4] + x.x, scale * dq[dt][4 * i4 + 1] + x.y),
+                     pack_bf16x2(scale * dq[dt][4 * i4 + 2] + x.z, scale * dq[dt][4 * i4 + 3] + x.w));
+    }
+}
+
+}  // namespace
+
+void launch_bwd_dq(const Dims& D, const BwdDqArgs& a, hipStream_t s) {
+  const int n_qtiles = (D.N + kBM - 1) / kBM;
+  dim3 grid(D.B * D.Hq, n_qtiles);
+  timing_begin(kKBwdDq, s);
+  hipLaunchKernelGGL(k_bwd_dq, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.scale, D.scale * 1.4426950408889634f,
+                     n_qtiles);
+  timing_end(kKBwdDq, s);
+}
+
+}  // namespace ssa

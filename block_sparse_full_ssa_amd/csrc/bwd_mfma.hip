@@ -15,19 +15,19 @@
 //
 // Kernels:
 //   bwd_pre:  per row, G_f / G_s in bf16, D_f / D_s from the rounded G, the
-//             lse values in log2 units, and a zeroed fp32 dQ accumulator row;
-//   bwd_mfma: key-stationary.  A workgroup owns 128 keys of one KV head (32
-//             per wave, kept in registers as K and V operands) and walks the
-//             G query heads of the group and every 32-query tile at or after
-//             its keys.  dK and dV accumulate in registers over all of them
-//             (no atomics) and leave with the sparse stream's fp32 dK / dV
-//             added; dQ of each tile is reduced over the 128 keys through
-//             LDS and added to the fp32 accumulator with atomics;
-//   convert:  dQ accumulator -> bf16.
+//             lse values in log2 units, and a zeroed fp32 dQ accumulator row
+//             for the sparse stream;
+//   bwd_mfma: dK / dV, key-stationary.  A workgroup owns 128 keys of one KV
+//             head (32 per wave, kept in registers as K and V operands) and
+//             walks the G query heads of the group and every 32-query tile
+//             at or after its keys.  dK and dV accumulate in registers over
+//             all of them (no atomics) and leave with the sparse stream's
+//             fp32 dK / dV added;
+//   bwd_dq:   dQ, query-stationary (bwd_dq.hip).
 //
 // Layout: the logits are kept as S = Q K^T (lane l owns key l % 32 and 16
 // queries), which is the B-operand layout of dV^T = G^T P and dK^T = Q^T dS;
-// the transposed A operands G^T, Q^T and dS come from row-major LDS tiles
+// the transposed A operands G^T and Q^T come from row-major LDS tiles
 // through transpose reads.  All MFMA guards are wave-uniform.
 
 #include "common.h"
@@ -79,7 +79,7 @@ __global__ void __launch_bounds__(256)
   }
   if (has_f) *reinterpret_cast<uint32_t*>(a.g_full + off) = gfw;
   if (has_s) *reinterpret_cast<uint32_t*>(a.g_sparse + off) = gsw;
-  *reinterpret_cast<float2*>(a.dq_acc + off) = make_float2(0.f, 0.f);
+  if (a.dq_acc) *reinterpret_cast<float2*>(a.dq_acc + off) = make_float2(0.f, 0.f);
   Df = wave_sum(Df);
   Ds = wave_sum(Ds);
   if (lane == 0) {
@@ -99,21 +99,17 @@ __global__ void __launch_bounds__(256)
 // dS^T tiles (64-byte rows).  Both the row reads of matrix operands and the
 // transpose reads then spread over all banks.
 __device__ __forceinline__ int swz_t(int r, int c) { return c ^ (r & 7); }
-__device__ __forceinline__ int swz_s(int r, int c) { return c ^ ((r >> 1) & 3); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
 __global__ void __launch_bounds__(256, 1)
     k_bwd_mfma(BwdMainArgs a, int Hq, int G, int N, float scale, float scale_log2) {
-  // LDS: the 128 x 128 key tile staged once at start, then two sets of
-  // {Q, G_f tiles [32][128], dS^T [128][32], row values [2][32] fp32}, each
+  // LDS: two sets of {Q, G_f tiles [32][128], row values [2][32] fp32}, each
   // buffer its own object so that the compiler can tell the set being read
   // from the set being filled by the HBM -> LDS copies
   constexpr int kT = kBM * kD;                       // one Q / G tile
-  __shared__ __attribute__((aligned(16))) uint16_t Kst[kBN * kD];
   __shared__ __attribute__((aligned(16))) uint16_t Q0[kT], Q1[kT], F0[kT], F1[kT];
-  __shared__ __attribute__((aligned(16))) uint16_t D0[kBN * kBM], D1[kBN * kBM];
   __shared__ __attribute__((aligned(16))) float R0[2 * kBM], R1[2 * kBM];
 
   const int tid = threadIdx.x;
@@ -121,7 +117,7 @@ __global__ void __launch_bounds__(256, 1)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, col = lane & 31;
   const int grp = lane >> 4, li = lane & 15;
-  const int gk = grp >> 1, sub16 = (grp & 1) * 16, srow = li >> 2, m4 = li & 3;
+  const int gk = grp >> 1, srow = li >> 2, m4 = li & 3;
 
   const int bc = blockIdx.x;                        // batch * Hkv + kv head
   const int Hkv = Hq / G;
@@ -132,21 +128,6 @@ __global__ void __launch_bounds__(256, 1)
   const uint16_t* kg = static_cast<const uint16_t*>(a.k) + kvbase;
   const uint16_t* vg = static_cast<const uint16_t*>(a.v) + kvbase;
 
-  // ---- stage the key tile for the dQ operand, read it transposed
-  for (int e = tid; e < kBN * kD / 8; e += 256) {
-    const int row = e >> 4, c8 = e & 15;
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (k0 + row < N) u = *reinterpret_cast<const uint4*>(kg + static_cast<int64_t>(k0 + row) * kD + 8 * c8);
-    *reinterpret_cast<uint4*>(&Kst[row * kD + 8 * c8]) = u;
-  }
-  __syncthreads();
-  // dQ B operand [16 keys x 32 d]: d = 32*wave + col, keys of k-step ks in slots
-  bf16x8 kq[kBN / 16];
-#pragma unroll
-  for (int ks = 0; ks < kBN / 16; ++ks) {
-    const uint16_t* p0 = &Kst[(16 * ks + 4 * gk + srow) * kD + 32 * wave + sub16 + 4 * m4];
-    kq[ks] = lds_tr_pair(p0, p0 + 8 * kD);
-  }
   // S and dP B operands [16 d x 32 keys]: key = kw0 + col, d = 16*ds + 8*g + s
   bf16x8 kb[kD / 16], vb[kD / 16];
   {
@@ -212,12 +193,11 @@ __global__ void __launch_bounds__(256, 1)
     }
   };
 
-  // one iteration on set (Q, Gf, dS, rv) while the next streams into (Qn, Fn, Rn)
-  auto step = [&](int it, const uint16_t* Q, const uint16_t* Gf, uint16_t* dS, const float* rv, uint16_t* Qn,
-                  uint16_t* Fn, float* Rn) {
+  // one iteration on set (Q, Gf, rv) while the next streams into (Qn, Fn, Rn)
+  auto step = [&](int it, const uint16_t* Q, const uint16_t* Gf, const float* rv, uint16_t* Qn, uint16_t* Fn,
+                  float* Rn) {
     int hq, q0;
     iter_coords(it, hq, q0);
-    const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N + q0;
     if (it + 1 < iters) {
       load_rows(it + 1);      // plain loads first: no VMEM load may follow the copies
       load_tiles(it + 1, Qn, Fn);
@@ -255,15 +235,6 @@ __global__ void __launch_bounds__(256, 1)
           dsv[i] = pf[i] * (dpf[i] - dfa[e]);
         }
       }
-      // ---- dS^T -> LDS (bf16) for the dQ reduction over the 128 keys
-      {
-        const int r = 32 * wave + col;
-#pragma unroll
-        for (int a4 = 0; a4 < 4; ++a4) {
-          uint2 u = make_uint2(pack_bf16x2(dsv[4 * a4], dsv[4 * a4 + 1]), pack_bf16x2(dsv[4 * a4 + 2], dsv[4 * a4 + 3]));
-          *reinterpret_cast<uint2*>(&dS[r * kBM + 8 * swz_s(r, a4) + 4 * g]) = u;
-        }
-      }
       // ---- dV^T += G^T P, dK^T += Q^T dS  (k = queries; 2 steps of 16)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -279,33 +250,10 @@ __global__ void __launch_bounds__(256, 1)
           dk[dt] = mfma32x32x16(lds_tr_pair(&Q[o0], &Q[o1]), bds, dk[dt]);
         }
       }
-    } else {
-      // no causal pairs for this wave: its dS rows are zero
-      const int r = 32 * wave + col;
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4)
-        *reinterpret_cast<uint2*>(&dS[r * kBM + 8 * swz_s(r, a4) + 4 * g]) = make_uint2(0, 0);
     }
     if (it + 1 < iters && tid < 2 * kBM) Rn[tid] = prow;
-    __builtin_amdgcn_s_waitcnt(0);     // next tiles landed, dS^T written
+    __builtin_amdgcn_s_waitcnt(0);     // next tiles landed
     __syncthreads();
-
-    // ---- dQ[32 q x 32 d] of this wave's d-slice = dS[32 q x 128 keys] K[128 keys x 32 d]
-    {
-      f32x16 dq0 = f32x16{}, dq1 = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < kBN / 16; ++ks) {
-        const int r0 = 16 * ks + 4 * gk + srow, r1 = r0 + 8;
-        const int cl = 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
-        const bf16x8 ds_op = lds_tr_pair(&dS[r0 * kBM + 8 * swz_s(r0, cl) + e4], &dS[r1 * kBM + 8 * swz_s(r1, cl) + e4]);
-        if (ks & 1) dq1 = mfma32x32x16(ds_op, kq[ks], dq1);
-        else dq0 = mfma32x32x16(ds_op, kq[ks], dq0);
-      }
-      float* dqp = a.dq_acc + (rowbase + 4 * g) * kD + 32 * wave + col;
-#pragma unroll
-      for (int i = 0; i < 16; ++i)
-        unsafeAtomicAdd(dqp + (8 * (i >> 2) + (i & 3)) * kD, scale * (dq0[i] + dq1[i]));
-    }
   };
 
   if (iters > 0) {
@@ -316,9 +264,9 @@ __global__ void __launch_bounds__(256, 1)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int it = 0; it < iters; it += 2) {
-    step(it, Q0, F0, D0, R0, Q1, F1, R1);
+    step(it, Q0, F0, R0, Q1, F1, R1);
     if (it + 1 >= iters) break;
-    step(it + 1, Q1, F1, D1, R1, Q0, F0, R0);
+    step(it + 1, Q1, F1, R1, Q0, F0, R0);
   }
 
   // ---- epilogue: dK = scale * dK^T^T (+ sparse stream), dV (+ sparse stream),

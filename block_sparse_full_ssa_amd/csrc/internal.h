@@ -36,6 +36,7 @@ enum KernelId {
   kKSparsePart,
   kKSparseMerge,
   kKBwdSparse,
+  kKBwdDq,
   kKernelCount
 };
 
@@ -82,18 +83,25 @@ struct BwdPreArgs {
   uint16_t *g_full, *g_sparse;      // bf16 stream gradients [rows][d]
   float *D_full, *D_sparse;         // rowsum(G o h)
   float *lse2_full, *lse2_sparse;   // lse * log2(e)
-  float* dq_acc;                    // zeroed here
+  float* dq_acc;                    // zeroed here when not null
   int mode;
 };
 // Full-stream backward: G_f, D_f, lse2_f of every row.
-struct BwdMainArgs {
+struct BwdMainArgs {                // dK, dV
   const void *q, *k, *v;
   const uint16_t* g_full;
   const float *lse2_full, *D_full;
-  float* dq_acc;
   void *dk, *dv;
   const float *dk_part, *dv_part;   // fp32 sparse-stream dK / dV to add (training modes) or null
 };
+struct BwdDqArgs {                  // dQ
+  const void *q, *k, *v;
+  const uint16_t* g_full;
+  const float *lse2_full, *D_full;
+  const float* dq_sparse;           // fp32 sparse-stream dQ to add (training modes) or null
+  void* dq;
+};
+void launch_bwd_dq(const Dims& D, const BwdDqArgs& a, hipStream_t s);
 bool bwd_mfma_supported(const Dims& D);
 void launch_bwd_pre(const Dims& D, const BwdPreArgs& a, float w_sparsity, float w_commit, hipStream_t s);
 void launch_bwd_mfma(const Dims& D, const BwdMainArgs& a, hipStream_t s);
