@@ -10,11 +10,14 @@
 // Two kernels:
 //   block_mean: mean of each key block, fp32, [B*Hkv][nb][d];
 //   select:     one workgroup per (head, up to 64 rows of one query block);
-//               candidate scores are computed chunk by chunk into LDS, then a
-//               wave ranks each row by a bitwise threshold search (see below).
+//               candidate scores are computed into LDS (fp32 matrix
+//               instructions up to 1024 key blocks, else fp32 FMAs chunk by
+//               chunk), then a wave ranks each row by a bitwise threshold
+//               search (see below).
 
 #include "common.h"
 #include "internal.h"
+#include "mfma.h"
 
 namespace ssa {
 
@@ -45,6 +48,73 @@ void launch_block_mean(const Dims& D, const void* k, float* mu, hipStream_t s) {
 }
 
 constexpr int kSelChunk = 64;     // candidate blocks scored per pass
+
+// Ranking of R rows whose candidate scores sit in LDS (scores[r * nb + j],
+// j < i): see the kernel comments.  Wave w ranks rows w*RW.. in steps of 4*RW.
+template <int TM>
+__device__ __forceinline__ void rank_rows(const float* scores, int32_t* out0, int R, int nb, int K, int i, int keep,
+                                          int lane, int wave) {
+  constexpr int RW = TM <= 8 ? 2 : 1;
+  const int nt = (i + 63) >> 6;     // registers holding candidates of this block
+  for (int r0 = wave * RW; r0 < R; r0 += 4 * RW) {
+    uint32_t u[RW][TM];
+#pragma unroll
+    for (int w = 0; w < RW; ++w)
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        const int j = 64 * t + lane;
+        // + 0.0f turns -0 into +0, so the two zeros tie as the values do
+        u[w][t] = (t < nt && j < i) ? ordered_bits(scores[(r0 + w) * nb + j] + 0.0f) : 0u;
+      }
+    // codes of absent candidates are 0, below every threshold tried (>= 1)
+    uint32_t th[RW];
+#pragma unroll
+    for (int w = 0; w < RW; ++w) th[w] = 0u;
+    for (int bit = 31; bit >= 0; --bit) {
+#pragma unroll
+      for (int w = 0; w < RW; ++w) {
+        const uint32_t c = th[w] | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int t = 0; t < TM; ++t) cnt += __popcll(__ballot(u[w][t] >= c));
+        th[w] = cnt >= keep ? c : th[w];
+      }
+    }
+#pragma unroll
+    for (int w = 0; w < RW; ++w) {
+      int32_t* out = out0 + static_cast<int64_t>(r0 + w) * K;
+      int need = keep;              // places left for codes equal to th
+#pragma unroll
+      for (int t = 0; t < TM; ++t) need -= __popcll(__ballot(u[w][t] > th[w]));
+      int base = 0;
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        {
+          uint64_t eq = __ballot(u[w][t] == th[w]);
+          if (__popcll(eq) > need) {    // keep only the `need` lowest lanes
+            uint64_t take = 0;
+            for (int n = 0; n < need; ++n) {
+              const uint64_t low = eq & (~eq + 1);
+              take |= low;
+              eq ^= low;
+            }
+            eq = take;
+          }
+          need -= __popcll(eq);
+          const uint64_t won = __ballot(u[w][t] > th[w]) | eq;
+          if ((won >> lane) & 1) {
+            const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(won >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(won), 0));
+            out[base + below] = 64 * t + lane;
+          }
+          base += __popcll(won);
+        }
+      }
+      for (int slot = keep + lane; slot < K; slot += 64) out[slot] = (slot == keep) ? i : -1;
+    }
+  }
+}
+
 
 // One workgroup (256 threads) per R rows of one query block (R divides the
 // block and R x nb fp32 scores fit in 64 KiB); the rows share the candidate
@@ -146,66 +216,104 @@ __global__ void __launch_bounds__(256) k_select(const T* __restrict__ q, const f
   }
   __syncthreads();
 
-  // ---- 2. ranking, RW rows per wave at a time
-  constexpr int RW = TM <= 8 ? 2 : 1;
-  const int nt = (i + 63) >> 6;     // registers holding candidates of this block
-  for (int r0 = wave * RW; r0 < R; r0 += 4 * RW) {
-    uint32_t u[RW][TM];
-#pragma unroll
-    for (int w = 0; w < RW; ++w)
-#pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        const int j = 64 * t + lane;
-        // + 0.0f turns -0 into +0, so the two zeros tie as the values do
-        u[w][t] = (t < nt && j < i) ? ordered_bits(scores[(r0 + w) * nb + j] + 0.0f) : 0u;
-      }
-    // codes of absent candidates are 0, below every threshold tried (>= 1)
-    uint32_t th[RW];
-#pragma unroll
-    for (int w = 0; w < RW; ++w) th[w] = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-#pragma unroll
-      for (int w = 0; w < RW; ++w) {
-        const uint32_t c = th[w] | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int t = 0; t < TM; ++t) cnt += __popcll(__ballot(u[w][t] >= c));
-        th[w] = cnt >= keep ? c : th[w];
-      }
+  rank_rows<TM>(scores, out0, R, nb, K, i, keep, lane, wave);
+}
+
+// Scores by fp32 matrix instructions (v_mfma_f32_32x32x2_f32), for up to
+// 1024 key blocks: one workgroup per R = 32 or 64 rows of one query block;
+// wave w computes the 32 x 32 score tiles (row tile w / CT, candidate tile
+// w % CT of each chunk of 32 CT candidates) with the rows' q (A operand:
+// lane (row l % 32, half g) holds d = (D/2) g .. (D/2) g + D/2 - 1) and the
+// candidates' block means (B operand, same split of d) in registers; the
+// scores go to LDS and the rows are ranked as above.  Products and sums are
+// fp32 (their order differs from a sequential dot product only by rounding).
+template <typename T, int TM, int D>
+__global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, const float* __restrict__ mu_all,
+                                                     int32_t* __restrict__ sel, int Hq, int G, int N, int block,
+                                                     int nb, int K, int R) {
+  extern __shared__ __attribute__((aligned(16))) float scores[];   // [R][nb]
+  const int bh = blockIdx.y;
+  const int b = bh / Hq, h = bh % Hq;
+  const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
+  const int t0 = blockIdx.x * R;    // R divides block, so all rows share i
+  const int i = t0 / block;         // own block = number of candidates
+  const int keep = min(K - 1, i);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int32_t* out0 = sel + (static_cast<int64_t>(bh) * N + t0) * K;
+  if (keep == i || keep == 0) {
+    for (int e = tid; e < R * K; e += blockDim.x) {
+      const int slot = e % K;
+      out0[e] = slot < keep ? slot : (slot == keep ? i : -1);
     }
+    return;
+  }
+  const int RT = R / 32, CT = 4 / RT;
+  const int rt = wave / CT, ct = wave % CT;
+  const int g = lane >> 5, col = lane & 31;
+  constexpr int H = D / 2;
+  // A operand: row 32 rt + col, d = H g + k
+  float qa[H];
+  {
+    const T* qr = q + (static_cast<int64_t>(bh) * N + t0 + 32 * rt + col) * D + H * g;
 #pragma unroll
-    for (int w = 0; w < RW; ++w) {
-      int32_t* out = out0 + static_cast<int64_t>(r0 + w) * K;
-      int need = keep;              // places left for codes equal to th
+    for (int k8 = 0; k8 < H; k8 += 8) {
 #pragma unroll
-      for (int t = 0; t < TM; ++t) need -= __popcll(__ballot(u[w][t] > th[w]));
-      int base = 0;
-#pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        {
-          uint64_t eq = __ballot(u[w][t] == th[w]);
-          if (__popcll(eq) > need) {    // keep only the `need` lowest lanes
-            uint64_t take = 0;
-            for (int n = 0; n < need; ++n) {
-              const uint64_t low = eq & (~eq + 1);
-              take |= low;
-              eq ^= low;
-            }
-            eq = take;
-          }
-          need -= __popcll(eq);
-          const uint64_t won = __ballot(u[w][t] > th[w]) | eq;
-          if ((won >> lane) & 1) {
-            const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(won >> 32),
-                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(won), 0));
-            out[base + below] = 64 * t + lane;
-          }
-          base += __popcll(won);
-        }
-      }
-      for (int slot = keep + lane; slot < K; slot += 64) out[slot] = (slot == keep) ? i : -1;
+      for (int e = 0; e < 8; ++e) qa[k8 + e] = to_f32(qr[k8 + e]);
     }
   }
+  const float* mu = mu_all + bc * nb * D;
+  for (int c0 = 0; c0 < i; c0 += 32 * CT) {
+    const int tile0 = c0 + 32 * ct;
+    if (tile0 >= i) continue;                       // uniform
+    const int cand = tile0 + col;
+    const float* mr = mu + static_cast<int64_t>(min(cand, nb - 1)) * D + H * g;
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int k4 = 0; k4 < H; k4 += 4) {
+      const float4 m4 = *reinterpret_cast<const float4*>(mr + k4);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4], m4.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4 + 1], m4.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4 + 2], m4.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4 + 3], m4.w, acc, 0, 0, 0);
+    }
+    // lane (candidate col, g): register e is row 8 (e / 4) + 4 g + e % 4
+    if (cand < i) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        scores[(32 * rt + 8 * (e >> 2) + 4 * g + (e & 3)) * nb + cand] = acc[e];
+    }
+  }
+  __syncthreads();
+  rank_rows<TM>(scores, out0, R, nb, K, i, keep, lane, wave);
+}
+
+// R rows per workgroup for the matrix-scored kernel (0: not applicable).
+static int mfma_rows(const Dims& D) {
+  if (D.block >= 64 && 64 * D.nb * 4 <= 64 * 1024) return 64;
+  if (32 * D.nb * 4 <= 128 * 1024) return 32;
+  return 0;
+}
+
+template <typename T, int TM, int DD>
+static void launch_select_mfma(const Dims& D, int R, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
+  dim3 grid(D.N / R, D.B * D.Hq);
+  const size_t lds = static_cast<size_t>(R) * D.nb * sizeof(float);
+  static size_t granted = 0;     // above 64 KiB of LDS must be requested
+  if (lds > granted) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_select_mfma<T, TM, DD>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    granted = lds;
+  }
+  hipLaunchKernelGGL((k_select_mfma<T, TM, DD>), grid, dim3(256), lds, s, static_cast<const T*>(q), mu, sel, D.Hq,
+                     D.G, D.N, D.block, D.nb, D.K, R);
+}
+
+template <typename T, int TM>
+static void launch_select_mfma_d(const Dims& D, int R, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
+  if (D.d == 64) launch_select_mfma<T, TM, 64>(D, R, q, mu, sel, s);
+  else launch_select_mfma<T, TM, 128>(D, R, q, mu, sel, s);
 }
 
 template <typename T, int TM>
@@ -230,6 +338,15 @@ static void launch_select_tm(const Dims& D, const void* q, const float* mu, int3
 template <typename T>
 static void launch_select_t(const Dims& D, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
   const int tm = (D.nb + 63) / 64;
+  const int R = mfma_rows(D);
+  if (R) {
+    if (tm <= 1) launch_select_mfma_d<T, 1>(D, R, q, mu, sel, s);
+    else if (tm <= 2) launch_select_mfma_d<T, 2>(D, R, q, mu, sel, s);
+    else if (tm <= 4) launch_select_mfma_d<T, 4>(D, R, q, mu, sel, s);
+    else if (tm <= 8) launch_select_mfma_d<T, 8>(D, R, q, mu, sel, s);
+    else launch_select_mfma_d<T, 16>(D, R, q, mu, sel, s);
+    return;
+  }
   if (tm <= 1) launch_select_tm<T, 1>(D, q, mu, sel, s);
   else if (tm <= 2) launch_select_tm<T, 2>(D, q, mu, sel, s);
   else if (tm <= 4) launch_select_tm<T, 4>(D, q, mu, sel, s);

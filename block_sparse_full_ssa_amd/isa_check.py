@@ -54,7 +54,7 @@ def device_asm(source: str) -> str:
         return open(out).read()
 
 
-MFMA_SOURCES = ("fwd_mfma.hip", "bwd_mfma.hip", "sparse_fwd.hip", "sparse_bwd.hip", "bwd_dq.hip")
+MFMA_SOURCES = ("select.hip", "fwd_mfma.hip", "bwd_mfma.hip", "sparse_fwd.hip", "sparse_bwd.hip", "bwd_dq.hip")
 
 
 def main() -> int:
