@@ -1,0 +1,238 @@
+"""GPU parity at the full sizes of the measured layers, on sampled rows.
+
+The whole layer runs through the C ABI exactly as the benchmark runs it
+(selection, dual forward, backward, same shapes and launch configuration).
+The fp64 oracle cannot redo a 16K or 64K layer inside a test, so it checks
+
+* sampled query rows one by one: the selection (rows whose fp64 cutoff
+  margin is below 1e-3 are exempt from the equality check, as screening would
+  have redrawn them; their GPU selection must still be a valid near-optimal
+  one), both streams, their log-sum-exps and delta recomputed by the oracle
+  from the GPU's selection of that row, and dq of those rows;
+* the tail keys of one KV head: dk and dv of the last keys depend only on the
+  queries at or after them, so the oracle gets them exactly from those rows;
+* properties that hold at any size over the whole layer: L_sparsity ==
+  L_commit == mean (h_full - h_sparse)^2 of the outputs, 0 <= delta < 1 with
+  delta = 1 - exp(lse_sparse - lse_full), and the backward sum rules (over a
+  KV head's keys, sum dk = 0 because every softmax Jacobian row sums to zero;
+  sum dv = the sum of the group's stream gradients G_full + G_sparse because
+  every probability row sums to one).
+
+Inputs are the unscreened seeded draws of the workloads (ssa_inputs).
+"""
+from __future__ import annotations
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssa_inputs as si
+from gpu_cases import TOL, assert_close
+
+pytestmark = pytest.mark.gpu
+
+MARGIN = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import block_sparse_full_ssa_amd  # noqa: F401  (fails loudly when libssa is missing)
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def ssa():
+    import block_sparse_full_ssa_amd as m
+    return m
+
+
+def _sample_rows(rng, N, block, K, n):
+    """Positions spanning the whole sequence, including rows that keep every
+    earlier block (own block < top_k) and both ends of a block."""
+    early = rng.integers(0, min(N, K * block), size=max(2, n // 8))
+    edges = np.array([block - 1, block, N - block, N - 1])
+    rest = rng.integers(0, N, size=n - early.size - edges.size)
+    return np.unique(np.concatenate([early, edges, rest]))
+
+
+def _check_selection(name, q_rows, t_idx, mu_c, block, K, gpu_rows):
+    """Equal to the oracle where the fp64 margin is >= MARGIN; elsewhere a
+    valid selection whose scores are within MARGIN of the optimum."""
+    ref, margin = oracle.select_rows(q_rows, t_idx, mu_c, block, K)
+    ok = margin >= MARGIN
+    bad = np.nonzero(ok & np.any(ref != gpu_rows, axis=1))[0]
+    assert bad.size == 0, f"{name}: selection differs on rows {t_idx[bad][:8]}"
+    for r in np.nonzero(~ok)[0]:
+        t, i = int(t_idx[r]), int(t_idx[r]) // block
+        row = gpu_rows[r]
+        kept = row[row >= 0]
+        assert kept.size == min(K, i + 1) and np.all(np.diff(kept) > 0) and kept[-1] == i, (name, t, row)
+        sigma = q_rows[r] @ mu_c[:i].T
+        cutoff = np.sort(sigma)[::-1][min(K - 1, i) - 1]
+        assert np.all(sigma[kept[:-1]] >= cutoff - MARGIN), (name, t)
+    return int((~ok).sum())
+
+
+def _check_rows_fwd(name, wl, b, h, t_idx, qf, kf, vf, sel_np, out, dual=True):
+    c = h // wl.group
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    ref = oracle.attend_rows(qf[b, h, t_idx], t_idx, kf[b, c], vf[b, c], sel_np[b, h, t_idx], wl.block, scale)
+    dt = wl.dtype
+    for key in ("h_full", "h_sparse", "lse_full", "lse_sparse") + (("delta",) if dual else ()):
+        assert_close(f"{name} {key} b{b} h{h}", out[key][b, h, torch.from_numpy(t_idx)], ref[key], dt)
+
+
+def _whole_layer_properties(name, out, dtype):
+    hf = out["h_full"].double()
+    hs = out["h_sparse"].double()
+    L = float(((hf - hs) ** 2).mean())
+    losses = out["losses"].cpu().numpy()
+    assert losses[0] == losses[1]
+    assert abs(losses[0] - L) <= 2e-2 * L + 1e-12, (name, losses, L)
+    delta = out["delta"]
+    assert float(delta.min()) >= 0.0 and float(delta.max()) < 1.0, name
+    expect = -torch.expm1(out["lse_sparse"].double() - out["lse_full"].double())
+    assert float((delta.double() - expect).abs().max()) <= 1e-5, name
+
+
+# ------------------------------------------------------------- 16K training --
+
+def test_train_layer_16k_full_size():
+    """B=2, 32 query / 8 KV heads, N=16384, d=128, block 64, top_k 16: the
+    benchmark's layer, one training step (sparse stream active)."""
+    wl = si.WORKLOADS["train_b2_h32_n16k"]
+    K, mode = wl.top_k, oracle.DUAL_ACTIVE_SPARSE
+    _say(f"full-size {wl.name}: draw")
+    q, k, v, _ = si.draw_qkv(wl, 0)
+    dout = si.draw_dout(wl, 0)
+    qd, kd, vd, gd = (x.to("cuda:0") for x in (q, k, v, dout))
+    _say("  select / fwd / bwd on the GPU")
+    sel = ssa().ssa_select_blocks(qd, kd, wl.block, K)
+    fwd = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, K, mode)
+    dq, dk, dv = ssa().ssa_attn_bwd(qd, kd, vd, sel, fwd, gd, wl.block, K, mode, 1.0, 1.0)
+    torch.cuda.synchronize()
+    out = {key: val.cpu() for key, val in fwd.items() if not key.startswith("_")}
+    sel_np = sel.cpu().numpy()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    del qd, kd, vd, gd, fwd, sel
+
+    _say("  whole-layer properties")
+    _whole_layer_properties(wl.name, out, wl.dtype)
+
+    qf, kf, vf, gf = (si.to_f64(x) for x in (q, k, v, dout))
+    mu = oracle.block_means(kf, wl.block)
+    rng = np.random.default_rng(1)
+    exempt = 0
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    for b, h in ((0, 0), (0, 13), (1, 31)):
+        t_idx = _sample_rows(rng, wl.seqlen, wl.block, K, 24)
+        _say(f"  rows b{b} h{h}: {t_idx.size}")
+        exempt += _check_selection(f"{wl.name} b{b} h{h}", qf[b, h, t_idx], t_idx, mu[b, h // wl.group],
+                                   wl.block, K, sel_np[b, h, t_idx])
+        _check_rows_fwd(wl.name, wl, b, h, t_idx, qf, kf, vf, sel_np, out)
+        ref_dq = oracle.dq_rows(qf, kf, vf, sel_np, wl.block, scale, wl.group, mode, gf, b, h, t_idx)
+        assert_close(f"{wl.name} dq b{b} h{h}", dq[b, h, torch.from_numpy(t_idx)], ref_dq, wl.dtype)
+    _say(f"  selection rows exempt by margin: {exempt}")
+
+    _say("  tail keys of one KV head")
+    i0 = wl.seqlen - 96
+    b, c = 1, 5
+    rk, rv = oracle.dkdv_tail(qf, kf, vf, sel_np, wl.block, scale, wl.group, mode, gf, b, c, i0)
+    assert_close(f"{wl.name} dk tail", dk[b, c, i0:], rk, wl.dtype)
+    assert_close(f"{wl.name} dv tail", dv[b, c, i0:], rv, wl.dtype)
+
+    _say("  backward sum rules")
+    g_f, g_s = oracle.stream_grads(mode, gf, out["h_full"].double().numpy(), out["h_sparse"].double().numpy(),
+                                   1.0, 1.0)
+    G = (g_f + g_s).reshape(wl.batch, wl.hkv, wl.group, wl.seqlen, wl.head_dim).sum(axis=(2, 3))
+    dvs = dv.double().numpy()
+    dks = dk.double().numpy()
+    sum_dv, abs_dv = dvs.sum(axis=2), np.abs(dvs).sum(axis=2)
+    sum_dk, abs_dk = dks.sum(axis=2), np.abs(dks).sum(axis=2)
+    assert np.all(np.abs(sum_dv - G) <= 2 ** -7 * abs_dv + 1e-6), np.abs(sum_dv - G).max()
+    assert np.all(np.abs(sum_dk) <= 2 ** -7 * abs_dk + 1e-6), np.abs(sum_dk).max()
+
+
+# ----------------------------------------------------------- 64K with sinks --
+
+def test_long_layer_64k_sinks_full_size():
+    """B=1, 16 query / 4 KV heads, N=65536, d=128, block 64, top_k 32, four
+    planted sink keys: dual forward with the sparse stream active."""
+    wl = si.WORKLOADS["long_n64k_sinks"]
+    K, mode = wl.top_k, oracle.DUAL_ACTIVE_SPARSE
+    _say(f"full-size {wl.name}: draw")
+    q, k, v, _ = si.draw_qkv(wl, 0)
+    qd, kd, vd = (x.to("cuda:0") for x in (q, k, v))
+    sel = ssa().ssa_select_blocks(qd, kd, wl.block, K)
+    fwd = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, K, mode)
+    torch.cuda.synchronize()
+    out = {key: val.cpu() for key, val in fwd.items() if not key.startswith("_")}
+    sel_np = sel.cpu().numpy()
+    del qd, kd, vd, fwd, sel
+    _whole_layer_properties(wl.name, out, wl.dtype)
+    # the sink block is kept by a large share of the queries
+    share = float((sel_np[..., 0] == 0).mean())
+    _say(f"  rows keeping block 0: {share:.3f}")
+    assert share > 0.3
+
+    qf, kf, vf = (si.to_f64(x) for x in (q, k, v))
+    mu = oracle.block_means(kf, wl.block)
+    rng = np.random.default_rng(2)
+    for b, h in ((0, 0), (0, 11)):
+        t_idx = _sample_rows(rng, wl.seqlen, wl.block, K, 16)
+        _say(f"  rows b{b} h{h}: {t_idx.size}")
+        _check_selection(f"{wl.name} b{b} h{h}", qf[b, h, t_idx], t_idx, mu[b, h // wl.group], wl.block, K,
+                         sel_np[b, h, t_idx])
+        _check_rows_fwd(wl.name, wl, b, h, t_idx, qf, kf, vf, sel_np, out)
+
+
+# ----------------------------------------------------------- 4-layer slice --
+
+def test_multilayer_slice_full_size():
+    """Four layers of B=4, 32 query / 8 KV heads, N=8192, d=128, block 64,
+    top_k 16, each with its own inputs: forward layer 1 to 4, then backward
+    layer 4 to 1, one active stream for the whole step; sampled rows of every
+    layer against the oracle."""
+    wl = si.WORKLOADS["multilayer_b4_n8k_l4"]
+    K = wl.top_k
+    mode = oracle.DUAL_ACTIVE_FULL if si.draw_modes(0, 1)[0] == 0 else oracle.DUAL_ACTIVE_SPARSE
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    saved = []
+    for layer in range(wl.layers):
+        _say(f"full-size {wl.name}: forward layer {layer + 1}")
+        q, k, v, _ = si.draw_qkv(wl, 0, layer)
+        qd, kd, vd = (x.to("cuda:0") for x in (q, k, v))
+        sel = ssa().ssa_select_blocks(qd, kd, wl.block, K)
+        fwd = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, K, mode)
+        saved.append((q, k, v, qd, kd, vd, sel, fwd))
+    grads = [None] * wl.layers
+    for layer in reversed(range(wl.layers)):
+        q, k, v, qd, kd, vd, sel, fwd = saved[layer]
+        gd = si.draw_dout(wl, 0, layer).to("cuda:0")
+        grads[layer] = ssa().ssa_attn_bwd(qd, kd, vd, sel, fwd, gd, wl.block, K, mode)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(3)
+    for layer in range(wl.layers):
+        q, k, v, qd, kd, vd, sel, fwd = saved[layer]
+        out = {key: val.cpu() for key, val in fwd.items() if not key.startswith("_")}
+        _whole_layer_properties(f"{wl.name} layer {layer + 1}", out, wl.dtype)
+        sel_np = sel.cpu().numpy()
+        qf, kf, vf = (si.to_f64(x) for x in (q, k, v))
+        gf = si.to_f64(si.draw_dout(wl, 0, layer))
+        b, h = layer % wl.batch, (7 * layer) % wl.hq
+        t_idx = _sample_rows(rng, wl.seqlen, wl.block, K, 12)
+        _say(f"  layer {layer + 1} rows b{b} h{h}: {t_idx.size}")
+        _check_rows_fwd(f"{wl.name} layer {layer + 1}", wl, b, h, t_idx, qf, kf, vf, sel_np, out)
+        ref_dq = oracle.dq_rows(qf, kf, vf, sel_np, wl.block, scale, wl.group, mode, gf, b, h, t_idx)
+        dq = grads[layer][0].cpu()
+        assert_close(f"{wl.name} layer {layer + 1} dq", dq[b, h, torch.from_numpy(t_idx)], ref_dq, wl.dtype)
+        del qf, kf, vf, gf
