@@ -43,6 +43,42 @@ def pairs(N: int, block: int, K: int):
     return p_full, p_sparse
 
 
+def algorithmic_flops_per_launch(d, pf, ps, heads):
+    """Algorithmic flops that one launch of each bf16 matrix kernel performs
+    (FlashAttention convention: per causal pair 4d forward, 10d backward).
+
+    fwd_mfma:   both streams' forward, 4d (P_full + P_sparse);
+    bwd_mfma:   full stream dK and dV with the S and dP they recompute, 8d P_full;
+    bwd_dq:     full stream dQ, 2d P_full (its own S / dP recompute is extra);
+    bwd_sparse: the sparse stream's whole backward, 10d P_sparse;
+    sparse_part: the sparse-only forward, 4d P_sparse.
+    """
+    return {"fwd_mfma": 4.0 * d * (pf + ps) * heads, "bwd_mfma": 8.0 * d * pf * heads,
+            "bwd_dq": 2.0 * d * pf * heads, "bwd_sparse": 10.0 * d * ps * heads,
+            "sparse_part": 4.0 * d * ps * heads}
+
+
+def measured_traffic(kernel, workload, top_k):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, calibrated by a plain copy), or None when
+    there is none for this workload or the kernel's source changed since."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        table = json.load(f)
+    rec = table.get(f"{kernel}/{workload}/top_k={top_k}")
+    if not rec:
+        return None
+    src = os.path.join(ROOT, "block_sparse_full_ssa_amd", "csrc", rec["source"])
+    with open(src, "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None
+    return rec["bytes_per_launch"]
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -214,14 +250,17 @@ def main():
 
     # dominant kernel and its roofline
     dom = max(kernels, key=lambda n: kernels[n]["total_ms"])
-    per_launch = {"fwd_mfma": 4.0 * d * (pf + ps) * B * Hq, "fwd_simt": 4.0 * d * (pf + ps) * B * Hq,
-                  "bwd_mfma": 10.0 * d * (pf + ps) * B * Hq, "bwd_simt": 10.0 * d * (pf + ps) * B * Hq}
+    per_launch = algorithmic_flops_per_launch(d, pf, ps, B * Hq)
     roofline = None
     if dom in per_launch:
         achieved = per_launch[dom] / (kernels[dom]["avg_ms"] / 1000.0) / 1e12
         roofline = {"kernel": dom, "bound": "mfma", "achieved": round(achieved, 2),
                     "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None}
+                    "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "traffic": measured_traffic(dom, wl.name, K),
+                    "flops_per_launch": per_launch[dom]}
+    kernel_frac = {n: round(per_launch[n] / (kk["avg_ms"] / 1000.0) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+                   for n, kk in kernels.items() if n in per_launch}
 
     sweep = None
     if args.sweep and wl.top_k_sweep:
@@ -262,6 +301,7 @@ def main():
         "algorithmic_flops_per_step": flops,
         "kernels_ms_avg": {n: round(kk["avg_ms"], 4) for n, kk in kernels.items()},
         "roofline": roofline,
+        "kernel_frac_of_bf16_peak": kernel_frac,
         "cpu_baseline": cpu,
     }
     if single:
