@@ -121,7 +121,12 @@ ssa_status_t ssa_select_blocks(const ssa_shape_t* shape, const void* q, const vo
  *   SSA_FULL_ONLY: writes h_full, lse_full; sel, h_sparse, lse_sparse, delta
  *     and losses may be NULL and are not touched.
  *   SSA_SPARSE_ONLY: writes h_sparse, lse_sparse; h_full, lse_full, delta and
- *     losses may be NULL.
+ *     losses may be NULL.  Computed key-block-stationary: the rows that
+ *     selected each key block are gathered, each (row, selected block) gets a
+ *     partial result and the partials are merged by their log-sum-exps, so
+ *     the work follows the selected pairs.  The rows of sel must be ascending
+ *     as ssa_select_blocks writes them; entries above a row's own block are
+ *     ignored.
  * lse pointers may be NULL when the caller will not run the backward.
  */
 ssa_status_t ssa_attn_fwd(const ssa_shape_t* shape, int32_t mode, const void* q,
