@@ -93,7 +93,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-single-stream", action="store_true",
                     help="skip the FULL_ONLY / SPARSE_ONLY measurements")
-    ap.add_argument("--cpu-rows", type=int, default=4096, help="query rows in the CPU-oracle sample")
+    ap.add_argument("--cpu-rows", type=int, default=12288, help="query rows in the CPU-oracle sample")
     return ap.parse_args()
 
 

@@ -121,13 +121,17 @@ static Buckets carve_buckets(const Dims& D, Carver& c) {
 
 struct FwdWs {
   float* row_sq;
+  double* loss_sums;
   Buckets bk;                 // sparse-only forward on buckets
   uint16_t* part_o;
   float* part_lse;
 };
 static FwdWs carve_fwd(const Dims& D, int mode, Carver& c) {
   FwdWs w{};
-  if (mode == kDualFull || mode == kDualSparse) w.row_sq = c.take<float>(D.rows() * sizeof(float));
+  if (mode == kDualFull || mode == kDualSparse) {
+    w.row_sq = c.take<float>(D.rows() * sizeof(float));
+    w.loss_sums = c.take<double>(loss_scratch_bytes());
+  }
   if (mode == kSparseOnly && sparse_fwd_supported(D)) {
     w.bk = carve_buckets(D, c);
     w.part_o = c.take<uint16_t>(bucket_capacity(D) * D.d * sizeof(uint16_t));
@@ -254,7 +258,7 @@ ssa_status_t ssa_attn_fwd(const ssa_shape_t* shape, int32_t mode, const void* q,
   else launch_fwd_simt(D, a, s);
   if ((st = launch_status()) != SSA_OK) return st;
   if (dual) {
-    launch_loss_reduce(w.row_sq, D.rows(), 1.0 / static_cast<double>(D.q_elems()), losses, s);
+    launch_loss_reduce(w.row_sq, D.rows(), 1.0 / static_cast<double>(D.q_elems()), w.loss_sums, losses, s);
     st = launch_status();
   }
   return st;

@@ -45,44 +45,66 @@ constexpr float kLog2e = 1.4426950408889634f;
 // ---------------------------------------------------------------- bwd_pre --
 __global__ void __launch_bounds__(256)
     k_bwd_pre(BwdPreArgs a, int64_t rows, float w_f, float w_s_align, float inv_m) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
-  const int64_t off = row * kD + lane * 2;
+  // 16 lanes per row, 8 elements (16 bytes) each; 16 rows per workgroup
+  const int li = threadIdx.x & 15;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const bool ok = row < rows;
+  const int64_t off = (ok ? row : 0) * kD + 8 * li;
   const bool has_f = a.mode != kSparseOnly, has_s = a.mode != kFullOnly;
   const bool dual = a.mode == kDualFull || a.mode == kDualSparse;
   const bool up_f = a.mode == kDualFull || a.mode == kFullOnly;
-  const uint16_t* dout = static_cast<const uint16_t*>(a.dout);
-  const uint16_t* hf = static_cast<const uint16_t*>(a.h_full);
-  const uint16_t* hs = static_cast<const uint16_t*>(a.h_sparse);
-  float Df = 0.f, Ds = 0.f;
-  uint32_t gfw = 0, gsw = 0;
+  auto load8 = [&](const void* p, float* x) {
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (p && ok) u = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + off);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const float g = dout ? to_f32(bf16_t{dout[off + e]}) : 0.f;
-    const float vf = has_f ? to_f32(bf16_t{hf[off + e]}) : 0.f;
-    const float vs = has_s ? to_f32(bf16_t{hs[off + e]}) : 0.f;
-    float gf = 0.f, gs = 0.f;
-    if (dual) {
-      const float diff = vf - vs;
-      gf = w_f * 2.f * inv_m * diff + (up_f ? g : 0.f);
-      gs = -w_s_align * 2.f * inv_m * diff + (up_f ? 0.f : g);
-    } else {
-      gf = up_f ? g : 0.f;
-      gs = up_f ? 0.f : g;
+    for (int k = 0; k < 4; ++k) {
+      x[2 * k] = __uint_as_float(w[k] << 16);
+      x[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
     }
-    const bf16_t bf = to_bf16(gf), bs = to_bf16(gs);
-    Df += to_f32(bf) * vf;
-    Ds += to_f32(bs) * vs;
-    gfw |= static_cast<uint32_t>(bf.bits) << (16 * e);
-    gsw |= static_cast<uint32_t>(bs.bits) << (16 * e);
+  };
+  float g[8], vf[8], vs[8];
+  load8(a.dout, g);
+  load8(has_f ? a.h_full : nullptr, vf);
+  load8(has_s ? a.h_sparse : nullptr, vs);
+  float Df = 0.f, Ds = 0.f;
+  uint32_t gfw[4], gsw[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float gf2[2], gs2[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int i = 2 * k + e;
+      float gf = 0.f, gs = 0.f;
+      if (dual) {
+        const float diff = vf[i] - vs[i];
+        gf = w_f * 2.f * inv_m * diff + (up_f ? g[i] : 0.f);
+        gs = -w_s_align * 2.f * inv_m * diff + (up_f ? 0.f : g[i]);
+      } else {
+        gf = up_f ? g[i] : 0.f;
+        gs = up_f ? 0.f : g[i];
+      }
+      gf2[e] = to_f32(to_bf16(gf));            // the stored (rounded) gradients
+      gs2[e] = to_f32(to_bf16(gs));
+      Df += gf2[e] * vf[i];
+      Ds += gs2[e] * vs[i];
+    }
+    gfw[k] = pack_bf16x2(gf2[0], gf2[1]);
+    gsw[k] = pack_bf16x2(gs2[0], gs2[1]);
   }
-  if (has_f) *reinterpret_cast<uint32_t*>(a.g_full + off) = gfw;
-  if (has_s) *reinterpret_cast<uint32_t*>(a.g_sparse + off) = gsw;
-  if (a.dq_acc) *reinterpret_cast<float2*>(a.dq_acc + off) = make_float2(0.f, 0.f);
-  Df = wave_sum(Df);
-  Ds = wave_sum(Ds);
-  if (lane == 0) {
+#pragma unroll
+  for (int o = 8; o >= 1; o >>= 1) {
+    Df += __shfl_xor(Df, o, 16);
+    Ds += __shfl_xor(Ds, o, 16);
+  }
+  if (!ok) return;
+  if (has_f) *reinterpret_cast<uint4*>(a.g_full + off) = make_uint4(gfw[0], gfw[1], gfw[2], gfw[3]);
+  if (has_s) *reinterpret_cast<uint4*>(a.g_sparse + off) = make_uint4(gsw[0], gsw[1], gsw[2], gsw[3]);
+  if (a.dq_acc) {
+    *reinterpret_cast<float4*>(a.dq_acc + off) = make_float4(0.f, 0.f, 0.f, 0.f);
+    *reinterpret_cast<float4*>(a.dq_acc + off + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  if (li == 0) {
     if (has_f) {
       a.D_full[row] = Df;
       a.lse2_full[row] = a.lse_full[row] * kLog2e;
@@ -157,17 +179,19 @@ __global__ void __launch_bounds__(256, 1)
   const int qt0 = k0 / kBM;                         // first query tile that sees these keys
   const int iters = G * (nqt - qt0);
 
-  auto iter_coords = [&](int it, int& hq, int& q0) {
-    const int hg = it / (nqt - qt0);
-    hq = c * G + hg;
-    q0 = (qt0 + it % (nqt - qt0)) * kBM;
+  // iteration coordinates (query head, first query), advanced incrementally:
+  // query tiles inner, the group's heads outer
+  auto advance = [&](int& hq, int& q0) {
+    q0 += kBM;
+    if (q0 >= N) {
+      q0 = qt0 * kBM;
+      ++hq;
+    }
   };
   // HBM -> LDS copy of the Q / G_f tiles of one iteration: 16 1 KiB
   // instructions, 4 per wave; lane l fills physical chunk l % 16 of row
   // 4n + l / 16 with the logical chunk stored there.
-  auto load_tiles = [&](int it, uint16_t* Qd, uint16_t* Fd) {
-    int hq, q0;
-    iter_coords(it, hq, q0);
+  auto load_tiles = [&](int hq, int q0, uint16_t* Qd, uint16_t* Fd) {
     const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N + q0;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -183,9 +207,7 @@ __global__ void __launch_bounds__(256, 1)
   };
   // row values (lse2, D) through registers
   float prow = 0.f;
-  auto load_rows = [&](int it) {
-    int hq, q0;
-    iter_coords(it, hq, q0);
+  auto load_rows = [&](int hq, int q0) {
     const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N + q0;
     if (tid < 2 * kBM) {
       const int which = tid >> 5, r = tid & 31;
@@ -194,13 +216,11 @@ __global__ void __launch_bounds__(256, 1)
   };
 
   // one iteration on set (Q, Gf, rv) while the next streams into (Qn, Fn, Rn)
-  auto step = [&](int it, const uint16_t* Q, const uint16_t* Gf, const float* rv, uint16_t* Qn, uint16_t* Fn,
-                  float* Rn) {
-    int hq, q0;
-    iter_coords(it, hq, q0);
+  auto step = [&](int it, int q0, int hq1, int q01, const uint16_t* Q, const uint16_t* Gf, const float* rv,
+                  uint16_t* Qn, uint16_t* Fn, float* Rn) {
     if (it + 1 < iters) {
-      load_rows(it + 1);      // plain loads first: no VMEM load may follow the copies
-      load_tiles(it + 1, Qn, Fn);
+      load_rows(hq1, q01);    // plain loads first: no VMEM load may follow the copies
+      load_tiles(hq1, q01, Qn, Fn);
     }
 
     const bool wave_has_pairs = q0 + kBM - 1 >= kw0 && kw0 < N;   // uniform
@@ -256,17 +276,24 @@ __global__ void __launch_bounds__(256, 1)
     __syncthreads();
   };
 
+  int hq = c * G, q0 = qt0 * kBM;                  // iteration it
+  int hq1 = hq, q01 = q0;                           // iteration it + 1
+  advance(hq1, q01);
   if (iters > 0) {
-    load_tiles(0, Q0, F0);
-    load_rows(0);
+    load_tiles(hq, q0, Q0, F0);
+    load_rows(hq, q0);
     if (tid < 2 * kBM) R0[tid] = prow;
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int it = 0; it < iters; it += 2) {
-    step(it, Q0, F0, R0, Q1, F1, R1);
+    step(it, q0, hq1, q01, Q0, F0, R0, Q1, F1, R1);
+    q0 = q01;
+    advance(hq1, q01);
     if (it + 1 >= iters) break;
-    step(it + 1, Q1, F1, R1, Q0, F0, R0);
+    step(it + 1, q0, hq1, q01, Q1, F1, R1, Q0, F0, R0);
+    q0 = q01;
+    advance(hq1, q01);
   }
 
   // ---- epilogue: dK = scale * dK^T^T (+ sparse stream), dV (+ sparse stream),
@@ -304,7 +331,7 @@ bool bwd_mfma_supported(const Dims& D) { return D.dtype == 1 && D.d == kD; }
 
 void launch_bwd_pre(const Dims& D, const BwdPreArgs& a, float w_sparsity, float w_commit, hipStream_t s) {
   const float inv_m = static_cast<float>(1.0 / static_cast<double>(D.q_elems()));
-  dim3 grid(static_cast<unsigned>((D.rows() + 3) / 4));
+  dim3 grid(static_cast<unsigned>((D.rows() + 15) / 16));
   timing_begin(kKBwdPre, s);
   hipLaunchKernelGGL(k_bwd_pre, grid, dim3(256), 0, s, a, D.rows(), w_sparsity, w_commit, inv_m);
   timing_end(kKBwdPre, s);

@@ -148,7 +148,8 @@ void launch_bwd_sparse(const Dims& D, const SparseBwdArgs& a, hipStream_t s);
 // --- small kernels (misc.hip) ---
 void launch_zero_f32(float* p, int64_t n, hipStream_t s);
 void launch_convert(const float* src, void* dst, int dtype, int64_t n, hipStream_t s);
-void launch_loss_reduce(const float* row_sq, int64_t n_rows, double inv_count, float* losses,
+size_t loss_scratch_bytes();
+void launch_loss_reduce(const float* row_sq, int64_t n_rows, double inv_count, double* scratch, float* losses,
                         hipStream_t s);
 
 }  // namespace ssa

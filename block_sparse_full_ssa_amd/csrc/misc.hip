@@ -47,30 +47,51 @@ void launch_convert(const float* src, void* dst, int dtype, int64_t n, hipStream
   timing_end(kKConvert, s);
 }
 
-// One workgroup: thread t adds partials t, t+1024, ... in fp64, then a fixed
-// tree combines the 1024 sums.
-__global__ void __launch_bounds__(1024) k_loss_reduce(const float* __restrict__ part, int64_t n,
-                                                      double inv_count, float* __restrict__ losses) {
-  __shared__ double buf[1024];
-  double acc = 0.0;
-  for (int64_t i = threadIdx.x; i < n; i += 1024) acc += static_cast<double>(part[i]);
+// Two levels, both in a fixed order (deterministic): workgroup w adds the
+// contiguous chunk w of the row partials in fp64 (thread strides, then a
+// tree), then one workgroup adds the kLossParts workgroup sums by a tree.
+constexpr int kLossParts = 256;
+
+__device__ __forceinline__ double block_sum_f64(double acc, double* buf) {
   buf[threadIdx.x] = acc;
   __syncthreads();
-  for (int w = 512; w >= 1; w >>= 1) {
-    if (threadIdx.x < w) buf[threadIdx.x] += buf[threadIdx.x + w];
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (static_cast<int>(threadIdx.x) < w) buf[threadIdx.x] += buf[threadIdx.x + w];
     __syncthreads();
   }
+  return buf[0];
+}
+
+__global__ void __launch_bounds__(256) k_loss_partial(const float* __restrict__ part, int64_t n,
+                                                      double* __restrict__ sums) {
+  __shared__ double buf[256];
+  const int64_t chunk = (n + kLossParts - 1) / kLossParts;
+  const int64_t i0 = static_cast<int64_t>(blockIdx.x) * chunk;
+  const int64_t i1 = i0 + chunk < n ? i0 + chunk : n;
+  double acc = 0.0;
+  for (int64_t i = i0 + threadIdx.x; i < i1; i += 256) acc += static_cast<double>(part[i]);
+  const double t = block_sum_f64(acc, buf);
+  if (threadIdx.x == 0) sums[blockIdx.x] = t;
+}
+
+__global__ void __launch_bounds__(256) k_loss_final(const double* __restrict__ sums, double inv_count,
+                                                    float* __restrict__ losses) {
+  __shared__ double buf[256];
+  const double t = block_sum_f64(sums[threadIdx.x], buf);
   if (threadIdx.x == 0) {
-    const float L = static_cast<float>(buf[0] * inv_count);
+    const float L = static_cast<float>(t * inv_count);
     losses[0] = L;   // L_sparsity
     losses[1] = L;   // L_commit
   }
 }
 
-void launch_loss_reduce(const float* row_sq, int64_t n_rows, double inv_count, float* losses,
+size_t loss_scratch_bytes() { return kLossParts * sizeof(double); }
+
+void launch_loss_reduce(const float* row_sq, int64_t n_rows, double inv_count, double* scratch, float* losses,
                         hipStream_t s) {
   timing_begin(kKLossReduce, s);
-  hipLaunchKernelGGL(k_loss_reduce, dim3(1), dim3(1024), 0, s, row_sq, n_rows, inv_count, losses);
+  hipLaunchKernelGGL(k_loss_partial, dim3(kLossParts), dim3(256), 0, s, row_sq, n_rows, scratch);
+  hipLaunchKernelGGL(k_loss_final, dim3(1), dim3(256), 0, s, scratch, inv_count, losses);
   timing_end(kKLossReduce, s);
 }
 
