@@ -113,11 +113,13 @@ __global__ void __launch_bounds__(256, 2)
         const bool diag = kbase + 31 > wave_q0;      // uniform
         float dsv[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kbase + 8 * (i >> 2) + 4 * g + (i & 3);
-          const bool live = !diag || key <= qrow;
-          const float p = live ? fast_exp2(s[i] * scale_log2 - lse2) : 0.f;
-          dsv[i] = p * (dp[i] - Dq);
+        for (int i = 0; i < 16; ++i) dsv[i] = fast_exp2(s[i] * scale_log2 - lse2) * (dp[i] - Dq);
+        if (diag) {                  // uniform: only the diagonal tiles need the causal mask
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kbase + 8 * (i >> 2) + 4 * g + (i & 3);
+            dsv[i] = key <= qrow ? dsv[i] : 0.f;
+          }
         }
         // ---- dQ^T += K^T dS^T over the 32 keys (two k-steps of 16)
 #pragma unroll

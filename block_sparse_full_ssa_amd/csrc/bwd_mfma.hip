@@ -250,9 +250,16 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * a4 + e;
-          const bool live = !diag || key <= q0 + qb + e;
-          pf[i] = live ? fast_exp2(s[i] * scale_log2 - lfa[e]) : 0.f;
+          pf[i] = fast_exp2(s[i] * scale_log2 - lfa[e]);
           dsv[i] = pf[i] * (dpf[i] - dfa[e]);
+        }
+      }
+      if (diag) {                 // uniform: only tiles that straddle the diagonal need the causal mask
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const bool live = key <= q0 + 8 * (i >> 2) + 4 * g + (i & 3);
+          pf[i] = live ? pf[i] : 0.f;
+          dsv[i] = live ? dsv[i] : 0.f;
         }
       }
       // ---- dV^T += G^T P, dK^T += Q^T dS  (k = queries; 2 steps of 16)
