@@ -30,8 +30,13 @@ constexpr int kTile = kBN * kD;
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-// Physical 16-byte chunk of logical chunk c in a 256-byte row r.
-__device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
+// Physical 16-byte chunk of logical chunk c in a 256-byte K / V row r (K is
+// read by rows and by transposes).
+// The transposed tiles use c ^ (2 (r % 8) + (r / 8) % 2): measured on gfx950
+// it keeps the transpose reads (ds_read_b64_tr_b16) free of bank conflicts
+// as well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave
+// the transpose reads two-way conflicted.
+__device__ __forceinline__ int swz_k(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
 
 __global__ void __launch_bounds__(256, 2)
     k_bwd_dq(BwdDqArgs a, int Hq, int G, int N, float scale, float scale_log2, int n_qtiles) {

@@ -117,10 +117,13 @@ __global__ void __launch_bounds__(256)
 }
 
 // --------------------------------------------------------------- bwd_mfma --
-// Physical 16-byte chunk of logical chunk c: Q / G tiles (256-byte rows) and
-// dS^T tiles (64-byte rows).  Both the row reads of matrix operands and the
-// transpose reads then spread over all banks.
-__device__ __forceinline__ int swz_t(int r, int c) { return c ^ (r & 7); }
+// Physical 16-byte chunk of logical chunk c in a 256-byte Q / G row r (read by
+// rows and by transposes).
+// The transposed tiles use c ^ (2 (r % 8) + (r / 8) % 2): measured on gfx950
+// it keeps the transpose reads (ds_read_b64_tr_b16) free of bank conflicts
+// as well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave
+// the transpose reads two-way conflicted.
+__device__ __forceinline__ int swz_t(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;

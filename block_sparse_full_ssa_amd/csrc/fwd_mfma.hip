@@ -51,9 +51,14 @@ typedef __attribute__((address_space(1))) void glb_void;
 
 enum { kModeDual = 0, kModeFull = 1, kModeSparse = 2 };
 
-// Physical 16-byte chunk of logical chunk c in row r.
+// Physical 16-byte chunk of logical chunk c in row r: K tiles are only read
+// by rows; V tiles by transpose reads.
+// The transposed tiles use c ^ (2 (r % 8) + (r / 8) % 2): measured on gfx950
+// it keeps the transpose reads (ds_read_b64_tr_b16) free of bank conflicts
+// as well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave
+// the transpose reads two-way conflicted.
 __device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
-__device__ __forceinline__ int swz_v(int r, int c) { return c ^ (((r >> 2) & 3) << 2); }
+__device__ __forceinline__ int swz_v(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
 
 __device__ __forceinline__ float max16(const f32x16& v) {
   float m = fmaxf(v[0], v[1]);

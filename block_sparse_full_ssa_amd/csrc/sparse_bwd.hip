@@ -32,7 +32,13 @@ namespace {
 
 constexpr int kD = 128;
 
-__device__ __forceinline__ int swz_t(int r, int c) { return c ^ (r & 7); }
+// Physical 16-byte chunk of logical chunk c: 256-byte Q / G rows (read by rows
+// and by transposes), 64-byte dS^T rows.
+// The transposed tiles use c ^ (2 (r % 8) + (r / 8) % 2): measured on gfx950
+// it keeps the transpose reads (ds_read_b64_tr_b16) free of bank conflicts
+// as well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave
+// the transpose reads two-way conflicted.
+__device__ __forceinline__ int swz_t(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
 __device__ __forceinline__ int swz_s(int r, int c) { return c ^ ((r >> 1) & 3); }
 
 typedef __attribute__((address_space(3))) void lds_void;

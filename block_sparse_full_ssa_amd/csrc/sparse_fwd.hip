@@ -35,7 +35,13 @@ namespace {
 constexpr int kD = 128;
 constexpr float kLn2 = 0.69314718055994531f;
 
-__device__ __forceinline__ int swz_v(int r, int c) { return c ^ (((r >> 2) & 3) << 2); }
+// Physical 16-byte chunk of logical chunk c in a 256-byte V row r (read by
+// transposes).
+// The transposed tiles use c ^ (2 (r % 8) + (r / 8) % 2): measured on gfx950
+// it keeps the transpose reads (ds_read_b64_tr_b16) free of bank conflicts
+// as well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave
+// the transpose reads two-way conflicted.
+__device__ __forceinline__ int swz_v(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
 
 // Physical 16-byte chunk of logical chunk c in a 256-byte K row r.
 __device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
