@@ -259,14 +259,23 @@ __global__ void __launch_bounds__(512, 1)
       // ---- S = Q K^T, dP = G_f V^T  [32 q x 32 keys], two independent
       // accumulation chains interleaved; lane: key col, queries 8(i/4)+4g+(i%4)
       f32x16 s = f32x16{}, dpf = f32x16{};
+      bf16x8 ok[8], ov[8], oq[8], of[8];
+      auto rd = [&](int ds) {
+        const int cs = 16 * (ds ^ c7);   // the same chunk for query row col and key row 32 kq + col
+        ok[ds] = lds_read8(&Kt[rowk + cs]);
+        ov[ds] = lds_read8(&Vt[rowk + cs]);
+        oq[ds] = lds_read8(&Qs[rowq + cs]);
+        of[ds] = lds_read8(&Fs[rowq + cs]);
+      };
+      rd(0);
 #pragma unroll
       for (int ds = 0; ds < kD / 16; ++ds) {
-        const int cs = 16 * (ds ^ c7);   // the same chunk for query row col and key row 32 kq + col
-        const bf16x8 kb = lds_read8(&Kt[rowk + cs]);
-        const bf16x8 vb = lds_read8(&Vt[rowk + cs]);
-        s = mfma32x32x16(lds_read8(&Qs[rowq + cs]), kb, s);
-        dpf = mfma32x32x16(lds_read8(&Fs[rowq + cs]), vb, dpf);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ds + 1 < kD / 16) rd(ds + 1);
+        s = mfma32x32x16(oq[ds], ok[ds], s);
+        dpf = mfma32x32x16(of[ds], ov[ds], dpf);
       }
+      __builtin_amdgcn_sched_barrier(0);
       // ---- probabilities and dS, packed to bf16 pairs (register i: query
       // 8(i/4) + 4g + i%4, visible iff 8(i/4) + i%4 >= t on diagonal tiles)
       const int t = kw0 + col - q0 - 4 * g;
@@ -295,18 +304,26 @@ __global__ void __launch_bounds__(512, 1)
         dsp[2 * a4 + 1] = pack_bf16x2(e[2], e[3]);
       }
       // ---- dV^T += G^T P, dK^T += Q^T dS  (k = queries; 2 steps of 16)
+      bf16x8 bpf[2], bds[2], tg[8], tq[8];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const bf16x8 bpf = __builtin_bit_cast(bf16x8, make_uint4(pfp[4 * st], pfp[4 * st + 1], pfp[4 * st + 2], pfp[4 * st + 3]));
-        const bf16x8 bds = __builtin_bit_cast(bf16x8, make_uint4(dsp[4 * st], dsp[4 * st + 1], dsp[4 * st + 2], dsp[4 * st + 3]));
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const int cx = 2048 * st + 32 * (dt ^ tx);
-          const int o0 = tb0 + cx, o1 = tb1 + cx;
-          dv[dt] = mfma32x32x16(lds_tr_pair(&Fs[o0], &Fs[o1]), bpf, dv[dt]);
-          dk[dt] = mfma32x32x16(lds_tr_pair(&Qs[o0], &Qs[o1]), bds, dk[dt]);
-        }
+        bpf[st] = __builtin_bit_cast(bf16x8, make_uint4(pfp[4 * st], pfp[4 * st + 1], pfp[4 * st + 2], pfp[4 * st + 3]));
+        bds[st] = __builtin_bit_cast(bf16x8, make_uint4(dsp[4 * st], dsp[4 * st + 1], dsp[4 * st + 2], dsp[4 * st + 3]));
       }
+      auto rdB = [&](int u) {
+        const int cx = 2048 * (u >> 2) + 32 * ((u & 3) ^ tx);
+        tg[u] = lds_tr_pair(&Fs[tb0 + cx], &Fs[tb1 + cx]);
+        tq[u] = lds_tr_pair(&Qs[tb0 + cx], &Qs[tb1 + cx]);
+      };
+      rdB(0);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (u + 1 < 8) rdB(u + 1);
+        dv[u & 3] = mfma32x32x16(tg[u], bpf[u >> 2], dv[u & 3]);
+        dk[u & 3] = mfma32x32x16(tq[u], bds[u >> 2], dk[u & 3]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (more && tid < 4 * kBM) Rn[tid] = prow;
     __builtin_amdgcn_s_waitcnt(0);     // next tiles landed
