@@ -107,12 +107,21 @@ __global__ void __launch_bounds__(256, 2)
         f32x16 s = f32x16{}, dp = f32x16{};
         {
           const int r = kh * 32 + col;
-#pragma unroll
-          for (int ds = 0; ds < kD / 16; ++ds) {
+          bf16x8 ok[kD / 16], ov[kD / 16];
+          auto rd = [&](int ds) {
             const int off = r * kD + 8 * swz_k(r, 2 * ds + g);
-            s = mfma32x32x16(lds_read8(&Ks[off]), qreg[ds], s);
-            dp = mfma32x32x16(lds_read8(&Vs[off]), greg[ds], dp);
+            ok[ds] = lds_read8(&Ks[off]);
+            ov[ds] = lds_read8(&Vs[off]);
+          };
+          rd(0);
+#pragma unroll
+          for (int ds = 0; ds < kD / 16; ++ds) {      // operands read one step ahead
+            __builtin_amdgcn_sched_barrier(0);
+            if (ds + 1 < kD / 16) rd(ds + 1);
+            s = mfma32x32x16(ok[ds], qreg[ds], s);
+            dp = mfma32x32x16(ov[ds], greg[ds], dp);
           }
+          __builtin_amdgcn_sched_barrier(0);
         }
         // ---- dS^T = P^T (dP^T - D); key of register i: kbase + 8(i/4) + 4g + i%4
         const bool diag = kbase + 31 > wave_q0;      // uniform
@@ -127,18 +136,25 @@ __global__ void __launch_bounds__(256, 2)
           }
         }
         // ---- dQ^T += K^T dS^T over the 32 keys (two k-steps of 16)
+        bf16x8 bds[2], ka[8];
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const bf16x8 bds = to_bf16x8(dsv[8 * st], dsv[8 * st + 1], dsv[8 * st + 2], dsv[8 * st + 3],
-                                       dsv[8 * st + 4], dsv[8 * st + 5], dsv[8 * st + 6], dsv[8 * st + 7]);
+        for (int st = 0; st < 2; ++st)
+          bds[st] = to_bf16x8(dsv[8 * st], dsv[8 * st + 1], dsv[8 * st + 2], dsv[8 * st + 3], dsv[8 * st + 4],
+                              dsv[8 * st + 5], dsv[8 * st + 6], dsv[8 * st + 7]);
+        auto rdk = [&](int u) {
+          const int st = u >> 2, dt = u & 3;
           const int r0 = kh * 32 + st * 16 + 4 * gk + srow, r1 = r0 + 8;
+          const int c = 4 * dt + 2 * (grp & 1) + (m4 >> 1), e = 4 * (m4 & 1);
+          ka[u] = lds_tr_pair(&Ks[r0 * kD + 8 * swz_k(r0, c) + e], &Ks[r1 * kD + 8 * swz_k(r1, c) + e]);
+        };
+        rdk(0);
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            const int c = 4 * dt + 2 * (grp & 1) + (m4 >> 1), e = 4 * (m4 & 1);
-            const bf16x8 ka = lds_tr_pair(&Ks[r0 * kD + 8 * swz_k(r0, c) + e], &Ks[r1 * kD + 8 * swz_k(r1, c) + e]);
-            dq[dt] = mfma32x32x16(ka, bds, dq[dt]);
-          }
+        for (int u = 0; u < 8; ++u) {                 // K^T read one step ahead
+          __builtin_amdgcn_sched_barrier(0);
+          if (u + 1 < 8) rdk(u + 1);
+          dq[u & 3] = mfma32x32x16(ka[u], bds[u >> 2], dq[u & 3]);
         }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     __builtin_amdgcn_s_waitcnt(0);     // the next tile has landed in LDS
