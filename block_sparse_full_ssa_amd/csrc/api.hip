@@ -145,9 +145,11 @@ struct BwdWs {
   float *dk_acc, *dv_acc;
   // MFMA path
   uint16_t *g_full, *g_sparse;
-  float *D_full, *D_sparse, *lse2_full, *lse2_sparse, *dq_acc;
+  float *D_full, *D_sparse, *lse2_full, *lse2_sparse;
+  float* dq_acc;              // sparse-only: the sparse stream's fp32 dQ
   Buckets bk;                 // sparse stream
-  float *dk_part, *dv_part;   // sparse-stream dK / dV in training modes
+  float *dk_part, *dv_part;   // training modes: the sparse stream's fp32 dK / dV
+  uint16_t* ds_rows;          // training modes: the sparse stream's dS rows for the dQ kernel
 };
 static BwdWs carve_bwd(const Dims& D, int mode, Carver& c) {
   BwdWs w{};
@@ -167,8 +169,9 @@ static BwdWs carve_bwd(const Dims& D, int mode, Carver& c) {
     if (f && sp) {
       w.dk_part = c.take<float>(D.kv_elems() * sizeof(float));
       w.dv_part = c.take<float>(D.kv_elems() * sizeof(float));
+      w.ds_rows = c.take<uint16_t>(static_cast<size_t>(bucket_capacity(D)) * D.block * sizeof(uint16_t));
     }
-    if (sp) w.dq_acc = c.take<float>(D.q_elems() * sizeof(float));
+    if (sp && !f) w.dq_acc = c.take<float>(D.q_elems() * sizeof(float));
   } else {
     w.dk_acc = c.take<float>(D.kv_elems() * sizeof(float));
     w.dv_acc = c.take<float>(D.kv_elems() * sizeof(float));
@@ -284,9 +287,10 @@ ssa_status_t ssa_attn_bwd(const ssa_shape_t* shape, int32_t mode, float w_sparsi
   Carver c{static_cast<char*>(ws)};
   BwdWs w = carve_bwd(D, mode, c);
   if (bwd_mfma_supported(D)) {
-    // stream gradients, then the sparse stream on key-block buckets (fp32 dQ,
-    // and dK / dV as fp32 partials when the full stream follows), then the
-    // full stream's dK / dV and dQ, each adding the sparse stream's part
+    // stream gradients, then the sparse stream on key-block buckets (sparse
+    // alone: dK / dV and an fp32 dQ; training modes: dK / dV as fp32 partials
+    // and the rows of dS), then the full stream's dK / dV and dQ, each adding
+    // the sparse stream's part
     BwdPreArgs p{d_out, h_full, h_sparse, lse_full, lse_sparse, w.g_full, w.g_sparse, w.D_full, w.D_sparse,
                  w.lse2_full, w.lse2_sparse, w.dq_acc, mode};
     launch_bwd_pre(D, p, w_sparsity, w_commit, s);
@@ -295,7 +299,7 @@ ssa_status_t ssa_attn_bwd(const ssa_shape_t* shape, int32_t mode, float w_sparsi
       launch_buckets(D, sel, w.bk, s);
       if ((st = launch_status()) != SSA_OK) return st;
       SparseBwdArgs sp{q, k, v, w.bk.offs, w.bk.rows, w.g_sparse, w.lse2_sparse, w.D_sparse, w.dq_acc,
-                       w.dk_part, w.dv_part, dk, dv};
+                       w.ds_rows, w.dk_part, w.dv_part, dk, dv};
       launch_bwd_sparse(D, sp, s);
       if ((st = launch_status()) != SSA_OK) return st;
     }
@@ -306,7 +310,8 @@ ssa_status_t ssa_attn_bwd(const ssa_shape_t* shape, int32_t mode, float w_sparsi
     BwdMainArgs m{q, k, v, w.g_full, w.lse2_full, w.D_full, dk, dv, w.dk_part, w.dv_part};
     launch_bwd_mfma(D, m, s);
     if ((st = launch_status()) != SSA_OK) return st;
-    BwdDqArgs dqa{q, k, v, w.g_full, w.lse2_full, w.D_full, w.dq_acc, dq};
+    BwdDqArgs dqa{q, k, v, w.g_full, w.lse2_full, w.D_full, w.ds_rows ? w.bk.mask : nullptr,
+                  w.ds_rows ? w.bk.wpos : nullptr, w.ds_rows, dq};
     launch_bwd_dq(D, dqa, s);
     return launch_status();
   }

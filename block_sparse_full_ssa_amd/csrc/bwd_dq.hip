@@ -12,8 +12,12 @@
 // with K^T read from the same K tile by transpose reads.  K / V tiles move
 // HBM -> LDS double-buffered, one barrier per tile.
 //
-// The epilogue adds the sparse stream's fp32 dQ (training modes) and writes
-// bf16.
+// Training modes add the sparse stream here as well: its dS rows (written by
+// the bucketed sparse backward, bf16) for the wave's queries that selected a
+// half's key block are added to the full stream's dS^T before the product,
+// so both streams share one dQ^T accumulation and no atomics are needed.  A
+// wave's 32 queries are one word of the block's bucket mask; a selected
+// query's row is entry wpos + popcount of the word's lower bits.
 
 #include "common.h"
 #include "internal.h"
@@ -38,8 +42,9 @@ typedef __attribute__((address_space(1))) void glb_void;
 // the transpose reads two-way conflicted.
 __device__ __forceinline__ int swz_k(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
 
+template <bool SPARSE>
 __global__ void __launch_bounds__(256, 2)
-    k_bwd_dq(BwdDqArgs a, int Hq, int G, int N, float scale, float scale_log2, int n_qtiles) {
+    k_bwd_dq(BwdDqArgs a, int Hq, int G, int N, int nb, int block, float scale, float scale_log2, int n_qtiles) {
   __shared__ __attribute__((aligned(16))) uint16_t K0[kTile], K1[kTile], V0[kTile], V1[kTile];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -103,6 +108,19 @@ __global__ void __launch_bounds__(256, 2)
       for (int kh = 0; kh < 2; ++kh) {
         const int kbase = j * kBN + kh * 32;
         if (kbase > wave_last_q) break;                // uniform: later keys are all masked
+        // the sparse stream's dS of this half for the queries that selected its block
+        uint4 sd0 = make_uint4(0, 0, 0, 0), sd1 = sd0;
+        if constexpr (SPARSE) {
+          const int blk = kbase / block;                 // uniform
+          const int64_t w = ((bc * nb + blk) * G + h % G) * (N / 32) + wave_q0 / 32;
+          const uint32_t m = __builtin_amdgcn_readfirstlane(a.mask[w]);
+          if (m != 0u && ((m >> col) & 1u)) {
+            const int e = a.wpos[w] + __builtin_popcount(m & ((1u << col) - 1u));
+            const uint16_t* src = a.ds_rows + static_cast<int64_t>(e) * block + (kbase - blk * block) + 16 * g;
+            sd0 = *reinterpret_cast<const uint4*>(src);
+            sd1 = *reinterpret_cast<const uint4*>(src + 8);
+          }
+        }
         // ---- S^T = K Q^T, dP^T = V G^T for 32 keys (A: key row kh*32 + col)
         f32x16 s = f32x16{}, dp = f32x16{};
         {
@@ -134,6 +152,12 @@ __global__ void __launch_bounds__(256, 2)
             const int key = kbase + 8 * (i >> 2) + 4 * g + (i & 3);
             dsv[i] = key <= qrow ? dsv[i] : 0.f;
           }
+        }
+        if constexpr (SPARSE) {                      // element i of the row: the key of register i
+          const uint32_t sw[8] = {sd0.x, sd0.y, sd0.z, sd0.w, sd1.x, sd1.y, sd1.z, sd1.w};
+#pragma unroll
+          for (int i = 0; i < 16; ++i)
+            dsv[i] += __uint_as_float((i & 1) ? (sw[i >> 1] & 0xffff0000u) : (sw[i >> 1] << 16));
         }
         // ---- dQ^T += K^T dS^T over the 32 keys (two k-steps of 16)
         bf16x8 bds[2], ka[8];
@@ -170,7 +194,7 @@ __global__ void __launch_bounds__(256, 2)
     step(j + 1, K1, V1, K0, V0);
   }
 
-  // ---- epilogue: dq = scale dQ^T^T (+ the sparse stream's fp32 dQ), bf16
+  // ---- epilogue: dq = scale dQ^T^T, bf16
   if (!wave_live || qrow >= N) return;
   uint16_t* out = static_cast<uint16_t*>(a.dq) + row * kD;
 #pragma unroll
@@ -178,11 +202,9 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int d0 = 32 * dt + 8 * i4 + 4 * g;
-      float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (a.dq_sparse) x = *reinterpret_cast<const float4*>(a.dq_sparse + row * kD + d0);
       *reinterpret_cast<uint2*>(out + d0) =
-          make_uint2(pack_bf16x2(scale * dq[dt][4 * i4] + x.x, scale * dq[dt][4 * i4 + 1] + x.y),
-                     pack_bf16x2(scale * dq[dt][4 * i4 + 2] + x.z, scale * dq[dt][4 * i4 + 3] + x.w));
+          make_uint2(pack_bf16x2(scale * dq[dt][4 * i4], scale * dq[dt][4 * i4 + 1]),
+                     pack_bf16x2(scale * dq[dt][4 * i4 + 2], scale * dq[dt][4 * i4 + 3]));
     }
 }
 
@@ -192,8 +214,12 @@ void launch_bwd_dq(const Dims& D, const BwdDqArgs& a, hipStream_t s) {
   const int n_qtiles = (D.N + kBM - 1) / kBM;
   dim3 grid(D.B * D.Hq, n_qtiles);
   timing_begin(kKBwdDq, s);
-  hipLaunchKernelGGL(k_bwd_dq, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.scale, D.scale * 1.4426950408889634f,
-                     n_qtiles);
+  if (a.ds_rows)
+    hipLaunchKernelGGL(k_bwd_dq<true>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.block, D.scale,
+                       D.scale * 1.4426950408889634f, n_qtiles);
+  else
+    hipLaunchKernelGGL(k_bwd_dq<false>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.block, D.scale,
+                       D.scale * 1.4426950408889634f, n_qtiles);
   timing_end(kKBwdDq, s);
 }
 

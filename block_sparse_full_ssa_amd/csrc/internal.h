@@ -98,7 +98,12 @@ struct BwdDqArgs {                  // dQ
   const void *q, *k, *v;
   const uint16_t* g_full;
   const float *lse2_full, *D_full;
-  const float* dq_sparse;           // fp32 sparse-stream dQ to add (training modes) or null
+  // training modes: the sparse stream's buckets and dS rows (bf16 [bucket
+  // entries][block], 32-key groups in the kernel's lane order), added to the
+  // full stream's dS before the dQ product; null for the full stream alone
+  const uint32_t* mask;
+  const int32_t* wpos;
+  const uint16_t* ds_rows;
   void* dq;
 };
 void launch_bwd_dq(const Dims& D, const BwdDqArgs& a, hipStream_t s);
@@ -138,7 +143,8 @@ struct SparseBwdArgs {
   const int32_t *offs, *rows;           // buckets
   const uint16_t* g_sparse;             // bf16 G_s [rows][d]
   const float *lse2_sparse, *D_sparse;
-  float* dq_acc;                        // fp32 [rows][d], added to atomically
+  float* dq_acc;                        // fp32 [rows][d], added to atomically (when ds_rows is null)
+  uint16_t* ds_rows;                    // bf16 [bucket entries][block] dS rows for the dQ kernel, or null
   float *dk_part, *dv_part;             // fp32 [B*Hkv][N][d] results, or null: write dk, dv (bf16)
   void *dk, *dv;
 };

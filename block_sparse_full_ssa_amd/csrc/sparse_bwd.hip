@@ -44,7 +44,7 @@ __device__ __forceinline__ int swz_s(int r, int c) { return c ^ ((r >> 1) & 3); 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-template <int KH>
+template <int KH, bool DSOUT>
 __global__ void __launch_bounds__(256, 1)
     k_bwd_sparse(SparseBwdArgs a, int Hq, int G, int N, int nb, float scale, float scale_log2) {
   constexpr int kBlk = 32 * KH;
@@ -134,14 +134,16 @@ __global__ void __launch_bounds__(256, 1)
   // dQ B operands [16 keys x 32 d]: d = slice + 32 dt + col, keys of k-step ks
   // in the transpose-read order of the dS^T tile
   constexpr int kDt = kSlice / 32;
-  bf16x8 kq[2 * KH][kDt];
+  bf16x8 kq[DSOUT ? 1 : 2 * KH][kDt];
+  if constexpr (!DSOUT) {
 #pragma unroll
-  for (int ks = 0; ks < 2 * KH; ++ks)
+    for (int ks = 0; ks < 2 * KH; ++ks)
 #pragma unroll
-    for (int dt = 0; dt < kDt; ++dt) {
-      const uint16_t* p = &Kst[(16 * ks + 4 * gk + srow) * kD + kSlice * kh + 32 * dt + sub16 + 4 * m4];
-      kq[ks][dt] = lds_tr_pair(p, p + 8 * kD);
-    }
+      for (int dt = 0; dt < kDt; ++dt) {
+        const uint16_t* p = &Kst[(16 * ks + 4 * gk + srow) * kD + kSlice * kh + 32 * dt + sub16 + 4 * m4];
+        kq[ks][dt] = lds_tr_pair(p, p + 8 * kD);
+      }
+  }
 
   const int nbat = (n + 31) >> 5;
   const int iters = (nbat + QS - 1) / QS;
@@ -256,6 +258,30 @@ __global__ void __launch_bounds__(256, 1)
           *reinterpret_cast<uint2*>(&dSs[r * 32 + 8 * swz_s(r, a4) + 4 * g]) = u;
         }
       }
+      if constexpr (DSOUT) {
+        // ---- the rows of dS of this wave's 32 keys -> HBM for the query-
+        // stationary dQ: the transposes of the wave's own dS^T rows for k-step
+        // ks = 2 kh + h give lane (query col, g) element s = key 16 ks +
+        // 8 (s / 4) + 4 g + s % 4.  A row of 32 keys is stored in the dQ
+        // kernel's lane order, position 16 g' + 4 a + e for key 8 a + 4 g' + e,
+        // so that element s of half h goes to position 16 g + 8 h + s.
+        // (the transposes take all lanes: a lane's result holds other lanes' reads)
+        uint4 u[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int ks = 2 * kh + h;
+          const int r0 = 16 * ks + 4 * gk + srow, r1 = r0 + 8;
+          const int cl = 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
+          u[h] = __builtin_bit_cast(
+              uint4, lds_tr_pair(&dSs[r0 * 32 + 8 * swz_s(r0, cl) + e4], &dSs[r1 * 32 + 8 * swz_s(r1, cl) + e4]));
+        }
+        const int idx = (it * QS + qs) * 32 + col;
+        if (idx < n) {
+          uint16_t* dst = a.ds_rows + static_cast<int64_t>(p0 + idx) * kBlk + 32 * kh;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) *reinterpret_cast<uint4*>(dst + 16 * g + 8 * h) = u[h];
+        }
+      }
       // ---- dV^T += G_s^T P, dK^T += Q^T dS  (k = queries; 2 steps of 16)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -277,7 +303,7 @@ __global__ void __launch_bounds__(256, 1)
     __syncthreads();
 
     // ---- dQ[32 q x slice] of the stream's batch = dS[32 q x block keys] K[block keys x slice]
-    if (has) {
+    if (!DSOUT && has) {
       f32x16 dq[kDt];
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) dq[dt] = f32x16{};
@@ -355,12 +381,13 @@ void launch_bwd_sparse(const Dims& D, const SparseBwdArgs& a, hipStream_t s) {
   dim3 grid(D.B * D.Hkv, D.nb);
   const float scale_log2 = D.scale * 1.4426950408889634f;
   timing_begin(kKBwdSparse, s);
-  if (D.block == 32)
-    hipLaunchKernelGGL(k_bwd_sparse<1>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.scale, scale_log2);
-  else if (D.block == 64)
-    hipLaunchKernelGGL(k_bwd_sparse<2>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.scale, scale_log2);
-  else
-    hipLaunchKernelGGL(k_bwd_sparse<4>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.scale, scale_log2);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.scale, scale_log2);
+  };
+  const bool rows_out = a.ds_rows != nullptr;
+  if (D.block == 32) rows_out ? go(k_bwd_sparse<1, true>) : go(k_bwd_sparse<1, false>);
+  else if (D.block == 64) rows_out ? go(k_bwd_sparse<2, true>) : go(k_bwd_sparse<2, false>);
+  else rows_out ? go(k_bwd_sparse<4, true>) : go(k_bwd_sparse<4, false>);
   timing_end(kKBwdSparse, s);
 }
 
