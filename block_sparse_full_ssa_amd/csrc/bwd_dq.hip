@@ -101,7 +101,32 @@ __global__ void __launch_bounds__(256, 2)
     }
   };
 
+  // bucket mask word and entry base of the wave's queries for each half of a
+  // tile (uniform), one tile ahead
+  uint32_t mw[2] = {0u, 0u}, mwn[2] = {0u, 0u};
+  int mp[2] = {0, 0}, mpn[2] = {0, 0};
+  auto mask_words = [&](int j, uint32_t* m, int* p) {
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      const int kbase = j * kBN + kh * 32;
+      m[kh] = 0u;
+      p[kh] = 0;
+      if (SPARSE && wave_live && kbase <= wave_last_q) {
+        const int64_t w = ((bc * nb + kbase / block) * G + h % G) * (N / 32) + wave_q0 / 32;
+        m[kh] = __builtin_amdgcn_readfirstlane(a.mask[w]);
+        p[kh] = __builtin_amdgcn_readfirstlane(a.wpos[w]);
+      }
+    }
+  };
   auto step = [&](int j, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn) {
+    if constexpr (SPARSE) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        mw[kh] = mwn[kh];
+        mp[kh] = mpn[kh];
+      }
+      if (j + 1 <= j_last) mask_words(j + 1, mwn, mpn);
+    }
     if (j + 1 <= j_last) load_tile(j + 1, Kn, Vn);
     if (wave_live && j * kBN <= wave_last_q) {
 #pragma unroll
@@ -112,10 +137,9 @@ __global__ void __launch_bounds__(256, 2)
         uint4 sd0 = make_uint4(0, 0, 0, 0), sd1 = sd0;
         if constexpr (SPARSE) {
           const int blk = kbase / block;                 // uniform
-          const int64_t w = ((bc * nb + blk) * G + h % G) * (N / 32) + wave_q0 / 32;
-          const uint32_t m = __builtin_amdgcn_readfirstlane(a.mask[w]);
+          const uint32_t m = mw[kh];
           if (m != 0u && ((m >> col) & 1u)) {
-            const int e = a.wpos[w] + __builtin_popcount(m & ((1u << col) - 1u));
+            const int e = mp[kh] + __builtin_popcount(m & ((1u << col) - 1u));
             const uint16_t* src = a.ds_rows + static_cast<int64_t>(e) * block + (kbase - blk * block) + 16 * g;
             sd0 = *reinterpret_cast<const uint4*>(src);
             sd1 = *reinterpret_cast<const uint4*>(src + 8);
@@ -185,6 +209,7 @@ __global__ void __launch_bounds__(256, 2)
     __syncthreads();
   };
 
+  if constexpr (SPARSE) mask_words(0, mwn, mpn);
   load_tile(0, K0, V0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
