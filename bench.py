@@ -47,14 +47,17 @@ def algorithmic_flops_per_launch(d, pf, ps, heads):
     """Algorithmic flops that one launch of each bf16 matrix kernel performs
     (FlashAttention convention: per causal pair 4d forward, 10d backward).
 
+    Training step (both streams):
     fwd_mfma:   both streams' forward, 4d (P_full + P_sparse);
     bwd_mfma:   full stream dK and dV with the S and dP they recompute, 8d P_full;
-    bwd_dq:     full stream dQ, 2d P_full (its own S / dP recompute is extra);
-    bwd_sparse: the sparse stream's whole backward, 10d P_sparse;
+    bwd_dq:     dQ of both streams, 2d (P_full + P_sparse) (the full stream's
+                S / dP recompute is extra; the sparse stream's dS comes in);
+    bwd_sparse: the sparse stream's S, dP, dK and dV, 8d P_sparse;
     sparse_part: the sparse-only forward, 4d P_sparse.
+    The kernels' shares add up to 14 d (P_full + P_sparse).
     """
     return {"fwd_mfma": 4.0 * d * (pf + ps) * heads, "bwd_mfma": 8.0 * d * pf * heads,
-            "bwd_dq": 2.0 * d * pf * heads, "bwd_sparse": 10.0 * d * ps * heads,
+            "bwd_dq": 2.0 * d * (pf + ps) * heads, "bwd_sparse": 8.0 * d * ps * heads,
             "sparse_part": 4.0 * d * ps * heads}
 
 

@@ -1,0 +1,114 @@
+"""Summaries of rocprofv3 runs for the measurement record.
+
+  python -m block_sparse_full_ssa_amd.profile_summary stats DIR OUT.md TITLE
+      kernel table from a `rocprofv3 --kernel-trace --stats --output-format
+      csv` output directory;
+  python -m block_sparse_full_ssa_amd.profile_summary traffic FETCH WRITE \\
+          CAL_FETCH CAL_WRITE OUT.md OUT.json WORKLOAD TOP_K TITLE
+      HBM bytes per launch from one `--pmc FETCH_SIZE` and one `--pmc
+      WRITE_SIZE` pass (KiB per dispatch, averaged over the dispatches of a
+      kernel), each scaled by what the same counter reads for the plain 1 GiB
+      device copy of hbm_calibration.py; the JSON records, per matrix
+      kernel, the bytes and the sha256 of the kernel's source so that a
+      reader can tell when the figures no longer describe the code.
+
+Commands are stated in the written summaries; this module only reads CSVs.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+COPY_BYTES = 1 << 30
+
+# matrix kernels whose traffic the benchmark's roofline reports: name prefix -> (id, source)
+KERNELS = [("k_bwd_mfma", "bwd_mfma", "bwd_mfma.hip"), ("k_fwd_mfma<0>", "fwd_mfma", "fwd_mfma.hip"),
+           ("k_bwd_dq", "bwd_dq", "bwd_dq.hip"), ("k_bwd_sparse", "bwd_sparse", "sparse_bwd.hip")]
+
+
+def short(name: str) -> str:
+    n = name.replace("(anonymous namespace)::", "").split("(")[0]
+    for pre in ("void ", "ssa::"):
+        n = n.replace(pre, "")
+    return n.strip()
+
+
+def counters(d: str):
+    """{kernel: {counter: mean value per dispatch}} over a --pmc output directory."""
+    tot, cnt = defaultdict(lambda: defaultdict(float)), defaultdict(lambda: defaultdict(set))
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter CSV under {d}")
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            k = short(r["Kernel_Name"])
+            tot[k][r["Counter_Name"]] += float(r["Counter_Value"])
+            cnt[k][r["Counter_Name"]].add(r.get("Dispatch_Id") or r.get("Correlation_Id") or len(cnt[k][r["Counter_Name"]]))
+    return {k: {c: v / max(1, len(cnt[k][c])) for c, v in cs.items()} for k, cs in tot.items()}
+
+
+def copy_kib(d: str, counter: str) -> float:
+    vals = [cs[counter] for k, cs in counters(d).items() if counter in cs and "copy" in k.lower()]
+    if not vals:
+        raise SystemExit(f"no copy kernel with {counter} under {d}")
+    return max(vals)
+
+
+def stats(d: str, out: str, title: str) -> None:
+    files = glob.glob(os.path.join(d, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {d}")
+    rows = list(csv.DictReader(open(files[0])))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = [f"| `{short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e6:.3f} | "
+             f"{float(r['MinNs']) / 1e6:.3f} | {float(r['MaxNs']) / 1e6:.3f} | "
+             f"{100 * float(r['TotalDurationNs']) / total:.1f}% |" for r in rows if short(r["Name"]).startswith("k_")]
+    with open(out, "w") as f:
+        f.write(title.rstrip() + "\n\n| kernel | calls | avg ms | min ms | max ms | share |\n|---|---|---|---|---|---|\n")
+        f.write("\n".join(lines) + "\n")
+
+
+def traffic(fd, wd, cfd, cwd, out_md, out_json, workload, top_k, title) -> None:
+    rf, wf = copy_kib(cfd, "FETCH_SIZE") * 1024 / COPY_BYTES, copy_kib(cwd, "WRITE_SIZE") * 1024 / COPY_BYTES
+    fetch, write = counters(fd), counters(wd)
+    names = sorted(set(fetch) | set(write), key=lambda k: -(fetch.get(k, {}).get("FETCH_SIZE", 0)
+                                                           + write.get(k, {}).get("WRITE_SIZE", 0)))
+    lines, table = [], {}
+    for k in names:
+        fk, wk = fetch.get(k, {}).get("FETCH_SIZE", 0.0), write.get(k, {}).get("WRITE_SIZE", 0.0)
+        if not k.startswith("k_"):
+            continue
+        rb, wb = fk * 1024 / rf, wk * 1024 / wf
+        lines.append(f"| `{k}` | {fk:.0f} | {wk:.0f} | {rb / 1e9:.3f} | {wb / 1e9:.3f} |")
+        for pre, kid, src in KERNELS:
+            if k.startswith(pre):
+                sha = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
+                table[f"{kid}/{workload}/top_k={top_k}"] = {
+                    "bytes_per_launch": int(rb + wb), "read_bytes": int(rb), "write_bytes": int(wb),
+                    "source": src, "source_sha256": sha, "from": os.path.relpath(out_md, os.path.dirname(HERE))}
+    with open(out_md, "w") as f:
+        f.write(title.rstrip() + f"\n\nCopy calibration: FETCH_SIZE reads {rf:.3f} KiB per KiB copied, "
+                f"WRITE_SIZE {wf:.3f}; bytes = counter KiB * 1024 / factor.\n\n"
+                "| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | read GB | write GB |\n|---|---|---|---|---|\n")
+        f.write("\n".join(lines) + "\n")
+    with open(out_json, "w") as f:
+        json.dump(table, f, indent=1)
+        f.write("\n")
+
+
+if __name__ == "__main__":
+    a = sys.argv[1:]
+    if a and a[0] == "stats" and len(a) == 4:
+        stats(a[1], a[2], a[3])
+    elif a and a[0] == "traffic" and len(a) == 10:
+        traffic(*a[1:8], int(a[8]), a[9])
+    else:
+        raise SystemExit(__doc__)
