@@ -128,26 +128,22 @@ __device__ __forceinline__ int swz_t(int r, int c) { return c ^ (((r & 7) << 1) 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-__global__ void __launch_bounds__(512, 1)
+__global__ void __launch_bounds__(256, 2)
     k_bwd_mfma(BwdMainArgs a, int Hq, int G, int N, float scale, float scale_log2) {
-  // Eight waves, two per SIMD: waves w and w + 4 own the same 32 keys (kq =
-  // w % 4) and take alternate iterations (par = w / 4), so that one wave's
-  // waits (LDS, the softmax, the barrier) overlap the other's MFMAs.  Their
-  // dK / dV partial sums meet in LDS at the end.
-  // LDS: K and V of the 128 keys (read as MFMA operands, 64 KiB) and two
-  // stages of {Q, G_f tiles of an iteration pair [2][32][128], row values}:
-  // one being read, one being filled by HBM -> LDS copies.  Each stage is its
-  // own object so that the compiler can tell the one being read from the one
-  // being filled.
+  // Two workgroups per CU, so that the two waves on a SIMD belong to
+  // different workgroups and drift apart: one's waits (LDS, the softmax, the
+  // barrier) overlap the other's MFMAs.  A workgroup owns 128 keys (32 per
+  // wave); K of the 128 keys sits in LDS as an MFMA operand, V in registers.
+  // LDS: K (32 KiB) and two sets of {Q, G_f tiles [32][128], row values}.
   constexpr int kT = kBM * kD;                       // one Q / G tile
-  __shared__ __attribute__((aligned(16))) uint16_t Kt[kBN * kD], Vt[kBN * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t Q0[2 * kT], F0[2 * kT], Q1[2 * kT], F1[2 * kT];
-  __shared__ __attribute__((aligned(16))) float R0[4 * kBM], R1[4 * kBM];   // [par][lse2, D][32]
+  __shared__ __attribute__((aligned(16))) uint16_t Kt[kBN * kD];
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[kT], F0[kT], Q1[kT], F1[kT];
+  __shared__ __attribute__((aligned(16))) float R0[2 * kBM], R1[2 * kBM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kq = wave & 3, par = wave >> 2;
+  const int kq = wave;
   const int g = lane >> 5, col = lane & 31;
   const int grp = lane >> 4, li = lane & 15;
   const int gk = grp >> 1, srow = li >> 2, m4 = li & 3;
@@ -165,19 +161,28 @@ __global__ void __launch_bounds__(512, 1)
   const int nqt = N / kBM;
   const int qt0 = k0 / kBM;                         // first query tile that sees these keys
   const int iters = G * (nqt - qt0);                // >= G >= 1
-  const int npairs = (iters + 1) >> 1;
 
-  // HBM -> LDS copies, 1 KiB (4 rows of 256 bytes) per instruction: lane l
-  // fills physical chunk l % 16 of row 4n + l / 16 with the logical chunk
-  // stored there.  K / V: 64 instructions, 8 per wave; keys past N repeat
-  // the last key (their pairs are masked).
+  // K of the 128 keys -> LDS: 32 instructions of 1 KiB (4 rows), 8 per wave;
+  // lane l fills physical chunk l % 16 of row 4n + l / 16 with the logical
+  // chunk stored there; keys past N repeat the last key (their pairs are masked)
 #pragma unroll
   for (int r = 0; r < 8; ++r) {
     const int n = wave * 8 + r;                     // uniform
-    const int row = 4 * (n & 31) + (lane >> 4);
+    const int row = 4 * n + (lane >> 4);
     const int64_t key = min(k0 + row, N - 1);
-    const uint16_t* src = ((n >> 5) ? vg : kg) + key * kD + 8 * swz_t(row, lane & 15);
-    __builtin_amdgcn_global_load_lds((const glb_void*)src, (lds_void*)(((n >> 5) ? Vt : Kt) + (n & 31) * 512), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((const glb_void*)(kg + key * kD + 8 * swz_t(row, lane & 15)),
+                                     (lds_void*)(Kt + n * 512), 16, 0, 0);
+  }
+  // dP B operand [16 d x 32 keys] from registers: key = kw0 + col, d = 16 ds + 8 g + s
+  bf16x8 vb[kD / 16];
+  {
+    const int key = kw0 + col;
+#pragma unroll
+    for (int ds = 0; ds < kD / 16; ++ds) {
+      uint4 w = make_uint4(0, 0, 0, 0);
+      if (key < N) w = *reinterpret_cast<const uint4*>(vg + static_cast<int64_t>(key) * kD + 16 * ds + 8 * g);
+      vb[ds] = __builtin_bit_cast(bf16x8, w);
+    }
   }
 
   // iteration coordinates (query head, first query), advanced incrementally:
@@ -189,38 +194,31 @@ __global__ void __launch_bounds__(512, 1)
       ++hq;
     }
   };
-  // Q / G_f tiles of the iteration pair (it, it + 1): 32 instructions, 4 per
-  // wave; tile t = (parity, Q or G) of n = 4 wave + r is n / 8.  The tile
-  // bases are uniform; the lane offsets are fixed.
+  // Q / G_f tiles of one iteration: 16 instructions, 4 per wave; the tile
+  // bases are uniform, the lane offsets fixed
   uint32_t dmo[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = 4 * ((wave * 4 + r) & 7) + (lane >> 4);
     dmo[r] = row * kD + 8 * swz_t(row, lane & 15);
   }
-  auto load_tiles = [&](int hqA, int qA, int hqB, int qB, bool hasB, uint16_t* Qd, uint16_t* Fd) {
+  auto load_tiles = [&](int hq, int q0, uint16_t* Qd, uint16_t* Fd) {
+    const int64_t tile = ((static_cast<int64_t>(b) * Hq + hq) * N + q0) * kD;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int n = wave * 4 + r;                   // 0..31, uniform
-      const int t = n >> 3, n8 = n & 7;
-      if ((t >> 1) && !hasB) continue;
-      const int hq = (t >> 1) ? hqB : hqA, q0 = (t >> 1) ? qB : qA;
-      const int64_t tile = ((static_cast<int64_t>(b) * Hq + hq) * N + q0) * kD;
-      const uint16_t* src = ((t & 1) ? a.g_full : static_cast<const uint16_t*>(a.q)) + tile;
-      uint16_t* dst = ((t & 1) ? Fd : Qd) + (t >> 1) * kT;
-      __builtin_amdgcn_global_load_lds((const glb_void*)(src + dmo[r]), (lds_void*)(dst + n8 * 512), 16, 0, 0);
+      const int n = wave * 4 + r;                   // 0..15, uniform
+      const uint16_t* src = ((n >> 3) ? a.g_full : static_cast<const uint16_t*>(a.q)) + tile;
+      uint16_t* dst = (n >> 3) ? Fd : Qd;
+      __builtin_amdgcn_global_load_lds((const glb_void*)(src + dmo[r]), (lds_void*)(dst + (n & 7) * 512), 16, 0, 0);
     }
   };
-  // row values (lse2, D) of the pair through registers: thread t < 128 holds
-  // value t % 32 of kind (t / 32) % 2 of parity t / 64
+  // row values (lse2, D) through registers
   float prow = 0.f;
-  auto load_rows = [&](int hqA, int qA, int hqB, int qB, bool hasB) {
-    if (tid < 4 * kBM) {
-      const int pr = tid >> 6, which = (tid >> 5) & 1, r = tid & 31;
-      if (pr == 0 || hasB) {
-        const int64_t rowbase = (static_cast<int64_t>(b) * Hq + (pr ? hqB : hqA)) * N + (pr ? qB : qA);
-        prow = (which == 0 ? a.lse2_full : a.D_full)[rowbase + r];
-      }
+  auto load_rows = [&](int hq, int q0) {
+    const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N + q0;
+    if (tid < 2 * kBM) {
+      const int which = tid >> 5, r = tid & 31;
+      prow = (which == 0 ? a.lse2_full : a.D_full)[rowbase + r];
     }
   };
 
@@ -231,39 +229,35 @@ __global__ void __launch_bounds__(512, 1)
     dk[dt] = f32x16{};
   }
 
-  // One iteration pair on stage (Qs, Fs, Rs) while the next pair streams
-  // into (Qn, Fn, Rn); this wave handles iteration 2p + par with first query q0.
-  auto step = [&](int p, int q0, int hqA1, int qA1, int hqB1, int qB1, const uint16_t* Qs, const uint16_t* Fs,
-                  const float* Rs, uint16_t* Qn, uint16_t* Fn, float* Rn) {
-    const bool more = p + 1 < npairs;
-    const bool hasB1 = 2 * p + 3 < iters;
+  // one iteration on set (Qs, Fs, rv) while the next streams into (Qn, Fn, Rn)
+  auto step = [&](int it, int q0, int hq1, int q01, const uint16_t* Qs, const uint16_t* Fs, const float* rv,
+                  uint16_t* Qn, uint16_t* Fn, float* Rn) {
+    const bool more = it + 1 < iters;
     if (more) {
-      load_rows(hqA1, qA1, hqB1, qB1, hasB1);   // plain loads first: no VMEM load may follow the copies
-      load_tiles(hqA1, qA1, hqB1, qB1, hasB1, Qn, Fn);
+      load_rows(hq1, q01);    // plain loads first: no VMEM load may follow the copies
+      load_tiles(hq1, q01, Qn, Fn);
     }
-    const float* rv = Rs + par * 2 * kBM;
-    const bool wave_has_pairs = 2 * p + par < iters && q0 + kBM - 1 >= kw0 && kw0 < N;   // uniform
-    const bool diag = q0 < kw0 + 31;                                                    // some key > some query
+    const bool wave_has_pairs = q0 + kBM - 1 >= kw0 && kw0 < N;   // uniform
+    const bool diag = q0 < kw0 + 31;                               // some key > some query
 
     if (wave_has_pairs) {
-      // LDS offsets, rebuilt from three lane constants in every iteration
-      // (loop-invariant copies would take 36 registers).  Row reads of d-step
-      // ds: base + 16 (ds ^ (col % 8)); transpose reads of (st, dt): tb +
-      // 2048 st + 32 (dt ^ tx), the second row eight below at tb1 + ...
+      // LDS offsets, rebuilt from lane constants in every iteration.  Row
+      // reads of d-step ds: base + 16 (ds ^ (col % 8)); transpose reads of
+      // (st, dt): tb + 2048 st + 32 (dt ^ tx), the second row eight below at tb1
       int c7 = col & 7, tx = 2 * gk + (srow >> 1);
       asm volatile("" : "+v"(c7), "+v"(tx));
-      const int rowq = par * kT + col * kD + 8 * (g ^ ((col >> 3) & 1));
+      const int rowq = col * kD + 8 * (g ^ ((col >> 3) & 1));
       const int rowk = (32 * kq + col) * kD + 8 * (g ^ ((col >> 3) & 1));
-      const int tb0 = par * kT + (4 * gk + srow) * kD + 8 * ((2 * (grp & 1) + (m4 >> 1)) ^ (2 * (srow & 1))) + 4 * (m4 & 1);
+      const int tb0 = (4 * gk + srow) * kD + 8 * ((2 * (grp & 1) + (m4 >> 1)) ^ (2 * (srow & 1))) + 4 * (m4 & 1);
       const int tb1 = tb0 + 8 * kD + 8 * (1 - 2 * ((m4 >> 1) & 1));
       // ---- S = Q K^T, dP = G_f V^T  [32 q x 32 keys], two independent
-      // accumulation chains interleaved; lane: key col, queries 8(i/4)+4g+(i%4)
+      // accumulation chains interleaved, operands read one step ahead; lane:
+      // key col, queries 8(i/4)+4g+(i%4)
       f32x16 s = f32x16{}, dpf = f32x16{};
-      bf16x8 ok[8], ov[8], oq[8], of[8];
+      bf16x8 ok[8], oq[8], of[8];
       auto rd = [&](int ds) {
         const int cs = 16 * (ds ^ c7);   // the same chunk for query row col and key row 32 kq + col
         ok[ds] = lds_read8(&Kt[rowk + cs]);
-        ov[ds] = lds_read8(&Vt[rowk + cs]);
         oq[ds] = lds_read8(&Qs[rowq + cs]);
         of[ds] = lds_read8(&Fs[rowq + cs]);
       };
@@ -273,7 +267,7 @@ __global__ void __launch_bounds__(512, 1)
         __builtin_amdgcn_sched_barrier(0);
         if (ds + 1 < kD / 16) rd(ds + 1);
         s = mfma32x32x16(oq[ds], ok[ds], s);
-        dpf = mfma32x32x16(of[ds], ov[ds], dpf);
+        dpf = mfma32x32x16(of[ds], vb[ds], dpf);
       }
       __builtin_amdgcn_sched_barrier(0);
       // ---- probabilities and dS, packed to bf16 pairs (register i: query
@@ -303,7 +297,8 @@ __global__ void __launch_bounds__(512, 1)
         dsp[2 * a4] = pack_bf16x2(e[0], e[1]);
         dsp[2 * a4 + 1] = pack_bf16x2(e[2], e[3]);
       }
-      // ---- dV^T += G^T P, dK^T += Q^T dS  (k = queries; 2 steps of 16)
+      // ---- dV^T += G^T P, dK^T += Q^T dS  (k = queries; 2 steps of 16),
+      // transpose reads one step ahead
       bf16x8 bpf[2], bds[2], tg[8], tq[8];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -325,72 +320,28 @@ __global__ void __launch_bounds__(512, 1)
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more && tid < 4 * kBM) Rn[tid] = prow;
+    if (more && tid < 2 * kBM) Rn[tid] = prow;
     __builtin_amdgcn_s_waitcnt(0);     // next tiles landed
     __syncthreads();
   };
 
-  // pair p covers iterations 2p (coordinates A) and 2p + 1 (B)
-  int hqA = c * G, qA = qt0 * kBM;
-  int hqB = hqA, qB = qA;
-  advance(hqB, qB);
-  {
-    load_rows(hqA, qA, hqB, qB, iters > 1);
-    load_tiles(hqA, qA, hqB, qB, iters > 1, Q0, F0);
-    if (tid < 4 * kBM) R0[tid] = prow;
-  }
+  int hq = c * G, q0 = qt0 * kBM;                  // iteration it
+  int hq1 = hq, q01 = q0;                           // iteration it + 1
+  advance(hq1, q01);
+  load_rows(hq, q0);
+  load_tiles(hq, q0, Q0, F0);
+  if (tid < 2 * kBM) R0[tid] = prow;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int p = 0; p < npairs; p += 2) {
-    int q0 = par ? qB : qA;
-    int hqA1 = hqB, qA1 = qB;
-    advance(hqA1, qA1);
-    int hqB1 = hqA1, qB1 = qA1;
-    advance(hqB1, qB1);
-    step(p, q0, hqA1, qA1, hqB1, qB1, Q0, F0, R0, Q1, F1, R1);
-    hqA = hqA1; qA = qA1; hqB = hqB1; qB = qB1;
-    if (p + 1 >= npairs) break;
-    q0 = par ? qB : qA;
-    hqA1 = hqB; qA1 = qB;
-    advance(hqA1, qA1);
-    hqB1 = hqA1; qB1 = qA1;
-    advance(hqB1, qB1);
-    step(p + 1, q0, hqA1, qA1, hqB1, qB1, Q1, F1, R1, Q0, F0, R0);
-    hqA = hqA1; qA = qA1; hqB = hqB1; qB = qB1;
+  for (int it = 0; it < iters; it += 2) {
+    step(it, q0, hq1, q01, Q0, F0, R0, Q1, F1, R1);
+    q0 = q01;
+    advance(hq1, q01);
+    if (it + 1 >= iters) break;
+    step(it + 1, q0, hq1, q01, Q1, F1, R1, Q0, F0, R0);
+    q0 = q01;
+    advance(hq1, q01);
   }
-
-  // ---- the odd-iteration waves hand their partial sums to their partners
-  // through LDS, dV first, then dK: a wave's 64 fp32 values per lane take
-  // 16 KiB laid out [value / 4][lane][4], waves kq = 0, 1 in the K buffer and
-  // kq = 2, 3 in the V buffer (both free once the loop has ended)
-  float* red = reinterpret_cast<float*>((kq >> 1) ? Vt : Kt) + (kq & 1) * 4096;
-  auto hand_over = [&](f32x16* acc) {
-    if (par) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; i += 4)
-          *reinterpret_cast<float4*>(&red[((dt * 16 + i) / 4 * 64 + lane) * 4]) =
-              make_float4(acc[dt][i], acc[dt][i + 1], acc[dt][i + 2], acc[dt][i + 3]);
-    }
-    __syncthreads();
-    if (!par) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int i = 0; i < 16; i += 4) {
-          const float4 x = *reinterpret_cast<const float4*>(&red[((dt * 16 + i) / 4 * 64 + lane) * 4]);
-          acc[dt][i] += x.x;
-          acc[dt][i + 1] += x.y;
-          acc[dt][i + 2] += x.z;
-          acc[dt][i + 3] += x.w;
-        }
-    }
-    __syncthreads();
-  };
-  hand_over(dv);
-  hand_over(dk);
-  if (par) return;
 
   // ---- epilogue: dK = scale * dK^T^T (+ sparse stream), dV (+ sparse stream),
   // in bf16; lane owns key kw0 + col
@@ -436,7 +387,7 @@ void launch_bwd_pre(const Dims& D, const BwdPreArgs& a, float w_sparsity, float 
 void launch_bwd_mfma(const Dims& D, const BwdMainArgs& a, hipStream_t s) {
   dim3 grid(D.B * D.Hkv, (D.N + kBN - 1) / kBN);
   timing_begin(kKBwdMfma, s);
-  hipLaunchKernelGGL(k_bwd_mfma, grid, dim3(512), 0, s, a, D.Hq, D.G, D.N, D.scale, D.scale * kLog2e);
+  hipLaunchKernelGGL(k_bwd_mfma, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.scale, D.scale * kLog2e);
   timing_end(kKBwdMfma, s);
 }
 
