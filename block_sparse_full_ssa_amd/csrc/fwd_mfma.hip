@@ -199,8 +199,8 @@ __global__ void __launch_bounds__(256, 2)
         for (int ds = 0; ds < kD / 16; ++ds)
           s = mfma32x32x16(lds_read8(&Ks[r * kD + 8 * swz_k(r, 2 * ds + g)]), qreg[ds], s);
       }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) s[i] *= scale_log2;
+      // logits stay unscaled: the scale (> 0) goes into the maximum and into
+      // each exponent's fused multiply-add
       if (kbase + 31 > wave_q0) {                  // uniform: the diagonal needs the causal mask
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -209,7 +209,7 @@ __global__ void __launch_bounds__(256, 2)
         }
       }
       float mx = max16(s);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
 
       // ---- new maxima (integers, moved lazily)
       float mfn = mf, alpha = 1.f;
@@ -236,7 +236,7 @@ __global__ void __launch_bounds__(256, 2)
           float p[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            p[e] = sb ? fast_exp2(s[8 * st + e] - msn) : 0.f;
+            p[e] = sb ? fast_exp2(fmaf(s[8 * st + e], scale_log2, -msn)) : 0.f;
             sum_s += p[e];
           }
           ps[st] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
@@ -245,11 +245,11 @@ __global__ void __launch_bounds__(256, 2)
 
       // ---- full stream
       bf16x8 pf[2];
+      float sum = 0.f;
       if (kFull) {
-        float sum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          s[i] = fast_exp2(s[i] - mfn);
+          s[i] = fast_exp2(fmaf(s[i], scale_log2, -mfn));
           sum += s[i];
         }
         lf = lf * alpha + sum;
@@ -265,16 +265,15 @@ __global__ void __launch_bounds__(256, 2)
       }
       if (kSparse && sparse_any) {
         if (rescale) {
-          // exact: the factor is a power of two
+          // exact: the factor is a power of two, so the row sum is the full
+          // stream's sum of this half times it, bit for bit
           const float c = sb ? fast_exp2(mfn - msn) : 0.f;
+          sum_s = sum * c;
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
             float p[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              p[e] = s[8 * st + e] * c;
-              sum_s += p[e];
-            }
+            for (int e = 0; e < 8; ++e) p[e] = s[8 * st + e] * c;
             ps[st] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
           }
         }
