@@ -68,17 +68,30 @@ __device__ __forceinline__ void rank_rows(const float* scores, int32_t* out0, in
       }
     // codes of absent candidates are 0, below every threshold tried (>= 1)
     uint32_t th[RW];
+    bool done[RW];
 #pragma unroll
-    for (int w = 0; w < RW; ++w) th[w] = 0u;
+    for (int w = 0; w < RW; ++w) {
+      th[w] = 0u;
+      done[w] = false;
+    }
+    // Once exactly `keep` candidates are >= the threshold, lower bits can only
+    // raise it within the gap below the keep-th largest code: the set >= th
+    // and hence the result no longer change, so the search stops (uniform:
+    // counts come from ballots).
     for (int bit = 31; bit >= 0; --bit) {
+      bool all = true;
 #pragma unroll
       for (int w = 0; w < RW; ++w) {
+        if (done[w]) continue;
         const uint32_t c = th[w] | (1u << bit);
         int cnt = 0;
 #pragma unroll
         for (int t = 0; t < TM; ++t) cnt += __popcll(__ballot(u[w][t] >= c));
         th[w] = cnt >= keep ? c : th[w];
+        done[w] = cnt == keep;
+        all = all && done[w];
       }
+      if (all) break;
     }
 #pragma unroll
     for (int w = 0; w < RW; ++w) {
