@@ -257,7 +257,7 @@ ssa_status_t ssa_attn_fwd(const ssa_shape_t* shape, int32_t mode, const void* q,
     return launch_status();
   }
   FwdArgs a{q, k, v, sel, h_full, h_sparse, lse_full, lse_sparse, delta, w.row_sq, mode};
-  if (fwd_mfma_supported(D)) launch_fwd_mfma(D, a, s);
+  if (mode != kSparseOnly && fwd_mfma_supported(D)) launch_fwd_mfma(D, a, s);   // dual and full modes
   else launch_fwd_simt(D, a, s);
   if ((st = launch_status()) != SSA_OK) return st;
   if (dual) {

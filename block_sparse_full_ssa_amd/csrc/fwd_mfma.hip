@@ -49,7 +49,7 @@ constexpr float kTau = 8.f;      // lazy-rescale threshold (log2 units)
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-enum { kModeDual = 0, kModeFull = 1, kModeSparse = 2 };
+enum { kModeDual = 0, kModeFull = 1 };   // both streams / the full stream alone
 
 // Physical 16-byte chunk of logical chunk c in row r: K tiles are only read
 // by rows; V tiles by transpose reads.
@@ -72,15 +72,13 @@ __device__ __forceinline__ float max16(const f32x16& v) {
 template <int MODE>
 __global__ void __launch_bounds__(256, 2)
     k_fwd_mfma(FwdArgs a, int Hq, int G, int N, int block, int nb, int K, float scale_log2, int n_qtiles) {
-  constexpr bool kFull = MODE != kModeSparse;
-  constexpr bool kSparse = MODE != kModeFull;
+  constexpr bool kSparse = MODE == kModeDual;
   // K and V tiles [64][128] (swizzled), two of each; separate objects so that
   // the compiler can tell the tile being read from the one being filled
   __shared__ __attribute__((aligned(16))) uint16_t K0[kTile], K1[kTile], V0[kTile], V1[kTile];
-  // dynamic LDS: the selection bits [kBM][W] of the rows and their union [W]
+  // dynamic LDS: the selection bits [kBM][W] of the rows
   extern __shared__ __attribute__((aligned(16))) uint32_t bits[];
   const int W = (nb + 31) >> 5;
-  uint32_t* anybits = bits + kBM * W;
 
   // The wave index and every condition that guards an MFMA are wave-uniform
   // for the compiler: matrix instructions must sit behind scalar branches,
@@ -100,16 +98,13 @@ __global__ void __launch_bounds__(256, 2)
 
   // ---- selection bits of the workgroup's rows
   if (kSparse) {
-    for (int e = tid; e < kBM * W + W; e += 256) bits[e] = 0u;
+    for (int e = tid; e < kBM * W; e += 256) bits[e] = 0u;
     __syncthreads();
     for (int e = tid; e < kBM * K; e += 256) {
       const int r = e / K, t = q0 + r;
       if (t < N) {
         const int blk = a.sel[(static_cast<int64_t>(bh) * N + t) * K + (e - r * K)];
-        if (blk >= 0) {
-          atomicOr(&bits[r * W + (blk >> 5)], 1u << (blk & 31));
-          atomicOr(&anybits[blk >> 5], 1u << (blk & 31));
-        }
+        if (blk >= 0) atomicOr(&bits[r * W + (blk >> 5)], 1u << (blk & 31));
       }
     }
   }
@@ -138,20 +133,6 @@ __global__ void __launch_bounds__(256, 2)
   const int j_last = min(N - 1, q0 + kBM - 1) / kBN;
   if (kSparse) __syncthreads();
 
-  // tile needed by the workgroup? (sparse-only mode skips unselected tiles)
-  auto tile_needed = [&](int j) -> bool {
-    if (MODE != kModeSparse) return true;
-    const int b0 = (j * kBN) / block, b1 = (j * kBN + kBN - 1) / block;
-    for (int bb = b0; bb <= b1 && bb < nb; ++bb)
-      if ((anybits[bb >> 5] >> (bb & 31)) & 1u) return true;
-    return false;
-  };
-  auto next_tile = [&](int j) -> int {
-    for (++j; j <= j_last; ++j)
-      if (tile_needed(j)) return j;
-    return j_last + 1;
-  };
-
   // HBM -> LDS copy of one K/V tile: each wave moves rows 16*wave .. +15, one
   // 1 KiB instruction per 4 rows; lane l fills physical chunk l % 16 of row
   // 4n + l / 16, so it fetches the logical chunk stored there.  Keys past the
@@ -170,11 +151,9 @@ __global__ void __launch_bounds__(256, 2)
     }
   };
 
-  // one tile: compute on (Ks, Vs) while the next needed tile streams into
-  // (Kn, Vn); returns the index of that next tile
-  auto step = [&](int j, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn) -> int {
-    const int jn = MODE == kModeSparse ? next_tile(j) : j + 1;
-    if (jn <= j_last) load_tile(jn, Kn, Vn);
+  // one tile: compute on (Ks, Vs) while the next streams into (Kn, Vn)
+  auto step = [&](int j, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn) {
+    if (j + 1 <= j_last) load_tile(j + 1, Kn, Vn);
   if (wave_live && j * kBN <= wave_last_q) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
@@ -188,7 +167,6 @@ __global__ void __launch_bounds__(256, 2)
         const int blk = kbase / block;
         sb = qrow < N && blk < nb && ((bits[(wave * 32 + col) * W + (blk >> 5)] >> (blk & 31)) & 1u);
         sparse_any = __builtin_amdgcn_readfirstlane(__any(sb) ? 1 : 0) != 0;
-        if (MODE == kModeSparse && !sparse_any) continue;
       }
 
       // ---- S^T = K Q^T for 32 keys, in log2 units
@@ -213,21 +191,18 @@ __global__ void __launch_bounds__(256, 2)
 
       // ---- new maxima (integers, moved lazily)
       float mfn = mf, alpha = 1.f;
-      if (kFull) {
-        if (mx > mf + kTau) mfn = ceilf(mx);
-        alpha = fast_exp2(mf - mfn);               // 1, 0 (first update) or an exact power of two
-      }
+      if (mx > mf + kTau) mfn = ceilf(mx);
+      alpha = fast_exp2(mf - mfn);                 // 1, 0 (first update) or an exact power of two
       float msn = ms, alpha_s = 1.f;
       bool rescale = false;
       if (kSparse && sparse_any) {
         const float mxs = sb ? mx : -INFINITY;
         if (mxs > ms + kTau) msn = ceilf(mxs);
         alpha_s = msn == -INFINITY ? 1.f : fast_exp2(ms - msn);
-        rescale = MODE == kModeDual &&
-                  __builtin_amdgcn_readfirstlane(__any(sb && mfn - msn > 64.f) ? 1 : 0) == 0;
+        rescale = __builtin_amdgcn_readfirstlane(__any(sb && mfn - msn > 64.f) ? 1 : 0) == 0;
       }
 
-      // ---- sparse probabilities evaluated directly (sparse-only, or factor too large)
+      // ---- sparse probabilities evaluated directly (factor too large)
       bf16x8 ps[2];
       float sum_s = 0.f;
       if (kSparse && sparse_any && !rescale) {
@@ -246,23 +221,21 @@ __global__ void __launch_bounds__(256, 2)
       // ---- full stream
       bf16x8 pf[2];
       float sum = 0.f;
-      if (kFull) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          s[i] = fast_exp2(fmaf(s[i], scale_log2, -mfn));
-          sum += s[i];
-        }
-        lf = lf * alpha + sum;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) of[dt] *= alpha;
-        }
-        mf = mfn;
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-          pf[st] = to_bf16x8(s[8 * st], s[8 * st + 1], s[8 * st + 2], s[8 * st + 3], s[8 * st + 4],
-                             s[8 * st + 5], s[8 * st + 6], s[8 * st + 7]);
+      for (int i = 0; i < 16; ++i) {
+        s[i] = fast_exp2(fmaf(s[i], scale_log2, -mfn));
+        sum += s[i];
       }
+      lf = lf * alpha + sum;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) of[dt] *= alpha;
+      }
+      mf = mfn;
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+        pf[st] = to_bf16x8(s[8 * st], s[8 * st + 1], s[8 * st + 2], s[8 * st + 3], s[8 * st + 4],
+                           s[8 * st + 5], s[8 * st + 6], s[8 * st + 7]);
       if (kSparse && sparse_any) {
         if (rescale) {
           // exact: the factor is a power of two, so the row sum is the full
@@ -295,7 +268,7 @@ __global__ void __launch_bounds__(256, 2)
           const int c = 4 * dt + 2 * (grp & 1) + (m4 >> 1);   // logical 16-byte chunk
           const int e = 4 * (m4 & 1);
           const bf16x8 va = lds_tr_pair(&Vs[r0 * kD + 8 * swz_v(r0, c) + e], &Vs[r1 * kD + 8 * swz_v(r1, c) + e]);
-          if (kFull) of[dt] = mfma32x32x16(va, pf[st2], of[dt]);
+          of[dt] = mfma32x32x16(va, pf[st2], of[dt]);
           if (kSparse && sparse_any) os[dt] = mfma32x32x16(va, ps[st2], os[dt]);
         }
       }
@@ -303,17 +276,15 @@ __global__ void __launch_bounds__(256, 2)
   }
     __builtin_amdgcn_s_waitcnt(0);     // the next tile has landed in LDS
     __syncthreads();
-    return jn;
   };
 
-  int j = MODE == kModeSparse ? next_tile(-1) : 0;
-  if (j <= j_last) load_tile(j, K0, V0);
+  load_tile(0, K0, V0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  while (j <= j_last) {
-    j = step(j, K0, V0, K1, V1);
-    if (j > j_last) break;
-    j = step(j, K1, V1, K0, V0);
+  for (int j = 0; j <= j_last; j += 2) {
+    step(j, K0, V0, K1, V1);
+    if (j + 1 > j_last) break;
+    step(j + 1, K1, V1, K0, V0);
   }
 
   // ---- epilogue
@@ -337,7 +308,7 @@ __global__ void __launch_bounds__(256, 2)
         if (MODE == kModeDual) sq += (hf[e] - hs[e]) * (hf[e] - hs[e]);
       }
       if (row_ok) {
-        if (kFull) {
+        {
           uint2 u = make_uint2(pack_bf16x2(hf[0], hf[1]), pack_bf16x2(hf[2], hf[3]));
           *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h_full) + row * kD + dcol) = u;
         }
@@ -352,7 +323,7 @@ __global__ void __launch_bounds__(256, 2)
   if (row_ok && g == 0) {
     const float lse_f = (mf + fast_log2(lf)) * kLn2;
     const float lse_s = (ms + fast_log2(ls)) * kLn2;
-    if (kFull && a.lse_full) a.lse_full[row] = lse_f;
+    if (a.lse_full) a.lse_full[row] = lse_f;
     if (kSparse && a.lse_sparse) a.lse_sparse[row] = lse_s;
     if (MODE == kModeDual) {
       a.delta[row] = -expm1f(lse_s - lse_f);
@@ -378,7 +349,7 @@ constexpr size_t kStaticLds = 4 * kTile * sizeof(uint16_t);
 
 size_t lds_bytes(const Dims& D) {   // dynamic part: selection bits
   const int W = (D.nb + 31) / 32;
-  return static_cast<size_t>(kBM * W + W) * sizeof(uint32_t);
+  return static_cast<size_t>(kBM * W) * sizeof(uint32_t);
 }
 
 }  // namespace
@@ -394,7 +365,6 @@ void launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s) {
   const float scale_log2 = D.scale * 1.4426950408889634f;
   timing_begin(kKFwdMfma, s);
   if (a.mode == kFullOnly) launch_mode<kModeFull>(D, a, lds, n_qtiles, scale_log2, s);
-  else if (a.mode == kSparseOnly) launch_mode<kModeSparse>(D, a, lds, n_qtiles, scale_log2, s);
   else launch_mode<kModeDual>(D, a, lds, n_qtiles, scale_log2, s);
   timing_end(kKFwdMfma, s);
 }

@@ -74,7 +74,7 @@ void launch_bwd_simt(const Dims& D, const BwdArgs& a, hipStream_t s);
 
 // --- bf16 MFMA kernels ---
 bool fwd_mfma_supported(const Dims& D);
-void launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s);
+void launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s);   // dual and FULL_ONLY modes
 
 struct BwdPreArgs {
   const void* dout;                 // may be null: zero upstream gradient
