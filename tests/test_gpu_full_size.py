@@ -162,6 +162,32 @@ def test_train_layer_16k_full_size():
     assert np.all(np.abs(sum_dk) <= 2 ** -7 * abs_dk + 1e-6), np.abs(sum_dk).max()
 
 
+# ------------------------------------------------ selection beyond 1024 blocks --
+
+@pytest.mark.parametrize("block, nb, top_k, d", [(32, 1100, 8, 64), (64, 4096, 16, 128)])
+def test_select_many_blocks(block, nb, top_k, d):
+    """More than 1024 key blocks (up to the supported 4096) take the
+    FMA-scored selection kernel instead of the matrix-scored one: sampled rows
+    against the oracle, margin-aware as above."""
+    wl = si.scaled_down(si.WORKLOADS["gqa_n4k_fwd"], seqlen=block * nb, hq=1, hkv=1, block=block,
+                        top_k=top_k, head_dim=d)
+    _say(f"select nb {nb} block {block} d {d}: draw")
+    q, k, _, _ = si.draw_qkv(wl, 0)
+    sel = ssa().ssa_select_blocks(q.to("cuda:0"), k.to("cuda:0"), block, top_k).cpu().numpy()
+    torch.cuda.synchronize()
+    qf, kf = si.to_f64(q), si.to_f64(k)
+    mu = oracle.block_means(kf, block)
+    t_idx = _sample_rows(np.random.default_rng(2), wl.seqlen, block, top_k, 64)
+    exempt = _check_selection(f"nb {nb}", qf[0, 0, t_idx], t_idx, mu[0, 0], block, top_k, sel[0, 0, t_idx])
+    _say(f"  rows {t_idx.size}, exempt by margin: {exempt}")
+    # every row: ascending, own block last among the kept, padded with -1
+    i = np.arange(wl.seqlen) // block
+    kept = (sel[0, 0] >= 0).sum(axis=1)
+    assert np.all(kept == np.minimum(top_k, i + 1))
+    last = sel[0, 0][np.arange(wl.seqlen), kept - 1]
+    assert np.all(last == i)
+
+
 # ----------------------------------------------------------- 64K with sinks --
 
 def test_long_layer_64k_sinks_full_size():
