@@ -188,6 +188,31 @@ def test_select_many_blocks(block, nb, top_k, d):
     assert np.all(last == i)
 
 
+# ---------------------------------------- sparse-only forward, > 64 blocks kept --
+
+def test_sparse_only_fwd_many_blocks_kept():
+    """top_k 128 of 128 blocks (top_k above 64 is accepted only when it keeps
+    every block): more than 64 partials per row take the merge's serial path;
+    sampled rows against the oracle for the GPU's selection."""
+    wl = si.scaled_down(si.WORKLOADS["gqa_n4k_fwd"], seqlen=8192, hq=2, hkv=1, top_k=128)
+    K = wl.top_k
+    _say("sparse-only forward, top_k 128 of 128 blocks: draw")
+    q, k, v, _ = si.draw_qkv(wl, 0)
+    qd, kd, vd = (x.to("cuda:0") for x in (q, k, v))
+    sel = ssa().ssa_select_blocks(qd, kd, wl.block, K)
+    fwd = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, K, oracle.SPARSE_ONLY)
+    torch.cuda.synchronize()
+    out = {key: val.cpu() for key, val in fwd.items() if not key.startswith("_")}
+    sel_np = sel.cpu().numpy()
+    qf, kf, vf = (si.to_f64(x) for x in (q, k, v))
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    for h in range(wl.hq):
+        t_idx = _sample_rows(np.random.default_rng(3 + h), wl.seqlen, wl.block, K, 48)
+        ref = oracle.attend_rows(qf[0, h, t_idx], t_idx, kf[0, 0], vf[0, 0], sel_np[0, h, t_idx], wl.block, scale)
+        for key in ("h_sparse", "lse_sparse"):
+            assert_close(f"top_k 128 {key} h{h}", out[key][0, h, torch.from_numpy(t_idx)], ref[key], wl.dtype)
+
+
 # ----------------------------------------------------------- 64K with sinks --
 
 def test_long_layer_64k_sinks_full_size():
