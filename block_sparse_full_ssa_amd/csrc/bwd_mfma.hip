@@ -15,15 +15,17 @@
 //
 // Kernels:
 //   bwd_pre:  per row, G_f / G_s in bf16, D_f / D_s from the rounded G, the
-//             lse values in log2 units, and a zeroed fp32 dQ accumulator row
-//             for the sparse stream;
+//             lse values in log2 units, and (sparse stream alone) a zeroed
+//             fp32 dQ accumulator row;
 //   bwd_mfma: dK / dV, key-stationary.  A workgroup owns 128 keys of one KV
-//             head (32 per wave, kept in registers as K and V operands) and
-//             walks the G query heads of the group and every 32-query tile
-//             at or after its keys.  dK and dV accumulate in registers over
-//             all of them (no atomics) and leave with the sparse stream's
-//             fp32 dK / dV added;
-//   bwd_dq:   dQ, query-stationary (bwd_dq.hip).
+//             head (32 per wave; K in LDS, V in registers as MFMA operands)
+//             and walks the G query heads of the group and every 32-query
+//             tile at or after its keys.  Two workgroups share a CU, so the
+//             two waves on a SIMD come from different workgroups and overlap
+//             each other's waits.  dK and dV accumulate in registers over
+//             all tiles (no atomics) and leave with the sparse stream's fp32
+//             dK / dV added;
+//   bwd_dq:   dQ of both streams, query-stationary (bwd_dq.hip).
 //
 // Layout: the logits are kept as S = Q K^T (lane l owns key l % 32 and 16
 // queries), which is the B-operand layout of dV^T = G^T P and dK^T = Q^T dS;

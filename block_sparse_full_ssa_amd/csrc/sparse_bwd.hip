@@ -9,16 +9,22 @@
 //   P  = 2^(S c - lse_s)  on the block's keys (own block: keys <= t),
 //   dS = P (G_s V^T - D_s),
 //   dV_j = sum over the bucket of P^T G_s,   dK_j = scale sum of dS^T Q,
-//   dQ_r += scale dS K_j                      (fp32 atomics, one per (row, block)),
 // over the gathered rows in batches of 32.  dK and dV of the block stay in
 // registers over the whole bucket and are written once: as fp32 partials
 // that the full-stream kernel adds (training modes), or as the bf16 result
-// (sparse-only).  Keys of a block that no row selected get zero.
+// (sparse-only).  Keys of a block that no row selected get zero.  The
+// stream's dQ = scale dS K leaves in one of two ways:
+//   training modes: each entry's row of dS over the block's keys (bf16, in
+//     the dQ kernel's lane order), which the query-stationary dQ kernel adds
+//     to the full stream's dS, so that no atomics are needed;
+//   sparse-only: dQ_r += scale dS K_j with one fp32 atomic per (row, block,
+//     column) into an accumulator.
 //
 // Waves: wave w owns key half kh = w % KH (32 keys, B operands in registers)
 // of query stream qs = w / KH; the 4 / KH streams take consecutive batches.
 // Each stream's gathered Q and G_s rows move HBM -> LDS (one row per 16
-// lanes, double-buffered); dS^T of the block passes through LDS so that each
+// lanes, double-buffered); dS^T of the block passes through LDS, where each
+// wave reads back its own keys' rows for the dS rows, or, sparse-only, each
 // wave of a stream reduces dQ over all the block's keys for its slice of d.
 // The layout of every product is the full-stream kernel's (S = Q K^T, lane l
 // owns key l % 32).
