@@ -167,21 +167,23 @@ __global__ void __launch_bounds__(256, 2)
         }
         // ---- dS^T = P^T (dP^T - D); key of register i: kbase + 8(i/4) + 4g + i%4
         const bool diag = kbase + 31 > wave_q0;      // uniform
+        // (training modes: plus the sparse stream's dS, element i of its row
+        // being the key of register i; it is zero wherever the mask is)
         float dsv[16];
+        {
+          const uint32_t sw[8] = {sd0.x, sd0.y, sd0.z, sd0.w, sd1.x, sd1.y, sd1.z, sd1.w};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dsv[i] = fast_exp2(s[i] * scale_log2 - lse2) * (dp[i] - Dq);
+          for (int i = 0; i < 16; ++i) {
+            const float sp = SPARSE ? __uint_as_float((i & 1) ? (sw[i >> 1] & 0xffff0000u) : (sw[i >> 1] << 16)) : 0.f;
+            dsv[i] = fmaf(fast_exp2(s[i] * scale_log2 - lse2), dp[i] - Dq, sp);
+          }
+        }
         if (diag) {                  // uniform: only the diagonal tiles need the causal mask
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int key = kbase + 8 * (i >> 2) + 4 * g + (i & 3);
             dsv[i] = key <= qrow ? dsv[i] : 0.f;
           }
-        }
-        if constexpr (SPARSE) {                      // element i of the row: the key of register i
-          const uint32_t sw[8] = {sd0.x, sd0.y, sd0.z, sd0.w, sd1.x, sd1.y, sd1.z, sd1.w};
-#pragma unroll
-          for (int i = 0; i < 16; ++i)
-            dsv[i] += __uint_as_float((i & 1) ? (sw[i >> 1] & 0xffff0000u) : (sw[i >> 1] << 16));
         }
         // ---- dQ^T += K^T dS^T over the 32 keys (two k-steps of 16)
         bf16x8 bds[2], ka[8];
