@@ -105,6 +105,8 @@ __global__ void __launch_bounds__(256, 2)
   // tile (uniform), one tile ahead
   uint32_t mw[2] = {0u, 0u}, mwn[2] = {0u, 0u};
   int mp[2] = {0, 0}, mpn[2] = {0, 0};
+  // (vector loads on purpose: a scalar load in flight would turn every wait
+  // for an LDS operand into a wait for all of them)
   auto mask_words = [&](int j, uint32_t* m, int* p) {
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
@@ -112,9 +114,11 @@ __global__ void __launch_bounds__(256, 2)
       m[kh] = 0u;
       p[kh] = 0;
       if (SPARSE && wave_live && kbase <= wave_last_q) {
-        const int64_t w = ((bc * nb + kbase / block) * G + h % G) * (N / 32) + wave_q0 / 32;
-        m[kh] = __builtin_amdgcn_readfirstlane(a.mask[w]);
-        p[kh] = __builtin_amdgcn_readfirstlane(a.wpos[w]);
+        int z = 0;
+        asm volatile("" : "+v"(z));
+        const int64_t w = ((bc * nb + kbase / block) * G + h % G) * (N / 32) + wave_q0 / 32 + z;
+        m[kh] = a.mask[w];
+        p[kh] = a.wpos[w];
       }
     }
   };
@@ -137,9 +141,9 @@ __global__ void __launch_bounds__(256, 2)
         uint4 sd0 = make_uint4(0, 0, 0, 0), sd1 = sd0;
         if constexpr (SPARSE) {
           const int blk = kbase / block;                 // uniform
-          const uint32_t m = mw[kh];
+          const uint32_t m = __builtin_amdgcn_readfirstlane(mw[kh]);
           if (m != 0u && ((m >> col) & 1u)) {
-            const int e = mp[kh] + __builtin_popcount(m & ((1u << col) - 1u));
+            const int e = __builtin_amdgcn_readfirstlane(mp[kh]) + __builtin_popcount(m & ((1u << col) - 1u));
             const uint16_t* src = a.ds_rows + static_cast<int64_t>(e) * block + (kbase - blk * block) + 16 * g;
             sd0 = *reinterpret_cast<const uint4*>(src);
             sd1 = *reinterpret_cast<const uint4*>(src + 8);
