@@ -152,7 +152,9 @@ __global__ void __launch_bounds__(256, 2)
 
   const int bc = blockIdx.x;                        // batch * Hkv + kv head
   const int Hkv = Hq / G;
-  const int b = bc / Hkv, c = bc % Hkv;
+  // the division runs on the vector unit: bring the results back to scalars
+  const int b = __builtin_amdgcn_readfirstlane(bc / Hkv);
+  const int c = bc - b * Hkv;
   const int k0 = blockIdx.y * kBN;
   const int kw0 = k0 + 32 * kq;                     // this wave's first key
   const int64_t kvbase = static_cast<int64_t>(bc) * N * kD;
@@ -198,18 +200,19 @@ __global__ void __launch_bounds__(256, 2)
   };
   // Q / G_f tiles of one iteration: 16 instructions, 4 per wave; the tile
   // bases are uniform, the lane offsets fixed
+  // (byte offsets, so that each load is a scalar base plus a 32-bit lane offset)
   uint32_t dmo[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int row = 4 * ((wave * 4 + r) & 7) + (lane >> 4);
-    dmo[r] = row * kD + 8 * swz_t(row, lane & 15);
+    dmo[r] = 2 * (row * kD + 8 * swz_t(row, lane & 15));
   }
   auto load_tiles = [&](int hq, int q0, uint16_t* Qd, uint16_t* Fd) {
-    const int64_t tile = ((static_cast<int64_t>(b) * Hq + hq) * N + q0) * kD;
+    const int64_t tile = ((static_cast<int64_t>(b) * Hq + hq) * N + q0) * (kD * 2);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int n = wave * 4 + r;                   // 0..15, uniform
-      const uint16_t* src = ((n >> 3) ? a.g_full : static_cast<const uint16_t*>(a.q)) + tile;
+      const char* src = static_cast<const char*>((n >> 3) ? a.g_full : a.q) + tile;
       uint16_t* dst = (n >> 3) ? Fd : Qd;
       __builtin_amdgcn_global_load_lds((const glb_void*)(src + dmo[r]), (lds_void*)(dst + (n & 7) * 512), 16, 0, 0);
     }
@@ -218,9 +221,9 @@ __global__ void __launch_bounds__(256, 2)
   float prow = 0.f;
   auto load_rows = [&](int hq, int q0) {
     const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N + q0;
-    if (tid < 2 * kBM) {
-      const int which = tid >> 5, r = tid & 31;
-      prow = (which == 0 ? a.lse2_full : a.D_full)[rowbase + r];
+    if (wave == 0) {                      // lanes 0-31: lse2 of the 32 rows, 32-63: D
+      if (lane < kBM) prow = a.lse2_full[rowbase + lane];
+      else prow = a.D_full[rowbase + lane - kBM];
     }
   };
 
@@ -273,29 +276,34 @@ __global__ void __launch_bounds__(256, 2)
       }
       __builtin_amdgcn_sched_barrier(0);
       // ---- probabilities and dS, packed to bf16 pairs (register i: query
-      // 8(i/4) + 4g + i%4, visible iff 8(i/4) + i%4 >= t on diagonal tiles)
-      const int t = kw0 + col - q0 - 4 * g;
+      // 8(i/4) + 4g + i%4, visible iff 8(i/4) + i%4 >= t on diagonal tiles;
+      // dS of a masked pair is zero because its P is)
+      float p[16];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const float4 lf = *reinterpret_cast<const float4*>(&rv[8 * a4 + 4 * g]);
+        const float lfa[4] = {lf.x, lf.y, lf.z, lf.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) p[4 * a4 + k] = fast_exp2(s[4 * a4 + k] * scale_log2 - lfa[k]);
+      }
+      if (diag) {
+        // uniform, and taken on one tile per wave and head, so a real branch
+        // (the empty asm keeps the compiler from turning it into selects)
+        asm volatile("");
+        const int t = kw0 + col - q0 - 4 * g;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) p[i] = 8 * (i / 4) + i % 4 >= t ? p[i] : 0.f;
+      }
       uint32_t pfp[8], dsp[8];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
-        const int qb = 8 * a4 + 4 * g;
-        const float4 lf = *reinterpret_cast<const float4*>(&rv[qb]);
-        const float4 df = *reinterpret_cast<const float4*>(&rv[kBM + qb]);
-        const float lfa[4] = {lf.x, lf.y, lf.z, lf.w};
+        const float4 df = *reinterpret_cast<const float4*>(&rv[kBM + 8 * a4 + 4 * g]);
         const float dfa[4] = {df.x, df.y, df.z, df.w};
-        float p[4], e[4];
+        float e[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int i = 4 * a4 + k;
-          p[k] = fast_exp2(s[i] * scale_log2 - lfa[k]);
-          e[k] = p[k] * (dpf[i] - dfa[k]);
-          if (diag) {             // uniform: only tiles that straddle the diagonal need the causal mask
-            p[k] = 8 * a4 + k >= t ? p[k] : 0.f;
-            e[k] = 8 * a4 + k >= t ? e[k] : 0.f;
-          }
-        }
-        pfp[2 * a4] = pack_bf16x2(p[0], p[1]);
-        pfp[2 * a4 + 1] = pack_bf16x2(p[2], p[3]);
+        for (int k = 0; k < 4; ++k) e[k] = p[4 * a4 + k] * (dpf[4 * a4 + k] - dfa[k]);
+        pfp[2 * a4] = pack_bf16x2(p[4 * a4], p[4 * a4 + 1]);
+        pfp[2 * a4 + 1] = pack_bf16x2(p[4 * a4 + 2], p[4 * a4 + 3]);
         dsp[2 * a4] = pack_bf16x2(e[0], e[1]);
         dsp[2 * a4 + 1] = pack_bf16x2(e[2], e[3]);
       }
