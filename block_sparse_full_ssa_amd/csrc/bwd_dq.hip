@@ -51,8 +51,9 @@ __global__ void __launch_bounds__(256, 2)
   const int g = lane >> 5, col = lane & 31;
   const int grp = lane >> 4, li = lane & 15;
   const int gk = grp >> 1, srow = li >> 2, m4 = li & 3;
-  const int bh = blockIdx.x;
-  const int q0 = (n_qtiles - 1 - static_cast<int>(blockIdx.y)) * kBM;   // longest tiles first
+  const QTileItem item = qtile_item(blockIdx.x, static_cast<int>(gridDim.x) / (n_qtiles * G), G, n_qtiles);
+  const int bh = item.bh;
+  const int q0 = (n_qtiles - 1 - item.rank) * kBM;   // longest tiles first
   const int b = bh / Hq, h = bh % Hq;
   const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
   const uint16_t* kg = static_cast<const uint16_t*>(a.k) + bc * N * kD;
@@ -243,7 +244,7 @@ __global__ void __launch_bounds__(256, 2)
 
 void launch_bwd_dq(const Dims& D, const BwdDqArgs& a, hipStream_t s) {
   const int n_qtiles = (D.N + kBM - 1) / kBM;
-  dim3 grid(D.B * D.Hq, n_qtiles);
+  dim3 grid(D.B * D.Hq * n_qtiles);   // work items from qtile_item
   timing_begin(kKBwdDq, s);
   if (a.ds_rows)
     hipLaunchKernelGGL(k_bwd_dq<true>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.block, D.scale,

@@ -190,12 +190,15 @@ __global__ void __launch_bounds__(256, 2)
   }
 
   // iteration coordinates (query head, first query), advanced incrementally:
-  // query tiles inner, the group's heads outer
+  // the group's heads inner, query tiles from the last one down to the first
+  // that sees these keys.  The workgroups of a KV head that start together
+  // then read the same Q / G_f tile at about the same time, so one L2 fill
+  // serves them all (ascending tiles put them 4 tiles apart, and heads outer
+  // lets them drift onto different heads).
   auto advance = [&](int& hq, int& q0) {
-    q0 += kBM;
-    if (q0 >= N) {
-      q0 = qt0 * kBM;
-      ++hq;
+    if (++hq == (c + 1) * G) {
+      hq = c * G;
+      q0 -= kBM;
     }
   };
   // Q / G_f tiles of one iteration: 16 instructions, 4 per wave; the tile
@@ -335,7 +338,7 @@ __global__ void __launch_bounds__(256, 2)
     __syncthreads();
   };
 
-  int hq = c * G, q0 = qt0 * kBM;                  // iteration it
+  int hq = c * G, q0 = N - kBM;                    // iteration it
   int hq1 = hq, q01 = q0;                           // iteration it + 1
   advance(hq1, q01);
   load_rows(hq, q0);

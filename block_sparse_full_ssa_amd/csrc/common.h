@@ -77,4 +77,36 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
   return x;
 }
 
+// Work item of a query-stationary grid (one workgroup per query head and
+// query tile), from the linear workgroup index L.  Workgroups are dispatched
+// round-robin over the eight XCDs (L % 8), each with its own L2.  Where the KV
+// heads divide evenly over the XCDs, or the XCDs over the KV heads, all G
+// query heads of a KV head run on the same XCD(s), so the K/V tiles they all
+// stream fill one L2 instead of up to G of them.  Query tiles go out longest
+// first: rank 0 is the last tile.  Results are uniform (scalar registers).
+struct QTileItem {
+  int bh;      // batch * Hq + query head
+  int rank;    // query tile n_qtiles - 1 - rank
+};
+__device__ __forceinline__ QTileItem qtile_item(int L, int nkv, int G, int nqt) {
+  constexpr int X = 8;
+  int bh, rank;
+  if (nkv % X == 0) {
+    const int per = (nkv / X) * G;              // items of one tile rank on an XCD
+    const int x = L % X, s = L / X, rem = s % per;
+    bh = (x + X * (rem / G)) * G + rem % G;
+    rank = s / per;
+  } else if (X % nkv == 0 && (G * nqt) % (X / nkv) == 0) {
+    const int r = X / nkv;                      // XCDs per KV head
+    const int x = L % X;
+    const int idx = (L / X) * r + x / nkv;      // item of KV head x % nkv
+    bh = (x % nkv) * G + idx % G;
+    rank = idx / G;
+  } else {
+    bh = L % (nkv * G);
+    rank = L / (nkv * G);
+  }
+  return {__builtin_amdgcn_readfirstlane(bh), __builtin_amdgcn_readfirstlane(rank)};
+}
+
 }  // namespace ssa

@@ -88,8 +88,9 @@ __global__ void __launch_bounds__(256, 2)
   const int g = lane >> 5, col = lane & 31;
   const int grp = lane >> 4, li = lane & 15;
   const int gk = grp >> 1, srow = li >> 2, m4 = li & 3;
-  const int bh = blockIdx.x;
-  const int q0 = (n_qtiles - 1 - static_cast<int>(blockIdx.y)) * kBM;   // longest tiles first
+  const QTileItem item = qtile_item(blockIdx.x, static_cast<int>(gridDim.x) / (n_qtiles * G), G, n_qtiles);
+  const int bh = item.bh;
+  const int q0 = (n_qtiles - 1 - item.rank) * kBM;   // longest tiles first
   const int b = bh / Hq, h = bh % Hq;
   const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
   const uint16_t* qg = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(bh) * N * kD;
@@ -340,7 +341,7 @@ void launch_mode(const Dims& D, const FwdArgs& a, size_t lds, int n_qtiles, floa
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     granted = lds;
   }
-  dim3 grid(D.B * D.Hq, n_qtiles);
+  dim3 grid(D.B * D.Hq * n_qtiles);   // work items from qtile_item
   hipLaunchKernelGGL(k_fwd_mfma<MODE>, grid, dim3(256), lds, s, a, D.Hq, D.G, D.N, D.block, D.nb, D.K,
                      scale_log2, n_qtiles);
 }
