@@ -177,6 +177,33 @@ def single_stream(ssa, q, k, v, dout, wl, ks, reps):
     return out
 
 
+def measured_ceilings(ssa, dev):
+    """The two machine probes of libssa, timed by its own event hooks: the bf16
+    matrix rate the chip sustains with every SIMD busy (two waves per SIMD,
+    independent chains), and the bandwidth of a plain 1 GiB device copy
+    (read + written bytes / time)."""
+    import torch
+
+    blocks, iters = 2048, 4000                   # 2 workgroups of 4 waves per CU, ~6 ms
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    ssa.ssa_probe_mfma(sink, blocks, 100)
+    ssa.ssa_probe_copy(src, dst)
+    torch.cuda.synchronize()
+    ssa.timing_enable(True)
+    for _ in range(3):
+        ssa.ssa_probe_mfma(sink, blocks, iters)
+        ssa.ssa_probe_copy(src, dst)
+    mfma_ms, n1 = ssa.timing_query("probe_mfma")
+    copy_ms, n2 = ssa.timing_query("probe_copy")
+    ssa.timing_enable(False)
+    nbytes = src.numel() * 4
+    return {"mfma_bf16_tflops": round(blocks * 16 * iters * 32768 / (mfma_ms / n1 / 1e3) / 1e12, 1),
+            "copy_gbs": round(2 * nbytes / (copy_ms / n2 / 1e3) / 1e9, 1),
+            "note": "dense 32x32x16 bf16 matrix loop on every SIMD; 1 GiB device copy (read + write)"}
+
+
 def cpu_baseline(wl, K, seed, rows):
     """The fp64 oracle on the host: select + forward + backward of the last
     ``rows`` query rows of batch 0 / query head 0 (each with all its causal
@@ -279,6 +306,10 @@ def main():
         ks = list(wl.top_k_sweep) if (args.sweep and wl.top_k_sweep) else [K]
         single = single_stream(ssa, q, k, v, dout, wl, ks, max(3, args.steps // 2))
 
+    ceilings = measured_ceilings(ssa, dev)
+    if roofline is not None:
+        roofline["frac_of_measured_peak"] = round(roofline["achieved"] / ceilings["mfma_bf16_tflops"], 4)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, K, args.seed, min(args.cpu_rows, N))
@@ -305,6 +336,8 @@ def main():
         "kernels_ms_avg": {n: round(kk["avg_ms"], 4) for n, kk in kernels.items()},
         "roofline": roofline,
         "kernel_frac_of_bf16_peak": kernel_frac,
+        "measured_ceilings": ceilings,
+        "frac_of_measured_mfma": round(tflops / ceilings["mfma_bf16_tflops"], 4),
         "cpu_baseline": cpu,
     }
     if single:

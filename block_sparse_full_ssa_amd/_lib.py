@@ -33,7 +33,7 @@ OP_BWD = 2
 EXPORTED = (
     "ssa_workspace_size", "ssa_select_blocks", "ssa_attn_fwd", "ssa_attn_bwd",
     "ssa_status_string", "ssa_last_error", "ssa_timing_enable", "ssa_timing_query",
-    "ssa_kernel_count", "ssa_kernel_name",
+    "ssa_kernel_count", "ssa_kernel_name", "ssa_probe_mfma", "ssa_probe_copy",
 )
 
 
@@ -94,6 +94,10 @@ def lib() -> ctypes.CDLL:
     L.ssa_kernel_count.restype = i32
     L.ssa_kernel_name.argtypes = [i32]
     L.ssa_kernel_name.restype = ctypes.c_char_p
+    L.ssa_probe_mfma.argtypes = [vp, i32, i32, vp]
+    L.ssa_probe_mfma.restype = i32
+    L.ssa_probe_copy.argtypes = [vp, vp, sz, vp]
+    L.ssa_probe_copy.restype = i32
     _lib = L
     return L
 

@@ -33,7 +33,7 @@ static std::vector<TimingRec> g_recs;
 static const char* kKernelNames[kKernelCount] = {
     "block_mean", "select", "fwd_simt", "fwd_mfma", "loss_reduce",
     "bwd_pre",    "bwd_simt", "bwd_mfma", "convert", "zero", "bucket", "sparse_part", "sparse_merge",
-    "bwd_sparse", "bwd_dq"};
+    "bwd_sparse", "bwd_dq", "probe_mfma", "probe_copy"};
 
 void timing_begin(int kernel, hipStream_t s) {
   if (!g_timing) return;
@@ -366,6 +366,23 @@ ssa_status_t ssa_timing_query(const char* kernel, double* total_ms, int64_t* lau
   *total_ms = tot;
   *launches = n;
   return SSA_OK;
+}
+
+ssa_status_t ssa_probe_mfma(float* sink, int32_t blocks, int32_t iters, void* stream) {
+  g_last_error.clear();
+  if (!sink) return fail(SSA_ERR_NULL, "null sink%s");
+  if (blocks < 1 || iters < 1) return fail(SSA_ERR_SHAPE, "blocks and iters must be positive%s");
+  launch_probe_mfma(sink, blocks, iters, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+ssa_status_t ssa_probe_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  g_last_error.clear();
+  if (!src || !dst) return fail(SSA_ERR_NULL, "null buffer%s");
+  if (bytes % 16 != 0) return fail(SSA_ERR_SHAPE, "bytes must be a multiple of 16%s");
+  if (bytes == 0) return SSA_OK;
+  launch_probe_copy(src, dst, static_cast<int64_t>(bytes), static_cast<hipStream_t>(stream));
+  return launch_status();
 }
 
 int32_t ssa_kernel_count(void) { return kKernelCount; }

@@ -37,6 +37,8 @@ enum KernelId {
   kKSparseMerge,
   kKBwdSparse,
   kKBwdDq,
+  kKProbeMfma,
+  kKProbeCopy,
   kKernelCount
 };
 
@@ -155,6 +157,11 @@ void launch_bwd_sparse(const Dims& D, const SparseBwdArgs& a, hipStream_t s);
 void launch_zero_f32(float* p, int64_t n, hipStream_t s);
 void launch_convert(const float* src, void* dst, int dtype, int64_t n, hipStream_t s);
 size_t loss_scratch_bytes();
+// Machine probes (measurement only): a dense bf16 matrix-core loop of
+// blocks x 4 waves x 4 chains x iters products, and a device copy of `bytes`
+// (a multiple of 16).
+void launch_probe_mfma(float* sink, int blocks, int iters, hipStream_t s);
+void launch_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 void launch_loss_reduce(const float* row_sq, int64_t n_rows, double inv_count, double* scratch, float* losses,
                         hipStream_t s);
 

@@ -145,3 +145,23 @@ def timing_query(kernel: str) -> Tuple[float, int]:
 def kernel_names():
     L = _lib.lib()
     return [L.ssa_kernel_name(i).decode() for i in range(L.ssa_kernel_count())]
+
+
+def ssa_probe_mfma(sink: torch.Tensor, blocks: int, iters: int) -> None:
+    """Enqueue the dense bf16 matrix-core probe (blocks * 16 * iters * 32768 flops).
+
+    ``sink`` is a CUDA float32 tensor of at least blocks * 256 elements."""
+    if not sink.is_cuda or sink.dtype != torch.float32 or sink.numel() < blocks * 256:
+        raise ValueError("sink must be a CUDA float32 tensor of >= blocks * 256 elements")
+    _lib.check(_lib.lib().ssa_probe_mfma(_ptr(sink), int(blocks), int(iters), _stream(sink.device)),
+               "ssa_probe_mfma")
+
+
+def ssa_probe_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
+    """Enqueue the plain device copy probe of src's bytes into dst."""
+    if not (src.is_cuda and dst.is_cuda) or not src.is_contiguous() or not dst.is_contiguous():
+        raise ValueError("src and dst must be contiguous CUDA tensors")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < nbytes:
+        raise ValueError("dst is smaller than src")
+    _lib.check(_lib.lib().ssa_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(src.device)), "ssa_probe_copy")

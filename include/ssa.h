@@ -177,6 +177,28 @@ ssa_status_t ssa_timing_query(const char* kernel, double* total_ms, int64_t* lau
 int32_t ssa_kernel_count(void);
 const char* ssa_kernel_name(int32_t i);
 
+/*
+ * Machine probes for measurement harnesses: the two ceilings that the
+ * attention kernels' rates are read against.  Not part of the attention
+ * method; timed through the hooks above as "probe_mfma" / "probe_copy".
+ *
+ * ssa_probe_mfma: a dense bf16 matrix-core loop.  `blocks` workgroups of 4
+ *   waves (two workgroups per compute unit when blocks >= 2 x the CU count);
+ *   every wave runs 4 independent chains of `iters` 32x32x16 bf16 matrix
+ *   products (32768 flops each): blocks * 16 * iters * 32768 flops in total.
+ *   `sink` (device, blocks * 256 floats, caller-owned) receives the lanes'
+ *   accumulator sums so that no product can be dropped; its values mean
+ *   nothing.  SSA_ERR_NULL for a null sink, SSA_ERR_SHAPE for blocks < 1 or
+ *   iters < 1.
+ * ssa_probe_copy: a plain device copy of `bytes` from src to dst (device,
+ *   caller-owned, not overlapping): `bytes` read and `bytes` written.
+ *   SSA_ERR_NULL for a null pointer, SSA_ERR_SHAPE if bytes is not a multiple
+ *   of 16; bytes == 0 returns SSA_OK and launches nothing.
+ * Both only enqueue on `stream`; SSA_ERR_HIP reports a launch failure.
+ */
+ssa_status_t ssa_probe_mfma(float* sink, int32_t blocks, int32_t iters, void* stream);
+ssa_status_t ssa_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

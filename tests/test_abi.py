@@ -119,6 +119,19 @@ def test_timing_api_host_side(L):
     assert L.ssa_timing_query(b"nope", ctypes.byref(ms), ctypes.byref(n)) == _lib.SSA_ERR_SHAPE
 
 
+def test_probe_argument_checks(L):
+    from block_sparse_full_ssa_amd import _lib
+    FAKE = ctypes.c_void_p(1 << 40)
+    assert L.ssa_probe_mfma(None, 4, 4, None) == _lib.SSA_ERR_NULL
+    assert L.ssa_probe_mfma(FAKE, 0, 4, None) == _lib.SSA_ERR_SHAPE
+    assert L.ssa_probe_mfma(FAKE, 4, 0, None) == _lib.SSA_ERR_SHAPE
+    assert L.ssa_probe_copy(None, FAKE, 16, None) == _lib.SSA_ERR_NULL
+    assert L.ssa_probe_copy(FAKE, FAKE, 24, None) == _lib.SSA_ERR_SHAPE
+    assert L.ssa_probe_copy(FAKE, FAKE, 0, None) == _lib.SSA_OK      # nothing to launch
+    names = [L.ssa_kernel_name(i).decode() for i in range(L.ssa_kernel_count())]
+    assert "probe_mfma" in names and "probe_copy" in names
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     import block_sparse_full_ssa_amd as ssa
