@@ -221,6 +221,45 @@ def alignment_loss(h_full, h_sparse):
 
 
 # ---------------------------------------------------------------------------
+# Diagnostics of the full stream
+# ---------------------------------------------------------------------------
+
+def full_stats(q, k, block, scale, group):
+    """Per-row statistics of the full-attention distribution p_f(t, .).
+
+    The pages measure two properties of the attention distribution without
+    defining a statistic for either; the readings fixed here are:
+      * sink mass: the total p_f(t, i) on the keys of the first key block
+        (i < block), the sink area at the start of the sequence whose
+        over-allocation of attention the English abstract ties to poor
+        length extrapolation (its last sentence);
+      * sparsity: the entropy -sum_i p_f(t, i) ln p_f(t, i) in nats over the
+        causal keys; lower means more concentrated ("intrinsically sparser")
+        attention, which SSA aims for (Sintesi Tecnica, section 5,
+        'Sparsita Intrinseca').
+    Returns (sink_mass, entropy), both [B, Hq, N], and head_means [B, Hq, 2]
+    (the mean over the N rows of each).
+    """
+    B, Hq, N, _ = q.shape
+    sink = np.zeros((B, Hq, N))
+    ent = np.zeros((B, Hq, N))
+    for b in range(B):
+        for h in range(Hq):
+            c = h // group
+            for t0 in range(0, N, _ROW_CHUNK):
+                t_idx = np.arange(t0, min(N, t0 + _ROW_CHUNK))
+                n_keys = int(t_idx.max()) + 1
+                z = scale * (q[b, h, t_idx] @ k[b, c, :n_keys].T)
+                causal = np.arange(n_keys)[None, :] <= t_idx[:, None]
+                p, _ = _softmax_rows(z, causal)
+                sink[b, h, t_idx] = p[:, :min(block, n_keys)].sum(axis=1)
+                plogp = np.where(p > 0, p * np.log(np.where(p > 0, p, 1.0)), 0.0)
+                ent[b, h, t_idx] = -plogp.sum(axis=1)
+    means = np.stack([sink.mean(axis=2), ent.mean(axis=2)], axis=2)
+    return sink, ent, means
+
+
+# ---------------------------------------------------------------------------
 # Backward
 # ---------------------------------------------------------------------------
 
