@@ -174,6 +174,15 @@ def single_stream(ssa, q, k, v, dout, wl, ks, reps):
                        "P_full/P_sparse": round(a / b, 2), "N/(K*block)": round(N / (kk * blk), 2)}
         del sel
     out["sparse_fwd_speedup"] = sp
+
+    # full-stream diagnostics (sink-block mass, entropy, per-head means) in the
+    # forward pass: cost over the plain FULL_ONLY forward, and the head means
+    ms_stats = time_calls(lambda: ssa.ssa_attn_fwd(q, k, v, None, blk, wl.top_k, ssa.FULL_ONLY, stats=True),
+                          reps)
+    st = ssa.ssa_attn_fwd(q, k, v, None, blk, wl.top_k, ssa.FULL_ONLY, stats=True)["head_stats"]
+    out["full_stats"] = {"fwd_ms": round(ms_stats, 3), "overhead": round(ms_stats / ms_full_fwd - 1.0, 4),
+                         "mean_sink_mass": round(float(st[..., 0].mean()), 5),
+                         "mean_entropy_nats": round(float(st[..., 1].mean()), 4)}
     return out
 
 

@@ -31,7 +31,7 @@ OP_FWD = 1
 OP_BWD = 2
 
 EXPORTED = (
-    "ssa_workspace_size", "ssa_select_blocks", "ssa_attn_fwd", "ssa_attn_bwd",
+    "ssa_workspace_size", "ssa_select_blocks", "ssa_attn_fwd", "ssa_attn_fwd_stats", "ssa_attn_bwd",
     "ssa_status_string", "ssa_last_error", "ssa_timing_enable", "ssa_timing_query",
     "ssa_kernel_count", "ssa_kernel_name", "ssa_probe_mfma", "ssa_probe_copy",
 )
@@ -78,6 +78,8 @@ def lib() -> ctypes.CDLL:
     L.ssa_select_blocks.restype = i32
     L.ssa_attn_fwd.argtypes = [shp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.ssa_attn_fwd.restype = i32
+    L.ssa_attn_fwd_stats.argtypes = [shp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.ssa_attn_fwd_stats.restype = i32
     L.ssa_attn_bwd.argtypes = [shp, i32, f32, f32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                vp, sz, vp]
     L.ssa_attn_bwd.restype = i32

@@ -230,11 +230,14 @@ ssa_status_t ssa_select_blocks(const ssa_shape_t* shape, const void* q, const vo
   return launch_status();
 }
 
-ssa_status_t ssa_attn_fwd(const ssa_shape_t* shape, int32_t mode, const void* q, const void* k,
-                          const void* v, const int32_t* sel, void* h_full, void* h_sparse,
-                          float* lse_full, float* lse_sparse, float* delta, float* losses, void* ws,
-                          size_t ws_bytes, void* stream) {
-  g_last_error.clear();
+}  // extern "C"
+
+namespace ssa {
+// The forward of ssa_attn_fwd and ssa_attn_fwd_stats (stats null: none).
+static ssa_status_t attn_fwd(const ssa_shape_t* shape, int32_t mode, const void* q, const void* k,
+                             const void* v, const int32_t* sel, void* h_full, void* h_sparse, float* lse_full,
+                             float* lse_sparse, float* delta, float* losses, float* sink_mass, float* entropy,
+                             float* head_stats, void* ws, size_t ws_bytes, void* stream) {
   Dims D;
   ssa_status_t st = make_dims(shape, &D);
   if (st != SSA_OK) return st;
@@ -256,15 +259,43 @@ ssa_status_t ssa_attn_fwd(const ssa_shape_t* shape, int32_t mode, const void* q,
     launch_sparse_fwd(D, p, s);
     return launch_status();
   }
-  FwdArgs a{q, k, v, sel, h_full, h_sparse, lse_full, lse_sparse, delta, w.row_sq, mode};
+  FwdArgs a{q, k, v, sel, h_full, h_sparse, lse_full, lse_sparse, delta, w.row_sq, mode, sink_mass, entropy};
   if (mode != kSparseOnly && fwd_mfma_supported(D)) launch_fwd_mfma(D, a, s);   // dual and full modes
   else launch_fwd_simt(D, a, s);
   if ((st = launch_status()) != SSA_OK) return st;
   if (dual) {
     launch_loss_reduce(w.row_sq, D.rows(), 1.0 / static_cast<double>(D.q_elems()), w.loss_sums, losses, s);
+    if ((st = launch_status()) != SSA_OK) return st;
+  }
+  if (head_stats) {
+    launch_head_means(sink_mass, entropy, static_cast<int64_t>(D.B) * D.Hq, D.N, head_stats, s);
     st = launch_status();
   }
   return st;
+}
+}  // namespace ssa
+
+extern "C" {
+
+ssa_status_t ssa_attn_fwd(const ssa_shape_t* shape, int32_t mode, const void* q, const void* k,
+                          const void* v, const int32_t* sel, void* h_full, void* h_sparse,
+                          float* lse_full, float* lse_sparse, float* delta, float* losses, void* ws,
+                          size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  return attn_fwd(shape, mode, q, k, v, sel, h_full, h_sparse, lse_full, lse_sparse, delta, losses, nullptr,
+                  nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+ssa_status_t ssa_attn_fwd_stats(const ssa_shape_t* shape, int32_t mode, const void* q, const void* k,
+                                const void* v, const int32_t* sel, void* h_full, void* h_sparse,
+                                float* lse_full, float* lse_sparse, float* delta, float* losses,
+                                float* sink_mass, float* entropy, float* head_stats, void* ws,
+                                size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  if (mode == kSparseOnly) return fail(SSA_ERR_UNSUPPORTED, "the statistics describe the full stream%s");
+  if (!sink_mass || !entropy) return fail(SSA_ERR_NULL, "sink_mass and entropy are required%s");
+  return attn_fwd(shape, mode, q, k, v, sel, h_full, h_sparse, lse_full, lse_sparse, delta, losses, sink_mass,
+                  entropy, head_stats, ws, ws_bytes, stream);
 }
 
 ssa_status_t ssa_attn_bwd(const ssa_shape_t* shape, int32_t mode, float w_sparsity, float w_commit,

@@ -69,7 +69,7 @@ __device__ __forceinline__ float max16(const f32x16& v) {
 
 // Two workgroups per CU (256 VGPRs and 68 KiB of LDS each at nb <= 256), so
 // one wave's softmax overlaps the other wave's matrix work on every SIMD.
-template <int MODE>
+template <int MODE, bool STATS>
 __global__ void __launch_bounds__(256, 2)
     k_fwd_mfma(FwdArgs a, int Hq, int G, int N, int block, int nb, int K, float scale_log2, int n_qtiles) {
   constexpr bool kSparse = MODE == kModeDual;
@@ -130,6 +130,10 @@ __global__ void __launch_bounds__(256, 2)
     os[dt] = f32x16{};
   }
   float mf = -INFINITY, lf = 0.f, ms = -INFINITY, ls = 0.f;
+  // diagnostics (STATS): the full stream's mass on the first key block, and
+  // sum_i e_i x_i with x_i = z_i log2(e) - mf and e_i = 2^x_i, both relative
+  // to the running maximum like lf, for the entropy ln2 (log2 lf - ex / lf)
+  float sink_l = 0.f, ex_l = 0.f;
 
   const int j_last = min(N - 1, q0 + kBM - 1) / kBN;
   if (kSparse) __syncthreads();
@@ -221,11 +225,20 @@ __global__ void __launch_bounds__(256, 2)
 
       // ---- full stream
       bf16x8 pf[2];
-      float sum = 0.f;
+      float sum = 0.f, ex = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        s[i] = fast_exp2(fmaf(s[i], scale_log2, -mfn));
+        float x = fmaf(s[i], scale_log2, -mfn);
+        if (STATS) x = fmaxf(x, -256.f);           // masked keys: e = 0 and e x = 0, not NaN
+        s[i] = fast_exp2(x);
         sum += s[i];
+        if (STATS) ex = fmaf(s[i], x, ex);
+      }
+      if (STATS) {
+        // moving the maximum by dm = mfn - mf shifts every earlier x by -dm
+        // and scales every earlier e by alpha (0 on the first update)
+        ex_l = (alpha == 0.f ? 0.f : alpha * fmaf(-(mfn - mf), lf, ex_l)) + ex;
+        sink_l = sink_l * alpha + (kbase < block ? sum : 0.f);
       }
       lf = lf * alpha + sum;
       if (__any(alpha != 1.f)) {
@@ -291,6 +304,10 @@ __global__ void __launch_bounds__(256, 2)
   // ---- epilogue
   if (!wave_live) return;
   lf += __shfl_xor(lf, 32, 64);
+  if (STATS) {
+    sink_l += __shfl_xor(sink_l, 32, 64);
+    ex_l += __shfl_xor(ex_l, 32, 64);
+  }
   ls += __shfl_xor(ls, 32, 64);
   const float inv_f = 1.f / lf, inv_s = 1.f / ls;
   const bool row_ok = qrow < N;
@@ -330,19 +347,23 @@ __global__ void __launch_bounds__(256, 2)
       a.delta[row] = -expm1f(lse_s - lse_f);
       a.row_sq[row] = sq;
     }
+    if (STATS) {
+      a.sink_mass[row] = sink_l / lf;
+      a.entropy[row] = kLn2 * (fast_log2(lf) - ex_l / lf);
+    }
   }
 }
 
-template <int MODE>
+template <int MODE, bool STATS>
 void launch_mode(const Dims& D, const FwdArgs& a, size_t lds, int n_qtiles, float scale_log2, hipStream_t s) {
   static size_t granted = 0;    // LDS above 64 KiB in total must be requested per kernel
   if (lds > granted) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fwd_mfma<MODE>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fwd_mfma<MODE, STATS>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     granted = lds;
   }
   dim3 grid(D.B * D.Hq * n_qtiles);   // work items from qtile_item
-  hipLaunchKernelGGL(k_fwd_mfma<MODE>, grid, dim3(256), lds, s, a, D.Hq, D.G, D.N, D.block, D.nb, D.K,
+  hipLaunchKernelGGL((k_fwd_mfma<MODE, STATS>), grid, dim3(256), lds, s, a, D.Hq, D.G, D.N, D.block, D.nb, D.K,
                      scale_log2, n_qtiles);
 }
 
@@ -365,8 +386,14 @@ void launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s) {
   const size_t lds = lds_bytes(D);
   const float scale_log2 = D.scale * 1.4426950408889634f;
   timing_begin(kKFwdMfma, s);
-  if (a.mode == kFullOnly) launch_mode<kModeFull>(D, a, lds, n_qtiles, scale_log2, s);
-  else launch_mode<kModeDual>(D, a, lds, n_qtiles, scale_log2, s);
+  const bool stats = a.sink_mass != nullptr;
+  if (a.mode == kFullOnly) {
+    if (stats) launch_mode<kModeFull, true>(D, a, lds, n_qtiles, scale_log2, s);
+    else launch_mode<kModeFull, false>(D, a, lds, n_qtiles, scale_log2, s);
+  } else {
+    if (stats) launch_mode<kModeDual, true>(D, a, lds, n_qtiles, scale_log2, s);
+    else launch_mode<kModeDual, false>(D, a, lds, n_qtiles, scale_log2, s);
+  }
   timing_end(kKFwdMfma, s);
 }
 

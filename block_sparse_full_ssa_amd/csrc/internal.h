@@ -58,6 +58,10 @@ struct FwdArgs {
   float *lse_full, *lse_sparse, *delta;
   float* row_sq;     // per-row sum of (h_full - h_sparse)^2, dual modes only
   int mode;
+  // optional full-stream diagnostics per row [B, Hq, N]: probability mass on
+  // the first key block, entropy (nats); both null or both set
+  float* sink_mass = nullptr;
+  float* entropy = nullptr;
 };
 void launch_fwd_simt(const Dims& D, const FwdArgs& a, hipStream_t s);
 
@@ -160,6 +164,8 @@ size_t loss_scratch_bytes();
 // Machine probes (measurement only): a dense bf16 matrix-core loop of
 // blocks x 4 waves x 4 chains x iters products, and a device copy of `bytes`
 // (a multiple of 16).
+// Per-head means over the N rows of two per-row arrays [B*Hq][N] -> out [B*Hq][2].
+void launch_head_means(const float* a, const float* b, int64_t n_heads, int N, float* out, hipStream_t s);
 void launch_probe_mfma(float* sink, int blocks, int iters, hipStream_t s);
 void launch_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 void launch_loss_reduce(const float* row_sq, int64_t n_rows, double inv_count, double* scratch, float* losses,

@@ -85,6 +85,32 @@ __global__ void __launch_bounds__(256) k_loss_final(const double* __restrict__ s
   }
 }
 
+// Per-head means of two per-row arrays: workgroup h adds rows h*N .. h*N+N-1
+// of each in fp64 (fixed order), out[2h] and out[2h+1] = the sums / N.
+__global__ void __launch_bounds__(256) k_head_means(const float* __restrict__ a, const float* __restrict__ b,
+                                                    int N, float* __restrict__ out) {
+  __shared__ double buf[256];
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * N;
+  double sa = 0.0, sb = 0.0;
+  for (int i = threadIdx.x; i < N; i += 256) {
+    sa += static_cast<double>(a[base + i]);
+    sb += static_cast<double>(b[base + i]);
+  }
+  const double ta = block_sum_f64(sa, buf);
+  __syncthreads();                        // buf is reused
+  const double tb = block_sum_f64(sb, buf);
+  if (threadIdx.x == 0) {
+    out[2 * static_cast<int64_t>(blockIdx.x)] = static_cast<float>(ta / N);
+    out[2 * static_cast<int64_t>(blockIdx.x) + 1] = static_cast<float>(tb / N);
+  }
+}
+
+void launch_head_means(const float* a, const float* b, int64_t n_heads, int N, float* out, hipStream_t s) {
+  timing_begin(kKLossReduce, s);
+  hipLaunchKernelGGL(k_head_means, dim3(static_cast<unsigned>(n_heads)), dim3(256), 0, s, a, b, N, out);
+  timing_end(kKLossReduce, s);
+}
+
 size_t loss_scratch_bytes() { return kLossParts * sizeof(double); }
 
 void launch_loss_reduce(const float* row_sq, int64_t n_rows, double inv_count, double* scratch, float* losses,

@@ -47,6 +47,10 @@ __global__ void __launch_bounds__(256) k_fwd_simt(FwdArgs a, int Hq, int G, int 
     os[e] = 0.f;
   }
   float mf = -INFINITY, lf = 0.f, ms = -INFINITY, ls = 0.f;
+  // optional diagnostics: full-stream mass on the first key block, and
+  // sum_i p_i (z_i - mf) with p_i = exp(z_i - mf), for the entropy
+  const bool stats = want_full && a.sink_mass != nullptr;
+  float sink_l = 0.f, ex_l = 0.f;
   int ptr = 0;
   int next_blk = want_sparse ? selp[0] : -1;
 
@@ -62,6 +66,11 @@ __global__ void __launch_bounds__(256) k_fwd_simt(FwdArgs a, int Hq, int G, int 
     if (want_full) {
       const float mn = fmaxf(mf, z);
       const float al = expf(mf - mn), p = expf(z - mn);
+      if (stats) {
+        // a new maximum shifts every earlier exponent by mf - mn (al = 0 on the first key)
+        ex_l = (al == 0.f ? 0.f : al * fmaf(mf - mn, lf, ex_l)) + p * (z - mn);
+        sink_l = sink_l * al + (i < block ? p : 0.f);
+      }
       lf = lf * al + p;
 #pragma unroll
       for (int e = 0; e < E; ++e) of[e] = of[e] * al + p * vv[e];
@@ -101,6 +110,10 @@ __global__ void __launch_bounds__(256) k_fwd_simt(FwdArgs a, int Hq, int G, int 
     if (want_full && want_sparse) {
       a.delta[row] = -expm1f(lse_s - lse_f);
       a.row_sq[row] = sq;
+    }
+    if (stats) {
+      a.sink_mass[row] = sink_l / lf;
+      a.entropy[row] = logf(lf) - ex_l / lf;
     }
   }
 }

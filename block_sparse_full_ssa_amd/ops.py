@@ -78,8 +78,13 @@ def ssa_select_blocks(q: torch.Tensor, k: torch.Tensor, block: int, top_k: int) 
 
 
 def ssa_attn_fwd(q, k, v, sel, block: int, top_k: int, mode: int = DUAL_ACTIVE_FULL,
-                 scale: Optional[float] = None, want_lse: bool = True) -> Dict[str, torch.Tensor]:
-    """Forward of one SSA layer; returns the outputs the mode defines."""
+                 scale: Optional[float] = None, want_lse: bool = True,
+                 stats: bool = False) -> Dict[str, torch.Tensor]:
+    """Forward of one SSA layer; returns the outputs the mode defines.
+
+    With ``stats`` (modes with the full stream) it calls ssa_attn_fwd_stats and
+    also returns the full stream's per-row ``sink_mass`` and ``entropy`` and
+    their per-head means ``head_stats`` [B, Hq, 2]."""
     dev = _dev_check(q, k, v, sel)
     shape = make_shape(q, k, block, top_k, scale)
     B, Hq, N, d = q.shape
@@ -98,12 +103,19 @@ def ssa_attn_fwd(q, k, v, sel, block: int, top_k: int, mode: int = DUAL_ACTIVE_F
         out["delta"] = torch.empty(B, Hq, N, **f32)
         out["losses"] = torch.empty(2, **f32)
     ws, wp, wn = _workspace(shape, mode, _lib.OP_FWD, dev)
-    st = _lib.lib().ssa_attn_fwd(
-        ctypes.byref(shape), int(mode), _ptr(q), _ptr(k), _ptr(v), _ptr(sel),
-        _ptr(out.get("h_full")), _ptr(out.get("h_sparse")), _ptr(out.get("lse_full")),
-        _ptr(out.get("lse_sparse")), _ptr(out.get("delta")), _ptr(out.get("losses")),
-        ctypes.c_void_p(wp), wn, _stream(dev))
-    _lib.check(st, "ssa_attn_fwd")
+    common = (ctypes.byref(shape), int(mode), _ptr(q), _ptr(k), _ptr(v), _ptr(sel),
+              _ptr(out.get("h_full")), _ptr(out.get("h_sparse")), _ptr(out.get("lse_full")),
+              _ptr(out.get("lse_sparse")), _ptr(out.get("delta")), _ptr(out.get("losses")))
+    if stats:
+        out["sink_mass"] = torch.empty(B, Hq, N, **f32)
+        out["entropy"] = torch.empty(B, Hq, N, **f32)
+        out["head_stats"] = torch.empty(B, Hq, 2, **f32)
+        st = _lib.lib().ssa_attn_fwd_stats(*common, _ptr(out["sink_mass"]), _ptr(out["entropy"]),
+                                           _ptr(out["head_stats"]), ctypes.c_void_p(wp), wn, _stream(dev))
+        _lib.check(st, "ssa_attn_fwd_stats")
+    else:
+        st = _lib.lib().ssa_attn_fwd(*common, ctypes.c_void_p(wp), wn, _stream(dev))
+        _lib.check(st, "ssa_attn_fwd")
     if ws is not None:
         out["_ws"] = ws   # keeps the workspace alive until the caller drops the dict
     return out

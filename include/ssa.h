@@ -135,6 +135,29 @@ ssa_status_t ssa_attn_fwd(const ssa_shape_t* shape, int32_t mode, const void* q,
                           float* losses, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * ssa_attn_fwd plus diagnostics of the full-attention distribution p_full,
+ * computed in the same pass.  The pages track how much attention lands on
+ * the sink area at the start of the sequence (English abstract, last
+ * sentence) and how sparse the attention is (Sintesi Tecnica, section 5,
+ * 'Sparsita Intrinseca') without defining a statistic; the ones written here:
+ *   sink_mass [B,Hq,N] fp32: sum of p_full(t, i) over the first key block
+ *     (keys i < block);
+ *   entropy   [B,Hq,N] fp32: -sum_i p_full(t, i) ln p_full(t, i) (nats) over
+ *     the causal keys;
+ *   head_stats [B,Hq,2] fp32 (optional, NULL to skip): the mean over the N
+ *     rows of sink_mass and of entropy, per head.
+ * Modes with the full stream only (dual, SSA_FULL_ONLY): SSA_SPARSE_ONLY
+ * returns SSA_ERR_UNSUPPORTED.  sink_mass and entropy are required
+ * (SSA_ERR_NULL).  All other arguments, the workspace size and the errors are
+ * those of ssa_attn_fwd.
+ */
+ssa_status_t ssa_attn_fwd_stats(const ssa_shape_t* shape, int32_t mode, const void* q,
+                                const void* k, const void* v, const int32_t* sel, void* h_full,
+                                void* h_sparse, float* lse_full, float* lse_sparse, float* delta,
+                                float* losses, float* sink_mass, float* entropy, float* head_stats,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Backward of one SSA layer.  With M = B*Hq*N*d the gradients reaching the
  * two outputs are
  *   G_full   = [active = full]   d_out + w_sparsity (2/M) (h_full - h_sparse)

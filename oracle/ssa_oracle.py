@@ -248,15 +248,21 @@ def full_stats(q, k, block, scale, group):
             c = h // group
             for t0 in range(0, N, _ROW_CHUNK):
                 t_idx = np.arange(t0, min(N, t0 + _ROW_CHUNK))
-                n_keys = int(t_idx.max()) + 1
-                z = scale * (q[b, h, t_idx] @ k[b, c, :n_keys].T)
-                causal = np.arange(n_keys)[None, :] <= t_idx[:, None]
-                p, _ = _softmax_rows(z, causal)
-                sink[b, h, t_idx] = p[:, :min(block, n_keys)].sum(axis=1)
-                plogp = np.where(p > 0, p * np.log(np.where(p > 0, p, 1.0)), 0.0)
-                ent[b, h, t_idx] = -plogp.sum(axis=1)
+                sink[b, h, t_idx], ent[b, h, t_idx] = stats_rows(q[b, h, t_idx], t_idx, k[b, c], block, scale)
     means = np.stack([sink.mean(axis=2), ent.mean(axis=2)], axis=2)
     return sink, ent, means
+
+
+def stats_rows(q_rows, t_idx, k_c, block, scale):
+    """(sink_mass, entropy) [R] of full_stats for some query rows of one head
+    (q_rows [R, d] at positions t_idx; k_c [N, d] of its KV head)."""
+    n_keys = int(t_idx.max()) + 1
+    z = scale * (q_rows @ k_c[:n_keys].T)
+    causal = np.arange(n_keys)[None, :] <= t_idx[:, None]
+    p, _ = _softmax_rows(z, causal)
+    sink = p[:, :min(block, n_keys)].sum(axis=1)
+    plogp = np.where(p > 0, p * np.log(np.where(p > 0, p, 1.0)), 0.0)
+    return sink, -plogp.sum(axis=1)
 
 
 # ---------------------------------------------------------------------------

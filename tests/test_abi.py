@@ -119,6 +119,22 @@ def test_timing_api_host_side(L):
     assert L.ssa_timing_query(b"nope", ctypes.byref(ms), ctypes.byref(n)) == _lib.SSA_ERR_SHAPE
 
 
+def test_fwd_stats_argument_checks(L):
+    from block_sparse_full_ssa_amd import _lib
+    FAKE = ctypes.c_void_p(1 << 40)
+    s = _shape()
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE]   # q .. losses
+    st = L.ssa_attn_fwd_stats(ctypes.byref(s), _lib.SPARSE_ONLY, *args, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == _lib.SSA_ERR_UNSUPPORTED
+    st = L.ssa_attn_fwd_stats(ctypes.byref(s), _lib.FULL_ONLY, *args, None, FAKE, None, FAKE, 1 << 30, None)
+    assert st == _lib.SSA_ERR_NULL
+    st = L.ssa_attn_fwd_stats(ctypes.byref(s), _lib.FULL_ONLY, *args, FAKE, None, None, FAKE, 1 << 30, None)
+    assert st == _lib.SSA_ERR_NULL
+    bad = _shape(seqlen=250)                      # not a multiple of the block
+    st = L.ssa_attn_fwd_stats(ctypes.byref(bad), _lib.FULL_ONLY, *args, FAKE, FAKE, None, FAKE, 1 << 30, None)
+    assert st == _lib.SSA_ERR_SHAPE
+
+
 def test_probe_argument_checks(L):
     from block_sparse_full_ssa_amd import _lib
     FAKE = ctypes.c_void_p(1 << 40)

@@ -246,6 +246,39 @@ def test_long_layer_64k_sinks_full_size():
         _check_rows_fwd(wl.name, wl, b, h, t_idx, qf, kf, vf, sel_np, out)
 
 
+def test_long_layer_64k_sink_stats_full_size():
+    """The 64K layer with planted sinks, full stream with its diagnostics:
+    sink-block mass and entropy on sampled rows against the oracle, and over
+    the whole layer 0 <= sink <= 1 (= 1 inside the first block),
+    0 <= entropy <= ln(t + 1), head means = the means of the rows."""
+    wl = si.WORKLOADS["long_n64k_sinks"]
+    _say(f"full-size {wl.name}: full stream with statistics")
+    q, k, v, _ = si.draw_qkv(wl, 0)
+    qd, kd, vd = (x.to("cuda:0") for x in (q, k, v))
+    fwd = ssa().ssa_attn_fwd(qd, kd, vd, None, wl.block, wl.top_k, oracle.FULL_ONLY, stats=True)
+    torch.cuda.synchronize()
+    sink, ent, hs = (fwd[key].double().cpu() for key in ("sink_mass", "entropy", "head_stats"))
+    del qd, kd, vd, fwd
+    t = torch.arange(wl.seqlen, dtype=torch.float64)
+    assert float(sink.min()) >= 0.0 and float(sink.max()) <= 1.0 + 1e-6
+    assert float((sink[..., :wl.block] - 1.0).abs().max()) <= 1e-6
+    assert float(ent.min()) >= -1e-5 and bool((ent <= torch.log(t + 1) + 1e-4).all())
+    assert float((hs[..., 0] - sink.mean(dim=2)).abs().max()) <= 1e-6
+    assert float((hs[..., 1] - ent.mean(dim=2)).abs().max()) <= 1e-5 * float(ent.abs().max())
+    _say(f"  mean sink mass {float(sink.mean()):.4f}, mean entropy {float(ent.mean()):.4f}")
+
+    qf, kf = si.to_f64(q), si.to_f64(k)
+    rng = np.random.default_rng(3)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    for b, h in ((0, 1), (0, 14)):
+        t_idx = _sample_rows(rng, wl.seqlen, wl.block, wl.top_k, 16)
+        _say(f"  rows b{b} h{h}: {t_idx.size}")
+        rs, re = oracle.stats_rows(qf[b, h, t_idx], t_idx, kf[b, h // wl.group], wl.block, scale)
+        idx = torch.from_numpy(t_idx)
+        assert float(np.abs(sink[b, h, idx].numpy() - rs).max()) <= 1e-4 + 1e-4 * float(np.abs(rs).max())
+        assert np.all(np.abs(ent[b, h, idx].numpy() - re) <= 1e-4 + 1e-4 * np.abs(re))
+
+
 # ----------------------------------------------------------- 4-layer slice --
 
 def test_multilayer_slice_full_size():

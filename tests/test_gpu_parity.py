@@ -5,6 +5,7 @@ Selection must match bit for bit on screened inputs (no two scores within
 gpu_cases.  Cases span several tiles, ragged tails, the block sizes 32 / 64 /
 128, GQA groups 1..4, top_k = 1 and top_k >= number of blocks.
 """
+import functools
 import math
 import sys
 
@@ -15,7 +16,7 @@ import torch
 import oracle
 import ssa_inputs as si
 
-from gpu_cases import (TOL, assert_close, assert_normwise, inputs, oracle_fwd, oracle_select,
+from gpu_cases import (TOL, assert_close, assert_normwise, excess, inputs, oracle_fwd, oracle_select,
                        scale_of, to_dev)
 
 pytestmark = pytest.mark.gpu
@@ -208,6 +209,55 @@ def test_fwd_deterministic():
     b = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, wl.top_k, oracle.DUAL_ACTIVE_FULL)
     for key in ("h_full", "h_sparse", "lse_full", "lse_sparse", "delta", "losses"):
         assert torch.equal(a[key], b[key]), key
+
+
+# ------------------------------------------------------------ diagnostics --
+
+# Statistics are fp32 outputs computed from the same rounded inputs as the
+# oracle; their error is the fp32 rounding of the logits (|z| <~ 30, ~1e-6)
+# and of ln2 (log2 l - A / l) with log2 l <~ 20 (~1e-5).
+STATS_TOL = {torch.bfloat16: (1e-4, 1e-4), torch.float32: (1e-5, 1e-5)}
+
+
+@functools.lru_cache(maxsize=None)
+def _oracle_stats(name):
+    wl = TINY if name == "tiny" else SMALL[name]
+    _, (qf, kf, _) = inputs(wl, 0, (wl.top_k,))
+    return oracle.full_stats(qf, kf, wl.block, scale_of(wl), wl.group)
+
+
+@pytest.mark.parametrize("mode", [oracle.DUAL_ACTIVE_FULL, oracle.FULL_ONLY])
+@pytest.mark.parametrize("name", ["tiny"] + list(SMALL))
+def test_fwd_stats_match_oracle(name, mode):
+    """Sink-block mass, entropy and their per-head means against the oracle;
+    the attention outputs of the statistics pass equal those of the plain
+    forward bit for bit."""
+    wl = TINY if name == "tiny" else SMALL[name]
+    _say(f"fwd stats {name} mode {mode}")
+    (q, k, v), _ = inputs(wl, 0, (wl.top_k,))
+    qd, kd, vd = to_dev(q, k, v)
+    sel = torch.from_numpy(oracle_select(wl, 0, (wl.top_k,), wl.top_k)[0]).to("cuda:0")
+    out = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, wl.top_k, mode, stats=True)
+    plain = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, wl.top_k, mode)
+    torch.cuda.synchronize()
+    sink, ent, means = _oracle_stats(name)
+    atol, rtol = STATS_TOL[wl.dtype]
+    for key, got, want in (("sink_mass", out["sink_mass"], sink), ("entropy", out["entropy"], ent),
+                           ("head_stats", out["head_stats"], means)):
+        e = excess(got, want, atol, rtol)
+        assert e <= 0, f"{name} {key}: exceeds tolerance by {e:.3g}"
+    for key in ("h_full", "lse_full", "h_sparse", "lse_sparse", "delta", "losses"):
+        if key in plain:
+            assert torch.equal(out[key], plain[key]), key
+
+
+def test_fwd_stats_sparse_only_unsupported():
+    wl = SMALL["gqa_n512_b64_k4"]
+    (q, k, v), _ = inputs(wl, 0, (wl.top_k,))
+    qd, kd, vd = to_dev(q, k, v)
+    sel = ssa().ssa_select_blocks(qd, kd, wl.block, wl.top_k)
+    with pytest.raises(ssa().SSAError):
+        ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, wl.top_k, oracle.SPARSE_ONLY, stats=True)
 
 
 # ---------------------------------------------------------------- backward --
