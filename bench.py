@@ -94,6 +94,7 @@ def parse():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--sweep", action="store_true", help="also time every top_k of the workload's sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the 128K-cache decode leg")
     ap.add_argument("--no-single-stream", action="store_true",
                     help="skip the FULL_ONLY / SPARSE_ONLY measurements")
     ap.add_argument("--cpu-rows", type=int, default=12288, help="query rows in the CPU-oracle sample")
@@ -184,6 +185,53 @@ def single_stream(ssa, q, k, v, dout, wl, ks, reps):
                          "mean_sink_mass": round(float(st[..., 0].mean()), 5),
                          "mean_entropy_nats": round(float(st[..., 1].mean()), 4)}
     return out
+
+
+def decode_128k(ssa, dev, reps):
+    """One decode step per sequence at the end of a 131072-token cache (B=4,
+    16 query / 4 KV heads, d 128, block 64, top_k 32, four planted sinks):
+    SPARSE_ONLY (selection against the block-mean cache + the selected
+    blocks) against FULL_ONLY (every cached key).  Bytes are the unique cache
+    rows a step must read: K and V of every key of each KV head (full), or
+    of the union of the blocks its G query heads selected plus the block
+    means (sparse)."""
+    import torch
+
+    import ssa_inputs as si
+
+    wl = si.WORKLOADS["decode_b4_n128k_sinks"]
+    q, k, v = (x.to(dev) for x in si.draw_decode(wl, 0))
+    L, blk, K, d = wl.seqlen, wl.block, wl.top_k, wl.head_dim
+    mu = torch.empty(wl.batch, wl.hkv, L // blk, d, dtype=torch.float32, device=dev)
+    ssa.ssa_cache_block_means(k, mu, blk, 0, L // blk)
+    pos = torch.full((wl.batch,), L - 1, dtype=torch.int32, device=dev)
+    sp = ssa.ssa_decode(q, k, v, mu, pos, blk, K, ssa.SPARSE_ONLY)
+    ssa.ssa_decode(q, k, v, None, pos, blk, K, ssa.FULL_ONLY)
+    torch.cuda.synchronize()
+
+    def gpu_ms(mode, m):
+        # the library's events around its decode launches (selection, parts,
+        # merge): device time, without the host's per-call overhead
+        ssa.timing_enable(True)
+        for _ in range(reps):
+            ssa.ssa_decode(q, k, v, m, pos, blk, K, mode)
+        total, n = ssa.timing_query("decode")
+        ssa.timing_enable(False)
+        return total / n
+
+    ms_sp = gpu_ms(ssa.SPARSE_ONLY, mu)
+    ms_fu = gpu_ms(ssa.FULL_ONLY, None)
+    row = d * k.element_size() * 2                                  # one key + one value row
+    sel = sp["sel"].view(wl.batch, wl.hkv, wl.group * K).cpu()
+    blocks = sum(len(set(x.tolist()) - {-1}) for x in sel.view(-1, wl.group * K))
+    bytes_sp = blocks * blk * row + mu.numel() * 4
+    bytes_fu = wl.batch * wl.hkv * L * row
+    return {"workload": wl.name, "positions": "last token of each sequence (t = 131071)",
+            "sparse_ms": round(ms_sp, 4), "full_ms": round(ms_fu, 4), "speedup": round(ms_fu / ms_sp, 2),
+            "sparse_GBps": round(bytes_sp / (ms_sp / 1e3) / 1e9, 1),
+            "full_GBps": round(bytes_fu / (ms_fu / 1e3) / 1e9, 1),
+            "sparse_bytes": bytes_sp, "full_bytes": bytes_fu,
+            "tokens_per_s_sparse": round(wl.batch / (ms_sp / 1e3), 1)}
 
 
 def measured_ceilings(ssa, dev):
@@ -315,6 +363,7 @@ def main():
         ks = list(wl.top_k_sweep) if (args.sweep and wl.top_k_sweep) else [K]
         single = single_stream(ssa, q, k, v, dout, wl, ks, max(3, args.steps // 2))
 
+    decode = None if args.no_decode else decode_128k(ssa, dev, max(10, args.steps))
     ceilings = measured_ceilings(ssa, dev)
     if roofline is not None:
         roofline["frac_of_measured_peak"] = round(roofline["achieved"] / ceilings["mfma_bf16_tflops"], 4)
@@ -346,6 +395,7 @@ def main():
         "roofline": roofline,
         "kernel_frac_of_bf16_peak": kernel_frac,
         "measured_ceilings": ceilings,
+        "decode_128k": decode,
         "frac_of_measured_mfma": round(tflops / ceilings["mfma_bf16_tflops"], 4),
         "cpu_baseline": cpu,
     }

@@ -29,11 +29,13 @@ SPARSE_ONLY = 3
 OP_SELECT = 0
 OP_FWD = 1
 OP_BWD = 2
+OP_DECODE = 3
 
 EXPORTED = (
     "ssa_workspace_size", "ssa_select_blocks", "ssa_attn_fwd", "ssa_attn_fwd_stats", "ssa_attn_bwd",
     "ssa_status_string", "ssa_last_error", "ssa_timing_enable", "ssa_timing_query",
     "ssa_kernel_count", "ssa_kernel_name", "ssa_probe_mfma", "ssa_probe_copy",
+    "ssa_cache_block_means", "ssa_decode",
 )
 
 
@@ -96,6 +98,10 @@ def lib() -> ctypes.CDLL:
     L.ssa_kernel_count.restype = i32
     L.ssa_kernel_name.argtypes = [i32]
     L.ssa_kernel_name.restype = ctypes.c_char_p
+    L.ssa_cache_block_means.argtypes = [shp, vp, vp, i32, i32, vp]
+    L.ssa_cache_block_means.restype = i32
+    L.ssa_decode.argtypes = [shp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.ssa_decode.restype = i32
     L.ssa_probe_mfma.argtypes = [vp, i32, i32, vp]
     L.ssa_probe_mfma.restype = i32
     L.ssa_probe_copy.argtypes = [vp, vp, sz, vp]

@@ -33,7 +33,7 @@ static std::vector<TimingRec> g_recs;
 static const char* kKernelNames[kKernelCount] = {
     "block_mean", "select", "fwd_simt", "fwd_mfma", "loss_reduce",
     "bwd_pre",    "bwd_simt", "bwd_mfma", "convert", "zero", "bucket", "sparse_part", "sparse_merge",
-    "bwd_sparse", "bwd_dq", "probe_mfma", "probe_copy"};
+    "bwd_sparse", "bwd_dq", "probe_mfma", "probe_copy", "decode"};
 
 void timing_begin(int kernel, hipStream_t s) {
   if (!g_timing) return;
@@ -179,10 +179,22 @@ static BwdWs carve_bwd(const Dims& D, int mode, Carver& c) {
   return w;
 }
 
+struct DecodeWs {
+  float *part_o, *part_ml;
+};
+static DecodeWs carve_decode(const Dims& D, int mode, Carver& c) {
+  const size_t n = static_cast<size_t>(D.B) * D.Hq * decode_parts(D, mode == kSparseOnly);
+  DecodeWs w{};
+  w.part_o = c.take<float>(n * D.d * sizeof(float));
+  w.part_ml = c.take<float>(n * 2 * sizeof(float));
+  return w;
+}
+
 static size_t ws_need(const Dims& D, int mode, int op) {
   Carver c{nullptr};
   if (op == SSA_OP_SELECT) c.take<float>(static_cast<size_t>(D.B) * D.Hkv * D.d * D.nb * sizeof(float));
   else if (op == SSA_OP_FWD) carve_fwd(D, mode, c);
+  else if (op == SSA_OP_DECODE) carve_decode(D, mode, c);
   else carve_bwd(D, mode, c);
   return c.used;
 }
@@ -210,7 +222,8 @@ extern "C" {
 
 size_t ssa_workspace_size(const ssa_shape_t* shape, int32_t mode, int32_t op) {
   Dims D;
-  if (make_dims(shape, &D) != SSA_OK || !valid_mode(mode) || op < SSA_OP_SELECT || op > SSA_OP_BWD) return 0;
+  if (make_dims(shape, &D) != SSA_OK || !valid_mode(mode) || op < SSA_OP_SELECT || op > SSA_OP_DECODE) return 0;
+  if (op == SSA_OP_DECODE && mode != kFullOnly && mode != kSparseOnly) return 0;
   return ws_need(D, mode, op);
 }
 
@@ -397,6 +410,39 @@ ssa_status_t ssa_timing_query(const char* kernel, double* total_ms, int64_t* lau
   *total_ms = tot;
   *launches = n;
   return SSA_OK;
+}
+
+ssa_status_t ssa_cache_block_means(const ssa_shape_t* shape, const void* k_cache, float* mu_cache,
+                                   int32_t block_begin, int32_t block_end, void* stream) {
+  g_last_error.clear();
+  Dims D;
+  ssa_status_t st = make_dims(shape, &D);
+  if (st != SSA_OK) return st;
+  if (!k_cache || !mu_cache) return fail(SSA_ERR_NULL, "k_cache and mu_cache are required%s");
+  if (block_begin < 0 || block_end > D.nb || block_begin > block_end)
+    return fail(SSA_ERR_SHAPE, "need 0 <= block_begin <= block_end <= seqlen / block%s");
+  if (block_begin == block_end) return SSA_OK;
+  launch_cache_means(D, k_cache, mu_cache, block_begin, block_end, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+ssa_status_t ssa_decode(const ssa_shape_t* shape, int32_t mode, const void* q, const void* k_cache,
+                        const void* v_cache, const float* mu_cache, const int32_t* pos, void* h, float* lse,
+                        int32_t* sel, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  Dims D;
+  ssa_status_t st = make_dims(shape, &D);
+  if (st != SSA_OK) return st;
+  if (mode != kFullOnly && mode != kSparseOnly)
+    return fail(SSA_ERR_UNSUPPORTED, "decode runs one stream: SSA_FULL_ONLY or SSA_SPARSE_ONLY%s");
+  if (!q || !k_cache || !v_cache || !pos || !h) return fail(SSA_ERR_NULL, "q, k_cache, v_cache, pos and h are required%s");
+  if (mode == kSparseOnly && (!mu_cache || !sel)) return fail(SSA_ERR_NULL, "mu_cache and sel are required%s");
+  if ((st = check_ws(D, mode, SSA_OP_DECODE, ws, ws_bytes)) != SSA_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  DecodeWs w = carve_decode(D, mode, c);
+  DecodeArgs a{q, k_cache, v_cache, mu_cache, pos, mode == kSparseOnly ? sel : nullptr, w.part_o, w.part_ml, h, lse};
+  launch_decode(D, a, static_cast<hipStream_t>(stream));
+  return launch_status();
 }
 
 ssa_status_t ssa_probe_mfma(float* sink, int32_t blocks, int32_t iters, void* stream) {

@@ -39,6 +39,7 @@ enum KernelId {
   kKBwdDq,
   kKProbeMfma,
   kKProbeCopy,
+  kKDecode,
   kKernelCount
 };
 
@@ -164,6 +165,22 @@ size_t loss_scratch_bytes();
 // Machine probes (measurement only): a dense bf16 matrix-core loop of
 // blocks x 4 waves x 4 chains x iters products, and a device copy of `bytes`
 // (a multiple of 16).
+// Single-token decode over a KV cache (D.N = cache capacity, D.nb its blocks).
+constexpr int kDecodeChunk = 8;          // blocks per part of the full stream
+struct DecodeArgs {
+  const void* q;             // [B, Hq, d]
+  const void *k, *v;         // caches [B, Hkv, N, d]
+  const float* mu;           // block-mean cache [B, Hkv, nb, d] (sparse)
+  const int32_t* pos;        // [B] position of the new token (keys 0..pos)
+  int32_t* sel;              // [B, Hq, K] selection (sparse), null for the full stream
+  float *part_o, *part_ml;   // workspace: parts' outputs [B*Hq][P][d], (max, sum) [B*Hq][P][2]
+  void* h;                   // [B, Hq, d]
+  float* lse;                // [B, Hq] or null
+};
+int decode_parts(const Dims& D, bool sparse);
+void launch_decode(const Dims& D, const DecodeArgs& a, hipStream_t s);
+void launch_cache_means(const Dims& D, const void* k, float* mu, int j0, int j1, hipStream_t s);
+
 // Per-head means over the N rows of two per-row arrays [B*Hq][N] -> out [B*Hq][2].
 void launch_head_means(const float* a, const float* b, int64_t n_heads, int N, float* out, hipStream_t s);
 void launch_probe_mfma(float* sink, int blocks, int iters, hipStream_t s);

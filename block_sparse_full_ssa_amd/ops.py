@@ -177,3 +177,58 @@ def ssa_probe_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("dst is smaller than src")
     _lib.check(_lib.lib().ssa_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(src.device)), "ssa_probe_copy")
+
+
+def _cache_shape(q: torch.Tensor, k_cache: torch.Tensor, block: int, top_k: int,
+                 scale: Optional[float]) -> _lib.ShapeT:
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, d] and k_cache [B, Hkv, L, d]")
+    B, Hq, d = q.shape
+    Hkv, L = k_cache.shape[1], k_cache.shape[2]
+    if k_cache.shape[0] != B or k_cache.shape[3] != d or Hkv < 1 or Hq % Hkv != 0:
+        raise ValueError(f"k_cache shape {tuple(k_cache.shape)} does not match q {tuple(q.shape)}")
+    if q.dtype not in _DT or k_cache.dtype != q.dtype:
+        raise ValueError("q and the caches must both be float32 or bfloat16")
+    return _lib.ShapeT(B, Hq, Hq // Hkv, L, d, int(block), int(top_k),
+                       0.0 if scale is None else float(scale), _DT[q.dtype])
+
+
+def ssa_cache_block_means(k_cache: torch.Tensor, mu_cache: torch.Tensor, block: int, block_begin: int,
+                          block_end: int) -> None:
+    """mu_cache[:, :, j] = mean of k_cache's keys of block j, for block_begin <= j < block_end.
+
+    k_cache [B, Hkv, L, d]; mu_cache [B, Hkv, L / block, d] float32 (both CUDA)."""
+    dev = _dev_check(k_cache, mu_cache)
+    B, Hkv, L, d = k_cache.shape
+    if mu_cache.dtype != torch.float32 or tuple(mu_cache.shape) != (B, Hkv, L // block, d):
+        raise ValueError("mu_cache must be float32 [B, Hkv, L / block, d]")
+    shape = _lib.ShapeT(B, Hkv, 1, L, d, int(block), 1, 0.0, _DT[k_cache.dtype])
+    _lib.check(_lib.lib().ssa_cache_block_means(ctypes.byref(shape), _ptr(k_cache), _ptr(mu_cache),
+                                                int(block_begin), int(block_end), _stream(dev)),
+               "ssa_cache_block_means")
+
+
+def ssa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, mu_cache: Optional[torch.Tensor],
+               pos: torch.Tensor, block: int, top_k: int, mode: int = SPARSE_ONLY,
+               scale: Optional[float] = None) -> Dict[str, torch.Tensor]:
+    """One decode step: q [B, Hq, d] of the tokens at positions pos [B] (int32,
+    CUDA) over the caches.  Returns h [B, Hq, d], lse [B, Hq] and, for
+    SPARSE_ONLY, the selection sel [B, Hq, top_k]."""
+    dev = _dev_check(q, k_cache, v_cache, mu_cache, pos)
+    if pos.dtype != torch.int32 or pos.numel() != q.shape[0]:
+        raise ValueError("pos must be int32 [B]")
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must match k_cache")
+    shape = _cache_shape(q, k_cache, block, top_k, scale)
+    B, Hq, d = q.shape
+    out = {"h": torch.empty_like(q), "lse": torch.empty(B, Hq, dtype=torch.float32, device=dev)}
+    if mode == SPARSE_ONLY:
+        out["sel"] = torch.empty(B, Hq, int(top_k), dtype=torch.int32, device=dev)
+    ws, wp, wn = _workspace(shape, mode, _lib.OP_DECODE, dev)
+    st = _lib.lib().ssa_decode(ctypes.byref(shape), int(mode), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                               _ptr(mu_cache), _ptr(pos), _ptr(out["h"]), _ptr(out["lse"]), _ptr(out.get("sel")),
+                               ctypes.c_void_p(wp), wn, _stream(dev))
+    _lib.check(st, "ssa_decode")
+    if ws is not None:
+        out["_ws"] = ws
+    return out

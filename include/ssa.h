@@ -79,7 +79,7 @@ typedef enum {
   SSA_SPARSE_ONLY = 3         /* block-sparse attention alone        */
 } ssa_mode_t;
 
-typedef enum { SSA_OP_SELECT = 0, SSA_OP_FWD = 1, SSA_OP_BWD = 2 } ssa_op_t;
+typedef enum { SSA_OP_SELECT = 0, SSA_OP_FWD = 1, SSA_OP_BWD = 2, SSA_OP_DECODE = 3 } ssa_op_t;
 
 typedef struct {
   int32_t batch;          /* B >= 1                                  */
@@ -199,6 +199,46 @@ ssa_status_t ssa_timing_enable(int32_t enabled);
 ssa_status_t ssa_timing_query(const char* kernel, double* total_ms, int64_t* launches);
 int32_t ssa_kernel_count(void);
 const char* ssa_kernel_name(int32_t i);
+
+/*
+ * Inference over a KV cache (Sintesi Tecnica, section 4, 'Efficienza': at
+ * inference SSA performs MoBA's operations, i.e. the sparse stream alone).
+ * The shape describes the cache: seqlen = its capacity L in tokens (a
+ * multiple of block), so the caches are
+ *   k_cache, v_cache [B, Hkv, L, d] (dtype), mu_cache [B, Hkv, L/block, d] fp32,
+ * all device memory owned by the caller.  A prompt is processed as a layer
+ * (ssa_select_blocks + ssa_attn_fwd over its N <= L tokens, with its keys
+ * and values copied into the caches by the caller).
+ *
+ * ssa_cache_block_means: mu_cache[b, c, j] = mean of k_cache[b, c, i] over the
+ *   keys i of block j, for blocks block_begin <= j < block_end (the same
+ *   means the selection scores against).  Call it for the complete blocks
+ *   after a prompt, and for block j once its last key (position
+ *   (j+1) * block - 1) is in the cache.  SSA_ERR_SHAPE unless
+ *   0 <= block_begin <= block_end <= L / block.
+ *
+ * ssa_decode: one new token per sequence.  q [B, Hq, d] (dtype) is the token
+ *   of sequence b at position pos[b] (device int32 [B]; positions outside
+ *   [0, L) are clamped), whose key and value are already at that position of
+ *   the caches; it attends causally to keys 0 .. pos[b].
+ *     SSA_FULL_ONLY: every key 0 .. pos[b].
+ *     SSA_SPARSE_ONLY: its own block (keys up to pos[b]) and the top_k - 1
+ *       earlier blocks with the largest q . mu (fp32 scores against
+ *       mu_cache, which must hold every complete earlier block), the lower
+ *       index winning a tie -- the rule of ssa_select_blocks.  The selection
+ *       is written to sel [B, Hq, top_k] (ascending, -1 padded; required).
+ *   Writes h [B, Hq, d] (dtype) and, if lse is not NULL, lse [B, Hq] fp32
+ *   (natural log).  The workspace is ssa_workspace_size(shape, mode,
+ *   SSA_OP_DECODE) bytes (per-part partial outputs).  Other modes return
+ *   SSA_ERR_UNSUPPORTED; other errors as for the layer entry points.
+ *   The work is the selected keys (sparse) or all pos[b] + 1 keys (full):
+ *   each key and value row is read once per query head.
+ */
+ssa_status_t ssa_cache_block_means(const ssa_shape_t* shape, const void* k_cache, float* mu_cache,
+                                   int32_t block_begin, int32_t block_end, void* stream);
+ssa_status_t ssa_decode(const ssa_shape_t* shape, int32_t mode, const void* q, const void* k_cache,
+                        const void* v_cache, const float* mu_cache, const int32_t* pos, void* h,
+                        float* lse, int32_t* sel, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Machine probes for measurement harnesses: the two ceilings that the

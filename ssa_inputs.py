@@ -54,7 +54,7 @@ def _wl(**kw) -> Workload:
     return Workload(**kw)
 
 
-# The five layer shapes the measurements are quoted on.
+# The layer shapes the measurements are quoted on, and the decode cache (128K).
 WORKLOADS: Dict[str, Workload] = {
     "tiny_mha_n256_fp32": _wl(
         name="tiny_mha_n256_fp32", batch=1, hq=2, hkv=2, seqlen=256, head_dim=64,
@@ -67,6 +67,9 @@ WORKLOADS: Dict[str, Workload] = {
         block=64, top_k=16, dtype=torch.bfloat16, top_k_sweep=(4, 8, 16, 32)),
     "long_n64k_sinks": _wl(
         name="long_n64k_sinks", batch=1, hq=16, hkv=4, seqlen=65536, head_dim=128,
+        block=64, top_k=32, dtype=torch.bfloat16, n_sinks=4),
+    "decode_b4_n128k_sinks": _wl(
+        name="decode_b4_n128k_sinks", batch=4, hq=16, hkv=4, seqlen=131072, head_dim=128,
         block=64, top_k=32, dtype=torch.bfloat16, n_sinks=4),
     "multilayer_b4_n8k_l4": _wl(
         name="multilayer_b4_n8k_l4", batch=4, hq=32, hkv=8, seqlen=8192, head_dim=128,
@@ -102,6 +105,20 @@ def draw_qkv(wl: Workload, seed: int, layer: int = 0):
     if wl.n_sinks:
         k = plant_sinks(k, gen, wl.n_sinks)
     return q, k, v, gen
+
+
+def draw_decode(wl: Workload, seed: int):
+    """A decode step's inputs: caches k, v [B,Hkv,N,d] (N = the cache's
+    capacity) and one query row per sequence and head, q [B,Hq,d], drawn in
+    the order k, v, q from stream seed + 3 (sinks planted as for a layer)."""
+    gen = generator(seed + 3)
+    B, N, d = wl.batch, wl.seqlen, wl.head_dim
+    k = draw(gen, (B, wl.hkv, N, d), wl.dtype, wl.prescale)
+    v = draw(gen, (B, wl.hkv, N, d), wl.dtype, wl.prescale)
+    q = draw(gen, (B, wl.hq, d), wl.dtype, wl.prescale)
+    if wl.n_sinks:
+        k = plant_sinks(k, gen, wl.n_sinks)
+    return q, k, v
 
 
 def plant_sinks(k: torch.Tensor, gen: torch.Generator, n_sinks: int) -> torch.Tensor:

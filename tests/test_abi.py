@@ -135,6 +135,35 @@ def test_fwd_stats_argument_checks(L):
     assert st == _lib.SSA_ERR_SHAPE
 
 
+def test_decode_argument_checks(L):
+    from block_sparse_full_ssa_amd import _lib
+    FAKE = ctypes.c_void_p(1 << 40)
+    s = _shape(seqlen=4096)
+    assert L.ssa_workspace_size(ctypes.byref(s), _lib.SPARSE_ONLY, _lib.OP_DECODE) > 0
+    assert L.ssa_workspace_size(ctypes.byref(s), _lib.FULL_ONLY, _lib.OP_DECODE) > 0
+    assert L.ssa_workspace_size(ctypes.byref(s), _lib.DUAL_ACTIVE_FULL, _lib.OP_DECODE) == 0
+    ws = 1 << 30
+    st = L.ssa_decode(ctypes.byref(s), _lib.DUAL_ACTIVE_FULL, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                      FAKE, ws, None)
+    assert st == _lib.SSA_ERR_UNSUPPORTED
+    st = L.ssa_decode(ctypes.byref(s), _lib.SPARSE_ONLY, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, FAKE,
+                      FAKE, ws, None)
+    assert st == _lib.SSA_ERR_NULL                # sparse needs the block means
+    st = L.ssa_decode(ctypes.byref(s), _lib.SPARSE_ONLY, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None,
+                      FAKE, ws, None)
+    assert st == _lib.SSA_ERR_NULL                # ... and sel
+    st = L.ssa_decode(ctypes.byref(s), _lib.FULL_ONLY, FAKE, FAKE, FAKE, None, None, FAKE, None, None,
+                      FAKE, ws, None)
+    assert st == _lib.SSA_ERR_NULL                # pos
+    st = L.ssa_decode(ctypes.byref(s), _lib.FULL_ONLY, FAKE, FAKE, FAKE, None, FAKE, FAKE, None, None,
+                      FAKE, 16, None)
+    assert st == _lib.SSA_ERR_WORKSPACE
+    assert L.ssa_cache_block_means(ctypes.byref(s), FAKE, FAKE, 3, 2, None) == _lib.SSA_ERR_SHAPE
+    assert L.ssa_cache_block_means(ctypes.byref(s), FAKE, FAKE, 0, 4096 // 64 + 1, None) == _lib.SSA_ERR_SHAPE
+    assert L.ssa_cache_block_means(ctypes.byref(s), None, FAKE, 0, 1, None) == _lib.SSA_ERR_NULL
+    assert L.ssa_cache_block_means(ctypes.byref(s), FAKE, FAKE, 2, 2, None) == _lib.SSA_OK   # nothing to do
+
+
 def test_probe_argument_checks(L):
     from block_sparse_full_ssa_amd import _lib
     FAKE = ctypes.c_void_p(1 << 40)
