@@ -180,11 +180,14 @@ static BwdWs carve_bwd(const Dims& D, int mode, Carver& c) {
 }
 
 struct DecodeWs {
+  uint32_t* codes;
   float *part_o, *part_ml;
 };
 static DecodeWs carve_decode(const Dims& D, int mode, Carver& c) {
-  const size_t n = static_cast<size_t>(D.B) * D.Hq * decode_parts(D, mode == kSparseOnly);
+  const size_t rows = static_cast<size_t>(D.B) * D.Hq;
+  const size_t n = rows * decode_parts(D, mode == kSparseOnly);
   DecodeWs w{};
+  if (mode == kSparseOnly) w.codes = c.take<uint32_t>(rows * D.nb * sizeof(uint32_t));
   w.part_o = c.take<float>(n * D.d * sizeof(float));
   w.part_ml = c.take<float>(n * 2 * sizeof(float));
   return w;
@@ -440,7 +443,8 @@ ssa_status_t ssa_decode(const ssa_shape_t* shape, int32_t mode, const void* q, c
   if ((st = check_ws(D, mode, SSA_OP_DECODE, ws, ws_bytes)) != SSA_OK) return st;
   Carver c{static_cast<char*>(ws)};
   DecodeWs w = carve_decode(D, mode, c);
-  DecodeArgs a{q, k_cache, v_cache, mu_cache, pos, mode == kSparseOnly ? sel : nullptr, w.part_o, w.part_ml, h, lse};
+  DecodeArgs a{q, k_cache, v_cache, mu_cache, pos, mode == kSparseOnly ? sel : nullptr, w.codes, w.part_o, w.part_ml,
+               h, lse};
   launch_decode(D, a, static_cast<hipStream_t>(stream));
   return launch_status();
 }

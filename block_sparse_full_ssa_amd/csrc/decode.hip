@@ -8,17 +8,22 @@
 // tie -- the same rule as the training layer, scored against block means
 // kept in a cache next to K and V.
 //
-// Three kernels:
+// Kernels:
 //   k_cache_means    mean of the keys of cached blocks [j0, j1) -> fp32 cache
-//   k_decode_select  one workgroup per (sequence, query head): scores of the
-//                    complete earlier blocks, a 32-step threshold search on
-//                    order-preserving codes, winners compacted in block order
-//   k_decode_attend  one wave per part (a selected block, or a chunk of
-//                    consecutive blocks for the full stream): lane = key for
-//                    the logits, lane = two columns of d for P V; a part's
+//   k_decode_scores  one thread per (query head, complete earlier block): the
+//                    order-preserving code of q . mu_j (fp32), spread over
+//                    many workgroups so that the block means stream in at
+//                    full width
+//   k_decode_topk    per (sequence, query head): a 32-step threshold search
+//                    on the codes, winners compacted in block order
+//   k_decode_attend  one wave per part: a selected block of one query head
+//                    (sparse), or a chunk of consecutive blocks for all the
+//                    query heads of a KV head (full: each key and value row
+//                    is read once for the group); lane = key for the logits,
+//                    lane = (key group, 8 columns) for P V; the part's
 //                    (o, max, sum) go to the workspace
-//   k_decode_merge   per (sequence, query head): the parts combined by their
-//                    maxima and sums -> h (input dtype) and lse (natural log)
+//   k_decode_merge   per (sequence, query head): the parts combined in one
+//                    pass by their maxima and sums -> h and lse
 // Decode is bound by HBM (each selected key and value is read once per
 // query head); none of it is a dense contraction worth the matrix cores.
 
@@ -59,6 +64,113 @@ __device__ __forceinline__ int block_scan_flag(bool flag, int* wsum, int* total)
   return before;
 }
 
+// Scores of the complete earlier blocks, one thread per (query head, block):
+// code = order-preserving bits of q . mu_j (fp32), for j < own block.
+template <typename T>
+__global__ void __launch_bounds__(256) k_decode_scores(const T* __restrict__ q, const float* __restrict__ mu,
+                                                       const int32_t* __restrict__ pos, uint32_t* __restrict__ codes,
+                                                       int Hq, int G, int d, int block, int nbmax) {
+  __shared__ float4 qs[32];
+  const int64_t bh = blockIdx.x;
+  const int b = static_cast<int>(bh / Hq), h = static_cast<int>(bh % Hq);
+  const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
+  const int t = min(max(pos[b], 0), nbmax * block - 1);
+  const int it = t / block;
+  const int j = static_cast<int>(blockIdx.y) * 256 + threadIdx.x;
+  if (static_cast<int>(blockIdx.y) * 256 >= it) return;         // uniform: no candidate here
+  if (threadIdx.x < d / 4) {
+    const int e = 4 * threadIdx.x;
+    qs[threadIdx.x] = make_float4(to_f32(q[bh * d + e]), to_f32(q[bh * d + e + 1]), to_f32(q[bh * d + e + 2]),
+                                  to_f32(q[bh * d + e + 3]));
+  }
+  __syncthreads();
+  if (j >= it) return;
+  const float4* m4 = reinterpret_cast<const float4*>(mu + (bc * nbmax + j) * d);
+  float s = 0.f;
+#pragma unroll 8
+  for (int e = 0; e < d / 4; ++e) {
+    const float4 m = m4[e], x = qs[e];
+    s = fmaf(x.x, m.x, s);
+    s = fmaf(x.y, m.y, s);
+    s = fmaf(x.z, m.z, s);
+    s = fmaf(x.w, m.w, s);
+  }
+  codes[bh * nbmax + j] = ordered_bits(s);
+}
+
+// Per (sequence, query head): the own block and the top_k - 1 largest codes,
+// ties to the lower block, written ascending with -1 padding.  Thread tid
+// holds codes tid + 256 r (r < 16: up to 4096 blocks) in registers; counts
+// are ballots summed per wave and over the 4 waves through LDS.
+__global__ void __launch_bounds__(256) k_decode_topk(const uint32_t* __restrict__ codes_g,
+                                                     const int32_t* __restrict__ pos, int32_t* __restrict__ sel,
+                                                     int Hq, int block, int nbmax, int K) {
+  constexpr int R = 16;
+  __shared__ int wsum[4];
+  __shared__ int wcnt[2][4];
+  const int64_t bh = blockIdx.x;
+  const int b = static_cast<int>(bh / Hq);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int t = min(max(pos[b], 0), nbmax * block - 1);   // positions outside the cache are clamped
+  const int it = t / block;                         // own block
+  const int keep = min(K - 1, it);                  // earlier blocks to keep
+  int32_t* out = sel + bh * K;
+  if (keep == it) {                                 // every earlier block is kept
+    for (int p = tid; p < K; p += 256) out[p] = p <= it ? p : -1;
+    return;
+  }
+  if (keep == 0) {                                  // top_k 1: the own block alone
+    for (int p = tid; p < K; p += 256) out[p] = p == 0 ? it : -1;
+    return;
+  }
+  const int nr = (it + 255) / 256;                  // uniform
+  uint32_t c[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int j = tid + 256 * r;
+    c[r] = (r < nr && j < it) ? codes_g[bh * nbmax + j] : 0u;
+  }
+  // number of the candidates (j < it) whose code is >= v: ballots per wave,
+  // then the 4 wave counts through LDS (two buffers: one barrier per count)
+  int buf = 0;
+  auto count_ge = [&](uint32_t v) {
+    int n = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < nr) n += __popcll(__ballot(tid + 256 * r < it && c[r] >= v));
+    if (lane == 0) wcnt[buf][w] = n;
+    __syncthreads();
+    const int total = wcnt[buf][0] + wcnt[buf][1] + wcnt[buf][2] + wcnt[buf][3];
+    buf ^= 1;
+    return total;
+  };
+  // the keep-th largest code: the largest v with #{codes >= v} >= keep
+  uint32_t thr = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = thr | (1u << bit);
+    if (count_ge(cand) >= keep) thr = cand;
+  }
+  const int n_gt = thr == 0xffffffffu ? 0 : count_ge(thr + 1);
+  const int need_eq = keep - n_gt;
+  int written = 0, eq_seen = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r >= nr) break;                             // uniform
+    const int j = tid + 256 * r;
+    const bool eq = j < it && c[r] == thr;
+    int eq_total;
+    const int eq_before = block_scan_flag(eq, wsum, &eq_total);
+    const bool win = j < it && (c[r] > thr || (eq && eq_seen + eq_before < need_eq));
+    int win_total;
+    const int win_before = block_scan_flag(win, wsum, &win_total);
+    if (win) out[written + win_before] = j;
+    written += win_total;
+    eq_seen += eq_total;
+  }
+  if (tid == 0) out[keep] = it;
+  for (int p = keep + 1 + tid; p < K; p += 256) out[p] = -1;
+}
+
 // Eight consecutive elements of a row as fp32 (16-byte loads for bf16).
 __device__ __forceinline__ void load8(const bf16_t* p, float* x) {
   const uint4 u = *reinterpret_cast<const uint4*>(p);
@@ -76,172 +188,172 @@ __device__ __forceinline__ void load8(const float* p, float* x) {
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
-template <typename T>
-__global__ void __launch_bounds__(256) k_decode_select(const T* __restrict__ q, const float* __restrict__ mu,
-                                                       const int32_t* __restrict__ pos, int32_t* __restrict__ sel,
-                                                       int Hq, int G, int d, int block, int nbmax, int K) {
-  __shared__ float qs[128];
-  __shared__ uint32_t codes[4096];
-  __shared__ int wsum[4];
-  __shared__ int cnt_s;
-  const int64_t bh = blockIdx.x;
-  const int b = static_cast<int>(bh / Hq), h = static_cast<int>(bh % Hq);
-  const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
-  const int tid = threadIdx.x;
-  const int t = min(max(pos[b], 0), nbmax * block - 1);   // positions outside the cache are clamped
-  const int it = t / block;                         // own block
-  const int keep = min(K - 1, it);                  // earlier blocks to keep
-  int32_t* out = sel + bh * K;
-  if (keep == it) {                                 // every earlier block is kept
-    for (int p = tid; p < K; p += 256) out[p] = p <= it ? p : -1;
-    return;
-  }
-  if (keep == 0) {                                  // top_k 1: the own block alone
-    for (int p = tid; p < K; p += 256) out[p] = p == 0 ? it : -1;
-    return;
-  }
-  if (tid < d) qs[tid] = to_f32(q[bh * d + tid]);
-  __syncthreads();
-  const float* muc = mu + bc * nbmax * d;
-  for (int j = tid; j < it; j += 256) {
-    const float4* m4 = reinterpret_cast<const float4*>(muc + static_cast<int64_t>(j) * d);
-    float s = 0.f;
-    for (int e = 0; e < d / 4; ++e) {
-      const float4 m = m4[e];
-      s = fmaf(qs[4 * e], m.x, s);
-      s = fmaf(qs[4 * e + 1], m.y, s);
-      s = fmaf(qs[4 * e + 2], m.z, s);
-      s = fmaf(qs[4 * e + 3], m.w, s);
-    }
-    codes[j] = ordered_bits(s);
-  }
-  __syncthreads();
-  // the keep-th largest code: the largest c with #{codes >= c} >= keep
-  uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = thr | (1u << bit);
-    int n = 0;
-    for (int j = tid; j < it; j += 256) n += codes[j] >= cand ? 1 : 0;
-    n = static_cast<int>(wave_sum(static_cast<float>(n)));
-    if (tid == 0) cnt_s = 0;
-    __syncthreads();
-    if ((tid & 63) == 0) atomicAdd(&cnt_s, n);
-    __syncthreads();
-    if (cnt_s >= keep) thr = cand;
-    __syncthreads();
-  }
-  // winners: codes above the threshold, then the lowest-index codes equal to it
-  int n_gt = 0;
-  {
-    int n = 0;
-    for (int j = tid; j < it; j += 256) n += codes[j] > thr ? 1 : 0;
-    n = static_cast<int>(wave_sum(static_cast<float>(n)));
-    if (tid == 0) cnt_s = 0;
-    __syncthreads();
-    if ((tid & 63) == 0) atomicAdd(&cnt_s, n);
-    __syncthreads();
-    n_gt = cnt_s;
-  }
-  const int need_eq = keep - n_gt;
-  int written = 0, eq_seen = 0;
-  for (int j0 = 0; j0 < it; j0 += 256) {
-    const int j = j0 + tid;
-    const uint32_t cj = j < it ? codes[j] : 0u;
-    const bool eq = j < it && cj == thr;
-    int eq_total;
-    const int eq_before = block_scan_flag(eq, wsum, &eq_total);
-    const bool win = j < it && (cj > thr || (eq && eq_seen + eq_before < need_eq));
-    int win_total;
-    const int win_before = block_scan_flag(win, wsum, &win_total);
-    if (win) out[written + win_before] = j;
-    written += win_total;
-    eq_seen += eq_total;
-  }
-  if (tid == 0) out[keep] = it;
-  for (int p = keep + 1 + tid; p < K; p += 256) out[p] = -1;
-}
-
-// Part p of row bh covers blocks [first, last] (sparse: one selected block;
-// full: a chunk of consecutive blocks).  One wave per part, 4 per workgroup.
-template <typename T, int E>
+// One wave per part: NH query heads of one KV head over the keys of blocks
+// [first, last] up to position t.  Logits: lane = key (its key row read once
+// for all NH heads).  P V: lane = (key group, 8 columns), each V row read
+// once for all NH heads; the key groups are combined at the end of the part.
+// Sparse: NH = 1, a part is one selected block of one query head.  Full:
+// NH = the group's heads, a part is a chunk of consecutive blocks.
+template <typename T, int D, int NH>
 __global__ void __launch_bounds__(256) k_decode_attend(const T* __restrict__ q, const T* __restrict__ kc,
                                                        const T* __restrict__ vc, const int32_t* __restrict__ pos,
                                                        const int32_t* __restrict__ sel, float* __restrict__ part_o,
                                                        float* __restrict__ part_ml, int Hq, int G, int L, int block,
                                                        int K, int chunk, int n_parts, float scale_log2) {
-  constexpr int d = 64 * E;
-  __shared__ float qs[4][d];
-  __shared__ float ps[4][64];
+  constexpr int LPR = D / 8;          // lanes per row (8 columns each)
+  constexpr int KG = 64 / LPR;        // key groups in P V
+  __shared__ float4 qs[4][NH][D / 4];
+  __shared__ float ps[4][NH][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t bh = blockIdx.x;
+  const int64_t unit = blockIdx.x;    // NH = 1: a query row (b, h); NH = G: a KV head (b, c)
   const int p = static_cast<int>(blockIdx.y) * 4 + w;
-  const int b = static_cast<int>(bh / Hq), h = static_cast<int>(bh % Hq);
-  const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
-  const int t = min(max(pos[b], 0), L - 1);        // positions outside the cache are clamped
   if (p >= n_parts) return;
-  int first, last;                                   // blocks of this part
+  int b, h0;
+  int64_t bc;
+  if (NH == 1) {
+    b = static_cast<int>(unit / Hq);
+    h0 = static_cast<int>(unit % Hq);
+    bc = static_cast<int64_t>(b) * (Hq / G) + h0 / G;
+  } else {
+    const int Hkv = Hq / G;
+    b = static_cast<int>(unit / Hkv);
+    bc = unit;
+    h0 = static_cast<int>(unit % Hkv) * G;
+  }
+  const int t = min(max(pos[b], 0), L - 1);        // positions outside the cache are clamped
+  int first, last;
   if (sel) {
-    first = last = sel[bh * K + p];
+    first = last = sel[unit * K + p];
   } else {
     first = p * chunk;
     last = min(first + chunk - 1, t / block);
   }
-  float* po = part_o + (bh * n_parts + p) * d;
-  float* pml = part_ml + (bh * n_parts + p) * 2;
+  const int64_t row0 = static_cast<int64_t>(b) * Hq + h0;   // output row of head h0
   if (first < 0 || first > t / block) {             // no keys: an empty part
-    for (int e = 0; e < E; ++e) po[lane * E + e] = 0.f;
-    if (lane == 0) {
-      pml[0] = -INFINITY;
-      pml[1] = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      float* po = part_o + ((row0 + hh) * n_parts + p) * D;
+      for (int e = lane; e < D; e += 64) po[e] = 0.f;
+      if (lane == 0) {
+        part_ml[((row0 + hh) * n_parts + p) * 2] = -INFINITY;
+        part_ml[((row0 + hh) * n_parts + p) * 2 + 1] = 0.f;
+      }
     }
     return;
   }
-  for (int e = 0; e < E; ++e) qs[w][lane * E + e] = to_f32(q[bh * d + lane * E + e]);
-  const T* kb = kc + bc * L * d;
-  const T* vb = vc + bc * L * d;
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh)
+    if (lane < D / 4) {
+      const T* qr = q + (row0 + hh) * D + 4 * lane;
+      qs[w][hh][lane] = make_float4(to_f32(qr[0]), to_f32(qr[1]), to_f32(qr[2]), to_f32(qr[3]));
+    }
+  __builtin_amdgcn_wave_barrier();
+  const T* kb = kc + bc * L * D;
+  const T* vb = vc + bc * L * D;
   const int k_end = min(t + 1, (last + 1) * block);  // keys [first * block, k_end)
-  float m = -INFINITY, l = 0.f, o[E];
-  for (int e = 0; e < E; ++e) o[e] = 0.f;
+  const int kg = lane / LPR, cc = (lane % LPR) * 8;
+  float m[NH], l[NH], o[NH][8];
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh) {
+    m[hh] = -INFINITY;
+    l[hh] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+  }
   for (int k0 = first * block; k0 < k_end; k0 += 64) {
     const int key = k0 + lane;
-    float s = -INFINITY;
+    float s[NH];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) s[hh] = -INFINITY;
     if (key < k_end) {
-      const T* kr = kb + static_cast<int64_t>(key) * d;
-      float acc = 0.f;
-#pragma unroll 4
-      for (int e0 = 0; e0 < d; e0 += 8) {
+      const T* kr = kb + static_cast<int64_t>(key) * D;
+      float acc[NH];
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) acc[hh] = 0.f;
+#pragma unroll
+      for (int e0 = 0; e0 < D; e0 += 8) {
         float x[8];
         load8(kr + e0, x);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc = fmaf(qs[w][e0 + i], x[i], acc);
+        for (int hh = 0; hh < NH; ++hh) {
+          const float4 a = qs[w][hh][e0 / 4], c = qs[w][hh][e0 / 4 + 1];
+          acc[hh] = fmaf(a.x, x[0], acc[hh]);
+          acc[hh] = fmaf(a.y, x[1], acc[hh]);
+          acc[hh] = fmaf(a.z, x[2], acc[hh]);
+          acc[hh] = fmaf(a.w, x[3], acc[hh]);
+          acc[hh] = fmaf(c.x, x[4], acc[hh]);
+          acc[hh] = fmaf(c.y, x[5], acc[hh]);
+          acc[hh] = fmaf(c.z, x[6], acc[hh]);
+          acc[hh] = fmaf(c.w, x[7], acc[hh]);
+        }
       }
-      s = acc * scale_log2;
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) s[hh] = acc[hh] * scale_log2;
     }
-    const float mx = wave_max(s);                    // finite: key k0 <= t is always present
-    const float mn = fmaxf(m, mx);
-    const float al = exp2f(m - mn);
-    const float pv = key < k_end ? exp2f(s - mn) : 0.f;
-    l = l * al + wave_sum(pv);
-    for (int e = 0; e < E; ++e) o[e] *= al;
-    m = mn;
-    ps[w][lane] = pv;
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      const float mx = wave_max(s[hh]);              // finite: key k0 <= t is present
+      const float mn = fmaxf(m[hh], mx);
+      const float al = exp2f(m[hh] - mn);
+      const float pv = key < k_end ? exp2f(s[hh] - mn) : 0.f;
+      l[hh] = l[hh] * al + wave_sum(pv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[hh][e] *= al;
+      m[hh] = mn;
+      ps[w][hh][lane] = pv;
+    }
     __builtin_amdgcn_wave_barrier();
     const int nk = min(64, k_end - k0);
-#pragma unroll 8
-    for (int i = 0; i < nk; ++i) {
-      const float pi = ps[w][i];
-      const T* vr = vb + static_cast<int64_t>(k0 + i) * d + lane * E;
-      for (int e = 0; e < E; ++e) o[e] = fmaf(pi, to_f32(vr[e]), o[e]);
+    if (nk == 64) {                                  // a whole group: every V load in flight at once
+      float x[64 / KG][8];
+#pragma unroll
+      for (int j = 0; j < 64 / KG; ++j) load8(vb + static_cast<int64_t>(k0 + kg + KG * j) * D + cc, x[j]);
+#pragma unroll
+      for (int j = 0; j < 64 / KG; ++j)
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+          const float pi = ps[w][hh][kg + KG * j];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(pi, x[j][e], o[hh][e]);
+        }
+    } else {
+      for (int i = kg; i < nk; i += KG) {
+        float x[8];
+        load8(vb + static_cast<int64_t>(k0 + i) * D + cc, x);
+#pragma unroll
+        for (int hh = 0; hh < NH; ++hh) {
+          const float pi = ps[w][hh][i];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(pi, x[e], o[hh][e]);
+        }
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }
-  for (int e = 0; e < E; ++e) po[lane * E + e] = o[e];
+  // combine the key groups: lanes with the same columns are LPR apart
+#pragma unroll
+  for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      for (int off = LPR; off < 64; off <<= 1) o[hh][e] += __shfl_xor(o[hh][e], off, 64);
+  if (kg == 0) {
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      float4* po = reinterpret_cast<float4*>(part_o + ((row0 + hh) * n_parts + p) * D + cc);
+      po[0] = make_float4(o[hh][0], o[hh][1], o[hh][2], o[hh][3]);
+      po[1] = make_float4(o[hh][4], o[hh][5], o[hh][6], o[hh][7]);
+    }
+  }
   if (lane == 0) {
-    pml[0] = m;                                      // log2 units
-    pml[1] = l;
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh) {
+      part_ml[((row0 + hh) * n_parts + p) * 2] = m[hh];        // log2 units
+      part_ml[((row0 + hh) * n_parts + p) * 2 + 1] = l[hh];
+    }
   }
 }
 
+// Per (sequence, query head): the parts combined in one pass (running maximum).
 template <typename T>
 __global__ void __launch_bounds__(128) k_decode_merge(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, T* __restrict__ h,
@@ -249,15 +361,21 @@ __global__ void __launch_bounds__(128) k_decode_merge(const float* __restrict__ 
   const int64_t bh = blockIdx.x;
   const int col = threadIdx.x;
   const float* pml = part_ml + bh * n_parts * 2;
-  float M = -INFINITY;
-  for (int p = 0; p < n_parts; ++p) M = fmaxf(M, pml[2 * p]);
-  float L = 0.f, o = 0.f;
+  const float* po = part_o + bh * n_parts * d + (col < d ? col : 0);
+  float M = -INFINITY, L = 0.f, o = 0.f;
   for (int p = 0; p < n_parts; ++p) {
     const float mp = pml[2 * p];
-    if (mp == -INFINITY) continue;
-    const float f = exp2f(mp - M);
-    L = fmaf(pml[2 * p + 1], f, L);
-    if (col < d) o = fmaf(part_o[(bh * n_parts + p) * d + col], f, o);
+    if (mp == -INFINITY) continue;                  // an empty part
+    const float lp = pml[2 * p + 1], op = po[static_cast<int64_t>(p) * d];
+    if (mp > M) {
+      const float f = exp2f(M - mp);                 // 0 on the first part
+      L *= f;
+      o *= f;
+      M = mp;
+    }
+    const float g = exp2f(mp - M);
+    L = fmaf(lp, g, L);
+    o = fmaf(op, g, o);
   }
   if (col < d) h[bh * d + col] = from_f32<T>(o / L);
   if (col == 0 && lse) lse[bh] = (M + log2f(L)) * 0.69314718055994531f;
@@ -282,44 +400,55 @@ void launch_cache_means(const Dims& D, const void* k, float* mu, int j0, int j1,
   timing_end(kKDecode, s);
 }
 
+template <typename T, int D, int NH>
+static void attend(const Dims& Dm, const DecodeArgs& a, int units, int P, float sl2, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(units), static_cast<unsigned>((P + 3) / 4));
+  hipLaunchKernelGGL((k_decode_attend<T, D, NH>), grid, dim3(256), 0, s, static_cast<const T*>(a.q),
+                     static_cast<const T*>(a.k), static_cast<const T*>(a.v), a.pos, a.sel, a.part_o, a.part_ml,
+                     Dm.Hq, Dm.G, Dm.N, Dm.block, Dm.K, kDecodeChunk, P, sl2);
+}
+
+template <typename T, int D>
+static void attend_all(const Dims& Dm, const DecodeArgs& a, int P, float sl2, hipStream_t s) {
+  const int rows = Dm.B * Dm.Hq, kv = Dm.B * Dm.Hkv;
+  if (a.sel) {                      // sparse: every query head has its own blocks
+    attend<T, D, 1>(Dm, a, rows, P, sl2, s);
+    return;
+  }
+  switch (Dm.G) {                   // full: the group's heads share each key and value row read
+    case 2: attend<T, D, 2>(Dm, a, kv, P, sl2, s); break;
+    case 4: attend<T, D, 4>(Dm, a, kv, P, sl2, s); break;
+    case 8: attend<T, D, 8>(Dm, a, kv, P, sl2, s); break;
+    default: attend<T, D, 1>(Dm, a, rows, P, sl2, s); break;
+  }
+}
+
 void launch_decode(const Dims& D, const DecodeArgs& a, hipStream_t s) {
   const bool sparse = a.sel != nullptr;
   const int P = decode_parts(D, sparse);
-  const int64_t rows = static_cast<int64_t>(D.B) * D.Hq;
+  const unsigned rows = static_cast<unsigned>(D.B * D.Hq);
   const float sl2 = D.scale * kLog2eD;
   timing_begin(kKDecode, s);
   if (D.dtype == 1) {
-    const bf16_t* q = static_cast<const bf16_t*>(a.q);
-    if (sparse)
-      hipLaunchKernelGGL(k_decode_select<bf16_t>, dim3(static_cast<unsigned>(rows)), dim3(256), 0, s, q, a.mu,
-                         a.pos, a.sel, D.Hq, D.G, D.d, D.block, D.nb, D.K);
-    const dim3 grid(static_cast<unsigned>(rows), static_cast<unsigned>((P + 3) / 4));
-    if (D.d == 128)
-      hipLaunchKernelGGL((k_decode_attend<bf16_t, 2>), grid, dim3(256), 0, s, q,
-                         static_cast<const bf16_t*>(a.k), static_cast<const bf16_t*>(a.v), a.pos, a.sel, a.part_o,
-                         a.part_ml, D.Hq, D.G, D.N, D.block, D.K, kDecodeChunk, P, sl2);
-    else
-      hipLaunchKernelGGL((k_decode_attend<bf16_t, 1>), grid, dim3(256), 0, s, q,
-                         static_cast<const bf16_t*>(a.k), static_cast<const bf16_t*>(a.v), a.pos, a.sel, a.part_o,
-                         a.part_ml, D.Hq, D.G, D.N, D.block, D.K, kDecodeChunk, P, sl2);
-    hipLaunchKernelGGL(k_decode_merge<bf16_t>, dim3(static_cast<unsigned>(rows)), dim3(128), 0, s, a.part_o,
-                       a.part_ml, static_cast<bf16_t*>(a.h), a.lse, D.d, P);
+    if (sparse) {
+      hipLaunchKernelGGL(k_decode_scores<bf16_t>, dim3(rows, static_cast<unsigned>((D.nb + 255) / 256)), dim3(256), 0,
+                         s, static_cast<const bf16_t*>(a.q), a.mu, a.pos, a.codes, D.Hq, D.G, D.d, D.block, D.nb);
+      hipLaunchKernelGGL(k_decode_topk, dim3(rows), dim3(256), 0, s, a.codes, a.pos, a.sel, D.Hq, D.block, D.nb, D.K);
+    }
+    if (D.d == 128) attend_all<bf16_t, 128>(D, a, P, sl2, s);
+    else attend_all<bf16_t, 64>(D, a, P, sl2, s);
+    hipLaunchKernelGGL(k_decode_merge<bf16_t>, dim3(rows), dim3(128), 0, s, a.part_o, a.part_ml,
+                       static_cast<bf16_t*>(a.h), a.lse, D.d, P);
   } else {
-    const float* q = static_cast<const float*>(a.q);
-    if (sparse)
-      hipLaunchKernelGGL(k_decode_select<float>, dim3(static_cast<unsigned>(rows)), dim3(256), 0, s, q, a.mu,
-                         a.pos, a.sel, D.Hq, D.G, D.d, D.block, D.nb, D.K);
-    const dim3 grid(static_cast<unsigned>(rows), static_cast<unsigned>((P + 3) / 4));
-    if (D.d == 128)
-      hipLaunchKernelGGL((k_decode_attend<float, 2>), grid, dim3(256), 0, s, q, static_cast<const float*>(a.k),
-                         static_cast<const float*>(a.v), a.pos, a.sel, a.part_o, a.part_ml, D.Hq, D.G, D.N,
-                         D.block, D.K, kDecodeChunk, P, sl2);
-    else
-      hipLaunchKernelGGL((k_decode_attend<float, 1>), grid, dim3(256), 0, s, q, static_cast<const float*>(a.k),
-                         static_cast<const float*>(a.v), a.pos, a.sel, a.part_o, a.part_ml, D.Hq, D.G, D.N,
-                         D.block, D.K, kDecodeChunk, P, sl2);
-    hipLaunchKernelGGL(k_decode_merge<float>, dim3(static_cast<unsigned>(rows)), dim3(128), 0, s, a.part_o,
-                       a.part_ml, static_cast<float*>(a.h), a.lse, D.d, P);
+    if (sparse) {
+      hipLaunchKernelGGL(k_decode_scores<float>, dim3(rows, static_cast<unsigned>((D.nb + 255) / 256)), dim3(256), 0,
+                         s, static_cast<const float*>(a.q), a.mu, a.pos, a.codes, D.Hq, D.G, D.d, D.block, D.nb);
+      hipLaunchKernelGGL(k_decode_topk, dim3(rows), dim3(256), 0, s, a.codes, a.pos, a.sel, D.Hq, D.block, D.nb, D.K);
+    }
+    if (D.d == 128) attend_all<float, 128>(D, a, P, sl2, s);
+    else attend_all<float, 64>(D, a, P, sl2, s);
+    hipLaunchKernelGGL(k_decode_merge<float>, dim3(rows), dim3(128), 0, s, a.part_o, a.part_ml,
+                       static_cast<float*>(a.h), a.lse, D.d, P);
   }
   timing_end(kKDecode, s);
 }

@@ -166,13 +166,14 @@ size_t loss_scratch_bytes();
 // blocks x 4 waves x 4 chains x iters products, and a device copy of `bytes`
 // (a multiple of 16).
 // Single-token decode over a KV cache (D.N = cache capacity, D.nb its blocks).
-constexpr int kDecodeChunk = 8;          // blocks per part of the full stream
+constexpr int kDecodeChunk = 16;         // blocks per part of the full stream
 struct DecodeArgs {
   const void* q;             // [B, Hq, d]
   const void *k, *v;         // caches [B, Hkv, N, d]
   const float* mu;           // block-mean cache [B, Hkv, nb, d] (sparse)
   const int32_t* pos;        // [B] position of the new token (keys 0..pos)
   int32_t* sel;              // [B, Hq, K] selection (sparse), null for the full stream
+  uint32_t* codes;           // workspace (sparse): score codes [B*Hq][nb]
   float *part_o, *part_ml;   // workspace: parts' outputs [B*Hq][P][d], (max, sum) [B*Hq][P][2]
   void* h;                   // [B, Hq, d]
   float* lse;                // [B, Hq] or null
