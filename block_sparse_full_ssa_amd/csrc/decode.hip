@@ -10,20 +10,20 @@
 //
 // Kernels:
 //   k_cache_means    mean of the keys of cached blocks [j0, j1) -> fp32 cache
-//   k_decode_scores  one thread per (query head, complete earlier block): the
-//                    order-preserving code of q . mu_j (fp32), spread over
-//                    many workgroups so that the block means stream in at
-//                    full width
-//   k_decode_topk    per (sequence, query head): a 32-step threshold search
-//                    on the codes, winners compacted in block order
+//   k_decode_scores  one thread per (KV head, complete earlier block): the
+//                    order-preserving codes of q . mu_j (fp32) for the G
+//                    query heads, spread over many workgroups so that the
+//                    block means stream in at full width, each read once
+//   k_decode_topk    per (sequence, query head): a radix-256 threshold
+//                    search on the codes, winners compacted in block order
 //   k_decode_attend  one wave per part: a selected block of one query head
 //                    (sparse), or a chunk of consecutive blocks for all the
 //                    query heads of a KV head (full: each key and value row
 //                    is read once for the group); lane = key for the logits,
 //                    lane = (key group, 8 columns) for P V; the part's
 //                    (o, max, sum) go to the workspace
-//   k_decode_merge   per (sequence, query head): the parts combined in one
-//                    pass by their maxima and sums -> h and lse
+//   k_decode_merge   per (sequence, query head): the parts' maxima, then
+//                    the parts combined by their weights -> h and lse
 // Decode is bound by HBM (each selected key and value is read once per
 // query head); none of it is a dense contraction worth the matrix cores.
 
@@ -64,50 +64,68 @@ __device__ __forceinline__ int block_scan_flag(bool flag, int* wsum, int* total)
   return before;
 }
 
-// Scores of the complete earlier blocks, one thread per (query head, block):
-// code = order-preserving bits of q . mu_j (fp32), for j < own block.
+// Scores of the complete earlier blocks: four threads per (KV head, block),
+// each with a quarter of d, combined by two shuffles; the block mean mu_j is
+// read once for the G query heads of the KV head (in passes of up to 8
+// heads); code = order-preserving bits of q . mu_j (fp32) for j < own block.
 template <typename T>
 __global__ void __launch_bounds__(256) k_decode_scores(const T* __restrict__ q, const float* __restrict__ mu,
                                                        const int32_t* __restrict__ pos, uint32_t* __restrict__ codes,
                                                        int Hq, int G, int d, int block, int nbmax) {
-  __shared__ float4 qs[32];
-  const int64_t bh = blockIdx.x;
-  const int b = static_cast<int>(bh / Hq), h = static_cast<int>(bh % Hq);
-  const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
+  __shared__ float4 qs[8][32];
+  const int64_t bc = blockIdx.x;
+  const int Hkv = Hq / G;
+  const int b = static_cast<int>(bc / Hkv), c = static_cast<int>(bc % Hkv);
   const int t = min(max(pos[b], 0), nbmax * block - 1);
   const int it = t / block;
-  const int j = static_cast<int>(blockIdx.y) * 256 + threadIdx.x;
-  if (static_cast<int>(blockIdx.y) * 256 >= it) return;         // uniform: no candidate here
-  if (threadIdx.x < d / 4) {
-    const int e = 4 * threadIdx.x;
-    qs[threadIdx.x] = make_float4(to_f32(q[bh * d + e]), to_f32(q[bh * d + e + 1]), to_f32(q[bh * d + e + 2]),
-                                  to_f32(q[bh * d + e + 3]));
+  const int quarter = threadIdx.x & 3;
+  const int j = static_cast<int>(blockIdx.y) * 64 + (threadIdx.x >> 2);
+  if (static_cast<int>(blockIdx.y) * 64 >= it) return;          // uniform: no candidate here
+  const int nq = d / 16;                                         // float4s per quarter
+  const float4* m4 = reinterpret_cast<const float4*>(mu + (bc * nbmax + min(j, it - 1)) * d) + quarter * nq;
+  for (int g0 = 0; g0 < G; g0 += 8) {
+    const int ng = min(8, G - g0);
+    __syncthreads();                                             // qs of the previous pass consumed
+    for (int e = threadIdx.x; e < ng * (d / 4); e += 256) {
+      const int g = e / (d / 4), x = 4 * (e % (d / 4));
+      const T* qr = q + (static_cast<int64_t>(b) * Hq + c * G + g0 + g) * d + x;
+      qs[g][e % (d / 4)] = make_float4(to_f32(qr[0]), to_f32(qr[1]), to_f32(qr[2]), to_f32(qr[3]));
+    }
+    __syncthreads();
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int e = 0; e < nq; ++e) {
+      const float4 m = m4[e];
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const float4 x = qs[g][quarter * nq + e];
+        acc[g] = fmaf(x.x, m.x, acc[g]);
+        acc[g] = fmaf(x.y, m.y, acc[g]);
+        acc[g] = fmaf(x.z, m.z, acc[g]);
+        acc[g] = fmaf(x.w, m.w, acc[g]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      acc[g] += __shfl_xor(acc[g], 1, 64);
+      acc[g] += __shfl_xor(acc[g], 2, 64);
+    }
+    if (j < it && quarter == 0)
+      for (int g = 0; g < ng; ++g)
+        codes[(static_cast<int64_t>(b) * Hq + c * G + g0 + g) * nbmax + j] = ordered_bits(acc[g]);
   }
-  __syncthreads();
-  if (j >= it) return;
-  const float4* m4 = reinterpret_cast<const float4*>(mu + (bc * nbmax + j) * d);
-  float s = 0.f;
-#pragma unroll 8
-  for (int e = 0; e < d / 4; ++e) {
-    const float4 m = m4[e], x = qs[e];
-    s = fmaf(x.x, m.x, s);
-    s = fmaf(x.y, m.y, s);
-    s = fmaf(x.z, m.z, s);
-    s = fmaf(x.w, m.w, s);
-  }
-  codes[bh * nbmax + j] = ordered_bits(s);
 }
 
 // Per (sequence, query head): the own block and the top_k - 1 largest codes,
 // ties to the lower block, written ascending with -1 padding.  Thread tid
-// holds codes tid + 256 r (r < 16: up to 4096 blocks) in registers; counts
-// are ballots summed per wave and over the 4 waves through LDS.
+// holds codes tid + 256 r (r < 16: up to 4096 blocks) in registers; the
+// threshold is found digit by digit (radix 256, four rounds).
 __global__ void __launch_bounds__(256) k_decode_topk(const uint32_t* __restrict__ codes_g,
                                                      const int32_t* __restrict__ pos, int32_t* __restrict__ sel,
                                                      int Hq, int block, int nbmax, int K) {
   constexpr int R = 16;
   __shared__ int wsum[4];
-  __shared__ int wcnt[2][4];
+  __shared__ int hist[256];
+  __shared__ int pick[2];
   const int64_t bh = blockIdx.x;
   const int b = static_cast<int>(bh / Hq);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -130,27 +148,41 @@ __global__ void __launch_bounds__(256) k_decode_topk(const uint32_t* __restrict_
     const int j = tid + 256 * r;
     c[r] = (r < nr && j < it) ? codes_g[bh * nbmax + j] : 0u;
   }
-  // number of the candidates (j < it) whose code is >= v: ballots per wave,
-  // then the 4 wave counts through LDS (two buffers: one barrier per count)
-  int buf = 0;
-  auto count_ge = [&](uint32_t v) {
-    int n = 0;
+  // the keep-th largest code, 8 bits per round: a histogram of the next
+  // digit among the codes that match the digits fixed so far, then the digit
+  // whose suffix count reaches the number still to find
+  uint32_t prefix = 0, mask = 0;
+  int remaining = keep;                             // codes still to take at or below the prefix
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (r < nr) n += __popcll(__ballot(tid + 256 * r < it && c[r] >= v));
-    if (lane == 0) wcnt[buf][w] = n;
+      if (r < nr && tid + 256 * r < it && (c[r] & mask) == prefix) atomicAdd(&hist[(c[r] >> shift) & 255u], 1);
     __syncthreads();
-    const int total = wcnt[buf][0] + wcnt[buf][1] + wcnt[buf][2] + wcnt[buf][3];
-    buf ^= 1;
-    return total;
-  };
-  // the keep-th largest code: the largest v with #{codes >= v} >= keep
-  uint32_t thr = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = thr | (1u << bit);
-    if (count_ge(cand) >= keep) thr = cand;
+    // suffix sums S(v) = #{matching codes with digit >= v}, v = tid
+    const int hv = hist[tid];
+    int sv = hv;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_down(sv, off, 64);
+      if (lane + off < 64) sv += y;
+    }
+    if (lane == 0) wsum[w] = sv;                    // the wave's total
+    __syncthreads();
+    for (int u = w + 1; u < 4; ++u) sv += wsum[u];
+    if (sv >= remaining && sv - hv < remaining) {   // exactly one digit
+      pick[0] = static_cast<int>(prefix | (static_cast<uint32_t>(tid) << shift));
+      pick[1] = remaining - (sv - hv);
+    }
+    __syncthreads();
+    prefix = static_cast<uint32_t>(pick[0]);
+    remaining = pick[1];
+    mask |= 255u << shift;
+    __syncthreads();                                // pick and wsum are reused next round
   }
-  const int n_gt = thr == 0xffffffffu ? 0 : count_ge(thr + 1);
+  const uint32_t thr = prefix;
+  const int n_gt = keep - remaining;                // codes above thr
   const int need_eq = keep - n_gt;
   int written = 0, eq_seen = 0;
 #pragma unroll
@@ -353,32 +385,33 @@ __global__ void __launch_bounds__(256) k_decode_attend(const T* __restrict__ q, 
   }
 }
 
-// Per (sequence, query head): the parts combined in one pass (running maximum).
+// Per (sequence, query head): the parts' maxima reduced first, then every
+// column adds its parts' outputs with known weights (independent loads).
 template <typename T>
 __global__ void __launch_bounds__(128) k_decode_merge(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, T* __restrict__ h,
                                                       float* __restrict__ lse, int d, int n_parts) {
+  __shared__ float red[2];
   const int64_t bh = blockIdx.x;
-  const int col = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
   const float* pml = part_ml + bh * n_parts * 2;
-  const float* po = part_o + bh * n_parts * d + (col < d ? col : 0);
-  float M = -INFINITY, L = 0.f, o = 0.f;
+  float mx = -INFINITY;
+  for (int p = tid; p < n_parts; p += 128) mx = fmaxf(mx, pml[2 * p]);
+  mx = wave_max(mx);
+  if (lane == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  const float M = fmaxf(red[0], red[1]);            // finite: the own block is never empty
+  const int col = tid < d ? tid : 0;
+  const float* po = part_o + bh * n_parts * d + col;
+  float L = 0.f, o = 0.f;
+#pragma unroll 8
   for (int p = 0; p < n_parts; ++p) {
-    const float mp = pml[2 * p];
-    if (mp == -INFINITY) continue;                  // an empty part
-    const float lp = pml[2 * p + 1], op = po[static_cast<int64_t>(p) * d];
-    if (mp > M) {
-      const float f = exp2f(M - mp);                 // 0 on the first part
-      L *= f;
-      o *= f;
-      M = mp;
-    }
-    const float g = exp2f(mp - M);
-    L = fmaf(lp, g, L);
-    o = fmaf(op, g, o);
+    const float g = exp2f(pml[2 * p] - M);           // 0 for an empty part (max -inf)
+    L = fmaf(pml[2 * p + 1], g, L);
+    o = fmaf(po[static_cast<int64_t>(p) * d], g, o);
   }
-  if (col < d) h[bh * d + col] = from_f32<T>(o / L);
-  if (col == 0 && lse) lse[bh] = (M + log2f(L)) * 0.69314718055994531f;
+  if (tid < d) h[bh * d + tid] = from_f32<T>(o / L);
+  if (tid == 0 && lse) lse[bh] = (M + log2f(L)) * 0.69314718055994531f;
 }
 
 }  // namespace
@@ -426,12 +459,12 @@ static void attend_all(const Dims& Dm, const DecodeArgs& a, int P, float sl2, hi
 void launch_decode(const Dims& D, const DecodeArgs& a, hipStream_t s) {
   const bool sparse = a.sel != nullptr;
   const int P = decode_parts(D, sparse);
-  const unsigned rows = static_cast<unsigned>(D.B * D.Hq);
+  const unsigned rows = static_cast<unsigned>(D.B * D.Hq), kvs = static_cast<unsigned>(D.B * D.Hkv);
   const float sl2 = D.scale * kLog2eD;
   timing_begin(kKDecode, s);
   if (D.dtype == 1) {
     if (sparse) {
-      hipLaunchKernelGGL(k_decode_scores<bf16_t>, dim3(rows, static_cast<unsigned>((D.nb + 255) / 256)), dim3(256), 0,
+      hipLaunchKernelGGL(k_decode_scores<bf16_t>, dim3(kvs, static_cast<unsigned>((D.nb + 63) / 64)), dim3(256), 0,
                          s, static_cast<const bf16_t*>(a.q), a.mu, a.pos, a.codes, D.Hq, D.G, D.d, D.block, D.nb);
       hipLaunchKernelGGL(k_decode_topk, dim3(rows), dim3(256), 0, s, a.codes, a.pos, a.sel, D.Hq, D.block, D.nb, D.K);
     }
@@ -441,7 +474,7 @@ void launch_decode(const Dims& D, const DecodeArgs& a, hipStream_t s) {
                        static_cast<bf16_t*>(a.h), a.lse, D.d, P);
   } else {
     if (sparse) {
-      hipLaunchKernelGGL(k_decode_scores<float>, dim3(rows, static_cast<unsigned>((D.nb + 255) / 256)), dim3(256), 0,
+      hipLaunchKernelGGL(k_decode_scores<float>, dim3(kvs, static_cast<unsigned>((D.nb + 63) / 64)), dim3(256), 0,
                          s, static_cast<const float*>(a.q), a.mu, a.pos, a.codes, D.Hq, D.G, D.d, D.block, D.nb);
       hipLaunchKernelGGL(k_decode_topk, dim3(rows), dim3(256), 0, s, a.codes, a.pos, a.sel, D.Hq, D.block, D.nb, D.K);
     }
