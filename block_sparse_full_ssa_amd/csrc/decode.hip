@@ -83,6 +83,9 @@ __global__ void __launch_bounds__(256) k_decode_scores(const T* __restrict__ q, 
   if (static_cast<int>(blockIdx.y) * 64 >= it) return;          // uniform: no candidate here
   const int nq = d / 16;                                         // float4s per quarter
   const float4* m4 = reinterpret_cast<const float4*>(mu + (bc * nbmax + min(j, it - 1)) * d) + quarter * nq;
+  float4 mv[8];                                                  // the block mean's quarter, loaded first
+#pragma unroll
+  for (int e = 0; e < 8; ++e) mv[e] = e < nq ? m4[e] : make_float4(0.f, 0.f, 0.f, 0.f);
   for (int g0 = 0; g0 < G; g0 += 8) {
     const int ng = min(8, G - g0);
     __syncthreads();                                             // qs of the previous pass consumed
@@ -93,8 +96,10 @@ __global__ void __launch_bounds__(256) k_decode_scores(const T* __restrict__ q, 
     }
     __syncthreads();
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int e = 0; e < nq; ++e) {
-      const float4 m = m4[e];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e >= nq) break;
+      const float4 m = mv[e];
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
         const float4 x = qs[g][quarter * nq + e];
@@ -125,7 +130,9 @@ __global__ void __launch_bounds__(256) k_decode_topk(const uint32_t* __restrict_
   constexpr int R = 16;
   __shared__ int wsum[4];
   __shared__ int hist[256];
-  __shared__ int pick[2];
+  __shared__ int pick[3];
+  __shared__ int list[64];
+  __shared__ int n_list;
   const int64_t bh = blockIdx.x;
   const int b = static_cast<int>(bh / Hq);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -174,6 +181,7 @@ __global__ void __launch_bounds__(256) k_decode_topk(const uint32_t* __restrict_
     if (sv >= remaining && sv - hv < remaining) {   // exactly one digit
       pick[0] = static_cast<int>(prefix | (static_cast<uint32_t>(tid) << shift));
       pick[1] = remaining - (sv - hv);
+      pick[2] = hv;                                 // last round: the codes equal to the threshold
     }
     __syncthreads();
     prefix = static_cast<uint32_t>(pick[0]);
@@ -183,7 +191,34 @@ __global__ void __launch_bounds__(256) k_decode_topk(const uint32_t* __restrict_
   }
   const uint32_t thr = prefix;
   const int n_gt = keep - remaining;                // codes above thr
+  const int n_eq = pick[2];
   const int need_eq = keep - n_gt;
+  if (need_eq == n_eq) {
+    // no tie at the threshold to break: the winners are the codes >= thr
+    // (keep <= 63 of them, top_k <= 64 here); gathered in any order, then
+    // sorted ascending by one wave
+    if (tid == 0) n_list = 0;
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < nr && tid + 256 * r < it && c[r] >= thr) list[atomicAdd(&n_list, 1)] = tid + 256 * r;
+    __syncthreads();
+    if (w == 0) {
+      int v = lane < keep ? list[lane] : 0x7fffffff;
+#pragma unroll
+      for (int k2 = 2; k2 <= 64; k2 <<= 1)
+#pragma unroll
+        for (int j2 = k2 >> 1; j2 > 0; j2 >>= 1) {
+          const int other = __shfl_xor(v, j2, 64);
+          const bool ascending = (lane & k2) == 0, lower = (lane & j2) == 0;
+          v = (lower == ascending) ? min(v, other) : max(v, other);
+        }
+      if (lane < keep) out[lane] = v;
+      if (lane == 0) out[keep] = it;
+    }
+    for (int p = keep + 1 + tid; p < K; p += 256) out[p] = -1;
+    return;
+  }
   int written = 0, eq_seen = 0;
 #pragma unroll
   for (int r = 0; r < R; ++r) {

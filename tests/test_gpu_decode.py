@@ -212,3 +212,37 @@ def test_decode_128k_cache_sampled_heads():
         assert_close(f"{tag} h_full", fu["h"][b, h][None], ref["h_full"], wl.dtype)
         assert_close(f"{tag} lse_full", fu["lse"][b, h][None], ref["lse_full"], wl.dtype)
     _say(f"  heads exempt by margin: {exempt}")
+
+
+@pytest.mark.parametrize("kind", ["zero_query", "three_levels"])
+def test_decode_ties_lower_block_wins(kind):
+    """Exact ties at the cutoff (scores exactly representable in fp32 and
+    fp64): q = 0 ties every block; q = e_0 over block means taking three
+    values ties five blocks at the top.  The lower block index must win, as
+    in the oracle."""
+    B, Hq, Hkv, L, d, blk, K = 2, 4, 2, 1024, 128, 64, 4
+    g = torch.Generator().manual_seed(11)
+    k = torch.zeros(B, Hkv, L, d)
+    k[..., 0] = ((torch.arange(L) // blk) % 3).float() * 0.5      # block j: mean (j % 3) / 2 in column 0
+    v = torch.randn(B, Hkv, L, d, generator=g)
+    q = torch.zeros(B, Hq, d)
+    if kind == "three_levels":
+        q[..., 0] = 1.0
+    q, k, v = (x.to(torch.bfloat16) for x in (q, k, v))
+    qd, kd, vd = (x.to("cuda:0") for x in (q, k, v))
+    mu = _means(kd, blk)
+    pos_l = [L - 1, 9 * blk + 3]
+    pos = torch.tensor(pos_l, dtype=torch.int32, device="cuda:0")
+    sp = ssa().ssa_decode(qd, kd, vd, mu, pos, blk, K, ssa().SPARSE_ONLY)
+    torch.cuda.synchronize()
+    kf, vf, qf = si.to_f64(k), si.to_f64(v), si.to_f64(q)
+    for b in range(B):
+        t = pos_l[b]
+        ti = np.array([t])
+        for h in range(Hq):
+            c = h // (Hq // Hkv)
+            mu_c = oracle.block_means(kf[b:b + 1, c:c + 1], blk)[0, 0]
+            ref_sel, _ = oracle.select_rows(qf[b, h][None], ti, mu_c, blk, K)
+            assert sp["sel"][b, h].tolist() == ref_sel[0].tolist(), (kind, b, h)
+            ref = oracle.attend_rows(qf[b, h][None], ti, kf[b, c], vf[b, c], ref_sel, blk, 1.0 / math.sqrt(d))
+            assert_close(f"ties {kind} b{b} h{h}", sp["h"][b, h][None], ref["h_sparse"], torch.bfloat16)
