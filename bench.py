@@ -144,6 +144,41 @@ def time_calls(fn, reps, warm=1):
     return (time.perf_counter() - t0) * 1000.0 / reps
 
 
+def hbm_rates(ssa, q, k, v, sel, wl, K, reps):
+    """GB/s of the HBM-bound steps (a2 selection, a8 sparse-only forward)
+    from the library's device-time events, against the 8 TB/s peak.  Bytes
+    are the compulsory ones: selection reads q and k, writes and reads the
+    block means and writes sel; the sparse-only forward reads q, k, v and sel,
+    writes h_sparse and lse_sparse, and writes and reads one partial (d bf16
+    values + an fp32 log-sum-exp) per selected (row, block)."""
+    B, Hq, N, d = q.shape
+    blk, nb = wl.block, N // wl.block
+    el = q.element_size()
+
+    def dev_ms(fn, names):
+        ssa.timing_enable(True)
+        for _ in range(reps):
+            fn()
+        ms = sum(ssa.timing_query(n)[0] for n in names) / reps
+        ssa.timing_enable(False)
+        return ms
+
+    ms_sel = dev_ms(lambda: ssa.ssa_select_blocks(q, k, blk, K), ("block_mean", "select"))
+    ms_sp = dev_ms(lambda: ssa.ssa_attn_fwd(q, k, v, sel, blk, K, ssa.SPARSE_ONLY, want_lse=True),
+                   ("bucket", "sparse_part", "sparse_merge"))
+    mu_bytes = B * wl.hkv * nb * d * 4
+    sel_bytes = q.numel() // d * K * 4
+    b_sel = q.numel() * el + k.numel() * el + 2 * mu_bytes + sel_bytes
+    entries = B * Hq * sum(min(K, t // blk + 1) for t in range(N))
+    b_sp = (q.numel() + k.numel() + v.numel()) * el + sel_bytes + q.numel() * el + q.numel() // d * 4 \
+        + 2 * entries * (d * 2 + 4)
+    return {"select_ms": round(ms_sel, 4), "select_GBps": round(b_sel / (ms_sel / 1e3) / 1e9, 1),
+            "select_frac_of_hbm": round(b_sel / (ms_sel / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "sparse_fwd_ms": round(ms_sp, 4), "sparse_fwd_GBps": round(b_sp / (ms_sp / 1e3) / 1e9, 1),
+            "sparse_fwd_frac_of_hbm": round(b_sp / (ms_sp / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "select_bytes": b_sel, "sparse_fwd_bytes": b_sp}
+
+
 def single_stream(ssa, q, k, v, dout, wl, ks, reps):
     """FULL_ONLY fwd+bwd TFLOP/s (14 d P_full B Hq per step) and, per top_k,
     the sparse-stream forward speedup t(FULL_ONLY fwd) / t(SPARSE_ONLY fwd)
@@ -172,7 +207,8 @@ def single_stream(ssa, q, k, v, dout, wl, ks, reps):
         sp[str(kk)] = {"sparse_only_fwd_ms": round(ms_sp, 3), "select_ms": round(ms_sel, 3),
                        "speedup": round(ms_full_fwd / ms_sp, 2),
                        "speedup_incl_select": round(ms_full_fwd / (ms_sp + ms_sel), 2),
-                       "P_full/P_sparse": round(a / b, 2), "N/(K*block)": round(N / (kk * blk), 2)}
+                       "P_full/P_sparse": round(a / b, 2), "N/(K*block)": round(N / (kk * blk), 2),
+                       "hbm": hbm_rates(ssa, q, k, v, sel, wl, kk, reps)}
         del sel
     out["sparse_fwd_speedup"] = sp
 
