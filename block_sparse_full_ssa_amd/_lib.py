@@ -35,7 +35,7 @@ EXPORTED = (
     "ssa_workspace_size", "ssa_select_blocks", "ssa_attn_fwd", "ssa_attn_fwd_stats", "ssa_attn_bwd",
     "ssa_status_string", "ssa_last_error", "ssa_timing_enable", "ssa_timing_query",
     "ssa_kernel_count", "ssa_kernel_name", "ssa_probe_mfma", "ssa_probe_copy",
-    "ssa_cache_block_means", "ssa_decode",
+    "ssa_cache_block_means", "ssa_decode", "ssa_prefill_workspace_size", "ssa_prefill",
 )
 
 
@@ -102,6 +102,10 @@ def lib() -> ctypes.CDLL:
     L.ssa_cache_block_means.restype = i32
     L.ssa_decode.argtypes = [shp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.ssa_decode.restype = i32
+    L.ssa_prefill_workspace_size.argtypes = [shp, i32, i32]
+    L.ssa_prefill_workspace_size.restype = sz
+    L.ssa_prefill.argtypes = [shp, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    L.ssa_prefill.restype = i32
     L.ssa_probe_mfma.argtypes = [vp, i32, i32, vp]
     L.ssa_probe_mfma.restype = i32
     L.ssa_probe_copy.argtypes = [vp, vp, sz, vp]

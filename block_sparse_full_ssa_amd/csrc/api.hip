@@ -83,6 +83,8 @@ static ssa_status_t make_dims(const ssa_shape_t* sh, Dims* D) {
   D->G = sh->group;
   D->Hkv = sh->heads_q / sh->group;
   D->N = sh->seqlen;
+  D->Nq = sh->seqlen;
+  D->q_off = 0;
   D->d = sh->head_dim;
   D->block = sh->block;
   D->nb = nb;
@@ -413,6 +415,63 @@ ssa_status_t ssa_timing_query(const char* kernel, double* total_ms, int64_t* lau
   *total_ms = tot;
   *launches = n;
   return SSA_OK;
+}
+
+}  // extern "C"
+
+namespace ssa {
+// Dimensions of a prefill chunk: Nq = chunk query rows at positions pos0 ..
+// against the cache of capacity seqlen.
+static ssa_status_t prefill_dims(const ssa_shape_t* shape, int32_t mode, int32_t pos0, int32_t chunk, Dims* D) {
+  ssa_status_t st = make_dims(shape, D);
+  if (st != SSA_OK) return st;
+  if (mode != kFullOnly && mode != kSparseOnly)
+    return fail(SSA_ERR_UNSUPPORTED, "prefill runs one stream: SSA_FULL_ONLY or SSA_SPARSE_ONLY%s");
+  if (D->dtype != 1 || D->d != 128) return fail(SSA_ERR_UNSUPPORTED, "prefill needs bf16 and head_dim 128%s");
+  if (chunk < 1 || pos0 < 0 || pos0 % D->block != 0 || chunk % D->block != 0 || pos0 + chunk > D->N)
+    return fail(SSA_ERR_SHAPE, "need pos0 and chunk multiples of block with pos0 + chunk <= seqlen%s");
+  D->Nq = chunk;
+  D->q_off = pos0;
+  return SSA_OK;
+}
+}  // namespace ssa
+
+extern "C" {
+
+size_t ssa_prefill_workspace_size(const ssa_shape_t* shape, int32_t mode, int32_t chunk) {
+  Dims D;
+  if (prefill_dims(shape, mode, 0, chunk, &D) != SSA_OK) {
+    g_last_error.clear();
+    return 0;
+  }
+  return ws_need(D, mode, SSA_OP_FWD);
+}
+
+ssa_status_t ssa_prefill(const ssa_shape_t* shape, int32_t mode, const void* q, int32_t pos0, int32_t chunk,
+                         const void* k_cache, const void* v_cache, const float* mu_cache, void* h, float* lse,
+                         int32_t* sel, void* ws, size_t ws_bytes, void* stream) {
+  g_last_error.clear();
+  Dims D;
+  ssa_status_t st = prefill_dims(shape, mode, pos0, chunk, &D);
+  if (st != SSA_OK) return st;
+  if (!q || !k_cache || !v_cache || !h) return fail(SSA_ERR_NULL, "q, k_cache, v_cache and h are required%s");
+  if (mode == kSparseOnly && (!mu_cache || !sel)) return fail(SSA_ERR_NULL, "mu_cache and sel are required%s");
+  if ((st = check_ws(D, mode, SSA_OP_FWD, ws, ws_bytes)) != SSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mode == kFullOnly) {
+    FwdArgs a{q, k_cache, v_cache, nullptr, h, nullptr, lse, nullptr, nullptr, nullptr, kFullOnly};
+    launch_fwd_mfma(D, a, s);
+    return launch_status();
+  }
+  Carver c{static_cast<char*>(ws)};
+  FwdWs w = carve_fwd(D, mode, c);
+  launch_select(D, q, mu_cache, sel, s);
+  if ((st = launch_status()) != SSA_OK) return st;
+  launch_buckets(D, sel, w.bk, s);
+  if ((st = launch_status()) != SSA_OK) return st;
+  SparseFwdArgs p{q, k_cache, v_cache, sel, w.bk.mask, w.bk.offs, w.bk.rows, w.bk.wpos, w.part_o, w.part_lse, h, lse};
+  launch_sparse_fwd(D, p, s);
+  return launch_status();
 }
 
 ssa_status_t ssa_cache_block_means(const ssa_shape_t* shape, const void* k_cache, float* mu_cache,

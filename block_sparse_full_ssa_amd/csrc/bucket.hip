@@ -14,12 +14,16 @@
 //          -> mask[b, c][j][h % G][tile]   (bit r: row 32 tile + r selected j)
 //   count: rows per bucket (popcounts of the bucket's masks);
 //   scan:  exclusive prefix of the counts -> offs (one workgroup);
-//   fill:  entries (h % G) * N + t of bucket (b, c, j), ordered by (head, t),
+//   fill:  entries (h % G) * Nq + r of bucket (b, c, j) (r: the query row,
+//          at position q_off + r), ordered by (head, r),
 //          at rows[offs[(b*Hkv + c)*nb + j] ...], and for every mask word the
 //          position of its first entry (wpos, same layout as mask), so that
 //          the entry of (row, j) is wpos[word] + popcount of the word's bits
 //          below the row.
 // Entries of sel that are negative or above the row's own block are ignored.
+// A layer has Nq = N query rows at positions 0 .. N-1 (q_off = 0); a prefill
+// chunk has Nq rows at positions q_off .. (both multiples of 32 and of the
+// block) against nb key blocks of the cache.
 
 #include "common.h"
 #include "internal.h"
@@ -54,18 +58,18 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* scratch, int* to
 }
 
 __global__ void __launch_bounds__(64) k_bucket_mask(const int32_t* __restrict__ sel, uint32_t* __restrict__ mask,
-                                                    int Hq, int G, int N, int nb, int K, int block) {
+                                                    int Hq, int G, int Nq, int q_off, int nb, int K, int block) {
   extern __shared__ uint32_t words[];    // [own block + 1]
   const int qt = blockIdx.x, bh = blockIdx.y;
   const int lane = threadIdx.x;
-  const int nqt = N / 32;
+  const int nqt = Nq / 32;
   const int b = bh / Hq, h = bh % Hq, Hkv = Hq / G;
   const int c = h / G, hl = h % G;
   const int t0 = qt * 32;
-  const int own = t0 / block;            // block >= 32 divides into whole tiles
+  const int own = (q_off + t0) / block;  // block >= 32 divides into whole tiles
   for (int j = lane; j <= own; j += 64) words[j] = 0u;
   __syncthreads();
-  const int32_t* s = sel + (static_cast<int64_t>(bh) * N + t0) * K;
+  const int32_t* s = sel + (static_cast<int64_t>(bh) * Nq + t0) * K;
   for (int e = lane; e < 32 * K; e += 64) {
     const int blk = s[e];
     if (blk >= 0 && blk <= own) atomicOr(&words[blk], 1u << (e / K));
@@ -76,12 +80,12 @@ __global__ void __launch_bounds__(64) k_bucket_mask(const int32_t* __restrict__ 
 }
 
 __global__ void __launch_bounds__(kScanThreads) k_bucket_count(const uint32_t* __restrict__ mask,
-                                                               int32_t* __restrict__ count, int G, int N,
-                                                               int nb, int block) {
+                                                               int32_t* __restrict__ count, int G, int Nq,
+                                                               int q_off, int nb, int block) {
   __shared__ int scratch[4];
   const int j = blockIdx.x, bc = blockIdx.y;
-  const int nqt = N / 32;
-  const int qt0 = j * block / 32;        // earlier rows cannot select block j
+  const int nqt = Nq / 32;
+  const int qt0 = max(0, j * block - q_off) / 32;   // earlier rows cannot select block j
   const uint32_t* m = mask + (static_cast<int64_t>(bc) * nb + j) * G * nqt;
   int cnt = 0;
   for (int hl = 0; hl < G; ++hl)
@@ -110,12 +114,12 @@ __global__ void __launch_bounds__(kScanThreads) k_bucket_scan(const int32_t* __r
 __global__ void __launch_bounds__(kScanThreads) k_bucket_fill(const uint32_t* __restrict__ mask,
                                                               const int32_t* __restrict__ offs,
                                                               int32_t* __restrict__ rows,
-                                                              int32_t* __restrict__ wpos, int G, int N, int nb,
-                                                              int block) {
+                                                              int32_t* __restrict__ wpos, int G, int Nq,
+                                                              int q_off, int nb, int block) {
   __shared__ int scratch[4];
   const int j = blockIdx.x, bc = blockIdx.y;
-  const int nqt = N / 32;
-  const int qt0 = j * block / 32;
+  const int nqt = Nq / 32;
+  const int qt0 = max(0, j * block - q_off) / 32;
   const int64_t w0 = (static_cast<int64_t>(bc) * nb + j) * G * nqt;
   const uint32_t* m = mask + w0;
   int run = offs[static_cast<int64_t>(bc) * nb + j];
@@ -129,7 +133,7 @@ __global__ void __launch_bounds__(kScanThreads) k_bucket_fill(const uint32_t* __
       while (w) {
         const int r = __builtin_ctz(w);
         w &= w - 1;
-        rows[pos++] = hl * N + 32 * qt + r;
+        rows[pos++] = hl * Nq + 32 * qt + r;
       }
       run += total;
     }
@@ -139,7 +143,7 @@ __global__ void __launch_bounds__(kScanThreads) k_bucket_fill(const uint32_t* __
 }  // namespace
 
 int64_t bucket_mask_words(const Dims& D) {
-  return static_cast<int64_t>(D.B) * D.Hkv * D.nb * D.G * (D.N / 32);
+  return static_cast<int64_t>(D.B) * D.Hkv * D.nb * D.G * (D.Nq / 32);
 }
 
 int64_t bucket_capacity(const Dims& D) {
@@ -149,13 +153,13 @@ int64_t bucket_capacity(const Dims& D) {
 void launch_buckets(const Dims& D, const int32_t* sel, const Buckets& bk, hipStream_t s) {
   const int nbk = D.B * D.Hkv * D.nb;
   timing_begin(kKBucket, s);
-  hipLaunchKernelGGL(k_bucket_mask, dim3(D.N / 32, D.B * D.Hq), dim3(64), static_cast<size_t>(D.nb) * 4, s, sel,
-                     bk.mask, D.Hq, D.G, D.N, D.nb, D.K, D.block);
+  hipLaunchKernelGGL(k_bucket_mask, dim3(D.Nq / 32, D.B * D.Hq), dim3(64), static_cast<size_t>(D.nb) * 4, s, sel,
+                     bk.mask, D.Hq, D.G, D.Nq, D.q_off, D.nb, D.K, D.block);
   hipLaunchKernelGGL(k_bucket_count, dim3(D.nb, D.B * D.Hkv), dim3(kScanThreads), 0, s, bk.mask, bk.count, D.G,
-                     D.N, D.nb, D.block);
+                     D.Nq, D.q_off, D.nb, D.block);
   hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(kScanThreads), 0, s, bk.count, bk.offs, nbk);
   hipLaunchKernelGGL(k_bucket_fill, dim3(D.nb, D.B * D.Hkv), dim3(kScanThreads), 0, s, bk.mask, bk.offs, bk.rows,
-                     bk.wpos, D.G, D.N, D.nb, D.block);
+                     bk.wpos, D.G, D.Nq, D.q_off, D.nb, D.block);
   timing_end(kKBucket, s);
 }
 

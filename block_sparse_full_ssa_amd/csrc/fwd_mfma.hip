@@ -71,7 +71,8 @@ __device__ __forceinline__ float max16(const f32x16& v) {
 // one wave's softmax overlaps the other wave's matrix work on every SIMD.
 template <int MODE, bool STATS>
 __global__ void __launch_bounds__(256, 2)
-    k_fwd_mfma(FwdArgs a, int Hq, int G, int N, int block, int nb, int K, float scale_log2, int n_qtiles) {
+    k_fwd_mfma(FwdArgs a, int Hq, int G, int N, int Nq, int q_off, int block, int nb, int K, float scale_log2,
+               int n_qtiles) {
   constexpr bool kSparse = MODE == kModeDual;
   // K and V tiles [64][128] (swizzled), two of each; separate objects so that
   // the compiler can tell the tile being read from the one being filled
@@ -90,10 +91,13 @@ __global__ void __launch_bounds__(256, 2)
   const int gk = grp >> 1, srow = li >> 2, m4 = li & 3;
   const QTileItem item = qtile_item(blockIdx.x, static_cast<int>(gridDim.x) / (n_qtiles * G), G, n_qtiles);
   const int bh = item.bh;
-  const int q0 = (n_qtiles - 1 - item.rank) * kBM;   // longest tiles first
+  // positions: the query rows 0 .. Nq-1 sit at q_off .. qend-1 (a layer: q_off 0,
+  // Nq = N); keys are the N positions of K / V
+  const int q0 = q_off + (n_qtiles - 1 - item.rank) * kBM;   // longest tiles first
+  const int qend = q_off + Nq;
   const int b = bh / Hq, h = bh % Hq;
   const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
-  const uint16_t* qg = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(bh) * N * kD;
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(bh) * Nq * kD;
   const uint16_t* kg = static_cast<const uint16_t*>(a.k) + bc * N * kD;
   const uint16_t* vg = static_cast<const uint16_t*>(a.v) + bc * N * kD;
 
@@ -103,8 +107,8 @@ __global__ void __launch_bounds__(256, 2)
     __syncthreads();
     for (int e = tid; e < kBM * K; e += 256) {
       const int r = e / K, t = q0 + r;
-      if (t < N) {
-        const int blk = a.sel[(static_cast<int64_t>(bh) * N + t) * K + (e - r * K)];
+      if (t < qend) {
+        const int blk = a.sel[(static_cast<int64_t>(bh) * Nq + (t - q_off)) * K + (e - r * K)];
         if (blk >= 0) atomicOr(&bits[r * W + (blk >> 5)], 1u << (blk & 31));
       }
     }
@@ -112,14 +116,14 @@ __global__ void __launch_bounds__(256, 2)
 
   // ---- the wave's 32 queries as B operands (query = col, d = 16*ds + 8*g + s)
   const int qrow = q0 + wave * 32 + col;           // this lane's query
-  const bool wave_live = q0 + wave * 32 < N;
+  const bool wave_live = q0 + wave * 32 < qend;
   const int wave_q0 = q0 + wave * 32;
-  const int wave_last_q = min(N - 1, wave_q0 + 31);
+  const int wave_last_q = min(qend - 1, wave_q0 + 31);
   bf16x8 qreg[kD / 16];
 #pragma unroll
   for (int ds = 0; ds < kD / 16; ++ds) {
     uint4 u = make_uint4(0, 0, 0, 0);
-    if (qrow < N) u = *reinterpret_cast<const uint4*>(qg + static_cast<int64_t>(qrow) * kD + 16 * ds + 8 * g);
+    if (qrow < qend) u = *reinterpret_cast<const uint4*>(qg + static_cast<int64_t>(qrow - q_off) * kD + 16 * ds + 8 * g);
     qreg[ds] = __builtin_bit_cast(bf16x8, u);
   }
 
@@ -135,7 +139,7 @@ __global__ void __launch_bounds__(256, 2)
   // to the running maximum like lf, for the entropy ln2 (log2 lf - ex / lf)
   float sink_l = 0.f, ex_l = 0.f;
 
-  const int j_last = min(N - 1, q0 + kBM - 1) / kBN;
+  const int j_last = min(qend - 1, q0 + kBM - 1) / kBN;
   if (kSparse) __syncthreads();
 
   // HBM -> LDS copy of one K/V tile: each wave moves rows 16*wave .. +15, one
@@ -170,7 +174,7 @@ __global__ void __launch_bounds__(256, 2)
       bool sparse_any = false;
       if (kSparse) {
         const int blk = kbase / block;
-        sb = qrow < N && blk < nb && ((bits[(wave * 32 + col) * W + (blk >> 5)] >> (blk & 31)) & 1u);
+        sb = qrow < qend && blk < nb && ((bits[(wave * 32 + col) * W + (blk >> 5)] >> (blk & 31)) & 1u);
         sparse_any = __builtin_amdgcn_readfirstlane(__any(sb) ? 1 : 0) != 0;
       }
 
@@ -310,8 +314,8 @@ __global__ void __launch_bounds__(256, 2)
   }
   ls += __shfl_xor(ls, 32, 64);
   const float inv_f = 1.f / lf, inv_s = 1.f / ls;
-  const bool row_ok = qrow < N;
-  const int64_t row = static_cast<int64_t>(bh) * N + qrow;
+  const bool row_ok = qrow < qend;
+  const int64_t row = static_cast<int64_t>(bh) * Nq + (qrow - q_off);
   float sq = 0.f;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) {
@@ -363,7 +367,8 @@ void launch_mode(const Dims& D, const FwdArgs& a, size_t lds, int n_qtiles, floa
     granted = lds;
   }
   dim3 grid(D.B * D.Hq * n_qtiles);   // work items from qtile_item
-  hipLaunchKernelGGL((k_fwd_mfma<MODE, STATS>), grid, dim3(256), lds, s, a, D.Hq, D.G, D.N, D.block, D.nb, D.K,
+  hipLaunchKernelGGL((k_fwd_mfma<MODE, STATS>), grid, dim3(256), lds, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.block,
+                     D.nb, D.K,
                      scale_log2, n_qtiles);
 }
 
@@ -382,8 +387,8 @@ bool fwd_mfma_supported(const Dims& D) {
 }
 
 void launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s) {
-  const int n_qtiles = (D.N + kBM - 1) / kBM;
-  const size_t lds = lds_bytes(D);
+  const int n_qtiles = (D.Nq + kBM - 1) / kBM;
+  const size_t lds = a.mode == kFullOnly ? 0 : lds_bytes(D);   // the full stream reads no selection bits
   const float scale_log2 = D.scale * 1.4426950408889634f;
   timing_begin(kKFwdMfma, s);
   const bool stats = a.sink_mass != nullptr;

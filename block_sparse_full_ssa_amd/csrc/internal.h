@@ -13,7 +13,11 @@ struct Dims {
   int B, Hq, Hkv, G, N, d, block, nb, K;
   int dtype;        // 0 fp32, 1 bf16
   float scale;      // softmax scale on q.k
-  int64_t rows() const { return static_cast<int64_t>(B) * Hq * N; }
+  // Query rows per head and the position of row 0.  A layer has Nq = N and
+  // q_off = 0; a prefill chunk has Nq rows at positions q_off .. q_off+Nq-1
+  // against N = the cache's capacity (keys at positions 0 .. q_off+Nq-1).
+  int Nq = 0, q_off = 0;
+  int64_t rows() const { return static_cast<int64_t>(B) * Hq * Nq; }
   int64_t q_elems() const { return rows() * d; }
   int64_t kv_elems() const { return static_cast<int64_t>(B) * Hkv * N * d; }
 };

@@ -145,8 +145,8 @@ __device__ __forceinline__ void rank_rows(const float* scores, int32_t* out0, in
 //     counts of the ballots place the winners ascending.
 template <typename T, int TM>
 __global__ void __launch_bounds__(256) k_select(const T* __restrict__ q, const float* __restrict__ mu_all,
-                                                int32_t* __restrict__ sel, int Hq, int G, int N,
-                                                int d, int block, int nb, int K, int R) {
+                                                int32_t* __restrict__ sel, int Hq, int G, int Nq,
+                                                int q_off, int d, int block, int nb, int K, int R) {
   // LDS: q rows [R][d + 4], candidate block means [64][d + 4], scores [R][nb]
   extern __shared__ __attribute__((aligned(16))) float smem[];
   const int dp = d + 4;
@@ -156,13 +156,13 @@ __global__ void __launch_bounds__(256) k_select(const T* __restrict__ q, const f
   const int bh = blockIdx.y;
   const int b = bh / Hq, h = bh % Hq;
   const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
-  const int t0 = blockIdx.x * R;    // R divides block, so all rows share i
-  const int i = t0 / block;         // own block = number of candidates
+  const int t0 = blockIdx.x * R;    // R divides block (and q_off), so all rows share i
+  const int i = (q_off + t0) / block;   // own block = number of candidates
   const int keep = min(K - 1, i);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const T* qrow0 = q + (static_cast<int64_t>(bh) * N + t0) * d;
-  int32_t* out0 = sel + (static_cast<int64_t>(bh) * N + t0) * K;
+  const T* qrow0 = q + (static_cast<int64_t>(bh) * Nq + t0) * d;
+  int32_t* out0 = sel + (static_cast<int64_t>(bh) * Nq + t0) * K;
 
   if (keep == i || keep == 0) {
     // nothing to rank: every earlier block (keep == i) or none (top_k == 1)
@@ -242,19 +242,19 @@ __global__ void __launch_bounds__(256) k_select(const T* __restrict__ q, const f
 // fp32 (their order differs from a sequential dot product only by rounding).
 template <typename T, int TM, int D>
 __global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, const float* __restrict__ mu_all,
-                                                     int32_t* __restrict__ sel, int Hq, int G, int N, int block,
-                                                     int nb, int K, int R) {
+                                                     int32_t* __restrict__ sel, int Hq, int G, int Nq,
+                                                     int q_off, int block, int nb, int K, int R) {
   extern __shared__ __attribute__((aligned(16))) float scores[];   // [R][nb]
   const int bh = blockIdx.y;
   const int b = bh / Hq, h = bh % Hq;
   const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
-  const int t0 = blockIdx.x * R;    // R divides block, so all rows share i
-  const int i = t0 / block;         // own block = number of candidates
+  const int t0 = blockIdx.x * R;    // R divides block (and q_off), so all rows share i
+  const int i = (q_off + t0) / block;   // own block = number of candidates
   const int keep = min(K - 1, i);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int32_t* out0 = sel + (static_cast<int64_t>(bh) * N + t0) * K;
+  int32_t* out0 = sel + (static_cast<int64_t>(bh) * Nq + t0) * K;
   if (keep == i || keep == 0) {
     for (int e = tid; e < R * K; e += blockDim.x) {
       const int slot = e % K;
@@ -269,7 +269,7 @@ __global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, co
   // A operand: row 32 rt + col, d = H g + k
   float qa[H];
   {
-    const T* qr = q + (static_cast<int64_t>(bh) * N + t0 + 32 * rt + col) * D + H * g;
+    const T* qr = q + (static_cast<int64_t>(bh) * Nq + t0 + 32 * rt + col) * D + H * g;
 #pragma unroll
     for (int k8 = 0; k8 < H; k8 += 8) {
 #pragma unroll
@@ -311,7 +311,7 @@ static int mfma_rows(const Dims& D) {
 
 template <typename T, int TM, int DD>
 static void launch_select_mfma(const Dims& D, int R, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
-  dim3 grid(D.N / R, D.B * D.Hq);
+  dim3 grid(D.Nq / R, D.B * D.Hq);
   const size_t lds = static_cast<size_t>(R) * D.nb * sizeof(float);
   static size_t granted = 0;     // above 64 KiB of LDS must be requested
   if (lds > granted) {
@@ -320,7 +320,7 @@ static void launch_select_mfma(const Dims& D, int R, const void* q, const float*
     granted = lds;
   }
   hipLaunchKernelGGL((k_select_mfma<T, TM, DD>), grid, dim3(256), lds, s, static_cast<const T*>(q), mu, sel, D.Hq,
-                     D.G, D.N, D.block, D.nb, D.K, R);
+                     D.G, D.Nq, D.q_off, D.block, D.nb, D.K, R);
 }
 
 template <typename T, int TM>
@@ -333,7 +333,7 @@ template <typename T, int TM>
 static void launch_select_tm(const Dims& D, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
   int R = D.block < 64 ? D.block : 64;
   while (R > 4 && static_cast<size_t>(R) * D.nb * sizeof(float) > 65536) R >>= 1;
-  dim3 grid(D.N / R, D.B * D.Hq);
+  dim3 grid(D.Nq / R, D.B * D.Hq);
   const size_t lds =
       (static_cast<size_t>(R + kSelChunk) * (D.d + 4) + static_cast<size_t>(R) * D.nb) * sizeof(float);
   static size_t granted = 0;     // above 64 KiB of LDS must be requested
@@ -343,7 +343,7 @@ static void launch_select_tm(const Dims& D, const void* q, const float* mu, int3
     granted = lds;
   }
   hipLaunchKernelGGL((k_select<T, TM>), grid, dim3(256), lds, s, static_cast<const T*>(q), mu, sel, D.Hq, D.G,
-                     D.N, D.d, D.block, D.nb, D.K, R);
+                     D.Nq, D.q_off, D.d, D.block, D.nb, D.K, R);
 }
 
 // TM = registers per lane for a row's candidates: ceil(nb / 64), rounded up

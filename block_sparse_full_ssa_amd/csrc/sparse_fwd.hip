@@ -47,8 +47,8 @@ __device__ __forceinline__ int swz_v(int r, int c) { return c ^ (((r & 7) << 1) 
 __device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
 
 template <int KH>   // the key block as KH halves of 32 keys
-__global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFwdArgs a, int Hq, int G, int N, int nb,
-                                                        float scale_log2) {
+__global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFwdArgs a, int Hq, int G, int N, int Nq,
+                                                        int q_off, int nb, float scale_log2) {
   constexpr int kBlk = 32 * KH;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlk * kD], Vs[kBlk * kD];
   // per-wave staging of a batch's partial outputs, so that they leave as
@@ -92,8 +92,8 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
     return (bt < nbat && idx < n) ? list[idx] : -1;
   };
   auto load_q = [&](int e, bf16x8* qb) {
-    const int hl = e >= 0 ? e / N : 0;
-    const int64_t R = e >= 0 ? (qhead0 + hl) * N + (e - hl * N) : 0;
+    const int hl = e >= 0 ? e / Nq : 0;
+    const int64_t R = e >= 0 ? (qhead0 + hl) * Nq + (e - hl * Nq) : 0;
 #pragma unroll
     for (int ds = 0; ds < kD / 16; ++ds) {
       uint4 u = make_uint4(0, 0, 0, 0);
@@ -109,7 +109,7 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
   for (; bt < nbat; bt += 4) {
     const int e_after = entry(bt + 8);
     const bool valid = e >= 0;
-    const int t = valid ? e % N : 0;
+    const int t = valid ? q_off + e % Nq : 0;       // the row's position
     // S^T for the block's keys (A: key 32 kh + col, d = 16 ds + 8 g + s), log2 units
     f32x16 s[KH];
 #pragma unroll
@@ -203,16 +203,16 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
 // selected blocks, lane i of a row looks up slots i, i + 16, ... in parallel
 // and the positions and weights are then broadcast within the 16 lanes;
 // wider rows (every block of a long sequence) take the serial loop.
-__global__ void __launch_bounds__(256) k_sparse_merge(SparseFwdArgs a, int64_t rows, int Hq, int G, int N, int nb,
+__global__ void __launch_bounds__(256) k_sparse_merge(SparseFwdArgs a, int64_t rows, int Hq, int G, int Nq, int nb,
                                                       int K, int Kc) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int li = threadIdx.x & 15;
   const bool live = row < rows;
   const int64_t rr = live ? row : 0;
-  const int64_t bh = rr / N;
-  const int t = static_cast<int>(rr - bh * N);
+  const int64_t bh = rr / Nq;
+  const int t = static_cast<int>(rr - bh * Nq);     // query row (bucket masks are indexed by rows)
   const int b = static_cast<int>(bh / Hq), h = static_cast<int>(bh % Hq);
-  const int Hkv = Hq / G, nqt = N / 32;
+  const int Hkv = Hq / G, nqt = Nq / 32;
   const int64_t bc = static_cast<int64_t>(b) * Hkv + h / G;
   const int hl = h % G, qt = t >> 5;
   const uint32_t below = (1u << (t & 31)) - 1u;
@@ -291,15 +291,15 @@ void launch_sparse_fwd(const Dims& D, const SparseFwdArgs& a, hipStream_t s) {
   dim3 grid(D.B * D.Hkv, D.nb);
   timing_begin(kKSparsePart, s);
   if (D.block == 32)
-    hipLaunchKernelGGL(k_sparse_part<1>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, scale_log2);
+    hipLaunchKernelGGL(k_sparse_part<1>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.nb, scale_log2);
   else if (D.block == 64)
-    hipLaunchKernelGGL(k_sparse_part<2>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, scale_log2);
+    hipLaunchKernelGGL(k_sparse_part<2>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.nb, scale_log2);
   else
-    hipLaunchKernelGGL(k_sparse_part<4>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, scale_log2);
+    hipLaunchKernelGGL(k_sparse_part<4>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.nb, scale_log2);
   timing_end(kKSparsePart, s);
   timing_begin(kKSparseMerge, s);
   hipLaunchKernelGGL(k_sparse_merge, dim3(static_cast<unsigned>((D.rows() + 15) / 16)), dim3(256), 0, s, a,
-                     D.rows(), D.Hq, D.G, D.N, D.nb, D.K, Kc);
+                     D.rows(), D.Hq, D.G, D.Nq, D.nb, D.K, Kc);
   timing_end(kKSparseMerge, s);
 }
 

@@ -232,3 +232,34 @@ def ssa_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, mu
     if ws is not None:
         out["_ws"] = ws
     return out
+
+
+def ssa_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, mu_cache: Optional[torch.Tensor],
+                pos0: int, block: int, top_k: int, mode: int = SPARSE_ONLY,
+                scale: Optional[float] = None) -> Dict[str, torch.Tensor]:
+    """A prefill chunk: q [B, Hq, C, d] of the tokens at positions pos0 .. pos0 + C - 1
+    over the caches [B, Hkv, L, d] (their keys and values already written).
+    Returns h [B, Hq, C, d], lse [B, Hq, C] and, for SPARSE_ONLY, sel [B, Hq, C, top_k]."""
+    dev = _dev_check(q, k_cache, v_cache, mu_cache)
+    if q.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, Hq, C, d] and k_cache [B, Hkv, L, d]")
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("v_cache must match k_cache")
+    B, Hq, C, d = q.shape
+    shape = _cache_shape(q[:, :, 0], k_cache, block, top_k, scale)
+    out = {"h": torch.empty_like(q), "lse": torch.empty(B, Hq, C, dtype=torch.float32, device=dev)}
+    if mode == SPARSE_ONLY:
+        out["sel"] = torch.empty(B, Hq, C, int(top_k), dtype=torch.int32, device=dev)
+    L = _lib.lib()
+    n = L.ssa_prefill_workspace_size(ctypes.byref(shape), int(mode), int(C))
+    ws, wp = None, 0
+    if n:
+        ws = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+        wp = ws.data_ptr() + (-ws.data_ptr()) % 256
+    st = L.ssa_prefill(ctypes.byref(shape), int(mode), _ptr(q), int(pos0), int(C), _ptr(k_cache), _ptr(v_cache),
+                       _ptr(mu_cache), _ptr(out["h"]), _ptr(out["lse"]), _ptr(out.get("sel")),
+                       ctypes.c_void_p(wp), n, _stream(dev))
+    _lib.check(st, "ssa_prefill")
+    if ws is not None:
+        out["_ws"] = ws
+    return out

@@ -206,9 +206,9 @@ const char* ssa_kernel_name(int32_t i);
  * The shape describes the cache: seqlen = its capacity L in tokens (a
  * multiple of block), so the caches are
  *   k_cache, v_cache [B, Hkv, L, d] (dtype), mu_cache [B, Hkv, L/block, d] fp32,
- * all device memory owned by the caller.  A prompt is processed as a layer
- * (ssa_select_blocks + ssa_attn_fwd over its N <= L tokens, with its keys
- * and values copied into the caches by the caller).
+ * all device memory owned by the caller, who also writes each token's key
+ * and value into the caches.  A prompt is processed in chunks
+ * (ssa_prefill), then one token at a time (ssa_decode).
  *
  * ssa_cache_block_means: mu_cache[b, c, j] = mean of k_cache[b, c, i] over the
  *   keys i of block j, for blocks block_begin <= j < block_end (the same
@@ -236,6 +236,31 @@ const char* ssa_kernel_name(int32_t i);
  */
 ssa_status_t ssa_cache_block_means(const ssa_shape_t* shape, const void* k_cache, float* mu_cache,
                                    int32_t block_begin, int32_t block_end, void* stream);
+
+/*
+ * ssa_prefill: a chunk of `chunk` prompt tokens at positions pos0 ..
+ *   pos0 + chunk - 1 of every sequence (chunked prefill), each attending
+ *   causally to the cached keys 0 .. its position.  The chunk's keys and
+ *   values must already be in the caches; for SSA_SPARSE_ONLY mu_cache must
+ *   hold every complete block up to the chunk's end (ssa_cache_block_means
+ *   over [0, (pos0 + chunk) / block)).
+ *     q [B, Hq, chunk, d], h [B, Hq, chunk, d] (dtype), lse [B, Hq, chunk]
+ *     fp32 (natural log, may be NULL), sel [B, Hq, chunk, top_k] int32
+ *     (SSA_SPARSE_ONLY: the rows' selection, written; required).
+ *   Rows are the layer's rows pos0 .. of the sequence: the same selection
+ *   rule and the same kernels as ssa_select_blocks + ssa_attn_fwd (the
+ *   sparse stream on key-block buckets, the full stream as the matrix
+ *   forward), with the queries offset against the cache.
+ *   Requires bf16 and head_dim 128 (else SSA_ERR_UNSUPPORTED), pos0 and
+ *   chunk multiples of block with pos0 + chunk <= seqlen (SSA_ERR_SHAPE),
+ *   mode SSA_FULL_ONLY or SSA_SPARSE_ONLY (SSA_ERR_UNSUPPORTED).  Workspace:
+ *   ssa_prefill_workspace_size(shape, mode, chunk) bytes (0 on an invalid
+ *   request; SSA_FULL_ONLY needs none).
+ */
+size_t ssa_prefill_workspace_size(const ssa_shape_t* shape, int32_t mode, int32_t chunk);
+ssa_status_t ssa_prefill(const ssa_shape_t* shape, int32_t mode, const void* q, int32_t pos0, int32_t chunk,
+                         const void* k_cache, const void* v_cache, const float* mu_cache, void* h,
+                         float* lse, int32_t* sel, void* ws, size_t ws_bytes, void* stream);
 ssa_status_t ssa_decode(const ssa_shape_t* shape, int32_t mode, const void* q, const void* k_cache,
                         const void* v_cache, const float* mu_cache, const int32_t* pos, void* h,
                         float* lse, int32_t* sel, void* ws, size_t ws_bytes, void* stream);

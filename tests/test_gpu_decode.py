@@ -246,3 +246,106 @@ def test_decode_ties_lower_block_wins(kind):
             assert sp["sel"][b, h].tolist() == ref_sel[0].tolist(), (kind, b, h)
             ref = oracle.attend_rows(qf[b, h][None], ti, kf[b, c], vf[b, c], ref_sel, blk, 1.0 / math.sqrt(d))
             assert_close(f"ties {kind} b{b} h{h}", sp["h"][b, h][None], ref["h_sparse"], torch.bfloat16)
+
+
+# --------------------------------------------------------- chunked prefill --
+
+@pytest.mark.parametrize("name", ["gqa_b2_n1024_k4", "mha_b2_n512_b32_k6", "gqa_b2_n768_b128_k3"])
+def test_prefill_chunks_equal_layer_rows(name):
+    """Chunks of a prompt processed against the cache reproduce the layer's
+    rows: the same selection (bit for bit) and both streams, and the oracle's
+    rows on a sample."""
+    wl = CASES[name]
+    _say(f"prefill {name}")
+    (q, k, v), (qf, kf, vf) = inputs(wl, 0, (wl.top_k,))
+    qd, kd, vd = (x.to("cuda:0") for x in (q, k, v))
+    N, blk, K = wl.seqlen, wl.block, wl.top_k
+    sel = ssa().ssa_select_blocks(qd, kd, blk, K)
+    fs = ssa().ssa_attn_fwd(qd, kd, vd, sel, blk, K, ssa().SPARSE_ONLY)
+    ff = ssa().ssa_attn_fwd(qd, kd, vd, None, blk, K, ssa().FULL_ONLY)
+    mu = _means(kd, blk)
+    mu_ref = oracle.block_means(kf, blk)
+    scale = scale_of(wl)
+    chunks = [(0, 2 * blk), (2 * blk, N // 2 - 2 * blk), (N // 2, blk), (N // 2 + blk, N // 2 - blk)]
+    rng = np.random.default_rng(8)
+    for p0, C in chunks:
+        qc = qd[:, :, p0:p0 + C].contiguous()
+        sp = ssa().ssa_prefill(qc, kd, vd, mu, p0, blk, K, ssa().SPARSE_ONLY)
+        fu = ssa().ssa_prefill(qc, kd, vd, None, p0, blk, K, ssa().FULL_ONLY)
+        torch.cuda.synchronize()
+        tag = f"{name} chunk {p0}+{C}"
+        assert torch.equal(sp["sel"], sel[:, :, p0:p0 + C]), tag
+        atol, rtol = TOL[wl.dtype]
+        for got, want in ((sp["h"], fs["h_sparse"][:, :, p0:p0 + C]), (sp["lse"], fs["lse_sparse"][:, :, p0:p0 + C]),
+                          (fu["h"], ff["h_full"][:, :, p0:p0 + C]), (fu["lse"], ff["lse_full"][:, :, p0:p0 + C])):
+            diff = (got.double() - want.double()).abs() - (atol + rtol * want.double().abs())
+            assert float(diff.max()) <= 0, tag
+        # a sample of the chunk's rows against the oracle
+        for b in range(wl.batch):
+            h = int(rng.integers(0, wl.hq))
+            c = h // wl.group
+            rows = np.unique(np.concatenate([[0, C - 1], rng.integers(0, C, size=4)]))
+            ti = p0 + rows
+            ref_sel, _ = oracle.select_rows(qf[b, h, ti], ti, mu_ref[b, c], blk, K)
+            assert np.array_equal(sp["sel"][b, h, torch.from_numpy(rows)].cpu().numpy(), ref_sel), tag
+            ref = oracle.attend_rows(qf[b, h, ti], ti, kf[b, c], vf[b, c], ref_sel, blk, scale)
+            idx = torch.from_numpy(rows)
+            assert_close(f"{tag} b{b} h{h} h_sparse", sp["h"][b, h, idx], ref["h_sparse"], wl.dtype)
+            assert_close(f"{tag} b{b} h{h} lse_sparse", sp["lse"][b, h, idx], ref["lse_sparse"], wl.dtype)
+            assert_close(f"{tag} b{b} h{h} h_full", fu["h"][b, h, idx], ref["h_full"], wl.dtype)
+            assert_close(f"{tag} b{b} h{h} lse_full", fu["lse"][b, h, idx], ref["lse_full"], wl.dtype)
+
+
+def test_prefill_argument_errors():
+    wl = CASES["gqa_b2_n1024_k4"]
+    (q, k, v), _ = inputs(wl, 0, (wl.top_k,))
+    qd, kd, vd = (x.to("cuda:0") for x in (q, k, v))
+    mu = _means(kd, wl.block)
+    with pytest.raises(ssa().SSAError):          # chunk past the cache
+        ssa().ssa_prefill(qd[:, :, :128].contiguous(), kd, vd, mu, 1024 - 64, wl.block, wl.top_k)
+    with pytest.raises(ssa().SSAError):          # position not on a block boundary
+        ssa().ssa_prefill(qd[:, :, :128].contiguous(), kd, vd, mu, 32, wl.block, wl.top_k)
+    with pytest.raises(ssa().SSAError):          # dual modes are training modes
+        ssa().ssa_prefill(qd[:, :, :128].contiguous(), kd, vd, mu, 0, wl.block, wl.top_k, ssa().DUAL_ACTIVE_FULL)
+
+
+def test_prefill_then_decode_128k_sampled():
+    """The last 4096-token chunk of a 131072-token prompt (B=4, 16/4 heads,
+    top_k 32, sinks), sparse and full, on sampled rows against the oracle;
+    then the decode step of the next position agrees with the same rows'
+    rule (full-size tolerance for near-ties)."""
+    wl = W["decode_b4_n128k_sinks"]
+    _say(f"prefill {wl.name}: draw")
+    _, k, v = si.draw_decode(wl, 0)
+    g = torch.Generator().manual_seed(21)
+    C, L, blk, K = 4096, wl.seqlen, wl.block, wl.top_k
+    p0 = L - C
+    qc = torch.randn(wl.batch, wl.hq, C, wl.head_dim, generator=g).to(torch.bfloat16)
+    qd, kd, vd = (x.to("cuda:0") for x in (qc, k, v))
+    mu = _means(kd, blk)
+    sp = ssa().ssa_prefill(qd, kd, vd, mu, p0, blk, K, ssa().SPARSE_ONLY)
+    fu = ssa().ssa_prefill(qd, kd, vd, None, p0, blk, K, ssa().FULL_ONLY)
+    torch.cuda.synchronize()
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    rng = np.random.default_rng(5)
+    exempt = 0
+    for b, h in ((0, 2), (3, 13)):
+        c = h // wl.group
+        kf, vf = si.to_f64(k[b, c]), si.to_f64(v[b, c])
+        mu_c = oracle.block_means(kf[None, None], blk)[0, 0]
+        rows = np.unique(np.concatenate([[0, blk - 1, C - 1], rng.integers(0, C, size=5)]))
+        ti = p0 + rows
+        qf = si.to_f64(qc[b, h])[rows]
+        ref_sel, margin = oracle.select_rows(qf, ti, mu_c, blk, K)
+        got = sp["sel"][b, h, torch.from_numpy(rows)].cpu().numpy()
+        for r in range(rows.size):
+            if margin[r] >= 1e-3:
+                assert np.array_equal(got[r], ref_sel[r]), (b, h, ti[r])
+            else:
+                exempt += 1
+        ref = oracle.attend_rows(qf, ti, kf, vf, got, blk, scale)
+        idx = torch.from_numpy(rows)
+        assert_close(f"128k prefill b{b} h{h} h_sparse", sp["h"][b, h, idx], ref["h_sparse"], wl.dtype)
+        assert_close(f"128k prefill b{b} h{h} h_full", fu["h"][b, h, idx], ref["h_full"], wl.dtype)
+        assert_close(f"128k prefill b{b} h{h} lse_full", fu["lse"][b, h, idx], ref["lse_full"], wl.dtype)
+    _say(f"  rows exempt by margin: {exempt}")
