@@ -9,11 +9,12 @@
 //
 // Two kernels:
 //   block_mean: mean of each key block, fp32, [B*Hkv][nb][d];
-//   select:     one workgroup per (head, up to 64 rows of one query block);
-//               candidate scores are computed into LDS (fp32 matrix
-//               instructions up to 1024 key blocks, else fp32 FMAs chunk by
-//               chunk), then a wave ranks each row by a bitwise threshold
-//               search (see below).
+//   select:     one workgroup per (head, 32 or 64 rows of one query block);
+//               candidate scores are computed into LDS by fp32 matrix
+//               instructions, up to 1024 candidates at a time, and a wave
+//               ranks each row by a bitwise threshold search (see below),
+//               carrying a row's winners from one chunk of candidates into
+//               the next.
 
 #include "common.h"
 #include "internal.h"
@@ -47,25 +48,44 @@ void launch_block_mean(const Dims& D, const void* k, float* mu, hipStream_t s) {
   timing_end(kKBlockMean, s);
 }
 
-constexpr int kSelChunk = 64;     // candidate blocks scored per pass
+constexpr int kCand = 1024;       // candidates scored and ranked per chunk
+constexpr int kCarry = 64;        // carried winners per row (top_k <= 64 here)
 
-// Ranking of R rows whose candidate scores sit in LDS (scores[r * nb + j],
-// j < i): see the kernel comments.  Wave w ranks rows w*RW.. in steps of 4*RW.
-template <int TM>
-__device__ __forceinline__ void rank_rows(const float* scores, int32_t* out0, int R, int nb, int K, int i, int keep,
-                                          int lane, int wave) {
+// Ranking of R rows over one chunk of candidates (scores[r * CH + c] for the
+// chunk's candidates c0 + c, c < nc) together with each row's winners so
+// far (carried: codes and block indices, ascending, ncar of them), keeping
+// `keep` winners.  Register slot 0 holds the carried entries (they precede
+// every candidate of the chunk in block order), slots 1.. the chunk's
+// candidates, so (slot, lane) order is block order: ties go to the lower
+// block.  The winners replace the carried entries (ascending); on the last
+// chunk they are written to the rows of sel instead, with the own block and
+// the padding.  Without CARRY (every candidate in one chunk) there is no
+// carried slot.  Wave w ranks rows w*RW.. in steps of 4*RW.
+template <int TM, bool CARRY>
+__device__ __forceinline__ void rank_chunk(const float* scores, int CH, int c0, int nc, uint32_t* car_code,
+                                           int32_t* car_idx, int ncar, int32_t* out0, int R, int K, int i, int keep,
+                                           bool last, int lane, int wave) {
   constexpr int RW = TM <= 8 ? 2 : 1;
-  const int nt = (i + 63) >> 6;     // registers holding candidates of this block
+  constexpr int C0 = CARRY ? 1 : 0;  // first candidate slot
+  constexpr int S = TM + C0;        // register slots: (carried +) candidates
+  const int nt = (nc + 63) >> 6;    // candidate registers in use
   for (int r0 = wave * RW; r0 < R; r0 += 4 * RW) {
-    uint32_t u[RW][TM];
+    uint32_t u[RW][S];
+    int32_t cidx[RW];
 #pragma unroll
-    for (int w = 0; w < RW; ++w)
+    for (int w = 0; w < RW; ++w) {
+      const int r = r0 + w;
+      if (CARRY) {
+        u[w][0] = lane < ncar ? car_code[r * kCarry + lane] : 0u;
+        cidx[w] = lane < ncar ? car_idx[r * kCarry + lane] : 0;
+      }
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
-        const int j = 64 * t + lane;
+        const int c = 64 * t + lane;
         // + 0.0f turns -0 into +0, so the two zeros tie as the values do
-        u[w][t] = (t < nt && j < i) ? ordered_bits(scores[(r0 + w) * nb + j] + 0.0f) : 0u;
+        u[w][t + C0] = (t < nt && c < nc) ? ordered_bits(scores[r * CH + c] + 0.0f) : 0u;
       }
+    }
     // codes of absent candidates are 0, below every threshold tried (>= 1)
     uint32_t th[RW];
     bool done[RW];
@@ -86,7 +106,7 @@ __device__ __forceinline__ void rank_rows(const float* scores, int32_t* out0, in
         const uint32_t c = th[w] | (1u << bit);
         int cnt = 0;
 #pragma unroll
-        for (int t = 0; t < TM; ++t) cnt += __popcll(__ballot(u[w][t] >= c));
+        for (int t = 0; t < S; ++t) cnt += __popcll(__ballot(u[w][t] >= c));
         th[w] = cnt >= keep ? c : th[w];
         done[w] = cnt == keep;
         all = all && done[w];
@@ -95,156 +115,64 @@ __device__ __forceinline__ void rank_rows(const float* scores, int32_t* out0, in
     }
 #pragma unroll
     for (int w = 0; w < RW; ++w) {
-      int32_t* out = out0 + static_cast<int64_t>(r0 + w) * K;
+      const int r = r0 + w;
+      int32_t* out = out0 + static_cast<int64_t>(r) * K;
       int need = keep;              // places left for codes equal to th
 #pragma unroll
-      for (int t = 0; t < TM; ++t) need -= __popcll(__ballot(u[w][t] > th[w]));
+      for (int t = 0; t < S; ++t) need -= __popcll(__ballot(u[w][t] > th[w]));
       int base = 0;
 #pragma unroll
-      for (int t = 0; t < TM; ++t) {
-        {
-          uint64_t eq = __ballot(u[w][t] == th[w]);
-          if (__popcll(eq) > need) {    // keep only the `need` lowest lanes
-            uint64_t take = 0;
-            for (int n = 0; n < need; ++n) {
-              const uint64_t low = eq & (~eq + 1);
-              take |= low;
-              eq ^= low;
-            }
-            eq = take;
+      for (int t = 0; t < S; ++t) {
+        uint64_t eq = __ballot(u[w][t] == th[w]);
+        if (__popcll(eq) > need) {    // keep only the `need` lowest lanes
+          uint64_t take = 0;
+          for (int n = 0; n < need; ++n) {
+            const uint64_t low = eq & (~eq + 1);
+            take |= low;
+            eq ^= low;
           }
-          need -= __popcll(eq);
-          const uint64_t won = __ballot(u[w][t] > th[w]) | eq;
-          if ((won >> lane) & 1) {
-            const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(won >> 32),
-                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(won), 0));
-            out[base + below] = 64 * t + lane;
-          }
-          base += __popcll(won);
+          eq = take;
         }
+        need -= __popcll(eq);
+        const uint64_t won = __ballot(u[w][t] > th[w]) | eq;
+        if ((won >> lane) & 1) {
+          const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(won >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(won), 0));
+          const int idx = (CARRY && t == 0) ? cidx[w] : c0 + 64 * (t - C0) + lane;
+          if (!CARRY || last) {
+            out[base + below] = idx;
+          } else {
+            car_code[r * kCarry + base + below] = u[w][t];
+            car_idx[r * kCarry + base + below] = idx;
+          }
+        }
+        base += __popcll(won);
       }
-      for (int slot = keep + lane; slot < K; slot += 64) out[slot] = (slot == keep) ? i : -1;
+      if (!CARRY || last)
+        for (int slot = keep + lane; slot < K; slot += 64) out[slot] = (slot == keep) ? i : -1;
     }
   }
 }
 
-
-// One workgroup (256 threads) per R rows of one query block (R divides the
-// block and R x nb fp32 scores fit in 64 KiB); the rows share the candidate
-// blocks j < i.
-//  1. Scores: candidates stream through in chunks of 64; each thread computes
-//     a tile of R/16 rows x 4 candidates (q . mu in fp32, sequential over the
-//     head dimension) into the row's score line in LDS.
-//  2. Ranking, in registers: lane l of a wave holds the scores of candidates
-//     l, l + 64, ..., l + 64 (TM - 1) of a row as order-preserving unsigned
-//     codes.  A 32-step bitwise search (one ballot and popcount per register
-//     per step) finds the largest code c with at least top_k - 1 candidates
-//     >= c: the (top_k - 1)-th largest score.  Every candidate above c is
-//     kept, and candidates equal to c fill the remaining places lowest index
-//     first.  Candidate order is (register, lane) = block order, so prefix
-//     counts of the ballots place the winners ascending.
-template <typename T, int TM>
-__global__ void __launch_bounds__(256) k_select(const T* __restrict__ q, const float* __restrict__ mu_all,
-                                                int32_t* __restrict__ sel, int Hq, int G, int Nq,
-                                                int q_off, int d, int block, int nb, int K, int R) {
-  // LDS: q rows [R][d + 4], candidate block means [64][d + 4], scores [R][nb]
-  extern __shared__ __attribute__((aligned(16))) float smem[];
-  const int dp = d + 4;
-  float* qs = smem;
-  float* mus = qs + R * dp;
-  float* scores = mus + kSelChunk * dp;
-  const int bh = blockIdx.y;
-  const int b = bh / Hq, h = bh % Hq;
-  const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
-  const int t0 = blockIdx.x * R;    // R divides block (and q_off), so all rows share i
-  const int i = (q_off + t0) / block;   // own block = number of candidates
-  const int keep = min(K - 1, i);
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const T* qrow0 = q + (static_cast<int64_t>(bh) * Nq + t0) * d;
-  int32_t* out0 = sel + (static_cast<int64_t>(bh) * Nq + t0) * K;
-
-  if (keep == i || keep == 0) {
-    // nothing to rank: every earlier block (keep == i) or none (top_k == 1)
-    for (int e = tid; e < R * K; e += blockDim.x) {
-      const int slot = e % K;
-      out0[e] = slot < keep ? slot : (slot == keep ? i : -1);
-    }
-    return;
-  }
-
-  for (int e = tid; e < R * d / 8; e += blockDim.x) {
-    const int r = (e * 8) / d, c0 = (e * 8) % d;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) qs[r * dp + c0 + u] = to_f32(qrow0[r * d + c0 + u]);
-  }
-
-  // ---- 1. scores
-  const float* mu = mu_all + bc * nb * d;
-  const int rpt = R >= 16 ? R >> 4 : 1;   // rows per scoring thread
-  const int rg = tid >> 4, cg = tid & 15;
-  for (int j0 = 0; j0 < i; j0 += kSelChunk) {
-    const int nc = min(kSelChunk, i - j0);
-    __syncthreads();                // q staged; previous chunk's means consumed
-    for (int e = tid; e < kSelChunk * d / 4; e += blockDim.x) {
-      const int cc = (e * 4) / d, dd = (e * 4) % d;
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (cc < nc) v = *reinterpret_cast<const float4*>(mu + static_cast<int64_t>(j0 + cc) * d + dd);
-      *reinterpret_cast<float4*>(mus + cc * dp + dd) = v;
-    }
-    __syncthreads();
-    if (rg * rpt < R) {
-      float acc[4][4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = 0.f;
-      for (int dd = 0; dd < d; dd += 4) {
-        float4 mv[4], qv[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) mv[c] = *reinterpret_cast<const float4*>(mus + (4 * cg + c) * dp + dd);
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-          if (a < rpt) qv[a] = *reinterpret_cast<const float4*>(qs + (rg * rpt + a) * dp + dd);
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          if (a < rpt) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              acc[a][c] = fmaf(qv[a].x, mv[c].x, acc[a][c]);
-              acc[a][c] = fmaf(qv[a].y, mv[c].y, acc[a][c]);
-              acc[a][c] = fmaf(qv[a].z, mv[c].z, acc[a][c]);
-              acc[a][c] = fmaf(qv[a].w, mv[c].w, acc[a][c]);
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-        if (a < rpt)
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-            if (4 * cg + c < nc) scores[(rg * rpt + a) * nb + j0 + 4 * cg + c] = acc[a][c];
-    }
-  }
-  __syncthreads();
-
-  rank_rows<TM>(scores, out0, R, nb, K, i, keep, lane, wave);
-}
-
-// Scores by fp32 matrix instructions (v_mfma_f32_32x32x2_f32), for up to
-// 1024 key blocks: one workgroup per R = 32 or 64 rows of one query block;
-// wave w computes the 32 x 32 score tiles (row tile w / CT, candidate tile
-// w % CT of each chunk of 32 CT candidates) with the rows' q (A operand:
-// lane (row l % 32, half g) holds d = (D/2) g .. (D/2) g + D/2 - 1) and the
-// candidates' block means (B operand, same split of d) in registers; the
-// scores go to LDS and the rows are ranked as above.  Products and sums are
-// fp32 (their order differs from a sequential dot product only by rounding).
-template <typename T, int TM, int D>
+// Scores by fp32 matrix instructions (v_mfma_f32_32x32x2_f32): one workgroup
+// per R = 32 or 64 rows of one query block (R divides the block, so the rows
+// share the candidate blocks j < i); wave w computes the 32 x 32 score tiles
+// (row tile w / CT, candidate tile w % CT of each pass over 32 CT
+// candidates) with the rows' q (A operand: lane (row l % 32, half g) holds
+// d = (D/2) g .. (D/2) g + D/2 - 1) and the candidates' block means (B
+// operand, same split of d) in registers, into the rows' score lines in LDS.
+// Candidates go in chunks of up to 1024: each chunk is scored, then ranked
+// with the winners carried from the earlier chunks (rank_chunk).  Products
+// and sums are fp32 (their order differs from a sequential dot product only
+// by rounding).
+template <typename T, int TM, int D, bool CARRY>
 __global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, const float* __restrict__ mu_all,
                                                      int32_t* __restrict__ sel, int Hq, int G, int Nq,
-                                                     int q_off, int block, int nb, int K, int R) {
-  extern __shared__ __attribute__((aligned(16))) float scores[];   // [R][nb]
+                                                     int q_off, int block, int nb, int K, int R, int CH) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  float* scores = smem;                                                   // [R][CH]
+  uint32_t* car_code = reinterpret_cast<uint32_t*>(smem + R * CH);       // [R][kCarry]
+  int32_t* car_idx = reinterpret_cast<int32_t*>(car_code + R * kCarry);  // [R][kCarry]
   const int bh = blockIdx.y;
   const int b = bh / Hq, h = bh % Hq;
   const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
@@ -277,96 +205,95 @@ __global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, co
     }
   }
   const float* mu = mu_all + bc * nb * D;
-  for (int c0 = 0; c0 < i; c0 += 32 * CT) {
-    const int tile0 = c0 + 32 * ct;
-    if (tile0 >= i) continue;                       // uniform
-    const int cand = tile0 + col;
-    const float* mr = mu + static_cast<int64_t>(min(cand, nb - 1)) * D + H * g;
-    f32x16 acc = f32x16{};
+  auto score_chunk = [&](int c0, int nc) {
+    for (int p0 = 0; p0 < nc; p0 += 32 * CT) {
+      const int tile0 = p0 + 32 * ct;
+      if (tile0 >= nc) continue;                    // uniform
+      const int cand = c0 + tile0 + col;
+      const float* mr = mu + static_cast<int64_t>(min(cand, nb - 1)) * D + H * g;
+      f32x16 acc = f32x16{};
 #pragma unroll
-    for (int k4 = 0; k4 < H; k4 += 4) {
-      const float4 m4 = *reinterpret_cast<const float4*>(mr + k4);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4], m4.x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4 + 1], m4.y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4 + 2], m4.z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4 + 3], m4.w, acc, 0, 0, 0);
+      for (int k4 = 0; k4 < H; k4 += 4) {
+        const float4 m4 = *reinterpret_cast<const float4*>(mr + k4);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4], m4.x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4 + 1], m4.y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4 + 2], m4.z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4 + 3], m4.w, acc, 0, 0, 0);
+      }
+      // lane (candidate col, g): register e is row 8 (e / 4) + 4 g + e % 4
+      if (tile0 + col < nc) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          scores[(32 * rt + 8 * (e >> 2) + 4 * g + (e & 3)) * CH + tile0 + col] = acc[e];
+      }
     }
-    // lane (candidate col, g): register e is row 8 (e / 4) + 4 g + e % 4
-    if (cand < i) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        scores[(32 * rt + 8 * (e >> 2) + 4 * g + (e & 3)) * nb + cand] = acc[e];
+    __syncthreads();
+  };
+  if constexpr (!CARRY) {
+    // every candidate in one chunk: q is dead once the scores are in LDS
+    score_chunk(0, i);
+    rank_chunk<TM, false>(scores, CH, 0, i, car_code, car_idx, 0, out0, R, K, i, keep, true, lane, wave);
+  } else {
+    int ncar = 0;
+    for (int c0 = 0; c0 < i; c0 += CH) {
+      const int nc = min(CH, i - c0);
+      if (c0 > 0) __syncthreads();                  // the previous chunk's scores consumed
+      score_chunk(c0, nc);
+      const bool last = c0 + CH >= i;
+      const int keep_now = min(K - 1, c0 + nc);   // winners among the candidates so far
+      rank_chunk<TM, true>(scores, CH, c0, nc, car_code, car_idx, ncar, out0, R, K, i, last ? keep : keep_now,
+                           last, lane, wave);
+      ncar = keep_now;
     }
   }
-  __syncthreads();
-  rank_rows<TM>(scores, out0, R, nb, K, i, keep, lane, wave);
 }
 
-// R rows per workgroup for the matrix-scored kernel (0: not applicable).
-static int mfma_rows(const Dims& D) {
-  if (D.block >= 64 && 64 * D.nb * 4 <= 64 * 1024) return 64;
-  if (32 * D.nb * 4 <= 128 * 1024) return 32;
-  return 0;
+// Rows per workgroup: 64 when a block holds them and their scores of every
+// candidate fit 64 KiB of LDS, else 32 (chunks of up to 1024 candidates).
+static int select_rows_per_wg(const Dims& D) {
+  return (D.block >= 64 && 64 * D.nb * 4 <= 64 * 1024) ? 64 : 32;
 }
 
-template <typename T, int TM, int DD>
+template <typename T, int TM, int DD, bool CARRY>
 static void launch_select_mfma(const Dims& D, int R, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
+  const int CH = D.nb < kCand ? D.nb : kCand;
   dim3 grid(D.Nq / R, D.B * D.Hq);
-  const size_t lds = static_cast<size_t>(R) * D.nb * sizeof(float);
+  // the carried winners need LDS only when the candidates span several chunks
+  const size_t lds = (static_cast<size_t>(R) * CH + (D.nb > CH ? 2 * static_cast<size_t>(R) * kCarry : 0)) *
+                     sizeof(float);
   static size_t granted = 0;     // above 64 KiB of LDS must be requested
   if (lds > granted) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_select_mfma<T, TM, DD>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_select_mfma<T, TM, DD, CARRY>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     granted = lds;
   }
-  hipLaunchKernelGGL((k_select_mfma<T, TM, DD>), grid, dim3(256), lds, s, static_cast<const T*>(q), mu, sel, D.Hq,
-                     D.G, D.Nq, D.q_off, D.block, D.nb, D.K, R);
+  hipLaunchKernelGGL((k_select_mfma<T, TM, DD, CARRY>), grid, dim3(256), lds, s, static_cast<const T*>(q), mu, sel, D.Hq,
+                     D.G, D.Nq, D.q_off, D.block, D.nb, D.K, R, CH);
 }
 
 template <typename T, int TM>
 static void launch_select_mfma_d(const Dims& D, int R, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
-  if (D.d == 64) launch_select_mfma<T, TM, 64>(D, R, q, mu, sel, s);
-  else launch_select_mfma<T, TM, 128>(D, R, q, mu, sel, s);
-}
-
-template <typename T, int TM>
-static void launch_select_tm(const Dims& D, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
-  int R = D.block < 64 ? D.block : 64;
-  while (R > 4 && static_cast<size_t>(R) * D.nb * sizeof(float) > 65536) R >>= 1;
-  dim3 grid(D.Nq / R, D.B * D.Hq);
-  const size_t lds =
-      (static_cast<size_t>(R + kSelChunk) * (D.d + 4) + static_cast<size_t>(R) * D.nb) * sizeof(float);
-  static size_t granted = 0;     // above 64 KiB of LDS must be requested
-  if (lds > granted) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_select<T, TM>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    granted = lds;
+  const bool carry = D.nb > kCand;          // candidates in several chunks
+  if (D.d == 64) {
+    if (carry) launch_select_mfma<T, TM, 64, true>(D, R, q, mu, sel, s);
+    else launch_select_mfma<T, TM, 64, false>(D, R, q, mu, sel, s);
+  } else {
+    if (carry) launch_select_mfma<T, TM, 128, true>(D, R, q, mu, sel, s);
+    else launch_select_mfma<T, TM, 128, false>(D, R, q, mu, sel, s);
   }
-  hipLaunchKernelGGL((k_select<T, TM>), grid, dim3(256), lds, s, static_cast<const T*>(q), mu, sel, D.Hq, D.G,
-                     D.Nq, D.q_off, D.d, D.block, D.nb, D.K, R);
 }
 
-// TM = registers per lane for a row's candidates: ceil(nb / 64), rounded up
-// to a power of two (nb <= 4096).
+// TM = registers per lane for a chunk's candidates: ceil(min(nb, 1024) / 64),
+// rounded up to a power of two.
 template <typename T>
 static void launch_select_t(const Dims& D, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
-  const int tm = (D.nb + 63) / 64;
-  const int R = mfma_rows(D);
-  if (R) {
-    if (tm <= 1) launch_select_mfma_d<T, 1>(D, R, q, mu, sel, s);
-    else if (tm <= 2) launch_select_mfma_d<T, 2>(D, R, q, mu, sel, s);
-    else if (tm <= 4) launch_select_mfma_d<T, 4>(D, R, q, mu, sel, s);
-    else if (tm <= 8) launch_select_mfma_d<T, 8>(D, R, q, mu, sel, s);
-    else launch_select_mfma_d<T, 16>(D, R, q, mu, sel, s);
-    return;
-  }
-  if (tm <= 1) launch_select_tm<T, 1>(D, q, mu, sel, s);
-  else if (tm <= 2) launch_select_tm<T, 2>(D, q, mu, sel, s);
-  else if (tm <= 4) launch_select_tm<T, 4>(D, q, mu, sel, s);
-  else if (tm <= 8) launch_select_tm<T, 8>(D, q, mu, sel, s);
-  else if (tm <= 16) launch_select_tm<T, 16>(D, q, mu, sel, s);
-  else if (tm <= 32) launch_select_tm<T, 32>(D, q, mu, sel, s);
-  else launch_select_tm<T, 64>(D, q, mu, sel, s);
+  const int tm = ((D.nb < kCand ? D.nb : kCand) + 63) / 64;
+  const int R = select_rows_per_wg(D);
+  if (tm <= 1) launch_select_mfma_d<T, 1>(D, R, q, mu, sel, s);
+  else if (tm <= 2) launch_select_mfma_d<T, 2>(D, R, q, mu, sel, s);
+  else if (tm <= 4) launch_select_mfma_d<T, 4>(D, R, q, mu, sel, s);
+  else if (tm <= 8) launch_select_mfma_d<T, 8>(D, R, q, mu, sel, s);
+  else launch_select_mfma_d<T, 16>(D, R, q, mu, sel, s);
 }
 
 void launch_select(const Dims& D, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
