@@ -147,10 +147,12 @@ def time_calls(fn, reps, warm=1):
 def hbm_rates(ssa, q, k, v, sel, wl, K, reps):
     """GB/s of the HBM-bound steps (a2 selection, a8 sparse-only forward)
     from the library's device-time events, against the 8 TB/s peak.  Bytes
-    are the compulsory ones: selection reads q and k, writes and reads the
-    block means and writes sel; the sparse-only forward reads q, k, v and sel,
-    writes h_sparse and lse_sparse, and writes and reads one partial (d bf16
-    values + an fp32 log-sum-exp) per selected (row, block)."""
+    are those each step must move: selection reads q and k, writes and reads
+    the block means and writes sel; the sparse-only forward reads k, v and
+    sel, gathers the query row of every selected (row, block) pair into its
+    key block's bucket (d bf16 values per pair), writes and reads one partial
+    per pair (d bf16 values + an fp32 log-sum-exp), and writes h_sparse and
+    lse_sparse."""
     B, Hq, N, d = q.shape
     blk, nb = wl.block, N // wl.block
     el = q.element_size()
@@ -170,7 +172,7 @@ def hbm_rates(ssa, q, k, v, sel, wl, K, reps):
     sel_bytes = q.numel() // d * K * 4
     b_sel = q.numel() * el + k.numel() * el + 2 * mu_bytes + sel_bytes
     entries = B * Hq * sum(min(K, t // blk + 1) for t in range(N))
-    b_sp = (q.numel() + k.numel() + v.numel()) * el + sel_bytes + q.numel() * el + q.numel() // d * 4 \
+    b_sp = (k.numel() + v.numel()) * el + sel_bytes + entries * d * el + q.numel() * el + q.numel() // d * 4 \
         + 2 * entries * (d * 2 + 4)
     return {"select_ms": round(ms_sel, 4), "select_GBps": round(b_sel / (ms_sel / 1e3) / 1e9, 1),
             "select_frac_of_hbm": round(b_sel / (ms_sel / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
