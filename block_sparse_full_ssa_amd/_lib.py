@@ -69,8 +69,7 @@ def lib() -> ctypes.CDLL:
         return _lib
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
-            "or `python block_sparse_full_ssa_amd/build.py` (hipcc, gfx950)")
+            f"{LIB_PATH} is missing: build it with `python block_sparse_full_ssa_amd/build.py` (hipcc, gfx950)")
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
     shp = ctypes.POINTER(ShapeT)
