@@ -12,6 +12,15 @@
       kernel, the bytes and the sha256 of the kernel's source so that a
       reader can tell when the figures no longer describe the code.
 
+  python -m block_sparse_full_ssa_amd.profile_summary mfma PMC STATS OUT.md TITLE
+      matrix-core use per kernel from one `--pmc MfmaUtil
+      SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE` pass: MfmaUtil (the
+      matrix pipes' busy cycles summed over the SIMDs over active cycles
+      times the SIMD count), the bf16 matrix flops the kernel executed (MOPS
+      x 512, the implemented work), and the clock the GPU ran at
+      (GRBM_GUI_ACTIVE per XCD over the kernel's average duration in the
+      stats run STATS).
+
 Commands are stated in the written summaries; this module only reads CSVs.
 """
 from __future__ import annotations
@@ -104,11 +113,34 @@ def traffic(fd, wd, cfd, cwd, out_md, out_json, workload, top_k, title) -> None:
         f.write("\n")
 
 
+def mfma(pd: str, sd: str, out: str, title: str, n_xcd: int = 8) -> None:
+    pmc = counters(pd)
+    files = glob.glob(os.path.join(sd, "**", "*kernel_stats.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no kernel_stats.csv under {sd}")
+    avg_ns = {short(r["Name"]): float(r["AverageNs"]) for r in csv.DictReader(open(files[0]))}
+    rows = [(k, cs) for k, cs in pmc.items() if k.startswith("k_") and cs.get("MfmaUtil", 0.0) > 0.0]
+    rows.sort(key=lambda kc: -kc[1].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0))
+    lines = []
+    for k, cs in rows:
+        flops = cs.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
+        ns = avg_ns.get(k)
+        clock = f"{cs.get('GRBM_GUI_ACTIVE', 0.0) / n_xcd / ns:.2f}" if ns else "-"
+        rate = f"{flops / ns / 1e3:.0f}" if ns and flops else "-"
+        lines.append(f"| `{k}` | {cs['MfmaUtil']:.1f} | {flops:.3g} | {rate} | {clock} |")
+    with open(out, "w") as f:
+        f.write(title.rstrip() + "\n\n| kernel | MfmaUtil % | bf16 matrix flops per launch | TFLOP/s (avg duration) "
+                "| clock GHz |\n|---|---|---|---|---|\n")
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     a = sys.argv[1:]
     if a and a[0] == "stats" and len(a) == 4:
         stats(a[1], a[2], a[3])
     elif a and a[0] == "traffic" and len(a) == 10:
         traffic(*a[1:8], int(a[8]), a[9])
+    elif a and a[0] == "mfma" and len(a) == 5:
+        mfma(a[1], a[2], a[3], a[4])
     else:
         raise SystemExit(__doc__)
