@@ -96,8 +96,11 @@ typedef struct {
 } ssa_shape_t;
 
 /* Bytes of workspace that ``op`` needs for ``shape`` in ``mode`` (0 on an
- * invalid shape).  A workspace of this size may be reused across calls that
- * are ordered on one stream. */
+ * invalid shape, or when the op needs none).  SSA_OP_SELECT / _FWD / _BWD
+ * size the layer entry points; SSA_OP_DECODE sizes ssa_decode for a cache
+ * of capacity shape->seqlen (modes SSA_FULL_ONLY and SSA_SPARSE_ONLY only).
+ * A prefill chunk is sized by ssa_prefill_workspace_size.  A workspace of
+ * this size may be reused across calls that are ordered on one stream. */
 size_t ssa_workspace_size(const ssa_shape_t* shape, int32_t mode, int32_t op);
 
 /*
