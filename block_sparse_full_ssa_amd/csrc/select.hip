@@ -48,7 +48,8 @@ void launch_block_mean(const Dims& D, const void* k, float* mu, hipStream_t s) {
   timing_end(kKBlockMean, s);
 }
 
-constexpr int kCand = 1024;       // candidates scored and ranked per chunk
+constexpr int kCand = 256;        // candidates scored and ranked per chunk
+constexpr int kRows = 32;         // query rows per workgroup (divides every block size)
 constexpr int kCarry = 64;        // carried winners per row (top_k <= 64 here)
 
 // Ranking of R rows over one chunk of candidates (scores[r * CH + c] for the
@@ -65,7 +66,7 @@ template <int TM, bool CARRY>
 __device__ __forceinline__ void rank_chunk(const float* scores, int CH, int c0, int nc, uint32_t* car_code,
                                            int32_t* car_idx, int ncar, int32_t* out0, int R, int K, int i, int keep,
                                            bool last, int lane, int wave) {
-  constexpr int RW = TM <= 8 ? 2 : 1;
+  constexpr int RW = 2;             // rows ranked together per wave
   constexpr int C0 = CARRY ? 1 : 0;  // first candidate slot
   constexpr int S = TM + C0;        // register slots: (carried +) candidates
   const int nt = (nc + 63) >> 6;    // candidate registers in use
@@ -155,16 +156,18 @@ __device__ __forceinline__ void rank_chunk(const float* scores, int CH, int c0, 
 }
 
 // Scores by fp32 matrix instructions (v_mfma_f32_32x32x2_f32): one workgroup
-// per R = 32 or 64 rows of one query block (R divides the block, so the rows
-// share the candidate blocks j < i); wave w computes the 32 x 32 score tiles
-// (row tile w / CT, candidate tile w % CT of each pass over 32 CT
-// candidates) with the rows' q (A operand: lane (row l % 32, half g) holds
-// d = (D/2) g .. (D/2) g + D/2 - 1) and the candidates' block means (B
-// operand, same split of d) in registers, into the rows' score lines in LDS.
-// Candidates go in chunks of up to 1024: each chunk is scored, then ranked
-// with the winners carried from the earlier chunks (rank_chunk).  Products
-// and sums are fp32 (their order differs from a sequential dot product only
-// by rounding).
+// per R = 32 rows of one query block (R divides the block, so the rows share
+// the candidate blocks j < i); wave w computes the 32 x 32 score tiles of
+// candidate tile w of each pass over 128 candidates, with the rows' q (A
+// operand: lane (row l % 32, half g) holds d = (D/2) g .. (D/2) g + D/2 - 1)
+// and the candidates' block means (B operand, same split of d) in
+// registers, into the rows' score lines in LDS.  Candidates go in chunks of
+// up to 256: each chunk is scored, then ranked with the winners carried
+// from the earlier chunks (rank_chunk).  Small chunks keep the LDS per
+// workgroup at 48 KiB (three workgroups per CU) and the ranking's registers
+// few; longer chunks measured slower at every length tried.  Products and
+// sums are fp32 (their order differs from a sequential dot product only by
+// rounding).
 template <typename T, int TM, int D, bool CARRY>
 __global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, const float* __restrict__ mu_all,
                                                      int32_t* __restrict__ sel, int Hq, int G, int Nq,
@@ -248,25 +251,14 @@ __global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, co
   }
 }
 
-// Rows per workgroup: 64 when a block holds them and their scores of every
-// candidate fit 64 KiB of LDS, else 32 (chunks of up to 1024 candidates).
-static int select_rows_per_wg(const Dims& D) {
-  return (D.block >= 64 && 64 * D.nb * 4 <= 64 * 1024) ? 64 : 32;
-}
-
 template <typename T, int TM, int DD, bool CARRY>
 static void launch_select_mfma(const Dims& D, int R, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
   const int CH = D.nb < kCand ? D.nb : kCand;
   dim3 grid(D.Nq / R, D.B * D.Hq);
   // the carried winners need LDS only when the candidates span several chunks
+  // (at most 32 KiB of scores + 16 KiB of winners)
   const size_t lds = (static_cast<size_t>(R) * CH + (D.nb > CH ? 2 * static_cast<size_t>(R) * kCarry : 0)) *
                      sizeof(float);
-  static size_t granted = 0;     // above 64 KiB of LDS must be requested
-  if (lds > granted) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_select_mfma<T, TM, DD, CARRY>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    granted = lds;
-  }
   hipLaunchKernelGGL((k_select_mfma<T, TM, DD, CARRY>), grid, dim3(256), lds, s, static_cast<const T*>(q), mu, sel, D.Hq,
                      D.G, D.Nq, D.q_off, D.block, D.nb, D.K, R, CH);
 }
@@ -283,17 +275,14 @@ static void launch_select_mfma_d(const Dims& D, int R, const void* q, const floa
   }
 }
 
-// TM = registers per lane for a chunk's candidates: ceil(min(nb, 1024) / 64),
+// TM = registers per lane for a chunk's candidates: ceil(min(nb, 256) / 64),
 // rounded up to a power of two.
 template <typename T>
 static void launch_select_t(const Dims& D, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
   const int tm = ((D.nb < kCand ? D.nb : kCand) + 63) / 64;
-  const int R = select_rows_per_wg(D);
-  if (tm <= 1) launch_select_mfma_d<T, 1>(D, R, q, mu, sel, s);
-  else if (tm <= 2) launch_select_mfma_d<T, 2>(D, R, q, mu, sel, s);
-  else if (tm <= 4) launch_select_mfma_d<T, 4>(D, R, q, mu, sel, s);
-  else if (tm <= 8) launch_select_mfma_d<T, 8>(D, R, q, mu, sel, s);
-  else launch_select_mfma_d<T, 16>(D, R, q, mu, sel, s);
+  if (tm <= 1) launch_select_mfma_d<T, 1>(D, kRows, q, mu, sel, s);
+  else if (tm <= 2) launch_select_mfma_d<T, 2>(D, kRows, q, mu, sel, s);
+  else launch_select_mfma_d<T, 4>(D, kRows, q, mu, sel, s);
 }
 
 void launch_select(const Dims& D, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
