@@ -103,9 +103,9 @@ __global__ void __launch_bounds__(256, 2)
   };
 
   // bucket mask word and entry base of the wave's queries for each half of a
-  // tile (uniform), one tile ahead
-  uint32_t mw[2] = {0u, 0u}, mwn[2] = {0u, 0u};
-  int mp[2] = {0, 0}, mpn[2] = {0, 0};
+  // tile (uniform): the current tile's, the next one's and the one after
+  uint32_t mw[2] = {0u, 0u}, mwn[2] = {0u, 0u}, mwn2[2] = {0u, 0u};
+  int mp[2] = {0, 0}, mpn[2] = {0, 0}, mpn2[2] = {0, 0};
   // (vector loads on purpose: a scalar load in flight would turn every wait
   // for an LDS operand into a wait for all of them)
   auto mask_words = [&](int j, uint32_t* m, int* p) {
@@ -123,14 +123,33 @@ __global__ void __launch_bounds__(256, 2)
       }
     }
   };
+  // The sparse stream's dS of one half (keys jj*64 + 32 kh ..) for the
+  // lanes whose queries selected its block, zero elsewhere.  Loads run one
+  // half ahead of their use: the rows of a tile's second half are fetched
+  // at its first half and those of the next tile's first half at the second.
+  uint4 sdc[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)}, sdx[2] = {sdc[0], sdc[1]};
+  auto load_sd = [&](int jj, int kh, uint32_t mword, int mpos, uint4* dst) {
+    dst[0] = dst[1] = make_uint4(0, 0, 0, 0);
+    const int kbase = jj * kBN + kh * 32;
+    const uint32_t m = __builtin_amdgcn_readfirstlane(mword);
+    if (wave_live && jj <= j_last && kbase <= wave_last_q && m != 0u && ((m >> col) & 1u)) {
+      const int blk = kbase / block;
+      const int e = __builtin_amdgcn_readfirstlane(mpos) + __builtin_popcount(m & ((1u << col) - 1u));
+      const uint16_t* src = a.ds_rows + static_cast<int64_t>(e) * block + (kbase - blk * block) + 16 * g;
+      dst[0] = *reinterpret_cast<const uint4*>(src);
+      dst[1] = *reinterpret_cast<const uint4*>(src + 8);
+    }
+  };
   auto step = [&](int j, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn) {
     if constexpr (SPARSE) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         mw[kh] = mwn[kh];
         mp[kh] = mpn[kh];
+        mwn[kh] = mwn2[kh];
+        mpn[kh] = mpn2[kh];
       }
-      if (j + 1 <= j_last) mask_words(j + 1, mwn, mpn);
+      if (j + 2 <= j_last) mask_words(j + 2, mwn2, mpn2);
     }
     if (j + 1 <= j_last) load_tile(j + 1, Kn, Vn);
     if (wave_live && j * kBN <= wave_last_q) {
@@ -138,17 +157,16 @@ __global__ void __launch_bounds__(256, 2)
       for (int kh = 0; kh < 2; ++kh) {
         const int kbase = j * kBN + kh * 32;
         if (kbase > wave_last_q) break;                // uniform: later keys are all masked
-        // the sparse stream's dS of this half for the queries that selected its block
-        uint4 sd0 = make_uint4(0, 0, 0, 0), sd1 = sd0;
         if constexpr (SPARSE) {
-          const int blk = kbase / block;                 // uniform
-          const uint32_t m = __builtin_amdgcn_readfirstlane(mw[kh]);
-          if (m != 0u && ((m >> col) & 1u)) {
-            const int e = __builtin_amdgcn_readfirstlane(mp[kh]) + __builtin_popcount(m & ((1u << col) - 1u));
-            const uint16_t* src = a.ds_rows + static_cast<int64_t>(e) * block + (kbase - blk * block) + 16 * g;
-            sd0 = *reinterpret_cast<const uint4*>(src);
-            sd1 = *reinterpret_cast<const uint4*>(src + 8);
-          }
+          // this half's rows were fetched one half earlier; a wait for a
+          // register load while tile copies are in flight waits for those
+          // copies too, so the second half takes one wait for everything
+          // before it fetches the next tile's first half
+          if (kh == 1) __builtin_amdgcn_s_waitcnt(0);
+          sdc[0] = sdx[0];
+          sdc[1] = sdx[1];
+          if (kh == 0) load_sd(j, 1, mw[1], mp[1], sdx);
+          else load_sd(j + 1, 0, mwn[0], mpn[0], sdx);
         }
         // ---- S^T = K Q^T, dP^T = V G^T for 32 keys (A: key row kh*32 + col)
         f32x16 s = f32x16{}, dp = f32x16{};
@@ -176,6 +194,7 @@ __global__ void __launch_bounds__(256, 2)
         // being the key of register i; it is zero wherever the mask is)
         float dsv[16];
         {
+          const uint4 sd0 = sdc[0], sd1 = sdc[1];
           const uint32_t sw[8] = {sd0.x, sd0.y, sd0.z, sd0.w, sd1.x, sd1.y, sd1.z, sd1.w};
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
@@ -216,7 +235,12 @@ __global__ void __launch_bounds__(256, 2)
     __syncthreads();
   };
 
-  if constexpr (SPARSE) mask_words(0, mwn, mpn);
+  if constexpr (SPARSE) {
+    mask_words(0, mwn, mpn);
+    if (1 <= j_last) mask_words(1, mwn2, mpn2);
+    __builtin_amdgcn_s_waitcnt(0);
+    load_sd(0, 0, mwn[0], mpn[0], sdx);
+  }
   load_tile(0, K0, V0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
