@@ -162,13 +162,13 @@ def test_train_layer_16k_full_size():
     assert np.all(np.abs(sum_dk) <= 2 ** -7 * abs_dk + 1e-6), np.abs(sum_dk).max()
 
 
-# ------------------------------------------------ selection beyond 1024 blocks --
+# ----------------------------------------------------- selection, many blocks --
 
 @pytest.mark.parametrize("block, nb, top_k, d", [(32, 1100, 8, 64), (64, 4096, 16, 128)])
 def test_select_many_blocks(block, nb, top_k, d):
-    """More than 1024 key blocks (up to the supported 4096) take the
-    FMA-scored selection kernel instead of the matrix-scored one: sampled rows
-    against the oracle, margin-aware as above."""
+    """1100 and 4096 key blocks (the supported maximum): five and sixteen
+    chunks of candidates with carried winners; sampled rows against the
+    oracle, margin-aware as above."""
     wl = si.scaled_down(si.WORKLOADS["gqa_n4k_fwd"], seqlen=block * nb, hq=1, hkv=1, block=block,
                         top_k=top_k, head_dim=d)
     _say(f"select nb {nb} block {block} d {d}: draw")
