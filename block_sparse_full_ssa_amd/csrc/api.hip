@@ -197,20 +197,25 @@ static DecodeWs carve_decode(const Dims& D, int mode, Carver& c) {
 
 static size_t ws_need(const Dims& D, int mode, int op) {
   Carver c{nullptr};
-  if (op == SSA_OP_SELECT) c.take<float>(static_cast<size_t>(D.B) * D.Hkv * D.d * D.nb * sizeof(float));
-  else if (op == SSA_OP_FWD) carve_fwd(D, mode, c);
+  if (op == SSA_OP_SELECT) {
+    c.take<float>(static_cast<size_t>(D.B) * D.Hkv * D.d * D.nb * sizeof(float));
+    c.take<uint16_t>(select_split_bytes(D));
+  } else if (op == SSA_OP_FWD) carve_fwd(D, mode, c);
   else if (op == SSA_OP_DECODE) carve_decode(D, mode, c);
   else carve_bwd(D, mode, c);
   return c.used;
 }
 
-static ssa_status_t check_ws(const Dims& D, int mode, int op, void* ws, size_t ws_bytes) {
-  const size_t need = ws_need(D, mode, op);
+static ssa_status_t check_ws_bytes(size_t need, void* ws, size_t ws_bytes) {
   if (need == 0) return SSA_OK;
   if (!ws) return fail(SSA_ERR_NULL, "workspace is NULL%s");
   if (ws_bytes < need) return fail(SSA_ERR_WORKSPACE, "workspace too small%s");
   if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(SSA_ERR_WORKSPACE, "workspace not 256-byte aligned%s");
   return SSA_OK;
+}
+
+static ssa_status_t check_ws(const Dims& D, int mode, int op, void* ws, size_t ws_bytes) {
+  return check_ws_bytes(ws_need(D, mode, op), ws, ws_bytes);
 }
 
 static ssa_status_t launch_status() {
@@ -241,10 +246,12 @@ ssa_status_t ssa_select_blocks(const ssa_shape_t* shape, const void* q, const vo
   if (!q || !k || !sel) return fail(SSA_ERR_NULL, "q, k and sel are required%s");
   if ((st = check_ws(D, 0, SSA_OP_SELECT, ws, ws_bytes)) != SSA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* mu = static_cast<float*>(ws);
+  Carver c{static_cast<char*>(ws)};
+  float* mu = c.take<float>(static_cast<size_t>(D.B) * D.Hkv * D.d * D.nb * sizeof(float));
+  uint16_t* split = c.take<uint16_t>(select_split_bytes(D));
   launch_block_mean(D, k, mu, s);
   if ((st = launch_status()) != SSA_OK) return st;
-  launch_select(D, q, mu, sel, s);
+  launch_select(D, q, mu, split, sel, s);
   return launch_status();
 }
 
@@ -434,6 +441,13 @@ static ssa_status_t prefill_dims(const ssa_shape_t* shape, int32_t mode, int32_t
   D->q_off = pos0;
   return SSA_OK;
 }
+
+// A sparse chunk also selects against the cache's means: the layer forward's
+// workspace plus the split of the means.
+static size_t prefill_need(const Dims& D, int32_t mode) {
+  const size_t fwd = ws_need(D, mode, SSA_OP_FWD);
+  return mode == kSparseOnly ? fwd + align256(select_split_bytes(D)) : fwd;
+}
 }  // namespace ssa
 
 extern "C" {
@@ -444,7 +458,7 @@ size_t ssa_prefill_workspace_size(const ssa_shape_t* shape, int32_t mode, int32_
     g_last_error.clear();
     return 0;
   }
-  return ws_need(D, mode, SSA_OP_FWD);
+  return prefill_need(D, mode);
 }
 
 ssa_status_t ssa_prefill(const ssa_shape_t* shape, int32_t mode, const void* q, int32_t pos0, int32_t chunk,
@@ -456,7 +470,7 @@ ssa_status_t ssa_prefill(const ssa_shape_t* shape, int32_t mode, const void* q, 
   if (st != SSA_OK) return st;
   if (!q || !k_cache || !v_cache || !h) return fail(SSA_ERR_NULL, "q, k_cache, v_cache and h are required%s");
   if (mode == kSparseOnly && (!mu_cache || !sel)) return fail(SSA_ERR_NULL, "mu_cache and sel are required%s");
-  if ((st = check_ws(D, mode, SSA_OP_FWD, ws, ws_bytes)) != SSA_OK) return st;
+  if ((st = check_ws_bytes(prefill_need(D, mode), ws, ws_bytes)) != SSA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (mode == kFullOnly) {
     FwdArgs a{q, k_cache, v_cache, nullptr, h, nullptr, lse, nullptr, nullptr, nullptr, kFullOnly};
@@ -465,7 +479,8 @@ ssa_status_t ssa_prefill(const ssa_shape_t* shape, int32_t mode, const void* q, 
   }
   Carver c{static_cast<char*>(ws)};
   FwdWs w = carve_fwd(D, mode, c);
-  launch_select(D, q, mu_cache, sel, s);
+  uint16_t* split = c.take<uint16_t>(select_split_bytes(D));
+  launch_select(D, q, mu_cache, split, sel, s);
   if ((st = launch_status()) != SSA_OK) return st;
   launch_buckets(D, sel, w.bk, s);
   if ((st = launch_status()) != SSA_OK) return st;

@@ -53,7 +53,10 @@ void timing_end(int kernel, hipStream_t s);
 
 // --- selection (select.hip) ---
 void launch_block_mean(const Dims& D, const void* k, float* mu, hipStream_t s);
-void launch_select(const Dims& D, const void* q, const float* mu, int32_t* sel, hipStream_t s);
+// split: select_split_bytes(D) of workspace (bf16 layers: the two-term bf16
+// split of the means that the matrix scoring reads).
+size_t select_split_bytes(const Dims& D);
+void launch_select(const Dims& D, const void* q, const float* mu, uint16_t* split, int32_t* sel, hipStream_t s);
 
 // --- generic SIMT kernels (simt.hip): every supported shape, fp32 and bf16 ---
 struct FwdArgs {

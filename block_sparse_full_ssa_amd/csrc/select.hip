@@ -7,14 +7,15 @@
 // block, and takes the top_k - 1 best earlier blocks, the lower index winning
 // a tie.  sel rows are written ascending, padded with -1.
 //
-// Two kernels:
-//   block_mean: mean of each key block, fp32, [B*Hkv][nb][d];
-//   select:     one workgroup per (head, 32 or 64 rows of one query block);
-//               candidate scores are computed into LDS by fp32 matrix
-//               instructions, up to 1024 candidates at a time, and a wave
-//               ranks each row by a bitwise threshold search (see below),
-//               carrying a row's winners from one chunk of candidates into
-//               the next.
+// Kernels:
+//   block_mean:  mean of each key block, fp32, [B*Hkv][nb][d];
+//   split_means: (bf16 layers) each mean as the sum of two bf16 numbers;
+//   select:      one workgroup per (head, 32 rows of one query block);
+//                candidate scores are computed into LDS by matrix
+//                instructions, up to 256 candidates at a time, and a wave
+//                ranks each row by a bitwise threshold search (see below),
+//                carrying a row's winners from one chunk of candidates into
+//                the next.
 
 #include "common.h"
 #include "internal.h"
@@ -46,6 +47,23 @@ void launch_block_mean(const Dims& D, const void* k, float* mu, hipStream_t s) {
     hipLaunchKernelGGL(k_block_mean<float>, grid, dim3(128), 0, s,
                        static_cast<const float*>(k), mu, D.N, D.d, D.block, D.nb);
   timing_end(kKBlockMean, s);
+}
+
+// Two-term bf16 split of the block means for bf16 layers: hi = bf16(mu),
+// lo = bf16(mu - hi).  mu - hi is exact in fp32 and lo rounds it to 8 bits,
+// so |mu - hi - lo| <= 2^-18 |mu|: the bf16 matrix products q.hi + q.lo
+// (exact products, fp32 sums) give the fp32 score up to that error.
+__global__ void __launch_bounds__(256) k_split_means(const float4* __restrict__ mu, uint2* __restrict__ hi,
+                                                     uint2* __restrict__ lo, int64_t n4) {
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n4;
+       e += static_cast<int64_t>(gridDim.x) * 256) {
+    const float4 m = mu[e];
+    const uint2 h = make_uint2(pack_bf16x2(m.x, m.y), pack_bf16x2(m.z, m.w));
+    const float hx = __uint_as_float(h.x << 16), hy = __uint_as_float(h.x & 0xffff0000u);
+    const float hz = __uint_as_float(h.y << 16), hw = __uint_as_float(h.y & 0xffff0000u);
+    hi[e] = h;
+    lo[e] = make_uint2(pack_bf16x2(m.x - hx, m.y - hy), pack_bf16x2(m.z - hz, m.w - hw));
+  }
 }
 
 constexpr int kCand = 256;        // candidates scored and ranked per chunk
@@ -155,13 +173,16 @@ __device__ __forceinline__ void rank_chunk(const float* scores, int CH, int c0, 
   }
 }
 
-// Scores by fp32 matrix instructions (v_mfma_f32_32x32x2_f32): one workgroup
-// per R = 32 rows of one query block (R divides the block, so the rows share
-// the candidate blocks j < i); wave w computes the 32 x 32 score tiles of
-// candidate tile w of each pass over 128 candidates, with the rows' q (A
-// operand: lane (row l % 32, half g) holds d = (D/2) g .. (D/2) g + D/2 - 1)
-// and the candidates' block means (B operand, same split of d) in
-// registers, into the rows' score lines in LDS.  Candidates go in chunks of
+// Scores by matrix instructions: one workgroup per R = 32 rows of one query
+// block (R divides the block, so the rows share the candidate blocks j < i);
+// wave w computes the 32 x 32 score tiles of candidate tile w of each pass
+// over 128 candidates, with the rows' q as the A operand (in registers) and
+// the candidates' block means as the B operand, into the rows' score lines
+// in LDS.  bf16 layers: v_mfma_f32_32x32x16_bf16 on q (exact) and the two
+// bf16 terms of each mean, into two accumulators added at the end (lane (row
+// l % 32, half g) holds d = 16 s + 8 g .. +7 of step s).  fp32 layers:
+// v_mfma_f32_32x32x2_f32 with lane (row l % 32, half g) holding d = (D/2) g
+// .. (D/2) g + D/2 - 1.  Candidates go in chunks of
 // up to 256: each chunk is scored, then ranked with the winners carried
 // from the earlier chunks (rank_chunk).  Small chunks keep the LDS per
 // workgroup at 48 KiB (three workgroups per CU) and the ranking's registers
@@ -170,8 +191,11 @@ __device__ __forceinline__ void rank_chunk(const float* scores, int CH, int c0, 
 // rounding).
 template <typename T, int TM, int D, bool CARRY>
 __global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, const float* __restrict__ mu_all,
-                                                     int32_t* __restrict__ sel, int Hq, int G, int Nq,
-                                                     int q_off, int block, int nb, int K, int R, int CH) {
+                                                     const uint16_t* __restrict__ mu_hi,
+                                                     const uint16_t* __restrict__ mu_lo, int32_t* __restrict__ sel,
+                                                     int Hq, int G, int Nq, int q_off, int block, int nb, int K,
+                                                     int R, int CH) {
+  constexpr bool kBf = sizeof(T) == 2;
   extern __shared__ __attribute__((aligned(16))) float smem[];
   float* scores = smem;                                                   // [R][CH]
   uint32_t* car_code = reinterpret_cast<uint32_t*>(smem + R * CH);       // [R][kCarry]
@@ -197,14 +221,19 @@ __global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, co
   const int rt = wave / CT, ct = wave % CT;
   const int g = lane >> 5, col = lane & 31;
   constexpr int H = D / 2;
-  // A operand: row 32 rt + col, d = H g + k
-  float qa[H];
+  // A operand of row 32 rt + col: bf16, d = 16 s + 8 g .. +7 in qb[s]; fp32,
+  // d = H g + k in qa[k]
+  float qa[kBf ? 1 : H];
+  bf16x8 qb[kBf ? D / 16 : 1];
   {
-    const T* qr = q + (static_cast<int64_t>(bh) * Nq + t0 + 32 * rt + col) * D + H * g;
+    const T* qr = q + (static_cast<int64_t>(bh) * Nq + t0 + 32 * rt + col) * D;
+    if constexpr (kBf) {
 #pragma unroll
-    for (int k8 = 0; k8 < H; k8 += 8) {
+      for (int s = 0; s < D / 16; ++s)
+        qb[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qr + 16 * s + 8 * g));
+    } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) qa[k8 + e] = to_f32(qr[k8 + e]);
+      for (int k = 0; k < H; ++k) qa[k] = to_f32(qr[H * g + k]);
     }
   }
   const float* mu = mu_all + bc * nb * D;
@@ -213,15 +242,30 @@ __global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, co
       const int tile0 = p0 + 32 * ct;
       if (tile0 >= nc) continue;                    // uniform
       const int cand = c0 + tile0 + col;
-      const float* mr = mu + static_cast<int64_t>(min(cand, nb - 1)) * D + H * g;
+      const int64_t mrow = (bc * nb + min(cand, nb - 1)) * D;
       f32x16 acc = f32x16{};
+      if constexpr (kBf) {
+        const uint16_t* mh = mu_hi + mrow + 8 * g;
+        const uint16_t* ml = mu_lo + mrow + 8 * g;
+        f32x16 acc_lo = f32x16{};
 #pragma unroll
-      for (int k4 = 0; k4 < H; k4 += 4) {
-        const float4 m4 = *reinterpret_cast<const float4*>(mr + k4);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4], m4.x, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4 + 1], m4.y, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4 + 2], m4.z, acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4 + 3], m4.w, acc, 0, 0, 0);
+        for (int s = 0; s < D / 16; ++s) {
+          acc = mfma32x32x16(qb[s], __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(mh + 16 * s)), acc);
+          acc_lo = mfma32x32x16(qb[s], __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ml + 16 * s)),
+                                acc_lo);
+        }
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[e] += acc_lo[e];
+      } else {
+        const float* mr = mu_all + mrow + H * g;
+#pragma unroll
+        for (int k4 = 0; k4 < H; k4 += 4) {
+          const float4 m4 = *reinterpret_cast<const float4*>(mr + k4);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4], m4.x, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4 + 1], m4.y, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4 + 2], m4.z, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[k4 + 3], m4.w, acc, 0, 0, 0);
+        }
       }
       // lane (candidate col, g): register e is row 8 (e / 4) + 4 g + e % 4
       if (tile0 + col < nc) {
@@ -252,43 +296,60 @@ __global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, co
 }
 
 template <typename T, int TM, int DD, bool CARRY>
-static void launch_select_mfma(const Dims& D, int R, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
+static void launch_select_mfma(const Dims& D, int R, const void* q, const float* mu, const uint16_t* mu_hi,
+                               const uint16_t* mu_lo, int32_t* sel, hipStream_t s) {
   const int CH = D.nb < kCand ? D.nb : kCand;
   dim3 grid(D.Nq / R, D.B * D.Hq);
   // the carried winners need LDS only when the candidates span several chunks
   // (at most 32 KiB of scores + 16 KiB of winners)
   const size_t lds = (static_cast<size_t>(R) * CH + (D.nb > CH ? 2 * static_cast<size_t>(R) * kCarry : 0)) *
                      sizeof(float);
-  hipLaunchKernelGGL((k_select_mfma<T, TM, DD, CARRY>), grid, dim3(256), lds, s, static_cast<const T*>(q), mu, sel, D.Hq,
-                     D.G, D.Nq, D.q_off, D.block, D.nb, D.K, R, CH);
+  hipLaunchKernelGGL((k_select_mfma<T, TM, DD, CARRY>), grid, dim3(256), lds, s, static_cast<const T*>(q), mu, mu_hi,
+                     mu_lo, sel, D.Hq, D.G, D.Nq, D.q_off, D.block, D.nb, D.K, R, CH);
 }
 
 template <typename T, int TM>
-static void launch_select_mfma_d(const Dims& D, int R, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
+static void launch_select_mfma_d(const Dims& D, int R, const void* q, const float* mu, const uint16_t* mu_hi,
+                                 const uint16_t* mu_lo, int32_t* sel, hipStream_t s) {
   const bool carry = D.nb > kCand;          // candidates in several chunks
   if (D.d == 64) {
-    if (carry) launch_select_mfma<T, TM, 64, true>(D, R, q, mu, sel, s);
-    else launch_select_mfma<T, TM, 64, false>(D, R, q, mu, sel, s);
+    if (carry) launch_select_mfma<T, TM, 64, true>(D, R, q, mu, mu_hi, mu_lo, sel, s);
+    else launch_select_mfma<T, TM, 64, false>(D, R, q, mu, mu_hi, mu_lo, sel, s);
   } else {
-    if (carry) launch_select_mfma<T, TM, 128, true>(D, R, q, mu, sel, s);
-    else launch_select_mfma<T, TM, 128, false>(D, R, q, mu, sel, s);
+    if (carry) launch_select_mfma<T, TM, 128, true>(D, R, q, mu, mu_hi, mu_lo, sel, s);
+    else launch_select_mfma<T, TM, 128, false>(D, R, q, mu, mu_hi, mu_lo, sel, s);
   }
 }
 
 // TM = registers per lane for a chunk's candidates: ceil(min(nb, 256) / 64),
 // rounded up to a power of two.
 template <typename T>
-static void launch_select_t(const Dims& D, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
+static void launch_select_t(const Dims& D, const void* q, const float* mu, const uint16_t* mu_hi,
+                            const uint16_t* mu_lo, int32_t* sel, hipStream_t s) {
   const int tm = ((D.nb < kCand ? D.nb : kCand) + 63) / 64;
-  if (tm <= 1) launch_select_mfma_d<T, 1>(D, kRows, q, mu, sel, s);
-  else if (tm <= 2) launch_select_mfma_d<T, 2>(D, kRows, q, mu, sel, s);
-  else launch_select_mfma_d<T, 4>(D, kRows, q, mu, sel, s);
+  if (tm <= 1) launch_select_mfma_d<T, 1>(D, kRows, q, mu, mu_hi, mu_lo, sel, s);
+  else if (tm <= 2) launch_select_mfma_d<T, 2>(D, kRows, q, mu, mu_hi, mu_lo, sel, s);
+  else launch_select_mfma_d<T, 4>(D, kRows, q, mu, mu_hi, mu_lo, sel, s);
 }
 
-void launch_select(const Dims& D, const void* q, const float* mu, int32_t* sel, hipStream_t s) {
+size_t select_split_bytes(const Dims& D) {
+  return D.dtype == 1 ? 2 * static_cast<size_t>(D.B) * D.Hkv * D.nb * D.d * sizeof(uint16_t) : 0;
+}
+
+void launch_select(const Dims& D, const void* q, const float* mu, uint16_t* split, int32_t* sel, hipStream_t s) {
   timing_begin(kKSelect, s);
-  if (D.dtype == 1) launch_select_t<bf16_t>(D, q, mu, sel, s);
-  else launch_select_t<float>(D, q, mu, sel, s);
+  if (D.dtype == 1) {
+    const int64_t n = static_cast<int64_t>(D.B) * D.Hkv * D.nb * D.d;   // d is a multiple of 4
+    uint16_t* hi = split;
+    uint16_t* lo = split + n;
+    const int64_t n4 = n / 4;
+    const int grid = static_cast<int>(n4 / 256 + 1 < 4096 ? n4 / 256 + 1 : 4096);
+    hipLaunchKernelGGL(k_split_means, dim3(grid), dim3(256), 0, s, reinterpret_cast<const float4*>(mu),
+                       reinterpret_cast<uint2*>(hi), reinterpret_cast<uint2*>(lo), n4);
+    launch_select_t<bf16_t>(D, q, mu, hi, lo, sel, s);
+  } else {
+    launch_select_t<float>(D, q, mu, nullptr, nullptr, sel, s);
+  }
   timing_end(kKSelect, s);
 }
 

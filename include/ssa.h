@@ -106,9 +106,12 @@ size_t ssa_workspace_size(const ssa_shape_t* shape, int32_t mode, int32_t op);
 /*
  * Block selection (the rule in the header comment).
  *   q [B,Hq,N,d], k [B,Hkv,N,d] in shape->dtype  -> sel [B,Hq,N,top_k] int32.
- * Block means are accumulated in fp32 and scores are fp32 dot products, so a
- * cutoff whose two scores differ by less than fp32 rounding may rank either
- * way.  Workspace: the fp32 block means.
+ * Block means are accumulated in fp32.  Scores of fp32 layers are fp32 dot
+ * products; those of bf16 layers multiply q (exact) by each mean split into
+ * two bf16 terms (hi = bf16(mu), lo = bf16(mu - hi), together within 2^-18
+ * of mu relative) with exact products and fp32 sums.  A cutoff whose two
+ * scores differ by less than this rounding may rank either way.
+ * Workspace: the fp32 block means and, for bf16, their two-term split.
  */
 ssa_status_t ssa_select_blocks(const ssa_shape_t* shape, const void* q, const void* k,
                                int32_t* sel, void* ws, size_t ws_bytes, void* stream);

@@ -2,9 +2,10 @@
 
 TEST INFRASTRUCTURE ONLY (tests, smoke check, benchmark CPU baseline).
 
-A GPU computes block scores in fp32 and the oracle in fp64, so a row whose
-top-k cutoff separates two scores closer than the rounding of fp32 could be
-ranked differently.  Rows whose cutoff margin (the oracle's fp64 score of
+A GPU computes block scores with fp32 sums (and bf16 layers with the means
+split into two bf16 terms) and the oracle in fp64, so a row whose top-k
+cutoff separates two scores closer than that rounding could be ranked
+differently.  Rows whose cutoff margin (the oracle's fp64 score of
 the last kept block minus that of the first dropped block) is below the
 threshold are redrawn from the same seeded stream, in (batch, head, token)
 order, until no row fails at any of the given top-k values.  k and v are
