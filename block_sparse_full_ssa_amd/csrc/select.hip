@@ -17,6 +17,8 @@
 //                carrying a row's winners from one chunk of candidates into
 //                the next.
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -80,10 +82,17 @@ constexpr int kCarry = 64;        // carried winners per row (top_k <= 64 here)
 // chunk they are written to the rows of sel instead, with the own block and
 // the padding.  Without CARRY (every candidate in one chunk) there is no
 // carried slot.  Wave w ranks rows w*RW.. in steps of 4*RW.
+//
+// After the first chunk (keep is then top_k - 1 throughout, as a chunk holds
+// more candidates than that), a candidate whose code does not exceed the
+// previous chunk's threshold car_th[r] cannot win: the carried entries are
+// `keep` codes at or above it, and earlier blocks win ties.  The others are
+// appended to the carried entries in LDS (block order kept); when they fit
+// in one register slot the search runs over that slot alone.
 template <int TM, bool CARRY>
 __device__ __forceinline__ void rank_chunk(const float* scores, int CH, int c0, int nc, uint32_t* car_code,
-                                           int32_t* car_idx, int ncar, int32_t* out0, int R, int K, int i, int keep,
-                                           bool last, int lane, int wave) {
+                                           int32_t* car_idx, uint32_t* car_th, int ncar, int32_t* out0, int R,
+                                           int K, int i, int keep, bool last, int lane, int wave) {
   constexpr int RW = 2;             // rows ranked together per wave
   constexpr int C0 = CARRY ? 1 : 0;  // first candidate slot
   constexpr int S = TM + C0;        // register slots: (carried +) candidates
@@ -105,71 +114,121 @@ __device__ __forceinline__ void rank_chunk(const float* scores, int CH, int c0, 
         u[w][t + C0] = (t < nt && c < nc) ? ordered_bits(scores[r * CH + c] + 0.0f) : 0u;
       }
     }
-    // codes of absent candidates are 0, below every threshold tried (>= 1)
-    uint32_t th[RW];
-    bool done[RW];
+    bool narrow = false;            // uniform: every live entry is in slot 0
+    if constexpr (CARRY) {
+      if (ncar > 0) {
+        int live[RW];
+        bool fit = true;
 #pragma unroll
-    for (int w = 0; w < RW; ++w) {
-      th[w] = 0u;
-      done[w] = false;
+        for (int w = 0; w < RW; ++w) {
+          const uint32_t th_old = car_th[r0 + w];
+          int n = ncar;
+#pragma unroll
+          for (int t = C0; t < S; ++t) {
+            u[w][t] = u[w][t] > th_old ? u[w][t] : 0u;
+            n += __popcll(__ballot(u[w][t] != 0u));
+          }
+          live[w] = n;
+          fit = fit && n <= 64;
+        }
+        if (fit) {
+          narrow = true;
+#pragma unroll
+          for (int w = 0; w < RW; ++w) {
+            const int r = r0 + w;
+            int base = ncar;
+#pragma unroll
+            for (int t = C0; t < S; ++t) {
+              const uint64_t b = __ballot(u[w][t] != 0u);
+              if ((b >> lane) & 1) {
+                const int pos = base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b), 0));
+                car_code[r * kCarry + pos] = u[w][t];
+                car_idx[r * kCarry + pos] = c0 + 64 * (t - C0) + lane;
+              }
+              base += __popcll(b);
+            }
+            // one wave owns the row: its LDS accesses complete in order
+            u[w][0] = lane < live[w] ? car_code[r * kCarry + lane] : 0u;
+            cidx[w] = lane < live[w] ? car_idx[r * kCarry + lane] : 0;
+          }
+        }
+      }
     }
-    // Once exactly `keep` candidates are >= the threshold, lower bits can only
-    // raise it within the gap below the keep-th largest code: the set >= th
-    // and hence the result no longer change, so the search stops (uniform:
-    // counts come from ballots).
-    for (int bit = 31; bit >= 0; --bit) {
-      bool all = true;
+    // threshold search and emission over the first NS register slots
+    auto finish = [&](auto ns_tag) {
+      constexpr int NS = decltype(ns_tag)::value;
+      // codes of absent candidates are 0, below every threshold tried (>= 1)
+      uint32_t th[RW];
+      bool done[RW];
 #pragma unroll
       for (int w = 0; w < RW; ++w) {
-        if (done[w]) continue;
-        const uint32_t c = th[w] | (1u << bit);
-        int cnt = 0;
-#pragma unroll
-        for (int t = 0; t < S; ++t) cnt += __popcll(__ballot(u[w][t] >= c));
-        th[w] = cnt >= keep ? c : th[w];
-        done[w] = cnt == keep;
-        all = all && done[w];
+        th[w] = 0u;
+        done[w] = false;
       }
-      if (all) break;
-    }
+      // Once exactly `keep` candidates are >= the threshold, lower bits can
+      // only raise it within the gap below the keep-th largest code: the set
+      // >= th and hence the result no longer change, so the search stops
+      // (uniform: counts come from ballots).
+      for (int bit = 31; bit >= 0; --bit) {
+        bool all = true;
 #pragma unroll
-    for (int w = 0; w < RW; ++w) {
-      const int r = r0 + w;
-      int32_t* out = out0 + static_cast<int64_t>(r) * K;
-      int need = keep;              // places left for codes equal to th
+        for (int w = 0; w < RW; ++w) {
+          if (done[w]) continue;
+          const uint32_t c = th[w] | (1u << bit);
+          int cnt = 0;
 #pragma unroll
-      for (int t = 0; t < S; ++t) need -= __popcll(__ballot(u[w][t] > th[w]));
-      int base = 0;
-#pragma unroll
-      for (int t = 0; t < S; ++t) {
-        uint64_t eq = __ballot(u[w][t] == th[w]);
-        if (__popcll(eq) > need) {    // keep only the `need` lowest lanes
-          uint64_t take = 0;
-          for (int n = 0; n < need; ++n) {
-            const uint64_t low = eq & (~eq + 1);
-            take |= low;
-            eq ^= low;
-          }
-          eq = take;
+          for (int t = 0; t < NS; ++t) cnt += __popcll(__ballot(u[w][t] >= c));
+          th[w] = cnt >= keep ? c : th[w];
+          done[w] = cnt == keep;
+          all = all && done[w];
         }
-        need -= __popcll(eq);
-        const uint64_t won = __ballot(u[w][t] > th[w]) | eq;
-        if ((won >> lane) & 1) {
-          const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(won >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(won), 0));
-          const int idx = (CARRY && t == 0) ? cidx[w] : c0 + 64 * (t - C0) + lane;
-          if (!CARRY || last) {
-            out[base + below] = idx;
-          } else {
-            car_code[r * kCarry + base + below] = u[w][t];
-            car_idx[r * kCarry + base + below] = idx;
-          }
-        }
-        base += __popcll(won);
+        if (all) break;
       }
-      if (!CARRY || last)
-        for (int slot = keep + lane; slot < K; slot += 64) out[slot] = (slot == keep) ? i : -1;
-    }
+#pragma unroll
+      for (int w = 0; w < RW; ++w) {
+        const int r = r0 + w;
+        int32_t* out = out0 + static_cast<int64_t>(r) * K;
+        int need = keep;              // places left for codes equal to th
+#pragma unroll
+        for (int t = 0; t < NS; ++t) need -= __popcll(__ballot(u[w][t] > th[w]));
+        int base = 0;
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+          uint64_t eq = __ballot(u[w][t] == th[w]);
+          if (__popcll(eq) > need) {    // keep only the `need` lowest lanes
+            uint64_t take = 0;
+            for (int n = 0; n < need; ++n) {
+              const uint64_t low = eq & (~eq + 1);
+              take |= low;
+              eq ^= low;
+            }
+            eq = take;
+          }
+          need -= __popcll(eq);
+          const uint64_t won = __ballot(u[w][t] > th[w]) | eq;
+          if ((won >> lane) & 1) {
+            const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(won >> 32),
+                                                        __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(won), 0));
+            const int idx = (CARRY && t == 0) ? cidx[w] : c0 + 64 * (t - C0) + lane;
+            if (!CARRY || last) {
+              out[base + below] = idx;
+            } else {
+              car_code[r * kCarry + base + below] = u[w][t];
+              car_idx[r * kCarry + base + below] = idx;
+            }
+          }
+          base += __popcll(won);
+        }
+        if (!CARRY || last) {
+          for (int slot = keep + lane; slot < K; slot += 64) out[slot] = (slot == keep) ? i : -1;
+        } else if (lane == 0) {
+          car_th[r] = th[w];            // every winner's code is >= th
+        }
+      }
+    };
+    if (narrow) finish(std::integral_constant<int, 1>{});
+    else finish(std::integral_constant<int, S>{});
   }
 }
 
@@ -200,6 +259,7 @@ __global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, co
   float* scores = smem;                                                   // [R][CH]
   uint32_t* car_code = reinterpret_cast<uint32_t*>(smem + R * CH);       // [R][kCarry]
   int32_t* car_idx = reinterpret_cast<int32_t*>(car_code + R * kCarry);  // [R][kCarry]
+  uint32_t* car_th = reinterpret_cast<uint32_t*>(car_idx + R * kCarry);  // [R]
   const int bh = blockIdx.y;
   const int b = bh / Hq, h = bh % Hq;
   const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
@@ -279,7 +339,7 @@ __global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, co
   if constexpr (!CARRY) {
     // every candidate in one chunk: q is dead once the scores are in LDS
     score_chunk(0, i);
-    rank_chunk<TM, false>(scores, CH, 0, i, car_code, car_idx, 0, out0, R, K, i, keep, true, lane, wave);
+    rank_chunk<TM, false>(scores, CH, 0, i, car_code, car_idx, car_th, 0, out0, R, K, i, keep, true, lane, wave);
   } else {
     int ncar = 0;
     for (int c0 = 0; c0 < i; c0 += CH) {
@@ -288,7 +348,7 @@ __global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, co
       score_chunk(c0, nc);
       const bool last = c0 + CH >= i;
       const int keep_now = min(K - 1, c0 + nc);   // winners among the candidates so far
-      rank_chunk<TM, true>(scores, CH, c0, nc, car_code, car_idx, ncar, out0, R, K, i, last ? keep : keep_now,
+      rank_chunk<TM, true>(scores, CH, c0, nc, car_code, car_idx, car_th, ncar, out0, R, K, i, last ? keep : keep_now,
                            last, lane, wave);
       ncar = keep_now;
     }
@@ -301,8 +361,8 @@ static void launch_select_mfma(const Dims& D, int R, const void* q, const float*
   const int CH = D.nb < kCand ? D.nb : kCand;
   dim3 grid(D.Nq / R, D.B * D.Hq);
   // the carried winners need LDS only when the candidates span several chunks
-  // (at most 32 KiB of scores + 16 KiB of winners)
-  const size_t lds = (static_cast<size_t>(R) * CH + (D.nb > CH ? 2 * static_cast<size_t>(R) * kCarry : 0)) *
+  // (at most 32 KiB of scores + 16 KiB of winners and their thresholds)
+  const size_t lds = (static_cast<size_t>(R) * CH + (D.nb > CH ? (2 * static_cast<size_t>(kCarry) + 1) * R : 0)) *
                      sizeof(float);
   hipLaunchKernelGGL((k_select_mfma<T, TM, DD, CARRY>), grid, dim3(256), lds, s, static_cast<const T*>(q), mu, mu_hi,
                      mu_lo, sel, D.Hq, D.G, D.Nq, D.q_off, D.block, D.nb, D.K, R, CH);
