@@ -362,7 +362,7 @@ def cpu_baseline(wl, K, seed, rows):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
               "(the attention path has no multi-GPU sharding)", file=sys.stderr)
         sys.exit(2)
 
