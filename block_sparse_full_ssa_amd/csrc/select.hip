@@ -227,7 +227,12 @@ __device__ __forceinline__ void rank_chunk(const float* scores, int CH, int c0, 
         }
       }
     };
-    if (narrow) finish(std::integral_constant<int, 1>{});
+    // only the slots that hold entries take part (uniform: nt is the chunk's)
+    const int ns = C0 + nt;
+    if (narrow || ns <= 1) finish(std::integral_constant<int, 1>{});
+    else if (ns == 2) finish(std::integral_constant<int, (2 < S ? 2 : S)>{});
+    else if (ns == 3) finish(std::integral_constant<int, (3 < S ? 3 : S)>{});
+    else if (ns == 4) finish(std::integral_constant<int, (4 < S ? 4 : S)>{});
     else finish(std::integral_constant<int, S>{});
   }
 }
