@@ -115,6 +115,11 @@ __device__ __forceinline__ void rank_chunk(const float* scores, int CH, int c0, 
       }
     }
     bool narrow = false;            // uniform: every live entry is in slot 0
+    // start of the threshold search: bits above `bit0` of th are known
+    uint32_t th0[RW];
+    int bit0 = 31;
+#pragma unroll
+    for (int w = 0; w < RW; ++w) th0[w] = 0u;
     if constexpr (CARRY) {
       if (ncar > 0) {
         int live[RW];
@@ -152,6 +157,24 @@ __device__ __forceinline__ void rank_chunk(const float* scores, int CH, int c0, 
             u[w][0] = lane < live[w] ? car_code[r * kCarry + lane] : 0u;
             cidx[w] = lane < live[w] ? car_idx[r * kCarry + lane] : 0;
           }
+          // The live codes lie between their minimum and maximum, so they
+          // share the leading bits on which those two agree; the threshold
+          // (between the keep-th largest code and the maximum) shares them
+          // too, and the search starts below them.
+          uint32_t mx[RW];
+          int common = 32;
+#pragma unroll
+          for (int w = 0; w < RW; ++w) {
+            const bool in = lane < live[w];
+            mx[w] = wave_max_u32_dpp(in ? u[w][0] : 0u);
+            const uint32_t mn = ~wave_max_u32_dpp(in ? ~u[w][0] : 0u);
+            const int agree = (mx[w] ^ mn) == 0u ? 32 : __builtin_clz(mx[w] ^ mn);
+            common = min(common, agree);
+          }
+          bit0 = 31 - common;
+          const uint32_t top = common >= 32 ? 0xffffffffu : ~(0xffffffffu >> common);
+#pragma unroll
+          for (int w = 0; w < RW; ++w) th0[w] = mx[w] & top;
         }
       }
     }
@@ -163,14 +186,14 @@ __device__ __forceinline__ void rank_chunk(const float* scores, int CH, int c0, 
       bool done[RW];
 #pragma unroll
       for (int w = 0; w < RW; ++w) {
-        th[w] = 0u;
+        th[w] = th0[w];
         done[w] = false;
       }
       // Once exactly `keep` candidates are >= the threshold, lower bits can
       // only raise it within the gap below the keep-th largest code: the set
       // >= th and hence the result no longer change, so the search stops
       // (uniform: counts come from ballots).
-      for (int bit = 31; bit >= 0; --bit) {
+      for (int bit = bit0; bit >= 0; --bit) {
         bool all = true;
 #pragma unroll
         for (int w = 0; w < RW; ++w) {
