@@ -104,16 +104,19 @@ def test_select_all_blocks_and_top1():
         assert np.array_equal(sel, want), K
 
 
-def test_select_chunked_candidates_all_rows():
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_select_chunked_candidates_all_rows(dtype):
     """530 key blocks: candidates are scored and ranked in chunks of 256 with
     each row's winners carried between chunks (256 + 256 + a ragged 18).
-    Every row bit for bit, top_k 8 and 64 (63 carried winners, the most)."""
-    wl = si.scaled_down(W["gqa_n4k_fwd"], seqlen=32 * 530, hq=2, hkv=1, block=32, head_dim=64, top_k=8)
+    Every row bit for bit, top_k 8 and 64 (63 carried winners, the most), on
+    a bf16 layer (two-term bf16 scores) and an fp32 one (fp32 scores)."""
+    wl = si.scaled_down(W["gqa_n4k_fwd"], seqlen=32 * 530, hq=2, hkv=1, block=32, head_dim=64, top_k=8,
+                        dtype=dtype)
     ks = (8, 64)
     (q, k, v), _ = inputs(wl, 0, ks)
     qd, kd = to_dev(q, k)
     for K in ks:
-        _say(f"select chunked nb 530 K={K}")
+        _say(f"select chunked nb 530 {dtype} K={K}")
         sel = ssa().ssa_select_blocks(qd, kd, wl.block, K)
         want, _ = oracle_select(wl, 0, ks, K)
         assert np.array_equal(sel.cpu().numpy(), want), K
