@@ -124,17 +124,24 @@ __global__ void __launch_bounds__(256, 2)
     }
   };
   // The sparse stream's dS of one half (keys jj*64 + 32 kh ..) for the
-  // lanes whose queries selected its block, zero elsewhere.  Loads run one
-  // half ahead of their use: the rows of a tile's second half are fetched
-  // at its first half and those of the next tile's first half at the second.
-  uint4 sdc[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)}, sdx[2] = {sdc[0], sdc[1]};
+  // lanes whose queries selected its block, zero elsewhere.  The rows of the
+  // next tile are fetched during the second half of the current one, so they
+  // land with the next tile's copies at the barrier: a wait for a register
+  // load while tile copies are in flight would wait for those copies too.
+  uint4 sd[2][2], sdn[2][2];
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) sd[kh][0] = sd[kh][1] = sdn[kh][0] = sdn[kh][1] = make_uint4(0, 0, 0, 0);
   auto load_sd = [&](int jj, int kh, uint32_t mword, int mpos, uint4* dst) {
     dst[0] = dst[1] = make_uint4(0, 0, 0, 0);
     const int kbase = jj * kBN + kh * 32;
     const uint32_t m = __builtin_amdgcn_readfirstlane(mword);
     if (wave_live && jj <= j_last && kbase <= wave_last_q && m != 0u && ((m >> col) & 1u)) {
       const int blk = kbase / block;
-      const int e = __builtin_amdgcn_readfirstlane(mpos) + __builtin_popcount(m & ((1u << col) - 1u));
+      // entries of the selected queries below this lane's in the word
+      // (lanes 32.. hold the same queries: mbcnt counts the whole word once more)
+      const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(m, __builtin_amdgcn_mbcnt_lo(m, 0u))) -
+                        (g ? __builtin_popcount(m) : 0);
+      const int e = __builtin_amdgcn_readfirstlane(mpos) + below;
       const uint16_t* src = a.ds_rows + static_cast<int64_t>(e) * block + (kbase - blk * block) + 16 * g;
       dst[0] = *reinterpret_cast<const uint4*>(src);
       dst[1] = *reinterpret_cast<const uint4*>(src + 8);
@@ -143,13 +150,18 @@ __global__ void __launch_bounds__(256, 2)
   auto step = [&](int j, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn) {
     if constexpr (SPARSE) {
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
+      for (int kh = 0; kh < 2; ++kh) {       // uniform: scalar registers
         mw[kh] = mwn[kh];
         mp[kh] = mpn[kh];
-        mwn[kh] = mwn2[kh];
-        mpn[kh] = mpn2[kh];
+        mwn[kh] = __builtin_amdgcn_readfirstlane(mwn2[kh]);
+        mpn[kh] = __builtin_amdgcn_readfirstlane(mpn2[kh]);
       }
       if (j + 2 <= j_last) mask_words(j + 2, mwn2, mpn2);
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        sd[kh][0] = sdn[kh][0];
+        sd[kh][1] = sdn[kh][1];
+      }
     }
     if (j + 1 <= j_last) load_tile(j + 1, Kn, Vn);
     if (wave_live && j * kBN <= wave_last_q) {
@@ -158,15 +170,10 @@ __global__ void __launch_bounds__(256, 2)
         const int kbase = j * kBN + kh * 32;
         if (kbase > wave_last_q) break;                // uniform: later keys are all masked
         if constexpr (SPARSE) {
-          // this half's rows were fetched one half earlier; a wait for a
-          // register load while tile copies are in flight waits for those
-          // copies too, so the second half takes one wait for everything
-          // before it fetches the next tile's first half
-          if (kh == 1) __builtin_amdgcn_s_waitcnt(0);
-          sdc[0] = sdx[0];
-          sdc[1] = sdx[1];
-          if (kh == 0) load_sd(j, 1, mw[1], mp[1], sdx);
-          else load_sd(j + 1, 0, mwn[0], mpn[0], sdx);
+          if (kh == 1) {
+            load_sd(j + 1, 0, mwn[0], mpn[0], sdn[0]);
+            load_sd(j + 1, 1, mwn[1], mpn[1], sdn[1]);
+          }
         }
         // ---- S^T = K Q^T, dP^T = V G^T for 32 keys (A: key row kh*32 + col)
         f32x16 s = f32x16{}, dp = f32x16{};
@@ -194,7 +201,7 @@ __global__ void __launch_bounds__(256, 2)
         // being the key of register i; it is zero wherever the mask is)
         float dsv[16];
         {
-          const uint4 sd0 = sdc[0], sd1 = sdc[1];
+          const uint4 sd0 = sd[kh][0], sd1 = sd[kh][1];
           const uint32_t sw[8] = {sd0.x, sd0.y, sd0.z, sd0.w, sd1.x, sd1.y, sd1.z, sd1.w};
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
@@ -239,7 +246,13 @@ __global__ void __launch_bounds__(256, 2)
     mask_words(0, mwn, mpn);
     if (1 <= j_last) mask_words(1, mwn2, mpn2);
     __builtin_amdgcn_s_waitcnt(0);
-    load_sd(0, 0, mwn[0], mpn[0], sdx);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      mwn[kh] = __builtin_amdgcn_readfirstlane(mwn[kh]);
+      mpn[kh] = __builtin_amdgcn_readfirstlane(mpn[kh]);
+    }
+    load_sd(0, 0, mwn[0], mpn[0], sdn[0]);
+    load_sd(0, 1, mwn[1], mpn[1], sdn[1]);
   }
   load_tile(0, K0, V0);
   __builtin_amdgcn_s_waitcnt(0);
