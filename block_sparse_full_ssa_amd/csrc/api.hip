@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -24,10 +25,13 @@ static ssa_status_t fail(ssa_status_t st, const char* fmt, const char* detail = 
 }
 
 // ---------------------------------------------------------------- timing ---
+// The library's only process-wide state: the optional event records of the
+// measurement hooks, guarded by one mutex.
 struct TimingRec {
   int kernel;
   hipEvent_t a, b;
 };
+static std::mutex g_timing_mu;
 static bool g_timing = false;
 static std::vector<TimingRec> g_recs;
 static const char* kKernelNames[kKernelCount] = {
@@ -35,7 +39,15 @@ static const char* kKernelNames[kKernelCount] = {
     "bwd_pre",    "bwd_simt", "bwd_mfma", "convert", "zero", "bucket", "sparse_part", "sparse_merge",
     "bwd_sparse", "bwd_dq", "probe_mfma", "probe_copy", "decode"};
 
+static thread_local int g_timing_paused = 0;
+TimingPause::TimingPause() { ++g_timing_paused; }
+TimingPause::~TimingPause() { --g_timing_paused; }
+
+void set_last_error(const char* msg) { g_last_error = msg; }
+
 void timing_begin(int kernel, hipStream_t s) {
+  if (g_timing_paused) return;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
   if (!g_timing) return;
   TimingRec r{kernel, nullptr, nullptr};
   if (hipEventCreate(&r.a) != hipSuccess || hipEventCreate(&r.b) != hipSuccess) return;
@@ -44,6 +56,8 @@ void timing_begin(int kernel, hipStream_t s) {
 }
 
 void timing_end(int kernel, hipStream_t s) {
+  if (g_timing_paused) return;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
   if (!g_timing || g_recs.empty()) return;
   TimingRec& r = g_recs.back();
   if (r.kernel == kernel) (void)hipEventRecord(r.b, s);
@@ -285,8 +299,12 @@ static ssa_status_t attn_fwd(const ssa_shape_t* shape, int32_t mode, const void*
     return launch_status();
   }
   FwdArgs a{q, k, v, sel, h_full, h_sparse, lse_full, lse_sparse, delta, w.row_sq, mode, sink_mass, entropy};
-  if (mode != kSparseOnly && fwd_mfma_supported(D)) launch_fwd_mfma(D, a, s);   // dual and full modes
-  else launch_fwd_simt(D, a, s);
+  if (mode != kSparseOnly && fwd_mfma_supported(D)) {   // dual and full modes
+    const hipError_t e = launch_fwd_mfma(D, a, s);
+    if (e != hipSuccess) return fail(SSA_ERR_HIP, "LDS grant of the forward kernel failed: %s", hipGetErrorString(e));
+  } else {
+    launch_fwd_simt(D, a, s);
+  }
   if ((st = launch_status()) != SSA_OK) return st;
   if (dual) {
     launch_loss_reduce(w.row_sq, D.rows(), 1.0 / static_cast<double>(D.q_elems()), w.loss_sums, losses, s);
@@ -398,6 +416,7 @@ const char* ssa_status_string(int32_t status) {
 const char* ssa_last_error(void) { return g_last_error.c_str(); }
 
 ssa_status_t ssa_timing_enable(int32_t enabled) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
   timing_clear();
   g_timing = enabled != 0;
   return SSA_OK;
@@ -409,6 +428,7 @@ ssa_status_t ssa_timing_query(const char* kernel, double* total_ms, int64_t* lau
   for (int i = 0; i < kKernelCount; ++i)
     if (strcmp(kernel, kKernelNames[i]) == 0) id = i;
   if (id < 0) return fail(SSA_ERR_SHAPE, "unknown kernel name %s", kernel);
+  std::lock_guard<std::mutex> lk(g_timing_mu);
   double tot = 0.0;
   int64_t n = 0;
   for (auto& r : g_recs) {
@@ -474,7 +494,8 @@ ssa_status_t ssa_prefill(const ssa_shape_t* shape, int32_t mode, const void* q, 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (mode == kFullOnly) {
     FwdArgs a{q, k_cache, v_cache, nullptr, h, nullptr, lse, nullptr, nullptr, nullptr, kFullOnly};
-    launch_fwd_mfma(D, a, s);
+    const hipError_t e = launch_fwd_mfma(D, a, s);
+    if (e != hipSuccess) return fail(SSA_ERR_HIP, "LDS grant of the forward kernel failed: %s", hipGetErrorString(e));
     return launch_status();
   }
   Carver c{static_cast<char*>(ws)};

@@ -109,7 +109,8 @@ __global__ void __launch_bounds__(256, 2)
       const int r = e / K, t = q0 + r;
       if (t < qend) {
         const int blk = a.sel[(static_cast<int64_t>(bh) * Nq + (t - q_off)) * K + (e - r * K)];
-        if (blk >= 0) atomicOr(&bits[r * W + (blk >> 5)], 1u << (blk & 31));
+        // entries outside 0 .. own block select nothing (and stay inside the row's words)
+        if (blk >= 0 && blk <= t / block) atomicOr(&bits[r * W + (blk >> 5)], 1u << (blk & 31));
       }
     }
   }
@@ -359,17 +360,18 @@ __global__ void __launch_bounds__(256, 2)
 }
 
 template <int MODE, bool STATS>
-void launch_mode(const Dims& D, const FwdArgs& a, size_t lds, int n_qtiles, float scale_log2, hipStream_t s) {
-  static size_t granted = 0;    // LDS above 64 KiB in total must be requested per kernel
-  if (lds > granted) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fwd_mfma<MODE, STATS>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
-    granted = lds;
+hipError_t launch_mode(const Dims& D, const FwdArgs& a, size_t lds, int n_qtiles, float scale_log2, hipStream_t s) {
+  // LDS above 64 KiB in total must be granted per kernel; the grant is set on
+  // every launch (the device current at the call), so no state is kept
+  const void* fn = reinterpret_cast<const void*>(&k_fwd_mfma<MODE, STATS>);
+  if (lds > 0) {
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
+    if (e != hipSuccess) return e;
   }
   dim3 grid(D.B * D.Hq * n_qtiles);   // work items from qtile_item
   hipLaunchKernelGGL((k_fwd_mfma<MODE, STATS>), grid, dim3(256), lds, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.block,
-                     D.nb, D.K,
-                     scale_log2, n_qtiles);
+                     D.nb, D.K, scale_log2, n_qtiles);
+  return hipSuccess;
 }
 
 constexpr size_t kStaticLds = 4 * kTile * sizeof(uint16_t);
@@ -386,20 +388,22 @@ bool fwd_mfma_supported(const Dims& D) {
   return D.dtype == 1 && D.d == kD && kStaticLds + lds_bytes(D) <= 160 * 1024;
 }
 
-void launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s) {
+hipError_t launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s) {
   const int n_qtiles = (D.Nq + kBM - 1) / kBM;
   const size_t lds = a.mode == kFullOnly ? 0 : lds_bytes(D);   // the full stream reads no selection bits
   const float scale_log2 = D.scale * 1.4426950408889634f;
   timing_begin(kKFwdMfma, s);
   const bool stats = a.sink_mass != nullptr;
+  hipError_t e;
   if (a.mode == kFullOnly) {
-    if (stats) launch_mode<kModeFull, true>(D, a, lds, n_qtiles, scale_log2, s);
-    else launch_mode<kModeFull, false>(D, a, lds, n_qtiles, scale_log2, s);
+    e = stats ? launch_mode<kModeFull, true>(D, a, lds, n_qtiles, scale_log2, s)
+              : launch_mode<kModeFull, false>(D, a, lds, n_qtiles, scale_log2, s);
   } else {
-    if (stats) launch_mode<kModeDual, true>(D, a, lds, n_qtiles, scale_log2, s);
-    else launch_mode<kModeDual, false>(D, a, lds, n_qtiles, scale_log2, s);
+    e = stats ? launch_mode<kModeDual, true>(D, a, lds, n_qtiles, scale_log2, s)
+              : launch_mode<kModeDual, false>(D, a, lds, n_qtiles, scale_log2, s);
   }
   timing_end(kKFwdMfma, s);
+  return e;
 }
 
 }  // namespace ssa

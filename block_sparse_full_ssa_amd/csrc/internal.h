@@ -50,6 +50,14 @@ enum KernelId {
 // Timing hooks (api.hip); no-ops unless timing is enabled.
 void timing_begin(int kernel, hipStream_t s);
 void timing_end(int kernel, hipStream_t s);
+// While a TimingPause lives, the calling thread records no events (entry
+// points that must not create HIP objects).
+struct TimingPause {
+  TimingPause();
+  ~TimingPause();
+};
+// Sets the text that ssa_last_error() reports on this thread.
+void set_last_error(const char* msg);
 
 // --- selection (select.hip) ---
 void launch_block_mean(const Dims& D, const void* k, float* mu, hipStream_t s);
@@ -88,7 +96,9 @@ void launch_bwd_simt(const Dims& D, const BwdArgs& a, hipStream_t s);
 
 // --- bf16 MFMA kernels ---
 bool fwd_mfma_supported(const Dims& D);
-void launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s);   // dual and FULL_ONLY modes
+// dual and FULL_ONLY modes; returns the status of the LDS grant (the launch's
+// own status comes from hipGetLastError)
+hipError_t launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s);
 
 struct BwdPreArgs {
   const void* dout;                 // may be null: zero upstream gradient

@@ -18,6 +18,8 @@
 // per key dZ = p (G . v - D) feeds dq (in registers), and dk, dv through fp32
 // atomics into zeroed accumulators.
 
+#include <limits.h>
+
 #include "common.h"
 #include "internal.h"
 
@@ -52,7 +54,9 @@ __global__ void __launch_bounds__(256) k_fwd_simt(FwdArgs a, int Hq, int G, int 
   const bool stats = want_full && a.sink_mass != nullptr;
   float sink_l = 0.f, ex_l = 0.f;
   int ptr = 0;
-  int next_blk = want_sparse ? selp[0] : -1;
+  // the row's entries in ascending order; negative entries are skipped, and
+  // past the last entry no block matches
+  int next_blk = want_sparse ? selp[0] : INT_MAX;
 
   for (int i = 0; i <= t; ++i) {
     float dot = 0.f;
@@ -78,9 +82,9 @@ __global__ void __launch_bounds__(256) k_fwd_simt(FwdArgs a, int Hq, int G, int 
     }
     if (want_sparse) {
       const int blk = i / block;
-      while (next_blk >= 0 && next_blk < blk) {
+      while (next_blk < blk) {
         ++ptr;
-        next_blk = ptr < K ? selp[ptr] : -1;
+        next_blk = ptr < K ? selp[ptr] : INT_MAX;
       }
       if (next_blk == blk) {
         const float mn = fmaxf(ms, z);
@@ -180,7 +184,9 @@ __global__ void __launch_bounds__(256) k_bwd_simt(BwdArgs a, int Hq, int G, int 
   const float lse_f = has_full ? a.lse_full[row] : 0.f;
   const float lse_s = has_sparse ? a.lse_sparse[row] : 0.f;
   int ptr = 0;
-  int next_blk = has_sparse ? selp[0] : -1;
+  // the row's entries in ascending order; negative entries are skipped, and
+  // past the last entry no block matches
+  int next_blk = has_sparse ? selp[0] : INT_MAX;
 
   for (int i = 0; i <= t; ++i) {
     float kv[E], vv[E];
@@ -201,9 +207,9 @@ __global__ void __launch_bounds__(256) k_bwd_simt(BwdArgs a, int Hq, int G, int 
     }
     if (has_sparse) {
       const int blk = i / block;
-      while (next_blk >= 0 && next_blk < blk) {
+      while (next_blk < blk) {
         ++ptr;
-        next_blk = ptr < K ? selp[ptr] : -1;
+        next_blk = ptr < K ? selp[ptr] : INT_MAX;
       }
       if (next_blk == blk) {
         ps = expf(z - lse_s);

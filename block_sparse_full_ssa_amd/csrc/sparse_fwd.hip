@@ -203,8 +203,8 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
 // selected blocks, lane i of a row looks up slots i, i + 16, ... in parallel
 // and the positions and weights are then broadcast within the 16 lanes;
 // wider rows (every block of a long sequence) take the serial loop.
-__global__ void __launch_bounds__(256) k_sparse_merge(SparseFwdArgs a, int64_t rows, int Hq, int G, int Nq, int nb,
-                                                      int K, int Kc) {
+__global__ void __launch_bounds__(256) k_sparse_merge(SparseFwdArgs a, int64_t rows, int Hq, int G, int Nq,
+                                                      int q_off, int block, int nb, int K, int Kc) {
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
   const int li = threadIdx.x & 15;
   const bool live = row < rows;
@@ -217,6 +217,14 @@ __global__ void __launch_bounds__(256) k_sparse_merge(SparseFwdArgs a, int64_t r
   const int hl = h % G, qt = t >> 5;
   const uint32_t below = (1u << (t & 31)) - 1u;
   const int32_t* s = a.sel + rr * K;
+  // Entries that name no causal block (negative, or above the row's own
+  // block) and repeats of the previous entry are ignored: the buckets hold
+  // no partial for them.
+  const int own = (q_off + t) / block;
+  auto entry = [&](int e) -> int {
+    const int j = s[e];
+    return (j >= 0 && j <= own && (e == 0 || s[e - 1] != j)) ? j : -1;
+  };
   auto pos_of = [&](int j) -> int64_t {
     const int64_t w = ((bc * nb + j) * G + hl) * nqt + qt;
     return a.wpos[w] + __popc(a.mask[w] & below);
@@ -238,7 +246,7 @@ __global__ void __launch_bounds__(256) k_sparse_merge(SparseFwdArgs a, int64_t r
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int e = 16 * r + li;
-      const int j = (live && e < Kc) ? s[e] : -1;
+      const int j = (live && e < Kc) ? entry(e) : -1;
       p[r] = j >= 0 ? pos_of(j) : 0;
       x[r] = j >= 0 ? a.part_lse[p[r]] : -INFINITY;
       m = fmaxf(m, x[r]);
@@ -261,10 +269,14 @@ __global__ void __launch_bounds__(256) k_sparse_merge(SparseFwdArgs a, int64_t r
 #pragma unroll
     for (int off = 8; off >= 1; off >>= 1) L += __shfl_xor(L, off, 16);
   } else if (live) {
-    int nv = 0;
-    for (int e = 0; e < Kc && s[e] >= 0; ++e, ++nv) m = fmaxf(m, a.part_lse[pos_of(s[e])]);
-    for (int e = 0; e < nv; ++e) {
-      const int64_t p = pos_of(s[e]);
+    for (int e = 0; e < Kc; ++e) {
+      const int j = entry(e);
+      if (j >= 0) m = fmaxf(m, a.part_lse[pos_of(j)]);
+    }
+    for (int e = 0; e < Kc; ++e) {
+      const int j = entry(e);
+      if (j < 0) continue;
+      const int64_t p = pos_of(j);
       const float wt = fast_exp2(a.part_lse[p] - m);
       L += wt;
       add(p, wt);
@@ -299,7 +311,7 @@ void launch_sparse_fwd(const Dims& D, const SparseFwdArgs& a, hipStream_t s) {
   timing_end(kKSparsePart, s);
   timing_begin(kKSparseMerge, s);
   hipLaunchKernelGGL(k_sparse_merge, dim3(static_cast<unsigned>((D.rows() + 15) / 16)), dim3(256), 0, s, a,
-                     D.rows(), D.Hq, D.G, D.Nq, D.nb, D.K, Kc);
+                     D.rows(), D.Hq, D.G, D.Nq, D.q_off, D.block, D.nb, D.K, Kc);
   timing_end(kKSparseMerge, s);
 }
 

@@ -32,6 +32,28 @@ def make_shape(q: torch.Tensor, k: torch.Tensor, block: int, top_k: int,
                        0.0 if scale is None else float(scale), _DT[q.dtype])
 
 
+def _check_layer(q, k, v, sel, top_k: int, need_sel: bool) -> None:
+    """Shapes and dtypes the kernels index by: v like k, sel int32 [B, Hq, N, top_k]."""
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError(f"v {tuple(v.shape)} {v.dtype} must match k {tuple(k.shape)} {k.dtype}")
+    if sel is None:
+        if need_sel:
+            raise ValueError("sel is required for modes with the sparse stream")
+        return
+    B, Hq, N, _ = q.shape
+    if sel.dtype != torch.int32 or tuple(sel.shape) != (B, Hq, N, int(top_k)):
+        raise ValueError(f"sel must be int32 {(B, Hq, N, int(top_k))}, got {sel.dtype} {tuple(sel.shape)}")
+
+
+def _check_like(name: str, t: Optional[torch.Tensor], shape, dtype, required: bool) -> None:
+    if t is None:
+        if required:
+            raise ValueError(f"{name} is required in this mode")
+        return
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} {tuple(shape)}, got {t.dtype} {tuple(t.shape)}")
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -87,6 +109,7 @@ def ssa_attn_fwd(q, k, v, sel, block: int, top_k: int, mode: int = DUAL_ACTIVE_F
     their per-head means ``head_stats`` [B, Hq, 2]."""
     dev = _dev_check(q, k, v, sel)
     shape = make_shape(q, k, block, top_k, scale)
+    _check_layer(q, k, v, sel, top_k, mode != FULL_ONLY)
     B, Hq, N, d = q.shape
     dual = mode in (DUAL_ACTIVE_FULL, DUAL_ACTIVE_SPARSE)
     out: Dict[str, torch.Tensor] = {}
@@ -125,8 +148,16 @@ def ssa_attn_bwd(q, k, v, sel, fwd: Dict[str, torch.Tensor], d_out: Optional[tor
                  block: int, top_k: int, mode: int = DUAL_ACTIVE_FULL, w_sparsity: float = 1.0,
                  w_commit: float = 1.0, scale: Optional[float] = None):
     """(dq, dk, dv) of one SSA layer from the forward's saved outputs."""
-    dev = _dev_check(q, k, v, sel, d_out)
+    dev = _dev_check(q, k, v, sel, d_out, *(fwd.get(n) for n in ("h_full", "h_sparse", "lse_full", "lse_sparse")))
     shape = make_shape(q, k, block, top_k, scale)
+    _check_layer(q, k, v, sel, top_k, mode != FULL_ONLY)
+    rows = tuple(q.shape[:3])
+    has_full, has_sparse = mode != SPARSE_ONLY, mode != FULL_ONLY
+    _check_like("d_out", d_out, q.shape, q.dtype, False)
+    _check_like("fwd['h_full']", fwd.get("h_full"), q.shape, q.dtype, has_full)
+    _check_like("fwd['lse_full']", fwd.get("lse_full"), rows, torch.float32, has_full)
+    _check_like("fwd['h_sparse']", fwd.get("h_sparse"), q.shape, q.dtype, has_sparse)
+    _check_like("fwd['lse_sparse']", fwd.get("lse_sparse"), rows, torch.float32, has_sparse)
     dq = torch.empty_like(q)
     dk = torch.empty_like(k)
     dv = torch.empty_like(v)

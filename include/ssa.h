@@ -130,9 +130,12 @@ ssa_status_t ssa_select_blocks(const ssa_shape_t* shape, const void* q, const vo
  *     losses may be NULL.  Computed key-block-stationary: the rows that
  *     selected each key block are gathered, each (row, selected block) gets a
  *     partial result and the partials are merged by their log-sum-exps, so
- *     the work follows the selected pairs.  The rows of sel must be ascending
- *     as ssa_select_blocks writes them; entries above a row's own block are
- *     ignored.
+ *     the work follows the selected pairs.
+ * In every mode the non-negative entries of a row of sel must be ascending,
+ *   as ssa_select_blocks writes them.  Entries that name no causal block of
+ *   the row (negative, above the row's own block, or >= N / block) are
+ *   ignored wherever they stand, and so is an entry equal to the one before
+ *   it.
  * lse pointers may be NULL when the caller will not run the backward.
  */
 ssa_status_t ssa_attn_fwd(const ssa_shape_t* shape, int32_t mode, const void* q,
@@ -199,7 +202,11 @@ const char* ssa_last_error(void);
  * kernels.  ssa_timing_query() waits for the recorded events and returns the
  * summed duration (ms) and launch count of one kernel, by name as returned
  * by ssa_kernel_name(i) for i = 0 .. ssa_kernel_count()-1.  Enabling clears
- * earlier records.  Host-side state, not thread-safe; off by default.
+ * earlier records.  Off by default.  These records are the library's only
+ * process-wide host state (guarded by a mutex; while enabled, launches from
+ * several threads all record into them); with timing off every entry point is
+ * reentrant.  Each record creates two HIP events, so harnesses should time
+ * headline wall-clock figures with timing off.
  */
 ssa_status_t ssa_timing_enable(int32_t enabled);
 ssa_status_t ssa_timing_query(const char* kernel, double* total_ms, int64_t* launches);

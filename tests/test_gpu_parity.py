@@ -355,3 +355,67 @@ def test_sparse_only_gradient_deficiency():
     assert float(dv[0, 0, outside].abs().max()) == 0.0
     inside = [i for i in range(t + 1) if i // wl.block in chosen]
     assert float(dv[0, 0, inside].abs().max()) > 0.0
+
+
+# --------------------------------------------------- ignored sel entries --
+
+def _spliced_sel(sel: torch.Tensor, block: int, nb: int) -> torch.Tensor:
+    """sel with the first -1 slot of each padded row replaced by an entry the
+    kernels must ignore: a repeat of the entry before it (rows t % 3 == 0), a
+    block above the row's own one (t % 3 == 1: own + 1 when it exists, else
+    nb), or a block far past the last (t % 3 == 2: 2^20, beyond any row's
+    selection words).  Non-negative entries stay ascending."""
+    s = sel.cpu().clone()
+    B, H, N, K = s.shape
+    t = torch.arange(N)
+    own = t // block
+    for b in range(B):
+        for h in range(H):
+            rows = s[b, h]
+            pad = (rows < 0).int().argmax(dim=1)           # first -1 slot
+            has_pad = (rows < 0).any(dim=1)
+            for r in torch.nonzero(has_pad).flatten().tolist():
+                p = int(pad[r])
+                kind = r % 3
+                if kind == 0:
+                    val = int(rows[r, p - 1])
+                elif kind == 1:
+                    val = int(own[r]) + 1 if int(own[r]) + 1 < nb else nb
+                else:
+                    val = 1 << 20
+                rows[r, p] = val
+    return s.to(sel.device)
+
+
+@pytest.mark.parametrize("mode", MODES[:2] + [oracle.SPARSE_ONLY])
+@pytest.mark.parametrize("name", ["tiny", "gqa_n512_b64_k4", "mha_n384_b32_k5"])
+def test_ignored_sel_entries_bit_identical(name, mode):
+    """Entries naming no causal block (above the own block, past the last
+    block) and repeated entries change nothing: forward and backward outputs
+    equal those of the clean selection bit for bit."""
+    wl = TINY if name == "tiny" else SMALL[name]
+    K = wl.top_k + 2                                   # every early row is padded
+    _say(f"ignored sel entries {name} mode {mode}")
+    (q, k, v), _ = inputs(wl, 0, (wl.top_k,))
+    g = si.draw_dout(wl, 0)
+    qd, kd, vd, gd = to_dev(q, k, v, g)
+    sel = ssa().ssa_select_blocks(qd, kd, wl.block, K)
+    bad = _spliced_sel(sel, wl.block, wl.nblocks)
+    assert not torch.equal(bad, sel)
+    outs = []
+    for s in (sel, bad):
+        fwd = ssa().ssa_attn_fwd(qd, kd, vd, s, wl.block, K, mode)
+        grads = ssa().ssa_attn_bwd(qd, kd, vd, s, fwd, gd, wl.block, K, mode)
+        outs.append((fwd, grads))
+    torch.cuda.synchronize()
+    (fa, ga), (fb, gb) = outs
+    for key in ("h_full", "h_sparse", "lse_full", "lse_sparse", "delta", "losses"):
+        if key in fa:
+            assert torch.equal(fa[key], fb[key]), key
+    for n, a, b in zip(("dq", "dk", "dv"), ga, gb):
+        # fp32 atomics (the generic path's dk / dv, the sparse-only dq) may
+        # add in another order: those compare within the dtype's tolerance
+        if wl.dtype == torch.bfloat16 and not (mode == oracle.SPARSE_ONLY and n == "dq"):
+            assert torch.equal(a, b), n
+        else:
+            assert_close(n, a, b.double().cpu().numpy(), wl.dtype)
