@@ -30,7 +30,9 @@
 // a selected block are P_full * 2^(m_full - m_sparse), an exact fp32 product,
 // whenever that exponent is at most 64; otherwise they are evaluated
 // directly.  When every block is selected the two streams execute identical
-// operations and agree bit for bit.
+// operations and agree bit for bit.  The probabilities enter the P V products
+// in bf16 and the row sums add exactly those rounded values, so each output
+// row is a weighted mean of value rows with the weights the products used.
 
 #include "common.h"
 #include "internal.h"
@@ -138,7 +140,7 @@ __global__ void __launch_bounds__(256, 2)
   // diagnostics (STATS): the full stream's mass on the first key block, and
   // sum_i e_i x_i with x_i = z_i log2(e) - mf and e_i = 2^x_i, both relative
   // to the running maximum like lf, for the entropy ln2 (log2 lf - ex / lf)
-  float sink_l = 0.f, ex_l = 0.f;
+  float sink_l = 0.f, ex_l = 0.f, lfe = 0.f;   // lfe: the unrounded row sum (diagnostics)
 
   const int j_last = min(qend - 1, q0 + kBM - 1) / kBN;
   if (kSparse) __syncthreads();
@@ -220,30 +222,45 @@ __global__ void __launch_bounds__(256, 2)
         for (int st = 0; st < 2; ++st) {
           float p[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            p[e] = sb ? fast_exp2(fmaf(s[8 * st + e], scale_log2, -msn)) : 0.f;
-            sum_s += p[e];
-          }
-          ps[st] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+          for (int e = 0; e < 8; ++e) p[e] = sb ? fast_exp2(fmaf(s[8 * st + e], scale_log2, -msn)) : 0.f;
+          ps[st] = to_bf16x8_sum(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], sum_s);
         }
       }
 
       // ---- full stream
       bf16x8 pf[2];
-      float sum = 0.f, ex = 0.f;
+      float sum = 0.f, ex = 0.f, sume = 0.f;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         float x = fmaf(s[i], scale_log2, -mfn);
         if (STATS) x = fmaxf(x, -256.f);           // masked keys: e = 0 and e x = 0, not NaN
         s[i] = fast_exp2(x);
-        sum += s[i];
-        if (STATS) ex = fmaf(s[i], x, ex);
+        if (STATS) {
+          sume += s[i];
+          ex = fmaf(s[i], x, ex);
+        }
+      }
+      // P enters the products in bf16: round it here, and let the row sum
+      // add exactly those weights (s keeps the rounded values)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        pf[st] = to_bf16x8_sum(s[8 * st], s[8 * st + 1], s[8 * st + 2], s[8 * st + 3], s[8 * st + 4],
+                               s[8 * st + 5], s[8 * st + 6], s[8 * st + 7], sum);
+        const uint4 u = __builtin_bit_cast(uint4, pf[st]);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          s[8 * st + 2 * k] = __uint_as_float(w[k] << 16);
+          s[8 * st + 2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        }
       }
       if (STATS) {
-        // moving the maximum by dm = mfn - mf shifts every earlier x by -dm
-        // and scales every earlier e by alpha (0 on the first update)
-        ex_l = (alpha == 0.f ? 0.f : alpha * fmaf(-(mfn - mf), lf, ex_l)) + ex;
-        sink_l = sink_l * alpha + (kbase < block ? sum : 0.f);
+        // the diagnostics use the unrounded weights: moving the maximum by
+        // dm = mfn - mf shifts every earlier x by -dm and scales every earlier
+        // e by alpha (0 on the first update)
+        ex_l = (alpha == 0.f ? 0.f : alpha * fmaf(-(mfn - mf), lfe, ex_l)) + ex;
+        sink_l = sink_l * alpha + (kbase < block ? sume : 0.f);
+        lfe = lfe * alpha + sume;
       }
       lf = lf * alpha + sum;
       if (__any(alpha != 1.f)) {
@@ -251,10 +268,6 @@ __global__ void __launch_bounds__(256, 2)
         for (int dt = 0; dt < 4; ++dt) of[dt] *= alpha;
       }
       mf = mfn;
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-        pf[st] = to_bf16x8(s[8 * st], s[8 * st + 1], s[8 * st + 2], s[8 * st + 3], s[8 * st + 4],
-                           s[8 * st + 5], s[8 * st + 6], s[8 * st + 7]);
       if (kSparse && sparse_any) {
         if (rescale) {
           // exact: the factor is a power of two, so the row sum is the full
@@ -312,6 +325,7 @@ __global__ void __launch_bounds__(256, 2)
   if (STATS) {
     sink_l += __shfl_xor(sink_l, 32, 64);
     ex_l += __shfl_xor(ex_l, 32, 64);
+    lfe += __shfl_xor(lfe, 32, 64);
   }
   ls += __shfl_xor(ls, 32, 64);
   const float inv_f = 1.f / lf, inv_s = 1.f / ls;
@@ -353,8 +367,8 @@ __global__ void __launch_bounds__(256, 2)
       a.row_sq[row] = sq;
     }
     if (STATS) {
-      a.sink_mass[row] = sink_l / lf;
-      a.entropy[row] = kLn2 * (fast_log2(lf) - ex_l / lf);
+      a.sink_mass[row] = sink_l / lfe;
+      a.entropy[row] = kLn2 * (fast_log2(lfe) - ex_l / lfe);
     }
   }
 }

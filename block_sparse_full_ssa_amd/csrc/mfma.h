@@ -64,6 +64,23 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float x0, float x1, float x2, float 
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// Eight fp32 weights -> one bf16 operand (round to nearest even), adding the
+// rounded values to `sum`: a softmax row sum built this way counts exactly
+// the weights that the matrix product with V uses, so the normalised output
+// is a true weighted mean of the value rows (a lone key gives its value row).
+__device__ __forceinline__ bf16x8 to_bf16x8_sum(float x0, float x1, float x2, float x3, float x4, float x5,
+                                                float x6, float x7, float& sum) {
+  uint4 u;
+  u.x = pack_bf16x2(x0, x1);
+  u.y = pack_bf16x2(x2, x3);
+  u.z = pack_bf16x2(x4, x5);
+  u.w = pack_bf16x2(x6, x7);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) sum += __uint_as_float(w[k] << 16) + __uint_as_float(w[k] & 0xffff0000u);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -144,16 +144,15 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
 #pragma unroll
     for (int kh = 0; kh < KH; ++kh) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        s[kh][i] = fast_exp2(s[kh][i] - m);
-        sum += s[kh][i];
-      }
+      for (int i = 0; i < 16; ++i) s[kh][i] = fast_exp2(s[kh][i] - m);
       // O^T += V^T P^T; V^T for k-step st: lane (d = 32 dt + col, g) holds
       // keys 32 kh + 16 st + 8 (s / 4) + 4 g + s % 4 (transpose reads)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        const bf16x8 pb = to_bf16x8(s[kh][8 * st], s[kh][8 * st + 1], s[kh][8 * st + 2], s[kh][8 * st + 3],
-                                    s[kh][8 * st + 4], s[kh][8 * st + 5], s[kh][8 * st + 6], s[kh][8 * st + 7]);
+        // P in bf16; the row sum adds exactly these rounded weights
+        const bf16x8 pb = to_bf16x8_sum(s[kh][8 * st], s[kh][8 * st + 1], s[kh][8 * st + 2], s[kh][8 * st + 3],
+                                        s[kh][8 * st + 4], s[kh][8 * st + 5], s[kh][8 * st + 6], s[kh][8 * st + 7],
+                                        sum);
         const int r0 = kh * 32 + st * 16 + 4 * gk + srow, r1 = r0 + 8;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
