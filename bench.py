@@ -7,11 +7,27 @@ outputs, delta, alignment losses) and the backward with the active stream
 drawn 50/50 per step from the seed.  Inputs are synthetic and resident in
 HBM before timing starts.
 
-Reported (one JSON line): algorithmic TFLOP/s of the step, tokens/s, the
-roofline of the dominant kernel (its algorithmic flops per launch over its
-HIP-event-timed average launch), the CPU oracle timed on a bounded sample of
-the same workload, the FULL_ONLY fwd+bwd rate on the same layer and the
-sparse-stream forward speedup t(FULL_ONLY fwd) / t(SPARSE_ONLY fwd).
+Reported (one JSON line):
+  value / ms_per_step   algorithmic TFLOP/s of the step, wall clock over the
+                        timed steps with the library's event timing off;
+  roofline              the dominant kernel: its algorithmic flops per launch
+                        over its average launch time, from HIP events recorded
+                        on the launch stream in a second pass of as many steps;
+  top_k_sweep           the step at top_k 4, 8, 16, 32;
+  full_only             FULL_ONLY fwd+bwd, the full stream alone (14 d P_full B Hq);
+  sparse_fwd_speedup    per top_k, t(FULL_ONLY fwd) / t(SPARSE_ONLY fwd) next to
+                        P_full / P_sparse and N / (top_k block), with the HBM
+                        rates of the selection and the sparse-only forward
+                        against their compulsory bytes;
+  sparse_only_train     SPARSE_ONLY fwd+bwd (pure sparse training) against
+                        FULL_ONLY fwd+bwd;
+  long_n64k_sinks       the 64K-context layer with planted sinks: selection +
+                        dual forward;
+  multilayer_b4_n8k_l4  four layers forward then backward, 10 timed steps;
+  decode_128k           sparse vs full decode and prefill over a 128K cache;
+  cpu_baseline          the fp64 oracle on the host's cores: one whole
+                        (batch, KV head) unit of the training step, scaled by
+                        the B * Hkv units of the layer to seconds per step.
 
 Algorithmic work (FlashAttention convention, recompute included): per causal
 (query, key) pair 4d flops forward and 10d backward, counted for the full
@@ -92,45 +108,27 @@ def parse():
     ap.add_argument("--seqlen", type=int, default=None, help="override N (experiments only)")
     ap.add_argument("--batch", type=int, default=None, help="override B (experiments only)")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--sweep", action="store_true", help="also time every top_k of the workload's sweep")
+    ap.add_argument("--no-sweep", action="store_true", help="skip the top_k sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the 128K-cache decode leg")
     ap.add_argument("--no-single-stream", action="store_true",
                     help="skip the FULL_ONLY / SPARSE_ONLY measurements")
-    ap.add_argument("--cpu-rows", type=int, default=12288, help="query rows in the CPU-oracle sample")
+    ap.add_argument("--no-other-layers", action="store_true",
+                    help="skip the 64K-context layer and the four-layer slice")
     return ap.parse_args()
 
 
-def run_steps(ssa, q, k, v, dout, wl, K, modes, steps, warmup):
-    import torch
-
-    def step(mode):
-        sel = ssa.ssa_select_blocks(q, k, wl.block, K)
-        fwd = ssa.ssa_attn_fwd(q, k, v, sel, wl.block, K, mode)
-        grads = ssa.ssa_attn_bwd(q, k, v, sel, fwd, dout, wl.block, K, mode)
-        return fwd, grads
-
-    for i in range(warmup):
-        step(modes[i])
-    torch.cuda.synchronize()
-    ssa.timing_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        out = step(modes[warmup + i])
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    kernels = {}
-    for name in ssa.kernel_names():
-        ms, n = ssa.timing_query(name)
-        if n:
-            kernels[name] = {"total_ms": ms, "launches": n, "avg_ms": ms / n}
-    ssa.timing_enable(False)
-    del out
-    return (t1 - t0) * 1000.0 / steps, kernels
+def train_steps(ssa, q, k, v, dout, block, K, modes):
+    """One training step per mode in ``modes``: select + dual fwd + bwd."""
+    out = None
+    for mode in modes:
+        sel = ssa.ssa_select_blocks(q, k, block, K)
+        fwd = ssa.ssa_attn_fwd(q, k, v, sel, block, K, mode)
+        out = ssa.ssa_attn_bwd(q, k, v, sel, fwd, dout, block, K, mode)
+    return out
 
 
-def time_calls(fn, reps, warm=1):
+def wall_ms(fn, calls, warm=1):
     """Wall-clock milliseconds per call of ``fn`` (GPU work included), after warm-up."""
     import torch
 
@@ -138,91 +136,204 @@ def time_calls(fn, reps, warm=1):
         fn()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(reps):
+    for _ in range(calls):
         fn()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) * 1000.0 / reps
+    return (time.perf_counter() - t0) * 1000.0 / calls
 
 
-def hbm_rates(ssa, q, k, v, sel, wl, K, reps):
-    """GB/s of the HBM-bound steps (a2 selection, a8 sparse-only forward)
-    from the library's device-time events, against the 8 TB/s peak.  Bytes
-    are those each step must move: selection reads q and k, writes and reads
-    the block means and writes sel; the sparse-only forward reads k, v and
-    sel, gathers the query row of every selected (row, block) pair into its
-    key block's bucket (d bf16 values per pair), writes and reads one partial
-    per pair (d bf16 values + an fp32 log-sum-exp), and writes h_sparse and
-    lse_sparse."""
+def kernel_times(ssa, fn):
+    """Per-kernel device times of ``fn()`` from the library's HIP events
+    (recorded on each kernel's launch stream): {name: (total ms, launches)}."""
+    import torch
+
+    torch.cuda.synchronize()
+    ssa.timing_enable(True)
+    fn()
+    torch.cuda.synchronize()
+    res = {}
+    for name in ssa.kernel_names():
+        ms, n = ssa.timing_query(name)
+        if n:
+            res[name] = (ms, n)
+    ssa.timing_enable(False)
+    return res
+
+
+def hbm_rates(ssa, q, k, v, sel, block, K, reps):
+    """HBM rates of the two HBM-bound steps (a2 selection, a8 sparse-only
+    forward), device time from the library's events, against the 8 TB/s peak.
+
+    Compulsory bytes (what the step must move at least): selection reads q
+    and k and writes sel; the sparse-only forward reads q, k, v and sel and
+    writes h_sparse and lse_sparse.  The implementation's bytes are given
+    apart: the selection also writes and reads the block means; the
+    sparse-only forward gathers the query row of every selected (row, block)
+    pair into its key block's bucket, and writes and reads one partial per
+    pair (d bf16 values and an fp32 log-sum-exp)."""
     B, Hq, N, d = q.shape
-    blk, nb = wl.block, N // wl.block
+    nb = N // block
     el = q.element_size()
 
     def dev_ms(fn, names):
-        ssa.timing_enable(True)
-        for _ in range(reps):
-            fn()
-        ms = sum(ssa.timing_query(n)[0] for n in names) / reps
-        ssa.timing_enable(False)
-        return ms
+        t = kernel_times(ssa, lambda: [fn() for _ in range(reps)])
+        return sum(t[n][0] for n in names if n in t) / reps
 
-    ms_sel = dev_ms(lambda: ssa.ssa_select_blocks(q, k, blk, K), ("block_mean", "select"))
-    ms_sp = dev_ms(lambda: ssa.ssa_attn_fwd(q, k, v, sel, blk, K, ssa.SPARSE_ONLY, want_lse=True),
+    ms_sel = dev_ms(lambda: ssa.ssa_select_blocks(q, k, block, K), ("block_mean", "select"))
+    ms_sp = dev_ms(lambda: ssa.ssa_attn_fwd(q, k, v, sel, block, K, ssa.SPARSE_ONLY),
                    ("bucket", "sparse_part", "sparse_merge"))
-    mu_bytes = B * wl.hkv * nb * d * 4
-    sel_bytes = q.numel() // d * K * 4
-    b_sel = q.numel() * el + k.numel() * el + 2 * mu_bytes + sel_bytes
-    entries = B * Hq * sum(min(K, t // blk + 1) for t in range(N))
-    b_sp = (k.numel() + v.numel()) * el + sel_bytes + entries * d * el + q.numel() * el + q.numel() // d * 4 \
-        + 2 * entries * (d * 2 + 4)
-    return {"select_ms": round(ms_sel, 4), "select_GBps": round(b_sel / (ms_sel / 1e3) / 1e9, 1),
-            "select_frac_of_hbm": round(b_sel / (ms_sel / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-            "sparse_fwd_ms": round(ms_sp, 4), "sparse_fwd_GBps": round(b_sp / (ms_sp / 1e3) / 1e9, 1),
-            "sparse_fwd_frac_of_hbm": round(b_sp / (ms_sp / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-            "select_bytes": b_sel, "sparse_fwd_bytes": b_sp}
+    rows = q.numel() // d
+    sel_bytes = rows * K * 4
+    mu_bytes = B * k.shape[1] * nb * d * 4
+    c_sel = (q.numel() + k.numel()) * el + sel_bytes
+    c_sp = (q.numel() + k.numel() + v.numel()) * el + sel_bytes + q.numel() * el + rows * 4
+    entries = B * Hq * sum(min(K, t // block + 1) for t in range(N))
+    i_sel = c_sel + 2 * mu_bytes
+    i_sp = c_sp + entries * d * el + 2 * entries * (d * 2 + 4)
+
+    def rate(b, ms):
+        return round(b / (ms / 1e3) / 1e9, 1)
+
+    return {"select_ms": round(ms_sel, 4), "select_bytes": c_sel, "select_GBps": rate(c_sel, ms_sel),
+            "select_frac_of_hbm": round(rate(c_sel, ms_sel) / HBM_PEAK_GBS, 4),
+            "sparse_fwd_ms": round(ms_sp, 4), "sparse_fwd_bytes": c_sp, "sparse_fwd_GBps": rate(c_sp, ms_sp),
+            "sparse_fwd_frac_of_hbm": round(rate(c_sp, ms_sp) / HBM_PEAK_GBS, 4),
+            "implementation": {"select_bytes": i_sel, "select_GBps": rate(i_sel, ms_sel),
+                               "sparse_fwd_bytes": i_sp, "sparse_fwd_GBps": rate(i_sp, ms_sp)},
+            "bytes": "compulsory: select q + k read, sel written; sparse-only fwd q, k, v, sel read, "
+                     "h_sparse + lse_sparse written"}
 
 
-def single_stream(ssa, q, k, v, dout, wl, ks, reps):
-    """FULL_ONLY fwd+bwd TFLOP/s (14 d P_full B Hq per step) and, per top_k,
-    the sparse-stream forward speedup t(FULL_ONLY fwd) / t(SPARSE_ONLY fwd)
-    next to P_full / P_sparse and N / (top_k block)."""
+def single_stream(ssa, q, k, v, dout, block, K0, ks, reps):
+    """FULL_ONLY fwd+bwd (14 d P_full B Hq per step), and per top_k the
+    sparse-stream forward speedup and the SPARSE_ONLY fwd+bwd step."""
     B, Hq, N, d = q.shape
-    blk = wl.block
-    pf, _ = pairs(N, blk, wl.top_k)
+    pf, _ = pairs(N, block, K0)
+
+    def full_fwd():
+        return ssa.ssa_attn_fwd(q, k, v, None, block, K0, ssa.FULL_ONLY)
 
     def full_step():
-        f = ssa.ssa_attn_fwd(q, k, v, None, blk, wl.top_k, ssa.FULL_ONLY)
-        ssa.ssa_attn_bwd(q, k, v, None, f, dout, blk, wl.top_k, ssa.FULL_ONLY)
+        f = full_fwd()
+        ssa.ssa_attn_bwd(q, k, v, None, f, dout, block, K0, ssa.FULL_ONLY)
 
-    ms_full = time_calls(full_step, reps)
-    ms_full_fwd = time_calls(lambda: ssa.ssa_attn_fwd(q, k, v, None, blk, wl.top_k, ssa.FULL_ONLY), reps)
+    ms_full = wall_ms(full_step, reps)
+    ms_full_fwd = wall_ms(full_fwd, reps)
     fl = 14.0 * d * pf * B * Hq
     out = {"full_only": {"ms_per_step": round(ms_full, 3), "TFLOP/s": round(fl / (ms_full / 1e3) / 1e12, 2),
                          "frac_of_bf16_peak": round(fl / (ms_full / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "fwd_ms": round(ms_full_fwd, 3),
+                         "fwd_ms": round(ms_full_fwd, 3), "bwd_ms": round(ms_full - ms_full_fwd, 3),
+                         "fwd_frac_of_bf16_peak": round(4.0 * d * pf * B * Hq / (ms_full_fwd / 1e3) / 1e12
+                                                        / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "ms_at_half_peak": round(fl / (0.5 * MFMA_BF16_PEAK_TFLOPS * 1e12) * 1e3, 3),
                          "step": "FULL_ONLY fwd + bwd, 14 d P_full B Hq flops"}}
-    sp = {}
+    sp, train = {}, {}
     for kk in ks:
-        sel = ssa.ssa_select_blocks(q, k, blk, kk)
-        ms_sel = time_calls(lambda: ssa.ssa_select_blocks(q, k, blk, kk), reps)
-        ms_sp = time_calls(lambda: ssa.ssa_attn_fwd(q, k, v, sel, blk, kk, ssa.SPARSE_ONLY), reps)
-        a, b = pairs(N, blk, kk)
+        sel = ssa.ssa_select_blocks(q, k, block, kk)
+        ms_sel = wall_ms(lambda: ssa.ssa_select_blocks(q, k, block, kk), reps)
+
+        def sp_fwd():
+            return ssa.ssa_attn_fwd(q, k, v, sel, block, kk, ssa.SPARSE_ONLY)
+
+        def sp_step():
+            f = sp_fwd()
+            ssa.ssa_attn_bwd(q, k, v, sel, f, dout, block, kk, ssa.SPARSE_ONLY)
+
+        ms_sp = wall_ms(sp_fwd, reps)
+        ms_sp_step = wall_ms(sp_step, reps)
+        a, b = pairs(N, block, kk)
         sp[str(kk)] = {"sparse_only_fwd_ms": round(ms_sp, 3), "select_ms": round(ms_sel, 3),
                        "speedup": round(ms_full_fwd / ms_sp, 2),
                        "speedup_incl_select": round(ms_full_fwd / (ms_sp + ms_sel), 2),
-                       "P_full/P_sparse": round(a / b, 2), "N/(K*block)": round(N / (kk * blk), 2),
-                       "hbm": hbm_rates(ssa, q, k, v, sel, wl, kk, reps)}
+                       "P_full/P_sparse": round(a / b, 2), "N/(K*block)": round(N / (kk * block), 2),
+                       "hbm": hbm_rates(ssa, q, k, v, sel, block, kk, reps)}
+        fl_sp = 14.0 * d * b * B * Hq
+        train[str(kk)] = {"sparse_only_fwd_bwd_ms": round(ms_sp_step, 3),
+                          "incl_select_ms": round(ms_sp_step + ms_sel, 3),
+                          "speedup_vs_full_only": round(ms_full / ms_sp_step, 2),
+                          "speedup_incl_select": round(ms_full / (ms_sp_step + ms_sel), 2),
+                          "TFLOP/s": round(fl_sp / (ms_sp_step / 1e3) / 1e12, 2),
+                          "P_full/P_sparse": round(a / b, 2)}
         del sel
     out["sparse_fwd_speedup"] = sp
+    out["sparse_only_train"] = {"per_top_k": train,
+                                "step": "SPARSE_ONLY fwd + bwd (pure sparse training) against FULL_ONLY fwd + bwd"}
 
     # full-stream diagnostics (sink-block mass, entropy, per-head means) in the
     # forward pass: cost over the plain FULL_ONLY forward, and the head means
-    ms_stats = time_calls(lambda: ssa.ssa_attn_fwd(q, k, v, None, blk, wl.top_k, ssa.FULL_ONLY, stats=True),
-                          reps)
-    st = ssa.ssa_attn_fwd(q, k, v, None, blk, wl.top_k, ssa.FULL_ONLY, stats=True)["head_stats"]
+    ms_stats = wall_ms(lambda: ssa.ssa_attn_fwd(q, k, v, None, block, K0, ssa.FULL_ONLY, stats=True), reps)
+    st = ssa.ssa_attn_fwd(q, k, v, None, block, K0, ssa.FULL_ONLY, stats=True)["head_stats"]
     out["full_stats"] = {"fwd_ms": round(ms_stats, 3), "overhead": round(ms_stats / ms_full_fwd - 1.0, 4),
                          "mean_sink_mass": round(float(st[..., 0].mean()), 5),
                          "mean_entropy_nats": round(float(st[..., 1].mean()), 4)}
     return out
+
+
+def long_layer(ssa, dev, seed, reps):
+    """The 64K-context layer with four planted sinks (B=1, 16/4 heads, block 64,
+    top_k 32): selection + dual forward (sparse stream active, full counterpart
+    and delta), inputs drawn on the GPU."""
+    import ssa_inputs as si
+
+    wl = si.WORKLOADS["long_n64k_sinks"]
+    q, k, v, _ = si.draw_qkv(wl, seed, device=str(dev))
+    K, blk = wl.top_k, wl.block
+
+    def step():
+        sel = ssa.ssa_select_blocks(q, k, blk, K)
+        return ssa.ssa_attn_fwd(q, k, v, sel, blk, K, ssa.DUAL_ACTIVE_SPARSE, want_lse=False)
+
+    ms = wall_ms(step, reps)
+    ms_sel = wall_ms(lambda: ssa.ssa_select_blocks(q, k, blk, K), reps)
+    pf, ps = pairs(wl.seqlen, blk, K)
+    fl = 4.0 * wl.head_dim * (pf + ps) * wl.batch * wl.hq
+    return {"workload": wl.name, "ms": round(ms, 3), "select_ms": round(ms_sel, 3),
+            "fwd_TFLOP/s": round(fl / ((ms - ms_sel) / 1e3) / 1e12, 1),
+            "tokens_per_s": round(wl.batch * wl.seqlen / (ms / 1e3), 1),
+            "step": "select + dual forward (4 d (P_full + P_sparse) B Hq forward flops)"}
+
+
+def multilayer(ssa, dev, seed, steps=10, warmup=3):
+    """Four layers (B=4, 32/8 heads, N=8192, top_k 16) with their own inputs:
+    per step every layer's selection and dual forward, then every layer's
+    backward from the last, the active stream drawn per step and shared by
+    the layers; ``steps`` timed steps after ``warmup``; tokens/s =
+    steps B N / t_total."""
+    import torch
+
+    import ssa_inputs as si
+
+    wl = si.WORKLOADS["multilayer_b4_n8k_l4"]
+    K, blk = wl.top_k, wl.block
+    layers = []
+    for layer in range(wl.layers):
+        q, k, v, _ = si.draw_qkv(wl, seed, layer, device=str(dev))
+        layers.append((q, k, v, si.draw_dout(wl, seed, layer, device=str(dev))))
+    modes = [ssa.DUAL_ACTIVE_FULL if m == 0 else ssa.DUAL_ACTIVE_SPARSE
+             for m in si.draw_modes(seed, warmup + steps)]
+
+    def step(mode):
+        saved = []
+        for q, k, v, _ in layers:
+            sel = ssa.ssa_select_blocks(q, k, blk, K)
+            saved.append((sel, ssa.ssa_attn_fwd(q, k, v, sel, blk, K, mode)))
+        for (q, k, v, g), (sel, fwd) in zip(reversed(layers), reversed(saved)):
+            ssa.ssa_attn_bwd(q, k, v, sel, fwd, g, blk, K, mode)
+
+    for i in range(warmup):
+        step(modes[i])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(modes[warmup + i])
+    torch.cuda.synchronize()
+    t = time.perf_counter() - t0
+    pf, ps = pairs(wl.seqlen, blk, K)
+    fl = 14.0 * wl.head_dim * (pf + ps) * wl.batch * wl.hq * wl.layers
+    return {"workload": wl.name, "steps": steps, "warmup": warmup, "seconds": round(t, 4),
+            "ms_per_step": round(t * 1e3 / steps, 3), "tokens_per_s": round(steps * wl.batch * wl.seqlen / t, 1),
+            "TFLOP/s": round(steps * fl / t / 1e12, 2),
+            "frac_of_bf16_peak": round(steps * fl / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
 def decode_128k(ssa, dev, reps):
@@ -238,7 +349,7 @@ def decode_128k(ssa, dev, reps):
     import ssa_inputs as si
 
     wl = si.WORKLOADS["decode_b4_n128k_sinks"]
-    q, k, v = (x.to(dev) for x in si.draw_decode(wl, 0))
+    q, k, v = si.draw_decode(wl, 0, device=str(dev))
     L, blk, K, d = wl.seqlen, wl.block, wl.top_k, wl.head_dim
     mu = torch.empty(wl.batch, wl.hkv, L // blk, d, dtype=torch.float32, device=dev)
     ssa.ssa_cache_block_means(k, mu, blk, 0, L // blk)
@@ -250,12 +361,8 @@ def decode_128k(ssa, dev, reps):
     def gpu_ms(mode, m):
         # the library's events around its decode launches (selection, parts,
         # merge): device time, without the host's per-call overhead
-        ssa.timing_enable(True)
-        for _ in range(reps):
-            ssa.ssa_decode(q, k, v, m, pos, blk, K, mode)
-        total, n = ssa.timing_query("decode")
-        ssa.timing_enable(False)
-        return total / n
+        t = kernel_times(ssa, lambda: [ssa.ssa_decode(q, k, v, m, pos, blk, K, mode) for _ in range(reps)])
+        return t["decode"][0] / t["decode"][1]
 
     ms_sp = gpu_ms(ssa.SPARSE_ONLY, mu)
     ms_fu = gpu_ms(ssa.FULL_ONLY, None)
@@ -266,23 +373,20 @@ def decode_128k(ssa, dev, reps):
     bytes_fu = wl.batch * wl.hkv * L * row
     # chunked prefill: the last 4096 prompt tokens against the same cache
     C = 4096
-    g = torch.Generator().manual_seed(21)
-    qc = torch.randn(wl.batch, wl.hq, C, d, generator=g).to(q.dtype).to(dev)
+    g = torch.Generator(device=dev).manual_seed(21)
+    qc = torch.randn(wl.batch, wl.hq, C, d, generator=g, device=dev).to(q.dtype)
 
     def dev_ms(fn, names):
         fn()
-        torch.cuda.synchronize()
-        ssa.timing_enable(True)
-        for _ in range(3):
-            fn()
-        ms = sum(ssa.timing_query(n)[0] for n in names) / 3
-        ssa.timing_enable(False)
-        return ms
+        t = kernel_times(ssa, lambda: [fn() for _ in range(3)])
+        return sum(t[n][0] for n in names if n in t) / 3
 
     pf_sp = dev_ms(lambda: ssa.ssa_prefill(qc, k, v, mu, L - C, blk, K, ssa.SPARSE_ONLY),
                    ("select", "bucket", "sparse_part", "sparse_merge"))
+    pf_sel = dev_ms(lambda: ssa.ssa_prefill(qc, k, v, mu, L - C, blk, K, ssa.SPARSE_ONLY), ("select",))
     pf_fu = dev_ms(lambda: ssa.ssa_prefill(qc, k, v, None, L - C, blk, K, ssa.FULL_ONLY), ("fwd_mfma",))
     prefill = {"chunk": C, "positions": f"{L - C} .. {L - 1}", "sparse_ms": round(pf_sp, 3),
+               "sparse_select_ms": round(pf_sel, 3),
                "full_ms": round(pf_fu, 3), "speedup": round(pf_fu / pf_sp, 2),
                "full_TFLOPs": round(4 * d * wl.batch * wl.hq * sum(range(L - C + 1, L + 1)) / (pf_fu / 1e3) / 1e12, 1)}
     return {"workload": wl.name, "prefill": prefill, "positions": "last token of each sequence (t = 131071)",
@@ -306,57 +410,72 @@ def measured_ceilings(ssa, dev):
     dst = torch.empty_like(src)
     ssa.ssa_probe_mfma(sink, blocks, 100)
     ssa.ssa_probe_copy(src, dst)
-    torch.cuda.synchronize()
-    ssa.timing_enable(True)
-    for _ in range(3):
-        ssa.ssa_probe_mfma(sink, blocks, iters)
-        ssa.ssa_probe_copy(src, dst)
-    mfma_ms, n1 = ssa.timing_query("probe_mfma")
-    copy_ms, n2 = ssa.timing_query("probe_copy")
-    ssa.timing_enable(False)
+
+    def both():
+        for _ in range(3):
+            ssa.ssa_probe_mfma(sink, blocks, iters)
+            ssa.ssa_probe_copy(src, dst)
+
+    t = kernel_times(ssa, both)
+    mfma_ms, n1 = t["probe_mfma"]
+    copy_ms, n2 = t["probe_copy"]
     nbytes = src.numel() * 4
     return {"mfma_bf16_tflops": round(blocks * 16 * iters * 32768 / (mfma_ms / n1 / 1e3) / 1e12, 1),
             "copy_gbs": round(2 * nbytes / (copy_ms / n2 / 1e3) / 1e9, 1),
             "note": "dense 32x32x16 bf16 matrix loop on every SIMD; 1 GiB device copy (read + write)"}
 
 
-def cpu_baseline(wl, K, seed, rows):
-    """The fp64 oracle on the host: select + forward + backward of the last
-    ``rows`` query rows of batch 0 / query head 0 (each with all its causal
-    keys), as algorithmic TFLOP/s of that sample."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_library() -> str:
+    try:
+        import threadpoolctl
+
+        info = [i for i in threadpoolctl.threadpool_info() if i.get("user_api") == "blas"]
+        if info:
+            i = info[0]
+            return f"{i.get('internal_api', '?')} {i.get('version', '')} ({os.path.basename(i.get('filepath', ''))})"
+    except Exception:                       # noqa: BLE001 -- informational only
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, K, seed, q, k, v, dout, mode):
+    """The fp64 oracle on the host's cores: one whole (batch 0, KV head 0)
+    unit of the training step -- selection, both streams and the backward of
+    its G query heads over all N rows, every key of the KV head -- on a
+    process pool with one BLAS thread per worker, scaled by the layer's
+    B * Hkv units to seconds per step."""
     import numpy as np
-    import threadpoolctl
 
-    import oracle
     import ssa_inputs as si
+    from oracle import parallel
 
-    q, k, v, _ = si.draw_qkv(wl, seed)
-    dout = si.draw_dout(wl, seed)
-    N, d, G = wl.seqlen, wl.head_dim, wl.group
-    t_idx = np.arange(N - rows, N)
-    # only the KV head of query head 0 and the sampled rows are converted
-    qf = si.to_f64(q[:1, :1])
-    kf, vf = si.to_f64(k[:1, :1]), si.to_f64(v[:1, :1])
-    gf = si.to_f64(dout[:1, :1])
-    scale = 1.0 / np.sqrt(d)
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info] or [1])
-    t0 = time.perf_counter()
-    mu = oracle.block_means(kf, wl.block)
-    sel_rows, _ = oracle.select_rows(qf[0, 0, t_idx], t_idx, mu[0, 0], wl.block, K)
-    sel = np.full((1, 1, N, K), -1, np.int32)
-    sel[0, 0, t_idx] = sel_rows
-    oracle.attend_rows(qf[0, 0, t_idx], t_idx, kf[0, 0], vf[0, 0], sel_rows, wl.block, scale)
-    oracle.dq_rows(qf, kf, vf, sel, wl.block, scale, 1, oracle.DUAL_ACTIVE_FULL, gf, 0, 0, t_idx)
-    dt = time.perf_counter() - t0
-    n_sparse = sum(min(K, t // wl.block + 1) * wl.block - (wl.block - 1 - t % wl.block) for t in t_idx)
-    n_full = int((t_idx + 1).sum())
-    flops = 14.0 * d * (n_full + n_sparse)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"batch 0, query head 0, last {rows} query rows with all their causal keys: "
-                      f"selection + dual forward + backward (dq and these rows' dk/dv terms), fp64 numpy; "
-                      f"{flops:.3g} algorithmic flops"}
+    G, d = wl.group, wl.head_dim
+    b, c = 0, 0
+    hs = slice(c * G, (c + 1) * G)
+    res = parallel.unit_step(si.to_f64(q[b, hs]), si.to_f64(k[b, c]), si.to_f64(v[b, c]), wl.block, K,
+                             1.0 / float(np.sqrt(d)), mode, dout_u=si.to_f64(dout[b, hs]), M=q.numel())
+    pf, ps = pairs(wl.seqlen, wl.block, K)
+    unit_flops = 14.0 * d * (pf + ps) * G
+    units = wl.batch * wl.hkv
+    sec = res["seconds"]
+    return {"value": unit_flops / sec / 1e12, "unit": "TFLOP/s", "cores": res["workers"], "kind": "oracle",
+            "seconds_unit": round(sec, 3), "units_per_step": units, "seconds_per_step": round(sec * units, 2),
+            "cpu_model": _cpu_model(), "blas": _blas_library(),
+            "sample": f"one whole (batch {b}, KV head {c}) unit of {wl.name} at top_k {K}: selection, both "
+                      f"streams and the backward of its {G} query heads over all {wl.seqlen} rows, every key "
+                      f"of the KV head; fp64 numpy oracle on {res['workers']} worker processes (1 BLAS thread "
+                      f"each); {unit_flops:.4g} algorithmic flops; scaled by the {units} units of the layer"}
 
 
 def main():
@@ -368,7 +487,6 @@ def main():
 
     import torch
 
-    import block_sparse_full_ssa_amd as ssa
     import ssa_inputs as si
 
     wl = si.WORKLOADS[args.workload]
@@ -380,17 +498,39 @@ def main():
     if changes:
         wl = si.scaled_down(wl, **changes)
     K = args.top_k or wl.top_k
+    q_c, k_c, v_c, _ = si.draw_qkv(wl, args.seed)
+    dout_c = si.draw_dout(wl, args.seed)
+    modes_bits = si.draw_modes(args.seed, args.warmup + args.steps)
+
+    # the CPU leg runs first, before the GPU is touched (its worker processes
+    # start from a process without GPU state)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, K, args.seed, q_c, k_c, v_c, dout_c, 1 if modes_bits[0] else 0)
+
+    import block_sparse_full_ssa_amd as ssa
+
     dev = torch.device("cuda:0")
-    q, k, v, _ = si.draw_qkv(wl, args.seed)
-    dout = si.draw_dout(wl, args.seed)
-    q, k, v, dout = (x.to(dev) for x in (q, k, v, dout))
-    modes = si.draw_modes(args.seed, args.warmup + args.steps)
-    modes = [ssa.DUAL_ACTIVE_FULL if m == 0 else ssa.DUAL_ACTIVE_SPARSE for m in modes]
+    q, k, v, dout = (x.to(dev) for x in (q_c, k_c, v_c, dout_c))
+    del q_c, k_c, v_c, dout_c
+    modes = [ssa.DUAL_ACTIVE_FULL if m == 0 else ssa.DUAL_ACTIVE_SPARSE for m in modes_bits]
     torch.cuda.synchronize()
 
     B, Hq, N, d = wl.batch, wl.hq, wl.seqlen, wl.head_dim
-    ms, kernels = run_steps(ssa, q, k, v, dout, wl, K, modes, args.steps, args.warmup)
-    pf, ps = pairs(N, wl.block, K)
+    blk = wl.block
+    # headline: W warm-up steps, then K timed steps with the event timing off
+    train_steps(ssa, q, k, v, dout, blk, K, modes[:args.warmup])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    train_steps(ssa, q, k, v, dout, blk, K, modes[args.warmup:])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / args.steps
+    # per-kernel device times: the same steps again with events on every launch
+    t1 = time.perf_counter()
+    kt = kernel_times(ssa, lambda: train_steps(ssa, q, k, v, dout, blk, K, modes[args.warmup:]))
+    ms_events = (time.perf_counter() - t1) * 1000.0 / args.steps
+    kernels = {n: {"total_ms": t, "launches": c, "avg_ms": t / c} for n, (t, c) in kt.items()}
+    pf, ps = pairs(N, blk, K)
     flops = 14.0 * d * (pf + ps) * B * Hq
     tflops = flops / (ms / 1000.0) / 1e12
 
@@ -409,27 +549,43 @@ def main():
                    for n, kk in kernels.items() if n in per_launch}
 
     sweep = None
-    if args.sweep and wl.top_k_sweep:
+    if not args.no_sweep and wl.top_k_sweep:
         sweep = {}
+        n_sw = max(4, args.steps // 2)
+        cyc = [modes[i % len(modes)] for i in range(2 + n_sw)]
         for kk in wl.top_k_sweep:
-            m2, _ = run_steps(ssa, q, k, v, dout, wl, kk, modes, max(3, args.steps // 2), 1)
-            a, b = pairs(N, wl.block, kk)
-            sweep[str(kk)] = {"ms_per_step": round(m2, 3),
-                              "TFLOP/s": round(14.0 * d * (a + b) * B * Hq / (m2 / 1000) / 1e12, 2)}
+            train_steps(ssa, q, k, v, dout, blk, kk, cyc[:2])
+            torch.cuda.synchronize()
+            ts = time.perf_counter()
+            train_steps(ssa, q, k, v, dout, blk, kk, cyc[2:])
+            torch.cuda.synchronize()
+            m2 = (time.perf_counter() - ts) * 1000.0 / n_sw
+            a, b = pairs(N, blk, kk)
+            f2 = 14.0 * d * (a + b) * B * Hq
+            sweep[str(kk)] = {"ms_per_step": round(m2, 3), "TFLOP/s": round(f2 / (m2 / 1000) / 1e12, 2),
+                              "frac_of_bf16_peak": round(f2 / (m2 / 1000) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                              "tokens_per_s": round(B * N / (m2 / 1000.0), 1)}
 
     single = None
     if not args.no_single_stream:
-        ks = list(wl.top_k_sweep) if (args.sweep and wl.top_k_sweep) else [K]
-        single = single_stream(ssa, q, k, v, dout, wl, ks, max(3, args.steps // 2))
+        ks = list(wl.top_k_sweep) if (not args.no_sweep and wl.top_k_sweep) else [K]
+        single = single_stream(ssa, q, k, v, dout, blk, K, ks, max(3, args.steps // 2))
+    del q, k, v, dout
+    torch.cuda.empty_cache()
+
+    others = {}
+    if not args.no_other_layers:
+        others["long_n64k_sinks"] = long_layer(ssa, dev, args.seed, 3)
+        torch.cuda.empty_cache()
+        others["multilayer_b4_n8k_l4"] = multilayer(ssa, dev, args.seed)
+        torch.cuda.empty_cache()
 
     decode = None if args.no_decode else decode_128k(ssa, dev, max(10, args.steps))
     ceilings = measured_ceilings(ssa, dev)
     if roofline is not None:
         roofline["frac_of_measured_peak"] = round(roofline["achieved"] / ceilings["mfma_bf16_tflops"], 4)
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, K, args.seed, min(args.cpu_rows, N))
+    if cpu is not None:
+        cpu["gpu_speedup"] = round(cpu["seconds_per_step"] / (ms / 1e3), 1)
 
     line = {
         "metric": "SSA fwd+bwd attention TFLOP/s and tokens/s at 16K ctx; % of bf16 MFMA peak",
@@ -445,23 +601,25 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": B, "heads_q": Hq, "heads_kv": wl.hkv, "seq_len": N,
-                   "head_dim": d, "block": wl.block, "top_k": K,
+                   "head_dim": d, "block": blk, "top_k": K,
                    "step": "select + dual fwd + bwd, active stream 50/50 per step"},
         "tokens_per_s": round(B * N / (ms / 1000.0), 1),
         "frac_of_bf16_peak": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
         "algorithmic_flops_per_step": flops,
+        "ms_per_step_with_kernel_events": round(ms_events, 3),
         "kernels_ms_avg": {n: round(kk["avg_ms"], 4) for n, kk in kernels.items()},
         "roofline": roofline,
         "kernel_frac_of_bf16_peak": kernel_frac,
         "measured_ceilings": ceilings,
-        "decode_128k": decode,
         "frac_of_measured_mfma": round(tflops / ceilings["mfma_bf16_tflops"], 4),
         "cpu_baseline": cpu,
     }
-    if single:
-        line.update(single)
     if sweep:
         line["top_k_sweep"] = sweep
+    if single:
+        line.update(single)
+    line.update(others)
+    line["decode_128k"] = decode
     print(json.dumps(line), flush=True)
 
 

@@ -77,27 +77,31 @@ WORKLOADS: Dict[str, Workload] = {
 }
 
 
-def generator(seed: int) -> torch.Generator:
-    g = torch.Generator(device="cpu")
+def generator(seed: int, device: str = "cpu") -> torch.Generator:
+    """A seeded torch generator.  The tests draw on the CPU (the same bits on
+    any machine); the benchmark may draw its largest layers on the GPU
+    (seeded too, but another stream of numbers than the CPU's)."""
+    g = torch.Generator(device=device)
     g.manual_seed(int(seed))
     return g
 
 
 def draw(gen: torch.Generator, shape, dtype: torch.dtype, prescale: float = 1.0) -> torch.Tensor:
-    """N(0, 1) * prescale, rounded (round-to-nearest-even) to ``dtype``."""
-    x = torch.randn(*shape, generator=gen, dtype=torch.float32)
+    """N(0, 1) * prescale, rounded (round-to-nearest-even) to ``dtype``, on the
+    generator's device."""
+    x = torch.randn(*shape, generator=gen, dtype=torch.float32, device=gen.device)
     if prescale != 1.0:
         x = x * prescale
     return x.to(dtype)
 
 
-def draw_qkv(wl: Workload, seed: int, layer: int = 0):
+def draw_qkv(wl: Workload, seed: int, layer: int = 0, device: str = "cpu"):
     """q [B,Hq,N,d], k and v [B,Hkv,N,d], drawn in that order from one stream.
 
     Also returns the generator, positioned after the last draw, so that a
     screening pass can keep redrawing query rows from the same stream.
     """
-    gen = generator(seed + 1000 * layer)
+    gen = generator(seed + 1000 * layer, device)
     B, N, d = wl.batch, wl.seqlen, wl.head_dim
     q = draw(gen, (B, wl.hq, N, d), wl.dtype, wl.prescale)
     k = draw(gen, (B, wl.hkv, N, d), wl.dtype, wl.prescale)
@@ -107,11 +111,11 @@ def draw_qkv(wl: Workload, seed: int, layer: int = 0):
     return q, k, v, gen
 
 
-def draw_decode(wl: Workload, seed: int):
+def draw_decode(wl: Workload, seed: int, device: str = "cpu"):
     """A decode step's inputs: caches k, v [B,Hkv,N,d] (N = the cache's
     capacity) and one query row per sequence and head, q [B,Hq,d], drawn in
     the order k, v, q from stream seed + 3 (sinks planted as for a layer)."""
-    gen = generator(seed + 3)
+    gen = generator(seed + 3, device)
     B, N, d = wl.batch, wl.seqlen, wl.head_dim
     k = draw(gen, (B, wl.hkv, N, d), wl.dtype, wl.prescale)
     v = draw(gen, (B, wl.hkv, N, d), wl.dtype, wl.prescale)
@@ -128,7 +132,7 @@ def plant_sinks(k: torch.Tensor, gen: torch.Generator, n_sinks: int) -> torch.Te
     (abstract); these planted high-norm keys give logits far above the rest.
     """
     B, H, N, d = k.shape
-    u = torch.randn(B, H, d, generator=gen, dtype=torch.float32)
+    u = torch.randn(B, H, d, generator=gen, dtype=torch.float32, device=gen.device)
     u = u / u.norm(dim=-1, keepdim=True)
     kf = k.float()
     kf[:, :, :n_sinks, :] += (8.0 * math.sqrt(d)) * u[:, :, None, :]
@@ -141,9 +145,9 @@ def redraw_rows(gen: torch.Generator, count: int, d: int, dtype: torch.dtype,
     return draw(gen, (count, d), dtype, prescale)
 
 
-def draw_dout(wl: Workload, seed: int, layer: int = 0) -> torch.Tensor:
+def draw_dout(wl: Workload, seed: int, layer: int = 0, device: str = "cpu") -> torch.Tensor:
     """Upstream gradient of the active output, N(0,1), [B,Hq,N,d], stream seed+1."""
-    gen = generator(seed + 1 + 1000 * layer)
+    gen = generator(seed + 1 + 1000 * layer, device)
     return draw(gen, (wl.batch, wl.hq, wl.seqlen, wl.head_dim), wl.dtype)
 
 

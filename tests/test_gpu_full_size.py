@@ -1,16 +1,19 @@
-"""GPU parity at the full sizes of the measured layers, on sampled rows.
+"""GPU parity at the full sizes of the measured layers.
 
 The whole layer runs through the C ABI exactly as the benchmark runs it
 (selection, dual forward, backward, same shapes and launch configuration).
-The fp64 oracle cannot redo a 16K or 64K layer inside a test, so it checks
+The fp64 oracle cannot redo a whole 16K or 64K layer inside a test, so it
+checks
 
+* whole (batch, KV head) units of the training layers: every row of the G
+  query heads (selection, both streams, lse, delta, dq) and every key of the
+  KV head (dk, dv), computed by the oracle on a process pool -- units are
+  independent, since dk and dv sum only over their own query heads;
 * sampled query rows one by one: the selection (rows whose fp64 cutoff
   margin is below 1e-3 are exempt from the equality check, as screening would
   have redrawn them; their GPU selection must still be a valid near-optimal
   one), both streams, their log-sum-exps and delta recomputed by the oracle
   from the GPU's selection of that row, and dq of those rows;
-* the tail keys of one KV head: dk and dv of the last keys depend only on the
-  queries at or after them, so the oracle gets them exactly from those rows;
 * properties that hold at any size over the whole layer: L_sparsity ==
   L_commit == mean (h_full - h_sparse)^2 of the outputs, 0 <= delta < 1 with
   delta = 1 - exp(lse_sparse - lse_full), and the backward sum rules (over a
@@ -31,11 +34,10 @@ import torch
 
 import oracle
 import ssa_inputs as si
-from gpu_cases import TOL, assert_close
+from gpu_cases import MARGIN, TOL, assert_close, check_selection as _check_selection
 
 pytestmark = pytest.mark.gpu
 
-MARGIN = 1e-3
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -64,24 +66,6 @@ def _sample_rows(rng, N, block, K, n):
     return np.unique(np.concatenate([early, edges, rest]))
 
 
-def _check_selection(name, q_rows, t_idx, mu_c, block, K, gpu_rows):
-    """Equal to the oracle where the fp64 margin is >= MARGIN; elsewhere a
-    valid selection whose scores are within MARGIN of the optimum."""
-    ref, margin = oracle.select_rows(q_rows, t_idx, mu_c, block, K)
-    ok = margin >= MARGIN
-    bad = np.nonzero(ok & np.any(ref != gpu_rows, axis=1))[0]
-    assert bad.size == 0, f"{name}: selection differs on rows {t_idx[bad][:8]}"
-    for r in np.nonzero(~ok)[0]:
-        t, i = int(t_idx[r]), int(t_idx[r]) // block
-        row = gpu_rows[r]
-        kept = row[row >= 0]
-        assert kept.size == min(K, i + 1) and np.all(np.diff(kept) > 0) and kept[-1] == i, (name, t, row)
-        sigma = q_rows[r] @ mu_c[:i].T
-        cutoff = np.sort(sigma)[::-1][min(K - 1, i) - 1]
-        assert np.all(sigma[kept[:-1]] >= cutoff - MARGIN), (name, t)
-    return int((~ok).sum())
-
-
 def _check_rows_fwd(name, wl, b, h, t_idx, qf, kf, vf, sel_np, out, dual=True):
     c = h // wl.group
     scale = 1.0 / math.sqrt(wl.head_dim)
@@ -104,14 +88,48 @@ def _whole_layer_properties(name, out, dtype):
     assert float((delta.double() - expect).abs().max()) <= 1e-5, name
 
 
+def _unit_check(name, wl, K, mode, b, c, q, k, v, dout, sel_np, out, grads):
+    """One whole (batch, KV head) unit against the oracle: the selection of
+    every row of its G query heads (margin-aware), both streams, lse and delta
+    of every row, dq of every row, and dk / dv of every key of the KV head
+    (the oracle on a process pool, from the GPU's selection of each row)."""
+    from oracle import parallel
+
+    G, N = wl.group, wl.seqlen
+    hs = slice(c * G, (c + 1) * G)
+    qf, gf = si.to_f64(q[b, hs]), si.to_f64(dout[b, hs])
+    kf, vf = si.to_f64(k[b, c]), si.to_f64(v[b, c])
+    mu_c = oracle.block_means(kf[None, None], wl.block)[0, 0]
+    t_all = np.arange(N)
+    exempt = 0
+    for i in range(G):
+        exempt += _check_selection(f"{name} unit b{b} c{c} head {i}", qf[i], t_all, mu_c, wl.block, K,
+                                   sel_np[b, c * G + i])
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    res = parallel.unit_step(qf, kf, vf, wl.block, K, scale, mode, dout_u=gf, sel_u=sel_np[b, hs],
+                             M=q.numel())
+    _say(f"  unit b{b} c{c}: {G} heads x {N} rows, oracle {res['seconds']:.1f} s on {res['workers']} "
+         f"processes, selection rows exempt by margin: {exempt}")
+    for key in ("h_full", "h_sparse", "lse_full", "lse_sparse", "delta"):
+        assert_close(f"{name} unit {key}", out[key][b, hs], res[key], wl.dtype)
+    dq, dk, dv = grads
+    assert_close(f"{name} unit dq", dq[b, hs], res["dq"], wl.dtype)
+    assert_close(f"{name} unit dk", dk[b, c], res["dk"], wl.dtype)
+    assert_close(f"{name} unit dv", dv[b, c], res["dv"], wl.dtype)
+
+
 # ------------------------------------------------------------- 16K training --
 
-def test_train_layer_16k_full_size():
-    """B=2, 32 query / 8 KV heads, N=16384, d=128, block 64, top_k 16: the
-    benchmark's layer, one training step (sparse stream active)."""
+@pytest.mark.parametrize("K, mode, unit", [(16, oracle.DUAL_ACTIVE_SPARSE, (1, 5)),
+                                           (4, oracle.DUAL_ACTIVE_FULL, (0, 2)),
+                                           (32, oracle.DUAL_ACTIVE_SPARSE, (1, 7))])
+def test_train_layer_16k_full_size(K, mode, unit):
+    """B=2, 32 query / 8 KV heads, N=16384, d=128, block 64, top_k 4 / 16 /
+    32 (the sweep's ends and the default): the benchmark's layer, one training
+    step.  One whole (batch, KV head) unit element by element, sampled rows of
+    other heads, and the whole layer's properties and sum rules."""
     wl = si.WORKLOADS["train_b2_h32_n16k"]
-    K, mode = wl.top_k, oracle.DUAL_ACTIVE_SPARSE
-    _say(f"full-size {wl.name}: draw")
+    _say(f"full-size {wl.name} top_k {K} mode {mode}: draw")
     q, k, v, _ = si.draw_qkv(wl, 0)
     dout = si.draw_dout(wl, 0)
     qd, kd, vd, gd = (x.to("cuda:0") for x in (q, k, v, dout))
@@ -127,6 +145,7 @@ def test_train_layer_16k_full_size():
 
     _say("  whole-layer properties")
     _whole_layer_properties(wl.name, out, wl.dtype)
+    _unit_check(f"{wl.name} K{K}", wl, K, mode, unit[0], unit[1], q, k, v, dout, sel_np, out, (dq, dk, dv))
 
     qf, kf, vf, gf = (si.to_f64(x) for x in (q, k, v, dout))
     mu = oracle.block_means(kf, wl.block)
@@ -141,14 +160,7 @@ def test_train_layer_16k_full_size():
         _check_rows_fwd(wl.name, wl, b, h, t_idx, qf, kf, vf, sel_np, out)
         ref_dq = oracle.dq_rows(qf, kf, vf, sel_np, wl.block, scale, wl.group, mode, gf, b, h, t_idx)
         assert_close(f"{wl.name} dq b{b} h{h}", dq[b, h, torch.from_numpy(t_idx)], ref_dq, wl.dtype)
-    _say(f"  selection rows exempt by margin: {exempt}")
-
-    _say("  tail keys of one KV head")
-    i0 = wl.seqlen - 96
-    b, c = 1, 5
-    rk, rv = oracle.dkdv_tail(qf, kf, vf, sel_np, wl.block, scale, wl.group, mode, gf, b, c, i0)
-    assert_close(f"{wl.name} dk tail", dk[b, c, i0:], rk, wl.dtype)
-    assert_close(f"{wl.name} dv tail", dv[b, c, i0:], rv, wl.dtype)
+    _say(f"  sampled selection rows exempt by margin: {exempt}")
 
     _say("  backward sum rules")
     g_f, g_s = oracle.stream_grads(mode, gf, out["h_full"].double().numpy(), out["h_sparse"].double().numpy(),
@@ -160,6 +172,52 @@ def test_train_layer_16k_full_size():
     sum_dk, abs_dk = dks.sum(axis=2), np.abs(dks).sum(axis=2)
     assert np.all(np.abs(sum_dv - G) <= 2 ** -7 * abs_dv + 1e-6), np.abs(sum_dv - G).max()
     assert np.all(np.abs(sum_dk) <= 2 ** -7 * abs_dk + 1e-6), np.abs(sum_dk).max()
+
+
+# ---------------------------------------------- 4K GQA layer, every unit --
+
+@pytest.mark.parametrize("mode", [oracle.DUAL_ACTIVE_FULL, oracle.DUAL_ACTIVE_SPARSE, oracle.FULL_ONLY,
+                                  oracle.SPARSE_ONLY])
+def test_gqa_n4k_layer_backward_every_unit(mode):
+    """B=1, 16 query / 4 KV heads, N=4096, d=128, block 64, top_k 16, unscreened:
+    a training step, and every (batch, KV head) unit of the layer element by
+    element (all rows' outputs and dq, every key's dk and dv)."""
+    wl = si.WORKLOADS["gqa_n4k_fwd"]
+    K = wl.top_k
+    _say(f"{wl.name} whole-layer backward mode {mode}")
+    q, k, v, _ = si.draw_qkv(wl, 0)
+    dout = si.draw_dout(wl, 0)
+    qd, kd, vd, gd = (x.to("cuda:0") for x in (q, k, v, dout))
+    sel = ssa().ssa_select_blocks(qd, kd, wl.block, K)
+    fwd = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, K, mode)
+    grads = ssa().ssa_attn_bwd(qd, kd, vd, sel, fwd, gd, wl.block, K, mode, 0.7, 1.3)
+    torch.cuda.synchronize()
+    out = {key: val.cpu() for key, val in fwd.items() if not key.startswith("_")}
+    grads = tuple(x.cpu() for x in grads)
+    sel_np = sel.cpu().numpy()
+    dual = mode in (oracle.DUAL_ACTIVE_FULL, oracle.DUAL_ACTIVE_SPARSE)
+    if dual:
+        _whole_layer_properties(wl.name, out, wl.dtype)
+    from oracle import parallel
+
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    G = wl.group
+    for c in range(wl.hkv):
+        hs = slice(c * G, (c + 1) * G)
+        qf, gf = si.to_f64(q[0, hs]), si.to_f64(dout[0, hs])
+        kf, vf = si.to_f64(k[0, c]), si.to_f64(v[0, c])
+        mu_c = oracle.block_means(kf[None, None], wl.block)[0, 0]
+        for i in range(G):
+            _check_selection(f"4k c{c} head {i}", qf[i], np.arange(wl.seqlen), mu_c, wl.block, K,
+                             sel_np[0, c * G + i])
+        res = parallel.unit_step(qf, kf, vf, wl.block, K, scale, mode, dout_u=gf, sel_u=sel_np[0, hs],
+                                 w_sparsity=0.7, w_commit=1.3, M=q.numel())
+        for key in ("h_full", "h_sparse", "lse_full", "lse_sparse", "delta"):
+            if key in res:
+                assert_close(f"4k c{c} {key}", out[key][0, hs], res[key], wl.dtype)
+        assert_close(f"4k c{c} dq", grads[0][0, hs], res["dq"], wl.dtype)
+        assert_close(f"4k c{c} dk", grads[1][0, c], res["dk"], wl.dtype)
+        assert_close(f"4k c{c} dv", grads[2][0, c], res["dv"], wl.dtype)
 
 
 # ----------------------------------------------------- selection, many blocks --
@@ -317,6 +375,10 @@ def test_multilayer_slice_full_size():
         _say(f"  layer {layer + 1} rows b{b} h{h}: {t_idx.size}")
         _check_rows_fwd(f"{wl.name} layer {layer + 1}", wl, b, h, t_idx, qf, kf, vf, sel_np, out)
         ref_dq = oracle.dq_rows(qf, kf, vf, sel_np, wl.block, scale, wl.group, mode, gf, b, h, t_idx)
-        dq = grads[layer][0].cpu()
-        assert_close(f"{wl.name} layer {layer + 1} dq", dq[b, h, torch.from_numpy(t_idx)], ref_dq, wl.dtype)
+        g_cpu = tuple(x.cpu() for x in grads[layer])
+        assert_close(f"{wl.name} layer {layer + 1} dq", g_cpu[0][b, h, torch.from_numpy(t_idx)], ref_dq, wl.dtype)
         del qf, kf, vf, gf
+        # one whole unit of every layer: dk / dv of all its keys, dq of all its rows
+        ub, uc = (layer + 1) % wl.batch, (3 * layer + 1) % wl.hkv
+        _unit_check(f"{wl.name} layer {layer + 1}", wl, K, mode, ub, uc, q, k, v, si.draw_dout(wl, 0, layer),
+                    sel_np, out, g_cpu)
