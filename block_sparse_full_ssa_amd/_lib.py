@@ -36,6 +36,7 @@ EXPORTED = (
     "ssa_status_string", "ssa_last_error", "ssa_timing_enable", "ssa_timing_query",
     "ssa_kernel_count", "ssa_kernel_name", "ssa_probe_mfma", "ssa_probe_copy",
     "ssa_cache_block_means", "ssa_decode", "ssa_prefill_workspace_size", "ssa_prefill",
+    "ssa_noalloc_scratch_bytes", "ssa_attn_fwd_noalloc",
 )
 
 
@@ -105,6 +106,10 @@ def lib() -> ctypes.CDLL:
     L.ssa_prefill_workspace_size.restype = sz
     L.ssa_prefill.argtypes = [shp, i32, vp, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.ssa_prefill.restype = i32
+    L.ssa_noalloc_scratch_bytes.argtypes = []
+    L.ssa_noalloc_scratch_bytes.restype = sz
+    L.ssa_attn_fwd_noalloc.argtypes = [shp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    L.ssa_attn_fwd_noalloc.restype = i32
     L.ssa_probe_mfma.argtypes = [vp, i32, i32, vp]
     L.ssa_probe_mfma.restype = i32
     L.ssa_probe_copy.argtypes = [vp, vp, sz, vp]

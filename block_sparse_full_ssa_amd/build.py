@@ -19,7 +19,7 @@ LIB = os.path.join(HERE, "libssa.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 
 SOURCES = ["api.hip", "select.hip", "simt.hip", "misc.hip", "fwd_mfma.hip", "bwd_mfma.hip", "bucket.hip",
-           "sparse_fwd.hip", "sparse_bwd.hip", "bwd_dq.hip", "probe.hip", "decode.hip"]
+           "sparse_fwd.hip", "sparse_bwd.hip", "bwd_dq.hip", "probe.hip", "decode.hip", "static_ws.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

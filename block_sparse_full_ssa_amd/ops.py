@@ -144,6 +144,34 @@ def ssa_attn_fwd(q, k, v, sel, block: int, top_k: int, mode: int = DUAL_ACTIVE_F
     return out
 
 
+def ssa_attn_fwd_noalloc(q, k, v, sel, block: int, top_k: int, mode: int = DUAL_ACTIVE_FULL,
+                         scale: Optional[float] = None) -> Dict[str, torch.Tensor]:
+    """ssa_attn_fwd with the library's static per-device workspace instead of
+    a caller buffer (the C entry point allocates nothing; this wrapper only
+    allocates the outputs)."""
+    dev = _dev_check(q, k, v, sel)
+    shape = make_shape(q, k, block, top_k, scale)
+    _check_layer(q, k, v, sel, top_k, mode != FULL_ONLY)
+    B, Hq, N, d = q.shape
+    f32 = dict(dtype=torch.float32, device=dev)
+    out: Dict[str, torch.Tensor] = {}
+    if mode != SPARSE_ONLY:
+        out["h_full"] = torch.empty_like(q)
+        out["lse_full"] = torch.empty(B, Hq, N, **f32)
+    if mode != FULL_ONLY:
+        out["h_sparse"] = torch.empty_like(q)
+        out["lse_sparse"] = torch.empty(B, Hq, N, **f32)
+    if mode in (DUAL_ACTIVE_FULL, DUAL_ACTIVE_SPARSE):
+        out["delta"] = torch.empty(B, Hq, N, **f32)
+        out["losses"] = torch.empty(2, **f32)
+    st = _lib.lib().ssa_attn_fwd_noalloc(
+        ctypes.byref(shape), int(mode), _ptr(q), _ptr(k), _ptr(v), _ptr(sel), _ptr(out.get("h_full")),
+        _ptr(out.get("h_sparse")), _ptr(out.get("lse_full")), _ptr(out.get("lse_sparse")), _ptr(out.get("delta")),
+        _ptr(out.get("losses")), _stream(dev))
+    _lib.check(st, "ssa_attn_fwd_noalloc")
+    return out
+
+
 def ssa_attn_bwd(q, k, v, sel, fwd: Dict[str, torch.Tensor], d_out: Optional[torch.Tensor],
                  block: int, top_k: int, mode: int = DUAL_ACTIVE_FULL, w_sparsity: float = 1.0,
                  w_commit: float = 1.0, scale: Optional[float] = None):

@@ -190,6 +190,28 @@ ssa_status_t ssa_attn_bwd(const ssa_shape_t* shape, int32_t mode, float w_sparsi
                           void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
                           void* stream);
 
+/*
+ * ssa_attn_fwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, hosts that forbid allocation).  Arguments, outputs and errors are
+ * those of ssa_attn_fwd; the same kernels run.  Their workspace comes from a
+ * static device array of ssa_noalloc_scratch_bytes() bytes (16 MiB), one per
+ * device, held until the process ends: a layer whose
+ * ssa_workspace_size(shape, mode, SSA_OP_FWD) exceeds it returns
+ * SSA_ERR_WORKSPACE and enqueues nothing.  (Dual modes need 4 bytes per query
+ * row, so up to about four million rows B*Hq*N; SSA_FULL_ONLY needs none;
+ * SSA_SPARSE_ONLY fits only small layers.)  Nothing is allocated and no HIP
+ * event is created, also with timing enabled; the first call on a device
+ * looks up the array's device address.  Every call on one device shares the
+ * array: calls that may overlap in time on one device (different streams or
+ * threads) race and must be ordered by the caller.
+ */
+size_t ssa_noalloc_scratch_bytes(void);
+ssa_status_t ssa_attn_fwd_noalloc(const ssa_shape_t* shape, int32_t mode, const void* q,
+                                  const void* k, const void* v, const int32_t* sel, void* h_full,
+                                  void* h_sparse, float* lse_full, float* lse_sparse, float* delta,
+                                  float* losses, void* stream);
+
 /* Static text for a status code. */
 const char* ssa_status_string(int32_t status);
 
