@@ -136,11 +136,10 @@ __global__ void __launch_bounds__(256, 2)
   // different workgroups and drift apart: one's waits (LDS, the softmax, the
   // barrier) overlap the other's MFMAs.  A workgroup owns 128 keys (32 per
   // wave); K of the 128 keys sits in LDS as an MFMA operand, V in registers.
-  // LDS: K (32 KiB) and two sets of {Q, G_f tiles [32][128], row values}.
+  // LDS: K (32 KiB) and two sets of {Q, G_f tiles [32][128]}.
   constexpr int kT = kBM * kD;                       // one Q / G tile
   __shared__ __attribute__((aligned(16))) uint16_t Kt[kBN * kD];
   __shared__ __attribute__((aligned(16))) uint16_t Q0[kT], F0[kT], Q1[kT], F1[kT];
-  __shared__ __attribute__((aligned(16))) float R0[2 * kBM], R1[2 * kBM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -220,15 +219,30 @@ __global__ void __launch_bounds__(256, 2)
       __builtin_amdgcn_global_load_lds((const glb_void*)(src + dmo[r]), (lds_void*)(dst + (n & 7) * 512), 16, 0, 0);
     }
   };
-  // row values (lse2, D) through registers
-  float prow = 0.f;
+  // Row values of the 32 queries: lane l holds lse2 and D of query l % 32.
+  // They enter the logits and dP through the accumulators: one extra matrix
+  // product each starts S at -lse2 / c and dP at -D (A: the value split into
+  // three bf16 terms in the k-slots 0..2 of the lanes of k-group 0, exact in
+  // fp32; B: ones in the same slots), so no per-element row value has to be
+  // fetched for the softmax and dS.
+  float rl = 0.f, rd = 0.f, rl_n = 0.f, rd_n = 0.f;
   auto load_rows = [&](int hq, int q0) {
-    const int64_t rowbase = (static_cast<int64_t>(b) * Hq + hq) * N + q0;
-    if (wave == 0) {                      // lanes 0-31: lse2 of the 32 rows, 32-63: D
-      if (lane < kBM) prow = a.lse2_full[rowbase + lane];
-      else prow = a.D_full[rowbase + lane - kBM];
-    }
+    const int64_t r = (static_cast<int64_t>(b) * Hq + hq) * N + q0 + col;
+    rl_n = a.lse2_full[r];
+    rd_n = a.D_full[r];
   };
+  auto split3 = [&](float x) -> bf16x8 {
+    const float t0 = to_f32(to_bf16(x));
+    const float r1 = x - t0;
+    const float t1 = to_f32(to_bf16(r1));
+    const float t2 = to_f32(to_bf16(r1 - t1));
+    uint4 u = make_uint4(pack_bf16x2(t0, t1), pack_bf16x2(t2, 0.f), 0u, 0u);
+    if (g) u = make_uint4(0u, 0u, 0u, 0u);
+    return __builtin_bit_cast(bf16x8, u);
+  };
+  const bf16x8 ones = __builtin_bit_cast(bf16x8, g ? make_uint4(0u, 0u, 0u, 0u)
+                                                   : make_uint4(0x3F803F80u, 0x00003F80u, 0u, 0u));
+  const float inv_c = 1.f / scale_log2;
 
   f32x16 dv[4], dk[4];
 #pragma unroll
@@ -237,10 +251,12 @@ __global__ void __launch_bounds__(256, 2)
     dk[dt] = f32x16{};
   }
 
-  // one iteration on set (Qs, Fs, rv) while the next streams into (Qn, Fn, Rn)
-  auto step = [&](int it, int q0, int hq1, int q01, const uint16_t* Qs, const uint16_t* Fs, const float* rv,
-                  uint16_t* Qn, uint16_t* Fn, float* Rn) {
+  // one iteration on set (Qs, Fs) while the next streams into (Qn, Fn)
+  auto step = [&](int it, int q0, int hq1, int q01, const uint16_t* Qs, const uint16_t* Fs, uint16_t* Qn,
+                  uint16_t* Fn) {
     const bool more = it + 1 < iters;
+    rl = rl_n;
+    rd = rd_n;
     if (more) {
       load_rows(hq1, q01);    // plain loads first: no VMEM load may follow the copies
       load_tiles(hq1, q01, Qn, Fn);
@@ -261,7 +277,8 @@ __global__ void __launch_bounds__(256, 2)
       // ---- S = Q K^T, dP = G_f V^T  [32 q x 32 keys], two independent
       // accumulation chains interleaved, operands read one step ahead; lane:
       // key col, queries 8(i/4)+4g+(i%4)
-      f32x16 s = f32x16{}, dpf = f32x16{};
+      f32x16 s = mfma32x32x16(split3(-rl * inv_c), ones, f32x16{});
+      f32x16 dpf = mfma32x32x16(split3(-rd), ones, f32x16{});
       bf16x8 ok[8], oq[8], of[8];
       auto rd = [&](int ds) {
         const int cs = 16 * (ds ^ c7);   // the same chunk for query row col and key row 32 kq + col
@@ -283,12 +300,7 @@ __global__ void __launch_bounds__(256, 2)
       // dS of a masked pair is zero because its P is)
       float p[16];
 #pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) {
-        const float4 lf = *reinterpret_cast<const float4*>(&rv[8 * a4 + 4 * g]);
-        const float lfa[4] = {lf.x, lf.y, lf.z, lf.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) p[4 * a4 + k] = fast_exp2(s[4 * a4 + k] * scale_log2 - lfa[k]);
-      }
+      for (int i = 0; i < 16; ++i) p[i] = fast_exp2(s[i] * scale_log2);
       if (diag) {
         // uniform, and taken on one tile per wave and head, so a real branch
         // (the empty asm keeps the compiler from turning it into selects)
@@ -300,11 +312,9 @@ __global__ void __launch_bounds__(256, 2)
       uint32_t pfp[8], dsp[8];
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
-        const float4 df = *reinterpret_cast<const float4*>(&rv[kBM + 8 * a4 + 4 * g]);
-        const float dfa[4] = {df.x, df.y, df.z, df.w};
         float e[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) e[k] = p[4 * a4 + k] * (dpf[4 * a4 + k] - dfa[k]);
+        for (int k = 0; k < 4; ++k) e[k] = p[4 * a4 + k] * dpf[4 * a4 + k];
         pfp[2 * a4] = pack_bf16x2(p[4 * a4], p[4 * a4 + 1]);
         pfp[2 * a4 + 1] = pack_bf16x2(p[4 * a4 + 2], p[4 * a4 + 3]);
         dsp[2 * a4] = pack_bf16x2(e[0], e[1]);
@@ -333,7 +343,6 @@ __global__ void __launch_bounds__(256, 2)
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (more && tid < 2 * kBM) Rn[tid] = prow;
     __builtin_amdgcn_s_waitcnt(0);     // next tiles landed
     __syncthreads();
   };
@@ -343,15 +352,14 @@ __global__ void __launch_bounds__(256, 2)
   advance(hq1, q01);
   load_rows(hq, q0);
   load_tiles(hq, q0, Q0, F0);
-  if (tid < 2 * kBM) R0[tid] = prow;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int it = 0; it < iters; it += 2) {
-    step(it, q0, hq1, q01, Q0, F0, R0, Q1, F1, R1);
+    step(it, q0, hq1, q01, Q0, F0, Q1, F1);
     q0 = q01;
     advance(hq1, q01);
     if (it + 1 >= iters) break;
-    step(it + 1, q0, hq1, q01, Q1, F1, R1, Q0, F0, R0);
+    step(it + 1, q0, hq1, q01, Q1, F1, Q0, F0);
     q0 = q01;
     advance(hq1, q01);
   }
