@@ -37,7 +37,7 @@ static std::vector<TimingRec> g_recs;
 static const char* kKernelNames[kKernelCount] = {
     "block_mean", "select", "fwd_simt", "fwd_mfma", "loss_reduce",
     "bwd_pre",    "bwd_simt", "bwd_mfma", "convert", "zero", "bucket", "sparse_part", "sparse_merge",
-    "bwd_sparse", "bwd_dq", "probe_mfma", "probe_copy", "decode"};
+    "bwd_sparse", "bwd_dq", "probe_mfma", "probe_copy", "decode", "dq_merge"};
 
 static thread_local int g_timing_paused = 0;
 TimingPause::TimingPause() { ++g_timing_paused; }
@@ -162,7 +162,7 @@ struct BwdWs {
   // MFMA path
   uint16_t *g_full, *g_sparse;
   float *D_full, *D_sparse, *lse2_full, *lse2_sparse;
-  float* dq_acc;              // sparse-only: the sparse stream's fp32 dQ
+  uint16_t* dq_part;          // sparse-only: the sparse stream's partial dQ rows (bucket order)
   Buckets bk;                 // sparse stream
   float *dk_part, *dv_part;   // training modes: the sparse stream's fp32 dK / dV
   uint16_t* ds_rows;          // training modes: the sparse stream's dS rows for the dQ kernel
@@ -187,7 +187,7 @@ static BwdWs carve_bwd(const Dims& D, int mode, Carver& c) {
       w.dv_part = c.take<float>(D.kv_elems() * sizeof(float));
       w.ds_rows = c.take<uint16_t>(static_cast<size_t>(bucket_capacity(D)) * D.block * sizeof(uint16_t));
     }
-    if (sp && !f) w.dq_acc = c.take<float>(D.q_elems() * sizeof(float));
+    if (sp && !f) w.dq_part = c.take<uint16_t>(static_cast<size_t>(bucket_capacity(D)) * D.d * sizeof(uint16_t));
   } else {
     w.dk_acc = c.take<float>(D.kv_elems() * sizeof(float));
     w.dv_acc = c.take<float>(D.kv_elems() * sizeof(float));
@@ -366,19 +366,19 @@ ssa_status_t ssa_attn_bwd(const ssa_shape_t* shape, int32_t mode, float w_sparsi
     // and the rows of dS), then the full stream's dK / dV and dQ, each adding
     // the sparse stream's part
     BwdPreArgs p{d_out, h_full, h_sparse, lse_full, lse_sparse, w.g_full, w.g_sparse, w.D_full, w.D_sparse,
-                 w.lse2_full, w.lse2_sparse, w.dq_acc, mode};
+                 w.lse2_full, w.lse2_sparse, mode};
     launch_bwd_pre(D, p, w_sparsity, w_commit, s);
     if ((st = launch_status()) != SSA_OK) return st;
     if (mode != kFullOnly) {
       launch_buckets(D, sel, w.bk, s);
       if ((st = launch_status()) != SSA_OK) return st;
-      SparseBwdArgs sp{q, k, v, w.bk.offs, w.bk.rows, w.g_sparse, w.lse2_sparse, w.D_sparse, w.dq_acc,
+      SparseBwdArgs sp{q, k, v, w.bk.offs, w.bk.rows, w.g_sparse, w.lse2_sparse, w.D_sparse, w.dq_part,
                        w.ds_rows, w.dk_part, w.dv_part, dk, dv};
       launch_bwd_sparse(D, sp, s);
       if ((st = launch_status()) != SSA_OK) return st;
     }
     if (mode == kSparseOnly) {
-      launch_convert(w.dq_acc, dq, D.dtype, D.q_elems(), s);
+      launch_sparse_dq_merge(D, sel, w.bk.mask, w.bk.wpos, w.dq_part, dq, s);
       return launch_status();
     }
     BwdMainArgs m{q, k, v, w.g_full, w.lse2_full, w.D_full, dk, dv, w.dk_part, w.dv_part};

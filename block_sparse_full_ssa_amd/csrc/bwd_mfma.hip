@@ -14,9 +14,8 @@
 //   dV  = P^T G_f,  dK = scale dS^T Q,  dQ = scale dS K.
 //
 // Kernels:
-//   bwd_pre:  per row, G_f / G_s in bf16, D_f / D_s from the rounded G, the
-//             lse values in log2 units, and (sparse stream alone) a zeroed
-//             fp32 dQ accumulator row;
+//   bwd_pre:  per row, G_f / G_s in bf16, D_f / D_s from the rounded G and
+//             the lse values in log2 units;
 //   bwd_mfma: dK / dV, key-stationary.  A workgroup owns 128 keys of one KV
 //             head (32 per wave; K in LDS, V in registers as MFMA operands)
 //             and walks the G query heads of the group and every 32-query
@@ -102,10 +101,6 @@ __global__ void __launch_bounds__(256)
   if (!ok) return;
   if (has_f) *reinterpret_cast<uint4*>(a.g_full + off) = make_uint4(gfw[0], gfw[1], gfw[2], gfw[3]);
   if (has_s) *reinterpret_cast<uint4*>(a.g_sparse + off) = make_uint4(gsw[0], gsw[1], gsw[2], gsw[3]);
-  if (a.dq_acc) {
-    *reinterpret_cast<float4*>(a.dq_acc + off) = make_float4(0.f, 0.f, 0.f, 0.f);
-    *reinterpret_cast<float4*>(a.dq_acc + off + 4) = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
   if (li == 0) {
     if (has_f) {
       a.D_full[row] = Df;

@@ -44,6 +44,7 @@ enum KernelId {
   kKProbeMfma,
   kKProbeCopy,
   kKDecode,
+  kKDqMerge,
   kKernelCount
 };
 
@@ -107,7 +108,6 @@ struct BwdPreArgs {
   uint16_t *g_full, *g_sparse;      // bf16 stream gradients [rows][d]
   float *D_full, *D_sparse;         // rowsum(G o h)
   float *lse2_full, *lse2_sparse;   // lse * log2(e)
-  float* dq_acc;                    // zeroed here when not null
   int mode;
 };
 // Full-stream backward: G_f, D_f, lse2_f of every row.
@@ -167,13 +167,16 @@ struct SparseBwdArgs {
   const int32_t *offs, *rows;           // buckets
   const uint16_t* g_sparse;             // bf16 G_s [rows][d]
   const float *lse2_sparse, *D_sparse;
-  float* dq_acc;                        // fp32 [rows][d], added to atomically (when ds_rows is null)
+  uint16_t* dq_part;                    // sparse-only: bf16 [bucket entries][d] partial dQ rows
   uint16_t* ds_rows;                    // bf16 [bucket entries][block] dS rows for the dQ kernel, or null
   float *dk_part, *dv_part;             // fp32 [B*Hkv][N][d] results, or null: write dk, dv (bf16)
   void *dk, *dv;
 };
 bool sparse_bwd_supported(const Dims& D);
 void launch_bwd_sparse(const Dims& D, const SparseBwdArgs& a, hipStream_t s);
+// sparse-only dQ: each row's partials summed over its selected blocks -> dq (bf16)
+void launch_sparse_dq_merge(const Dims& D, const int32_t* sel, const uint32_t* mask, const int32_t* wpos,
+                            const uint16_t* part, void* dq, hipStream_t s);
 
 // --- small kernels (misc.hip) ---
 void launch_zero_f32(float* p, int64_t n, hipStream_t s);

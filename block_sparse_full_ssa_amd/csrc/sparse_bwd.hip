@@ -17,8 +17,11 @@
 //   training modes: each entry's row of dS over the block's keys (bf16, in
 //     the dQ kernel's lane order), which the query-stationary dQ kernel adds
 //     to the full stream's dS, so that no atomics are needed;
-//   sparse-only: dQ_r += scale dS K_j with one fp32 atomic per (row, block,
-//     column) into an accumulator.
+//   sparse-only: each entry's partial dQ over the block's keys,
+//     scale dS K_j (bf16, one row of d per bucket entry), which a merge
+//     kernel adds up per query row over its selected blocks in selection
+//     order: deterministic, and no atomics (fp32 atomics on this chip run at
+//     a small fraction of the store bandwidth).
 //
 // Waves: wave w owns key half kh = w % KH (32 keys, B operands in registers)
 // of query stream qs = w / KH; the 4 / KH streams take consecutive batches.
@@ -64,7 +67,7 @@ __global__ void __launch_bounds__(256, 1)
   __shared__ __attribute__((aligned(16))) uint16_t Kst[kBlk * kD];
   __shared__ __attribute__((aligned(16))) uint16_t Q0[QS * kT], Q1[QS * kT], F0[QS * kT], F1[QS * kT];
   __shared__ __attribute__((aligned(16))) uint16_t D0[QS * kDS], D1[QS * kDS];
-  // row values per stream: lse2 [32], D [32], t [32] (int, -1: no row), row id [32] (int)
+  // row values per stream: lse2 [32], D [32], t [32] (int, -1: no row), 32 unused
   __shared__ __attribute__((aligned(16))) float R0[QS * 128], R1[QS * 128];
 
   const int tid = threadIdx.x;
@@ -203,7 +206,6 @@ __global__ void __launch_bounds__(256, 1)
       r[col] = rv_lse;
       r[32 + col] = rv_d;
       r[64 + col] = __int_as_float(rv_t);
-      r[96 + col] = __int_as_float(rv_r);
     }
   };
 
@@ -220,9 +222,8 @@ __global__ void __launch_bounds__(256, 1)
     const uint16_t* Fs = F + qs * kT;
     uint16_t* dSs = dS + qs * kDS;
     const float* rs = rv + qs * 128;
-    // row ids and validity of the lane's 16 query rows for the dQ atomics,
-    // taken before the barrier (the row values are refilled after it)
-    int rq[16];
+    // validity of the lane's 16 query rows for the dQ partials, taken before
+    // the barrier (the row values are refilled after it)
     uint32_t rowok = 0u;
     if (has) {
       // ---- S = Q K^T, dP = G_s V^T [32 q x 32 keys]; lane: key col, queries 8(i/4)+4g+(i%4)
@@ -242,13 +243,10 @@ __global__ void __launch_bounds__(256, 1)
         const float4 d4 = *reinterpret_cast<const float4*>(&rs[32 + qb]);
         const float4 t4 = *reinterpret_cast<const float4*>(&rs[64 + qb]);
         const float la[4] = {l4.x, l4.y, l4.z, l4.w}, da[4] = {d4.x, d4.y, d4.z, d4.w};
-        const float4 r4 = *reinterpret_cast<const float4*>(&rs[96 + qb]);
         const int ta[4] = {__float_as_int(t4.x), __float_as_int(t4.y), __float_as_int(t4.z), __float_as_int(t4.w)};
-        const int ra[4] = {__float_as_int(r4.x), __float_as_int(r4.y), __float_as_int(r4.z), __float_as_int(r4.w)};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * a4 + e;
-          rq[i] = ra[e];
           rowok |= ta[e] >= 0 ? (1u << i) : 0u;
           const bool live = key <= ta[e];                  // t = -1: no row
           p[i] = live ? fast_exp2(s[i] * scale_log2 - la[e]) : 0.f;
@@ -322,12 +320,15 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
         for (int dt = 0; dt < kDt; ++dt) dq[dt] = mfma32x32x16(ds_op, kq[ks][dt], dq[dt]);
       }
+      // the batch's entries are p0 + 32 bt + r (r: the query of register i)
+      const int64_t e0 = static_cast<int64_t>(p0) + (it * QS + qs) * 32;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (!((rowok >> i) & 1u)) continue;
-        float* dqp = a.dq_acc + static_cast<int64_t>(rq[i]) * kD + kSlice * kh + col;
+        const int r = 8 * (i >> 2) + 4 * g + (i & 3);
+        uint16_t* dst = a.dq_part + (e0 + r) * kD + kSlice * kh + col;
 #pragma unroll
-        for (int dt = 0; dt < kDt; ++dt) unsafeAtomicAdd(dqp + 32 * dt, scale * dq[dt][i]);
+        for (int dt = 0; dt < kDt; ++dt) dst[32 * dt] = to_bf16(scale * dq[dt][i]).bits;
       }
     }
   };
@@ -379,7 +380,75 @@ __global__ void __launch_bounds__(256, 1)
   if (qs == 0) write_kv(dk, dv);
 }
 
+// Sparse-only dQ: the sum of a query row's partials over its selected
+// blocks, in selection order.  16 lanes per row (8 columns of d each), 16
+// rows per workgroup; the partial of (row, block j) is the row's entry in
+// bucket (b, c, j), found through the bucket mask word and its position.
+// Entries naming no causal block, and repeats, are skipped (no partial).
+__global__ void __launch_bounds__(256) k_sparse_dq_merge(const int32_t* __restrict__ sel,
+                                                         const uint32_t* __restrict__ mask,
+                                                         const int32_t* __restrict__ wpos,
+                                                         const uint16_t* __restrict__ part, void* dq, int64_t rows,
+                                                         int Hq, int G, int N, int block, int nb, int K, int Kc) {
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  const int li = threadIdx.x & 15;
+  const bool live = row < rows;
+  const int64_t rr = live ? row : 0;
+  const int64_t bh = rr / N;
+  const int t = static_cast<int>(rr - bh * N);
+  const int b = static_cast<int>(bh / Hq), h = static_cast<int>(bh % Hq);
+  const int Hkv = Hq / G, nqt = N / 32;
+  const int64_t bc = static_cast<int64_t>(b) * Hkv + h / G;
+  const int hl = h % G, qt = t >> 5;
+  const uint32_t below = (1u << (t & 31)) - 1u;
+  const int own = t / block;
+  const int32_t* s = sel + rr * K;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int e0 = 0; e0 < Kc; e0 += 16) {
+    // lane li looks up slot e0 + li; the 16 lanes then take the slots in order
+    const int e = e0 + li;
+    int j = (live && e < Kc) ? s[e] : -1;
+    if (j > own || (e > 0 && j >= 0 && s[e - 1] == j)) j = -1;
+    int64_t p = 0;
+    if (j >= 0) {
+      const int64_t w = ((bc * nb + j) * G + hl) * nqt + qt;
+      p = wpos[w] + __popc(mask[w] & below);
+    }
+    const int nslot = min(16, Kc - e0);
+    for (int i = 0; i < nslot; ++i) {
+      const int ji = __shfl(j, i, 16);
+      if (ji < 0) continue;
+      const uint32_t plo = __shfl(static_cast<uint32_t>(p), i, 16);
+      const uint32_t phi = __shfl(static_cast<uint32_t>(p >> 32), i, 16);
+      const int64_t pi = (static_cast<int64_t>(phi) << 32) | plo;
+      const uint4 u = *reinterpret_cast<const uint4*>(part + pi * kD + 8 * li);
+      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k2 = 0; k2 < 4; ++k2) {
+        acc[2 * k2] += __uint_as_float(wd[k2] << 16);
+        acc[2 * k2 + 1] += __uint_as_float(wd[k2] & 0xffff0000u);
+      }
+    }
+  }
+  if (!live) return;
+  uint4 o;
+  o.x = pack_bf16x2(acc[0], acc[1]);
+  o.y = pack_bf16x2(acc[2], acc[3]);
+  o.z = pack_bf16x2(acc[4], acc[5]);
+  o.w = pack_bf16x2(acc[6], acc[7]);
+  *reinterpret_cast<uint4*>(static_cast<uint16_t*>(dq) + row * kD + 8 * li) = o;
+}
+
 }  // namespace
+
+void launch_sparse_dq_merge(const Dims& D, const int32_t* sel, const uint32_t* mask, const int32_t* wpos,
+                            const uint16_t* part, void* dq, hipStream_t s) {
+  const int Kc = D.K < D.nb ? D.K : D.nb;
+  timing_begin(kKDqMerge, s);
+  hipLaunchKernelGGL(k_sparse_dq_merge, dim3(static_cast<unsigned>((D.rows() + 15) / 16)), dim3(256), 0, s, sel, mask,
+                     wpos, part, dq, D.rows(), D.Hq, D.G, D.N, D.block, D.nb, D.K, Kc);
+  timing_end(kKDqMerge, s);
+}
 
 bool sparse_bwd_supported(const Dims& D) { return D.dtype == 1 && D.d == kD; }
 
