@@ -420,9 +420,33 @@ def measured_ceilings(ssa, dev):
     mfma_ms, n1 = t["probe_mfma"]
     copy_ms, n2 = t["probe_copy"]
     nbytes = src.numel() * 4
+    # fp32 atomics on 64 hot 16 KiB tiles (2 GiB of payload), and LDS operand
+    # reads (16-byte and transposing 8-byte) with two workgroups per CU
+    abuf = torch.zeros(64 * 4096, dtype=torch.float32, device=dev)
+    lsink = torch.empty(512 * 256, dtype=torch.float32, device=dev)
+    ssa.ssa_probe_atomic(abuf, 2048, 4)
+    ssa.ssa_probe_lds(lsink, 512, 100, 0)
+
+    def probes():
+        ssa.ssa_probe_atomic(abuf, 2048, 64)
+        ssa.ssa_probe_lds(lsink, 512, 20000, 0)
+        ssa.ssa_probe_lds(lsink, 512, 20000, 1)
+
+    t2 = kernel_times(ssa, probes)
+    at_ms, _ = t2["probe_atomic"]
+    lds_tot, _ = t2["probe_lds"]
+    t3 = kernel_times(ssa, lambda: ssa.ssa_probe_lds(lsink, 512, 20000, 1))
+    tr_ms = t3["probe_lds"][0]
+    b128_ms = lds_tot - tr_ms
+    lds_reads = 512 * 4 * 20000 * 8
     return {"mfma_bf16_tflops": round(blocks * 16 * iters * 32768 / (mfma_ms / n1 / 1e3) / 1e12, 1),
             "copy_gbs": round(2 * nbytes / (copy_ms / n2 / 1e3) / 1e9, 1),
-            "note": "dense 32x32x16 bf16 matrix loop on every SIMD; 1 GiB device copy (read + write)"}
+            "atomic_f32_gbs": round(2048 * 64 * 16384 / (at_ms / 1e3) / 1e9, 1),
+            "lds_read_b128_tbs": round(lds_reads * 1024 / (b128_ms / 1e3) / 1e12, 1),
+            "lds_read_tr_b64_tbs": round(lds_reads * 512 / (tr_ms / 1e3) / 1e12, 1),
+            "note": "dense 32x32x16 bf16 matrix loop on every SIMD; 1 GiB device copy (read + write); fp32 "
+                    "global atomics on hot tiles (payload bytes); LDS reads chip-wide, 16-byte and transposing "
+                    "8-byte per lane"}
 
 
 def _cpu_model() -> str:

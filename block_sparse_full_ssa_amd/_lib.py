@@ -36,7 +36,7 @@ EXPORTED = (
     "ssa_status_string", "ssa_last_error", "ssa_timing_enable", "ssa_timing_query",
     "ssa_kernel_count", "ssa_kernel_name", "ssa_probe_mfma", "ssa_probe_copy",
     "ssa_cache_block_means", "ssa_decode", "ssa_prefill_workspace_size", "ssa_prefill",
-    "ssa_noalloc_scratch_bytes", "ssa_attn_fwd_noalloc",
+    "ssa_noalloc_scratch_bytes", "ssa_attn_fwd_noalloc", "ssa_probe_atomic", "ssa_probe_lds",
 )
 
 
@@ -114,6 +114,10 @@ def lib() -> ctypes.CDLL:
     L.ssa_probe_mfma.restype = i32
     L.ssa_probe_copy.argtypes = [vp, vp, sz, vp]
     L.ssa_probe_copy.restype = i32
+    L.ssa_probe_atomic.argtypes = [vp, ctypes.c_int64, i32, i32, vp]
+    L.ssa_probe_atomic.restype = i32
+    L.ssa_probe_lds.argtypes = [vp, i32, i32, i32, vp]
+    L.ssa_probe_lds.restype = i32
     _lib = L
     return L
 

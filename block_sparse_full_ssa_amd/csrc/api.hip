@@ -37,7 +37,7 @@ static std::vector<TimingRec> g_recs;
 static const char* kKernelNames[kKernelCount] = {
     "block_mean", "select", "fwd_simt", "fwd_mfma", "loss_reduce",
     "bwd_pre",    "bwd_simt", "bwd_mfma", "convert", "zero", "bucket", "sparse_part", "sparse_merge",
-    "bwd_sparse", "bwd_dq", "probe_mfma", "probe_copy", "decode", "dq_merge"};
+    "bwd_sparse", "bwd_dq", "probe_mfma", "probe_copy", "decode", "dq_merge", "probe_atomic", "probe_lds"};
 
 static thread_local int g_timing_paused = 0;
 TimingPause::TimingPause() { ++g_timing_paused; }
@@ -558,6 +558,25 @@ ssa_status_t ssa_probe_copy(const void* src, void* dst, size_t bytes, void* stre
   if (bytes % 16 != 0) return fail(SSA_ERR_SHAPE, "bytes must be a multiple of 16%s");
   if (bytes == 0) return SSA_OK;
   launch_probe_copy(src, dst, static_cast<int64_t>(bytes), static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+ssa_status_t ssa_probe_atomic(float* buf, int64_t n_floats, int32_t blocks, int32_t iters, void* stream) {
+  g_last_error.clear();
+  if (!buf) return fail(SSA_ERR_NULL, "null buffer%s");
+  if (n_floats < 4096 || n_floats % 4096 != 0 || n_floats / 4096 > (1 << 20))
+    return fail(SSA_ERR_SHAPE, "n_floats must be a positive multiple of 4096 (at most 2^20 tiles)%s");
+  if (blocks < 1 || iters < 1) return fail(SSA_ERR_SHAPE, "blocks and iters must be positive%s");
+  launch_probe_atomic(buf, static_cast<int>(n_floats / 4096), blocks, iters, static_cast<hipStream_t>(stream));
+  return launch_status();
+}
+
+ssa_status_t ssa_probe_lds(float* sink, int32_t blocks, int32_t iters, int32_t mode, void* stream) {
+  g_last_error.clear();
+  if (!sink) return fail(SSA_ERR_NULL, "null sink%s");
+  if (blocks < 1 || iters < 1 || mode < 0 || mode > 1)
+    return fail(SSA_ERR_SHAPE, "blocks and iters must be positive and mode 0 or 1%s");
+  launch_probe_lds(sink, blocks, iters, mode, static_cast<hipStream_t>(stream));
   return launch_status();
 }
 

@@ -45,6 +45,8 @@ enum KernelId {
   kKProbeCopy,
   kKDecode,
   kKDqMerge,
+  kKProbeAtomic,
+  kKProbeLds,
   kKernelCount
 };
 
@@ -206,6 +208,8 @@ void launch_cache_means(const Dims& D, const void* k, float* mu, int j0, int j1,
 void launch_head_means(const float* a, const float* b, int64_t n_heads, int N, float* out, hipStream_t s);
 void launch_probe_mfma(float* sink, int blocks, int iters, hipStream_t s);
 void launch_probe_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+void launch_probe_atomic(float* buf, int ntiles, int blocks, int iters, hipStream_t s);
+void launch_probe_lds(float* sink, int blocks, int iters, int mode, hipStream_t s);
 void launch_loss_reduce(const float* row_sq, int64_t n_rows, double inv_count, double* scratch, float* losses,
                         hipStream_t s);
 

@@ -1,5 +1,5 @@
-// Machine probes for the measurement harness: a dense bf16 matrix-core loop
-// and a plain device copy.  They measure the two ceilings that the attention
+// Machine probes for the measurement harness: a dense bf16 matrix-core loop,
+// a plain device copy, fp32 global atomics and LDS operand reads.  They measure the two ceilings that the attention
 // kernels' rates are read against -- the matrix rate the chip sustains under
 // full load (its clock then sits below the one the datasheet peak assumes)
 // and the HBM bandwidth a streaming kernel reaches.  They compute nothing of
@@ -56,7 +56,69 @@ __global__ void __launch_bounds__(256) k_probe_copy(const uint4* __restrict__ sr
   }
 }
 
+// fp32 global atomics: workgroup w adds 1.0 to every float of 16 KiB tile
+// w % ntiles, `iters` times (16 coalesced atomic instructions per wave per
+// pass).  The tiles stay resident in the caches, so the time is the rate at
+// which the chip performs the atomics themselves.
+__global__ void __launch_bounds__(256) k_probe_atomic(float* buf, int ntiles, int iters) {
+  float* t = buf + static_cast<int64_t>(blockIdx.x % ntiles) * 4096;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) atomicAdd(&t[r * 256 + threadIdx.x], 1.0f);
+  }
+}
+
+// LDS reads: every wave reads its own 8 KiB of a 32 KiB tile, eight reads per
+// pass, either 16 bytes per lane (ds_read_b128, conflict-free: lane l reads
+// chunk l) or 8 bytes per lane as transposes (ds_read_b64_tr_b16, the
+// operand reads of the attention kernels); the values are folded into the
+// sink so that no read is dropped.
+__global__ void __launch_bounds__(256, 2) k_probe_lds(float* sink, int iters, int mode) {
+  __shared__ __attribute__((aligned(16))) uint16_t buf[256 * 64];
+  const int t = threadIdx.x;
+  for (int i = t; i < 256 * 64; i += 256) buf[i] = static_cast<uint16_t>(i * 7);
+  __syncthreads();
+  const int wave = t >> 6, lane = t & 63;
+  uint32_t acc = 0u;
+  if (mode == 0) {
+    const uint4* p = reinterpret_cast<const uint4*>(buf) + wave * 64 + lane;   // chunk < 256 + 64
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const uint4 v = p[(r * 256) & 1023];                                    // chunk < 2048
+        acc += v.x ^ v.y ^ v.z ^ v.w;
+        asm volatile("" : "+v"(acc));
+      }
+    }
+  } else {
+    const int grp = lane >> 4, li = lane & 15;
+    const int row = wave * 16 + grp * 4 + (li >> 2), col = 4 * (li & 3);       // row < 64, col < 16
+    const uint16_t* base = buf + row * 64 + col;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * (r & 3)));
+        acc += static_cast<uint32_t>(v[0] ^ v[1] ^ v[2] ^ v[3]);
+        asm volatile("" : "+v"(acc));
+      }
+    }
+  }
+  sink[static_cast<int64_t>(blockIdx.x) * 256 + t] = static_cast<float>(acc);
+}
+
 }  // namespace
+
+void launch_probe_atomic(float* buf, int ntiles, int blocks, int iters, hipStream_t s) {
+  timing_begin(kKProbeAtomic, s);
+  hipLaunchKernelGGL(k_probe_atomic, dim3(blocks), dim3(256), 0, s, buf, ntiles, iters);
+  timing_end(kKProbeAtomic, s);
+}
+
+void launch_probe_lds(float* sink, int blocks, int iters, int mode, hipStream_t s) {
+  timing_begin(kKProbeLds, s);
+  hipLaunchKernelGGL(k_probe_lds, dim3(blocks), dim3(256), 0, s, sink, iters, mode);
+  timing_end(kKProbeLds, s);
+}
 
 void launch_probe_mfma(float* sink, int blocks, int iters, hipStream_t s) {
   timing_begin(kKProbeMfma, s);

@@ -238,6 +238,23 @@ def ssa_probe_copy(src: torch.Tensor, dst: torch.Tensor) -> None:
     _lib.check(_lib.lib().ssa_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(src.device)), "ssa_probe_copy")
 
 
+def ssa_probe_atomic(buf: torch.Tensor, blocks: int, iters: int) -> None:
+    """Enqueue the fp32 atomic probe on ``buf`` (CUDA float32, a multiple of
+    4096 elements): blocks * iters * 16 KiB of atomic adds."""
+    if not buf.is_cuda or buf.dtype != torch.float32 or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous CUDA float32 tensor")
+    _lib.check(_lib.lib().ssa_probe_atomic(_ptr(buf), buf.numel(), int(blocks), int(iters), _stream(buf.device)),
+               "ssa_probe_atomic")
+
+
+def ssa_probe_lds(sink: torch.Tensor, blocks: int, iters: int, mode: int) -> None:
+    """Enqueue the LDS read probe (mode 0: 16-byte reads, 1: transposing 8-byte reads)."""
+    if not sink.is_cuda or sink.dtype != torch.float32 or sink.numel() < blocks * 256:
+        raise ValueError("sink must be a CUDA float32 tensor of >= blocks * 256 elements")
+    _lib.check(_lib.lib().ssa_probe_lds(_ptr(sink), int(blocks), int(iters), int(mode), _stream(sink.device)),
+               "ssa_probe_lds")
+
+
 def _cache_shape(q: torch.Tensor, k_cache: torch.Tensor, block: int, top_k: int,
                  scale: Optional[float]) -> _lib.ShapeT:
     if q.dim() != 3 or k_cache.dim() != 4:

@@ -322,6 +322,28 @@ ssa_status_t ssa_decode(const ssa_shape_t* shape, int32_t mode, const void* q, c
 ssa_status_t ssa_probe_mfma(float* sink, int32_t blocks, int32_t iters, void* stream);
 ssa_status_t ssa_probe_copy(const void* src, void* dst, size_t bytes, void* stream);
 
+/*
+ * Two more probes, timed as "probe_atomic" / "probe_lds": the rates that
+ * decide how a kernel may combine partial results (atomics) and how much
+ * operand traffic it can take from LDS.
+ *
+ * ssa_probe_atomic: `blocks` workgroups of 256 threads; workgroup w adds 1.0
+ *   with fp32 global atomics to every float of 16 KiB tile w % (n_floats /
+ *   4096) of `buf` (device, caller-owned, n_floats floats), `iters` times:
+ *   blocks * iters * 16 KiB of atomic payload.  Each float of a tile ends up
+ *   incremented by iters times the number of workgroups mapped to its tile
+ *   (exact for totals below 2^24).  SSA_ERR_NULL for a null buffer,
+ *   SSA_ERR_SHAPE unless n_floats is a positive multiple of 4096 (at most
+ *   2^20 tiles) and blocks, iters >= 1.
+ * ssa_probe_lds: `blocks` workgroups of 4 waves (two per CU); every wave
+ *   performs iters * 8 LDS reads, of 16 bytes per lane (mode 0, 1 KiB per
+ *   read) or 8 bytes per lane by transposing reads (mode 1, 512 bytes per
+ *   read).  `sink` (device, blocks * 256 floats) receives meaningless
+ *   values.  SSA_ERR_NULL / SSA_ERR_SHAPE as above (mode must be 0 or 1).
+ */
+ssa_status_t ssa_probe_atomic(float* buf, int64_t n_floats, int32_t blocks, int32_t iters, void* stream);
+ssa_status_t ssa_probe_lds(float* sink, int32_t blocks, int32_t iters, int32_t mode, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

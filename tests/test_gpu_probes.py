@@ -37,3 +37,28 @@ def test_probe_mfma_rate_plausible():
     tflops = blocks * 16 * iters * 32768 / (ms / 1e3) / 1e12
     assert 250.0 < tflops < 2600.0, tflops
     assert torch.isfinite(sink).all()
+
+
+def test_probe_atomic_counts_exact():
+    """Every float of every tile is incremented exactly (workgroups per tile) x iters times."""
+    import block_sparse_full_ssa_amd as ssa
+    ntiles, blocks, iters = 64, 512, 16
+    buf = torch.zeros(ntiles * 4096, dtype=torch.float32, device="cuda")
+    ssa.timing_enable(True)
+    ssa.ssa_probe_atomic(buf, blocks, iters)
+    ms, n = ssa.timing_query("probe_atomic")
+    ssa.timing_enable(False)
+    assert n == 1 and ms > 0
+    assert bool((buf == float(blocks // ntiles * iters)).all())
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+def test_probe_lds_runs(mode):
+    import block_sparse_full_ssa_amd as ssa
+    blocks = 512
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    ssa.timing_enable(True)
+    ssa.ssa_probe_lds(sink, blocks, 200, mode)
+    ms, n = ssa.timing_query("probe_lds")
+    ssa.timing_enable(False)
+    assert n == 1 and ms > 0 and torch.isfinite(sink).all()
