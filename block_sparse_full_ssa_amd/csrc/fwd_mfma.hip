@@ -19,10 +19,11 @@
 // processed in halves of 32 so that the logits need 16 registers and both
 // output accumulators stay in VGPRs.
 //
-// K/V tiles of 64 keys move from HBM straight into LDS (global_load_lds,
-// 16 bytes per lane), double-buffered, one barrier per tile.  16-byte chunks
-// are XOR-swizzled within each 256-byte row so that the matrix-operand reads
-// of K rows and the transpose reads of V columns avoid bank conflicts.
+// K/V tiles of 64 keys (32 for the full stream alone) move from HBM straight
+// into LDS (global_load_lds, 16 bytes per lane), double-buffered, one barrier
+// per tile.  16-byte chunks are XOR-swizzled within each 256-byte row so that
+// the matrix-operand reads of K rows and the transpose reads of V columns
+// avoid bank conflicts.
 //
 // Softmax: the running maxima are integers (ceil of a tile maximum) and move
 // lazily, only when a tile exceeds them by more than kTau, so every rescale
@@ -43,15 +44,22 @@ namespace {
 
 constexpr int kD = 128;          // head dimension
 constexpr int kBM = 128;         // queries per workgroup
-constexpr int kBN = 64;          // keys per tile
-constexpr int kTile = kBN * kD;  // elements of one K or V tile
+// Keys per K/V tile: 64 for both streams, 32 for the full stream alone, whose
+// smaller tiles (32 KiB of LDS) and registers (at most 168) let three
+// workgroups share a CU instead of two.
+enum { kModeDual = 0, kModeFull = 1 };   // both streams / the full stream alone
+
+template <int MODE> struct FwdTile {
+  static constexpr int kBN = MODE == kModeFull ? 32 : 64;
+  static constexpr int kTile = kBN * kD;   // elements of one K or V tile
+  static constexpr int kPerCu = MODE == kModeFull ? 3 : 2;
+};
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kTau = 8.f;      // lazy-rescale threshold (log2 units)
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-enum { kModeDual = 0, kModeFull = 1 };   // both streams / the full stream alone
 
 // Physical 16-byte chunk of logical chunk c in row r: K tiles are only read
 // by rows; V tiles by transpose reads.
@@ -69,15 +77,17 @@ __device__ __forceinline__ float max16(const f32x16& v) {
   return m;
 }
 
-// Two workgroups per CU (256 VGPRs and 68 KiB of LDS each at nb <= 256), so
-// one wave's softmax overlaps the other wave's matrix work on every SIMD.
+// Two or three workgroups per CU (see FwdTile), so one wave's softmax
+// overlaps another wave's matrix work on every SIMD.
 template <int MODE, bool STATS>
-__global__ void __launch_bounds__(256, 2)
+__global__ void __launch_bounds__(256, FwdTile<MODE>::kPerCu)
     k_fwd_mfma(FwdArgs a, int Hq, int G, int N, int Nq, int q_off, int block, int nb, int K, float scale_log2,
                int n_qtiles) {
   constexpr bool kSparse = MODE == kModeDual;
   // K and V tiles [64][128] (swizzled), two of each; separate objects so that
   // the compiler can tell the tile being read from the one being filled
+  constexpr int kBN = FwdTile<MODE>::kBN;
+  constexpr int kTile = FwdTile<MODE>::kTile;
   __shared__ __attribute__((aligned(16))) uint16_t K0[kTile], K1[kTile], V0[kTile], V1[kTile];
   // dynamic LDS: the selection bits [kBM][W] of the rows
   extern __shared__ __attribute__((aligned(16))) uint32_t bits[];
@@ -145,14 +155,14 @@ __global__ void __launch_bounds__(256, 2)
   const int j_last = min(qend - 1, q0 + kBM - 1) / kBN;
   if (kSparse) __syncthreads();
 
-  // HBM -> LDS copy of one K/V tile: each wave moves rows 16*wave .. +15, one
-  // 1 KiB instruction per 4 rows; lane l fills physical chunk l % 16 of row
+  // HBM -> LDS copy of one K/V tile: each wave moves a quarter of its rows,
+  // one 1 KiB instruction per 4 rows; lane l fills physical chunk l % 16 of row
   // 4n + l / 16, so it fetches the logical chunk stored there.  Keys past the
   // end read the last key: finite values that the causal mask removes.
   auto load_tile = [&](int j, uint16_t* Kd, uint16_t* Vd) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = wave * 4 + r;
+    for (int r = 0; r < kBN / 16; ++r) {
+      const int n = wave * (kBN / 16) + r;
       const int row = 4 * n + (lane >> 4);
       const int p = lane & 15;
       const int64_t key = min(j * kBN + row, N - 1);
@@ -168,7 +178,7 @@ __global__ void __launch_bounds__(256, 2)
     if (j + 1 <= j_last) load_tile(j + 1, Kn, Vn);
   if (wave_live && j * kBN <= wave_last_q) {
 #pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
+    for (int kh = 0; kh < kBN / 32; ++kh) {
       const int kbase = j * kBN + kh * 32;          // first key of this half
       if (kbase > wave_last_q) break;               // uniform: later keys are all masked
 
@@ -199,7 +209,7 @@ __global__ void __launch_bounds__(256, 2)
         }
       }
       float mx = max16(s);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * scale_log2;
+      mx = pair32_max(mx) * scale_log2;
 
       // ---- new maxima (integers, moved lazily)
       float mfn = mf, alpha = 1.f;
@@ -321,13 +331,13 @@ __global__ void __launch_bounds__(256, 2)
 
   // ---- epilogue
   if (!wave_live) return;
-  lf += __shfl_xor(lf, 32, 64);
+  lf = pair32_sum(lf);
   if (STATS) {
-    sink_l += __shfl_xor(sink_l, 32, 64);
-    ex_l += __shfl_xor(ex_l, 32, 64);
-    lfe += __shfl_xor(lfe, 32, 64);
+    sink_l = pair32_sum(sink_l);
+    ex_l = pair32_sum(ex_l);
+    lfe = pair32_sum(lfe);
   }
-  ls += __shfl_xor(ls, 32, 64);
+  ls = pair32_sum(ls);
   const float inv_f = 1.f / lf, inv_s = 1.f / ls;
   const bool row_ok = qrow < qend;
   const int64_t row = static_cast<int64_t>(bh) * Nq + (qrow - q_off);
@@ -356,7 +366,7 @@ __global__ void __launch_bounds__(256, 2)
       }
     }
   }
-  if (MODE == kModeDual) sq += __shfl_xor(sq, 32, 64);
+  if (MODE == kModeDual) sq = pair32_sum(sq);
   if (row_ok && g == 0) {
     const float lse_f = (mf + fast_log2(lf)) * kLn2;
     const float lse_s = (ms + fast_log2(ls)) * kLn2;
@@ -388,7 +398,7 @@ hipError_t launch_mode(const Dims& D, const FwdArgs& a, size_t lds, int n_qtiles
   return hipSuccess;
 }
 
-constexpr size_t kStaticLds = 4 * kTile * sizeof(uint16_t);
+constexpr size_t kStaticLds = 4 * FwdTile<kModeDual>::kTile * sizeof(uint16_t);   // the larger tiles
 
 size_t lds_bytes(const Dims& D) {   // dynamic part: selection bits
   const int W = (D.nb + 31) / 32;

@@ -75,12 +75,27 @@ __device__ __forceinline__ bf16x8 to_bf16x8_sum(float x0, float x1, float x2, fl
   u.y = pack_bf16x2(x2, x3);
   u.z = pack_bf16x2(x4, x5);
   u.w = pack_bf16x2(x6, x7);
+  // each pair enters the sum through one dot product with (1, 1): the
+  // products are the rounded weights themselves, accumulated in fp32
+  const bf16x2v one2 = __builtin_bit_cast(bf16x2v, 0x3F803F80u);
   const uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
-  for (int k = 0; k < 4; ++k) sum += __uint_as_float(w[k] << 16) + __uint_as_float(w[k] & 0xffff0000u);
+  for (int k = 0; k < 4; ++k) sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, w[k]), one2, sum, false);
   return __builtin_bit_cast(bf16x8, u);
 }
 
+// Lane l and lane l ^ 32 combined without LDS: v_permlane32_swap exchanges
+// the upper half of one copy with the lower half of the other, so the two
+// results hold (own, partner) in some order on every lane and their max or
+// sum is the pair's, the same in both lanes (both operations commute).
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
