@@ -454,7 +454,7 @@ static ssa_status_t prefill_dims(const ssa_shape_t* shape, int32_t mode, int32_t
   if (st != SSA_OK) return st;
   if (mode != kFullOnly && mode != kSparseOnly)
     return fail(SSA_ERR_UNSUPPORTED, "prefill runs one stream: SSA_FULL_ONLY or SSA_SPARSE_ONLY%s");
-  if (D->dtype != 1 || D->d != 128) return fail(SSA_ERR_UNSUPPORTED, "prefill needs bf16 and head_dim 128%s");
+  if (D->dtype != 1) return fail(SSA_ERR_UNSUPPORTED, "prefill needs bf16%s");
   if (chunk < 1 || pos0 < 0 || pos0 % D->block != 0 || chunk % D->block != 0 || pos0 + chunk > D->N)
     return fail(SSA_ERR_SHAPE, "need pos0 and chunk multiples of block with pos0 + chunk <= seqlen%s");
   D->Nq = chunk;

@@ -26,25 +26,28 @@
 namespace ssa {
 namespace {
 
-constexpr int kD = 128;
 constexpr int kBM = 128;         // queries per workgroup
 constexpr int kBN = 64;          // keys per tile
-constexpr int kTile = kBN * kD;
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-// Physical 16-byte chunk of logical chunk c in a 256-byte K / V row r (K is
-// read by rows and by transposes).
-// The transposed tiles use c ^ (2 (r % 8) + (r / 8) % 2): measured on gfx950
-// it keeps the transpose reads (ds_read_b64_tr_b16) free of bank conflicts
-// as well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave
-// the transpose reads two-way conflicted.
-__device__ __forceinline__ int swz_k(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
+// Physical 16-byte chunk of logical chunk c in a K / V row r of 2 HD bytes (K
+// is read by rows and by transposes).
+// 256-byte rows (HD = 128): c ^ (2 (r % 8) + (r / 8) % 2), measured on gfx950
+// to keep the transpose reads (ds_read_b64_tr_b16) free of bank conflicts as
+// well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave the
+// transpose reads two-way conflicted.  128-byte rows (HD = 64): c ^ (r % 8).
+template <int HD> __device__ __forceinline__ int swz_k(int r, int c) {
+  return HD == 128 ? c ^ (((r & 7) << 1) | ((r >> 3) & 1)) : c ^ (r & 7);
+}
 
-template <bool SPARSE>
+template <bool SPARSE, int HD>   // HD: head dimension
 __global__ void __launch_bounds__(256, 2)
     k_bwd_dq(BwdDqArgs a, int Hq, int G, int N, int nb, int block, float scale, float scale_log2, int n_qtiles) {
+  constexpr int kD = HD;
+  constexpr int kDT = HD / 32;                 // 32-column tiles of dQ
+  constexpr int kTile = kBN * kD;
   __shared__ __attribute__((aligned(16))) uint16_t K0[kTile], K1[kTile], V0[kTile], V1[kTile];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -79,25 +82,28 @@ __global__ void __launch_bounds__(256, 2)
   const float lse2 = qrow < N ? a.lse2_full[row] : 0.f;
   const float Dq = qrow < N ? a.D_full[row] : 0.f;
 
-  f32x16 dq[4];
+  f32x16 dq[kDT];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) dq[dt] = f32x16{};
+  for (int dt = 0; dt < kDT; ++dt) dq[dt] = f32x16{};
 
   const int j_last = min(N - 1, q0 + kBM - 1) / kBN;
 
-  // HBM -> LDS copy of one K/V tile: each wave moves rows 16*wave .. +15, one
-  // 1 KiB instruction per 4 rows; lane l fills physical chunk l % 16 of row
-  // 4n + l / 16.  Keys past the end read the last key (masked later).
+  // HBM -> LDS copy of one K/V tile: each wave moves a quarter of its rows,
+  // one 1 KiB instruction per kRowsOp rows; lane l fills physical chunk
+  // l % (HD / 8) of row kRowsOp n + l / (HD / 8).  Keys past the end read the
+  // last key (masked later).
+  constexpr int kRowsOp = 512 / HD;
+  constexpr int kOps = kBN / kRowsOp / 4;
   auto load_tile = [&](int j, uint16_t* Kd, uint16_t* Vd) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = wave * 4 + r;
-      const int rw = 4 * n + (lane >> 4);
-      const int p = lane & 15;
+    for (int r = 0; r < kOps; ++r) {
+      const int n = wave * kOps + r;
+      const int rw = kRowsOp * n + lane / (HD / 8);
+      const int p = lane % (HD / 8);
       const int64_t key = min(j * kBN + rw, N - 1);
-      __builtin_amdgcn_global_load_lds((const glb_void*)(kg + key * kD + 8 * swz_k(rw, p)),
+      __builtin_amdgcn_global_load_lds((const glb_void*)(kg + key * kD + 8 * swz_k<HD>(rw, p)),
                                        (lds_void*)(Kd + n * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const glb_void*)(vg + key * kD + 8 * swz_k(rw, p)),
+      __builtin_amdgcn_global_load_lds((const glb_void*)(vg + key * kD + 8 * swz_k<HD>(rw, p)),
                                        (lds_void*)(Vd + n * 512), 16, 0, 0);
     }
   };
@@ -181,7 +187,7 @@ __global__ void __launch_bounds__(256, 2)
           const int r = kh * 32 + col;
           bf16x8 ok[kD / 16], ov[kD / 16];
           auto rd = [&](int ds) {
-            const int off = r * kD + 8 * swz_k(r, 2 * ds + g);
+            const int off = r * kD + 8 * swz_k<HD>(r, 2 * ds + g);
             ok[ds] = lds_read8(&Ks[off]);
             ov[ds] = lds_read8(&Vs[off]);
           };
@@ -217,23 +223,23 @@ __global__ void __launch_bounds__(256, 2)
           }
         }
         // ---- dQ^T += K^T dS^T over the 32 keys (two k-steps of 16)
-        bf16x8 bds[2], ka[8];
+        bf16x8 bds[2], ka[2 * kDT];
 #pragma unroll
         for (int st = 0; st < 2; ++st)
           bds[st] = to_bf16x8(dsv[8 * st], dsv[8 * st + 1], dsv[8 * st + 2], dsv[8 * st + 3], dsv[8 * st + 4],
                               dsv[8 * st + 5], dsv[8 * st + 6], dsv[8 * st + 7]);
         auto rdk = [&](int u) {
-          const int st = u >> 2, dt = u & 3;
+          const int st = u / kDT, dt = u % kDT;
           const int r0 = kh * 32 + st * 16 + 4 * gk + srow, r1 = r0 + 8;
           const int c = 4 * dt + 2 * (grp & 1) + (m4 >> 1), e = 4 * (m4 & 1);
-          ka[u] = lds_tr_pair(&Ks[r0 * kD + 8 * swz_k(r0, c) + e], &Ks[r1 * kD + 8 * swz_k(r1, c) + e]);
+          ka[u] = lds_tr_pair(&Ks[r0 * kD + 8 * swz_k<HD>(r0, c) + e], &Ks[r1 * kD + 8 * swz_k<HD>(r1, c) + e]);
         };
         rdk(0);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {                 // K^T read one step ahead
+        for (int u = 0; u < 2 * kDT; ++u) {           // K^T read one step ahead
           __builtin_amdgcn_sched_barrier(0);
-          if (u + 1 < 8) rdk(u + 1);
-          dq[u & 3] = mfma32x32x16(ka[u], bds[u >> 2], dq[u & 3]);
+          if (u + 1 < 2 * kDT) rdk(u + 1);
+          dq[u % kDT] = mfma32x32x16(ka[u], bds[u / kDT], dq[u % kDT]);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -267,7 +273,7 @@ __global__ void __launch_bounds__(256, 2)
   if (!wave_live || qrow >= N) return;
   uint16_t* out = static_cast<uint16_t*>(a.dq) + row * kD;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
+  for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int d0 = 32 * dt + 8 * i4 + 4 * g;
@@ -283,12 +289,12 @@ void launch_bwd_dq(const Dims& D, const BwdDqArgs& a, hipStream_t s) {
   const int n_qtiles = (D.N + kBM - 1) / kBM;
   dim3 grid(D.B * D.Hq * n_qtiles);   // work items from qtile_item
   timing_begin(kKBwdDq, s);
-  if (a.ds_rows)
-    hipLaunchKernelGGL(k_bwd_dq<true>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.block, D.scale,
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.block, D.scale,
                        D.scale * 1.4426950408889634f, n_qtiles);
-  else
-    hipLaunchKernelGGL(k_bwd_dq<false>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.block, D.scale,
-                       D.scale * 1.4426950408889634f, n_qtiles);
+  };
+  if (D.d == 64) a.ds_rows ? go(k_bwd_dq<true, 64>) : go(k_bwd_dq<false, 64>);
+  else a.ds_rows ? go(k_bwd_dq<true, 128>) : go(k_bwd_dq<false, 128>);
   timing_end(kKBwdDq, s);
 }
 

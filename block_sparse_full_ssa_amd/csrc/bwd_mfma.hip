@@ -38,17 +38,18 @@
 namespace ssa {
 namespace {
 
-constexpr int kD = 128;
 constexpr int kBN = 128;       // keys per workgroup
 constexpr int kBM = 32;        // queries per iteration
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---------------------------------------------------------------- bwd_pre --
+template <int HD>   // head dimension
 __global__ void __launch_bounds__(256)
     k_bwd_pre(BwdPreArgs a, int64_t rows, float w_f, float w_s_align, float inv_m) {
-  // 16 lanes per row, 8 elements (16 bytes) each; 16 rows per workgroup
-  const int li = threadIdx.x & 15;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+  // LR = HD / 8 lanes per row, 8 elements (16 bytes) each; 256 / LR rows per workgroup
+  constexpr int kD = HD, LR = HD / 8;
+  const int li = threadIdx.x % LR;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (256 / LR) + (threadIdx.x / LR);
   const bool ok = row < rows;
   const int64_t off = (ok ? row : 0) * kD + 8 * li;
   const bool has_f = a.mode != kSparseOnly, has_s = a.mode != kFullOnly;
@@ -94,9 +95,9 @@ __global__ void __launch_bounds__(256)
     gsw[k] = pack_bf16x2(gs2[0], gs2[1]);
   }
 #pragma unroll
-  for (int o = 8; o >= 1; o >>= 1) {
-    Df += __shfl_xor(Df, o, 16);
-    Ds += __shfl_xor(Ds, o, 16);
+  for (int o = LR / 2; o >= 1; o >>= 1) {
+    Df += __shfl_xor(Df, o, LR);
+    Ds += __shfl_xor(Ds, o, LR);
   }
   if (!ok) return;
   if (has_f) *reinterpret_cast<uint4*>(a.g_full + off) = make_uint4(gfw[0], gfw[1], gfw[2], gfw[3]);
@@ -114,24 +115,32 @@ __global__ void __launch_bounds__(256)
 }
 
 // --------------------------------------------------------------- bwd_mfma --
-// Physical 16-byte chunk of logical chunk c in a 256-byte Q / G row r (read by
-// rows and by transposes).
-// The transposed tiles use c ^ (2 (r % 8) + (r / 8) % 2): measured on gfx950
-// it keeps the transpose reads (ds_read_b64_tr_b16) free of bank conflicts
-// as well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave
-// the transpose reads two-way conflicted.
-__device__ __forceinline__ int swz_t(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
+// Physical 16-byte chunk of logical chunk c in a K / Q / G row r of 2 HD bytes
+// (read by rows and by transposes).
+// 256-byte rows (HD = 128): c ^ (2 (r % 8) + (r / 8) % 2), measured on gfx950
+// to keep the transpose reads (ds_read_b64_tr_b16) free of bank conflicts as
+// well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave the
+// transpose reads two-way conflicted.  128-byte rows (HD = 64): c ^ (r % 8).
+template <int HD> __device__ __forceinline__ int swz_t(int r, int c) {
+  return HD == 128 ? c ^ (((r & 7) << 1) | ((r >> 3) & 1)) : c ^ (r & 7);
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
+template <int HD>   // head dimension
 __global__ void __launch_bounds__(256, 2)
     k_bwd_mfma(BwdMainArgs a, int Hq, int G, int N, float scale, float scale_log2) {
-  // Two workgroups per CU, so that the two waves on a SIMD belong to
-  // different workgroups and drift apart: one's waits (LDS, the softmax, the
-  // barrier) overlap the other's MFMAs.  A workgroup owns 128 keys (32 per
-  // wave); K of the 128 keys sits in LDS as an MFMA operand, V in registers.
-  // LDS: K (32 KiB) and two sets of {Q, G_f tiles [32][128]}.
+  // Two workgroups per CU, so that the waves on a SIMD belong to different
+  // workgroups and drift apart: one's waits (LDS, the softmax, the barrier)
+  // overlap the other's MFMAs (three spill at HD = 64).  A workgroup owns 128
+  // keys (32 per wave); K of the 128 keys sits in LDS as an MFMA operand, V
+  // in registers.  LDS: K (32 KiB at HD = 128) and two sets of {Q, G_f tiles
+  // [32][HD]}.
+  constexpr int kD = HD;
+  constexpr int kDT = HD / 32;                       // 32-column tiles of dK / dV
+  constexpr int kCh = HD / 8;                        // 16-byte chunks per row
+  constexpr int kRowsOp = 512 / HD;                  // rows of one 1 KiB copy
   constexpr int kT = kBM * kD;                       // one Q / G tile
   __shared__ __attribute__((aligned(16))) uint16_t Kt[kBN * kD];
   __shared__ __attribute__((aligned(16))) uint16_t Q0[kT], F0[kT], Q1[kT], F1[kT];
@@ -160,15 +169,17 @@ __global__ void __launch_bounds__(256, 2)
   const int qt0 = k0 / kBM;                         // first query tile that sees these keys
   const int iters = G * (nqt - qt0);                // >= G >= 1
 
-  // K of the 128 keys -> LDS: 32 instructions of 1 KiB (4 rows), 8 per wave;
-  // lane l fills physical chunk l % 16 of row 4n + l / 16 with the logical
-  // chunk stored there; keys past N repeat the last key (their pairs are masked)
+  // K of the 128 keys -> LDS: instructions of 1 KiB (kRowsOp rows), a quarter
+  // per wave; lane l fills physical chunk l % kCh of row kRowsOp n + l / kCh
+  // with the logical chunk stored there; keys past N repeat the last key
+  // (their pairs are masked)
+  constexpr int kOpsK = kBN / kRowsOp / 4;
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int n = wave * 8 + r;                     // uniform
-    const int row = 4 * n + (lane >> 4);
+  for (int r = 0; r < kOpsK; ++r) {
+    const int n = wave * kOpsK + r;                 // uniform
+    const int row = kRowsOp * n + lane / kCh;
     const int64_t key = min(k0 + row, N - 1);
-    __builtin_amdgcn_global_load_lds((const glb_void*)(kg + key * kD + 8 * swz_t(row, lane & 15)),
+    __builtin_amdgcn_global_load_lds((const glb_void*)(kg + key * kD + 8 * swz_t<HD>(row, lane % kCh)),
                                      (lds_void*)(Kt + n * 512), 16, 0, 0);
   }
   // dP B operand [16 d x 32 keys] from registers: key = kw0 + col, d = 16 ds + 8 g + s
@@ -195,23 +206,26 @@ __global__ void __launch_bounds__(256, 2)
       q0 -= kBM;
     }
   };
-  // Q / G_f tiles of one iteration: 16 instructions, 4 per wave; the tile
-  // bases are uniform, the lane offsets fixed
+  // Q / G_f tiles of one iteration: HD / 16 instructions of 1 KiB per tile,
+  // HD / 32 per wave; the tile bases are uniform, the lane offsets fixed
   // (byte offsets, so that each load is a scalar base plus a 32-bit lane offset)
-  uint32_t dmo[4];
+  constexpr int kOpsT = HD / 16, kOpsW = HD / 32;
+  uint32_t dmo[kOpsW];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 4 * ((wave * 4 + r) & 7) + (lane >> 4);
-    dmo[r] = 2 * (row * kD + 8 * swz_t(row, lane & 15));
+  for (int r = 0; r < kOpsW; ++r) {
+    const int row = kRowsOp * ((wave * kOpsW + r) % kOpsT) + lane / kCh;
+    dmo[r] = 2 * (row * kD + 8 * swz_t<HD>(row, lane % kCh));
   }
   auto load_tiles = [&](int hq, int q0, uint16_t* Qd, uint16_t* Fd) {
     const int64_t tile = ((static_cast<int64_t>(b) * Hq + hq) * N + q0) * (kD * 2);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int n = wave * 4 + r;                   // 0..15, uniform
-      const char* src = static_cast<const char*>((n >> 3) ? a.g_full : a.q) + tile;
-      uint16_t* dst = (n >> 3) ? Fd : Qd;
-      __builtin_amdgcn_global_load_lds((const glb_void*)(src + dmo[r]), (lds_void*)(dst + (n & 7) * 512), 16, 0, 0);
+    for (int r = 0; r < kOpsW; ++r) {
+      const int n = wave * kOpsW + r;               // uniform
+      const bool gt = n >= kOpsT;                   // the G tile's half of the copies
+      const char* src = static_cast<const char*>(gt ? a.g_full : a.q) + tile;
+      uint16_t* dst = gt ? Fd : Qd;
+      __builtin_amdgcn_global_load_lds((const glb_void*)(src + dmo[r]), (lds_void*)(dst + (n % kOpsT) * 512), 16, 0,
+                                       0);
     }
   };
   // Row values of the 32 queries: lane l holds lse2 and D of query l % 32.
@@ -239,9 +253,9 @@ __global__ void __launch_bounds__(256, 2)
                                                    : make_uint4(0x3F803F80u, 0x00003F80u, 0u, 0u));
   const float inv_c = 1.f / scale_log2;
 
-  f32x16 dv[4], dk[4];
+  f32x16 dv[kDT], dk[kDT];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+  for (int dt = 0; dt < kDT; ++dt) {
     dv[dt] = f32x16{};
     dk[dt] = f32x16{};
   }
@@ -265,8 +279,9 @@ __global__ void __launch_bounds__(256, 2)
       // (st, dt): tb + 2048 st + 32 (dt ^ tx), the second row eight below at tb1
       int c7 = col & 7, tx = 2 * gk + (srow >> 1);
       asm volatile("" : "+v"(c7), "+v"(tx));
-      const int rowq = col * kD + 8 * (g ^ ((col >> 3) & 1));
-      const int rowk = (32 * kq + col) * kD + 8 * (g ^ ((col >> 3) & 1));
+      // (HD = 128: the swizzle folded into these offsets; HD = 64 calls it)
+      const int rowq = HD == 128 ? col * kD + 8 * (g ^ ((col >> 3) & 1)) : col * kD;
+      const int rowk = HD == 128 ? (32 * kq + col) * kD + 8 * (g ^ ((col >> 3) & 1)) : (32 * kq + col) * kD;
       const int tb0 = (4 * gk + srow) * kD + 8 * ((2 * (grp & 1) + (m4 >> 1)) ^ (2 * (srow & 1))) + 4 * (m4 & 1);
       const int tb1 = tb0 + 8 * kD + 8 * (1 - 2 * ((m4 >> 1) & 1));
       // ---- S = Q K^T, dP = G_f V^T  [32 q x 32 keys], two independent
@@ -276,7 +291,8 @@ __global__ void __launch_bounds__(256, 2)
       f32x16 dpf = mfma32x32x16(split3(-rd), ones, f32x16{});
       bf16x8 ok[8], oq[8], of[8];
       auto rd = [&](int ds) {
-        const int cs = 16 * (ds ^ c7);   // the same chunk for query row col and key row 32 kq + col
+        // the same chunk for query row col and key row 32 kq + col
+        const int cs = HD == 128 ? 16 * (ds ^ c7) : 8 * swz_t<HD>(col, 2 * ds + g);
         ok[ds] = lds_read8(&Kt[rowk + cs]);
         oq[ds] = lds_read8(&Qs[rowq + cs]);
         of[ds] = lds_read8(&Fs[rowq + cs]);
@@ -317,24 +333,33 @@ __global__ void __launch_bounds__(256, 2)
       }
       // ---- dV^T += G^T P, dK^T += Q^T dS  (k = queries; 2 steps of 16),
       // transpose reads one step ahead
-      bf16x8 bpf[2], bds[2], tg[8], tq[8];
+      bf16x8 bpf[2], bds[2], tg[2 * kDT], tq[2 * kDT];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         bpf[st] = __builtin_bit_cast(bf16x8, make_uint4(pfp[4 * st], pfp[4 * st + 1], pfp[4 * st + 2], pfp[4 * st + 3]));
         bds[st] = __builtin_bit_cast(bf16x8, make_uint4(dsp[4 * st], dsp[4 * st + 1], dsp[4 * st + 2], dsp[4 * st + 3]));
       }
+      // step u: k-step st = u / kDT (16 queries), column tile dt = u % kDT
       auto rdB = [&](int u) {
-        const int cx = 2048 * (u >> 2) + 32 * ((u & 3) ^ tx);
-        tg[u] = lds_tr_pair(&Fs[tb0 + cx], &Fs[tb1 + cx]);
-        tq[u] = lds_tr_pair(&Qs[tb0 + cx], &Qs[tb1 + cx]);
+        if constexpr (HD == 128) {
+          const int cx = 2048 * (u >> 2) + 32 * ((u & 3) ^ tx);
+          tg[u] = lds_tr_pair(&Fs[tb0 + cx], &Fs[tb1 + cx]);
+          tq[u] = lds_tr_pair(&Qs[tb0 + cx], &Qs[tb1 + cx]);
+        } else {
+          const int r0 = 16 * (u / kDT) + 4 * gk + srow, r1 = r0 + 8;
+          const int cl = 4 * (u % kDT) + 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
+          const int o0 = r0 * kD + 8 * swz_t<HD>(r0, cl) + e4, o1 = r1 * kD + 8 * swz_t<HD>(r1, cl) + e4;
+          tg[u] = lds_tr_pair(&Fs[o0], &Fs[o1]);
+          tq[u] = lds_tr_pair(&Qs[o0], &Qs[o1]);
+        }
       };
       rdB(0);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 2 * kDT; ++u) {
         __builtin_amdgcn_sched_barrier(0);
-        if (u + 1 < 8) rdB(u + 1);
-        dv[u & 3] = mfma32x32x16(tg[u], bpf[u >> 2], dv[u & 3]);
-        dk[u & 3] = mfma32x32x16(tq[u], bds[u >> 2], dk[u & 3]);
+        if (u + 1 < 2 * kDT) rdB(u + 1);
+        dv[u % kDT] = mfma32x32x16(tg[u], bpf[u / kDT], dv[u % kDT]);
+        dk[u % kDT] = mfma32x32x16(tq[u], bds[u / kDT], dk[u % kDT]);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -367,7 +392,7 @@ __global__ void __launch_bounds__(256, 2)
     uint16_t* dkg = static_cast<uint16_t*>(a.dk) + kro;
     uint16_t* dvg = static_cast<uint16_t*>(a.dv) + kro;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
+    for (int dt = 0; dt < kDT; ++dt) {
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int d0 = 32 * dt + 8 * a4 + 4 * g;
@@ -390,20 +415,23 @@ __global__ void __launch_bounds__(256, 2)
 
 }  // namespace
 
-bool bwd_mfma_supported(const Dims& D) { return D.dtype == 1 && D.d == kD; }
+bool bwd_mfma_supported(const Dims& D) { return D.dtype == 1 && (D.d == 128 || D.d == 64); }
 
 void launch_bwd_pre(const Dims& D, const BwdPreArgs& a, float w_sparsity, float w_commit, hipStream_t s) {
   const float inv_m = static_cast<float>(1.0 / static_cast<double>(D.q_elems()));
-  dim3 grid(static_cast<unsigned>((D.rows() + 15) / 16));
+  const int rows_wg = D.d == 64 ? 32 : 16;
+  dim3 grid(static_cast<unsigned>((D.rows() + rows_wg - 1) / rows_wg));
   timing_begin(kKBwdPre, s);
-  hipLaunchKernelGGL(k_bwd_pre, grid, dim3(256), 0, s, a, D.rows(), w_sparsity, w_commit, inv_m);
+  if (D.d == 64) hipLaunchKernelGGL(k_bwd_pre<64>, grid, dim3(256), 0, s, a, D.rows(), w_sparsity, w_commit, inv_m);
+  else hipLaunchKernelGGL(k_bwd_pre<128>, grid, dim3(256), 0, s, a, D.rows(), w_sparsity, w_commit, inv_m);
   timing_end(kKBwdPre, s);
 }
 
 void launch_bwd_mfma(const Dims& D, const BwdMainArgs& a, hipStream_t s) {
   dim3 grid(D.B * D.Hkv, (D.N + kBN - 1) / kBN);
   timing_begin(kKBwdMfma, s);
-  hipLaunchKernelGGL(k_bwd_mfma, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.scale, D.scale * kLog2e);
+  if (D.d == 64) hipLaunchKernelGGL(k_bwd_mfma<64>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.scale, D.scale * kLog2e);
+  else hipLaunchKernelGGL(k_bwd_mfma<128>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.scale, D.scale * kLog2e);
   timing_end(kKBwdMfma, s);
 }
 

@@ -35,6 +35,8 @@
 // in bf16 and the row sums add exactly those rounded values, so each output
 // row is a weighted mean of value rows with the weights the products used.
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -42,17 +44,19 @@
 namespace ssa {
 namespace {
 
-constexpr int kD = 128;          // head dimension
 constexpr int kBM = 128;         // queries per workgroup
-// Keys per K/V tile: 64 for both streams, 32 for the full stream alone, whose
-// smaller tiles (32 KiB of LDS) and registers (at most 168) let three
-// workgroups share a CU instead of two.
 enum { kModeDual = 0, kModeFull = 1 };   // both streams / the full stream alone
 
-template <int MODE> struct FwdTile {
-  static constexpr int kBN = MODE == kModeFull ? 32 : 64;
-  static constexpr int kTile = kBN * kD;   // elements of one K or V tile
-  static constexpr int kPerCu = MODE == kModeFull ? 3 : 2;
+// Keys per K/V tile and workgroups per CU, by head dimension D (128 or 64).
+// D = 128: 64-key tiles for both streams (two workgroups per CU: both output
+// accumulators take 128 registers), 32-key tiles for the full stream alone,
+// whose smaller tiles (32 KiB of LDS) and registers (at most 168) let three
+// workgroups share a CU.  D = 64 needs half the registers and LDS: 64-key
+// tiles, three workgroups per CU with both streams and four with one.
+template <int MODE, int D> struct FwdTile {
+  static constexpr int kBN = (MODE == kModeFull && D == 128) ? 32 : 64;
+  static constexpr int kTile = kBN * D;   // elements of one K or V tile
+  static constexpr int kPerCu = D == 64 ? (MODE == kModeFull ? 4 : 3) : (MODE == kModeFull ? 3 : 2);
 };
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kTau = 8.f;      // lazy-rescale threshold (log2 units)
@@ -63,12 +67,17 @@ typedef __attribute__((address_space(1))) void glb_void;
 
 // Physical 16-byte chunk of logical chunk c in row r: K tiles are only read
 // by rows; V tiles by transpose reads.
-// The transposed tiles use c ^ (2 (r % 8) + (r / 8) % 2): measured on gfx950
-// it keeps the transpose reads (ds_read_b64_tr_b16) free of bank conflicts
-// as well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave
-// the transpose reads two-way conflicted.
-__device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
-__device__ __forceinline__ int swz_v(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
+// 256-byte rows (D = 128): the transposed tiles use c ^ (2 (r % 8) + (r / 8) % 2):
+// measured on gfx950 it keeps the transpose reads (ds_read_b64_tr_b16) free
+// of bank conflicts as well as the 16-byte row reads, where c ^ (r % 8) or
+// c ^ (r % 16) leave the transpose reads two-way conflicted.  128-byte rows
+// (D = 64) hold 8 chunks, permuted by c ^ (r % 8) in both tiles.
+template <int D> __device__ __forceinline__ int swz_k(int r, int c) {
+  return D == 128 ? c ^ (r & 15) : c ^ (r & 7);
+}
+template <int D> __device__ __forceinline__ int swz_v(int r, int c) {
+  return D == 128 ? c ^ (((r & 7) << 1) | ((r >> 3) & 1)) : c ^ (r & 7);
+}
 
 __device__ __forceinline__ float max16(const f32x16& v) {
   float m = fmaxf(v[0], v[1]);
@@ -77,17 +86,17 @@ __device__ __forceinline__ float max16(const f32x16& v) {
   return m;
 }
 
-// Two or three workgroups per CU (see FwdTile), so one wave's softmax
+// Two to four workgroups per CU (see FwdTile), so one wave's softmax
 // overlaps another wave's matrix work on every SIMD.
-template <int MODE, bool STATS>
-__global__ void __launch_bounds__(256, FwdTile<MODE>::kPerCu)
+template <int MODE, bool STATS, int HD>
+__global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
     k_fwd_mfma(FwdArgs a, int Hq, int G, int N, int Nq, int q_off, int block, int nb, int K, float scale_log2,
                int n_qtiles) {
   constexpr bool kSparse = MODE == kModeDual;
   // K and V tiles [64][128] (swizzled), two of each; separate objects so that
   // the compiler can tell the tile being read from the one being filled
-  constexpr int kBN = FwdTile<MODE>::kBN;
-  constexpr int kTile = FwdTile<MODE>::kTile;
+  constexpr int kBN = FwdTile<MODE, HD>::kBN;
+  constexpr int kTile = FwdTile<MODE, HD>::kTile;
   __shared__ __attribute__((aligned(16))) uint16_t K0[kTile], K1[kTile], V0[kTile], V1[kTile];
   // dynamic LDS: the selection bits [kBM][W] of the rows
   extern __shared__ __attribute__((aligned(16))) uint32_t bits[];
@@ -109,9 +118,9 @@ __global__ void __launch_bounds__(256, FwdTile<MODE>::kPerCu)
   const int qend = q_off + Nq;
   const int b = bh / Hq, h = bh % Hq;
   const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
-  const uint16_t* qg = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(bh) * Nq * kD;
-  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + bc * N * kD;
-  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + bc * N * kD;
+  const uint16_t* qg = static_cast<const uint16_t*>(a.q) + static_cast<int64_t>(bh) * Nq * HD;
+  const uint16_t* kg = static_cast<const uint16_t*>(a.k) + bc * N * HD;
+  const uint16_t* vg = static_cast<const uint16_t*>(a.v) + bc * N * HD;
 
   // ---- selection bits of the workgroup's rows
   if (kSparse) {
@@ -132,17 +141,18 @@ __global__ void __launch_bounds__(256, FwdTile<MODE>::kPerCu)
   const bool wave_live = q0 + wave * 32 < qend;
   const int wave_q0 = q0 + wave * 32;
   const int wave_last_q = min(qend - 1, wave_q0 + 31);
-  bf16x8 qreg[kD / 16];
+  bf16x8 qreg[HD / 16];
 #pragma unroll
-  for (int ds = 0; ds < kD / 16; ++ds) {
+  for (int ds = 0; ds < HD / 16; ++ds) {
     uint4 u = make_uint4(0, 0, 0, 0);
-    if (qrow < qend) u = *reinterpret_cast<const uint4*>(qg + static_cast<int64_t>(qrow - q_off) * kD + 16 * ds + 8 * g);
+    if (qrow < qend) u = *reinterpret_cast<const uint4*>(qg + static_cast<int64_t>(qrow - q_off) * HD + 16 * ds + 8 * g);
     qreg[ds] = __builtin_bit_cast(bf16x8, u);
   }
 
-  f32x16 of[4], os[4];
+  constexpr int kDT = HD / 32;       // 32-column output tiles
+  f32x16 of[kDT], os[kDT];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+  for (int dt = 0; dt < kDT; ++dt) {
     of[dt] = f32x16{};
     os[dt] = f32x16{};
   }
@@ -156,18 +166,21 @@ __global__ void __launch_bounds__(256, FwdTile<MODE>::kPerCu)
   if (kSparse) __syncthreads();
 
   // HBM -> LDS copy of one K/V tile: each wave moves a quarter of its rows,
-  // one 1 KiB instruction per 4 rows; lane l fills physical chunk l % 16 of row
-  // 4n + l / 16, so it fetches the logical chunk stored there.  Keys past the
-  // end read the last key: finite values that the causal mask removes.
+  // one 1 KiB instruction per kRowsOp rows; lane l fills physical chunk
+  // l % (HD / 8) of row kRowsOp n + l / (HD / 8), so it fetches the logical chunk
+  // stored there.  Keys past the end read the last key: finite values that the
+  // causal mask removes.
+  constexpr int kRowsOp = 512 / HD;             // rows of one 1 KiB copy
+  constexpr int kOps = kBN / kRowsOp / 4;      // copies per wave and tile
   auto load_tile = [&](int j, uint16_t* Kd, uint16_t* Vd) {
 #pragma unroll
-    for (int r = 0; r < kBN / 16; ++r) {
-      const int n = wave * (kBN / 16) + r;
-      const int row = 4 * n + (lane >> 4);
-      const int p = lane & 15;
+    for (int r = 0; r < kOps; ++r) {
+      const int n = wave * kOps + r;
+      const int row = kRowsOp * n + lane / (HD / 8);
+      const int p = lane % (HD / 8);
       const int64_t key = min(j * kBN + row, N - 1);
-      const uint16_t* srck = kg + key * kD + 8 * swz_k(row, p);
-      const uint16_t* srcv = vg + key * kD + 8 * swz_v(row, p);
+      const uint16_t* srck = kg + key * HD + 8 * swz_k<HD>(row, p);
+      const uint16_t* srcv = vg + key * HD + 8 * swz_v<HD>(row, p);
       __builtin_amdgcn_global_load_lds((const glb_void*)srck, (lds_void*)(Kd + n * 512), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((const glb_void*)srcv, (lds_void*)(Vd + n * 512), 16, 0, 0);
     }
@@ -196,8 +209,8 @@ __global__ void __launch_bounds__(256, FwdTile<MODE>::kPerCu)
       {
         const int r = kh * 32 + col;
 #pragma unroll
-        for (int ds = 0; ds < kD / 16; ++ds)
-          s = mfma32x32x16(lds_read8(&Ks[r * kD + 8 * swz_k(r, 2 * ds + g)]), qreg[ds], s);
+        for (int ds = 0; ds < HD / 16; ++ds)
+          s = mfma32x32x16(lds_read8(&Ks[r * HD + 8 * swz_k<HD>(r, 2 * ds + g)]), qreg[ds], s);
       }
       // logits stay unscaled: the scale (> 0) goes into the maximum and into
       // each exponent's fused multiply-add
@@ -275,7 +288,7 @@ __global__ void __launch_bounds__(256, FwdTile<MODE>::kPerCu)
       lf = lf * alpha + sum;
       if (__any(alpha != 1.f)) {
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) of[dt] *= alpha;
+        for (int dt = 0; dt < kDT; ++dt) of[dt] *= alpha;
       }
       mf = mfn;
       if (kSparse && sparse_any) {
@@ -295,7 +308,7 @@ __global__ void __launch_bounds__(256, FwdTile<MODE>::kPerCu)
         ls = ls * alpha_s + sum_s;
         if (__any(alpha_s != 1.f)) {
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt) os[dt] *= alpha_s;
+          for (int dt = 0; dt < kDT; ++dt) os[dt] *= alpha_s;
         }
         ms = msn;
       }
@@ -306,10 +319,11 @@ __global__ void __launch_bounds__(256, FwdTile<MODE>::kPerCu)
         const int r0 = kh * 32 + st2 * 16 + 4 * gk + srow;   // key row of this lane's first read
         const int r1 = r0 + 8;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int dt = 0; dt < kDT; ++dt) {
           const int c = 4 * dt + 2 * (grp & 1) + (m4 >> 1);   // logical 16-byte chunk
           const int e = 4 * (m4 & 1);
-          const bf16x8 va = lds_tr_pair(&Vs[r0 * kD + 8 * swz_v(r0, c) + e], &Vs[r1 * kD + 8 * swz_v(r1, c) + e]);
+          const bf16x8 va =
+              lds_tr_pair(&Vs[r0 * HD + 8 * swz_v<HD>(r0, c) + e], &Vs[r1 * HD + 8 * swz_v<HD>(r1, c) + e]);
           of[dt] = mfma32x32x16(va, pf[st2], of[dt]);
           if (kSparse && sparse_any) os[dt] = mfma32x32x16(va, ps[st2], os[dt]);
         }
@@ -343,7 +357,7 @@ __global__ void __launch_bounds__(256, FwdTile<MODE>::kPerCu)
   const int64_t row = static_cast<int64_t>(bh) * Nq + (qrow - q_off);
   float sq = 0.f;
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+  for (int dt = 0; dt < kDT; ++dt) {
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       const int dcol = 32 * dt + 8 * i4 + 4 * g;
@@ -357,11 +371,11 @@ __global__ void __launch_bounds__(256, FwdTile<MODE>::kPerCu)
       if (row_ok) {
         {
           uint2 u = make_uint2(pack_bf16x2(hf[0], hf[1]), pack_bf16x2(hf[2], hf[3]));
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h_full) + row * kD + dcol) = u;
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h_full) + row * HD + dcol) = u;
         }
         if (kSparse) {
           uint2 u = make_uint2(pack_bf16x2(hs[0], hs[1]), pack_bf16x2(hs[2], hs[3]));
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h_sparse) + row * kD + dcol) = u;
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.h_sparse) + row * HD + dcol) = u;
         }
       }
     }
@@ -383,22 +397,22 @@ __global__ void __launch_bounds__(256, FwdTile<MODE>::kPerCu)
   }
 }
 
-template <int MODE, bool STATS>
+template <int MODE, bool STATS, int HD>
 hipError_t launch_mode(const Dims& D, const FwdArgs& a, size_t lds, int n_qtiles, float scale_log2, hipStream_t s) {
   // LDS above 64 KiB in total must be granted per kernel; the grant is set on
   // every launch (the device current at the call), so no state is kept
-  const void* fn = reinterpret_cast<const void*>(&k_fwd_mfma<MODE, STATS>);
+  const void* fn = reinterpret_cast<const void*>(&k_fwd_mfma<MODE, STATS, HD>);
   if (lds > 0) {
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(lds));
     if (e != hipSuccess) return e;
   }
   dim3 grid(D.B * D.Hq * n_qtiles);   // work items from qtile_item
-  hipLaunchKernelGGL((k_fwd_mfma<MODE, STATS>), grid, dim3(256), lds, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.block,
+  hipLaunchKernelGGL((k_fwd_mfma<MODE, STATS, HD>), grid, dim3(256), lds, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.block,
                      D.nb, D.K, scale_log2, n_qtiles);
   return hipSuccess;
 }
 
-constexpr size_t kStaticLds = 4 * FwdTile<kModeDual>::kTile * sizeof(uint16_t);   // the larger tiles
+constexpr size_t kStaticLds = 4 * FwdTile<kModeDual, 128>::kTile * sizeof(uint16_t);   // the largest tiles
 
 size_t lds_bytes(const Dims& D) {   // dynamic part: selection bits
   const int W = (D.nb + 31) / 32;
@@ -409,7 +423,7 @@ size_t lds_bytes(const Dims& D) {   // dynamic part: selection bits
 
 bool fwd_mfma_supported(const Dims& D) {
   // the selection bits of 128 rows must fit in LDS next to the K/V tiles
-  return D.dtype == 1 && D.d == kD && kStaticLds + lds_bytes(D) <= 160 * 1024;
+  return D.dtype == 1 && (D.d == 128 || D.d == 64) && kStaticLds + lds_bytes(D) <= 160 * 1024;
 }
 
 hipError_t launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s) {
@@ -419,13 +433,15 @@ hipError_t launch_fwd_mfma(const Dims& D, const FwdArgs& a, hipStream_t s) {
   timing_begin(kKFwdMfma, s);
   const bool stats = a.sink_mass != nullptr;
   hipError_t e;
-  if (a.mode == kFullOnly) {
-    e = stats ? launch_mode<kModeFull, true>(D, a, lds, n_qtiles, scale_log2, s)
-              : launch_mode<kModeFull, false>(D, a, lds, n_qtiles, scale_log2, s);
-  } else {
-    e = stats ? launch_mode<kModeDual, true>(D, a, lds, n_qtiles, scale_log2, s)
-              : launch_mode<kModeDual, false>(D, a, lds, n_qtiles, scale_log2, s);
-  }
+  auto go = [&](auto d_tag) {
+    constexpr int DD = decltype(d_tag)::value;
+    if (a.mode == kFullOnly)
+      return stats ? launch_mode<kModeFull, true, DD>(D, a, lds, n_qtiles, scale_log2, s)
+                   : launch_mode<kModeFull, false, DD>(D, a, lds, n_qtiles, scale_log2, s);
+    return stats ? launch_mode<kModeDual, true, DD>(D, a, lds, n_qtiles, scale_log2, s)
+                 : launch_mode<kModeDual, false, DD>(D, a, lds, n_qtiles, scale_log2, s);
+  };
+  e = D.d == 64 ? go(std::integral_constant<int, 64>{}) : go(std::integral_constant<int, 128>{});
   timing_end(kKFwdMfma, s);
   return e;
 }

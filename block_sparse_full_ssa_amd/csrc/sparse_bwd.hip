@@ -32,6 +32,8 @@
 // The layout of every product is the full-stream kernel's (S = Q K^T, lane l
 // owns key l % 32).
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -39,28 +41,33 @@
 namespace ssa {
 namespace {
 
-constexpr int kD = 128;
-
-// Physical 16-byte chunk of logical chunk c: 256-byte Q / G rows (read by rows
-// and by transposes), 64-byte dS^T rows.
-// The transposed tiles use c ^ (2 (r % 8) + (r / 8) % 2): measured on gfx950
-// it keeps the transpose reads (ds_read_b64_tr_b16) free of bank conflicts
-// as well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave
-// the transpose reads two-way conflicted.
-__device__ __forceinline__ int swz_t(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
+// Physical 16-byte chunk of logical chunk c: Q / G rows of 2 HD bytes (read by
+// rows and by transposes), 64-byte dS^T rows.
+// 256-byte rows (HD = 128): c ^ (2 (r % 8) + (r / 8) % 2), measured on gfx950
+// to keep the transpose reads (ds_read_b64_tr_b16) free of bank conflicts as
+// well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave the
+// transpose reads two-way conflicted.  128-byte rows (HD = 64): c ^ (r % 8).
+template <int HD> __device__ __forceinline__ int swz_t(int r, int c) {
+  return HD == 128 ? c ^ (((r & 7) << 1) | ((r >> 3) & 1)) : c ^ (r & 7);
+}
 __device__ __forceinline__ int swz_s(int r, int c) { return c ^ ((r >> 1) & 3); }
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
-template <int KH, bool DSOUT>
+template <int KH, bool DSOUT, int HD>   // HD: head dimension
 __global__ void __launch_bounds__(256, 1)
     k_bwd_sparse(SparseBwdArgs a, int Hq, int G, int N, int nb, float scale, float scale_log2) {
+  constexpr int kD = HD;
+  constexpr int kDT = HD / 32;               // 32-column tiles of dK / dV
+  constexpr int kCh = HD / 8;                // 16-byte chunks per row
   constexpr int kBlk = 32 * KH;
   constexpr int QS = 4 / KH;                 // query streams
   constexpr int kT = 32 * kD;                // one Q / G tile
   constexpr int kDS = kBlk * 32;             // one dS^T tile
-  constexpr int kSlice = kD / KH;            // dQ columns per wave
+  // dQ columns per wave (sparse-only): a stream's waves split d, at least 32
+  // columns each (HD = 64 with 128-key blocks: waves kh >= 2 have none)
+  constexpr int kSlice = kD / KH >= 32 ? kD / KH : 32;
   // LDS: the key block (for the dQ operand), then per stream two sets of
   // {Q, G_s tiles, dS^T tile, row values}; separate objects per set so that
   // the compiler can tell the set being read from the one being filled
@@ -95,7 +102,7 @@ __global__ void __launch_bounds__(256, 1)
   // result rows of the lane's key: d = 32 dt + 8 a4 + 4 g + e
   auto write_kv = [&](const f32x16* dk, const f32x16* dv) {
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
         const int d0 = 32 * dt + 8 * a4 + 4 * g;
@@ -115,9 +122,9 @@ __global__ void __launch_bounds__(256, 1)
       }
   };
 
-  f32x16 dv[4], dk[4];
+  f32x16 dv[kDT], dk[kDT];
 #pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
+  for (int dt = 0; dt < kDT; ++dt) {
     dv[dt] = f32x16{};
     dk[dt] = f32x16{};
   }
@@ -127,8 +134,8 @@ __global__ void __launch_bounds__(256, 1)
   }
 
   // ---- the key block in LDS (plain layout) for the dQ operand
-  for (int e = tid; e < kBlk * kD / 8; e += 256) {
-    const int row = e >> 4, c8 = e & 15;
+  for (int e = tid; e < kBlk * kCh; e += 256) {
+    const int row = e / kCh, c8 = e % kCh;
     *reinterpret_cast<uint4*>(&Kst[row * kD + 8 * c8]) =
         *reinterpret_cast<const uint4*>(kg + static_cast<int64_t>(kblk0 + row) * kD + 8 * c8);
   }
@@ -143,8 +150,9 @@ __global__ void __launch_bounds__(256, 1)
   // dQ B operands [16 keys x 32 d]: d = slice + 32 dt + col, keys of k-step ks
   // in the transpose-read order of the dS^T tile
   constexpr int kDt = kSlice / 32;
+  const bool has_slice = kSlice * kh < kD;    // uniform
   bf16x8 kq[DSOUT ? 1 : 2 * KH][kDt];
-  if constexpr (!DSOUT) {
+  if (!DSOUT && has_slice) {
 #pragma unroll
     for (int ks = 0; ks < 2 * KH; ++ks)
 #pragma unroll
@@ -166,20 +174,21 @@ __global__ void __launch_bounds__(256, 1)
     const int hl = e / N;
     return static_cast<int>((qhead0 + hl) * N + (e - hl * N));
   };
-  // HBM -> LDS copy of the stream's Q and G_s rows of an entry set: 16
-  // instructions of 4 rows, split over the stream's KH waves; lane l fills
-  // physical chunk l % 16 of row 4 n + l / 16
+  // HBM -> LDS copy of the stream's Q and G_s rows of an entry set: 2 kOpsT
+  // instructions of kRowsOp rows, split over the stream's KH waves; lane l
+  // fills physical chunk l % kCh of row kRowsOp n + l / kCh
+  constexpr int kRowsOp = 512 / HD, kOpsT = HD / 16;
   auto load_tiles = [&](int e, uint16_t* Qd, uint16_t* Fd) {
     const int R = row_of(e);
 #pragma unroll
-    for (int u = 0; u < 16 / KH; ++u) {
-      const int nn = u * KH + kh;                 // 0..15, uniform
-      const int which = nn >> 3, n8 = nn & 7;
-      const int row = 4 * n8 + (lane >> 4);
+    for (int u = 0; u < 2 * kOpsT / KH; ++u) {
+      const int nn = u * KH + kh;                 // uniform
+      const int which = nn / kOpsT, n8 = nn % kOpsT;
+      const int row = kRowsOp * n8 + lane / kCh;
       const int Rr = __shfl(R, row, 64);
       const uint16_t* src = which == 0 ? static_cast<const uint16_t*>(a.q) : a.g_sparse;
       uint16_t* dst = (which == 0 ? Qd : Fd) + qs * kT;
-      const int cl = swz_t(row, lane & 15);
+      const int cl = swz_t<HD>(row, lane % kCh);
       __builtin_amdgcn_global_load_lds((const glb_void*)(src + static_cast<int64_t>(Rr) * kD + 8 * cl),
                                        (lds_void*)(dst + n8 * 512), 16, 0, 0);
     }
@@ -231,7 +240,7 @@ __global__ void __launch_bounds__(256, 1)
       const int ra = col * kD;
 #pragma unroll
       for (int ds = 0; ds < kD / 16; ++ds) {
-        const int off = ra + 8 * swz_t(col, 2 * ds + g);
+        const int off = ra + 8 * swz_t<HD>(col, 2 * ds + g);
         s = mfma32x32x16(lds_read8(&Qs[off]), kb[ds], s);
         dp = mfma32x32x16(lds_read8(&Fs[off]), vb[ds], dp);
       }
@@ -294,9 +303,9 @@ __global__ void __launch_bounds__(256, 1)
         const bf16x8 bds = to_bf16x8(dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3], dsv[o + 4], dsv[o + 5], dsv[o + 6], dsv[o + 7]);
         const int r0 = 16 * st + 4 * gk + srow, r1 = r0 + 8;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int dt = 0; dt < kDT; ++dt) {
           const int cl = 4 * dt + 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
-          const int o0 = r0 * kD + 8 * swz_t(r0, cl) + e4, o1 = r1 * kD + 8 * swz_t(r1, cl) + e4;
+          const int o0 = r0 * kD + 8 * swz_t<HD>(r0, cl) + e4, o1 = r1 * kD + 8 * swz_t<HD>(r1, cl) + e4;
           dv[dt] = mfma32x32x16(lds_tr_pair(&Fs[o0], &Fs[o1]), bp, dv[dt]);
           dk[dt] = mfma32x32x16(lds_tr_pair(&Qs[o0], &Qs[o1]), bds, dk[dt]);
         }
@@ -307,7 +316,7 @@ __global__ void __launch_bounds__(256, 1)
     __syncthreads();
 
     // ---- dQ[32 q x slice] of the stream's batch = dS[32 q x block keys] K[block keys x slice]
-    if (!DSOUT && has) {
+    if (!DSOUT && has && has_slice) {
       f32x16 dq[kDt];
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) dq[dt] = f32x16{};
@@ -363,14 +372,14 @@ __global__ void __launch_bounds__(256, 1)
         __syncthreads();
         if (qs == o) {
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
+          for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) red[(dt * 16 + i) * 64 + lane] = acc[dt][i];
         }
         __syncthreads();
         if (qs == 0) {
 #pragma unroll
-          for (int dt = 0; dt < 4; ++dt)
+          for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[dt][i] += red[(dt * 16 + i) * 64 + lane];
         }
@@ -381,17 +390,20 @@ __global__ void __launch_bounds__(256, 1)
 }
 
 // Sparse-only dQ: the sum of a query row's partials over its selected
-// blocks, in selection order.  16 lanes per row (8 columns of d each), 16
-// rows per workgroup; the partial of (row, block j) is the row's entry in
-// bucket (b, c, j), found through the bucket mask word and its position.
-// Entries naming no causal block, and repeats, are skipped (no partial).
+// blocks, in selection order.  LR = HD / 8 lanes per row (8 columns of d
+// each), 256 / LR rows per workgroup; the partial of (row, block j) is the
+// row's entry in bucket (b, c, j), found through the bucket mask word and its
+// position.  Entries naming no causal block, and repeats, are skipped (no
+// partial).
+template <int HD>
 __global__ void __launch_bounds__(256) k_sparse_dq_merge(const int32_t* __restrict__ sel,
                                                          const uint32_t* __restrict__ mask,
                                                          const int32_t* __restrict__ wpos,
                                                          const uint16_t* __restrict__ part, void* dq, int64_t rows,
                                                          int Hq, int G, int N, int block, int nb, int K, int Kc) {
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
-  const int li = threadIdx.x & 15;
+  constexpr int kD = HD, LR = HD / 8;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (256 / LR) + (threadIdx.x / LR);
+  const int li = threadIdx.x % LR;
   const bool live = row < rows;
   const int64_t rr = live ? row : 0;
   const int64_t bh = rr / N;
@@ -404,8 +416,8 @@ __global__ void __launch_bounds__(256) k_sparse_dq_merge(const int32_t* __restri
   const int own = t / block;
   const int32_t* s = sel + rr * K;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int e0 = 0; e0 < Kc; e0 += 16) {
-    // lane li looks up slot e0 + li; the 16 lanes then take the slots in order
+  for (int e0 = 0; e0 < Kc; e0 += LR) {
+    // lane li looks up slot e0 + li; the LR lanes then take the slots in order
     const int e = e0 + li;
     int j = (live && e < Kc) ? s[e] : -1;
     if (j > own || (e > 0 && j >= 0 && s[e - 1] == j)) j = -1;
@@ -414,12 +426,12 @@ __global__ void __launch_bounds__(256) k_sparse_dq_merge(const int32_t* __restri
       const int64_t w = ((bc * nb + j) * G + hl) * nqt + qt;
       p = wpos[w] + __popc(mask[w] & below);
     }
-    const int nslot = min(16, Kc - e0);
+    const int nslot = min(LR, Kc - e0);
     for (int i = 0; i < nslot; ++i) {
-      const int ji = __shfl(j, i, 16);
+      const int ji = __shfl(j, i, LR);
       if (ji < 0) continue;
-      const uint32_t plo = __shfl(static_cast<uint32_t>(p), i, 16);
-      const uint32_t phi = __shfl(static_cast<uint32_t>(p >> 32), i, 16);
+      const uint32_t plo = __shfl(static_cast<uint32_t>(p), i, LR);
+      const uint32_t phi = __shfl(static_cast<uint32_t>(p >> 32), i, LR);
       const int64_t pi = (static_cast<int64_t>(phi) << 32) | plo;
       const uint4 u = *reinterpret_cast<const uint4*>(part + pi * kD + 8 * li);
       const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
@@ -444,13 +456,19 @@ __global__ void __launch_bounds__(256) k_sparse_dq_merge(const int32_t* __restri
 void launch_sparse_dq_merge(const Dims& D, const int32_t* sel, const uint32_t* mask, const int32_t* wpos,
                             const uint16_t* part, void* dq, hipStream_t s) {
   const int Kc = D.K < D.nb ? D.K : D.nb;
+  const int rows_wg = 256 / (D.d / 8);
+  const dim3 grid(static_cast<unsigned>((D.rows() + rows_wg - 1) / rows_wg));
   timing_begin(kKDqMerge, s);
-  hipLaunchKernelGGL(k_sparse_dq_merge, dim3(static_cast<unsigned>((D.rows() + 15) / 16)), dim3(256), 0, s, sel, mask,
-                     wpos, part, dq, D.rows(), D.Hq, D.G, D.N, D.block, D.nb, D.K, Kc);
+  if (D.d == 64)
+    hipLaunchKernelGGL(k_sparse_dq_merge<64>, grid, dim3(256), 0, s, sel, mask, wpos, part, dq, D.rows(), D.Hq, D.G,
+                       D.N, D.block, D.nb, D.K, Kc);
+  else
+    hipLaunchKernelGGL(k_sparse_dq_merge<128>, grid, dim3(256), 0, s, sel, mask, wpos, part, dq, D.rows(), D.Hq, D.G,
+                       D.N, D.block, D.nb, D.K, Kc);
   timing_end(kKDqMerge, s);
 }
 
-bool sparse_bwd_supported(const Dims& D) { return D.dtype == 1 && D.d == kD; }
+bool sparse_bwd_supported(const Dims& D) { return D.dtype == 1 && (D.d == 128 || D.d == 64); }
 
 void launch_bwd_sparse(const Dims& D, const SparseBwdArgs& a, hipStream_t s) {
   dim3 grid(D.B * D.Hkv, D.nb);
@@ -460,9 +478,14 @@ void launch_bwd_sparse(const Dims& D, const SparseBwdArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.scale, scale_log2);
   };
   const bool rows_out = a.ds_rows != nullptr;
-  if (D.block == 32) rows_out ? go(k_bwd_sparse<1, true>) : go(k_bwd_sparse<1, false>);
-  else if (D.block == 64) rows_out ? go(k_bwd_sparse<2, true>) : go(k_bwd_sparse<2, false>);
-  else rows_out ? go(k_bwd_sparse<4, true>) : go(k_bwd_sparse<4, false>);
+  auto by_block = [&](auto hd_tag) {
+    constexpr int HD = decltype(hd_tag)::value;
+    if (D.block == 32) rows_out ? go(k_bwd_sparse<1, true, HD>) : go(k_bwd_sparse<1, false, HD>);
+    else if (D.block == 64) rows_out ? go(k_bwd_sparse<2, true, HD>) : go(k_bwd_sparse<2, false, HD>);
+    else rows_out ? go(k_bwd_sparse<4, true, HD>) : go(k_bwd_sparse<4, false, HD>);
+  };
+  if (D.d == 64) by_block(std::integral_constant<int, 64>{});
+  else by_block(std::integral_constant<int, 128>{});
   timing_end(kKBwdSparse, s);
 }
 

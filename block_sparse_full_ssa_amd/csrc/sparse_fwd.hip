@@ -25,6 +25,8 @@
 // S^T accumulator.  Nothing is copied HBM -> LDS asynchronously inside the
 // loop, so the partial stores of one batch stay in flight during the next.
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 #include "mfma.h"
@@ -32,24 +34,27 @@
 namespace ssa {
 namespace {
 
-constexpr int kD = 128;
 constexpr float kLn2 = 0.69314718055994531f;
 
-// Physical 16-byte chunk of logical chunk c in a 256-byte V row r (read by
-// transposes).
-// The transposed tiles use c ^ (2 (r % 8) + (r / 8) % 2): measured on gfx950
-// it keeps the transpose reads (ds_read_b64_tr_b16) free of bank conflicts
-// as well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave
-// the transpose reads two-way conflicted.
-__device__ __forceinline__ int swz_v(int r, int c) { return c ^ (((r & 7) << 1) | ((r >> 3) & 1)); }
+// Physical 16-byte chunk of logical chunk c in a V row r (read by
+// transposes), for head dimension HD (rows of 2 HD bytes).
+// 256-byte rows: c ^ (2 (r % 8) + (r / 8) % 2), measured on gfx950 to keep
+// the transpose reads (ds_read_b64_tr_b16) free of bank conflicts as well as
+// the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave the
+// transpose reads two-way conflicted; 128-byte rows: c ^ (r % 8).
+template <int HD> __device__ __forceinline__ int swz_v(int r, int c) {
+  return HD == 128 ? c ^ (((r & 7) << 1) | ((r >> 3) & 1)) : c ^ (r & 7);
+}
 
-// Physical 16-byte chunk of logical chunk c in a 256-byte K row r.
-__device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & 15); }
+// Physical 16-byte chunk of logical chunk c in a K row r.
+template <int HD> __device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & (HD / 8 - 1)); }
 
-template <int KH>   // the key block as KH halves of 32 keys
+template <int KH, int HD>   // the key block as KH halves of 32 keys; head dimension HD
 __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFwdArgs a, int Hq, int G, int N, int Nq,
                                                         int q_off, int nb, float scale_log2) {
   constexpr int kBlk = 32 * KH;
+  constexpr int kD = HD;
+  constexpr int kCh = HD / 8;      // 16-byte chunks per row
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBlk * kD], Vs[kBlk * kD];
   // per-wave staging of a batch's partial outputs, so that they leave as
   // whole rows (4 consecutive partials of 256 bytes per store instruction)
@@ -74,11 +79,11 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
   const int64_t qhead0 = static_cast<int64_t>(b) * Hq + c * G;   // first query head of the group
 
   // K and V blocks -> LDS, 16-byte chunks swizzled per row
-  for (int e = tid; e < kBlk * kD / 8; e += 256) {
-    const int r = e >> 4, cc = e & 15;
-    *reinterpret_cast<uint4*>(&Ks[r * kD + 8 * swz_k(r, cc)]) =
+  for (int e = tid; e < kBlk * kCh; e += 256) {
+    const int r = e / kCh, cc = e % kCh;
+    *reinterpret_cast<uint4*>(&Ks[r * kD + 8 * swz_k<HD>(r, cc)]) =
         *reinterpret_cast<const uint4*>(kg + static_cast<int64_t>(r) * kD + 8 * cc);
-    *reinterpret_cast<uint4*>(&Vs[r * kD + 8 * swz_v(r, cc)]) =
+    *reinterpret_cast<uint4*>(&Vs[r * kD + 8 * swz_v<HD>(r, cc)]) =
         *reinterpret_cast<const uint4*>(vg + static_cast<int64_t>(r) * kD + 8 * cc);
   }
   __syncthreads();
@@ -119,7 +124,7 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
 #pragma unroll
       for (int kh = 0; kh < KH; ++kh) {
         const int r = kh * 32 + col;
-        s[kh] = mfma32x32x16(lds_read8(&Ks[r * kD + 8 * swz_k(r, 2 * ds + g)]), qb[ds], s[kh]);
+        s[kh] = mfma32x32x16(lds_read8(&Ks[r * kD + 8 * swz_k<HD>(r, 2 * ds + g)]), qb[ds], s[kh]);
       }
     __builtin_amdgcn_sched_barrier(0);    // keep the phases' operand reads apart (register pressure)
     // own block: keys <= t
@@ -138,9 +143,10 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m = valid ? mx : 0.f;      // a valid row always has key j * block <= t
     float sum = 0.f;
-    f32x16 o[4];
+    constexpr int kDT = HD / 32;     // 32-column output tiles
+    f32x16 o[kDT];
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+    for (int dt = 0; dt < kDT; ++dt) o[dt] = f32x16{};
 #pragma unroll
     for (int kh = 0; kh < KH; ++kh) {
 #pragma unroll
@@ -155,10 +161,10 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
                                         sum);
         const int r0 = kh * 32 + st * 16 + 4 * gk + srow, r1 = r0 + 8;
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
+        for (int dt = 0; dt < kDT; ++dt) {
           const int cc = 4 * dt + 2 * (grp & 1) + (m4 >> 1), ee = 4 * (m4 & 1);
           const bf16x8 va =
-              lds_tr_pair(&Vs[r0 * kD + 8 * swz_v(r0, cc) + ee], &Vs[r1 * kD + 8 * swz_v(r1, cc) + ee]);
+              lds_tr_pair(&Vs[r0 * kD + 8 * swz_v<HD>(r0, cc) + ee], &Vs[r1 * kD + 8 * swz_v<HD>(r1, cc) + ee]);
           o[dt] = mfma32x32x16(va, pb, o[dt]);
         }
       }
@@ -169,26 +175,27 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
     if (bt + 4 < nbat) load_q(e_next, qb);
     // partials of entries p0 + 32 bt + r (the bucket's rows are contiguous):
     // O^T / sum -> LDS row col (16-byte chunk 4 dt + i4 of d at physical
-    // chunk (4 dt + i4) ^ (col & 15)), then 16 lanes store each row
+    // chunk (4 dt + i4) ^ (col % kCh)), then kCh lanes store each row
     {
       const float inv = valid ? 1.f / sum : 0.f;
       uint16_t* ot = Ot + wave * 32 * kD;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
         for (int i4 = 0; i4 < 4; ++i4) {
           const f32x16& od = o[dt];
-          *reinterpret_cast<uint2*>(&ot[col * kD + 8 * ((4 * dt + i4) ^ (col & 15)) + 4 * g]) =
+          *reinterpret_cast<uint2*>(&ot[col * kD + 8 * ((4 * dt + i4) ^ (col & (kCh - 1))) + 4 * g]) =
               make_uint2(pack_bf16x2(od[4 * i4] * inv, od[4 * i4 + 1] * inv),
                          pack_bf16x2(od[4 * i4 + 2] * inv, od[4 * i4 + 3] * inv));
         }
       const int64_t pr0 = static_cast<int64_t>(p0) + bt * 32;
       const int rows_here = min(32, n - bt * 32);
+      constexpr int kRowsSt = 64 / kCh;            // rows per store instruction
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int r = 4 * i + (lane >> 4), pc = lane & 15;
+      for (int i = 0; i < 32 / kRowsSt; ++i) {
+        const int r = kRowsSt * i + lane / kCh, pc = lane % kCh;
         const uint4 u = *reinterpret_cast<const uint4*>(&ot[r * kD + 8 * pc]);
-        if (r < rows_here) *reinterpret_cast<uint4*>(a.part_o + (pr0 + r) * kD + 8 * (pc ^ (r & 15))) = u;
+        if (r < rows_here) *reinterpret_cast<uint4*>(a.part_o + (pr0 + r) * kD + 8 * (pc ^ (r & (kCh - 1)))) = u;
       }
       if (valid && g == 0) a.part_lse[pr0 + col] = m + fast_log2(sum);
     }
@@ -197,15 +204,18 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
   }
 }
 
-// 16 lanes per row (8 dims each), 16 rows per workgroup.  The partial of
-// (row, selected block j) is the row's entry in bucket (b, c, j).  Up to 64
-// selected blocks, lane i of a row looks up slots i, i + 16, ... in parallel
-// and the positions and weights are then broadcast within the 16 lanes;
-// wider rows (every block of a long sequence) take the serial loop.
+// LR = HD / 8 lanes per row (8 dims each), 256 / LR rows per workgroup.  The
+// partial of (row, selected block j) is the row's entry in bucket (b, c, j).
+// Up to 64 selected blocks, lane i of a row looks up slots i, i + LR, ... in
+// parallel and the positions and weights are then broadcast within the LR
+// lanes; wider rows (every block of a long sequence) take the serial loop.
+template <int HD>
 __global__ void __launch_bounds__(256) k_sparse_merge(SparseFwdArgs a, int64_t rows, int Hq, int G, int Nq,
                                                       int q_off, int block, int nb, int K, int Kc) {
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
-  const int li = threadIdx.x & 15;
+  constexpr int kD = HD;
+  constexpr int LR = HD / 8;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * (256 / LR) + (threadIdx.x / LR);
+  const int li = threadIdx.x % LR;
   const bool live = row < rows;
   const int64_t rr = live ? row : 0;
   const int64_t bh = rr / Nq;
@@ -240,33 +250,34 @@ __global__ void __launch_bounds__(256) k_sparse_merge(SparseFwdArgs a, int64_t r
   };
   float m = -INFINITY, L = 0.f;
   if (Kc <= 64) {
-    int64_t p[4];
-    float x[4];
+    constexpr int kSlots = 64 / LR;     // lookups per lane
+    int64_t p[kSlots];
+    float x[kSlots];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int e = 16 * r + li;
+    for (int r = 0; r < kSlots; ++r) {
+      const int e = LR * r + li;
       const int j = (live && e < Kc) ? entry(e) : -1;
       p[r] = j >= 0 ? pos_of(j) : 0;
       x[r] = j >= 0 ? a.part_lse[p[r]] : -INFINITY;
       m = fmaxf(m, x[r]);
     }
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 16));
+    for (int off = LR / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, LR));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
+    for (int r = 0; r < kSlots; ++r) {
       const float wt = x[r] == -INFINITY ? 0.f : fast_exp2(x[r] - m);
       L += wt;
-      if (16 * r >= Kc) continue;      // uniform
+      if (LR * r >= Kc) continue;      // uniform
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float wi = __shfl(wt, i, 16);
-        const uint32_t plo = __shfl(static_cast<uint32_t>(p[r]), i, 16);
-        const uint32_t phi = __shfl(static_cast<uint32_t>(p[r] >> 32), i, 16);
+      for (int i = 0; i < LR; ++i) {
+        const float wi = __shfl(wt, i, LR);
+        const uint32_t plo = __shfl(static_cast<uint32_t>(p[r]), i, LR);
+        const uint32_t phi = __shfl(static_cast<uint32_t>(p[r] >> 32), i, LR);
         if (wi != 0.f) add((static_cast<int64_t>(phi) << 32) | plo, wi);
       }
     }
 #pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) L += __shfl_xor(L, off, 16);
+    for (int off = LR / 2; off >= 1; off >>= 1) L += __shfl_xor(L, off, LR);
   } else if (live) {
     for (int e = 0; e < Kc; ++e) {
       const int j = entry(e);
@@ -294,24 +305,33 @@ __global__ void __launch_bounds__(256) k_sparse_merge(SparseFwdArgs a, int64_t r
 
 }  // namespace
 
-bool sparse_fwd_supported(const Dims& D) { return D.dtype == 1 && D.d == kD; }
+bool sparse_fwd_supported(const Dims& D) { return D.dtype == 1 && (D.d == 128 || D.d == 64); }
 
 void launch_sparse_fwd(const Dims& D, const SparseFwdArgs& a, hipStream_t s) {
   const int Kc = D.K < D.nb ? D.K : D.nb;
   const float scale_log2 = D.scale * 1.4426950408889634f;
   dim3 grid(D.B * D.Hkv, D.nb);
-  timing_begin(kKSparsePart, s);
-  if (D.block == 32)
-    hipLaunchKernelGGL(k_sparse_part<1>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.nb, scale_log2);
-  else if (D.block == 64)
-    hipLaunchKernelGGL(k_sparse_part<2>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.nb, scale_log2);
-  else
-    hipLaunchKernelGGL(k_sparse_part<4>, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.nb, scale_log2);
-  timing_end(kKSparsePart, s);
-  timing_begin(kKSparseMerge, s);
-  hipLaunchKernelGGL(k_sparse_merge, dim3(static_cast<unsigned>((D.rows() + 15) / 16)), dim3(256), 0, s, a,
-                     D.rows(), D.Hq, D.G, D.Nq, D.q_off, D.block, D.nb, D.K, Kc);
-  timing_end(kKSparseMerge, s);
+  auto go = [&](auto hd_tag) {
+    constexpr int HD = decltype(hd_tag)::value;
+    timing_begin(kKSparsePart, s);
+    if (D.block == 32)
+      hipLaunchKernelGGL((k_sparse_part<1, HD>), grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.nb,
+                         scale_log2);
+    else if (D.block == 64)
+      hipLaunchKernelGGL((k_sparse_part<2, HD>), grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.nb,
+                         scale_log2);
+    else
+      hipLaunchKernelGGL((k_sparse_part<4, HD>), grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.nb,
+                         scale_log2);
+    timing_end(kKSparsePart, s);
+    constexpr int kRowsWg = 256 / (HD / 8);
+    timing_begin(kKSparseMerge, s);
+    hipLaunchKernelGGL(k_sparse_merge<HD>, dim3(static_cast<unsigned>((D.rows() + kRowsWg - 1) / kRowsWg)),
+                       dim3(256), 0, s, a, D.rows(), D.Hq, D.G, D.Nq, D.q_off, D.block, D.nb, D.K, Kc);
+    timing_end(kKSparseMerge, s);
+  };
+  if (D.d == 64) go(std::integral_constant<int, 64>{});
+  else go(std::integral_constant<int, 128>{});
 }
 
 }  // namespace ssa

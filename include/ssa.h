@@ -286,7 +286,7 @@ ssa_status_t ssa_cache_block_means(const ssa_shape_t* shape, const void* k_cache
  *   rule and the same kernels as ssa_select_blocks + ssa_attn_fwd (the
  *   sparse stream on key-block buckets, the full stream as the matrix
  *   forward), with the queries offset against the cache.
- *   Requires bf16 and head_dim 128 (else SSA_ERR_UNSUPPORTED), pos0 and
+ *   Requires bf16 (else SSA_ERR_UNSUPPORTED), pos0 and
  *   chunk multiples of block with pos0 + chunk <= seqlen (SSA_ERR_SHAPE),
  *   mode SSA_FULL_ONLY or SSA_SPARSE_ONLY (SSA_ERR_UNSUPPORTED).  Workspace:
  *   ssa_prefill_workspace_size(shape, mode, chunk) bytes (0 on an invalid

@@ -29,6 +29,7 @@ CASES = {
     "mha_b2_n512_b32_k6": si.scaled_down(W["gqa_n4k_fwd"], batch=2, seqlen=512, hq=2, hkv=2, block=32, top_k=6),
     "gqa_b2_n768_b128_k3": si.scaled_down(W["gqa_n4k_fwd"], batch=2, seqlen=768, hq=4, hkv=1, block=128, top_k=3),
     "fp32_b2_n256_d64": si.scaled_down(W["tiny_mha_n256_fp32"], batch=2),
+    "gqa_b2_n1024_d64_k4": si.scaled_down(W["gqa_n4k_fwd"], batch=2, seqlen=1024, hq=4, hkv=2, head_dim=64, top_k=4),
 }
 
 

@@ -182,7 +182,20 @@ def test_gqa_n4k_layer_backward_every_unit(mode):
     """B=1, 16 query / 4 KV heads, N=4096, d=128, block 64, top_k 16, unscreened:
     a training step, and every (batch, KV head) unit of the layer element by
     element (all rows' outputs and dq, every key's dk and dv)."""
-    wl = si.WORKLOADS["gqa_n4k_fwd"]
+    _gqa_n4k_every_unit(si.WORKLOADS["gqa_n4k_fwd"], mode)
+
+
+@pytest.mark.parametrize("mode", [oracle.DUAL_ACTIVE_FULL, oracle.DUAL_ACTIVE_SPARSE, oracle.FULL_ONLY,
+                                  oracle.SPARSE_ONLY])
+def test_gqa_n4k_d64_layer_backward_every_unit(mode):
+    """The same layer with 64-wide heads and 128-key blocks at top_k 8 (the
+    matrix kernels' d = 64 variants, four key halves per block in the bucket
+    kernels): every unit element by element."""
+    wl = si.scaled_down(si.WORKLOADS["gqa_n4k_fwd"], name="gqa_n4k_d64_b128", head_dim=64, block=128, top_k=8)
+    _gqa_n4k_every_unit(wl, mode)
+
+
+def _gqa_n4k_every_unit(wl, mode):
     K = wl.top_k
     _say(f"{wl.name} whole-layer backward mode {mode}")
     q, k, v, _ = si.draw_qkv(wl, 0)

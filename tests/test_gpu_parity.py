@@ -31,6 +31,12 @@ SMALL = {
     "gqa_n512_b128_k2": si.scaled_down(W["gqa_n4k_fwd"], seqlen=512, hq=4, hkv=1, block=128, top_k=2),
     "sinks_n1024_k8": si.scaled_down(W["long_n64k_sinks"], seqlen=1024, hq=4, hkv=1, top_k=8),
     "gqa_n256_d64": si.scaled_down(W["gqa_n4k_fwd"], seqlen=256, hq=2, hkv=1, head_dim=64, top_k=2),
+    # d = 64 on the matrix kernels: 32-key blocks with a ragged last query tile,
+    # and 128-key blocks (four key halves per block in the bucket kernels)
+    "gqa_n640_d64_b32_k5": si.scaled_down(W["gqa_n4k_fwd"], seqlen=640, hq=4, hkv=2, block=32, head_dim=64,
+                                          top_k=5),
+    "mha_n512_d64_b128_k2": si.scaled_down(W["gqa_n4k_fwd"], seqlen=512, hq=2, hkv=2, block=128, head_dim=64,
+                                           top_k=2),
 }
 MODES = [oracle.DUAL_ACTIVE_FULL, oracle.DUAL_ACTIVE_SPARSE, oracle.FULL_ONLY, oracle.SPARSE_ONLY]
 
