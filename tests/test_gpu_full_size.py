@@ -8,7 +8,8 @@ checks
 * whole (batch, KV head) units of the training layers: every row of the G
   query heads (selection, both streams, lse, delta, dq) and every key of the
   KV head (dk, dv), computed by the oracle on a process pool -- units are
-  independent, since dk and dv sum only over their own query heads;
+  independent, since dk and dv sum only over their own query heads -- and a
+  whole unit of the 64K layer's forward;
 * sampled query rows one by one: the selection (rows whose fp64 cutoff
   margin is below 1e-3 are exempt from the equality check, as screening would
   have redrawn them; their GPU selection must still be a valid near-optimal
@@ -315,6 +316,21 @@ def test_long_layer_64k_sinks_full_size():
         _check_selection(f"{wl.name} b{b} h{h}", qf[b, h, t_idx], t_idx, mu[b, h // wl.group], wl.block, K,
                          sel_np[b, h, t_idx])
         _check_rows_fwd(wl.name, wl, b, h, t_idx, qf, kf, vf, sel_np, out)
+
+    # one whole (batch, KV head) unit: every row of its G query heads
+    from oracle import parallel
+
+    c = 2
+    G = wl.group
+    hs = slice(c * G, (c + 1) * G)
+    for i in range(G):
+        _check_selection(f"{wl.name} unit c{c} head {i}", qf[0, c * G + i], np.arange(wl.seqlen), mu[0, c],
+                         wl.block, K, sel_np[0, c * G + i])
+    res = parallel.unit_step(qf[0, hs], kf[0, c], vf[0, c], wl.block, K, 1.0 / math.sqrt(wl.head_dim), mode,
+                             sel_u=sel_np[0, hs], backward=False)
+    _say(f"  unit b0 c{c}: {G} heads x {wl.seqlen} rows, oracle {res['seconds']:.1f} s on {res['workers']} processes")
+    for key in ("h_full", "h_sparse", "lse_full", "lse_sparse", "delta"):
+        assert_close(f"{wl.name} unit {key}", out[key][0, hs], res[key], wl.dtype)
 
 
 def test_long_layer_64k_sink_stats_full_size():
