@@ -101,8 +101,8 @@ def measured_traffic(kernel, workload, top_k):
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="train_b2_h32_n16k")
     ap.add_argument("--top-k", type=int, default=None)
     ap.add_argument("--seqlen", type=int, default=None, help="override N (experiments only)")
