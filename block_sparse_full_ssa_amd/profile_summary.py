@@ -38,7 +38,7 @@ CSRC = os.path.join(HERE, "csrc")
 COPY_BYTES = 1 << 30
 
 # matrix kernels whose traffic the benchmark's roofline reports: name prefix -> (id, source)
-KERNELS = [("k_bwd_mfma", "bwd_mfma", "bwd_mfma.hip"), ("k_fwd_mfma<0, false>", "fwd_mfma", "fwd_mfma.hip"),
+KERNELS = [("k_bwd_mfma", "bwd_mfma", "bwd_mfma.hip"), ("k_fwd_mfma<0, false,", "fwd_mfma", "fwd_mfma.hip"),
            ("k_bwd_dq", "bwd_dq", "bwd_dq.hip"), ("k_bwd_sparse", "bwd_sparse", "sparse_bwd.hip")]
 
 
