@@ -336,6 +336,35 @@ def multilayer(ssa, dev, seed, steps=10, warmup=3):
             "frac_of_bf16_peak": round(steps * fl / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
 
 
+def head64_layer(ssa, dev, seed, steps=10, warmup=3):
+    """The training layer with 64-wide heads (B=2, 32/8 heads, N=16384, d=64,
+    block 64, top_k 16: the head size of the pages' 1B model): ``steps`` timed
+    training steps (selection, dual forward, backward) after ``warmup``, the
+    active stream drawn per step."""
+    import torch
+
+    import ssa_inputs as si
+
+    wl = si.scaled_down(si.WORKLOADS["train_b2_h32_n16k"], name="train_b2_h32_n16k_d64", head_dim=64)
+    q, k, v, _ = si.draw_qkv(wl, seed, device=str(dev))
+    dout = si.draw_dout(wl, seed, device=str(dev))
+    modes = [ssa.DUAL_ACTIVE_FULL if m == 0 else ssa.DUAL_ACTIVE_SPARSE
+             for m in si.draw_modes(seed, warmup + steps)]
+    K, blk = wl.top_k, wl.block
+    train_steps(ssa, q, k, v, dout, blk, K, modes[:warmup])
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    train_steps(ssa, q, k, v, dout, blk, K, modes[warmup:])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    pf, ps = pairs(wl.seqlen, blk, K)
+    fl = 14.0 * wl.head_dim * (pf + ps) * wl.batch * wl.hq
+    return {"workload": wl.name, "steps": steps, "warmup": warmup, "ms_per_step": round(ms, 3),
+            "TFLOP/s": round(fl / (ms / 1e3) / 1e12, 2),
+            "frac_of_bf16_peak": round(fl / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+            "tokens_per_s": round(wl.batch * wl.seqlen / (ms / 1e3), 1)}
+
+
 def decode_128k(ssa, dev, reps):
     """One decode step per sequence at the end of a 131072-token cache (B=4,
     16 query / 4 KV heads, d 128, block 64, top_k 32, four planted sinks):
@@ -602,6 +631,7 @@ def main():
         others["long_n64k_sinks"] = long_layer(ssa, dev, args.seed, 3)
         torch.cuda.empty_cache()
         others["multilayer_b4_n8k_l4"] = multilayer(ssa, dev, args.seed)
+        others["train_b2_h32_n16k_d64"] = head64_layer(ssa, dev, args.seed)
         torch.cuda.empty_cache()
 
     decode = None if args.no_decode else decode_128k(ssa, dev, max(10, args.steps))
