@@ -19,9 +19,10 @@
 // processed in halves of 32 so that the logits need 16 registers and both
 // output accumulators stay in VGPRs.
 //
-// K/V tiles of 64 keys (32 for the full stream alone) move from HBM straight
+// The head dimension HD (64 or 128) is a template parameter.  K/V tiles of
+// 64 keys (32 for the full stream alone at HD = 128) move from HBM straight
 // into LDS (global_load_lds, 16 bytes per lane), double-buffered, one barrier
-// per tile.  16-byte chunks are XOR-swizzled within each 256-byte row so that
+// per tile.  16-byte chunks are XOR-swizzled within each row so that
 // the matrix-operand reads of K rows and the transpose reads of V columns
 // avoid bank conflicts.
 //
@@ -67,7 +68,7 @@ typedef __attribute__((address_space(1))) void glb_void;
 
 // Physical 16-byte chunk of logical chunk c in row r: K tiles are only read
 // by rows; V tiles by transpose reads.
-// 256-byte rows (D = 128): the transposed tiles use c ^ (2 (r % 8) + (r / 8) % 2):
+// 256-byte rows (D = 128): the transposed tiles use c ^ (2 (r % 8) + (r / 8) % 2);
 // measured on gfx950 it keeps the transpose reads (ds_read_b64_tr_b16) free
 // of bank conflicts as well as the 16-byte row reads, where c ^ (r % 8) or
 // c ^ (r % 16) leave the transpose reads two-way conflicted.  128-byte rows
@@ -93,7 +94,7 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
     k_fwd_mfma(FwdArgs a, int Hq, int G, int N, int Nq, int q_off, int block, int nb, int K, float scale_log2,
                int n_qtiles) {
   constexpr bool kSparse = MODE == kModeDual;
-  // K and V tiles [64][128] (swizzled), two of each; separate objects so that
+  // K and V tiles [kBN][HD] (swizzled), two of each; separate objects so that
   // the compiler can tell the tile being read from the one being filled
   constexpr int kBN = FwdTile<MODE, HD>::kBN;
   constexpr int kTile = FwdTile<MODE, HD>::kTile;

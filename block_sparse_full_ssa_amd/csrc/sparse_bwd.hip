@@ -25,8 +25,9 @@
 //
 // Waves: wave w owns key half kh = w % KH (32 keys, B operands in registers)
 // of query stream qs = w / KH; the 4 / KH streams take consecutive batches.
-// Each stream's gathered Q and G_s rows move HBM -> LDS (one row per 16
-// lanes, double-buffered); dS^T of the block passes through LDS, where each
+// Each stream's gathered Q and G_s rows move HBM -> LDS (one row per HD / 8
+// lanes, double-buffered; HD, the head dimension 64 or 128, is a template
+// parameter); dS^T of the block passes through LDS, where each
 // wave reads back its own keys' rows for the dS rows, or, sparse-only, each
 // wave of a stream reduces dQ over all the block's keys for its slice of d.
 // The layout of every product is the full-stream kernel's (S = Q K^T, lane l
