@@ -23,6 +23,7 @@ pytestmark = pytest.mark.gpu
 W = si.WORKLOADS
 TINY = W["tiny_mha_n256_fp32"]
 SMALL_BF16 = si.scaled_down(W["gqa_n4k_fwd"], seqlen=512, hq=4, hkv=2, top_k=4)
+SMALL_BF16_D64 = si.scaled_down(W["gqa_n4k_fwd"], seqlen=384, hq=4, hkv=2, head_dim=64, block=32, top_k=3)
 ACTIVE = {oracle.DUAL_ACTIVE_FULL: "h_full", oracle.DUAL_ACTIVE_SPARSE: "h_sparse",
           oracle.FULL_ONLY: "h_full", oracle.SPARSE_ONLY: "h_sparse"}
 
@@ -61,9 +62,9 @@ def _run(wl, mode, ws, wc, with_dout=True):
 
 @pytest.mark.parametrize("mode", [oracle.DUAL_ACTIVE_FULL, oracle.DUAL_ACTIVE_SPARSE, oracle.FULL_ONLY,
                                   oracle.SPARSE_ONLY])
-@pytest.mark.parametrize("name", ["tiny", "bf16"])
+@pytest.mark.parametrize("name", ["tiny", "bf16", "bf16_d64"])
 def test_autograd_matches_oracle(name, mode):
-    wl = TINY if name == "tiny" else SMALL_BF16
+    wl = {"tiny": TINY, "bf16": SMALL_BF16, "bf16_d64": SMALL_BF16_D64}[name]
     print(f"autograd {name} mode {mode}", flush=True)
     sys.stdout.flush()
     out, ref, got, want = _run(wl, mode, 0.7, 1.3)

@@ -92,7 +92,9 @@ def test_noalloc_two_calls_second_smaller():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     cases = [("gqa_n4k dual-sparse", W["gqa_n4k_fwd"], DUAL_SPARSE),
-             ("gqa n1024 dual-full", si.scaled_down(W["gqa_n4k_fwd"], seqlen=1024, hq=4, hkv=2, top_k=4), DUAL_FULL)]
+             ("gqa n1024 dual-full", si.scaled_down(W["gqa_n4k_fwd"], seqlen=1024, hq=4, hkv=2, top_k=4), DUAL_FULL),
+             ("gqa n512 d64 dual-sparse",
+              si.scaled_down(W["gqa_n4k_fwd"], seqlen=512, hq=4, hkv=2, head_dim=64, top_k=4), DUAL_SPARSE)]
     for name, wl, mode in cases:
         print(f"noalloc {name}", flush=True)
         sys.stdout.flush()
