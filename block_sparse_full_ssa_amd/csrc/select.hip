@@ -10,8 +10,9 @@
 // Kernels:
 //   block_mean:  mean of each key block, fp32, [B*Hkv][nb][d];
 //   split_means: (bf16 layers) each mean as the sum of two bf16 numbers;
-//   select:      one workgroup per (head, 32 rows of one query block);
-//                candidate scores are computed into LDS by matrix
+//   select:      one workgroup per (head, 32 rows of one query block), the
+//                row tiles of a KV head's query heads on one XCD, the
+//                longest rows first; candidate scores are computed into LDS by matrix
 //                instructions, up to 256 candidates at a time, and a wave
 //                ranks each row by a bitwise threshold search (see below),
 //                carrying a row's winners from one chunk of candidates into
@@ -288,10 +289,14 @@ __global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, co
   uint32_t* car_code = reinterpret_cast<uint32_t*>(smem + R * CH);       // [R][kCarry]
   int32_t* car_idx = reinterpret_cast<int32_t*>(car_code + R * kCarry);  // [R][kCarry]
   uint32_t* car_th = reinterpret_cast<uint32_t*>(car_idx + R * kCarry);  // [R]
-  const int bh = blockIdx.y;
+  // work item: the row tiles of the G query heads of a KV head on one XCD
+  // (its block means then stay in that XCD's L2), longest rows first
+  const int n_rt = Nq / R;
+  const QTileItem item = qtile_item(blockIdx.x, static_cast<int>(gridDim.x) / (n_rt * G), G, n_rt);
+  const int bh = item.bh;
   const int b = bh / Hq, h = bh % Hq;
   const int64_t bc = static_cast<int64_t>(b) * (Hq / G) + h / G;
-  const int t0 = blockIdx.x * R;    // R divides block (and q_off), so all rows share i
+  const int t0 = (n_rt - 1 - item.rank) * R;    // R divides block (and q_off), so all rows share i
   const int i = (q_off + t0) / block;   // own block = number of candidates
   const int keep = min(K - 1, i);
   const int tid = threadIdx.x;
@@ -387,7 +392,7 @@ template <typename T, int TM, int DD, bool CARRY>
 static void launch_select_mfma(const Dims& D, int R, const void* q, const float* mu, const uint16_t* mu_hi,
                                const uint16_t* mu_lo, int32_t* sel, hipStream_t s) {
   const int CH = D.nb < kCand ? D.nb : kCand;
-  dim3 grid(D.Nq / R, D.B * D.Hq);
+  dim3 grid((D.Nq / R) * D.B * D.Hq);
   // the carried winners need LDS only when the candidates span several chunks
   // (at most 32 KiB of scores + 16 KiB of winners and their thresholds)
   const size_t lds = (static_cast<size_t>(R) * CH + (D.nb > CH ? (2 * static_cast<size_t>(kCarry) + 1) * R : 0)) *
