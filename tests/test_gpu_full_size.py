@@ -175,6 +175,29 @@ def test_train_layer_16k_full_size(K, mode, unit):
     assert np.all(np.abs(sum_dk) <= 2 ** -7 * abs_dk + 1e-6), np.abs(sum_dk).max()
 
 
+def test_train_layer_16k_d64_full_size():
+    """The benchmark's training layer with 64-wide heads (B=2, 32 query / 8 KV
+    heads, N=16384, d=64, block 64, top_k 16): one training step, one whole
+    (batch, KV head) unit element by element and the whole layer's
+    properties."""
+    wl = si.scaled_down(si.WORKLOADS["train_b2_h32_n16k"], name="train_b2_h32_n16k_d64", head_dim=64)
+    K, mode = wl.top_k, oracle.DUAL_ACTIVE_FULL
+    _say(f"full-size {wl.name} top_k {K} mode {mode}: draw")
+    q, k, v, _ = si.draw_qkv(wl, 0)
+    dout = si.draw_dout(wl, 0)
+    qd, kd, vd, gd = (x.to("cuda:0") for x in (q, k, v, dout))
+    sel = ssa().ssa_select_blocks(qd, kd, wl.block, K)
+    fwd = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, K, mode)
+    dq, dk, dv = ssa().ssa_attn_bwd(qd, kd, vd, sel, fwd, gd, wl.block, K, mode, 1.0, 1.0)
+    torch.cuda.synchronize()
+    out = {key: val.cpu() for key, val in fwd.items() if not key.startswith("_")}
+    sel_np = sel.cpu().numpy()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    del qd, kd, vd, gd, fwd, sel
+    _whole_layer_properties(wl.name, out, wl.dtype)
+    _unit_check(wl.name, wl, K, mode, 0, 3, q, k, v, dout, sel_np, out, (dq, dk, dv))
+
+
 # ---------------------------------------------- 4K GQA layer, every unit --
 
 @pytest.mark.parametrize("mode", [oracle.DUAL_ACTIVE_FULL, oracle.DUAL_ACTIVE_SPARSE, oracle.FULL_ONLY,
