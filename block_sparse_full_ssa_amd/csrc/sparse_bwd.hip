@@ -23,15 +23,19 @@
 //     order: deterministic, and no atomics (fp32 atomics on this chip run at
 //     a small fraction of the store bandwidth).
 //
-// Waves: wave w owns key half kh = w % KH (32 keys, B operands in registers)
-// of query stream qs = w / KH; the 4 / KH streams take consecutive batches.
-// Each stream's gathered Q and G_s rows move HBM -> LDS (one row per HD / 8
-// lanes, double-buffered; HD, the head dimension 64 or 128, is a template
-// parameter); dS^T of the block passes through LDS, where each
-// wave reads back its own keys' rows for the dS rows, or, sparse-only, each
-// wave of a stream reduces dQ over all the block's keys for its slice of d.
-// The layout of every product is the full-stream kernel's (S = Q K^T, lane l
-// owns key l % 32).
+// Waves: 2 KH per workgroup, wave w owns key half kh = w % KH (32 keys) in
+// role w / KH.  Role 0 computes S = Q K^T (K rows of its keys as B operands
+// in registers), P, and accumulates dV; role 1 computes dP = G_s V^T (V rows
+// in registers), takes P from role 0 through LDS after a barrier, forms dS
+// and accumulates dK.  Each wave so holds one accumulator and one operand
+// set, which keeps it within half the register file: two workgroups (two
+// waves per SIMD) share a CU.  The batch's gathered Q and G_s rows move HBM ->
+// LDS (one row per HD / 8 lanes, double-buffered; HD, the head dimension 64
+// or 128, is a template parameter); dS^T of the block passes through LDS,
+// where each role-1 wave reads back its own keys' rows for the dS rows, or,
+// sparse-only, every wave reduces dQ over all the block's keys for its slice
+// of d.  The layout of every product is the full-stream kernel's (S = Q K^T,
+// lane l owns key l % 32).
 
 #include <type_traits>
 
@@ -56,32 +60,36 @@ __device__ __forceinline__ int swz_s(int r, int c) { return c ^ ((r >> 1) & 3); 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(1))) void glb_void;
 
+// Barrier for LDS data only: memory operations in flight (the next batch's
+// rows) are not waited for, as a plain __syncthreads would.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 template <int KH, bool DSOUT, int HD>   // HD: head dimension
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(128 * KH, 2)
     k_bwd_sparse(SparseBwdArgs a, int Hq, int G, int N, int nb, float scale, float scale_log2) {
   constexpr int kD = HD;
   constexpr int kDT = HD / 32;               // 32-column tiles of dK / dV
   constexpr int kCh = HD / 8;                // 16-byte chunks per row
   constexpr int kBlk = 32 * KH;
-  constexpr int QS = 4 / KH;                 // query streams
+  constexpr int kW = 2 * KH;                 // waves: (key half, role)
   constexpr int kT = 32 * kD;                // one Q / G tile
   constexpr int kDS = kBlk * 32;             // one dS^T tile
-  // dQ columns per wave (sparse-only): a stream's waves split d, at least 32
-  // columns each (HD = 64 with 128-key blocks: waves kh >= 2 have none)
-  constexpr int kSlice = kD / KH >= 32 ? kD / KH : 32;
-  // LDS: the key block (for the dQ operand), then per stream two sets of
-  // {Q, G_s tiles, dS^T tile, row values}; separate objects per set so that
-  // the compiler can tell the set being read from the one being filled
+  // dQ columns per wave (sparse-only): the waves split d, at least 32
+  // columns each (waves past the end of d have none)
+  constexpr int kSlice = kD / kW >= 32 ? kD / kW : 32;
+  // LDS: the key block (for the dQ operand), two sets of {Q, G_s tiles, row
+  // values} (one being read while the next batch's is filled), the dS^T tile
+  // and each key half's P
   __shared__ __attribute__((aligned(16))) uint16_t Kst[kBlk * kD];
-  __shared__ __attribute__((aligned(16))) uint16_t Q0[QS * kT], Q1[QS * kT], F0[QS * kT], F1[QS * kT];
-  __shared__ __attribute__((aligned(16))) uint16_t D0[QS * kDS], D1[QS * kDS];
-  // row values per stream: lse2 [32], D [32], t [32] (int, -1: no row), 32 unused
-  __shared__ __attribute__((aligned(16))) float R0[QS * 128], R1[QS * 128];
-
+  __shared__ __attribute__((aligned(16))) uint16_t Q0[kT], Q1[kT], F0[kT], F1[kT];
+  __shared__ __attribute__((aligned(16))) uint16_t DS[kDS];
+  __shared__ __attribute__((aligned(16))) float PX[KH * 1024];
+  // row values: lse2 [32], D [32], t [32] (int, -1: no row), 32 unused
+  __shared__ __attribute__((aligned(16))) float R0[128], R1[128];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kh = wave % KH, qs = wave / KH;
+  const int kh = wave % KH, role = wave / KH;   // role 0: S, P, dV; role 1: dP, dS, dK
   const int g = lane >> 5, col = lane & 31;
   const int grp = lane >> 4, li = lane & 15;
   const int gk = grp >> 1, sub16 = (grp & 1) * 16, srow = li >> 2, m4 = li & 3;
@@ -100,8 +108,10 @@ __global__ void __launch_bounds__(256, 1)
   const uint16_t* vg = static_cast<const uint16_t*>(a.v) + kvbase;
   const int64_t qhead0 = static_cast<int64_t>(b) * Hq + c * G;
 
-  // result rows of the lane's key: d = 32 dt + 8 a4 + 4 g + e
-  auto write_kv = [&](const f32x16* dk, const f32x16* dv) {
+  // the wave's result rows of the lane's key (dV for role 0, dK for role 1):
+  // d = 32 dt + 8 a4 + 4 g + e
+  auto write_out = [&](const f32x16* acc) {
+    const float f = role ? scale : 1.f;
 #pragma unroll
     for (int dt = 0; dt < kDT; ++dt)
 #pragma unroll
@@ -110,166 +120,229 @@ __global__ void __launch_bounds__(256, 1)
         const int i = 4 * a4;
         const int64_t o = kvbase + static_cast<int64_t>(key) * kD + d0;
         if (a.dk_part) {
-          *reinterpret_cast<float4*>(a.dk_part + o) =
-              make_float4(scale * dk[dt][i], scale * dk[dt][i + 1], scale * dk[dt][i + 2], scale * dk[dt][i + 3]);
-          *reinterpret_cast<float4*>(a.dv_part + o) = make_float4(dv[dt][i], dv[dt][i + 1], dv[dt][i + 2], dv[dt][i + 3]);
+          *reinterpret_cast<float4*>((role ? a.dk_part : a.dv_part) + o) =
+              make_float4(f * acc[dt][i], f * acc[dt][i + 1], f * acc[dt][i + 2], f * acc[dt][i + 3]);
         } else {
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.dk) + o) =
-              make_uint2(pack_bf16x2(scale * dk[dt][i], scale * dk[dt][i + 1]),
-                         pack_bf16x2(scale * dk[dt][i + 2], scale * dk[dt][i + 3]));
-          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(a.dv) + o) =
-              make_uint2(pack_bf16x2(dv[dt][i], dv[dt][i + 1]), pack_bf16x2(dv[dt][i + 2], dv[dt][i + 3]));
+          *reinterpret_cast<uint2*>(static_cast<uint16_t*>(role ? a.dk : a.dv) + o) =
+              make_uint2(pack_bf16x2(f * acc[dt][i], f * acc[dt][i + 1]),
+                         pack_bf16x2(f * acc[dt][i + 2], f * acc[dt][i + 3]));
         }
       }
   };
 
-  f32x16 dv[kDT], dk[kDT];
+  f32x16 acc[kDT];
 #pragma unroll
-  for (int dt = 0; dt < kDT; ++dt) {
-    dv[dt] = f32x16{};
-    dk[dt] = f32x16{};
-  }
+  for (int dt = 0; dt < kDT; ++dt) acc[dt] = f32x16{};
   if (n == 0) {                                // nobody selected this block
-    if (qs == 0) write_kv(dk, dv);
+    write_out(acc);
     return;
   }
 
   // ---- the key block in LDS (plain layout) for the dQ operand
-  for (int e = tid; e < kBlk * kCh; e += 256) {
-    const int row = e / kCh, c8 = e % kCh;
-    *reinterpret_cast<uint4*>(&Kst[row * kD + 8 * c8]) =
-        *reinterpret_cast<const uint4*>(kg + static_cast<int64_t>(kblk0 + row) * kD + 8 * c8);
+  if constexpr (!DSOUT) {
+    for (int e = tid; e < kBlk * kCh; e += 64 * kW) {
+      const int row = e / kCh, c8 = e % kCh;
+      *reinterpret_cast<uint4*>(&Kst[row * kD + 8 * c8]) =
+          *reinterpret_cast<const uint4*>(kg + static_cast<int64_t>(kblk0 + row) * kD + 8 * c8);
+    }
   }
-  // S and dP B operands [16 d x 32 keys]: key = this lane's key, d = 16 ds + 8 g + s
-  bf16x8 kb[kD / 16], vb[kD / 16];
+  // B operand [16 d x 32 keys] of S (role 0: K) or dP (role 1: V): key = this
+  // lane's key, d = 16 ds + 8 g + s
+  bf16x8 kvb[kD / 16];
+  {
+    const uint16_t* src = (role ? vg : kg) + static_cast<int64_t>(key) * kD + 8 * g;
 #pragma unroll
-  for (int ds = 0; ds < kD / 16; ++ds) {
-    kb[ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(kg + static_cast<int64_t>(key) * kD + 16 * ds + 8 * g));
-    vb[ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(vg + static_cast<int64_t>(key) * kD + 16 * ds + 8 * g));
+    for (int ds = 0; ds < kD / 16; ++ds) kvb[ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(src + 16 * ds));
   }
   __syncthreads();
   // dQ B operands [16 keys x 32 d]: d = slice + 32 dt + col, keys of k-step ks
   // in the transpose-read order of the dS^T tile
   constexpr int kDt = kSlice / 32;
-  const bool has_slice = kSlice * kh < kD;    // uniform
+  const bool has_slice = kSlice * wave < kD;   // uniform
   bf16x8 kq[DSOUT ? 1 : 2 * KH][kDt];
   if (!DSOUT && has_slice) {
 #pragma unroll
     for (int ks = 0; ks < 2 * KH; ++ks)
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) {
-        const uint16_t* p = &Kst[(16 * ks + 4 * gk + srow) * kD + kSlice * kh + 32 * dt + sub16 + 4 * m4];
+        const uint16_t* p = &Kst[(16 * ks + 4 * gk + srow) * kD + kSlice * wave + 32 * dt + sub16 + 4 * m4];
         kq[ks][dt] = lds_tr_pair(p, p + 8 * kD);
       }
   }
 
   const int nbat = (n + 31) >> 5;
-  const int iters = (nbat + QS - 1) / QS;
-  // lane col's entry of the stream's batch bt (-1: none)
-  auto entry = [&](int bt) -> int {
-    const int idx = bt * 32 + col;
-    return (bt < nbat && idx < n) ? list[idx] : -1;
+  // Lane col's entry of batch bt, loaded unconditionally (past the bucket's
+  // end: its last entry) so that every batch issues the same memory
+  // instructions, and whether it is one of the bucket's: the loaded value is
+  // combined with nothing before its use a batch later, so that the compiler
+  // does not wait for the load as soon as it is issued.
+  auto entry = [&](int bt) -> int { return list[min(bt * 32 + col, n - 1)]; };
+  auto live = [&](int bt) -> bool { return bt * 32 + col < n; };
+  auto row_of = [&](int e, bool ok) -> int {
+    const int hl = ok ? e / N : 0;
+    return ok ? static_cast<int>((qhead0 + hl) * N + (e - hl * N)) : 0;
   };
-  auto row_of = [&](int e) -> int {
-    if (e < 0) return 0;
-    const int hl = e / N;
-    return static_cast<int>((qhead0 + hl) * N + (e - hl * N));
-  };
-  // HBM -> LDS copy of the stream's Q and G_s rows of an entry set: 2 kOpsT
-  // instructions of kRowsOp rows, split over the stream's KH waves; lane l
-  // fills physical chunk l % kCh of row kRowsOp n + l / kCh
+  // The Q and G_s rows of an entry set: 2 kOpsT 16-byte copies of kRowsOp
+  // rows, split over the kW waves; lane l takes physical chunk l % kCh of
+  // row kRowsOp n + l / kCh.  Training modes copy HBM -> LDS directly at the
+  // start of a batch, into the other of two separately declared tile sets
+  // (with the loop unrolled twice, the compiler can tell the set being filled
+  // from the one being read).  Sparse-only, whose dQ products need more
+  // registers, goes through registers: loads at the start of a batch, LDS
+  // stores at its end, in a loop that is not unrolled (measured faster there,
+  // and the twice-unrolled form spills).
   constexpr int kRowsOp = 512 / HD, kOpsT = HD / 16;
-  auto load_tiles = [&](int e, uint16_t* Qd, uint16_t* Fd) {
-    const int R = row_of(e);
+  static_assert((2 * kOpsT) % kW == 0, "tile copies must split evenly over the waves");
+  constexpr int kPer = 2 * kOpsT / kW;
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // (a native vector stays in registers)
+  auto copy_src = [&](int R, int u) {
+    const int nn = u * kW + wave;               // uniform
+    const int which = nn / kOpsT, n8 = nn % kOpsT;
+    const int row = kRowsOp * n8 + lane / kCh;
+    const int Rr = __shfl(R, row, 64);
+    const uint16_t* src = which == 0 ? static_cast<const uint16_t*>(a.q) : a.g_sparse;
+    return src + static_cast<int64_t>(Rr) * kD + 8 * swz_t<HD>(row, lane % kCh);
+  };
+  auto copy_dst = [&](uint16_t* Qd, uint16_t* Fd, int u) {
+    const int nn = u * kW + wave;
+    return (nn / kOpsT == 0 ? Qd : Fd) + (nn % kOpsT) * 512;
+  };
+  u32x4 pre[DSOUT ? 1 : kPer];
+  // The copies' address registers stay allocated until the end of the batch:
+  // an LDS read into a register that a copy in flight takes its address from
+  // makes the compiler wait for every load and copy, the prefetch included.
+  const uint16_t* src_of[kPer];
+  auto load_tiles = [&](int e, bool ok, uint16_t* Qd, uint16_t* Fd) {
+    const int R = row_of(e, ok);
 #pragma unroll
-    for (int u = 0; u < 2 * kOpsT / KH; ++u) {
-      const int nn = u * KH + kh;                 // uniform
-      const int which = nn / kOpsT, n8 = nn % kOpsT;
-      const int row = kRowsOp * n8 + lane / kCh;
-      const int Rr = __shfl(R, row, 64);
-      const uint16_t* src = which == 0 ? static_cast<const uint16_t*>(a.q) : a.g_sparse;
-      uint16_t* dst = (which == 0 ? Qd : Fd) + qs * kT;
-      const int cl = swz_t<HD>(row, lane % kCh);
-      __builtin_amdgcn_global_load_lds((const glb_void*)(src + static_cast<int64_t>(Rr) * kD + 8 * cl),
-                                       (lds_void*)(dst + n8 * 512), 16, 0, 0);
+    for (int u = 0; u < kPer; ++u) {
+      src_of[u] = copy_src(R, u);
+      if constexpr (DSOUT)
+        __builtin_amdgcn_global_load_lds((const glb_void*)src_of[u], (lds_void*)copy_dst(Qd, Fd, u), 16, 0, 0);
+      else
+        pre[u] = *reinterpret_cast<const u32x4*>(src_of[u]);
     }
   };
-  // row values of an entry set, through registers (lanes 0..31 of wave kh = 0)
+  auto hold_sources = [&]() {
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) asm volatile("" ::"v"(src_of[u]));
+  };
+  auto store_tiles = [&](uint16_t* Qd, uint16_t* Fd) {
+    if constexpr (!DSOUT) {
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) *reinterpret_cast<u32x4*>(copy_dst(Qd, Fd, u) + 8 * lane) = pre[u];
+    }
+  };
+  // row values of an entry set, through registers (lanes 0..31 of wave 0)
+  // (loaded unconditionally as well; a row past the bucket's end stores
+  // lse = inf, D = 0, t = -1)
   float rv_lse = 0.f, rv_d = 0.f;
-  int rv_t = -1, rv_r = 0;
-  auto load_rows = [&](int e) {
-    rv_t = -1;
-    rv_r = 0;
-    rv_lse = INFINITY;
-    rv_d = 0.f;
-    if (e >= 0) {
-      const int hl = e / N;
-      rv_t = e - hl * N;
-      rv_r = row_of(e);
-      rv_lse = a.lse2_sparse[rv_r];
-      rv_d = a.D_sparse[rv_r];
+  int rv_t = -1;
+  auto load_rows = [&](int e, bool ok) {
+    if (wave == 0) {
+      const int r = row_of(e, ok);
+      rv_lse = a.lse2_sparse[r];
+      rv_d = a.D_sparse[r];
+      rv_t = ok ? e - (e / N) * N : -1;
     }
   };
-  auto store_rows = [&](float* Rd) {
-    if (kh == 0 && g == 0) {
-      float* r = Rd + qs * 128;
-      r[col] = rv_lse;
-      r[32 + col] = rv_d;
-      r[64 + col] = __int_as_float(rv_t);
+  auto store_rows = [&](float* Rd, bool ok) {
+    if (wave == 0 && g == 0) {
+      Rd[col] = ok ? rv_lse : INFINITY;
+      Rd[32 + col] = ok ? rv_d : 0.f;
+      Rd[64 + col] = __int_as_float(rv_t);
     }
   };
 
-  // one iteration on set (Q, F, dS, rv) while the next batch streams into (Qn, Fn, Rn)
-  auto step = [&](int it, int e_next, const uint16_t* Q, const uint16_t* F, uint16_t* dS, const float* rv,
-                  uint16_t* Qn, uint16_t* Fn, float* Rn) {
-    const bool more = it + 1 < iters;
+  // P of the lane's 16 queries, element-major so that each access is one
+  // contiguous 1 KiB row of the key half's buffer
+  float* px = PX + kh * 1024 + lane * 4;
+
+  // one batch on set (Q, F, rv) while the next batch streams into (Qn, Fn, Rn)
+  auto step = [&](int it, int e_next, const uint16_t* Qs, const uint16_t* Fs, const float* rs, uint16_t* Qn,
+                  uint16_t* Fn, float* Rn) {
+    const bool more = it + 1 < nbat;
+    const bool ok_next = live(it + 1);
     if (more) {
-      load_rows(e_next);
-      load_tiles(e_next, Qn, Fn);
+      load_rows(e_next, ok_next);
+      load_tiles(e_next, ok_next, Qn, Fn);
     }
-    const bool has = it * QS + qs < nbat;                       // uniform
-    const uint16_t* Qs = Q + qs * kT;
-    const uint16_t* Fs = F + qs * kT;
-    uint16_t* dSs = dS + qs * kDS;
-    const float* rs = rv + qs * 128;
-    // validity of the lane's 16 query rows for the dQ partials, taken before
-    // the barrier (the row values are refilled after it)
-    uint32_t rowok = 0u;
-    if (has) {
-      // ---- S = Q K^T, dP = G_s V^T [32 q x 32 keys]; lane: key col, queries 8(i/4)+4g+(i%4)
-      f32x16 s = f32x16{}, dp = f32x16{};
-      const int ra = col * kD;
+    // The lane parts of the LDS offsets, opaque to the compiler in each
+    // batch: otherwise it keeps every offset of both tile sets in registers
+    // across the loop and the wave no longer fits half the register file.
+    int cx = col, rx = 4 * gk + srow, cq = 2 * (grp & 1) + (m4 >> 1);
+    asm volatile("" : "+v"(cx), "+v"(rx), "+v"(cq));
+    const int e4 = 4 * (m4 & 1);
+    // A operand [32 q x 16 d] of S / dP (k-step ds) from a Q / G_s tile
+    auto rdA = [&](const uint16_t* T, int ds) { return lds_read8(&T[cx * kD + 8 * swz_t<HD>(cx, 2 * ds + g)]); };
+    // A operand [32 d x 16 q] (transposed tile, k-step st, d tile dt)
+    auto rdT = [&](const uint16_t* T, int st, int dt) {
+      const int r0 = 16 * st + rx, r1 = r0 + 8, cl = 4 * dt + cq;
+      return lds_tr_pair(&T[r0 * kD + 8 * swz_t<HD>(r0, cl) + e4], &T[r1 * kD + 8 * swz_t<HD>(r1, cl) + e4]);
+    };
+    // transposing read of the dS^T tile for k-step ks (keys 16 ks ..)
+    auto rdS = [&](int ks) {
+      const int r0 = 16 * ks + rx, r1 = r0 + 8;
+      return lds_tr_pair(&DS[r0 * 32 + 8 * swz_s(r0, cq) + e4], &DS[r1 * 32 + 8 * swz_s(r1, cq) + e4]);
+    };
+    // the lane's 16 query rows (queries 8(i/4)+4g+(i%4)): bit i of rowok says
+    // the row exists (t >= 0), bit i of causal that the lane's key is <= t
+    uint32_t rowok = 0u, causal = 0u;
 #pragma unroll
-      for (int ds = 0; ds < kD / 16; ++ds) {
-        const int off = ra + 8 * swz_t<HD>(col, 2 * ds + g);
-        s = mfma32x32x16(lds_read8(&Qs[off]), kb[ds], s);
-        dp = mfma32x32x16(lds_read8(&Fs[off]), vb[ds], dp);
+    for (int a4 = 0; a4 < 4; ++a4) {
+      const float4 t4 = *reinterpret_cast<const float4*>(&rs[64 + 8 * a4 + 4 * g]);
+      const int ta[4] = {__float_as_int(t4.x), __float_as_int(t4.y), __float_as_int(t4.z), __float_as_int(t4.w)};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        rowok |= ta[e] >= 0 ? (1u << (4 * a4 + e)) : 0u;
+        causal |= key <= ta[e] ? (1u << (4 * a4 + e)) : 0u;   // t = -1: no row
       }
-      float p[16], dsv[16];
+    }
+
+    // ---- role 0: S = Q K^T, role 1: dP = G_s V^T [32 q x 32 keys];
+    // lane: key col, queries 8(i/4)+4g+(i%4)
+    f32x16 x = f32x16{};
+    {
+      const uint16_t* A = role ? Fs : Qs;
+#pragma unroll
+      for (int ds = 0; ds < kD / 16; ++ds) x = mfma32x32x16(rdA(A, ds), kvb[ds], x);
+    }
+    // w: role 0 P, role 1 dS -- the B operand of the wave's product
+    float w[16];
+    if (role == 0) {
+      // ---- P = 2^(S c - lse_s) on the causal keys -> LDS for role 1
 #pragma unroll
       for (int a4 = 0; a4 < 4; ++a4) {
-        const int qb = 8 * a4 + 4 * g;
-        const float4 l4 = *reinterpret_cast<const float4*>(&rs[qb]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&rs[32 + qb]);
-        const float4 t4 = *reinterpret_cast<const float4*>(&rs[64 + qb]);
-        const float la[4] = {l4.x, l4.y, l4.z, l4.w}, da[4] = {d4.x, d4.y, d4.z, d4.w};
-        const int ta[4] = {__float_as_int(t4.x), __float_as_int(t4.y), __float_as_int(t4.z), __float_as_int(t4.w)};
+        const float4 l4 = *reinterpret_cast<const float4*>(&rs[8 * a4 + 4 * g]);
+        const float la[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int i = 4 * a4 + e;
-          rowok |= ta[e] >= 0 ? (1u << i) : 0u;
-          const bool live = key <= ta[e];                  // t = -1: no row
-          p[i] = live ? fast_exp2(s[i] * scale_log2 - la[e]) : 0.f;
-          dsv[i] = p[i] * (dp[i] - da[e]);
+          const float v = fast_exp2(x[i] * scale_log2 - la[e]);
+          w[i] = (causal >> i) & 1u ? v : 0.f;
         }
+        *reinterpret_cast<float4*>(px + 256 * a4) = make_float4(w[4 * a4], w[4 * a4 + 1], w[4 * a4 + 2], w[4 * a4 + 3]);
       }
-      // ---- dS^T -> LDS (bf16) for the dQ reduction over the block's keys
+    }
+    lds_barrier();                     // P of every key half visible
+    if (role != 0) {
+      // ---- dS = P (dP - D)
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) {
+        const float4 p4 = *reinterpret_cast<const float4*>(px + 256 * a4);
+        const float4 d4 = *reinterpret_cast<const float4*>(&rs[32 + 8 * a4 + 4 * g]);
+        w[4 * a4] = p4.x * (x[4 * a4] - d4.x);
+        w[4 * a4 + 1] = p4.y * (x[4 * a4 + 1] - d4.y);
+        w[4 * a4 + 2] = p4.z * (x[4 * a4 + 2] - d4.z);
+        w[4 * a4 + 3] = p4.w * (x[4 * a4 + 3] - d4.w);
+      }
+      // ---- dS^T -> LDS (bf16): the dS rows, or the dQ reduction over the block's keys
       {
-        const int r = 32 * kh + col;
+        const int r = 32 * kh + cx;
 #pragma unroll
         for (int a4 = 0; a4 < 4; ++a4) {
-          uint2 u = make_uint2(pack_bf16x2(dsv[4 * a4], dsv[4 * a4 + 1]), pack_bf16x2(dsv[4 * a4 + 2], dsv[4 * a4 + 3]));
-          *reinterpret_cast<uint2*>(&dSs[r * 32 + 8 * swz_s(r, a4) + 4 * g]) = u;
+          uint2 u = make_uint2(pack_bf16x2(w[4 * a4], w[4 * a4 + 1]), pack_bf16x2(w[4 * a4 + 2], w[4 * a4 + 3]));
+          *reinterpret_cast<uint2*>(&DS[r * 32 + 8 * swz_s(r, a4) + 4 * g]) = u;
         }
       }
       if constexpr (DSOUT) {
@@ -279,115 +352,93 @@ __global__ void __launch_bounds__(256, 1)
         // 8 (s / 4) + 4 g + s % 4.  A row of 32 keys is stored in the dQ
         // kernel's lane order, position 16 g' + 4 a + e for key 8 a + 4 g' + e,
         // so that element s of half h goes to position 16 g + 8 h + s.
-        // (the transposes take all lanes: a lane's result holds other lanes' reads)
+        // (the transposes take all lanes, outside the store's lane condition:
+        // a lane's result holds other lanes' reads)
         uint4 u[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int ks = 2 * kh + h;
-          const int r0 = 16 * ks + 4 * gk + srow, r1 = r0 + 8;
-          const int cl = 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
-          u[h] = __builtin_bit_cast(
-              uint4, lds_tr_pair(&dSs[r0 * 32 + 8 * swz_s(r0, cl) + e4], &dSs[r1 * 32 + 8 * swz_s(r1, cl) + e4]));
-        }
-        const int idx = (it * QS + qs) * 32 + col;
+        for (int h = 0; h < 2; ++h) u[h] = __builtin_bit_cast(uint4, rdS(2 * kh + h));
+        const int idx = it * 32 + col;
         if (idx < n) {
           uint16_t* dst = a.ds_rows + static_cast<int64_t>(p0 + idx) * kBlk + 32 * kh;
 #pragma unroll
           for (int h = 0; h < 2; ++h) *reinterpret_cast<uint4*>(dst + 16 * g + 8 * h) = u[h];
         }
       }
-      // ---- dV^T += G_s^T P, dK^T += Q^T dS  (k = queries; 2 steps of 16)
+    }
+    // ---- role 0: dV^T += G_s^T P, role 1: dK^T += Q^T dS  (k = queries; 2 steps of 16)
+    {
+      const uint16_t* T = role ? Qs : Fs;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int o = 8 * st;
-        const bf16x8 bp = to_bf16x8(p[o], p[o + 1], p[o + 2], p[o + 3], p[o + 4], p[o + 5], p[o + 6], p[o + 7]);
-        const bf16x8 bds = to_bf16x8(dsv[o], dsv[o + 1], dsv[o + 2], dsv[o + 3], dsv[o + 4], dsv[o + 5], dsv[o + 6], dsv[o + 7]);
-        const int r0 = 16 * st + 4 * gk + srow, r1 = r0 + 8;
+        const bf16x8 bw = to_bf16x8(w[o], w[o + 1], w[o + 2], w[o + 3], w[o + 4], w[o + 5], w[o + 6], w[o + 7]);
 #pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) {
-          const int cl = 4 * dt + 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
-          const int o0 = r0 * kD + 8 * swz_t<HD>(r0, cl) + e4, o1 = r1 * kD + 8 * swz_t<HD>(r1, cl) + e4;
-          dv[dt] = mfma32x32x16(lds_tr_pair(&Fs[o0], &Fs[o1]), bp, dv[dt]);
-          dk[dt] = mfma32x32x16(lds_tr_pair(&Qs[o0], &Qs[o1]), bds, dk[dt]);
-        }
+        for (int dt = 0; dt < kDT; ++dt) acc[dt] = mfma32x32x16(rdT(T, st, dt), bw, acc[dt]);
       }
     }
-    if (more) store_rows(Rn);
-    __builtin_amdgcn_s_waitcnt(0);     // next tiles landed, dS^T written
-    __syncthreads();
+    if (more) {
+      hold_sources();
+      store_rows(Rn, ok_next);
+      store_tiles(Qn, Fn);
+    }
+    if constexpr (DSOUT) {
+      __builtin_amdgcn_s_waitcnt(0);   // the next batch's copies landed
+      __syncthreads();
+    } else {
+      lds_barrier();                   // the next batch's tiles and dS^T in LDS
+    }
 
-    // ---- dQ[32 q x slice] of the stream's batch = dS[32 q x block keys] K[block keys x slice]
-    if (!DSOUT && has && has_slice) {
+    // ---- dQ[32 q x slice] of the batch = dS[32 q x block keys] K[block keys x slice]
+    if (!DSOUT && has_slice) {
       f32x16 dq[kDt];
 #pragma unroll
       for (int dt = 0; dt < kDt; ++dt) dq[dt] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < 2 * KH; ++ks) {
-        const int r0 = 16 * ks + 4 * gk + srow, r1 = r0 + 8;
-        const int cl = 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
-        const bf16x8 ds_op =
-            lds_tr_pair(&dSs[r0 * 32 + 8 * swz_s(r0, cl) + e4], &dSs[r1 * 32 + 8 * swz_s(r1, cl) + e4]);
+        const bf16x8 ds_op = rdS(ks);
 #pragma unroll
         for (int dt = 0; dt < kDt; ++dt) dq[dt] = mfma32x32x16(ds_op, kq[ks][dt], dq[dt]);
       }
-      // the batch's entries are p0 + 32 bt + r (r: the query of register i)
-      const int64_t e0 = static_cast<int64_t>(p0) + (it * QS + qs) * 32;
+      // the batch's entries are p0 + 32 it + r (r: the query of register i)
+      const int64_t e0 = static_cast<int64_t>(p0) + it * 32;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         if (!((rowok >> i) & 1u)) continue;
         const int r = 8 * (i >> 2) + 4 * g + (i & 3);
-        uint16_t* dst = a.dq_part + (e0 + r) * kD + kSlice * kh + col;
+        uint16_t* dst = a.dq_part + (e0 + r) * kD + kSlice * wave + col;
 #pragma unroll
         for (int dt = 0; dt < kDt; ++dt) dst[32 * dt] = to_bf16(scale * dq[dt][i]).bits;
       }
     }
   };
 
-  // prologue: the first batch of every stream
-  int e_cur = entry(qs);
-  load_rows(e_cur);
-  load_tiles(e_cur, Q0, F0);
-  store_rows(R0);
-  int e_next = entry(QS + qs);
+  // prologue: the first batch
+  load_rows(entry(0), live(0));
+  load_tiles(entry(0), live(0), Q0, F0);
+  store_rows(R0, live(0));
+  store_tiles(Q0, F0);
+  int e_next = entry(1);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int it = 0; it < iters; it += 2) {
-    int e_after = entry((it + 2) * QS + qs);
-    step(it, e_next, Q0, F0, D0, R0, Q1, F1, R1);
-    e_next = e_after;
-    if (it + 1 >= iters) break;
-    e_after = entry((it + 3) * QS + qs);
-    step(it + 1, e_next, Q1, F1, D1, R1, Q0, F0, R0);
-    e_next = e_after;
-  }
-
-  // ---- reduce dK / dV over the streams of each key half (one stream and
-  // one tensor at a time through 16 KiB of the free Q tiles: Q0 for key
-  // half 0, Q1 for key half 1), then write
-  if (QS > 1) {
-    float* red = reinterpret_cast<float*>(kh == 0 ? Q0 : Q1);
-    for (int o = 1; o < QS; ++o) {
-#pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        f32x16* acc = part == 0 ? dk : dv;
-        __syncthreads();
-        if (qs == o) {
-#pragma unroll
-          for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) red[(dt * 16 + i) * 64 + lane] = acc[dt][i];
-        }
-        __syncthreads();
-        if (qs == 0) {
-#pragma unroll
-          for (int dt = 0; dt < kDT; ++dt)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) acc[dt][i] += red[(dt * 16 + i) * 64 + lane];
-        }
-      }
+  if constexpr (DSOUT) {
+    for (int it = 0; it < nbat; it += 2) {
+      int e_after = entry(it + 2);
+      step(it, e_next, Q0, F0, R0, Q1, F1, R1);
+      e_next = e_after;
+      if (it + 1 >= nbat) break;
+      e_after = entry(it + 3);
+      step(it + 1, e_next, Q1, F1, R1, Q0, F0, R0);
+      e_next = e_after;
+    }
+  } else {
+    for (int it = 0; it < nbat; ++it) {
+      const int e_after = entry(it + 2);
+      const bool odd = it & 1;
+      step(it, e_next, odd ? Q1 : Q0, odd ? F1 : F0, odd ? R1 : R0, odd ? Q0 : Q1, odd ? F0 : F1, odd ? R0 : R1);
+      e_next = e_after;
     }
   }
-  if (qs == 0) write_kv(dk, dv);
+  write_out(acc);
 }
 
 // Sparse-only dQ: the sum of a query row's partials over its selected
@@ -475,15 +526,15 @@ void launch_bwd_sparse(const Dims& D, const SparseBwdArgs& a, hipStream_t s) {
   dim3 grid(D.B * D.Hkv, D.nb);
   const float scale_log2 = D.scale * 1.4426950408889634f;
   timing_begin(kKBwdSparse, s);
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.scale, scale_log2);
+  auto go = [&](auto kern, int kh) {       // 2 kh waves: (key half, role)
+    hipLaunchKernelGGL(kern, grid, dim3(128 * kh), 0, s, a, D.Hq, D.G, D.N, D.nb, D.scale, scale_log2);
   };
   const bool rows_out = a.ds_rows != nullptr;
   auto by_block = [&](auto hd_tag) {
     constexpr int HD = decltype(hd_tag)::value;
-    if (D.block == 32) rows_out ? go(k_bwd_sparse<1, true, HD>) : go(k_bwd_sparse<1, false, HD>);
-    else if (D.block == 64) rows_out ? go(k_bwd_sparse<2, true, HD>) : go(k_bwd_sparse<2, false, HD>);
-    else rows_out ? go(k_bwd_sparse<4, true, HD>) : go(k_bwd_sparse<4, false, HD>);
+    if (D.block == 32) rows_out ? go(k_bwd_sparse<1, true, HD>, 1) : go(k_bwd_sparse<1, false, HD>, 1);
+    else if (D.block == 64) rows_out ? go(k_bwd_sparse<2, true, HD>, 2) : go(k_bwd_sparse<2, false, HD>, 2);
+    else rows_out ? go(k_bwd_sparse<4, true, HD>, 4) : go(k_bwd_sparse<4, false, HD>, 4);
   };
   if (D.d == 64) by_block(std::integral_constant<int, 64>{});
   else by_block(std::integral_constant<int, 128>{});

@@ -1,12 +1,14 @@
-"""Static check of the compiled gfx950 code: no matrix instruction may be
-issued while EXEC is narrowed without a branch around it.
+"""Static checks of the compiled gfx950 code for two instruction classes that
+combine the data of all 64 lanes and so must not run under a narrowed EXEC.
 
 The compiler implements an `if` whose condition it believes to be per-lane by
-masking EXEC; matrix (MFMA) instructions combine all 64 lanes and were
-observed to run even under EXEC = 0 in that form, adding stale operands to
-accumulators.  Kernels therefore make every MFMA guard wave-uniform
-(readfirstlane); this check compiles the kernels to assembly and fails if an
-MFMA follows an EXEC-narrowing instruction without an execz branch between.
+masking EXEC.  Matrix (MFMA) instructions were observed to run even under
+EXEC = 0 in that form, adding stale operands to accumulators: kernels make
+every MFMA guard wave-uniform (readfirstlane), and the check fails if an MFMA
+follows an EXEC-narrowing instruction without an execz branch between.
+Transposing LDS reads (ds_read_b64_tr_b16) hand each lane data that other
+lanes read, so under a partial EXEC they return unread data: the check fails
+on any such read after an EXEC-narrowing instruction.
 """
 from __future__ import annotations
 
@@ -43,6 +45,25 @@ def masked_mfmas(asm: str):
     return found
 
 
+def masked_transposes(asm: str):
+    """(line number, instruction) of every transposing LDS read issued under a
+    narrowed EXEC (guarded by an execz branch or not)."""
+    lines = [l.split(";")[0].strip() for l in asm.splitlines()]
+    found = []
+    for i, t in enumerate(lines):
+        if not re.match(r"ds_read_b\d+_tr", t):
+            continue
+        j = i - 1
+        while j >= 0:
+            u = lines[j]
+            if _EXEC_WRITE.match(u) or (u.startswith(".LBB") and u.endswith(":")):
+                break
+            j -= 1
+        if j >= 0 and _NARROW.match(lines[j]):
+            found.append((i, t))
+    return found
+
+
 def device_asm(source: str) -> str:
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "k.s")
@@ -62,7 +83,8 @@ def main() -> int:
     for src in MFMA_SOURCES:
         if not os.path.exists(os.path.join(_build.CSRC, src)):
             continue
-        hits = masked_mfmas(device_asm(src))
+        asm = device_asm(src)
+        hits = masked_mfmas(asm) + masked_transposes(asm)
         for ln, ins in hits[:5]:
             print(f"{src}: asm line {ln}: {ins}", file=sys.stderr)
         bad += len(hits)
