@@ -17,7 +17,14 @@
 // half's key block are added to the full stream's dS^T before the product,
 // so both streams share one dQ^T accumulation and no atomics are needed.  A
 // wave's 32 queries are one word of the block's bucket mask; a selected
-// query's row is entry wpos + popcount of the word's lower bits.
+// query's row is entry wpos + popcount of the word's lower bits.  With 64-key
+// blocks (one block per tile) the selected queries' rows of a tile are
+// consecutive entries, so a wave copies them HBM -> LDS with the next tile
+// (up to 12 rows; a wave with more reads the rest from HBM when it uses
+// them); other block sizes load each selected lane's part of its row into
+// registers during the previous tile.
+
+#include <type_traits>
 
 #include "common.h"
 #include "internal.h"
@@ -42,13 +49,21 @@ template <int HD> __device__ __forceinline__ int swz_k(int r, int c) {
   return HD == 128 ? c ^ (((r & 7) << 1) | ((r >> 3) & 1)) : c ^ (r & 7);
 }
 
-template <bool SPARSE, int HD>   // HD: head dimension
+// SP: 0 the full stream alone; 1 with the sparse stream's dS rows through
+// registers (any block size); 2 through LDS (64-key blocks).  HD: head dimension.
+template <int SP, int HD>
 __global__ void __launch_bounds__(256, 2)
-    k_bwd_dq(BwdDqArgs a, int Hq, int G, int N, int nb, int block, float scale, float scale_log2, int n_qtiles) {
+    k_bwd_dq(BwdDqArgs a, int Hq, int G, int N, int nb, int block, float scale, float scale_log2, int n_qtiles,
+             int64_t ds_elems) {
+  constexpr bool SPARSE = SP != 0;
   constexpr int kD = HD;
   constexpr int kDT = HD / 32;                 // 32-column tiles of dQ
   constexpr int kTile = kBN * kD;
   __shared__ __attribute__((aligned(16))) uint16_t K0[kTile], K1[kTile], V0[kTile], V1[kTile];
+  // SP = 2: each wave's first kSDRows dS rows of the current / next tile
+  constexpr int kSDRows = 12;
+  constexpr int kSD = SP == 2 ? 4 * kSDRows * kBN : 8;
+  __shared__ __attribute__((aligned(16))) uint16_t SD0[kSD], SD1[kSD];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, col = lane & 31;
@@ -134,9 +149,11 @@ __global__ void __launch_bounds__(256, 2)
   // next tile are fetched during the second half of the current one, so they
   // land with the next tile's copies at the barrier: a wait for a register
   // load while tile copies are in flight would wait for those copies too.
-  uint4 sd[2][2], sdn[2][2];
+  // (SP = 1 only: the arrays are unused otherwise)
+  constexpr int kSdH = SP == 1 ? 2 : 1;
+  uint4 sd[kSdH][2], sdn[kSdH][2];
 #pragma unroll
-  for (int kh = 0; kh < 2; ++kh) sd[kh][0] = sd[kh][1] = sdn[kh][0] = sdn[kh][1] = make_uint4(0, 0, 0, 0);
+  for (int kh = 0; kh < kSdH; ++kh) sd[kh][0] = sd[kh][1] = sdn[kh][0] = sdn[kh][1] = make_uint4(0, 0, 0, 0);
   auto load_sd = [&](int jj, int kh, uint32_t mword, int mpos, uint4* dst) {
     dst[0] = dst[1] = make_uint4(0, 0, 0, 0);
     const int kbase = jj * kBN + kh * 32;
@@ -153,7 +170,23 @@ __global__ void __launch_bounds__(256, 2)
       dst[1] = *reinterpret_cast<const uint4*>(src + 8);
     }
   };
-  auto step = [&](int j, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn) {
+  // SP = 2: the dS rows of the wave's selected queries of a tile (its mask
+  // word and entry position, uniform) -> LDS, at most kSDRows of them; the
+  // source is clamped to the buffer (rows past the tile's are never read)
+  auto copy_rows = [&](uint32_t word, int pos, uint16_t* SDd) {
+    uint16_t* dst = SDd + wave * kSDRows * kBN;
+    const int cnt = __builtin_popcount(word);
+    const int64_t base = static_cast<int64_t>(pos) * kBN;
+#pragma unroll
+    for (int u = 0; u < (kSDRows * kBN * 2 + 1023) / 1024; ++u) {
+      if (u * 8 < cnt && u * 1024 + 16 * lane < kSDRows * kBN * 2) {
+        const int64_t off = min(base + u * 512 + 8 * lane, ds_elems - 8);
+        __builtin_amdgcn_global_load_lds((const glb_void*)(a.ds_rows + off), (lds_void*)(dst + u * 512), 16, 0, 0);
+      }
+    }
+  };
+  auto step = [&](int j, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn, const uint16_t* SDs,
+                  uint16_t* SDn) {
     if constexpr (SPARSE) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {       // uniform: scalar registers
@@ -163,6 +196,8 @@ __global__ void __launch_bounds__(256, 2)
         mpn[kh] = __builtin_amdgcn_readfirstlane(mpn2[kh]);
       }
       if (j + 2 <= j_last) mask_words(j + 2, mwn2, mpn2);
+    }
+    if constexpr (SP == 1) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         sd[kh][0] = sdn[kh][0];
@@ -170,12 +205,15 @@ __global__ void __launch_bounds__(256, 2)
       }
     }
     if (j + 1 <= j_last) load_tile(j + 1, Kn, Vn);
+    if constexpr (SP == 2) {
+      if (wave_live && j + 1 <= j_last && mwn[0] != 0u) copy_rows(mwn[0], mpn[0], SDn);
+    }
     if (wave_live && j * kBN <= wave_last_q) {
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {
         const int kbase = j * kBN + kh * 32;
         if (kbase > wave_last_q) break;                // uniform: later keys are all masked
-        if constexpr (SPARSE) {
+        if constexpr (SP == 1) {
           if (kh == 1) {
             load_sd(j + 1, 0, mwn[0], mpn[0], sdn[0]);
             load_sd(j + 1, 1, mwn[1], mpn[1], sdn[1]);
@@ -207,7 +245,32 @@ __global__ void __launch_bounds__(256, 2)
         // being the key of register i; it is zero wherever the mask is)
         float dsv[16];
         {
-          const uint4 sd0 = sd[kh][0], sd1 = sd[kh][1];
+          uint4 sd0 = make_uint4(0, 0, 0, 0), sd1 = make_uint4(0, 0, 0, 0);
+          if constexpr (SP == 1) {
+            sd0 = sd[kh][0];
+            sd1 = sd[kh][1];
+          } else if constexpr (SP == 2) {
+            const uint32_t m = mw[0];        // (one block per tile: both halves' word)
+            if (m != 0u) {                   // uniform
+              const bool mine = (m >> col) & 1u;
+              const int below = static_cast<int>(__builtin_amdgcn_mbcnt_hi(m, __builtin_amdgcn_mbcnt_lo(m, 0u))) -
+                                (g ? __builtin_popcount(m) : 0);
+              if (mine && below < kSDRows) {
+                const uint16_t* src = SDs + (wave * kSDRows + below) * kBN + kh * 32 + 16 * g;
+                sd0 = *reinterpret_cast<const uint4*>(src);
+                sd1 = *reinterpret_cast<const uint4*>(src + 8);
+              }
+              if (__builtin_popcount(m) > kSDRows) {   // uniform, rare: the rest from HBM
+                if (mine && below >= kSDRows) {
+                  const uint16_t* src = a.ds_rows + static_cast<int64_t>(mp[0] + below) * kBN + kh * 32 + 16 * g;
+                  sd0 = *reinterpret_cast<const uint4*>(src);
+                  sd1 = *reinterpret_cast<const uint4*>(src + 8);
+                }
+                // (waited for here, so that no other tile's use of the rows waits)
+                __builtin_amdgcn_s_waitcnt(0);
+              }
+            }
+          }
           const uint32_t sw[8] = {sd0.x, sd0.y, sd0.z, sd0.w, sd1.x, sd1.y, sd1.z, sd1.w};
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
@@ -257,16 +320,20 @@ __global__ void __launch_bounds__(256, 2)
       mwn[kh] = __builtin_amdgcn_readfirstlane(mwn[kh]);
       mpn[kh] = __builtin_amdgcn_readfirstlane(mpn[kh]);
     }
-    load_sd(0, 0, mwn[0], mpn[0], sdn[0]);
-    load_sd(0, 1, mwn[1], mpn[1], sdn[1]);
+    if constexpr (SP == 1) {
+      load_sd(0, 0, mwn[0], mpn[0], sdn[0]);
+      load_sd(0, 1, mwn[1], mpn[1], sdn[1]);
+    } else {
+      if (wave_live && mwn[0] != 0u) copy_rows(mwn[0], mpn[0], SD0);
+    }
   }
   load_tile(0, K0, V0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int j = 0; j <= j_last; j += 2) {
-    step(j, K0, V0, K1, V1);
+    step(j, K0, V0, K1, V1, SD0, SD1);
     if (j + 1 > j_last) break;
-    step(j + 1, K1, V1, K0, V0);
+    step(j + 1, K1, V1, K0, V0, SD1, SD0);
   }
 
   // ---- epilogue: dq = scale dQ^T^T, bf16
@@ -291,10 +358,16 @@ void launch_bwd_dq(const Dims& D, const BwdDqArgs& a, hipStream_t s) {
   timing_begin(kKBwdDq, s);
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.nb, D.block, D.scale,
-                       D.scale * 1.4426950408889634f, n_qtiles);
+                       D.scale * 1.4426950408889634f, n_qtiles, a.ds_rows ? bucket_capacity(D) * D.block : int64_t{0});
   };
-  if (D.d == 64) a.ds_rows ? go(k_bwd_dq<true, 64>) : go(k_bwd_dq<false, 64>);
-  else a.ds_rows ? go(k_bwd_dq<true, 128>) : go(k_bwd_dq<false, 128>);
+  auto by_mode = [&](auto hd_tag) {
+    constexpr int HD = decltype(hd_tag)::value;
+    if (!a.ds_rows) go(k_bwd_dq<0, HD>);
+    else if (D.block == kBN) go(k_bwd_dq<2, HD>);
+    else go(k_bwd_dq<1, HD>);
+  };
+  if (D.d == 64) by_mode(std::integral_constant<int, 64>{});
+  else by_mode(std::integral_constant<int, 128>{});
   timing_end(kKBwdDq, s);
 }
 
