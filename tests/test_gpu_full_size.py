@@ -175,6 +175,43 @@ def test_train_layer_16k_full_size(K, mode, unit):
     assert np.all(np.abs(sum_dk) <= 2 ** -7 * abs_dk + 1e-6), np.abs(sum_dk).max()
 
 
+def test_train_layer_16k_sparse_only_unit():
+    """The benchmark's layer (B=2, 32 query / 8 KV heads, N=16384, d=128,
+    block 64, top_k 16) trained on the sparse stream alone: one whole (batch,
+    KV head) unit element by element -- h_sparse and lse_sparse of every row,
+    dq of every row and dk / dv of every key, the buckets of the 16K layer
+    (thousands of rows per early key block) through the sparse-only backward
+    and its dQ merge."""
+    wl = si.WORKLOADS["train_b2_h32_n16k"]
+    K, mode, b, c = 16, oracle.SPARSE_ONLY, 1, 3
+    _say(f"full-size {wl.name} sparse-only unit b{b} c{c}: draw")
+    q, k, v, _ = si.draw_qkv(wl, 0)
+    dout = si.draw_dout(wl, 0)
+    qd, kd, vd, gd = (x.to("cuda:0") for x in (q, k, v, dout))
+    sel = ssa().ssa_select_blocks(qd, kd, wl.block, K)
+    fwd = ssa().ssa_attn_fwd(qd, kd, vd, sel, wl.block, K, mode)
+    dq, dk, dv = ssa().ssa_attn_bwd(qd, kd, vd, sel, fwd, gd, wl.block, K, mode)
+    torch.cuda.synchronize()
+    out = {key: val.cpu() for key, val in fwd.items() if not key.startswith("_")}
+    sel_np = sel.cpu().numpy()
+    dq, dk, dv = dq.cpu(), dk.cpu(), dv.cpu()
+    del qd, kd, vd, gd, fwd, sel
+    from oracle import parallel
+
+    G = wl.group
+    hs = slice(c * G, (c + 1) * G)
+    scale = 1.0 / math.sqrt(wl.head_dim)
+    res = parallel.unit_step(si.to_f64(q[b, hs]), si.to_f64(k[b, c]), si.to_f64(v[b, c]), wl.block, K, scale, mode,
+                             dout_u=si.to_f64(dout[b, hs]), sel_u=sel_np[b, hs], M=q.numel())
+    _say(f"  unit b{b} c{c}: oracle {res['seconds']:.1f} s on {res['workers']} processes")
+    assert "h_full" not in res and "h_full" not in out
+    for key in ("h_sparse", "lse_sparse"):
+        assert_close(f"16k sparse-only unit {key}", out[key][b, hs], res[key], wl.dtype)
+    assert_close("16k sparse-only unit dq", dq[b, hs], res["dq"], wl.dtype)
+    assert_close("16k sparse-only unit dk", dk[b, c], res["dk"], wl.dtype)
+    assert_close("16k sparse-only unit dv", dv[b, c], res["dv"], wl.dtype)
+
+
 def test_train_layer_16k_d64_full_size():
     """The benchmark's training layer with 64-wide heads (B=2, 32 query / 8 KV
     heads, N=16384, d=64, block 64, top_k 16): one training step, one whole
