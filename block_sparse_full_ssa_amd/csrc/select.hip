@@ -340,12 +340,25 @@ __global__ void __launch_bounds__(256) k_select_mfma(const T* __restrict__ q, co
       if constexpr (kBf) {
         const uint16_t* mh = mu_hi + mrow + 8 * g;
         const uint16_t* ml = mu_lo + mrow + 8 * g;
+        // the operands of half the k-steps in flight at once before their
+        // products (interleaved with the products, the compiler keeps only
+        // three loads in flight; all of them at once costs a wave per SIMD)
         f32x16 acc_lo = f32x16{};
+        constexpr int kHalf = D / 32;       // k-steps per group of loads
 #pragma unroll
-        for (int s = 0; s < D / 16; ++s) {
-          acc = mfma32x32x16(qb[s], __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(mh + 16 * s)), acc);
-          acc_lo = mfma32x32x16(qb[s], __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ml + 16 * s)),
-                                acc_lo);
+        for (int s0 = 0; s0 < D / 16; s0 += kHalf) {
+          bf16x8 bh[kHalf], bl[kHalf];
+#pragma unroll
+          for (int s = 0; s < kHalf; ++s) {
+            bh[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(mh + 16 * (s0 + s)));
+            bl[s] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(ml + 16 * (s0 + s)));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int s = 0; s < kHalf; ++s) {
+            acc = mfma32x32x16(qb[s0 + s], bh[s], acc);
+            acc_lo = mfma32x32x16(qb[s0 + s], bl[s], acc_lo);
+          }
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[e] += acc_lo[e];
