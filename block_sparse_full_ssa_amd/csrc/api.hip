@@ -150,8 +150,9 @@ static FwdWs carve_fwd(const Dims& D, int mode, Carver& c) {
   }
   if (mode == kSparseOnly && sparse_fwd_supported(D)) {
     w.bk = carve_buckets(D, c);
-    w.part_o = c.take<uint16_t>(bucket_capacity(D) * D.d * sizeof(uint16_t));
-    w.part_lse = c.take<float>(bucket_capacity(D) * sizeof(float));
+    // (one spare entry past the buckets' for the part kernel's rows past a bucket's end)
+    w.part_o = c.take<uint16_t>((bucket_capacity(D) + 1) * D.d * sizeof(uint16_t));
+    w.part_lse = c.take<float>((bucket_capacity(D) + 1) * sizeof(float));
   }
   return w;
 }

@@ -155,8 +155,8 @@ struct SparseFwdArgs {
   const int32_t* sel;
   const uint32_t* mask;                 // buckets
   const int32_t *offs, *rows, *wpos;
-  uint16_t* part_o;                     // [bucket entries][d] bf16 partial outputs, bucket order
-  float* part_lse;                      // [bucket entries] partial log-sum-exps (log2 units)
+  uint16_t* part_o;                     // [bucket capacity + 1][d] bf16 partial outputs, bucket order
+  float* part_lse;                      // [bucket capacity + 1] partial log-sum-exps (log2 units)
   void* h_sparse;
   float* lse_sparse;                    // may be null
 };

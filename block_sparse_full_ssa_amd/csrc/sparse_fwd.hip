@@ -51,7 +51,7 @@ template <int HD> __device__ __forceinline__ int swz_k(int r, int c) { return c 
 
 template <int KH, int HD>   // the key block as KH halves of 32 keys; head dimension HD
 __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFwdArgs a, int Hq, int G, int N, int Nq,
-                                                        int q_off, int nb, float scale_log2) {
+                                                        int q_off, int nb, float scale_log2, int64_t spare) {
   constexpr int kBlk = 32 * KH;
   constexpr int kD = HD;
   constexpr int kCh = HD / 8;      // 16-byte chunks per row
@@ -91,29 +91,29 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
   // The wave's batches are bt = wave, wave + 4, ...; lane col owns batch
   // row col (entry -1 past the bucket's end) and loads that row's Q as its
   // B operand: d = 16 ds + 8 g + s.
+  // (Loads are unconditional, at a clamped index -- a lane past the
+  // bucket's end takes its last entry, whose logits are then masked -- and
+  // validity comes from the position alone: every batch issues the same
+  // memory instructions and no loaded value is combined before its use, so
+  // the compiler's waits are for the loads they need.)
   const int nbat = (n + 31) >> 5;
-  auto entry = [&](int bt) -> int {
-    const int idx = bt * 32 + col;
-    return (bt < nbat && idx < n) ? list[idx] : -1;
-  };
+  auto entry = [&](int bt) -> int { return list[min(bt * 32 + col, n - 1)]; };
   auto load_q = [&](int e, bf16x8* qb) {
-    const int hl = e >= 0 ? e / Nq : 0;
-    const int64_t R = e >= 0 ? (qhead0 + hl) * Nq + (e - hl * Nq) : 0;
+    const int hl = e / Nq;
+    const int64_t R = (qhead0 + hl) * Nq + (e - hl * Nq);
 #pragma unroll
-    for (int ds = 0; ds < kD / 16; ++ds) {
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (e >= 0) u = *reinterpret_cast<const uint4*>(qg + R * kD + 16 * ds + 8 * g);
-      qb[ds] = __builtin_bit_cast(bf16x8, u);
-    }
+    for (int ds = 0; ds < kD / 16; ++ds)
+      qb[ds] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(qg + R * kD + 16 * ds + 8 * g));
   };
 
   bf16x8 qb[kD / 16];
   int bt = wave;
+  if (bt >= nbat) return;
   int e = entry(bt), e_next = entry(bt + 4);
   load_q(e, qb);
   for (; bt < nbat; bt += 4) {
     const int e_after = entry(bt + 8);
-    const bool valid = e >= 0;
+    const bool valid = bt * 32 + col < n;
     const int t = valid ? q_off + e % Nq : 0;       // the row's position
     // S^T for the block's keys (A: key 32 kh + col, d = 16 ds + 8 g + s), log2 units
     f32x16 s[KH];
@@ -127,6 +127,8 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
         s[kh] = mfma32x32x16(lds_read8(&Ks[r * kD + 8 * swz_k<HD>(r, 2 * ds + g)]), qb[ds], s[kh]);
       }
     __builtin_amdgcn_sched_barrier(0);    // keep the phases' operand reads apart (register pressure)
+    // the next batch's rows load while this one's softmax, P V and stores run
+    if (bt + 4 < nbat) load_q(e_next, qb);
     // own block: keys <= t
     const bool diag = valid && t / kBlk == j;
     float mx = -INFINITY;
@@ -171,8 +173,6 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
     }
     sum += __shfl_xor(sum, 32, 64);
     __builtin_amdgcn_sched_barrier(0);
-    // the next batch's rows load while this one is written out
-    if (bt + 4 < nbat) load_q(e_next, qb);
     // partials of entries p0 + 32 bt + r (the bucket's rows are contiguous):
     // O^T / sum -> LDS row col (16-byte chunk 4 dt + i4 of d at physical
     // chunk (4 dt + i4) ^ (col % kCh)), then kCh lanes store each row
@@ -188,6 +188,11 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
               make_uint2(pack_bf16x2(od[4 * i4] * inv, od[4 * i4 + 1] * inv),
                          pack_bf16x2(od[4 * i4 + 2] * inv, od[4 * i4 + 3] * inv));
         }
+      // Rows past the bucket's end go to the spare entry (`spare`, past
+      // every bucket's): unconditional stores keep every batch's memory
+      // instructions the same, so that the wait for the next batch's rows
+      // does not also wait for these stores.  (Both lanes of a row store the
+      // same log-sum-exp.)
       const int64_t pr0 = static_cast<int64_t>(p0) + bt * 32;
       const int rows_here = min(32, n - bt * 32);
       constexpr int kRowsSt = 64 / kCh;            // rows per store instruction
@@ -195,9 +200,10 @@ __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFw
       for (int i = 0; i < 32 / kRowsSt; ++i) {
         const int r = kRowsSt * i + lane / kCh, pc = lane % kCh;
         const uint4 u = *reinterpret_cast<const uint4*>(&ot[r * kD + 8 * pc]);
-        if (r < rows_here) *reinterpret_cast<uint4*>(a.part_o + (pr0 + r) * kD + 8 * (pc ^ (r & (kCh - 1)))) = u;
+        const int64_t dst = r < rows_here ? pr0 + r : spare;
+        *reinterpret_cast<uint4*>(a.part_o + dst * kD + 8 * (pc ^ (r & (kCh - 1)))) = u;
       }
-      if (valid && g == 0) a.part_lse[pr0 + col] = m + fast_log2(sum);
+      a.part_lse[valid ? pr0 + col : spare] = m + fast_log2(sum);
     }
     e = e_next;
     e_next = e_after;
@@ -316,13 +322,13 @@ void launch_sparse_fwd(const Dims& D, const SparseFwdArgs& a, hipStream_t s) {
     timing_begin(kKSparsePart, s);
     if (D.block == 32)
       hipLaunchKernelGGL((k_sparse_part<1, HD>), grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.nb,
-                         scale_log2);
+                         scale_log2, bucket_capacity(D));
     else if (D.block == 64)
       hipLaunchKernelGGL((k_sparse_part<2, HD>), grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.nb,
-                         scale_log2);
+                         scale_log2, bucket_capacity(D));
     else
       hipLaunchKernelGGL((k_sparse_part<4, HD>), grid, dim3(256), 0, s, a, D.Hq, D.G, D.N, D.Nq, D.q_off, D.nb,
-                         scale_log2);
+                         scale_log2, bucket_capacity(D));
     timing_end(kKSparsePart, s);
     constexpr int kRowsWg = 256 / (HD / 8);
     timing_begin(kKSparseMerge, s);
