@@ -11,7 +11,8 @@
 //
 // Built in four steps, deterministic (no global atomics):
 //   mask:  per (b, h, 32-row tile) of sel, one 32-bit row mask per key block
-//          -> mask[b, c][j][h % G][tile]   (bit r: row 32 tile + r selected j)
+//          -> mask[b, c][j][h % G][tile]   (bit r: row 32 tile + r selected j),
+//          a workgroup building the words of several consecutive tiles;
 //   count: rows per bucket (popcounts of the bucket's masks);
 //   scan:  exclusive prefix of the counts -> offs (one workgroup);
 //   fill:  entries (h % G) * Nq + r of bucket (b, c, j) (r: the query row,
@@ -57,26 +58,40 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int* scratch, int* to
   return base + incl - x;
 }
 
-__global__ void __launch_bounds__(64) k_bucket_mask(const int32_t* __restrict__ sel, uint32_t* __restrict__ mask,
-                                                    int Hq, int G, int Nq, int q_off, int nb, int K, int block) {
-  extern __shared__ uint32_t words[];    // [own block + 1]
-  const int qt = blockIdx.x, bh = blockIdx.y;
-  const int lane = threadIdx.x;
+// One workgroup per T consecutive 32-row tiles of one (b, h): the words of
+// every key block for the T tiles are built in LDS and leave as runs of T
+// consecutive words (the tiles of one block are adjacent in the layout).
+// Words of blocks above a tile's own block are written as zeros; no reader
+// looks at them.
+__global__ void __launch_bounds__(kScanThreads) k_bucket_mask(const int32_t* __restrict__ sel,
+                                                              uint32_t* __restrict__ mask, int Hq, int G, int Nq,
+                                                              int q_off, int nb, int K, int block, int T) {
+  extern __shared__ uint32_t words[];    // [own block of the last tile + 1][T]
+  const int qt0 = blockIdx.x * T, bh = blockIdx.y;
+  const int tid = threadIdx.x;
   const int nqt = Nq / 32;
+  const int nt = min(T, nqt - qt0);      // tiles of this workgroup
   const int b = bh / Hq, h = bh % Hq, Hkv = Hq / G;
   const int c = h / G, hl = h % G;
-  const int t0 = qt * 32;
-  const int own = (q_off + t0) / block;  // block >= 32 divides into whole tiles
-  for (int j = lane; j <= own; j += 64) words[j] = 0u;
+  const int own_last = (q_off + (qt0 + nt - 1) * 32) / block;   // block >= 32 divides into whole tiles
+  const int nw = (own_last + 1) * T;
+  for (int e = tid; e < nw; e += kScanThreads) words[e] = 0u;
   __syncthreads();
-  const int32_t* s = sel + (static_cast<int64_t>(bh) * Nq + t0) * K;
-  for (int e = lane; e < 32 * K; e += 64) {
-    const int blk = s[e];
-    if (blk >= 0 && blk <= own) atomicOr(&words[blk], 1u << (e / K));
+  for (int tt = 0; tt < nt; ++tt) {
+    const int t0 = (qt0 + tt) * 32;
+    const int own = (q_off + t0) / block;
+    const int32_t* s = sel + (static_cast<int64_t>(bh) * Nq + t0) * K;
+    for (int e = tid; e < 32 * K; e += kScanThreads) {
+      const int blk = s[e];
+      if (blk >= 0 && blk <= own) atomicOr(&words[blk * T + tt], 1u << (e / K));
+    }
   }
   __syncthreads();
-  uint32_t* out = mask + ((static_cast<int64_t>(b) * Hkv + c) * nb * G + hl) * nqt + qt;
-  for (int j = lane; j <= own; j += 64) out[static_cast<int64_t>(j) * G * nqt] = words[j];
+  uint32_t* out = mask + ((static_cast<int64_t>(b) * Hkv + c) * nb * G + hl) * nqt + qt0;
+  for (int e = tid; e < nw; e += kScanThreads) {
+    const int j = e / T, tt = e - j * T;
+    if (tt < nt) out[static_cast<int64_t>(j) * G * nqt + tt] = words[e];
+  }
 }
 
 __global__ void __launch_bounds__(kScanThreads) k_bucket_count(const uint32_t* __restrict__ mask,
@@ -96,19 +111,22 @@ __global__ void __launch_bounds__(kScanThreads) k_bucket_count(const uint32_t* _
   if (threadIdx.x == 0) count[static_cast<int64_t>(bc) * nb + j] = total;
 }
 
+// One workgroup: thread t sums its own contiguous run of counts, the runs'
+// sums are scanned once, and each thread writes its run's offsets.
 __global__ void __launch_bounds__(kScanThreads) k_bucket_scan(const int32_t* __restrict__ count,
                                                               int32_t* __restrict__ offs, int n) {
   __shared__ int scratch[4];
-  int carry = 0;
-  for (int i0 = 0; i0 < n; i0 += kScanThreads) {
-    const int i = i0 + static_cast<int>(threadIdx.x);
-    const int x = i < n ? count[i] : 0;
-    int total;
-    const int ex = block_exclusive_scan(x, scratch, &total);
-    if (i < n) offs[i] = carry + ex;
-    carry += total;
+  const int per = (n + kScanThreads - 1) / kScanThreads;
+  const int i0 = min(n, static_cast<int>(threadIdx.x) * per), i1 = min(n, i0 + per);
+  int sum = 0;
+  for (int i = i0; i < i1; ++i) sum += count[i];
+  int total;
+  int run = block_exclusive_scan(sum, scratch, &total);
+  for (int i = i0; i < i1; ++i) {
+    offs[i] = run;
+    run += count[i];
   }
-  if (threadIdx.x == 0) offs[n] = carry;
+  if (threadIdx.x == 0) offs[n] = total;
 }
 
 __global__ void __launch_bounds__(kScanThreads) k_bucket_fill(const uint32_t* __restrict__ mask,
@@ -153,8 +171,13 @@ int64_t bucket_capacity(const Dims& D) {
 void launch_buckets(const Dims& D, const int32_t* sel, const Buckets& bk, hipStream_t s) {
   const int nbk = D.B * D.Hkv * D.nb;
   timing_begin(kKBucket, s);
-  hipLaunchKernelGGL(k_bucket_mask, dim3(D.Nq / 32, D.B * D.Hq), dim3(64), static_cast<size_t>(D.nb) * 4, s, sel,
-                     bk.mask, D.Hq, D.G, D.Nq, D.q_off, D.nb, D.K, D.block);
+  // tiles per mask workgroup: at most 32, and their words within 64 KiB of LDS
+  int T = 1;
+  while (T < 32 && static_cast<int64_t>(D.nb) * (2 * T) * 4 <= 65536) T *= 2;
+  const int nqt = D.Nq / 32;
+  hipLaunchKernelGGL(k_bucket_mask, dim3((nqt + T - 1) / T, D.B * D.Hq), dim3(kScanThreads),
+                     static_cast<size_t>(D.nb) * T * 4, s, sel, bk.mask, D.Hq, D.G, D.Nq, D.q_off, D.nb, D.K,
+                     D.block, T);
   hipLaunchKernelGGL(k_bucket_count, dim3(D.nb, D.B * D.Hkv), dim3(kScanThreads), 0, s, bk.mask, bk.count, D.G,
                      D.Nq, D.q_off, D.nb, D.block);
   hipLaunchKernelGGL(k_bucket_scan, dim3(1), dim3(kScanThreads), 0, s, bk.count, bk.offs, nbk);
