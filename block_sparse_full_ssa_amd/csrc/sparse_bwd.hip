@@ -478,19 +478,27 @@ __global__ void __launch_bounds__(256) k_sparse_dq_merge(const int32_t* __restri
       const int64_t w = ((bc * nb + j) * G + hl) * nqt + qt;
       p = wpos[w] + __popc(mask[w] & below);
     }
+    // every slot's partial loads at once (an absent slot loads entry 0, a
+    // real address, and its contribution is selected away), then the sums
+    // in slot order
     const int nslot = min(LR, Kc - e0);
-    for (int i = 0; i < nslot; ++i) {
-      const int ji = __shfl(j, i, LR);
-      if (ji < 0) continue;
+    uint4 u[LR];
+    bool ok[LR];
+#pragma unroll
+    for (int i = 0; i < LR; ++i) {
+      ok[i] = i < nslot && __shfl(j, i, LR) >= 0;
       const uint32_t plo = __shfl(static_cast<uint32_t>(p), i, LR);
       const uint32_t phi = __shfl(static_cast<uint32_t>(p >> 32), i, LR);
-      const int64_t pi = (static_cast<int64_t>(phi) << 32) | plo;
-      const uint4 u = *reinterpret_cast<const uint4*>(part + pi * kD + 8 * li);
-      const uint32_t wd[4] = {u.x, u.y, u.z, u.w};
+      const int64_t pi = ok[i] ? (static_cast<int64_t>(phi) << 32) | plo : 0;
+      u[i] = *reinterpret_cast<const uint4*>(part + pi * kD + 8 * li);
+    }
+#pragma unroll
+    for (int i = 0; i < LR; ++i) {
+      const uint32_t wd[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
 #pragma unroll
       for (int k2 = 0; k2 < 4; ++k2) {
-        acc[2 * k2] += __uint_as_float(wd[k2] << 16);
-        acc[2 * k2 + 1] += __uint_as_float(wd[k2] & 0xffff0000u);
+        acc[2 * k2] += ok[i] ? __uint_as_float(wd[k2] << 16) : 0.f;
+        acc[2 * k2 + 1] += ok[i] ? __uint_as_float(wd[k2] & 0xffff0000u) : 0.f;
       }
     }
   }

@@ -274,12 +274,27 @@ __global__ void __launch_bounds__(256) k_sparse_merge(SparseFwdArgs a, int64_t r
       const float wt = x[r] == -INFINITY ? 0.f : fast_exp2(x[r] - m);
       L += wt;
       if (LR * r >= Kc) continue;      // uniform
+      // every slot's partial loads at once (an absent slot loads entry 0, a
+      // real address, and its contribution is selected away), then the sums
+      uint4 u[LR];
+      float wv[LR];
 #pragma unroll
       for (int i = 0; i < LR; ++i) {
-        const float wi = __shfl(wt, i, LR);
+        wv[i] = __shfl(wt, i, LR);
         const uint32_t plo = __shfl(static_cast<uint32_t>(p[r]), i, LR);
         const uint32_t phi = __shfl(static_cast<uint32_t>(p[r] >> 32), i, LR);
-        if (wi != 0.f) add((static_cast<int64_t>(phi) << 32) | plo, wi);
+        const int64_t pi = wv[i] != 0.f ? (static_cast<int64_t>(phi) << 32) | plo : 0;
+        u[i] = *reinterpret_cast<const uint4*>(a.part_o + (pi * kD + 8 * li));
+      }
+#pragma unroll
+      for (int i = 0; i < LR; ++i) {
+        const uint32_t wd[4] = {u[i].x, u[i].y, u[i].z, u[i].w};
+#pragma unroll
+        for (int k2 = 0; k2 < 4; ++k2) {
+          const float lo = __uint_as_float(wd[k2] << 16), hi = __uint_as_float(wd[k2] & 0xffff0000u);
+          acc[2 * k2] += wv[i] != 0.f ? wv[i] * lo : 0.f;
+          acc[2 * k2 + 1] += wv[i] != 0.f ? wv[i] * hi : 0.f;
+        }
       }
     }
 #pragma unroll
