@@ -163,6 +163,7 @@ struct BwdWs {
   // MFMA path
   uint16_t *g_full, *g_sparse;
   float *D_full, *D_sparse, *lse2_full, *lse2_sparse;
+  uint4* rowv_full;
   uint16_t* dq_part;          // sparse-only: the sparse stream's partial dQ rows (bucket order)
   Buckets bk;                 // sparse stream
   float *dk_part, *dv_part;   // training modes: the sparse stream's fp32 dK / dV
@@ -176,6 +177,7 @@ static BwdWs carve_bwd(const Dims& D, int mode, Carver& c) {
       w.g_full = c.take<uint16_t>(D.q_elems() * sizeof(uint16_t));
       w.D_full = c.take<float>(D.rows() * sizeof(float));
       w.lse2_full = c.take<float>(D.rows() * sizeof(float));
+      w.rowv_full = c.take<uint4>(D.rows() * sizeof(uint4));
     }
     if (sp) {
       w.g_sparse = c.take<uint16_t>(D.q_elems() * sizeof(uint16_t));
@@ -367,7 +369,7 @@ ssa_status_t ssa_attn_bwd(const ssa_shape_t* shape, int32_t mode, float w_sparsi
     // and the rows of dS), then the full stream's dK / dV and dQ, each adding
     // the sparse stream's part
     BwdPreArgs p{d_out, h_full, h_sparse, lse_full, lse_sparse, w.g_full, w.g_sparse, w.D_full, w.D_sparse,
-                 w.lse2_full, w.lse2_sparse, mode};
+                 w.lse2_full, w.lse2_sparse, w.rowv_full, mode};
     launch_bwd_pre(D, p, w_sparsity, w_commit, s);
     if ((st = launch_status()) != SSA_OK) return st;
     if (mode != kFullOnly) {
@@ -382,7 +384,7 @@ ssa_status_t ssa_attn_bwd(const ssa_shape_t* shape, int32_t mode, float w_sparsi
       launch_sparse_dq_merge(D, sel, w.bk.mask, w.bk.wpos, w.dq_part, dq, s);
       return launch_status();
     }
-    BwdMainArgs m{q, k, v, w.g_full, w.lse2_full, w.D_full, dk, dv, w.dk_part, w.dv_part};
+    BwdMainArgs m{q, k, v, w.g_full, w.rowv_full, dk, dv, w.dk_part, w.dv_part};
     launch_bwd_mfma(D, m, s);
     if ((st = launch_status()) != SSA_OK) return st;
     BwdDqArgs dqa{q, k, v, w.g_full, w.lse2_full, w.D_full, w.ds_rows ? w.bk.mask : nullptr,

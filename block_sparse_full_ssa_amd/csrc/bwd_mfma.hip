@@ -42,10 +42,21 @@ constexpr int kBN = 128;       // keys per workgroup
 constexpr int kBM = 32;        // queries per iteration
 constexpr float kLog2e = 1.4426950408889634f;
 
+// x as three bf16 terms t0 + t1 + t2 (t0 = bf16(x), t1 = bf16(x - t0),
+// t2 = bf16(x - t0 - t1); the residuals are exact in fp32, so the sum equals
+// x up to 2^-24 |x|), packed {t0 | t1 << 16, t2}
+__device__ __forceinline__ uint2 split3_bf16(float x) {
+  const float t0 = to_f32(to_bf16(x));
+  const float r1 = x - t0;
+  const float t1 = to_f32(to_bf16(r1));
+  const float t2 = to_f32(to_bf16(r1 - t1));
+  return make_uint2(pack_bf16x2(t0, t1), pack_bf16x2(t2, 0.f));
+}
+
 // ---------------------------------------------------------------- bwd_pre --
 template <int HD>   // head dimension
 __global__ void __launch_bounds__(256)
-    k_bwd_pre(BwdPreArgs a, int64_t rows, float w_f, float w_s_align, float inv_m) {
+    k_bwd_pre(BwdPreArgs a, int64_t rows, float w_f, float w_s_align, float inv_m, float scale_log2) {
   // LR = HD / 8 lanes per row, 8 elements (16 bytes) each; 256 / LR rows per workgroup
   constexpr int kD = HD, LR = HD / 8;
   const int li = threadIdx.x % LR;
@@ -104,8 +115,11 @@ __global__ void __launch_bounds__(256)
   if (has_s) *reinterpret_cast<uint4*>(a.g_sparse + off) = make_uint4(gsw[0], gsw[1], gsw[2], gsw[3]);
   if (li == 0) {
     if (has_f) {
+      const float l2 = a.lse_full[row] * kLog2e;
       a.D_full[row] = Df;
-      a.lse2_full[row] = a.lse_full[row] * kLog2e;
+      a.lse2_full[row] = l2;
+      const uint2 tl = split3_bf16(-l2 * (1.f / scale_log2)), td = split3_bf16(-Df);
+      a.rowv_full[row] = make_uint4(tl.x, tl.y, td.x, td.y);
     }
     if (has_s) {
       a.D_sparse[row] = Ds;
@@ -228,30 +242,20 @@ __global__ void __launch_bounds__(256, 2)
                                        0);
     }
   };
-  // Row values of the 32 queries: lane l holds lse2 and D of query l % 32.
-  // They enter the logits and dP through the accumulators: one extra matrix
-  // product each starts S at -lse2 / c and dP at -D (A: the value split into
-  // three bf16 terms in the k-slots 0..2 of the lanes of k-group 0, exact in
-  // fp32; B: ones in the same slots), so no per-element row value has to be
-  // fetched for the softmax and dS.
-  float rl = 0.f, rd = 0.f, rl_n = 0.f, rd_n = 0.f;
+  // Row values of the 32 queries: lane l holds those of query l % 32.  They
+  // enter the logits and dP through the accumulators: one extra matrix
+  // product each starts S at -lse2 / c and dP at -D (A: the value's three
+  // bf16 terms, written by bwd_pre, in the k-slots 0..2; B: ones in the same
+  // slots of the lanes of k-group 0 and zeros elsewhere, so the k-group 1
+  // lanes' copies of the terms add nothing), so no per-element row value has
+  // to be fetched for the softmax and dS.
+  u32x4 rv = u32x4{0u, 0u, 0u, 0u}, rv_n = rv;
   auto load_rows = [&](int hq, int q0) {
     const int64_t r = (static_cast<int64_t>(b) * Hq + hq) * N + q0 + col;
-    rl_n = a.lse2_full[r];
-    rd_n = a.D_full[r];
-  };
-  auto split3 = [&](float x) -> bf16x8 {
-    const float t0 = to_f32(to_bf16(x));
-    const float r1 = x - t0;
-    const float t1 = to_f32(to_bf16(r1));
-    const float t2 = to_f32(to_bf16(r1 - t1));
-    uint4 u = make_uint4(pack_bf16x2(t0, t1), pack_bf16x2(t2, 0.f), 0u, 0u);
-    if (g) u = make_uint4(0u, 0u, 0u, 0u);
-    return __builtin_bit_cast(bf16x8, u);
+    rv_n = *reinterpret_cast<const u32x4*>(a.rowv_full + r);
   };
   const bf16x8 ones = __builtin_bit_cast(bf16x8, g ? make_uint4(0u, 0u, 0u, 0u)
                                                    : make_uint4(0x3F803F80u, 0x00003F80u, 0u, 0u));
-  const float inv_c = 1.f / scale_log2;
 
   f32x16 dv[kDT], dk[kDT];
 #pragma unroll
@@ -264,8 +268,7 @@ __global__ void __launch_bounds__(256, 2)
   auto step = [&](int it, int q0, int hq1, int q01, const uint16_t* Qs, const uint16_t* Fs, uint16_t* Qn,
                   uint16_t* Fn) {
     const bool more = it + 1 < iters;
-    rl = rl_n;
-    rd = rd_n;
+    rv = rv_n;
     if (more) {
       load_rows(hq1, q01);    // plain loads first: no VMEM load may follow the copies
       load_tiles(hq1, q01, Qn, Fn);
@@ -287,8 +290,8 @@ __global__ void __launch_bounds__(256, 2)
       // ---- S = Q K^T, dP = G_f V^T  [32 q x 32 keys], two independent
       // accumulation chains interleaved, operands read one step ahead; lane:
       // key col, queries 8(i/4)+4g+(i%4)
-      f32x16 s = mfma32x32x16(split3(-rl * inv_c), ones, f32x16{});
-      f32x16 dpf = mfma32x32x16(split3(-rd), ones, f32x16{});
+      f32x16 s = mfma32x32x16(__builtin_bit_cast(bf16x8, u32x4{rv[0], rv[1], 0u, 0u}), ones, f32x16{});
+      f32x16 dpf = mfma32x32x16(__builtin_bit_cast(bf16x8, u32x4{rv[2], rv[3], 0u, 0u}), ones, f32x16{});
       bf16x8 ok[8], oq[8], of[8];
       auto rd = [&](int ds) {
         // the same chunk for query row col and key row 32 kq + col
@@ -422,8 +425,11 @@ void launch_bwd_pre(const Dims& D, const BwdPreArgs& a, float w_sparsity, float 
   const int rows_wg = D.d == 64 ? 32 : 16;
   dim3 grid(static_cast<unsigned>((D.rows() + rows_wg - 1) / rows_wg));
   timing_begin(kKBwdPre, s);
-  if (D.d == 64) hipLaunchKernelGGL(k_bwd_pre<64>, grid, dim3(256), 0, s, a, D.rows(), w_sparsity, w_commit, inv_m);
-  else hipLaunchKernelGGL(k_bwd_pre<128>, grid, dim3(256), 0, s, a, D.rows(), w_sparsity, w_commit, inv_m);
+  const float scale_log2 = D.scale * kLog2e;
+  if (D.d == 64)
+    hipLaunchKernelGGL(k_bwd_pre<64>, grid, dim3(256), 0, s, a, D.rows(), w_sparsity, w_commit, inv_m, scale_log2);
+  else
+    hipLaunchKernelGGL(k_bwd_pre<128>, grid, dim3(256), 0, s, a, D.rows(), w_sparsity, w_commit, inv_m, scale_log2);
   timing_end(kKBwdPre, s);
 }
 

@@ -110,13 +110,18 @@ struct BwdPreArgs {
   uint16_t *g_full, *g_sparse;      // bf16 stream gradients [rows][d]
   float *D_full, *D_sparse;         // rowsum(G o h)
   float *lse2_full, *lse2_sparse;   // lse * log2(e)
+  // per row of the full stream, the dK / dV kernel's row operands: -lse2 / c
+  // (c = scale * log2(e)) and -D, each split into three bf16 terms t0, t1, t2
+  // with t0 + t1 + t2 equal to the value up to 2^-24 of it, stored as
+  // {t0 | t1 << 16, t2} per value
+  uint4* rowv_full;
   int mode;
 };
 // Full-stream backward: G_f, D_f, lse2_f of every row.
 struct BwdMainArgs {                // dK, dV
   const void *q, *k, *v;
   const uint16_t* g_full;
-  const float *lse2_full, *D_full;
+  const uint4* rowv_full;           // BwdPreArgs::rowv_full
   void *dk, *dv;
   const float *dk_part, *dv_part;   // fp32 sparse-stream dK / dV to add (training modes) or null
 };

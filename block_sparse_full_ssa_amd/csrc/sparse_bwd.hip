@@ -194,7 +194,6 @@ __global__ void __launch_bounds__(128 * KH, 2)
   constexpr int kRowsOp = 512 / HD, kOpsT = HD / 16;
   static_assert((2 * kOpsT) % kW == 0, "tile copies must split evenly over the waves");
   constexpr int kPer = 2 * kOpsT / kW;
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // (a native vector stays in registers)
   auto copy_src = [&](int R, int u) {
     const int nn = u * kW + wave;               // uniform
     const int which = nn / kOpsT, n8 = nn % kOpsT;
