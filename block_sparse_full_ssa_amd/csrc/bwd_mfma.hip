@@ -263,6 +263,40 @@ __global__ void __launch_bounds__(256, 2)
     dv[dt] = f32x16{};
     dk[dt] = f32x16{};
   }
+  // Byte offsets of the row reads of d-step ds: the same chunk of query row
+  // col in the Q / G_f tiles and of key row 32 kq + col in K.  HD = 128:
+  // those of d-steps 0..3 are computed once and held in registers; d-step
+  // ds + 4 flips bit 7 of d-step ds's (the chunk index ds ^ (col % 8) flips
+  // its bit 2), and the key row's adds kq_off, whose bits (>= 13) the query
+  // offsets (< 8192) never use, so an OR.
+  constexpr int kRO = HD == 128 ? 4 : kD / 16;
+  int roff[kRO];
+#pragma unroll
+  for (int ds = 0; ds < kRO; ++ds)
+    roff[ds] = 2 * (HD == 128 ? col * kD + 8 * (g ^ ((col >> 3) & 1)) + 16 * (ds ^ (col & 7))
+                              : col * kD + 8 * swz_t<HD>(col, 2 * ds + g));
+  const int kq_off = 2 * 32 * kq * kD;              // uniform
+  auto qoff = [&](int ds) { return HD == 128 ? (ds < 4 ? roff[ds] : roff[ds - 4] ^ 128) : roff[ds]; };
+  auto koff = [&](int ds) { return HD == 128 ? qoff(ds) | kq_off : roff[ds] + kq_off; };
+  // Byte offsets of the transpose reads (HD = 128): those of k-step st and
+  // column tile dt are trb[0] ^ 64 dt and trb[1] ^ 64 dt (rows eight apart)
+  // plus 4096 st.  In elements a row's read sits at tb + 32 (dt ^ tx), and tb
+  // leaves bits 5 and 6 clear, so that equals (tb | 32 tx) ^ 32 dt.
+  int trb[2] = {0, 0};
+  if constexpr (HD == 128) {
+    const int tx = 2 * gk + (srow >> 1);
+    const int tb0 = (4 * gk + srow) * kD + 8 * ((2 * (grp & 1) + (m4 >> 1)) ^ (2 * (srow & 1))) + 4 * (m4 & 1);
+    const int tb1 = tb0 + 8 * kD + 8 * (1 - 2 * ((m4 >> 1) & 1));
+    trb[0] = 2 * (tb0 | 32 * tx);
+    trb[1] = 2 * (tb1 | 32 * tx);
+  }
+  auto tr16 = [](const uint16_t* base, int o0, int o1) {
+    const char* b8 = reinterpret_cast<const char*>(base);
+    return lds_tr_pair(reinterpret_cast<const uint16_t*>(b8 + o0), reinterpret_cast<const uint16_t*>(b8 + o1));
+  };
+  auto rd16 = [](const uint16_t* base, int off) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + off));
+  };
 
   // one iteration on set (Qs, Fs) while the next streams into (Qn, Fn)
   auto step = [&](int it, int q0, int hq1, int q01, const uint16_t* Qs, const uint16_t* Fs, uint16_t* Qn,
@@ -277,28 +311,22 @@ __global__ void __launch_bounds__(256, 2)
     const bool diag = q0 < kw0 + 31;                               // some key > some query
 
     if (wave_has_pairs) {
-      // LDS offsets, rebuilt from lane constants in every iteration.  Row
-      // reads of d-step ds: base + 16 (ds ^ (col % 8)); transpose reads of
-      // (st, dt): tb + 2048 st + 32 (dt ^ tx), the second row eight below at tb1
-      int c7 = col & 7, tx = 2 * gk + (srow >> 1);
-      asm volatile("" : "+v"(c7), "+v"(tx));
-      // (HD = 128: the swizzle folded into these offsets; HD = 64 calls it)
-      const int rowq = HD == 128 ? col * kD + 8 * (g ^ ((col >> 3) & 1)) : col * kD;
-      const int rowk = HD == 128 ? (32 * kq + col) * kD + 8 * (g ^ ((col >> 3) & 1)) : (32 * kq + col) * kD;
-      const int tb0 = (4 * gk + srow) * kD + 8 * ((2 * (grp & 1) + (m4 >> 1)) ^ (2 * (srow & 1))) + 4 * (m4 & 1);
-      const int tb1 = tb0 + 8 * kD + 8 * (1 - 2 * ((m4 >> 1) & 1));
       // ---- S = Q K^T, dP = G_f V^T  [32 q x 32 keys], two independent
       // accumulation chains interleaved, operands read one step ahead; lane:
       // key col, queries 8(i/4)+4g+(i%4)
       f32x16 s = mfma32x32x16(__builtin_bit_cast(bf16x8, u32x4{rv[0], rv[1], 0u, 0u}), ones, f32x16{});
       f32x16 dpf = mfma32x32x16(__builtin_bit_cast(bf16x8, u32x4{rv[2], rv[3], 0u, 0u}), ones, f32x16{});
       bf16x8 ok[8], oq[8], of[8];
+      // (opaque to the compiler, so that the derived offsets are rebuilt
+      // here rather than hoisted out of the loop into more registers)
+#pragma unroll
+      for (int i = 0; i < kRO; ++i) asm volatile("" : "+v"(roff[i]));
+      if constexpr (HD == 128) asm volatile("" : "+v"(trb[0]), "+v"(trb[1]));
       auto rd = [&](int ds) {
-        // the same chunk for query row col and key row 32 kq + col
-        const int cs = HD == 128 ? 16 * (ds ^ c7) : 8 * swz_t<HD>(col, 2 * ds + g);
-        ok[ds] = lds_read8(&Kt[rowk + cs]);
-        oq[ds] = lds_read8(&Qs[rowq + cs]);
-        of[ds] = lds_read8(&Fs[rowq + cs]);
+        const int o = qoff(ds);
+        ok[ds] = rd16(Kt, koff(ds));
+        oq[ds] = rd16(Qs, o);
+        of[ds] = rd16(Fs, o);
       };
       rd(0);
 #pragma unroll
@@ -345,9 +373,10 @@ __global__ void __launch_bounds__(256, 2)
       // step u: k-step st = u / kDT (16 queries), column tile dt = u % kDT
       auto rdB = [&](int u) {
         if constexpr (HD == 128) {
-          const int cx = 2048 * (u >> 2) + 32 * ((u & 3) ^ tx);
-          tg[u] = lds_tr_pair(&Fs[tb0 + cx], &Fs[tb1 + cx]);
-          tq[u] = lds_tr_pair(&Qs[tb0 + cx], &Qs[tb1 + cx]);
+          const int x0 = (trb[0] ^ (64 * (u & 3))) + 4096 * (u >> 2);
+          const int x1 = (trb[1] ^ (64 * (u & 3))) + 4096 * (u >> 2);
+          tg[u] = tr16(Fs, x0, x1);
+          tq[u] = tr16(Qs, x0, x1);
         } else {
           const int r0 = 16 * (u / kDT) + 4 * gk + srow, r1 = r0 + 8;
           const int cl = 4 * (u % kDT) + 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
