@@ -21,7 +21,7 @@
 //
 // The head dimension HD (64 or 128) is a template parameter.  K/V tiles of
 // 64 keys (32 for the full stream alone at HD = 128) move from HBM straight
-// into LDS (global_load_lds, 16 bytes per lane), double-buffered, one barrier
+// into LDS (buffer loads to LDS, 16 bytes per lane), double-buffered, one barrier
 // per tile.  16-byte chunks are XOR-swizzled within each row so that
 // the matrix-operand reads of K rows and the transpose reads of V columns
 // avoid bank conflicts.
@@ -63,7 +63,6 @@ constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kTau = 8.f;      // lazy-rescale threshold (log2 units)
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
 
 
 // Physical 16-byte chunk of logical chunk c in row r: K tiles are only read
@@ -169,21 +168,29 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
   // HBM -> LDS copy of one K/V tile: each wave moves a quarter of its rows,
   // one 1 KiB instruction per kRowsOp rows; lane l fills physical chunk
   // l % (HD / 8) of row kRowsOp n + l / (HD / 8), so it fetches the logical chunk
-  // stored there.  Keys past the end read the last key: finite values that the
-  // causal mask removes.
+  // stored there (byte offsets within the tile, fixed per lane).  Keys past the
+  // end lie outside the tile's buffer resource and read zeros, which the causal
+  // mask removes.
   constexpr int kRowsOp = 512 / HD;             // rows of one 1 KiB copy
   constexpr int kOps = kBN / kRowsOp / 4;      // copies per wave and tile
+  uint32_t koff[kOps], voff[kOps];
+#pragma unroll
+  for (int r = 0; r < kOps; ++r) {
+    const int row = kRowsOp * (wave * kOps + r) + lane / (HD / 8);
+    const int p = lane % (HD / 8);
+    koff[r] = 2 * (row * HD + 8 * swz_k<HD>(row, p));
+    voff[r] = 2 * (row * HD + 8 * swz_v<HD>(row, p));
+  }
   auto load_tile = [&](int j, uint16_t* Kd, uint16_t* Vd) {
+    const int k0 = j * kBN;
+    const uint32_t bytes = static_cast<uint32_t>(min(kBN, N - k0)) * (HD * 2);
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kg + static_cast<int64_t>(k0) * HD, bytes);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vg + static_cast<int64_t>(k0) * HD, bytes);
 #pragma unroll
     for (int r = 0; r < kOps; ++r) {
       const int n = wave * kOps + r;
-      const int row = kRowsOp * n + lane / (HD / 8);
-      const int p = lane % (HD / 8);
-      const int64_t key = min(j * kBN + row, N - 1);
-      const uint16_t* srck = kg + key * HD + 8 * swz_k<HD>(row, p);
-      const uint16_t* srcv = vg + key * HD + 8 * swz_v<HD>(row, p);
-      __builtin_amdgcn_global_load_lds((const glb_void*)srck, (lds_void*)(Kd + n * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const glb_void*)srcv, (lds_void*)(Vd + n * 512), 16, 0, 0);
+      buffer_to_lds16(rk, Kd + n * 512, koff[r]);
+      buffer_to_lds16(rv, Vd + n * 512, voff[r]);
     }
   };
 

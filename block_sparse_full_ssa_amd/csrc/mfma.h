@@ -31,6 +31,27 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
+// HBM -> LDS copies of 16 bytes per lane through a buffer resource: the
+// tile's base address and its size in bytes sit in the (uniform) resource and
+// each lane's byte offset in one register, so a copy costs no per-lane 64-bit
+// address arithmetic.  A lane whose offset is at or past the size reads zeros.
+// (The resource's last word is the raw 32-bit-format value for gfx9-family
+// chips.)
+typedef __attribute__((address_space(3))) void lds_void_t;
+// base and bytes must be the same on every lane; they are read from the first
+// lane, so that the resource is built in scalar registers (a resource the
+// compiler cannot prove uniform costs a loop over the lanes at every copy).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(a >> 32));
+  void* p = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(p, 0, static_cast<int>(__builtin_amdgcn_readfirstlane(bytes)), 0x00020000);
+}
+__device__ __forceinline__ void buffer_to_lds16(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)(lds), 16, voff, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -67,7 +67,7 @@ def masked_transposes(asm: str):
 def device_asm(source: str) -> str:
     with tempfile.TemporaryDirectory() as d:
         out = os.path.join(d, "k.s")
-        cmd = [_build.hipcc(), *_build.HIPCC_FLAGS, "-S", "--cuda-device-only",
+        cmd = [_build.hipcc(), *_build.flags_for(source), "-S", "--cuda-device-only",
                os.path.join(_build.CSRC, source), "-o", out]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
