@@ -36,8 +36,6 @@ namespace {
 constexpr int kBM = 128;         // queries per workgroup
 constexpr int kBN = 64;          // keys per tile
 
-typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void glb_void;
 
 // Physical 16-byte chunk of logical chunk c in a K / V row r of 2 HD bytes (K
 // is read by rows and by transposes).
@@ -105,21 +103,27 @@ __global__ void __launch_bounds__(256, 2)
 
   // HBM -> LDS copy of one K/V tile: each wave moves a quarter of its rows,
   // one 1 KiB instruction per kRowsOp rows; lane l fills physical chunk
-  // l % (HD / 8) of row kRowsOp n + l / (HD / 8).  Keys past the end read the
-  // last key (masked later).
+  // l % (HD / 8) of row kRowsOp n + l / (HD / 8) (byte offsets within the
+  // tile, fixed per lane).  Keys past the end lie outside the tile's buffer
+  // resource and read zeros (masked later).
   constexpr int kRowsOp = 512 / HD;
   constexpr int kOps = kBN / kRowsOp / 4;
+  uint32_t toff[kOps];
+#pragma unroll
+  for (int r = 0; r < kOps; ++r) {
+    const int rw = kRowsOp * (wave * kOps + r) + lane / (HD / 8);
+    toff[r] = 2 * (rw * kD + 8 * swz_k<HD>(rw, lane % (HD / 8)));
+  }
   auto load_tile = [&](int j, uint16_t* Kd, uint16_t* Vd) {
+    const int k0 = j * kBN;
+    const uint32_t bytes = static_cast<uint32_t>(min(kBN, N - k0)) * (kD * 2);
+    const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kg + static_cast<int64_t>(k0) * kD, bytes);
+    const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vg + static_cast<int64_t>(k0) * kD, bytes);
 #pragma unroll
     for (int r = 0; r < kOps; ++r) {
       const int n = wave * kOps + r;
-      const int rw = kRowsOp * n + lane / (HD / 8);
-      const int p = lane % (HD / 8);
-      const int64_t key = min(j * kBN + rw, N - 1);
-      __builtin_amdgcn_global_load_lds((const glb_void*)(kg + key * kD + 8 * swz_k<HD>(rw, p)),
-                                       (lds_void*)(Kd + n * 512), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const glb_void*)(vg + key * kD + 8 * swz_k<HD>(rw, p)),
-                                       (lds_void*)(Vd + n * 512), 16, 0, 0);
+      buffer_to_lds16(rk, Kd + n * 512, toff[r]);
+      buffer_to_lds16(rv, Vd + n * 512, toff[r]);
     }
   };
 
@@ -172,17 +176,19 @@ __global__ void __launch_bounds__(256, 2)
   };
   // SP = 2: the dS rows of the wave's selected queries of a tile (its mask
   // word and entry position, uniform) -> LDS, at most kSDRows of them; the
-  // source is clamped to the buffer (rows past the tile's are never read)
+  // resource ends with the buffer, so parts past it read zeros (rows past
+  // the tile's are never read)
   auto copy_rows = [&](uint32_t word, int pos, uint16_t* SDd) {
     uint16_t* dst = SDd + wave * kSDRows * kBN;
     const int cnt = __builtin_popcount(word);
     const int64_t base = static_cast<int64_t>(pos) * kBN;
+    const int64_t left = ds_elems - base;          // elements from the first row to the buffer's end
+    const int64_t span = left < kSDRows * kBN ? (left > 0 ? left : 0) : kSDRows * kBN;
+    const __amdgpu_buffer_rsrc_t rr = tile_rsrc(a.ds_rows + base, static_cast<uint32_t>(span) * 2);
 #pragma unroll
     for (int u = 0; u < (kSDRows * kBN * 2 + 1023) / 1024; ++u) {
-      if (u * 8 < cnt && u * 1024 + 16 * lane < kSDRows * kBN * 2) {
-        const int64_t off = min(base + u * 512 + 8 * lane, ds_elems - 8);
-        __builtin_amdgcn_global_load_lds((const glb_void*)(a.ds_rows + off), (lds_void*)(dst + u * 512), 16, 0, 0);
-      }
+      if (u * 8 < cnt && u * 1024 + 16 * lane < kSDRows * kBN * 2)
+        buffer_to_lds16(rr, dst + u * 512, static_cast<uint32_t>(u * 1024 + 16 * lane));
     }
   };
   auto step = [&](int j, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn, const uint16_t* SDs,

@@ -231,15 +231,14 @@ __global__ void __launch_bounds__(256, 2)
     dmo[r] = 2 * (row * kD + 8 * swz_t<HD>(row, lane % kCh));
   }
   auto load_tiles = [&](int hq, int q0, uint16_t* Qd, uint16_t* Fd) {
-    const int64_t tile = ((static_cast<int64_t>(b) * Hq + hq) * N + q0) * (kD * 2);
+    const int64_t tile = ((static_cast<int64_t>(b) * Hq + hq) * N + q0) * kD;
+    const __amdgpu_buffer_rsrc_t rq = tile_rsrc(static_cast<const uint16_t*>(a.q) + tile, kT * 2);
+    const __amdgpu_buffer_rsrc_t rg = tile_rsrc(a.g_full + tile, kT * 2);
 #pragma unroll
     for (int r = 0; r < kOpsW; ++r) {
       const int n = wave * kOpsW + r;               // uniform
       const bool gt = n >= kOpsT;                   // the G tile's half of the copies
-      const char* src = static_cast<const char*>(gt ? a.g_full : a.q) + tile;
-      uint16_t* dst = gt ? Fd : Qd;
-      __builtin_amdgcn_global_load_lds((const glb_void*)(src + dmo[r]), (lds_void*)(dst + (n % kOpsT) * 512), 16, 0,
-                                       0);
+      buffer_to_lds16(gt ? rg : rq, (gt ? Fd : Qd) + (n % kOpsT) * 512, dmo[r]);
     }
   };
   // Row values of the 32 queries: lane l holds those of query l % 32.  They

@@ -62,7 +62,6 @@ template <int MODE, int D> struct FwdTile {
 constexpr float kLn2 = 0.69314718055994531f;
 constexpr float kTau = 8.f;      // lazy-rescale threshold (log2 units)
 
-typedef __attribute__((address_space(3))) void lds_void;
 
 
 // Physical 16-byte chunk of logical chunk c in row r: K tiles are only read
