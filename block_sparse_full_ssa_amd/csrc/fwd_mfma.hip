@@ -271,19 +271,11 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
         }
       }
       // P enters the products in bf16: round it here, and let the row sum
-      // add exactly those weights (s keeps the rounded values)
+      // add exactly those weights
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < 2; ++st)
         pf[st] = to_bf16x8_sum(s[8 * st], s[8 * st + 1], s[8 * st + 2], s[8 * st + 3], s[8 * st + 4],
                                s[8 * st + 5], s[8 * st + 6], s[8 * st + 7], sum);
-        const uint4 u = __builtin_bit_cast(uint4, pf[st]);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          s[8 * st + 2 * k] = __uint_as_float(w[k] << 16);
-          s[8 * st + 2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
-        }
-      }
       if (STATS) {
         // the diagnostics use the unrounded weights: moving the maximum by
         // dm = mfn - mf shifts every earlier x by -dm and scales every earlier
@@ -300,16 +292,17 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
       mf = mfn;
       if (kSparse && sparse_any) {
         if (rescale) {
-          // exact: the factor is a power of two, so the row sum is the full
-          // stream's sum of this half times it, bit for bit
+          // the factor c is a power of two, so each product s c is exact and
+          // rounds to the full stream's rounded weight times c (c = 1 when
+          // both maxima agree: then the weights and the sum are the full
+          // stream's, bit for bit); the row sum adds the rounded weights
           const float c = sb ? fast_exp2(mfn - msn) : 0.f;
-          sum_s = sum * c;
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
             float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) p[e] = s[8 * st + e] * c;
-            ps[st] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
+            ps[st] = to_bf16x8_sum(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], sum_s);
           }
         }
         ls = ls * alpha_s + sum_s;
