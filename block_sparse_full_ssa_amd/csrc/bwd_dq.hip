@@ -38,13 +38,10 @@ constexpr int kBN = 64;          // keys per tile
 
 
 // Physical 16-byte chunk of logical chunk c in a K / V row r of 2 HD bytes (K
-// is read by rows and by transposes).
-// 256-byte rows (HD = 128): c ^ (2 (r % 8) + (r / 8) % 2), measured on gfx950
-// to keep the transpose reads (ds_read_b64_tr_b16) free of bank conflicts as
-// well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave the
-// transpose reads two-way conflicted.  128-byte rows (HD = 64): c ^ (r % 8).
+// is read by rows and by transposes): swz256 for 256-byte rows (HD = 128),
+// c ^ (r % 8) for 128-byte rows (HD = 64).
 template <int HD> __device__ __forceinline__ int swz_k(int r, int c) {
-  return HD == 128 ? c ^ (((r & 7) << 1) | ((r >> 3) & 1)) : c ^ (r & 7);
+  return HD == 128 ? swz256(r, c) : c ^ (r & 7);
 }
 
 // SP: 0 the full stream alone; 1 with the sparse stream's dS rows through
@@ -191,6 +188,23 @@ __global__ void __launch_bounds__(256, 2)
         buffer_to_lds16(rr, dst + u * 512, static_cast<uint32_t>(u * 1024 + 16 * lane));
     }
   };
+  // HD = 128: byte offsets of the K / V row reads of d-steps 0..3 (key row
+  // col; rows 32 further share the swizzle, and d-step ds + 4 flips bit 7:
+  // its logical chunk 2 ds + g flips bit 3, and so does the physical one) and
+  // of the K^T transpose reads of rows 4 gk + srow and 8 further (column tile
+  // dt: an XOR of 64 dt, the swizzle's 32 srow kept apart on bits 5 and 6,
+  // which the rest leaves clear), held in registers
+  int roff[4] = {0, 0, 0, 0}, tk[2] = {0, 0};
+  if constexpr (HD == 128) {
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) roff[ds] = 2 * (col * kD + 8 * swz_k<HD>(col, 2 * ds + g));
+    const int y = 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
+    tk[0] = 2 * ((4 * gk + srow) * kD + 8 * (y ^ gk) + e4 + 32 * srow);
+    tk[1] = 2 * ((4 * gk + srow + 8) * kD + 8 * (y ^ (gk + 2)) + e4 + 32 * srow);
+  }
+  auto rd16 = [](const uint16_t* base, int off) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + off));
+  };
   auto step = [&](int j, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn, const uint16_t* SDs,
                   uint16_t* SDn) {
     if constexpr (SPARSE) {
@@ -231,9 +245,15 @@ __global__ void __launch_bounds__(256, 2)
           const int r = kh * 32 + col;
           bf16x8 ok[kD / 16], ov[kD / 16];
           auto rd = [&](int ds) {
-            const int off = r * kD + 8 * swz_k<HD>(r, 2 * ds + g);
-            ok[ds] = lds_read8(&Ks[off]);
-            ov[ds] = lds_read8(&Vs[off]);
+            if constexpr (HD == 128) {
+              const int o = (ds < 4 ? roff[ds] : roff[ds - 4] ^ 128) + 2 * kD * kh * 32;
+              ok[ds] = rd16(Ks, o);
+              ov[ds] = rd16(Vs, o);
+            } else {
+              const int off = r * kD + 8 * swz_k<HD>(r, 2 * ds + g);
+              ok[ds] = lds_read8(&Ks[off]);
+              ov[ds] = lds_read8(&Vs[off]);
+            }
           };
           rd(0);
 #pragma unroll
@@ -299,9 +319,16 @@ __global__ void __launch_bounds__(256, 2)
                               dsv[8 * st + 5], dsv[8 * st + 6], dsv[8 * st + 7]);
         auto rdk = [&](int u) {
           const int st = u / kDT, dt = u % kDT;
-          const int r0 = kh * 32 + st * 16 + 4 * gk + srow, r1 = r0 + 8;
-          const int c = 4 * dt + 2 * (grp & 1) + (m4 >> 1), e = 4 * (m4 & 1);
-          ka[u] = lds_tr_pair(&Ks[r0 * kD + 8 * swz_k<HD>(r0, c) + e], &Ks[r1 * kD + 8 * swz_k<HD>(r1, c) + e]);
+          if constexpr (HD == 128) {
+            const int rb = 2 * kD * (kh * 32 + st * 16);
+            const char* kb = reinterpret_cast<const char*>(Ks);
+            ka[u] = lds_tr_pair(reinterpret_cast<const uint16_t*>(kb + ((tk[0] ^ (64 * dt)) + rb)),
+                                reinterpret_cast<const uint16_t*>(kb + ((tk[1] ^ (64 * dt)) + rb)));
+          } else {
+            const int r0 = kh * 32 + st * 16 + 4 * gk + srow, r1 = r0 + 8;
+            const int c = 4 * dt + 2 * (grp & 1) + (m4 >> 1), e = 4 * (m4 & 1);
+            ka[u] = lds_tr_pair(&Ks[r0 * kD + 8 * swz_k<HD>(r0, c) + e], &Ks[r1 * kD + 8 * swz_k<HD>(r1, c) + e]);
+          }
         };
         rdk(0);
 #pragma unroll

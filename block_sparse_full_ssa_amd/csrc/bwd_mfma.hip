@@ -130,13 +130,10 @@ __global__ void __launch_bounds__(256)
 
 // --------------------------------------------------------------- bwd_mfma --
 // Physical 16-byte chunk of logical chunk c in a K / Q / G row r of 2 HD bytes
-// (read by rows and by transposes).
-// 256-byte rows (HD = 128): c ^ (2 (r % 8) + (r / 8) % 2), measured on gfx950
-// to keep the transpose reads (ds_read_b64_tr_b16) free of bank conflicts as
-// well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave the
-// transpose reads two-way conflicted.  128-byte rows (HD = 64): c ^ (r % 8).
+// (read by rows and by transposes): swz256 for 256-byte rows (HD = 128),
+// c ^ (r % 8) for 128-byte rows (HD = 64).
 template <int HD> __device__ __forceinline__ int swz_t(int r, int c) {
-  return HD == 128 ? c ^ (((r & 7) << 1) | ((r >> 3) & 1)) : c ^ (r & 7);
+  return HD == 128 ? swz256(r, c) : c ^ (r & 7);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -263,31 +260,32 @@ __global__ void __launch_bounds__(256, 2)
     dk[dt] = f32x16{};
   }
   // Byte offsets of the row reads of d-step ds: the same chunk of query row
-  // col in the Q / G_f tiles and of key row 32 kq + col in K.  HD = 128:
-  // those of d-steps 0..3 are computed once and held in registers; d-step
-  // ds + 4 flips bit 7 of d-step ds's (the chunk index ds ^ (col % 8) flips
-  // its bit 2), and the key row's adds kq_off, whose bits (>= 13) the query
+  // col in the Q / G_f tiles and of key row 32 kq + col in K (the same
+  // swizzle: rows 16 apart share it).  HD = 128: those of d-steps 0..3 are
+  // computed once and held in registers; d-step ds + 4 flips bit 7 of d-step
+  // ds's (its logical chunk 2 ds + g flips bit 3, and so does the physical
+  // one), and the key row's adds kq_off, whose bits (>= 13) the query
   // offsets (< 8192) never use, so an OR.
   constexpr int kRO = HD == 128 ? 4 : kD / 16;
   int roff[kRO];
 #pragma unroll
   for (int ds = 0; ds < kRO; ++ds)
-    roff[ds] = 2 * (HD == 128 ? col * kD + 8 * (g ^ ((col >> 3) & 1)) + 16 * (ds ^ (col & 7))
-                              : col * kD + 8 * swz_t<HD>(col, 2 * ds + g));
+    roff[ds] = 2 * (col * kD + 8 * swz_t<HD>(col, 2 * ds + g));
   const int kq_off = 2 * 32 * kq * kD;              // uniform
   auto qoff = [&](int ds) { return HD == 128 ? (ds < 4 ? roff[ds] : roff[ds - 4] ^ 128) : roff[ds]; };
   auto koff = [&](int ds) { return HD == 128 ? qoff(ds) | kq_off : roff[ds] + kq_off; };
   // Byte offsets of the transpose reads (HD = 128): those of k-step st and
   // column tile dt are trb[0] ^ 64 dt and trb[1] ^ 64 dt (rows eight apart)
-  // plus 4096 st.  In elements a row's read sits at tb + 32 (dt ^ tx), and tb
-  // leaves bits 5 and 6 clear, so that equals (tb | 32 tx) ^ 32 dt.
+  // plus 4096 st.  The lane reads logical chunk 4 dt + y (y = 2 (grp % 2) +
+  // m4 / 2) of row r = 16 st + 4 gk + srow (+ 8), whose swizzle term is
+  // 4 srow + gk (+ 2); so the physical chunk is 4 (dt ^ srow) + (y ^ (gk (+ 2))),
+  // and in elements 32 (dt ^ srow) = 32 srow ^ 32 dt on bits 5 and 6, which
+  // the rest of the offset leaves clear.
   int trb[2] = {0, 0};
   if constexpr (HD == 128) {
-    const int tx = 2 * gk + (srow >> 1);
-    const int tb0 = (4 * gk + srow) * kD + 8 * ((2 * (grp & 1) + (m4 >> 1)) ^ (2 * (srow & 1))) + 4 * (m4 & 1);
-    const int tb1 = tb0 + 8 * kD + 8 * (1 - 2 * ((m4 >> 1) & 1));
-    trb[0] = 2 * (tb0 | 32 * tx);
-    trb[1] = 2 * (tb1 | 32 * tx);
+    const int y = 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
+    trb[0] = 2 * ((4 * gk + srow) * kD + 8 * (y ^ gk) + e4 + 32 * srow);
+    trb[1] = 2 * ((4 * gk + srow + 8) * kD + 8 * (y ^ (gk + 2)) + e4 + 32 * srow);
   }
   auto tr16 = [](const uint16_t* base, int o0, int o1) {
     const char* b8 = reinterpret_cast<const char*>(base);

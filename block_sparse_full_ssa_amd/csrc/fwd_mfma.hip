@@ -65,17 +65,14 @@ constexpr float kTau = 8.f;      // lazy-rescale threshold (log2 units)
 
 
 // Physical 16-byte chunk of logical chunk c in row r: K tiles are only read
-// by rows; V tiles by transpose reads.
-// 256-byte rows (D = 128): the transposed tiles use c ^ (2 (r % 8) + (r / 8) % 2);
-// measured on gfx950 it keeps the transpose reads (ds_read_b64_tr_b16) free
-// of bank conflicts as well as the 16-byte row reads, where c ^ (r % 8) or
-// c ^ (r % 16) leave the transpose reads two-way conflicted.  128-byte rows
-// (D = 64) hold 8 chunks, permuted by c ^ (r % 8) in both tiles.
+// by rows, c ^ (r % 16) for 256-byte rows (D = 128); V tiles by transpose
+// reads, swz256.  128-byte rows (D = 64) hold 8 chunks, permuted by c ^ (r % 8)
+// in both tiles.
 template <int D> __device__ __forceinline__ int swz_k(int r, int c) {
   return D == 128 ? c ^ (r & 15) : c ^ (r & 7);
 }
 template <int D> __device__ __forceinline__ int swz_v(int r, int c) {
-  return D == 128 ? c ^ (((r & 7) << 1) | ((r >> 3) & 1)) : c ^ (r & 7);
+  return D == 128 ? swz256(r, c) : c ^ (r & 7);
 }
 
 __device__ __forceinline__ float max16(const f32x16& v) {
@@ -192,6 +189,16 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
       buffer_to_lds16(rv, Vd + n * 512, voff[r]);
     }
   };
+
+  // Byte offsets of the V transpose reads of rows 4 gk + srow and 8 further
+  // (HD = 128), chunk term 32 srow of the dt ^ srow part kept apart on bits 5
+  // and 6 (the rest leaves them clear) so that column tile dt is an XOR of 64 dt
+  int tv[2] = {0, 0};
+  if constexpr (HD == 128) {
+    const int y = 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
+    tv[0] = 2 * ((4 * gk + srow) * HD + 8 * (y ^ gk) + e4 + 32 * srow);
+    tv[1] = 2 * ((4 * gk + srow + 8) * HD + 8 * (y ^ (gk + 2)) + e4 + 32 * srow);
+  }
 
   // one tile: compute on (Ks, Vs) while the next streams into (Kn, Vn)
   auto step = [&](int j, const uint16_t* Ks, const uint16_t* Vs, uint16_t* Kn, uint16_t* Vn) {
@@ -320,10 +327,20 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
         const int r1 = r0 + 8;
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) {
-          const int c = 4 * dt + 2 * (grp & 1) + (m4 >> 1);   // logical 16-byte chunk
-          const int e = 4 * (m4 & 1);
-          const bf16x8 va =
-              lds_tr_pair(&Vs[r0 * HD + 8 * swz_v<HD>(r0, c) + e], &Vs[r1 * HD + 8 * swz_v<HD>(r1, c) + e]);
+          bf16x8 va;
+          if constexpr (HD == 128) {
+            // rows r0, r1 = r0 + 8 at 32 (kh + st2 / 2) + 4 gk + srow: swizzle
+            // terms 4 srow + gk and 4 srow + gk + 2, so the physical chunk of
+            // logical 4 dt + y is 4 (dt ^ srow) + (y ^ gk (+ 2)); the row part
+            // is a constant of the unrolled loop
+            const int x = 64 * dt, rb = 2 * HD * (kh * 32 + st2 * 16);
+            va = lds_tr_pair(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(Vs) + ((tv[0] ^ x) + rb)),
+                             reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(Vs) + ((tv[1] ^ x) + rb)));
+          } else {
+            const int c = 4 * dt + 2 * (grp & 1) + (m4 >> 1);   // logical 16-byte chunk
+            const int e = 4 * (m4 & 1);
+            va = lds_tr_pair(&Vs[r0 * HD + 8 * swz_v<HD>(r0, c) + e], &Vs[r1 * HD + 8 * swz_v<HD>(r1, c) + e]);
+          }
           of[dt] = mfma32x32x16(va, pf[st2], of[dt]);
           if (kSparse && sparse_any) os[dt] = mfma32x32x16(va, ps[st2], os[dt]);
         }

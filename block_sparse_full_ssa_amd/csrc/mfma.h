@@ -56,6 +56,19 @@ __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Physical 16-byte chunk of logical chunk c (0..15) in row r of an LDS tile
+// with 256-byte rows (64 bf16): c ^ (4 (r % 4) + (r / 4) % 4).  A 256-byte
+// row spans all 64 banks, so only the chunk positions decide conflicts.  A
+// 16-byte row read serves 16 lanes per cycle, 16 consecutive rows at one
+// logical chunk: the XOR term runs through all 16 values over r % 16.  A
+// transpose read (ds_read_b64_tr_b16) serves 32 lanes per cycle, 4
+// consecutive rows (from a multiple of 4) times the 4 chunks of one aligned
+// group of 4: the term's high half r % 4 sends the 4 rows to 4 different
+// groups.  Measured on gfx950 with the LDS bank-conflict counter: no
+// conflict cycles for either (c ^ (2 (r % 8) + (r / 8) % 2) takes twice the
+// cycles on the transposes, c ^ (r % 16) four times).
+__device__ __forceinline__ int swz256(int r, int c) { return c ^ (((r & 3) << 2) | ((r >> 2) & 3)); }
+
 // Two transpose reads (slots 0..3 from p0, 4..7 from p1) as one operand.
 __device__ __forceinline__ bf16x8 lds_tr_pair(const uint16_t* p0, const uint16_t* p1) {
   i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p0));

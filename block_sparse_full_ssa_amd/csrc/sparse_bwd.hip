@@ -48,12 +48,9 @@ namespace {
 
 // Physical 16-byte chunk of logical chunk c: Q / G rows of 2 HD bytes (read by
 // rows and by transposes), 64-byte dS^T rows.
-// 256-byte rows (HD = 128): c ^ (2 (r % 8) + (r / 8) % 2), measured on gfx950
-// to keep the transpose reads (ds_read_b64_tr_b16) free of bank conflicts as
-// well as the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave the
-// transpose reads two-way conflicted.  128-byte rows (HD = 64): c ^ (r % 8).
+// swz256 for 256-byte rows (HD = 128), c ^ (r % 8) for 128-byte rows (HD = 64).
 template <int HD> __device__ __forceinline__ int swz_t(int r, int c) {
-  return HD == 128 ? c ^ (((r & 7) << 1) | ((r >> 3) & 1)) : c ^ (r & 7);
+  return HD == 128 ? swz256(r, c) : c ^ (r & 7);
 }
 __device__ __forceinline__ int swz_s(int r, int c) { return c ^ ((r >> 1) & 3); }
 

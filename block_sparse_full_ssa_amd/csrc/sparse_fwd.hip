@@ -37,13 +37,10 @@ namespace {
 constexpr float kLn2 = 0.69314718055994531f;
 
 // Physical 16-byte chunk of logical chunk c in a V row r (read by
-// transposes), for head dimension HD (rows of 2 HD bytes).
-// 256-byte rows: c ^ (2 (r % 8) + (r / 8) % 2), measured on gfx950 to keep
-// the transpose reads (ds_read_b64_tr_b16) free of bank conflicts as well as
-// the 16-byte row reads, where c ^ (r % 8) or c ^ (r % 16) leave the
-// transpose reads two-way conflicted; 128-byte rows: c ^ (r % 8).
+// transposes), for head dimension HD (rows of 2 HD bytes): swz256 for
+// 256-byte rows, c ^ (r % 8) for 128-byte rows.
 template <int HD> __device__ __forceinline__ int swz_v(int r, int c) {
-  return HD == 128 ? c ^ (((r & 7) << 1) | ((r >> 3) & 1)) : c ^ (r & 7);
+  return HD == 128 ? swz256(r, c) : c ^ (r & 7);
 }
 
 // Physical 16-byte chunk of logical chunk c in a K row r.
