@@ -39,9 +39,9 @@ constexpr int kBN = 64;          // keys per tile
 
 // Physical 16-byte chunk of logical chunk c in a K / V row r of 2 HD bytes (K
 // is read by rows and by transposes): swz256 for 256-byte rows (HD = 128),
-// c ^ (r % 8) for 128-byte rows (HD = 64).
+// swz128 for 128-byte rows (HD = 64).
 template <int HD> __device__ __forceinline__ int swz_k(int r, int c) {
-  return HD == 128 ? swz256(r, c) : c ^ (r & 7);
+  return HD == 128 ? swz256(r, c) : swz128(r, c);
 }
 
 // SP: 0 the full stream alone; 1 with the sparse stream's dS rows through
@@ -194,13 +194,16 @@ __global__ void __launch_bounds__(256, 2)
   // of the K^T transpose reads of rows 4 gk + srow and 8 further (column tile
   // dt: an XOR of 64 dt, the swizzle's 32 srow kept apart on bits 5 and 6,
   // which the rest leaves clear), held in registers
-  int roff[4] = {0, 0, 0, 0}, tk[2] = {0, 0};
-  if constexpr (HD == 128) {
+  constexpr int kRO = kD / 32, kFlip = kD;   // (HD = 128: 4 offsets, bit 7; HD = 64: 2, bit 6)
+  int roff[kRO], tk[2];
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds) roff[ds] = 2 * (col * kD + 8 * swz_k<HD>(col, 2 * ds + g));
+  for (int ds = 0; ds < kRO; ++ds) roff[ds] = 2 * (col * kD + 8 * swz_k<HD>(col, 2 * ds + g));
+  {
+    // (HD = 64: swizzle term 4 ((srow / 2) % 2) + gk (+ 2))
     const int y = 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
-    tk[0] = 2 * ((4 * gk + srow) * kD + 8 * (y ^ gk) + e4 + 32 * srow);
-    tk[1] = 2 * ((4 * gk + srow + 8) * kD + 8 * (y ^ (gk + 2)) + e4 + 32 * srow);
+    const int t = HD == 128 ? srow : (srow >> 1) & 1;
+    tk[0] = 2 * ((4 * gk + srow) * kD + 8 * (y ^ gk) + e4 + 32 * t);
+    tk[1] = 2 * ((4 * gk + srow + 8) * kD + 8 * (y ^ (gk + 2)) + e4 + 32 * t);
   }
   auto rd16 = [](const uint16_t* base, int off) {
     return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(reinterpret_cast<const char*>(base) + off));
@@ -245,15 +248,9 @@ __global__ void __launch_bounds__(256, 2)
           const int r = kh * 32 + col;
           bf16x8 ok[kD / 16], ov[kD / 16];
           auto rd = [&](int ds) {
-            if constexpr (HD == 128) {
-              const int o = (ds < 4 ? roff[ds] : roff[ds - 4] ^ 128) + 2 * kD * kh * 32;
-              ok[ds] = rd16(Ks, o);
-              ov[ds] = rd16(Vs, o);
-            } else {
-              const int off = r * kD + 8 * swz_k<HD>(r, 2 * ds + g);
-              ok[ds] = lds_read8(&Ks[off]);
-              ov[ds] = lds_read8(&Vs[off]);
-            }
+            const int o = (ds < kRO ? roff[ds] : roff[ds - kRO] ^ kFlip) + 2 * kD * kh * 32;
+            ok[ds] = rd16(Ks, o);
+            ov[ds] = rd16(Vs, o);
           };
           rd(0);
 #pragma unroll
@@ -319,16 +316,10 @@ __global__ void __launch_bounds__(256, 2)
                               dsv[8 * st + 5], dsv[8 * st + 6], dsv[8 * st + 7]);
         auto rdk = [&](int u) {
           const int st = u / kDT, dt = u % kDT;
-          if constexpr (HD == 128) {
-            const int rb = 2 * kD * (kh * 32 + st * 16);
-            const char* kb = reinterpret_cast<const char*>(Ks);
-            ka[u] = lds_tr_pair(reinterpret_cast<const uint16_t*>(kb + ((tk[0] ^ (64 * dt)) + rb)),
-                                reinterpret_cast<const uint16_t*>(kb + ((tk[1] ^ (64 * dt)) + rb)));
-          } else {
-            const int r0 = kh * 32 + st * 16 + 4 * gk + srow, r1 = r0 + 8;
-            const int c = 4 * dt + 2 * (grp & 1) + (m4 >> 1), e = 4 * (m4 & 1);
-            ka[u] = lds_tr_pair(&Ks[r0 * kD + 8 * swz_k<HD>(r0, c) + e], &Ks[r1 * kD + 8 * swz_k<HD>(r1, c) + e]);
-          }
+          const int rb = 2 * kD * (kh * 32 + st * 16);
+          const char* kb = reinterpret_cast<const char*>(Ks);
+          ka[u] = lds_tr_pair(reinterpret_cast<const uint16_t*>(kb + ((tk[0] ^ (64 * dt)) + rb)),
+                              reinterpret_cast<const uint16_t*>(kb + ((tk[1] ^ (64 * dt)) + rb)));
         };
         rdk(0);
 #pragma unroll

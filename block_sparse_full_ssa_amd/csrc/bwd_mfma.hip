@@ -131,9 +131,9 @@ __global__ void __launch_bounds__(256)
 // --------------------------------------------------------------- bwd_mfma --
 // Physical 16-byte chunk of logical chunk c in a K / Q / G row r of 2 HD bytes
 // (read by rows and by transposes): swz256 for 256-byte rows (HD = 128),
-// c ^ (r % 8) for 128-byte rows (HD = 64).
+// swz128 for 128-byte rows (HD = 64).
 template <int HD> __device__ __forceinline__ int swz_t(int r, int c) {
-  return HD == 128 ? swz256(r, c) : c ^ (r & 7);
+  return HD == 128 ? swz256(r, c) : swz128(r, c);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -261,31 +261,34 @@ __global__ void __launch_bounds__(256, 2)
   }
   // Byte offsets of the row reads of d-step ds: the same chunk of query row
   // col in the Q / G_f tiles and of key row 32 kq + col in K (the same
-  // swizzle: rows 16 apart share it).  HD = 128: those of d-steps 0..3 are
-  // computed once and held in registers; d-step ds + 4 flips bit 7 of d-step
-  // ds's (its logical chunk 2 ds + g flips bit 3, and so does the physical
-  // one), and the key row's adds kq_off, whose bits (>= 13) the query
-  // offsets (< 8192) never use, so an OR.
-  constexpr int kRO = HD == 128 ? 4 : kD / 16;
+  // swizzle: rows 16 apart share it).  Those of the first half of the
+  // d-steps are computed once and held in registers; d-step ds + kRO flips
+  // one bit of d-step ds's (its logical chunk 2 ds + g flips the top bit,
+  // and so does the physical one: bit 7 of the offset at HD = 128, bit 6 at
+  // HD = 64), and the key row's adds kq_off, whose bits the query offsets
+  // (< 64 HD) never use, so an OR.
+  constexpr int kRO = kD / 32, kFlip = kD;
   int roff[kRO];
 #pragma unroll
   for (int ds = 0; ds < kRO; ++ds)
     roff[ds] = 2 * (col * kD + 8 * swz_t<HD>(col, 2 * ds + g));
   const int kq_off = 2 * 32 * kq * kD;              // uniform
-  auto qoff = [&](int ds) { return HD == 128 ? (ds < 4 ? roff[ds] : roff[ds - 4] ^ 128) : roff[ds]; };
-  auto koff = [&](int ds) { return HD == 128 ? qoff(ds) | kq_off : roff[ds] + kq_off; };
-  // Byte offsets of the transpose reads (HD = 128): those of k-step st and
-  // column tile dt are trb[0] ^ 64 dt and trb[1] ^ 64 dt (rows eight apart)
-  // plus 4096 st.  The lane reads logical chunk 4 dt + y (y = 2 (grp % 2) +
-  // m4 / 2) of row r = 16 st + 4 gk + srow (+ 8), whose swizzle term is
-  // 4 srow + gk (+ 2); so the physical chunk is 4 (dt ^ srow) + (y ^ (gk (+ 2))),
-  // and in elements 32 (dt ^ srow) = 32 srow ^ 32 dt on bits 5 and 6, which
-  // the rest of the offset leaves clear.
-  int trb[2] = {0, 0};
-  if constexpr (HD == 128) {
+  auto qoff = [&](int ds) { return ds < kRO ? roff[ds] : roff[ds - kRO] ^ kFlip; };
+  auto koff = [&](int ds) { return qoff(ds) | kq_off; };
+  // Byte offsets of the transpose reads: those of k-step st and column tile
+  // dt are trb[0] ^ 64 dt and trb[1] ^ 64 dt (rows eight apart) plus
+  // 32 HD st.  The lane reads logical chunk 4 dt + y (y = 2 (grp % 2) +
+  // m4 / 2) of row r = 16 st + 4 gk + srow (+ 8).  Its swizzle term is
+  // 4 srow + gk (+ 2) at HD = 128 and 4 sb + gk (+ 2), sb = (srow / 2) % 2, at
+  // HD = 64, so the physical chunk is 4 (dt ^ t) + (y ^ (gk (+ 2))) with t =
+  // srow or sb, and in elements 32 (dt ^ t) = 32 t ^ 32 dt on the bits above
+  // the chunk's low two, which the rest of the offset leaves clear.
+  int trb[2];
+  {
     const int y = 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
-    trb[0] = 2 * ((4 * gk + srow) * kD + 8 * (y ^ gk) + e4 + 32 * srow);
-    trb[1] = 2 * ((4 * gk + srow + 8) * kD + 8 * (y ^ (gk + 2)) + e4 + 32 * srow);
+    const int t = HD == 128 ? srow : (srow >> 1) & 1;
+    trb[0] = 2 * ((4 * gk + srow) * kD + 8 * (y ^ gk) + e4 + 32 * t);
+    trb[1] = 2 * ((4 * gk + srow + 8) * kD + 8 * (y ^ (gk + 2)) + e4 + 32 * t);
   }
   auto tr16 = [](const uint16_t* base, int o0, int o1) {
     const char* b8 = reinterpret_cast<const char*>(base);
@@ -318,7 +321,7 @@ __global__ void __launch_bounds__(256, 2)
       // here rather than hoisted out of the loop into more registers)
 #pragma unroll
       for (int i = 0; i < kRO; ++i) asm volatile("" : "+v"(roff[i]));
-      if constexpr (HD == 128) asm volatile("" : "+v"(trb[0]), "+v"(trb[1]));
+      asm volatile("" : "+v"(trb[0]), "+v"(trb[1]));
       auto rd = [&](int ds) {
         const int o = qoff(ds);
         ok[ds] = rd16(Kt, koff(ds));
@@ -369,18 +372,10 @@ __global__ void __launch_bounds__(256, 2)
       }
       // step u: k-step st = u / kDT (16 queries), column tile dt = u % kDT
       auto rdB = [&](int u) {
-        if constexpr (HD == 128) {
-          const int x0 = (trb[0] ^ (64 * (u & 3))) + 4096 * (u >> 2);
-          const int x1 = (trb[1] ^ (64 * (u & 3))) + 4096 * (u >> 2);
-          tg[u] = tr16(Fs, x0, x1);
-          tq[u] = tr16(Qs, x0, x1);
-        } else {
-          const int r0 = 16 * (u / kDT) + 4 * gk + srow, r1 = r0 + 8;
-          const int cl = 4 * (u % kDT) + 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
-          const int o0 = r0 * kD + 8 * swz_t<HD>(r0, cl) + e4, o1 = r1 * kD + 8 * swz_t<HD>(r1, cl) + e4;
-          tg[u] = lds_tr_pair(&Fs[o0], &Fs[o1]);
-          tq[u] = lds_tr_pair(&Qs[o0], &Qs[o1]);
-        }
+        const int x0 = (trb[0] ^ (64 * (u % kDT))) + 32 * kD * (u / kDT);
+        const int x1 = (trb[1] ^ (64 * (u % kDT))) + 32 * kD * (u / kDT);
+        tg[u] = tr16(Fs, x0, x1);
+        tq[u] = tr16(Qs, x0, x1);
       };
       rdB(0);
 #pragma unroll

@@ -66,13 +66,12 @@ constexpr float kTau = 8.f;      // lazy-rescale threshold (log2 units)
 
 // Physical 16-byte chunk of logical chunk c in row r: K tiles are only read
 // by rows, c ^ (r % 16) for 256-byte rows (D = 128); V tiles by transpose
-// reads, swz256.  128-byte rows (D = 64) hold 8 chunks, permuted by c ^ (r % 8)
-// in both tiles.
+// reads, swz256.  128-byte rows (D = 64): swz128 in both tiles.
 template <int D> __device__ __forceinline__ int swz_k(int r, int c) {
-  return D == 128 ? c ^ (r & 15) : c ^ (r & 7);
+  return D == 128 ? c ^ (r & 15) : swz128(r, c);
 }
 template <int D> __device__ __forceinline__ int swz_v(int r, int c) {
-  return D == 128 ? swz256(r, c) : c ^ (r & 7);
+  return D == 128 ? swz256(r, c) : swz128(r, c);
 }
 
 __device__ __forceinline__ float max16(const f32x16& v) {
@@ -190,14 +189,18 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
     }
   };
 
-  // Byte offsets of the V transpose reads of rows 4 gk + srow and 8 further
-  // (HD = 128), chunk term 32 srow of the dt ^ srow part kept apart on bits 5
-  // and 6 (the rest leaves them clear) so that column tile dt is an XOR of 64 dt
-  int tv[2] = {0, 0};
-  if constexpr (HD == 128) {
+  // Byte offsets of the V transpose reads of rows 4 gk + srow and 8 further:
+  // the swizzle term of those rows is 4 t + gk (+ 2), t = srow (HD = 128) or
+  // (srow / 2) % 2 (HD = 64), so logical chunk 4 dt + y sits at physical
+  // 4 (dt ^ t) + (y ^ gk (+ 2)); the term 32 t of the dt ^ t part is kept
+  // apart on bits the rest leaves clear, so that column tile dt is an XOR of
+  // 64 dt (bytes) and the row part (32 kh + 16 st2) a constant
+  int tv[2];
+  {
     const int y = 2 * (grp & 1) + (m4 >> 1), e4 = 4 * (m4 & 1);
-    tv[0] = 2 * ((4 * gk + srow) * HD + 8 * (y ^ gk) + e4 + 32 * srow);
-    tv[1] = 2 * ((4 * gk + srow + 8) * HD + 8 * (y ^ (gk + 2)) + e4 + 32 * srow);
+    const int t = HD == 128 ? srow : (srow >> 1) & 1;
+    tv[0] = 2 * ((4 * gk + srow) * HD + 8 * (y ^ gk) + e4 + 32 * t);
+    tv[1] = 2 * ((4 * gk + srow + 8) * HD + 8 * (y ^ (gk + 2)) + e4 + 32 * t);
   }
 
   // one tile: compute on (Ks, Vs) while the next streams into (Kn, Vn)
@@ -323,24 +326,14 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
       // ---- O^T += V^T P^T over the 32 keys (two k-steps of 16)
 #pragma unroll
       for (int st2 = 0; st2 < 2; ++st2) {
-        const int r0 = kh * 32 + st2 * 16 + 4 * gk + srow;   // key row of this lane's first read
-        const int r1 = r0 + 8;
 #pragma unroll
         for (int dt = 0; dt < kDT; ++dt) {
-          bf16x8 va;
-          if constexpr (HD == 128) {
-            // rows r0, r1 = r0 + 8 at 32 (kh + st2 / 2) + 4 gk + srow: swizzle
-            // terms 4 srow + gk and 4 srow + gk + 2, so the physical chunk of
-            // logical 4 dt + y is 4 (dt ^ srow) + (y ^ gk (+ 2)); the row part
-            // is a constant of the unrolled loop
-            const int x = 64 * dt, rb = 2 * HD * (kh * 32 + st2 * 16);
-            va = lds_tr_pair(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(Vs) + ((tv[0] ^ x) + rb)),
-                             reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(Vs) + ((tv[1] ^ x) + rb)));
-          } else {
-            const int c = 4 * dt + 2 * (grp & 1) + (m4 >> 1);   // logical 16-byte chunk
-            const int e = 4 * (m4 & 1);
-            va = lds_tr_pair(&Vs[r0 * HD + 8 * swz_v<HD>(r0, c) + e], &Vs[r1 * HD + 8 * swz_v<HD>(r1, c) + e]);
-          }
+          // key rows kh 32 + st2 16 + 4 gk + srow and 8 further (tv), the row
+          // part a constant of the unrolled loop
+          const int x = 64 * dt, rb = 2 * HD * (kh * 32 + st2 * 16);
+          const bf16x8 va =
+              lds_tr_pair(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(Vs) + ((tv[0] ^ x) + rb)),
+                          reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(Vs) + ((tv[1] ^ x) + rb)));
           of[dt] = mfma32x32x16(va, pf[st2], of[dt]);
           if (kSparse && sparse_any) os[dt] = mfma32x32x16(va, ps[st2], os[dt]);
         }

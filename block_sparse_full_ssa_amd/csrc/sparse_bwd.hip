@@ -48,9 +48,9 @@ namespace {
 
 // Physical 16-byte chunk of logical chunk c: Q / G rows of 2 HD bytes (read by
 // rows and by transposes), 64-byte dS^T rows.
-// swz256 for 256-byte rows (HD = 128), c ^ (r % 8) for 128-byte rows (HD = 64).
+// swz256 for 256-byte rows (HD = 128), swz128 for 128-byte rows (HD = 64).
 template <int HD> __device__ __forceinline__ int swz_t(int r, int c) {
-  return HD == 128 ? swz256(r, c) : c ^ (r & 7);
+  return HD == 128 ? swz256(r, c) : swz128(r, c);
 }
 __device__ __forceinline__ int swz_s(int r, int c) { return c ^ ((r >> 1) & 3); }
 

@@ -38,13 +38,13 @@ constexpr float kLn2 = 0.69314718055994531f;
 
 // Physical 16-byte chunk of logical chunk c in a V row r (read by
 // transposes), for head dimension HD (rows of 2 HD bytes): swz256 for
-// 256-byte rows, c ^ (r % 8) for 128-byte rows.
+// 256-byte rows, swz128 for 128-byte rows.
 template <int HD> __device__ __forceinline__ int swz_v(int r, int c) {
-  return HD == 128 ? swz256(r, c) : c ^ (r & 7);
+  return HD == 128 ? swz256(r, c) : swz128(r, c);
 }
 
-// Physical 16-byte chunk of logical chunk c in a K row r.
-template <int HD> __device__ __forceinline__ int swz_k(int r, int c) { return c ^ (r & (HD / 8 - 1)); }
+// Physical 16-byte chunk of logical chunk c in a K row r (read by rows).
+template <int HD> __device__ __forceinline__ int swz_k(int r, int c) { return HD == 128 ? c ^ (r & 15) : swz128(r, c); }
 
 template <int KH, int HD>   // the key block as KH halves of 32 keys; head dimension HD
 __global__ void __launch_bounds__(256, (KH <= 2 ? 2 : 1)) k_sparse_part(SparseFwdArgs a, int Hq, int G, int N, int Nq,
