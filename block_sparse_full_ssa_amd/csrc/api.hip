@@ -577,8 +577,8 @@ ssa_status_t ssa_probe_atomic(float* buf, int64_t n_floats, int32_t blocks, int3
 ssa_status_t ssa_probe_lds(float* sink, int32_t blocks, int32_t iters, int32_t mode, void* stream) {
   g_last_error.clear();
   if (!sink) return fail(SSA_ERR_NULL, "null sink%s");
-  if (blocks < 1 || iters < 1 || mode < 0 || mode > 1)
-    return fail(SSA_ERR_SHAPE, "blocks and iters must be positive and mode 0 or 1%s");
+  if (blocks < 1 || iters < 1 || mode < 0 || mode > 9)
+    return fail(SSA_ERR_SHAPE, "blocks and iters must be positive and mode 0 .. 9%s");
   launch_probe_lds(sink, blocks, iters, mode, static_cast<hipStream_t>(stream));
   return launch_status();
 }

@@ -71,8 +71,9 @@ __global__ void __launch_bounds__(256) k_probe_atomic(float* buf, int ntiles, in
 // LDS reads: every wave reads its own 8 KiB of a 32 KiB tile, eight reads per
 // pass, either 16 bytes per lane (ds_read_b128, conflict-free: lane l reads
 // chunk l) or 8 bytes per lane as transposes (ds_read_b64_tr_b16, the
-// operand reads of the attention kernels); the values are folded into the
-// sink so that no read is dropped.
+// operand reads of the attention kernels); modes 2..9 replay the kernels'
+// read patterns on swizzled tiles.  The values are folded into the sink so
+// that no read is dropped.
 __global__ void __launch_bounds__(256, 2) k_probe_lds(float* sink, int iters, int mode) {
   __shared__ __attribute__((aligned(16))) uint16_t buf[256 * 64];
   const int t = threadIdx.x;
@@ -90,7 +91,7 @@ __global__ void __launch_bounds__(256, 2) k_probe_lds(float* sink, int iters, in
         asm volatile("" : "+v"(acc));
       }
     }
-  } else {
+  } else if (mode == 1) {
     const int grp = lane >> 4, li = lane & 15;
     const int row = wave * 16 + grp * 4 + (li >> 2), col = 4 * (li & 3);       // row < 64, col < 16
     const uint16_t* base = buf + row * 64 + col;
@@ -99,6 +100,63 @@ __global__ void __launch_bounds__(256, 2) k_probe_lds(float* sink, int iters, in
       for (int r = 0; r < 8; ++r) {
         const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 16 * (r & 3)));
         acc += static_cast<uint32_t>(v[0] ^ v[1] ^ v[2] ^ v[3]);
+        asm volatile("" : "+v"(acc));
+      }
+    }
+  } else {
+    // Modes 2..9: the attention kernels' operand reads of a swizzled tile
+    // (rows of 256 bytes, 64 bf16, or of 128 bytes, 32 bf16), whose bank
+    // conflicts the LDS conflict counter shows.  Row reads: lane (col, g)
+    // reads logical chunk 2 s + g of row 32 (s % 2) + col (16 bytes).
+    // Transposes: lane (grp, li) reads half (li % 2) of logical chunk
+    // 4 dt + 2 (grp % 2) + (li % 4) / 2 of row 16 st + 4 (grp / 2) + li / 4
+    // and of the row 8 below.  Swizzles (physical chunk of logical c in row r):
+    //   2: transposes, 256-byte rows, c ^ (2 (r % 8) + (r / 8) % 2)
+    //   3: transposes, 256-byte rows, c ^ (4 (r % 4) + (r / 4) % 4)
+    //   4: transposes, 256-byte rows, c ^ (r % 16)
+    //   5: row reads, 256-byte rows, c ^ (4 (r % 4) + (r / 4) % 4)
+    //   6: row reads, 128-byte rows, c ^ (r % 8)
+    //   7: row reads, 128-byte rows, c ^ (4 ((r / 2) % 2) + (r / 4) % 4)
+    //   8: transposes, 128-byte rows, c ^ (r % 8)
+    //   9: transposes, 128-byte rows, c ^ (4 ((r / 2) % 2) + (r / 4) % 4)
+    const bool wide = mode <= 5, tr = mode <= 4 || mode >= 8;
+    const int rowe = wide ? 128 : 64;                      // elements per row
+    auto swz = [&](int r, int c) {
+      switch (mode) {
+        case 2: return c ^ (((r & 7) << 1) | ((r >> 3) & 1));
+        case 4: return c ^ (r & 15);
+        case 6: case 8: return c ^ (r & 7);
+        case 3: case 5: return c ^ (((r & 3) << 2) | ((r >> 2) & 3));
+        default: return c ^ ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+      }
+    };
+    const int g = lane >> 5, col = lane & 31, grp = lane >> 4, li = lane & 15;
+    int o0[8], o1[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (tr) {
+        const int st = u >> 2, dt = u & (wide ? 3 : 1);
+        const int r0 = 16 * st + 4 * (grp >> 1) + (li >> 2) + (wide ? 0 : 32 * ((u >> 1) & 1));
+        const int c = 4 * dt + 2 * (grp & 1) + ((li & 3) >> 1), e = 4 * (li & 1);
+        o0[u] = r0 * rowe + 8 * swz(r0, c) + e;
+        o1[u] = (r0 + 8) * rowe + 8 * swz(r0 + 8, c) + e;
+      } else {
+        const int r = 32 * (u & 1) + col, s = (u >> 1) & (wide ? 3 : 1);
+        o0[u] = r * rowe + 8 * swz(r, 2 * s + g);
+        o1[u] = 0;
+      }
+    }
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (tr) {
+          const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + o0[u]));
+          const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(buf + o1[u]));
+          acc += static_cast<uint32_t>(a[0] ^ a[3] ^ b[1] ^ b[2]);
+        } else {
+          const uint4 v = *reinterpret_cast<const uint4*>(buf + o0[u]);
+          acc += v.x ^ v.y ^ v.z ^ v.w;
+        }
         asm volatile("" : "+v"(acc));
       }
     }

@@ -21,6 +21,12 @@
       (GRBM_GUI_ACTIVE per XCD over the kernel's average duration in the
       stats run STATS).
 
+  python -m block_sparse_full_ssa_amd.profile_summary lds PMC OUT.md TITLE
+      per mode of the LDS probe (lds_patterns.py launches modes 0 .. 9 once
+      each, in order) from one `--pmc SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE
+      SQ_INSTS_LDS GRBM_GUI_ACTIVE` pass: LDS cycles per read instruction and
+      the share of them lost to bank conflicts.
+
 Commands are stated in the written summaries; this module only reads CSVs.
 """
 from __future__ import annotations
@@ -134,6 +140,41 @@ def mfma(pd: str, sd: str, out: str, title: str, n_xcd: int = 8) -> None:
         f.write("\n".join(lines) + "\n")
 
 
+LDS_MODES = ["16-byte reads, lane l reads chunk l", "transposes, plain 128-byte rows",
+             "transposes, 256-byte rows, c ^ (2 (r % 8) + (r / 8) % 2)",
+             "transposes, 256-byte rows, c ^ (4 (r % 4) + (r / 4) % 4)",
+             "transposes, 256-byte rows, c ^ (r % 16)",
+             "row reads, 256-byte rows, c ^ (4 (r % 4) + (r / 4) % 4)",
+             "row reads, 128-byte rows, c ^ (r % 8)",
+             "row reads, 128-byte rows, c ^ (4 ((r / 2) % 2) + (r / 4) % 4)",
+             "transposes, 128-byte rows, c ^ (r % 8)",
+             "transposes, 128-byte rows, c ^ (4 ((r / 2) % 2) + (r / 4) % 4)"]
+
+
+def lds(pd: str, out: str, title: str) -> None:
+    files = glob.glob(os.path.join(pd, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter CSV under {pd}")
+    by = defaultdict(lambda: defaultdict(float))
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if "probe_lds" in r["Kernel_Name"]:
+                by[int(r.get("Dispatch_Id") or r["Correlation_Id"])][r["Counter_Name"]] += float(r["Counter_Value"])
+    ids = sorted(by)
+    if len(ids) != len(LDS_MODES):
+        raise SystemExit(f"expected {len(LDS_MODES)} probe dispatches, found {len(ids)}")
+    lines = []
+    for mode, d in enumerate(ids):
+        c = by[d]
+        cyc = c["SQ_LDS_IDX_ACTIVE"] / c["SQ_INSTS_LDS"]
+        share = c["SQ_LDS_BANK_CONFLICT"] / max(c["SQ_LDS_IDX_ACTIVE"], 1.0)
+        lines.append(f"| {mode} | {LDS_MODES[mode]} | {cyc:.2f} | {100 * share:.1f} |")
+    with open(out, "w") as f:
+        f.write(title.rstrip() + "\n\n| mode | pattern | LDS cycles per read instruction | conflict cycles % |\n"
+                "|---|---|---|---|\n")
+        f.write("\n".join(lines) + "\n")
+
+
 if __name__ == "__main__":
     a = sys.argv[1:]
     if a and a[0] == "stats" and len(a) == 4:
@@ -142,5 +183,7 @@ if __name__ == "__main__":
         traffic(*a[1:8], int(a[8]), a[9])
     elif a and a[0] == "mfma" and len(a) == 5:
         mfma(a[1], a[2], a[3], a[4])
+    elif a and a[0] == "lds" and len(a) == 4:
+        lds(a[1], a[2], a[3])
     else:
         raise SystemExit(__doc__)

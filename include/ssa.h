@@ -338,8 +338,15 @@ ssa_status_t ssa_probe_copy(const void* src, void* dst, size_t bytes, void* stre
  * ssa_probe_lds: `blocks` workgroups of 4 waves (two per CU); every wave
  *   performs iters * 8 LDS reads, of 16 bytes per lane (mode 0, 1 KiB per
  *   read) or 8 bytes per lane by transposing reads (mode 1, 512 bytes per
- *   read).  `sink` (device, blocks * 256 floats) receives meaningless
- *   values.  SSA_ERR_NULL / SSA_ERR_SHAPE as above (mode must be 0 or 1).
+ *   read).  Modes 2..9 replay the attention kernels' operand reads (16-byte
+ *   row reads, or pairs of transposing reads) on tiles of 256- or 128-byte
+ *   rows under several chunk swizzles, for the LDS bank-conflict counter:
+ *   2, 3, 4 transposes on 256-byte rows with c ^ (2 (r % 8) + (r / 8) % 2),
+ *   c ^ (4 (r % 4) + (r / 4) % 4) and c ^ (r % 16); 5 row reads, 256-byte
+ *   rows, the second; 6, 7 row reads and 8, 9 transposes on 128-byte rows
+ *   with c ^ (r % 8) and c ^ (4 ((r / 2) % 2) + (r / 4) % 4).  `sink`
+ *   (device, blocks * 256 floats) receives meaningless values.
+ *   SSA_ERR_NULL / SSA_ERR_SHAPE as above (mode must be 0 .. 9).
  */
 ssa_status_t ssa_probe_atomic(float* buf, int64_t n_floats, int32_t blocks, int32_t iters, void* stream);
 ssa_status_t ssa_probe_lds(float* sink, int32_t blocks, int32_t iters, int32_t mode, void* stream);

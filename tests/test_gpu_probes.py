@@ -52,7 +52,7 @@ def test_probe_atomic_counts_exact():
     assert bool((buf == float(blocks // ntiles * iters)).all())
 
 
-@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("mode", list(range(10)))
 def test_probe_lds_runs(mode):
     import block_sparse_full_ssa_amd as ssa
     blocks = 512
