@@ -90,7 +90,16 @@ __global__ void __launch_bounds__(256, 2)
     greg[ds] = __builtin_bit_cast(bf16x8, w);
   }
   const float lse2 = qrow < N ? a.lse2_full[row] : 0.f;
-  const float Dq = qrow < N ? a.D_full[row] : 0.f;
+  // dP^T starts at -D of the lane's query: one extra product, -D as three
+  // bf16 terms in the k-slots 0..2 of the B operand (lanes of k-group 0)
+  // against ones in the same k-slots of the A operand, so that dS needs no
+  // per-element subtraction
+  bf16x8 dterm, ones;
+  {
+    const uint2 t = split3_bf16(-(qrow < N ? a.D_full[row] : 0.f));
+    dterm = __builtin_bit_cast(bf16x8, g ? make_uint4(0u, 0u, 0u, 0u) : make_uint4(t.x, t.y, 0u, 0u));
+    ones = __builtin_bit_cast(bf16x8, g ? make_uint4(0u, 0u, 0u, 0u) : make_uint4(0x3F803F80u, 0x00003F80u, 0u, 0u));
+  }
 
   f32x16 dq[kDT];
 #pragma unroll
@@ -243,7 +252,7 @@ __global__ void __launch_bounds__(256, 2)
           }
         }
         // ---- S^T = K Q^T, dP^T = V G^T for 32 keys (A: key row kh*32 + col)
-        f32x16 s = f32x16{}, dp = f32x16{};
+        f32x16 s = f32x16{}, dp = mfma32x32x16(ones, dterm, f32x16{});
         {
           const int r = kh * 32 + col;
           bf16x8 ok[kD / 16], ov[kD / 16];
@@ -298,7 +307,7 @@ __global__ void __launch_bounds__(256, 2)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const float sp = SPARSE ? __uint_as_float((i & 1) ? (sw[i >> 1] & 0xffff0000u) : (sw[i >> 1] << 16)) : 0.f;
-            dsv[i] = fmaf(fast_exp2(s[i] * scale_log2 - lse2), dp[i] - Dq, sp);
+            dsv[i] = fmaf(fast_exp2(s[i] * scale_log2 - lse2), dp[i], sp);
           }
         }
         if (diag) {                  // uniform: only the diagonal tiles need the causal mask

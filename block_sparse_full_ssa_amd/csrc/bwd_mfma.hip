@@ -42,17 +42,6 @@ constexpr int kBN = 128;       // keys per workgroup
 constexpr int kBM = 32;        // queries per iteration
 constexpr float kLog2e = 1.4426950408889634f;
 
-// x as three bf16 terms t0 + t1 + t2 (t0 = bf16(x), t1 = bf16(x - t0),
-// t2 = bf16(x - t0 - t1); the residuals are exact in fp32, so the sum equals
-// x up to 2^-24 |x|), packed {t0 | t1 << 16, t2}
-__device__ __forceinline__ uint2 split3_bf16(float x) {
-  const float t0 = to_f32(to_bf16(x));
-  const float r1 = x - t0;
-  const float t1 = to_f32(to_bf16(r1));
-  const float t2 = to_f32(to_bf16(r1 - t1));
-  return make_uint2(pack_bf16x2(t0, t1), pack_bf16x2(t2, 0.f));
-}
-
 // ---------------------------------------------------------------- bwd_pre --
 template <int HD>   // head dimension
 __global__ void __launch_bounds__(256)

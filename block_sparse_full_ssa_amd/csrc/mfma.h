@@ -97,6 +97,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
 }
 
+// x as three bf16 terms t0 + t1 + t2 (t0 = bf16(x), t1 = bf16(x - t0),
+// t2 = bf16(x - t0 - t1); the residuals are exact in fp32, so the sum equals
+// x up to 2^-24 |x|), packed {t0 | t1 << 16, t2}.  Against ones in the same
+// k-slots of the other operand, one matrix product adds x to every element.
+__device__ __forceinline__ uint2 split3_bf16(float x) {
+  const float t0 = __uint_as_float(pack_bf16x2(x, 0.f) << 16);
+  const float r1 = x - t0;
+  const float t1 = __uint_as_float(pack_bf16x2(r1, 0.f) << 16);
+  const float t2 = __uint_as_float(pack_bf16x2(r1 - t1, 0.f) << 16);
+  return make_uint2(pack_bf16x2(t0, t1), pack_bf16x2(t2, 0.f));
+}
+
 // Eight fp32 values -> one bf16 operand (round to nearest even).
 __device__ __forceinline__ bf16x8 to_bf16x8(float x0, float x1, float x2, float x3, float x4,
                                             float x5, float x6, float x7) {
