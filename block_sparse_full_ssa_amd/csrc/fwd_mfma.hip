@@ -75,10 +75,11 @@ template <int D> __device__ __forceinline__ int swz_v(int r, int c) {
 }
 
 __device__ __forceinline__ float max16(const f32x16& v) {
-  float m = fmaxf(v[0], v[1]);
+  // a chain of three-input maxima (v_max3_f32): two new values per instruction
+  float m = __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), v[2]);
 #pragma unroll
-  for (int i = 2; i < 16; i += 2) m = fmaxf(m, fmaxf(v[i], v[i + 1]));
-  return m;
+  for (int i = 3; i < 15; i += 2) m = __builtin_fmaxf(__builtin_fmaxf(m, v[i]), v[i + 1]);
+  return __builtin_fmaxf(m, v[15]);
 }
 
 // Two to four workgroups per CU (see FwdTile), so one wave's softmax
