@@ -269,12 +269,30 @@ __global__ void __launch_bounds__(128 * KH, 2)
     int cx = col, rx = 4 * gk + srow, cq = 2 * (grp & 1) + (m4 >> 1);
     asm volatile("" : "+v"(cx), "+v"(rx), "+v"(cq));
     const int e4 = 4 * (m4 & 1);
+    // Byte offsets, built once per batch from those lane parts.  Row reads of
+    // d-step ds (row cx): the first half computed, d-step ds + kRO flipping
+    // one bit (its logical chunk 2 ds + g flips the top bit, and so does the
+    // physical one: bit 7 at HD = 128, bit 6 at HD = 64).  Transposes of
+    // k-step st and d tile dt (rows 16 st + rx and 8 below): logical chunk
+    // 4 dt + cq of a row whose swizzle term is 4 t + rx / 4 (+ 2), t = rx % 4
+    // (HD = 128) or (rx % 4) / 2 % 2 (HD = 64), sits at 4 (dt ^ t) + (cq ^
+    // (rx / 4 (+ 2))); the term 32 t is kept on bits the rest leaves clear,
+    // so dt is an XOR of 64 dt and st a constant.
+    constexpr int kRO = kD / 32;
+    int ro[kRO];
+#pragma unroll
+    for (int ds = 0; ds < kRO; ++ds) ro[ds] = 2 * (cx * kD + 8 * swz_t<HD>(cx, 2 * ds + g));
+    const int tt = HD == 128 ? (rx & 3) : ((rx & 3) >> 1) & 1;
+    const int tb0 = 2 * (rx * kD + 8 * (cq ^ (rx >> 2)) + e4 + 32 * tt);
+    const int tb1 = 2 * ((rx + 8) * kD + 8 * (cq ^ ((rx >> 2) + 2)) + e4 + 32 * tt);
+    auto at = [](const uint16_t* T, int off) {
+      return reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(T) + off);
+    };
     // A operand [32 q x 16 d] of S / dP (k-step ds) from a Q / G_s tile
-    auto rdA = [&](const uint16_t* T, int ds) { return lds_read8(&T[cx * kD + 8 * swz_t<HD>(cx, 2 * ds + g)]); };
+    auto rdA = [&](const uint16_t* T, int ds) { return lds_read8(at(T, ds < kRO ? ro[ds] : ro[ds - kRO] ^ kD)); };
     // A operand [32 d x 16 q] (transposed tile, k-step st, d tile dt)
     auto rdT = [&](const uint16_t* T, int st, int dt) {
-      const int r0 = 16 * st + rx, r1 = r0 + 8, cl = 4 * dt + cq;
-      return lds_tr_pair(&T[r0 * kD + 8 * swz_t<HD>(r0, cl) + e4], &T[r1 * kD + 8 * swz_t<HD>(r1, cl) + e4]);
+      return lds_tr_pair(at(T, (tb0 ^ (64 * dt)) + 32 * kD * st), at(T, (tb1 ^ (64 * dt)) + 32 * kD * st));
     };
     // transposing read of the dS^T tile for k-step ks (keys 16 ks ..)
     auto rdS = [&](int ks) {
