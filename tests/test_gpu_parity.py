@@ -37,6 +37,12 @@ SMALL = {
                                           top_k=5),
     "mha_n512_d64_b128_k2": si.scaled_down(W["gqa_n4k_fwd"], seqlen=512, hq=2, hkv=2, block=128, head_dim=64,
                                            top_k=2),
+    # N an odd multiple of 32: the last 64-key tile of the dual forward and
+    # the dQ kernel (and of the d = 64 forward) reaches past the keys, whose
+    # copies read zeros that the causal mask removes
+    "mha_n352_b32_k4": si.scaled_down(W["gqa_n4k_fwd"], seqlen=352, hq=2, hkv=1, block=32, top_k=4),
+    "gqa_n288_d64_b32_k3": si.scaled_down(W["gqa_n4k_fwd"], seqlen=288, hq=4, hkv=2, block=32, head_dim=64,
+                                          top_k=3),
 }
 MODES = [oracle.DUAL_ACTIVE_FULL, oracle.DUAL_ACTIVE_SPARSE, oracle.FULL_ONLY, oracle.SPARSE_ONLY]
 
