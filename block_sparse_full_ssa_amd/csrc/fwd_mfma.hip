@@ -230,6 +230,22 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
         for (int ds = 0; ds < HD / 16; ++ds)
           s = mfma32x32x16(lds_read8(&Ks[r * HD + 8 * swz_k<HD>(r, 2 * ds + g)]), qreg[ds], s);
       }
+      // V^T operand of P V step u: key rows kh 32 + (u / kDT) 16 + 4 gk +
+      // srow and 8 further (tv), column tile u % kDT; the row part is a
+      // constant of the unrolled loops
+      auto rd_vt = [&](int u) {
+        const int x = 64 * (u % kDT), rb = 2 * HD * (kh * 32 + (u / kDT) * 16);
+        return lds_tr_pair(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(Vs) + ((tv[0] ^ x) + rb)),
+                           reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(Vs) + ((tv[1] ^ x) + rb)));
+      };
+      // (the diagnostics variant keeps its registers for its sums: no read-ahead)
+      constexpr bool kAhead = !STATS;
+      bf16x8 va_n, va_nn;
+      if constexpr (kAhead) {
+        va_n = rd_vt(0);
+        va_nn = rd_vt(1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // logits stay unscaled: the scale (> 0) goes into the maximum and into
       // each exponent's fused multiply-add
       if (kbase + 31 > wave_q0) {                  // uniform: the diagonal needs the causal mask
@@ -324,21 +340,27 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
         ms = msn;
       }
 
-      // ---- O^T += V^T P^T over the 32 keys (two k-steps of 16)
+      // ---- O^T += V^T P^T over the 32 keys (two k-steps of 16); step u
+      // is k-step u / kDT and column tile u % kDT, its V^T operand read two
+      // steps ahead (the first two during the softmax)
 #pragma unroll
-      for (int st2 = 0; st2 < 2; ++st2) {
-#pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) {
-          // key rows kh 32 + st2 16 + 4 gk + srow and 8 further (tv), the row
-          // part a constant of the unrolled loop
-          const int x = 64 * dt, rb = 2 * HD * (kh * 32 + st2 * 16);
-          const bf16x8 va =
-              lds_tr_pair(reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(Vs) + ((tv[0] ^ x) + rb)),
-                          reinterpret_cast<const uint16_t*>(reinterpret_cast<const char*>(Vs) + ((tv[1] ^ x) + rb)));
-          of[dt] = mfma32x32x16(va, pf[st2], of[dt]);
-          if (kSparse && sparse_any) os[dt] = mfma32x32x16(va, ps[st2], os[dt]);
+      for (int u = 0; u < 2 * kDT; ++u) {
+        bf16x8 va;
+        if constexpr (kAhead) {
+          va = va_n;
+          va_n = va_nn;
+          __builtin_amdgcn_sched_barrier(0);
+          if (u + 2 < 2 * kDT) {
+            va_nn = rd_vt(u + 2);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // the two reads before the products
+          }
+        } else {
+          va = rd_vt(u);
         }
+        of[u % kDT] = mfma32x32x16(va, pf[u / kDT], of[u % kDT]);
+        if (kSparse && sparse_any) os[u % kDT] = mfma32x32x16(va, ps[u / kDT], os[u % kDT]);
       }
+      if constexpr (kAhead) __builtin_amdgcn_sched_barrier(0);
     }
   }
     __builtin_amdgcn_s_waitcnt(0);     // the next tile has landed in LDS
