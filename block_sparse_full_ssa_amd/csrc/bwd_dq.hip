@@ -271,6 +271,19 @@ __global__ void __launch_bounds__(256, 2)
           }
           __builtin_amdgcn_sched_barrier(0);
         }
+        // K^T operands of the dQ products (step u: k-step u / kDT, column
+        // tile u % kDT); the first two are read during dS
+        bf16x8 ka[2 * kDT];
+        auto rdk = [&](int u) {
+          const int st = u / kDT, dt = u % kDT;
+          const int rb = 2 * kD * (kh * 32 + st * 16);
+          const char* kb = reinterpret_cast<const char*>(Ks);
+          ka[u] = lds_tr_pair(reinterpret_cast<const uint16_t*>(kb + ((tk[0] ^ (64 * dt)) + rb)),
+                              reinterpret_cast<const uint16_t*>(kb + ((tk[1] ^ (64 * dt)) + rb)));
+        };
+        rdk(0);
+        rdk(1);
+        __builtin_amdgcn_sched_barrier(0);
         // ---- dS^T = P^T (dP^T - D); key of register i: kbase + 8(i/4) + 4g + i%4
         const bool diag = kbase + 31 > wave_q0;      // uniform
         // (training modes: plus the sparse stream's dS, element i of its row
@@ -318,23 +331,19 @@ __global__ void __launch_bounds__(256, 2)
           }
         }
         // ---- dQ^T += K^T dS^T over the 32 keys (two k-steps of 16)
-        bf16x8 bds[2], ka[2 * kDT];
+        bf16x8 bds[2];
 #pragma unroll
         for (int st = 0; st < 2; ++st)
           bds[st] = to_bf16x8(dsv[8 * st], dsv[8 * st + 1], dsv[8 * st + 2], dsv[8 * st + 3], dsv[8 * st + 4],
                               dsv[8 * st + 5], dsv[8 * st + 6], dsv[8 * st + 7]);
-        auto rdk = [&](int u) {
-          const int st = u / kDT, dt = u % kDT;
-          const int rb = 2 * kD * (kh * 32 + st * 16);
-          const char* kb = reinterpret_cast<const char*>(Ks);
-          ka[u] = lds_tr_pair(reinterpret_cast<const uint16_t*>(kb + ((tk[0] ^ (64 * dt)) + rb)),
-                              reinterpret_cast<const uint16_t*>(kb + ((tk[1] ^ (64 * dt)) + rb)));
-        };
-        rdk(0);
 #pragma unroll
-        for (int u = 0; u < 2 * kDT; ++u) {           // K^T read one step ahead
+        for (int u = 0; u < 2 * kDT; ++u) {           // K^T read two steps ahead
           __builtin_amdgcn_sched_barrier(0);
-          if (u + 1 < 2 * kDT) rdk(u + 1);
+          if (u + 2 < 2 * kDT) {
+            rdk(u + 2);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // the reads, then the product
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          }
           dq[u % kDT] = mfma32x32x16(ka[u], bds[u / kDT], dq[u % kDT]);
         }
         __builtin_amdgcn_sched_barrier(0);

@@ -326,6 +326,19 @@ __global__ void __launch_bounds__(256, 2)
         dpf = mfma32x32x16(of[ds], vb[ds], dpf);
       }
       __builtin_amdgcn_sched_barrier(0);
+      // G^T and Q^T operands of the dV / dK products (step u: k-step u / kDT
+      // of 16 queries, column tile u % kDT), read two steps ahead: the first
+      // two during the softmax
+      bf16x8 tg[2 * kDT], tq[2 * kDT];
+      auto rdB = [&](int u) {
+        const int x0 = (trb[0] ^ (64 * (u % kDT))) + 32 * kD * (u / kDT);
+        const int x1 = (trb[1] ^ (64 * (u % kDT))) + 32 * kD * (u / kDT);
+        tg[u] = tr16(Fs, x0, x1);
+        tq[u] = tr16(Qs, x0, x1);
+      };
+      rdB(0);
+      rdB(1);
+      __builtin_amdgcn_sched_barrier(0);
       // ---- probabilities and dS, packed to bf16 pairs (register i: query
       // 8(i/4) + 4g + i%4, visible iff 8(i/4) + i%4 >= t on diagonal tiles;
       // dS of a masked pair is zero because its P is)
@@ -351,26 +364,21 @@ __global__ void __launch_bounds__(256, 2)
         dsp[2 * a4] = pack_bf16x2(e[0], e[1]);
         dsp[2 * a4 + 1] = pack_bf16x2(e[2], e[3]);
       }
-      // ---- dV^T += G^T P, dK^T += Q^T dS  (k = queries; 2 steps of 16),
-      // transpose reads one step ahead
-      bf16x8 bpf[2], bds[2], tg[2 * kDT], tq[2 * kDT];
+      // ---- dV^T += G^T P, dK^T += Q^T dS  (k = queries; 2 steps of 16)
+      bf16x8 bpf[2], bds[2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         bpf[st] = __builtin_bit_cast(bf16x8, make_uint4(pfp[4 * st], pfp[4 * st + 1], pfp[4 * st + 2], pfp[4 * st + 3]));
         bds[st] = __builtin_bit_cast(bf16x8, make_uint4(dsp[4 * st], dsp[4 * st + 1], dsp[4 * st + 2], dsp[4 * st + 3]));
       }
-      // step u: k-step st = u / kDT (16 queries), column tile dt = u % kDT
-      auto rdB = [&](int u) {
-        const int x0 = (trb[0] ^ (64 * (u % kDT))) + 32 * kD * (u / kDT);
-        const int x1 = (trb[1] ^ (64 * (u % kDT))) + 32 * kD * (u / kDT);
-        tg[u] = tr16(Fs, x0, x1);
-        tq[u] = tr16(Qs, x0, x1);
-      };
-      rdB(0);
 #pragma unroll
       for (int u = 0; u < 2 * kDT; ++u) {
         __builtin_amdgcn_sched_barrier(0);
-        if (u + 1 < 2 * kDT) rdB(u + 1);
+        if (u + 2 < 2 * kDT) {
+          rdB(u + 2);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // the reads, then the products
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
         dv[u % kDT] = mfma32x32x16(tg[u], bpf[u / kDT], dv[u % kDT]);
         dk[u % kDT] = mfma32x32x16(tq[u], bds[u / kDT], dk[u % kDT]);
       }
