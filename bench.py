@@ -77,13 +77,13 @@ def algorithmic_flops_per_launch(d, pf, ps, heads):
             "sparse_part": 4.0 * d * ps * heads}
 
 
-def measured_traffic(kernel, workload, top_k):
-    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter
-    summary (FETCH_SIZE + WRITE_SIZE, calibrated by a plain copy), or None when
-    there is none for this workload or the kernel's source changed since."""
+def profile_record(name, kernel, workload, top_k):
+    """The record of ``kernel`` in the committed rocprofv3 summary
+    ``profiles/<name>.json``, or None when there is none for this workload or
+    the kernel's source changed since the counters were taken."""
     import hashlib
 
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    path = os.path.join(ROOT, "profiles", name + ".json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -95,7 +95,25 @@ def measured_traffic(kernel, workload, top_k):
     with open(src, "rb") as f:
         if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
             return None
-    return rec["bytes_per_launch"]
+    return rec
+
+
+def measured_traffic(kernel, workload, top_k):
+    """HBM bytes per launch of ``kernel`` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated by a plain copy), or None."""
+    rec = profile_record("hbm_traffic", kernel, workload, top_k)
+    return rec["bytes_per_launch"] if rec else None
+
+
+def matrix_pipe_use(kernels, workload, top_k):
+    """Per matrix kernel, rocprofv3's MfmaUtil (matrix pipes busy over active
+    cycles), the executed bf16 matrix flops and the clock, from the committed
+    counter summary; None for a kernel whose source changed since."""
+    out = {}
+    for kid in kernels:
+        rec = profile_record("mfma_util", kid, workload, top_k)
+        out[kid] = None if rec is None else {k: rec[k] for k in ("mfma_util_pct", "clock_ghz", "executed_bf16_flops")}
+    return out
 
 
 def parse():
@@ -664,6 +682,8 @@ def main():
         "kernels_ms_avg": {n: round(kk["avg_ms"], 4) for n, kk in kernels.items()},
         "roofline": roofline,
         "kernel_frac_of_bf16_peak": kernel_frac,
+        "matrix_pipe_use": dict(matrix_pipe_use(("bwd_mfma", "fwd_mfma", "bwd_dq", "bwd_sparse"), wl.name, K),
+                                source="profiles/mfma_util_train_b2_h32_n16k.md (rocprofv3 --pmc MfmaUtil)"),
         "measured_ceilings": ceilings,
         "frac_of_measured_mfma": round(tflops / ceilings["mfma_bf16_tflops"], 4),
         "cpu_baseline": cpu,

@@ -12,14 +12,15 @@
       kernel, the bytes and the sha256 of the kernel's source so that a
       reader can tell when the figures no longer describe the code.
 
-  python -m block_sparse_full_ssa_amd.profile_summary mfma PMC STATS OUT.md TITLE
+  python -m block_sparse_full_ssa_amd.profile_summary mfma PMC STATS OUT.md [OUT.json WORKLOAD TOP_K] TITLE
       matrix-core use per kernel from one `--pmc MfmaUtil
       SQ_INSTS_VALU_MFMA_MOPS_BF16 GRBM_GUI_ACTIVE` pass: MfmaUtil (the
       matrix pipes' busy cycles summed over the SIMDs over active cycles
       times the SIMD count), the bf16 matrix flops the kernel executed (MOPS
       x 512, the implemented work), and the clock the GPU ran at
       (GRBM_GUI_ACTIVE per XCD over the kernel's average duration in the
-      stats run STATS).
+      stats run STATS); with OUT.json, those figures of the matrix kernels
+      with the sha256 of each kernel's source, as for the traffic.
 
   python -m block_sparse_full_ssa_amd.profile_summary lds PMC OUT.md TITLE
       per mode of the LDS probe (lds_patterns.py launches modes 0 .. 9 once
@@ -119,7 +120,8 @@ def traffic(fd, wd, cfd, cwd, out_md, out_json, workload, top_k, title) -> None:
         f.write("\n")
 
 
-def mfma(pd: str, sd: str, out: str, title: str, n_xcd: int = 8) -> None:
+def mfma(pd: str, sd: str, out: str, title: str, out_json: str = None, workload: str = None, top_k: int = None,
+         n_xcd: int = 8) -> None:
     pmc = counters(pd)
     files = glob.glob(os.path.join(sd, "**", "*kernel_stats.csv"), recursive=True)
     if not files:
@@ -127,13 +129,24 @@ def mfma(pd: str, sd: str, out: str, title: str, n_xcd: int = 8) -> None:
     avg_ns = {short(r["Name"]): float(r["AverageNs"]) for r in csv.DictReader(open(files[0]))}
     rows = [(k, cs) for k, cs in pmc.items() if k.startswith("k_") and cs.get("MfmaUtil", 0.0) > 0.0]
     rows.sort(key=lambda kc: -kc[1].get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0))
-    lines = []
+    lines, table = [], {}
     for k, cs in rows:
         flops = cs.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512
         ns = avg_ns.get(k)
         clock = f"{cs.get('GRBM_GUI_ACTIVE', 0.0) / n_xcd / ns:.2f}" if ns else "-"
         rate = f"{flops / ns / 1e3:.0f}" if ns and flops else "-"
         lines.append(f"| `{k}` | {cs['MfmaUtil']:.1f} | {flops:.3g} | {rate} | {clock} |")
+        for pre, kid, src in KERNELS:
+            if out_json and k.startswith(pre):
+                sha = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
+                table[f"{kid}/{workload}/top_k={top_k}"] = {
+                    "mfma_util_pct": round(cs["MfmaUtil"], 1), "executed_bf16_flops": flops,
+                    "clock_ghz": round(cs.get("GRBM_GUI_ACTIVE", 0.0) / n_xcd / ns, 2) if ns else None,
+                    "source": src, "source_sha256": sha, "from": os.path.relpath(out, os.path.dirname(HERE))}
+    if out_json:
+        with open(out_json, "w") as f:
+            json.dump(table, f, indent=1)
+            f.write("\n")
     with open(out, "w") as f:
         f.write(title.rstrip() + "\n\n| kernel | MfmaUtil % | bf16 matrix flops per launch | TFLOP/s (avg duration) "
                 "| clock GHz |\n|---|---|---|---|---|\n")
@@ -183,6 +196,8 @@ if __name__ == "__main__":
         traffic(*a[1:8], int(a[8]), a[9])
     elif a and a[0] == "mfma" and len(a) == 5:
         mfma(a[1], a[2], a[3], a[4])
+    elif a and a[0] == "mfma" and len(a) == 8:
+        mfma(a[1], a[2], a[3], a[7], a[4], a[5], int(a[6]))
     elif a and a[0] == "lds" and len(a) == 4:
         lds(a[1], a[2], a[3])
     else:

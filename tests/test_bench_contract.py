@@ -49,3 +49,30 @@ def test_headline_flops_per_step():
     pf, ps = bench.pairs(16384, 64, 16)
     assert (pf, ps) == (134225920, 15769600)
     assert abs(14 * 128 * (pf + ps) * 2 * 32 - 1.7203e13) < 1e10
+
+
+def test_profile_records_are_dropped_when_the_source_changes(tmp_path, monkeypatch):
+    """Counter figures (traffic, matrix-pipe use) are reported only while the
+    kernel's source is the one they were taken on."""
+    import hashlib
+    import json
+
+    import bench
+
+    csrc = tmp_path / "block_sparse_full_ssa_amd" / "csrc"
+    csrc.mkdir(parents=True)
+    (tmp_path / "profiles").mkdir()
+    (csrc / "k.hip").write_text("kernel v1\n")
+    sha = hashlib.sha256(b"kernel v1\n").hexdigest()
+    rec = {"mfma_util_pct": 50.0, "clock_ghz": 1.5, "executed_bf16_flops": 1.0, "bytes_per_launch": 7,
+           "source": "k.hip", "source_sha256": sha}
+    for name in ("mfma_util", "hbm_traffic"):
+        (tmp_path / "profiles" / f"{name}.json").write_text(json.dumps({"bwd_mfma/w/top_k=16": rec}))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.matrix_pipe_use(("bwd_mfma", "bwd_dq"), "w", 16) == {
+        "bwd_mfma": {"mfma_util_pct": 50.0, "clock_ghz": 1.5, "executed_bf16_flops": 1.0}, "bwd_dq": None}
+    assert bench.measured_traffic("bwd_mfma", "w", 16) == 7
+    assert bench.measured_traffic("bwd_mfma", "w", 4) is None
+    (csrc / "k.hip").write_text("kernel v2\n")
+    assert bench.matrix_pipe_use(("bwd_mfma",), "w", 16) == {"bwd_mfma": None}
+    assert bench.measured_traffic("bwd_mfma", "w", 16) is None
