@@ -322,15 +322,19 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
           // the factor c is a power of two, so each product s c is exact and
           // rounds to the full stream's rounded weight times c (c = 1 when
           // both maxima agree: then the weights and the sum are the full
-          // stream's, bit for bit); the row sum adds the rounded weights
+          // stream's, bit for bit).  The lane's 16 keys lie in one block, so
+          // its sparse half-sum is c times its full half-sum: scaling every
+          // term of a rounded fp32 sum by a power of two scales the sum
+          // exactly (weights below the bf16 normal range aside)
           const float c = sb ? fast_exp2(mfn - msn) : 0.f;
 #pragma unroll
           for (int st = 0; st < 2; ++st) {
             float p[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) p[e] = s[8 * st + e] * c;
-            ps[st] = to_bf16x8_sum(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7], sum_s);
+            ps[st] = to_bf16x8(p[0], p[1], p[2], p[3], p[4], p[5], p[6], p[7]);
           }
+          sum_s = sum * c;
         }
         ls = ls * alpha_s + sum_s;
         if (__any(alpha_s != 1.f)) {
