@@ -219,7 +219,7 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
       if (kSparse) {
         const int blk = kbase / block;
         sb = qrow < qend && blk < nb && ((bits[(wave * 32 + col) * W + (blk >> 5)] >> (blk & 31)) & 1u);
-        sparse_any = __builtin_amdgcn_readfirstlane(__any(sb) ? 1 : 0) != 0;
+        sparse_any = __builtin_amdgcn_ballot_w64(sb) != 0;   // a scalar mask: uniform
       }
 
       // ---- S^T = K Q^T for 32 keys, in log2 units
@@ -268,7 +268,7 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
         const float mxs = sb ? mx : -INFINITY;
         if (mxs > ms + kTau) msn = ceilf(mxs);
         alpha_s = msn == -INFINITY ? 1.f : fast_exp2(ms - msn);
-        rescale = __builtin_amdgcn_readfirstlane(__any(sb && mfn - msn > 64.f) ? 1 : 0) == 0;
+        rescale = __builtin_amdgcn_ballot_w64(sb && mfn - msn > 64.f) == 0;
       }
 
       // ---- sparse probabilities evaluated directly (factor too large)
