@@ -223,13 +223,15 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
       }
 
       // ---- S^T = K Q^T for 32 keys, in log2 units
-      f32x16 s = f32x16{};
-      {
+      auto logits = [&]() {
+        f32x16 acc = f32x16{};
         const int r = kh * 32 + col;
 #pragma unroll
         for (int ds = 0; ds < HD / 16; ++ds)
-          s = mfma32x32x16(lds_read8(&Ks[r * HD + 8 * swz_k<HD>(r, 2 * ds + g)]), qreg[ds], s);
-      }
+          acc = mfma32x32x16(lds_read8(&Ks[r * HD + 8 * swz_k<HD>(r, 2 * ds + g)]), qreg[ds], acc);
+        return acc;
+      };
+      f32x16 s = logits();
       // V^T operand of P V step u: key rows kh 32 + (u / kDT) 16 + 4 gk +
       // srow and 8 further (tv), column tile u % kDT; the row part is a
       // constant of the unrolled loops
@@ -248,20 +250,34 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
       }
       // logits stay unscaled: the scale (> 0) goes into the maximum and into
       // each exponent's fused multiply-add
-      if (kbase + 31 > wave_q0) {                  // uniform: the diagonal needs the causal mask
+      auto mask = [&](f32x16& x) {
+        if (kbase + 31 > wave_q0) {                // uniform: the diagonal needs the causal mask
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kbase + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key > qrow) s[i] = -INFINITY;
+          for (int i = 0; i < 16; ++i) {
+            const int key = kbase + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (key > qrow) x[i] = -INFINITY;
+          }
         }
+      };
+      mask(s);
+      // The full stream alone keeps its reference maximum fixed and finds no
+      // tile maximum: it takes the weights against the reference and moves
+      // the reference (recomputing the tile's logits) only where a lane's
+      // half-sum exceeds 2^64 or is not finite (a wave's first tile), so
+      // every weight stays below 2^64 and every rescale is a power of two.
+      constexpr bool kFixRef = MODE == kModeFull && !STATS;
+      float mx = 0.f;
+      if constexpr (!kFixRef) {
+        mx = max16(s);
+        mx = pair32_max(mx) * scale_log2;
       }
-      float mx = max16(s);
-      mx = pair32_max(mx) * scale_log2;
 
       // ---- new maxima (integers, moved lazily)
       float mfn = mf, alpha = 1.f;
-      if (mx > mf + kTau) mfn = ceilf(mx);
-      alpha = fast_exp2(mf - mfn);                 // 1, 0 (first update) or an exact power of two
+      if constexpr (!kFixRef) {
+        if (mx > mf + kTau) mfn = ceilf(mx);
+        alpha = fast_exp2(mf - mfn);               // 1, 0 (first update) or an exact power of two
+      }
       float msn = ms, alpha_s = 1.f;
       bool rescale = false;
       if (kSparse && sparse_any) {
@@ -287,22 +303,36 @@ __global__ void __launch_bounds__(256, (FwdTile<MODE, HD>::kPerCu))
       // ---- full stream
       bf16x8 pf[2];
       float sum = 0.f, ex = 0.f, sume = 0.f;
+      auto weights = [&]() {
+        sum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float x = fmaf(s[i], scale_log2, -mfn);
-        if (STATS) x = fmaxf(x, -256.f);           // masked keys: e = 0 and e x = 0, not NaN
-        s[i] = fast_exp2(x);
-        if (STATS) {
-          sume += s[i];
-          ex = fmaf(s[i], x, ex);
+        for (int i = 0; i < 16; ++i) {
+          float x = fmaf(s[i], scale_log2, -mfn);
+          if (STATS) x = fmaxf(x, -256.f);         // masked keys: e = 0 and e x = 0, not NaN
+          s[i] = fast_exp2(x);
+          if (STATS) {
+            sume += s[i];
+            ex = fmaf(s[i], x, ex);
+          }
+        }
+        // P enters the products in bf16: round it here, and let the row sum
+        // add exactly those weights
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+          pf[st] = to_bf16x8_sum(s[8 * st], s[8 * st + 1], s[8 * st + 2], s[8 * st + 3], s[8 * st + 4],
+                                 s[8 * st + 5], s[8 * st + 6], s[8 * st + 7], sum);
+      };
+      weights();
+      if constexpr (kFixRef) {
+        if (__builtin_amdgcn_ballot_w64(!(sum <= 0x1p64f)) != 0) {   // uniform, rare
+          s = logits();
+          mask(s);
+          mx = pair32_max(max16(s)) * scale_log2;
+          if (mx > mf + kTau) mfn = ceilf(mx);
+          alpha = fast_exp2(mf - mfn);
+          weights();
         }
       }
-      // P enters the products in bf16: round it here, and let the row sum
-      // add exactly those weights
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-        pf[st] = to_bf16x8_sum(s[8 * st], s[8 * st + 1], s[8 * st + 2], s[8 * st + 3], s[8 * st + 4],
-                               s[8 * st + 5], s[8 * st + 6], s[8 * st + 7], sum);
       if (STATS) {
         // the diagnostics use the unrounded weights: moving the maximum by
         // dm = mfn - mf shifts every earlier x by -dm and scales every earlier

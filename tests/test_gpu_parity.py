@@ -161,6 +161,33 @@ def test_fwd_small_bf16(name, mode):
     _check_fwd(name, wl, out, oracle_fwd(wl, 0, (wl.top_k,), wl.top_k, mode), mode)
 
 
+@pytest.mark.parametrize("mode", [oracle.FULL_ONLY, oracle.DUAL_ACTIVE_FULL])
+@pytest.mark.parametrize("name", ["gqa_n512_b64_k4", "gqa_n256_d64"])
+def test_fwd_late_logit_spike(name, mode):
+    """Queries 200.. of one head meet at key 200 a logit about 100 (log2
+    units) above every earlier logit of theirs, so the reference maximum of
+    their softmax has to move mid-row by more than 2^64 (the full stream
+    alone moves it only when a tile's weights would exceed 2^64); every output
+    still matches the oracle."""
+    wl = SMALL[name]
+    _say(f"fwd late logit spike {name} mode {mode}")
+    (q, k, v), _ = inputs(wl, 0, ())
+    q, k = q.clone(), k.clone()               # the cached inputs of the other tests stay as drawn
+    u = torch.zeros(wl.head_dim)
+    u[0] = 1.0
+    t0 = 200
+    q[0, 0, t0:] = u.to(q.dtype)              # query head 0 reads KV head 0
+    k[0, 0, t0] = (800.0 * u).to(k.dtype)     # logit 800 / sqrt(d) > 70 nats
+    qf, kf, vf = (si.to_f64(x) for x in (q, k, v))
+    sel, _ = oracle.select_blocks(qf, kf, wl.block, wl.top_k, wl.group)
+    qd, kd, vd = to_dev(q, k, v)
+    out = ssa().ssa_attn_fwd(qd, kd, vd, torch.from_numpy(sel).to("cuda:0"), wl.block, wl.top_k, mode)
+    torch.cuda.synchronize()
+    ref = oracle.forward(qf, kf, vf, sel, wl.block, scale_of(wl), wl.group, mode)
+    assert float(ref["lse_full"][0, 0, t0:].min()) > 64 * math.log(2.0)    # the spike dominates
+    _check_fwd(f"spike {name}", wl, out, ref, mode)
+
+
 @pytest.mark.parametrize("top_k", [1, 2, 8, 11])
 def test_sparse_only_fwd_topk_extremes(top_k):
     """SPARSE_ONLY on key-block buckets when each query keeps only its own
