@@ -28,7 +28,9 @@
 //
 // Softmax: the running maxima are integers (ceil of a tile maximum) and move
 // lazily, only when a tile exceeds them by more than kTau, so every rescale
-// factor is an exact power of two.  In particular the sparse probabilities of
+// factor is an exact power of two (the full stream alone skips the tile
+// maximum and moves its reference only when a tile's weights would pass
+// 2^64).  In particular the sparse probabilities of
 // a selected block are P_full * 2^(m_full - m_sparse), an exact fp32 product,
 // whenever that exponent is at most 64; otherwise they are evaluated
 // directly.  When every block is selected the two streams execute identical
